@@ -1,0 +1,151 @@
+"""CPU oracle for the dense fp32 product C = A x B (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never does, and this package imports nothing from it.
+
+The arithmetic lives in ``gemm_oracle.c`` (plain C, binary64 accumulation);
+this module only compiles it with gcc, loads it with ctypes and marshals
+numpy arrays.  See the C file's header for what each function follows on the
+pages ("03 CUDA Shared Memory: Tiling, Bank Conflicts, and Reduction" and the
+PMPP chapter 5 notes "메모리 계층과 데이터 지역성").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gemm_oracle.c")
+_LIB = os.path.join(_HERE, "libgemm_oracle.so")
+
+_i64 = ctypes.c_int64
+_fp = ctypes.POINTER(ctypes.c_float)
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int64)
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle into a shared library (gcc, strict IEEE arithmetic)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
+           "-shared", "-fPIC", "-pthread", "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle library; returns the CDLL."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or _LIB
+    if not os.path.exists(p):
+        build(out=p)
+    lib = ctypes.CDLL(p)
+    lib.oracle_gemm_rows.argtypes = [_i64, _i64, _i64, _fp, _i64, _fp, _i64,
+                                     _dp, _i64, _dp, _i64, _i64, _i64, ctypes.c_int]
+    lib.oracle_gemm_rows.restype = ctypes.c_int
+    lib.oracle_gemm.argtypes = [_i64, _i64, _i64, _fp, _i64, _fp, _i64,
+                                _dp, _i64, _dp, _i64, ctypes.c_int]
+    lib.oracle_gemm.restype = ctypes.c_int
+    lib.oracle_gemm_entries.argtypes = [_i64, _i64, _i64, _fp, _i64, _fp, _i64,
+                                        _i64, _ip, _ip, _dp, _dp]
+    lib.oracle_gemm_entries.restype = ctypes.c_int
+    lib.oracle_tiled_traffic.argtypes = [_i64] * 6 + [_ip]
+    lib.oracle_tiled_traffic.restype = ctypes.c_int
+    lib.oracle_bank_conflict_degree.argtypes = [_i64, _ip, _i64]
+    lib.oracle_bank_conflict_degree.restype = _i64
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _matrix_arg(X: np.ndarray):
+    """(pointer, leading dimension) of a 2-D float32 row-major (possibly
+    padded) view; the view's rows may be spaced wider than its columns."""
+    if X.dtype != np.float32 or X.ndim != 2:
+        raise TypeError("oracle operands must be 2-D float32 arrays")
+    if X.size == 0:
+        return ctypes.cast(ctypes.c_void_p(X.ctypes.data), _fp), max(X.shape[1], 1)
+    if X.shape[1] > 1 and X.strides[1] != 4:
+        raise ValueError("oracle operands need unit column stride")
+    if X.strides[0] % 4:
+        raise ValueError("row stride must be a whole number of floats")
+    ld = X.strides[0] // 4 if X.shape[0] > 1 else max(X.shape[1], 1)
+    ld = max(ld, X.shape[1], 1)
+    ptr = X.ctypes.data_as(_fp)
+    return ptr, ld
+
+
+def gemm(A: np.ndarray, B: np.ndarray, threads: int = 1, rows=None, lib=None):
+    """Returns (C, S): binary64 product A x B and sum_k |A_ik B_kj|.
+
+    ``rows=(r0, r1)`` computes only that band of rows (the other rows of the
+    returned arrays stay zero)."""
+    lib = lib or load()
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    C = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    pa, lda = _matrix_arg(A)
+    pb, ldb = _matrix_arg(B)
+    r0, r1 = (0, M) if rows is None else rows
+    rc = lib.oracle_gemm_rows(M, N, K, pa, lda, pb, ldb,
+                              C.ctypes.data_as(_dp), max(N, 1),
+                              S.ctypes.data_as(_dp), max(N, 1),
+                              r0, r1, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_rows rejected its arguments (rc={rc})")
+    return C, S
+
+
+def gemm_entries(A: np.ndarray, B: np.ndarray, ii, jj, lib=None):
+    """Returns (c, s) for the entries (ii[t], jj[t]) of A x B only."""
+    lib = lib or load()
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    if ii.shape != jj.shape or ii.ndim != 1:
+        raise ValueError("ii and jj must be 1-D of equal length")
+    c = np.zeros(ii.shape[0], dtype=np.float64)
+    s = np.zeros(ii.shape[0], dtype=np.float64)
+    pa, lda = _matrix_arg(A)
+    pb, ldb = _matrix_arg(B)
+    rc = lib.oracle_gemm_entries(M, N, K, pa, lda, pb, ldb, ii.shape[0],
+                                 ii.ctypes.data_as(_ip), jj.ctypes.data_as(_ip),
+                                 c.ctypes.data_as(_dp), s.ctypes.data_as(_dp))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_entries rejected its arguments (rc={rc})")
+    return c, s
+
+
+TRAFFIC_FIELDS = ("a_loads", "b_loads", "a_ghosts", "b_ghosts",
+                  "macs_issued", "macs_useful", "tiles", "phases")
+
+
+def tiled_traffic(M, N, K, BM, BN, BK, lib=None) -> dict:
+    """Brute-force count of global reads / ghost slots / multiply-adds of the
+    tiled phase loop with BM x BN output tiles and BK-deep phases."""
+    lib = lib or load()
+    out = (ctypes.c_int64 * 8)()
+    rc = lib.oracle_tiled_traffic(M, N, K, BM, BN, BK, out)
+    if rc != 0:
+        raise ValueError("oracle_tiled_traffic rejected its arguments")
+    return dict(zip(TRAFFIC_FIELDS, list(out)))
+
+
+def bank_conflict_degree(word_addrs, banks: int = 32, lib=None) -> int:
+    """Conflict degree of one shared-memory access (4-byte word addresses)."""
+    lib = lib or load()
+    w = np.ascontiguousarray(word_addrs, dtype=np.int64)
+    return int(lib.oracle_bank_conflict_degree(w.shape[0], w.ctypes.data_as(_ip), banks))

@@ -1,0 +1,326 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Every check takes the loaded oracle library (a ctypes CDLL) and raises
+AssertionError on a mismatch.  ``test_oracle.py`` runs them on the real
+oracle; ``test_oracle_mutations.py`` runs them, in a subprocess, on copies of
+the oracle with a planted mistake and expects at least one to fail.
+
+None of these checks re-types the oracle's formula: they compare it with exact
+integer arithmetic, closed forms, algebraic identities, an independent
+binary64 library product, or the numbers the pages print
+(``golden/pages_numbers.json``).
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "pages_numbers.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _ints(gen, rows, cols, lo=-2, hi=2):
+    return gen.integers(lo, hi + 1, size=(rows, cols)).astype(np.float32)
+
+
+def _py_product(A, B):
+    """Exact integer product with Python ints (brute force)."""
+    M, K = A.shape
+    N = B.shape[1]
+    a = [[int(x) for x in row] for row in A]
+    b = [[int(x) for x in row] for row in B]
+    C = [[0] * N for _ in range(M)]
+    S = [[0] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            c = s = 0
+            for k in range(K):
+                p = a[i][k] * b[k][j]
+                c += p
+                s += abs(p)
+            C[i][j] = c
+            S[i][j] = s
+    return C, S
+
+
+# ---------------------------------------------------------------- products --
+
+def check_bruteforce_tiny(lib):
+    """Integer inputs, every M, N, K in 1..9 and K = 0: exact equality with
+    Python-int brute force, for C and for S."""
+    gen = np.random.default_rng(101)
+    sizes = [1, 2, 3, 5, 8, 9]
+    for M, N, K in itertools.product(sizes, sizes, [0] + sizes):
+        A = _ints(gen, M, K, -9, 9)
+        B = _ints(gen, K, N, -9, 9)
+        C, S = oracle.gemm(A, B, lib=lib)
+        Ce, Se = _py_product(A, B)
+        assert np.array_equal(C, np.array(Ce, dtype=np.float64).reshape(M, N)), (M, N, K)
+        assert np.array_equal(S, np.array(Se, dtype=np.float64).reshape(M, N)), (M, N, K)
+
+
+def check_bruteforce_tile_straddling(lib):
+    """Integer inputs at sizes one below/above one and two tile edges for the
+    tile sizes the kernels use: exact equality with int64 arithmetic."""
+    gen = np.random.default_rng(102)
+    for T in (16, 32, 64, 128):
+        for (M, N, K) in ((T - 1, T + 1, 2 * T + 1), (T + 1, 2 * T - 1, T - 1),
+                          (2 * T + 1, T - 1, T + 1)):
+            A = _ints(gen, M, K)
+            B = _ints(gen, K, N)
+            C, S = oracle.gemm(A, B, threads=4, lib=lib)
+            Ai, Bi = A.astype(np.int64), B.astype(np.int64)
+            assert np.array_equal(C, (Ai @ Bi).astype(np.float64)), (T, M, N, K)
+            assert np.array_equal(S, (np.abs(Ai) @ np.abs(Bi)).astype(np.float64)), (T, M, N, K)
+
+
+def check_identity_and_zero(lib):
+    """A I = A and I B = B exactly; A 0 and 0 B are +0 (not -0)."""
+    gen = np.random.default_rng(103)
+    A = (2 * gen.random((37, 23), dtype=np.float32) - 1).astype(np.float32)
+    B = (2 * gen.random((23, 41), dtype=np.float32) - 1).astype(np.float32)
+    C, _ = oracle.gemm(A, np.eye(23, dtype=np.float32), lib=lib)
+    assert np.array_equal(C, A.astype(np.float64))
+    C, _ = oracle.gemm(np.eye(23, dtype=np.float32), B, lib=lib)
+    assert np.array_equal(C, B.astype(np.float64))
+    C, S = oracle.gemm(A, np.zeros((23, 19), np.float32), lib=lib)
+    assert np.all(C == 0) and not np.any(np.signbit(C)) and np.all(S == 0)
+    C, S = oracle.gemm(np.zeros((11, 23), np.float32), B, lib=lib)
+    assert np.all(C == 0) and not np.any(np.signbit(C)) and np.all(S == 0)
+    # every product is -0 here; the sum starts from +0, so the result is +0
+    C, _ = oracle.gemm(-np.ones((3, 23), np.float32), np.zeros((23, 4), np.float32), lib=lib)
+    assert np.all(C == 0) and not np.any(np.signbit(C))
+    # an empty sum (K = 0) is +0
+    C, S = oracle.gemm(np.zeros((3, 0), np.float32), np.zeros((0, 4), np.float32), lib=lib)
+    assert np.all(C == 0) and not np.any(np.signbit(C)) and np.all(S == 0)
+
+
+def check_closed_forms(lib):
+    """All-ones gives K everywhere; A[i,k] = (i mod 7) - 3, B[k,j] = (j mod 5) - 2
+    gives K ((i mod 7) - 3)((j mod 5) - 2)."""
+    for (M, N, K) in ((33, 65, 17), (129, 31, 257)):
+        C, S = oracle.gemm(np.ones((M, K), np.float32), np.ones((K, N), np.float32), lib=lib)
+        assert np.all(C == K) and np.all(S == K)
+        i = np.arange(M)[:, None]
+        j = np.arange(N)[None, :]
+        A = np.broadcast_to((i % 7) - 3, (M, K)).astype(np.float32)
+        B = np.broadcast_to((j % 5) - 2, (K, N)).astype(np.float32)
+        C, S = oracle.gemm(np.ascontiguousarray(A), np.ascontiguousarray(B), lib=lib)
+        assert np.array_equal(C, (K * ((i % 7) - 3) * ((j % 5) - 2)).astype(np.float64))
+        assert np.array_equal(S, (K * np.abs((i % 7) - 3) * np.abs((j % 5) - 2)).astype(np.float64))
+
+
+def check_library_float64(lib):
+    """Against numpy's binary64 matmul on float inputs: within 1e-12 S."""
+    gen = np.random.default_rng(104)
+    for (M, N, K) in ((64, 48, 100), (17, 130, 257)):
+        A = (2 * gen.random((M, K), dtype=np.float32) - 1).astype(np.float32)
+        B = gen.standard_normal((K, N), dtype=np.float32)
+        C, S = oracle.gemm(A, B, lib=lib)
+        ref = A.astype(np.float64) @ B.astype(np.float64)
+        sref = np.abs(A.astype(np.float64)) @ np.abs(B.astype(np.float64))
+        assert np.all(np.abs(C - ref) <= 1e-12 * sref)
+        assert np.all(np.abs(S - sref) <= 1e-12 * sref)
+        assert np.all(sref > 0)
+
+
+def check_linearity_and_scaling(lib):
+    """C(A, B1 + B2) = C(A, B1) + C(A, B2) to rounding (the sums B1 + B2 are
+    exact in binary32 here), and C(2A, B) = 2 C(A, B) bit for bit."""
+    gen = np.random.default_rng(105)
+    M, N, K = 40, 50, 300
+    A = (2 * gen.random((M, K), dtype=np.float32) - 1).astype(np.float32)
+    B1 = (2 * gen.random((K, N), dtype=np.float32) - 1).astype(np.float32)
+    B2 = (2 * gen.random((K, N), dtype=np.float32) - 1).astype(np.float32)
+    Bs = (B1 + B2).astype(np.float32)
+    assert np.array_equal(Bs.astype(np.float64), B1.astype(np.float64) + B2.astype(np.float64))
+    C12, S12 = oracle.gemm(A, Bs, lib=lib)
+    C1, S1 = oracle.gemm(A, B1, lib=lib)
+    C2, S2 = oracle.gemm(A, B2, lib=lib)
+    assert np.all(np.abs(C12 - C1 - C2) <= 1e-13 * (S1 + S2))
+    C2A, S2A = oracle.gemm((2 * A).astype(np.float32), B1, lib=lib)
+    assert np.array_equal(C2A, 2 * C1) and np.array_equal(S2A, 2 * S1)
+    CA2, _ = oracle.gemm(A, (0.5 * B1).astype(np.float32), lib=lib)
+    assert np.array_equal(CA2, 0.5 * C1)
+
+
+def check_transpose_identity(lib):
+    """(A B)^T = B^T A^T bit for bit: each entry sums the same products in the
+    same k order, so a swapped operand or index shows up here."""
+    gen = np.random.default_rng(106)
+    A = gen.standard_normal((23, 57), dtype=np.float32)
+    B = gen.standard_normal((57, 31), dtype=np.float32)
+    C, S = oracle.gemm(A, B, lib=lib)
+    Ct, St = oracle.gemm(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T), lib=lib)
+    assert np.array_equal(C.T, Ct) and np.array_equal(S.T, St)
+
+
+def check_padded_views(lib):
+    """Leading dimensions larger than the column count and a base offset of one
+    float give the same bits as compact storage; NaN padding is never read."""
+    gen = np.random.default_rng(107)
+    M, N, K = 19, 29, 37
+    A = gen.standard_normal((M, K), dtype=np.float32)
+    B = gen.standard_normal((K, N), dtype=np.float32)
+    C0, S0 = oracle.gemm(A, B, lib=lib)
+    for lda, ldb, off in ((K + 3, N + 5, 1), (K + 8, N + 1, 3)):
+        abuf = np.full(off + M * lda + 16, np.nan, np.float32)
+        bbuf = np.full(off + K * ldb + 16, np.nan, np.float32)
+        Av = abuf[off:off + M * lda].reshape(M, lda)[:, :K]
+        Bv = bbuf[off:off + K * ldb].reshape(K, ldb)[:, :N]
+        Av[:] = A
+        Bv[:] = B
+        C, S = oracle.gemm(Av, Bv, lib=lib)
+        assert np.array_equal(C, C0) and np.array_equal(S, S0)
+
+
+def check_entries_rows_threads(lib):
+    """Selected entries, row bands and any thread count reproduce the full
+    single-threaded product bit for bit."""
+    gen = np.random.default_rng(108)
+    M, N, K = 45, 38, 129
+    A = gen.standard_normal((M, K), dtype=np.float32)
+    B = gen.standard_normal((K, N), dtype=np.float32)
+    C1, S1 = oracle.gemm(A, B, threads=1, lib=lib)
+    C7, S7 = oracle.gemm(A, B, threads=7, lib=lib)
+    assert np.array_equal(C1, C7) and np.array_equal(S1, S7)
+    Cb, Sb = oracle.gemm(A, B, rows=(10, 21), threads=3, lib=lib)
+    assert np.array_equal(Cb[10:21], C1[10:21]) and np.all(Cb[:10] == 0) and np.all(Cb[21:] == 0)
+    ii = gen.integers(0, M, 200)
+    jj = gen.integers(0, N, 200)
+    c, s = oracle.gemm_entries(A, B, ii, jj, lib=lib)
+    assert np.array_equal(c, C1[ii, jj]) and np.array_equal(s, S1[ii, jj])
+
+
+# ------------------------------------------------------ traffic bookkeeping --
+
+def check_naive_intensity(lib):
+    """One thread per output reads one A and one B float per multiply-add:
+    0.25 FLOP/B, the pages' naive figure, for square and ragged shapes."""
+    g = _golden()["naive_intensity"]["flop_per_byte"]
+    for (M, N, K) in ((8, 8, 8), (5, 7, 3), (16, 4, 9)):
+        t = oracle.tiled_traffic(M, N, K, 1, 1, 1, lib=lib)
+        flop = 2 * t["macs_useful"]
+        byts = 4 * (t["a_loads"] + t["b_loads"])
+        assert flop / byts == g and t["a_ghosts"] == 0 and t["b_ghosts"] == 0
+        assert t["macs_useful"] == M * N * K
+
+
+def check_tiled_intensity_and_traffic(lib):
+    """Square N, tile T dividing N: 8NT bytes and 2N T^2 FLOP per block,
+    intensity T/4 (4 at 16, 8 at 32), 2N/T floats read per output, and the
+    traffic ratios 1/16 and 1/32 -- all as printed on the pages."""
+    gold = _golden()
+    ai = gold["tiled_intensity"]["flop_per_byte_by_tile"]
+    gain = gold["tiled_intensity"]["gain_over_naive_by_tile"]
+    ratio = gold["traffic_per_output"]["ratio_by_tile"]
+    naive = gold["naive_intensity"]["flop_per_byte"]
+    for T in (16, 32):
+        N = 4 * T
+        t = oracle.tiled_traffic(N, N, N, T, T, T, lib=lib)
+        blocks = t["tiles"]
+        assert blocks == (N // T) ** 2 and t["phases"] == N // T
+        bytes_per_block = 4 * (t["a_loads"] + t["b_loads"]) / blocks
+        flop_per_block = 2 * t["macs_useful"] / blocks
+        assert bytes_per_block == 8 * N * T
+        assert flop_per_block == 2 * N * T * T
+        assert flop_per_block / bytes_per_block == ai[str(T)]
+        assert (flop_per_block / bytes_per_block) / naive == gain[str(T)]
+        per_output = (t["a_loads"] + t["b_loads"]) / (N * N)
+        assert per_output == 2 * N / T
+        assert per_output / (2 * N) == ratio[str(T)]
+
+
+def check_tiled_traffic_ragged(lib):
+    """Ragged shapes: reads are M K ceil(N/BN) + K N ceil(M/BM), ghosts fill
+    the rest of every staged tile, useful multiply-adds are M N K, and the
+    per-phase staging of a square T tile is the pages' 2 T^2 floats."""
+    for (M, N, K, BM, BN, BK) in ((37, 45, 29, 16, 16, 16), (33, 17, 65, 32, 16, 8),
+                                  (100, 100, 100, 64, 32, 16), (5, 6, 7, 8, 8, 8)):
+        t = oracle.tiled_traffic(M, N, K, BM, BN, BK, lib=lib)
+        tm, tn, ph = -(-M // BM), -(-N // BN), -(-K // BK)
+        assert t["tiles"] == tm * tn and t["phases"] == ph
+        assert t["a_loads"] == M * K * tn and t["b_loads"] == K * N * tm
+        assert t["a_loads"] + t["a_ghosts"] == tm * tn * ph * BM * BK
+        assert t["b_loads"] + t["b_ghosts"] == tm * tn * ph * BK * BN
+        assert t["macs_issued"] == tm * tn * ph * BM * BN * BK
+        assert t["macs_useful"] == M * N * K
+    smem = _golden()["shared_memory_per_block"]
+    for T in (16, 32, 64):
+        t = oracle.tiled_traffic(T, T, T, T, T, T, lib=lib)
+        staged_bytes = 4 * (t["a_loads"] + t["a_ghosts"] + t["b_loads"] + t["b_ghosts"])
+        assert staged_bytes == smem["kb_by_tile"][str(T)] * 1024
+        assert smem["limit_kb"] * 1024 // staged_bytes == smem["blocks_by_tile"][str(T)]
+
+
+def check_naive_roofline_context(lib):
+    """The pages' A100 context: bandwidth times the naive intensity gives the
+    0.375 TFLOPS bound, about 1.9 percent of 19.5 TFLOPS."""
+    g = _golden()["naive_roofline_a100"]
+    t = oracle.tiled_traffic(4, 4, 4, 1, 1, 1, lib=lib)
+    ai = 2 * t["macs_useful"] / (4 * (t["a_loads"] + t["b_loads"]))
+    bound = g["bandwidth_tb_s"] * ai
+    assert math.isclose(bound, g["bound_tflops"], rel_tol=1e-12)
+    assert round(100 * bound / g["peak_tflops"], 1) == g["fraction_percent"]
+
+
+# ------------------------------------------------------------- bank model --
+
+def check_bank_model(lib):
+    """gcd(S, 32)-way conflicts for the pages' strides; column reads of a
+    [32][32] tile are 32-way, of a [32][33] tile conflict free; an XOR-swizzled
+    [32][32] tile is conflict free by rows and by columns; in the tiled product
+    the B-tile row read is spread and the A-tile read is a broadcast."""
+    g = _golden()["bank_conflicts"]
+    lanes = np.arange(32, dtype=np.int64)
+    for S, deg in g["degree_by_stride"].items():
+        assert oracle.bank_conflict_degree(lanes * int(S), g["banks"], lib=lib) == deg
+        assert deg == math.gcd(int(S), 32)
+    c = 5
+    assert oracle.bank_conflict_degree(lanes * 32 + c, lib=lib) == g["transpose_column_read_32x32"]
+    assert oracle.bank_conflict_degree(lanes * 33 + c, lib=lib) == g["transpose_column_read_32x33"]
+    for y in range(32):   # row y written by lanes x = 0..31 at column x ^ y
+        assert oracle.bank_conflict_degree(y * 32 + (lanes ^ y), lib=lib) == g["transpose_xor_swizzle_row_and_column"]
+    for x in range(32):   # column x read by lanes y = 0..31 at column y ^ x ... of row y
+        assert oracle.bank_conflict_degree(lanes * 32 + (x ^ lanes), lib=lib) == g["transpose_xor_swizzle_row_and_column"]
+    k, ty = 7, 3
+    assert oracle.bank_conflict_degree(k * 32 + lanes, lib=lib) == g["tiled_product_reads"]       # Bs[k][tx]
+    assert oracle.bank_conflict_degree(np.full(32, ty * 32 + k), lib=lib) == g["tiled_product_reads"]  # As[ty][k]
+
+
+ALL_CHECKS = [
+    check_bruteforce_tiny, check_bruteforce_tile_straddling, check_identity_and_zero,
+    check_closed_forms, check_library_float64, check_linearity_and_scaling,
+    check_transpose_identity, check_padded_views, check_entries_rows_threads,
+    check_naive_intensity, check_tiled_intensity_and_traffic, check_tiled_traffic_ragged,
+    check_naive_roofline_context, check_bank_model,
+]
+
+
+def run_all(lib):
+    """Runs every check; returns the names of those that failed."""
+    failed = []
+    for chk in ALL_CHECKS:
+        try:
+            chk(lib)
+        except AssertionError:
+            failed.append(chk.__name__)
+    return failed
+
+
+if __name__ == "__main__":      # used by the mutation test in a subprocess
+    import sys
+    lib = oracle.load(sys.argv[1])
+    bad = run_all(lib)
+    print("FAILED:" + ",".join(bad))
+    sys.exit(3 if bad else 0)

@@ -1,0 +1,54 @@
+"""Plants plausible mistakes in copies of the oracle (on the CPU) and checks
+that the pins catch every one of them.
+
+Each mutant is a textual edit of ``oracle/gemm_oracle.c`` compiled into a
+temporary library; the pin battery runs in a subprocess (a mutant may read out
+of bounds) and must report at least one failure or die.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "gemm_oracle.c")
+
+MUTANTS = {
+    "transposed_B_index": ("(double)B[k * ldb + j]", "(double)B[j * ldb + k]"),
+    "A_uses_ldb": ("(double)A[i * lda + k]", "(double)A[i * ldb + k]"),
+    "dropped_first_term": ("for (int64_t k = 0; k < K; ++k) {\n        double prod",
+                           "for (int64_t k = 1; k < K; ++k) {\n        double prod"),
+    "dropped_last_term": ("for (int64_t k = 0; k < K; ++k) {\n        double prod",
+                          "for (int64_t k = 0; k < K - 1; ++k) {\n        double prod"),
+    "wrong_sign": ("acc += prod;", "acc -= prod;"),
+    "single_precision_accumulator": ("double acc = 0.0;", "float acc = 0.0f;"),
+    "magnitude_without_abs": ("mag += fabs(prod);", "mag += prod;"),
+    "negative_zero_start": ("double acc = 0.0;", "double acc = -0.0;"),
+    "swapped_output_index": ("job->C[i * job->ldc + j] = c;", "job->C[j * job->ldc + i] = c;"),
+    "traffic_ghost_as_load": ("if (row < M && k < K) out[0]++; else out[2]++;",
+                              "if (row <= M && k < K) out[0]++; else out[2]++;"),
+    "traffic_B_tile_transposed": ("if (k < K && col < N) out[1]++; else out[3]++;",
+                                  "if (k < N && col < K) out[1]++; else out[3]++;"),
+    "bank_broadcast_counted": ("if (!seen)\n                distinct++;", "distinct++;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique/found"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(text.replace(old, new))
+    lib = str(tmp_path / "libmutant.so")
+    oracle.build(src=str(mutant_src), out=lib)
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_pins.py"), lib],
+                          cwd=ROOT, capture_output=True, text=True, timeout=300,
+                          env={**os.environ, "PYTHONPATH": ROOT})
+    # exit 3: some pin failed; negative or other non-zero: the mutant crashed
+    assert proc.returncode != 0, f"no pin caught mutant {name}: {proc.stdout}{proc.stderr}"
+    if proc.returncode == 3:
+        assert "FAILED:" in proc.stdout and proc.stdout.strip() != "FAILED:"
