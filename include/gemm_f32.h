@@ -1,0 +1,125 @@
+/*
+ * gemm_f32.h -- C ABI of the MI355X (gfx950) fp32 matrix-product library.
+ *
+ * The operation is the dense product C = A x B of the pages on shared-memory
+ * tiling ("03 CUDA Shared Memory: Tiling, Bank Conflicts, and Reduction",
+ * section "Shared Memory와 Tiling"; PMPP chapter 5 notes
+ * "메모리 계층과 데이터 지역성", sections 5.4 and 5.5): every output element is
+ * the dot product of one row of A with one column of B, matrices are stored
+ * row by row, sizes need not be multiples of the tile because out-of-range
+ * tile slots hold zero, and only the final store is range checked.  The pages
+ * state it for square Width x Width matrices; this interface takes the
+ * general M x K times K x N case with BLAS-style leading dimensions (an
+ * offset sub-matrix view is a base pointer plus a leading dimension, as in
+ * the first page's "Global Memory와 Coalescing" section).
+ *
+ * Layout (all three matrices row-major, binary32):
+ *   A is M x K,  element (i, k) at A[i*lda + k],  lda >= max(1, K)
+ *   B is K x N,  element (k, j) at B[k*ldb + j],  ldb >= max(1, N)
+ *   C is M x N,  element (i, j) at C[i*ldc + j],  ldc >= max(1, N)
+ *
+ * Result: C[i*ldc + j] = sum_{k<K} A[i*lda + k] * B[k*ldb + j] for i < M,
+ * j < N, rounded in binary32 (summation order and fused multiply-adds vary
+ * by kernel; see the accuracy note below).  C is OVERWRITTEN (no alpha, no
+ * beta, C is never read).  Entries of C outside the M x N window -- the
+ * padding between N and ldc -- are never written.  K == 0 writes +0 to the
+ * whole window.  M == 0 or N == 0 is a no-op that returns GEMM_F32_OK.
+ *
+ * Memory and ownership: A, B and C are DEVICE pointers on the current HIP
+ * device, owned by the caller; the library allocates nothing, keeps no
+ * pointer after returning and holds no state.  A and B are read only.  C
+ * must not overlap A or B (the result is undefined otherwise).  Pointers need
+ * 4-byte alignment only; 16-byte alignment is not required.
+ *
+ * Streams and errors: `stream` is a hipStream_t (NULL = the null stream).
+ * Every call only enqueues work: it returns before the product is computed,
+ * and the caller synchronises the stream to see the result.  Argument errors
+ * are detected synchronously, before anything is enqueued, and are returned
+ * as a nonzero status with no launch.  GEMM_F32_ERR_LAUNCH reports a launch
+ * rejected by the HIP runtime; a fault during execution surfaces at the
+ * caller's next synchronisation, as for any HIP kernel.  All entry points are
+ * thread safe.
+ *
+ * Accuracy: the result of every kernel satisfies, per element,
+ *   |C - C_exact| <= 1e-5 * sum_k |A_ik| |B_kj|
+ * on the workloads the library is tested on, and is bit exact whenever every
+ * product and partial sum is an integer below 2^24 in magnitude (for
+ * instance small-integer inputs).
+ */
+#ifndef GEMM_F32_H
+#define GEMM_F32_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define GEMM_F32_OK                  0
+#define GEMM_F32_ERR_INVALID_DIM     1  /* M, N or K negative                       */
+#define GEMM_F32_ERR_INVALID_LD      2  /* lda < max(1,K), ldb or ldc < max(1,N)     */
+#define GEMM_F32_ERR_NULL_PTR        3  /* a pointer is NULL while its matrix is non-empty */
+#define GEMM_F32_ERR_MISALIGNED      4  /* a pointer is not 4-byte aligned           */
+#define GEMM_F32_ERR_INVALID_VARIANT 5  /* unknown kernel variant                    */
+#define GEMM_F32_ERR_TOO_LARGE       6  /* M, N or K >= 2^31, or the grid would not fit */
+#define GEMM_F32_ERR_LAUNCH          7  /* the HIP runtime rejected the launch       */
+#define GEMM_F32_ERR_DEVICE          8  /* no usable current HIP device              */
+
+/* Kernel ladder.  Each rung computes the same product; each is tested against
+ * the oracle and against the rung below it.
+ *   0  naive: one thread per output element, 16 x 16 workgroups, operands read
+ *      straight from global memory (PMPP one-volume notes, naive matrix
+ *      product; first page, naive kernel)
+ *   1  LDS-tiled: the pages' tiled kernel with T = 32 -- 32 x 32 A and B tiles
+ *      staged cooperatively in LDS with ghost zeros, two barriers per phase,
+ *      rows padded by 4 words, 128-bit coalesced global loads
+ *   2  register-blocked, double-buffered: 128 x 128 workgroup tile, 8 x 8
+ *      outputs per thread in registers, two LDS buffers and one barrier per
+ *      phase, next tile prefetched into registers during the current phase
+ *   3  MFMA: v_mfma_f32_32x32x2_f32 matrix-core contraction on LDS-staged,
+ *      padded, double-buffered tiles (the default)
+ * Variants numbered from 16 up are diagnostic layouts of the same rungs, kept
+ * so that their hardware counters can be compared; see
+ * gemm_f32_variant_name().
+ */
+#define GEMM_F32_VARIANT_NAIVE    0
+#define GEMM_F32_VARIANT_TILED    1
+#define GEMM_F32_VARIANT_REGBLOCK 2
+#define GEMM_F32_VARIANT_MFMA     3
+
+/* C = A x B with the library's best kernel for the shape (the MFMA rung). */
+int gemm_f32(int64_t M, int64_t N, int64_t K,
+             const float *A, int64_t lda,
+             const float *B, int64_t ldb,
+             float *C, int64_t ldc,
+             void *stream);
+
+/* Same contract, with the kernel chosen by `variant` (see above).
+ * Returns GEMM_F32_ERR_INVALID_VARIANT for an unknown number. */
+int gemm_f32_variant(int variant,
+                     int64_t M, int64_t N, int64_t K,
+                     const float *A, int64_t lda,
+                     const float *B, int64_t ldb,
+                     float *C, int64_t ldc,
+                     void *stream);
+
+/* Number of ladder rungs (variants 0 .. n-1). */
+int gemm_f32_num_variants(void);
+
+/* Static, NUL-terminated name of a variant, or NULL if it does not exist.
+ * Valid numbers are 0 .. gemm_f32_num_variants()-1 and the diagnostic
+ * numbers 16 .. 16 + gemm_f32_num_diagnostic_variants() - 1. */
+const char *gemm_f32_variant_name(int variant);
+
+/* Number of diagnostic variants (numbered from 16). */
+int gemm_f32_num_diagnostic_variants(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *gemm_f32_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F32_H */

@@ -1,0 +1,151 @@
+"""Python binding of libgemm_f32.so (argument marshalling only).
+
+The functions mirror the C entry points of ``include/gemm_f32.h`` one to one;
+every step of the product runs in the library's HIP kernels.  torch provides
+device memory and streams: matrix arguments may be torch CUDA tensors (their
+``data_ptr()``, which includes any storage offset) or raw device addresses.
+
+torch is imported before the library is loaded so that both use torch's HIP
+runtime.  There is no fallback: if the library is missing and cannot be
+built, or a call returns a nonzero status, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # noqa: F401  (must precede loading the HIP library)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libgemm_f32.so")
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_lib = None
+_lock = threading.Lock()
+
+OK = 0
+VARIANTS = {"naive": 0, "tiled": 1, "regblock": 2, "mfma": 3}
+DIAGNOSTIC_BASE = 16
+
+
+class GemmError(RuntimeError):
+    """A nonzero status returned by the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"gemm_f32 status {status}: {message}")
+        self.status = status
+
+
+def load_library():
+    """Loads libgemm_f32.so, building it only if no built library exists."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(library_path):
+            from . import build as _build
+            _build.build()
+        lib = ctypes.CDLL(library_path)
+        sig = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+        lib.gemm_f32.argtypes = sig
+        lib.gemm_f32.restype = ctypes.c_int
+        lib.gemm_f32_variant.argtypes = [ctypes.c_int] + sig
+        lib.gemm_f32_variant.restype = ctypes.c_int
+        lib.gemm_f32_num_variants.argtypes = []
+        lib.gemm_f32_num_variants.restype = ctypes.c_int
+        lib.gemm_f32_num_diagnostic_variants.argtypes = []
+        lib.gemm_f32_num_diagnostic_variants.restype = ctypes.c_int
+        lib.gemm_f32_variant_name.argtypes = [ctypes.c_int]
+        lib.gemm_f32_variant_name.restype = ctypes.c_char_p
+        lib.gemm_f32_status_string.argtypes = [ctypes.c_int]
+        lib.gemm_f32_status_string.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _addr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        if x.numel() and not x.is_cuda:
+            raise TypeError("matrix tensors must live on the GPU")
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise GemmError(status, gemm_f32_status_string(status))
+
+
+def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
+    """C = A x B on the library's default kernel; see gemm_f32.h."""
+    lib = load_library()
+    _check(lib.gemm_f32(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _stream(stream)))
+
+
+def gemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
+    """C = A x B on a chosen rung (0..3) or diagnostic variant (16..)."""
+    lib = load_library()
+    if isinstance(variant, str):
+        variant = VARIANTS[variant]
+    _check(lib.gemm_f32_variant(int(variant), M, N, K, _addr(A), lda, _addr(B), ldb,
+                                _addr(C), ldc, _stream(stream)))
+
+
+def gemm_f32_num_variants() -> int:
+    return load_library().gemm_f32_num_variants()
+
+
+def gemm_f32_num_diagnostic_variants() -> int:
+    return load_library().gemm_f32_num_diagnostic_variants()
+
+
+def gemm_f32_variant_name(variant: int) -> str | None:
+    name = load_library().gemm_f32_variant_name(int(variant))
+    return name.decode() if name is not None else None
+
+
+def gemm_f32_status_string(status: int) -> str:
+    return load_library().gemm_f32_status_string(int(status)).decode()
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.dtype != torch.float32:
+        raise TypeError("matrices must be 2-D float32 tensors")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("matrices must be row-major (unit column stride)")
+    return max(t.stride(0) if t.shape[0] > 1 else t.shape[1], t.shape[1], 1)
+
+
+def gemm(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
+         variant=None, stream=None) -> torch.Tensor:
+    """Tensor form: returns ``out`` (allocated if None) = A @ B.  Row-major
+    views with a leading dimension (``stride(0)``) and a storage offset are
+    passed through as they are."""
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    args = (M, N, K, A, _ld(A), B, _ld(B), out, _ld(out))
+    if variant is None:
+        gemm_f32(*args, stream=stream)
+    else:
+        gemm_f32_variant(variant, *args, stream=stream)
+    return out

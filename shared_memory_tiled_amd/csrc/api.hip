@@ -1,0 +1,136 @@
+// api.hip -- the C-ABI entry points declared in include/gemm_f32.h.
+//
+// Argument checking follows the error-checking habit of the PMPP one-volume
+// notes (host program structure: every runtime call's status is checked):
+// every error is reported as a status code, synchronously, before anything
+// is enqueued.  The degenerate sizes follow the tiled kernel's phase loop
+// (PMPP chapter 5 notes, section 5.4): with K = 0 there are no phases and
+// every output is the initial +0; with M = 0 or N = 0 there is no output.
+#include "gemm_f32.h"
+#include "gemm_internal.h"
+
+#include <limits.h>
+
+namespace gemmf32 {
+namespace {
+
+constexpr int kNumRungs = 4;
+constexpr int kDiagBase = 16;
+
+// Diagnostic variants (numbered from 16): same rungs, other layouts or tile
+// shapes, built so their hardware counters can be compared.
+struct Diagnostic { const char* name; int rung; int config; };
+const Diagnostic kDiagnostics[] = {
+    {"tiled32_pad0", 1, 0},
+    {"tiled32_pad1", 1, 1},
+    {"regblock128x128_bk8_padA0", 2, 1},
+    {"regblock128x128_bk16_padA4", 2, 2},
+    {"mfma256x256_bk16_w2x2", 3, 0},
+    {"mfma128x128_bk16_w2x2", 3, 1},
+    {"mfma256x128_bk16_w2x2", 3, 2},
+    {"mfma128x128_bk32_w2x2", 3, 3},
+    {"mfma64x64_bk16_w2x2", 3, 4},
+};
+constexpr int kNumDiagnostics = (int)(sizeof(kDiagnostics) / sizeof(kDiagnostics[0]));
+
+const char* const kRungNames[kNumRungs] = {
+    "naive16x16", "tiled32_pad4", "regblock128x128_bk8_padA4", "mfma_auto"};
+
+bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 3u) != 0; }
+
+// (rows - 1) * ld + cols must be addressable with 64-bit element offsets.
+bool extent_fits(int64_t rows, int64_t cols, int64_t ld) {
+    if (rows == 0 || cols == 0) return true;
+    int64_t last;
+    if (__builtin_mul_overflow(rows - 1, ld, &last)) return false;
+    return !__builtin_add_overflow(last, cols, &last);
+}
+
+int validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+             int64_t ldb, const float* C, int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0) return GEMM_F32_ERR_INVALID_DIM;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+        return GEMM_F32_ERR_INVALID_LD;
+    if (M == 0 || N == 0) return GEMM_F32_OK;           // nothing is read or written
+    if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return GEMM_F32_ERR_NULL_PTR;
+    if (misaligned(C) || (K > 0 && (misaligned(A) || misaligned(B)))) return GEMM_F32_ERR_MISALIGNED;
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_F32_ERR_TOO_LARGE;
+    if (!extent_fits(M, K, lda) || !extent_fits(K, N, ldb) || !extent_fits(M, N, ldc))
+        return GEMM_F32_ERR_TOO_LARGE;
+    // every launch uses at most one block per 16 x 16 outputs and at most 1024
+    // threads per block; keep the grid below 2^32 work-items
+    const int64_t blocks16 = ((M + 15) / 16) * ((N + 15) / 16);
+    if (blocks16 > (int64_t)0xFFFFFFFF / 256) return GEMM_F32_ERR_TOO_LARGE;
+    return GEMM_F32_OK;
+}
+
+int run(int rung, int config, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+        const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != GEMM_F32_OK) return st;
+    if (M == 0 || N == 0) return GEMM_F32_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_F32_ERR_DEVICE;
+    GemmArgs p{(int)M, (int)N, (int)K, A, lda, B, ldb, C, ldc};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    switch (rung) {
+        case 0: e = launch_naive(p, s); break;
+        case 1: e = launch_tiled(p, s, config); break;
+        case 2: e = launch_regblock(p, s, config); break;
+        default: e = launch_mfma(p, s, config < 0 ? mfma_pick_config(p.M, p.N, p.K) : config); break;
+    }
+    if (e == hipErrorInvalidValue) return GEMM_F32_ERR_TOO_LARGE;
+    return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace gemmf32
+
+using namespace gemmf32;
+
+extern "C" int gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                        const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+    return run(3, -1, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+extern "C" int gemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const float* A,
+                                int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                                void* stream) {
+    if (variant >= 0 && variant < kNumRungs) {
+        const int config = variant == 1 ? 4 : (variant == 2 ? 0 : -1);   // rung defaults
+        return run(variant, config, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    }
+    const int d = variant - kDiagBase;
+    if (d >= 0 && d < kNumDiagnostics)
+        return run(kDiagnostics[d].rung, kDiagnostics[d].config, M, N, K, A, lda, B, ldb, C, ldc,
+                   stream);
+    return GEMM_F32_ERR_INVALID_VARIANT;
+}
+
+extern "C" int gemm_f32_num_variants(void) { return kNumRungs; }
+
+extern "C" int gemm_f32_num_diagnostic_variants(void) { return kNumDiagnostics; }
+
+extern "C" const char* gemm_f32_variant_name(int variant) {
+    if (variant >= 0 && variant < kNumRungs) return kRungNames[variant];
+    const int d = variant - kDiagBase;
+    if (d >= 0 && d < kNumDiagnostics) return kDiagnostics[d].name;
+    return nullptr;
+}
+
+extern "C" const char* gemm_f32_status_string(int status) {
+    switch (status) {
+        case GEMM_F32_OK: return "ok";
+        case GEMM_F32_ERR_INVALID_DIM: return "invalid dimension: M, N and K must be >= 0";
+        case GEMM_F32_ERR_INVALID_LD:
+            return "invalid leading dimension: need lda >= max(1,K), ldb >= max(1,N), ldc >= max(1,N)";
+        case GEMM_F32_ERR_NULL_PTR: return "null pointer for a non-empty matrix";
+        case GEMM_F32_ERR_MISALIGNED: return "pointer not 4-byte aligned";
+        case GEMM_F32_ERR_INVALID_VARIANT: return "unknown kernel variant";
+        case GEMM_F32_ERR_TOO_LARGE: return "problem too large for the kernel index range or grid";
+        case GEMM_F32_ERR_LAUNCH: return "kernel launch rejected by the HIP runtime";
+        case GEMM_F32_ERR_DEVICE: return "no usable current HIP device";
+        default: return "unknown status";
+    }
+}

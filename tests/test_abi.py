@@ -1,0 +1,129 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry
+point, and rejects bad arguments synchronously with the documented codes."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_f32.h")
+
+
+def _header_text():
+    text = open(HEADER).read()
+    return re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+
+
+def declared_functions():
+    return sorted(set(re.findall(r"\b(gemm_f32\w*)\s*\(", _header_text())))
+
+
+def declared_codes():
+    return {m[0]: int(m[1]) for m in re.findall(r"#define\s+(GEMM_F32_\w+)\s+(-?\d+)", _header_text())}
+
+
+@pytest.fixture(scope="module")
+def binding():
+    from shared_memory_tiled_amd import binding as b
+    b.load_library()
+    return b
+
+
+@pytest.fixture(scope="module")
+def lib(binding):
+    return binding.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"gemm_f32", "gemm_f32_variant", "gemm_f32_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in gemm_f32.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "shared_memory_tiled_amd", "libgemm_f32.so")],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gemm_f32\w*)$", out, flags=re.M))
+    assert exported == set(names), exported ^ set(names)
+
+
+def test_library_is_independent_of_the_oracle():
+    so = os.path.join(ROOT, "shared_memory_tiled_amd", "libgemm_f32.so")
+    syms = subprocess.run(["nm", "-D", so], capture_output=True, text=True, check=True).stdout
+    assert "oracle" not in syms
+    needed = subprocess.run(["readelf", "-d", so], capture_output=True, text=True, check=True).stdout
+    assert "oracle" not in needed
+    pkg = os.path.join(ROOT, "shared_memory_tiled_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+                assert "gemm_oracle" not in text, f
+
+
+def test_status_codes_and_strings(binding):
+    codes = declared_codes()
+    statuses = {v for k, v in codes.items() if k.startswith(("GEMM_F32_OK", "GEMM_F32_ERR"))}
+    assert statuses == set(range(len(statuses)))
+    msgs = [binding.gemm_f32_status_string(s) for s in sorted(statuses)]
+    assert msgs[0] == "ok" and len(set(msgs)) == len(msgs)
+    assert binding.gemm_f32_status_string(999) == "unknown status"
+
+
+def test_variant_names(binding):
+    codes = declared_codes()
+    n = binding.gemm_f32_num_variants()
+    assert n == 4 and codes["GEMM_F32_VARIANT_MFMA"] == 3
+    names = [binding.gemm_f32_variant_name(v) for v in range(n)]
+    assert all(names) and len(set(names)) == n
+    nd = binding.gemm_f32_num_diagnostic_variants()
+    diag = [binding.gemm_f32_variant_name(16 + d) for d in range(nd)]
+    assert all(diag) and len(set(diag)) == nd
+    assert binding.gemm_f32_variant_name(n) is None
+    assert binding.gemm_f32_variant_name(16 + nd) is None
+    assert binding.gemm_f32_variant_name(-1) is None
+
+
+FAKE = 0x10000          # an aligned, never dereferenced address
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_DIM"),
+    ((4, -2, 4, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_DIM"),
+    ((4, 4, -3, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_DIM"),
+    ((4, 4, 8, FAKE, 7, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_LD"),
+    ((4, 6, 4, FAKE, 4, FAKE, 5, FAKE, 6), "GEMM_F32_ERR_INVALID_LD"),
+    ((4, 6, 4, FAKE, 4, FAKE, 6, FAKE, 5), "GEMM_F32_ERR_INVALID_LD"),
+    ((4, 4, 0, FAKE, 0, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_LD"),
+    ((4, 4, 4, None, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_NULL_PTR"),
+    ((4, 4, 4, FAKE, 4, None, 4, FAKE, 4), "GEMM_F32_ERR_NULL_PTR"),
+    ((4, 4, 4, FAKE, 4, FAKE, 4, None, 4), "GEMM_F32_ERR_NULL_PTR"),
+    ((4, 4, 0, None, 1, None, 4, None, 4), "GEMM_F32_ERR_NULL_PTR"),
+    ((4, 4, 4, FAKE + 2, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_MISALIGNED"),
+    ((4, 4, 4, FAKE, 4, FAKE + 1, 4, FAKE, 4), "GEMM_F32_ERR_MISALIGNED"),
+    ((4, 4, 4, FAKE, 4, FAKE, 4, FAKE + 3, 4), "GEMM_F32_ERR_MISALIGNED"),
+    ((2**31, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_TOO_LARGE"),
+    ((4, 4, 2**31, FAKE, 2**31, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_TOO_LARGE"),
+    ((4, 4, 4, FAKE, 2**62, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_TOO_LARGE"),
+    ((2**30, 2**30, 4, FAKE, 4, FAKE, 2**30, FAKE, 2**30), "GEMM_F32_ERR_TOO_LARGE"),
+    ((0, 4, 4, None, 4, None, 4, None, 4), "GEMM_F32_OK"),      # empty: no launch
+    ((4, 0, 4, None, 4, None, 1, None, 1), "GEMM_F32_OK"),
+])
+def test_validation_without_launch(lib, args, code):
+    want = declared_codes()[code]
+    M, N, K, A, lda, B, ldb, C, ldc = args
+    assert lib.gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, None) == want
+    for v in (0, 1, 2, 3, 16):
+        assert lib.gemm_f32_variant(v, M, N, K, A, lda, B, ldb, C, ldc, None) == want
+
+
+def test_unknown_variant(lib):
+    code = declared_codes()["GEMM_F32_ERR_INVALID_VARIANT"]
+    for v in (4, 15, -1, 16 + lib.gemm_f32_num_diagnostic_variants(), 1000):
+        assert lib.gemm_f32_variant(v, 4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, None) == code
+
+
+def test_python_errors_are_raised(binding):
+    with pytest.raises(binding.GemmError) as e:
+        binding.gemm_f32(-1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, stream=0)
+    assert e.value.status == declared_codes()["GEMM_F32_ERR_INVALID_DIM"]
