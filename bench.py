@@ -1,0 +1,198 @@
+"""Throughput of the fp32 GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one C = A x B call through the C ABI (gemm_f32, the default
+kernel) on seeded synthetic operands already resident in HBM.  W untimed
+steps, then exactly K timed steps between two device synchronisations.  One
+JSON line is printed with the metric (TFLOP/s = 2MNK per step / seconds),
+the roofline of the kernel (algorithmic FLOP per launch over the average
+launch time from HIP events on the launch stream, against the chip's
+published fp32 peak, plus the HBM bytes per launch from hardware counters
+when those were taken on the current kernel source), and a CPU baseline:
+the oracle timed on this host's cores on a bounded band of output rows.
+
+Extra modes (used for counter runs under rocprofv3):
+    --ladder            time every rung and diagnostic variant instead
+    --copy-probe-mib N  first run one device-to-device copy of N MiB, the
+                        reference for scaling HBM byte counters
+    --no-cpu-baseline   skip the oracle timing
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP32_TFLOPS = 157.3        # MI355X published dense fp32 (vector and matrix)
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "square8192"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mfma_square8192_hbm_traffic.txt")
+KERNEL_SOURCES = ["shared_memory_tiled_amd/csrc/mfma.hip",
+                  "shared_memory_tiled_amd/csrc/gemm_internal.h",
+                  "shared_memory_tiled_amd/csrc/api.hip"]
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None if it
+    is missing, for another workload, or taken on different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = [l for l in f if l.startswith("TRAFFIC_JSON ")]
+        rec = json.loads(lines[-1][len("TRAFFIC_JSON "):])
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(A, B, w, budget_s: float = 12.0):
+    """The oracle as it is, on all host cores, over a band of output rows."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    rows = min(cores, w.M)                  # one row per thread to size the sample
+    t0 = time.perf_counter()
+    oracle.gemm(A.view, B.view, threads=cores, rows=(0, rows))
+    probe = time.perf_counter() - t0
+    rows = max(rows, min(w.M, int(rows * budget_s / max(probe, 1e-3))))
+    rows -= rows % cores if rows > cores else 0
+    t0 = time.perf_counter()
+    oracle.gemm(A.view, B.view, threads=cores, rows=(0, rows))
+    dt = time.perf_counter() - t0
+    flop = 2.0 * rows * w.N * w.K
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} product "
+                      f"({rows * w.N} outputs, {flop:.3e} FLOP) in {dt:.2f} s, binary64 "
+                      f"triple loop, {cores} threads"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--variant", type=int, default=None, help="time gemm_f32_variant(v) instead")
+    ap.add_argument("--ladder", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    from shared_memory_tiled_amd import binding, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    w = inputs.WORKLOADS[args.workload]
+    A, B = inputs.operands(w)
+    dev = torch.device("cuda:0")
+    a = torch.from_numpy(A.buf).to(dev)
+    b = torch.from_numpy(B.buf).to(dev)
+    c = torch.empty(w.offset + w.M * w.ldc + 64, dtype=torch.float32, device=dev)
+    call_args = (w.M, w.N, w.K, a.data_ptr() + 4 * w.offset, w.lda,
+                 b.data_ptr() + 4 * w.offset, w.ldb, c.data_ptr() + 4 * w.offset, w.ldc)
+    flop = 2.0 * w.M * w.N * w.K
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n}), flush=True)
+        del src, dst
+
+    def one(v):
+        if v is None:
+            binding.gemm_f32(*call_args)
+        else:
+            binding.gemm_f32_variant(v, *call_args)
+
+    def timed(v, steps, warmup):
+        for _ in range(warmup):
+            one(v)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()      # the stream the library launches on
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            one(v)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, e0.elapsed_time(e1) / steps
+
+    if args.ladder:
+        variants = list(range(binding.gemm_f32_num_variants())) + \
+            [binding.DIAGNOSTIC_BASE + d for d in range(binding.gemm_f32_num_diagnostic_variants())]
+        for v in variants:
+            steps = max(1, min(args.steps, 3 if v == 0 else args.steps))
+            wall, ms = timed(v, steps, 1)
+            print(json.dumps({"variant": v, "name": binding.gemm_f32_variant_name(v),
+                              "workload": w.name, "ms_per_launch": round(ms, 4),
+                              "tflops": round(flop / ms / 1e9, 2),
+                              "frac_of_peak": round(flop / ms / 1e9 / PEAK_FP32_TFLOPS, 4)}), flush=True)
+        return 0
+
+    wall, ms_event = timed(args.variant, args.steps, args.warmup)
+    value = flop * args.steps / wall / 1e12
+    achieved = flop / (ms_event * 1e-3) / 1e12
+    kernel_name = binding.gemm_f32_variant_name(3 if args.variant is None else args.variant)
+    line = {
+        "metric": "fp32 GEMM TFLOP/s and % of MI355X fp32 peak at N=4096/8192",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb,
+                   "ldc": w.ldc, "view_offset_floats": w.offset, "values": w.dist,
+                   "entry_point": "gemm_f32" if args.variant is None else f"gemm_f32_variant({args.variant})",
+                   "kernel": kernel_name, "percent_of_peak": round(100 * value / PEAK_FP32_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+                     "traffic": recorded_traffic(w.name) if args.variant is None else None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(A, B, w)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
