@@ -77,8 +77,10 @@ extern "C" {
  *   2  register-blocked, double-buffered: 128 x 128 workgroup tile, 8 x 8
  *      outputs per thread in registers, two LDS buffers and one barrier per
  *      phase, next tile prefetched into registers during the current phase
- *   3  MFMA: v_mfma_f32_32x32x2_f32 matrix-core contraction on LDS-staged,
- *      padded, double-buffered tiles (the default)
+ *   3  MFMA: v_mfma_f32_32x32x2_f32 matrix-core contraction on double-
+ *      buffered LDS tiles; large problems use 256 x 256 tiles, eight waves
+ *      and direct global-to-LDS copies into an XOR-swizzled layout (the
+ *      default)
  * Variants numbered from 16 up are diagnostic layouts of the same rungs, kept
  * so that their hardware counters can be compared; see
  * gemm_f32_variant_name().

@@ -30,6 +30,12 @@ const Diagnostic kDiagnostics[] = {
     {"mfma256x128_bk16_w2x2", 3, 2},
     {"mfma128x128_bk32_w2x2", 3, 3},
     {"mfma64x64_bk16_w2x2", 3, 4},
+    {"mfma256x256_bk32_w2x4", 3, 5},
+    {"mfma128x256_bk16_w2x2", 3, 6},
+    {"mfma256x256_bk32_w2x4_direct", 3, 7},
+    {"mfma256x256_bk16_w2x4_direct", 3, 8},
+    {"mfma256x256_bk32_w4x2_direct", 3, 9},
+    {"mfma256x256_bk32_w2x4_direct_swz32", 3, 10},
 };
 constexpr int kNumDiagnostics = (int)(sizeof(kDiagnostics) / sizeof(kDiagnostics[0]));
 

@@ -1,0 +1,91 @@
+"""The LDS layouts of the tiled kernels against the brute-force bank model.
+
+These are design checks, not parity checks: each layout's word addresses (as
+the kernels compute them, restated here) are fed, one LDS cycle's worth of
+lanes at a time, to the oracle's bank-conflict model.  The bank geometry is
+the one the hardware counters establish for gfx950: 128-bit accesses are
+served 16 lanes per cycle from 64 four-byte banks, 32-bit accesses 32 lanes
+per cycle.  The outcomes match the measured SQ_LDS_BANK_CONFLICT counts
+recorded with the ladder profile.
+"""
+import pytest
+
+import oracle
+
+
+def degree(lane_words, width_words, banks, lanes_per_cycle):
+    """Worst conflict degree over the cycles of one wave-wide access; each
+    lane touches width_words consecutive words."""
+    worst = 0
+    for p0 in range(0, len(lane_words), lanes_per_cycle):
+        words = [w + e for w in lane_words[p0:p0 + lanes_per_cycle] for e in range(width_words)]
+        worst = max(worst, oracle.bank_conflict_degree(words, banks))
+    return worst
+
+
+def a_read_words(bk, row_stride, chunk_of):
+    """128-bit A-operand reads of the MFMA kernels: lane (i, h) reads row i,
+    logical chunk c + h, for each even c."""
+    cpr = bk // 4
+    return [[r * row_stride + 4 * chunk_of(r, c + h) for h in (0, 1) for r in range(32)]
+            for c in range(0, cpr, 2)]
+
+
+def swizzle(bk, banks):
+    cpr = bk // 4
+    rows_per_sweep = banks // bk
+    return lambda r, lc: lc ^ ((r // rows_per_sweep) % cpr)
+
+
+@pytest.mark.parametrize("bk", [16, 32])
+def test_swizzle_for_64_banks_is_conflict_free(bk):
+    for words in a_read_words(bk, bk, swizzle(bk, 64)):
+        assert degree(words, 4, 64, 16) == 1
+    # the 1 KB direct copy: lane l writes physical chunk l % cpr of row l // cpr
+    cpr = bk // 4
+    assert degree([(l // cpr) * bk + 4 * (l % cpr) for l in range(64)], 4, 64, 16) == 1
+
+
+@pytest.mark.parametrize("bk", [16, 32])
+def test_swizzle_for_32_banks_conflicts_on_gfx950(bk):
+    worst = max(degree(w, 4, 64, 16) for w in a_read_words(bk, bk, swizzle(bk, 32)))
+    assert worst == 2          # the measured 1.34e8 conflict cycles of the *_swz32 variant
+
+
+@pytest.mark.parametrize("bk", [16, 32])
+def test_padded_a_rows_read_conflict_free(bk):
+    for words in a_read_words(bk, bk + 4, lambda r, lc: lc):
+        assert degree(words, 4, 64, 16) == 1
+
+
+def test_unpadded_rows_would_conflict():
+    worst = max(degree(w, 4, 64, 16) for w in a_read_words(32, 32, lambda r, lc: lc))
+    assert worst >= 2
+
+
+def test_regblock_transposed_store_needs_the_pad():
+    """Rung 2 stores a 128 x 8 A chunk transposed: lane t writes word
+    (c + e) * SA + r with r = t // 2, c = 4 (t % 2)."""
+    def words(sa, e):
+        return [((4 * (t % 2)) + e) * sa + t // 2 for t in range(64)]
+    assert max(degree(words(128, e), 1, 64, 32) for e in range(4)) == 2      # measured: conflicts
+    assert max(degree(words(132, e), 1, 64, 32) for e in range(4)) == 1      # measured: none
+
+
+def test_b_operand_reads_conflict_free():
+    """MFMA B operand: lanes 0-31 read 32 consecutive words of row k, lanes
+    32-63 of row k + 4, rows 264 words apart."""
+    for k in range(4):
+        words = [(k + 4 * (l // 32)) * 264 + (l % 32) for l in range(64)]
+        assert degree(words, 1, 64, 32) == 1
+
+
+@pytest.mark.parametrize("bk,expected", [(16, 2), (32, 1)])
+def test_register_path_a_stores(bk, expected):
+    """The register-staged MFMA kernels store 128-bit A chunks (lane q: row
+    q // (bk/4), chunk q % (bk/4)) into rows padded to bk + 4 words.  Their
+    measured counts (conflicts at bk = 16, none at bk = 32) fit 128-bit stores
+    served 8 lanes per cycle over 32 banks."""
+    cpr = bk // 4
+    words = [(q // cpr) * (bk + 4) + 4 * (q % cpr) for q in range(64)]
+    assert degree(words, 4, 32, 8) == expected
