@@ -31,10 +31,14 @@ _lib = None
 
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
-    """Compile the oracle into a shared library (gcc, strict IEEE arithmetic)."""
+    """Compile the oracle into a shared library (gcc, strict IEEE arithmetic).
+    The library is written under a temporary name and renamed into place, so
+    concurrent builders never expose a partly written file."""
+    tmp = f"{out}.tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
-           "-shared", "-fPIC", "-pthread", "-o", out, src, "-lm"]
+           "-shared", "-fPIC", "-pthread", "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
     return out
 
 
@@ -47,6 +51,12 @@ def load(path: str | None = None):
     if not os.path.exists(p):
         build(out=p)
     lib = ctypes.CDLL(p)
+    lib.oracle_gemm_op_rows.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _fp, _i64,
+                                        _fp, _i64, _dp, _i64, _dp, _i64, _i64, _i64, ctypes.c_int]
+    lib.oracle_gemm_op_rows.restype = ctypes.c_int
+    lib.oracle_gemm_op_entries.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _fp, _i64,
+                                           _fp, _i64, _i64, _ip, _ip, _dp, _dp]
+    lib.oracle_gemm_op_entries.restype = ctypes.c_int
     lib.oracle_gemm_rows.argtypes = [_i64, _i64, _i64, _fp, _i64, _fp, _i64,
                                      _dp, _i64, _dp, _i64, _i64, _i64, ctypes.c_int]
     lib.oracle_gemm_rows.restype = ctypes.c_int
@@ -82,37 +92,57 @@ def _matrix_arg(X: np.ndarray):
     return ptr, ld
 
 
-def gemm(A: np.ndarray, B: np.ndarray, threads: int = 1, rows=None, lib=None):
-    """Returns (C, S): binary64 product A x B and sum_k |A_ik B_kj|.
+def _op(op) -> int:
+    if op in (0, "N", "n"):
+        return 0
+    if op in (1, "T", "t"):
+        return 1
+    raise ValueError(f"op must be 'N' or 'T', not {op!r}")
 
-    ``rows=(r0, r1)`` computes only that band of rows (the other rows of the
-    returned arrays stay zero)."""
-    lib = lib or load()
-    M, K = A.shape
-    K2, N = B.shape
+
+def _shapes(A, B, op_a, op_b):
+    M, K = A.shape if op_a == 0 else A.shape[::-1]
+    K2, N = B.shape if op_b == 0 else B.shape[::-1]
     if K != K2:
         raise ValueError("inner dimensions differ")
+    return M, N, K
+
+
+def gemm(A: np.ndarray, B: np.ndarray, threads: int = 1, rows=None, lib=None,
+         op_a="N", op_b="N"):
+    """Returns (C, S): binary64 product op(A) x op(B) and sum_k |op(A)_ik op(B)_kj|.
+
+    A and B are the STORED matrices: with op_a = 'T', A is K x M and op(A)
+    is its transpose; with op_b = 'T', B is N x K.  ``rows=(r0, r1)``
+    computes only that band of rows (the other rows stay zero)."""
+    lib = lib or load()
+    oa, ob = _op(op_a), _op(op_b)
+    M, N, K = _shapes(A, B, oa, ob)
     C = np.zeros((M, N), dtype=np.float64)
     S = np.zeros((M, N), dtype=np.float64)
     pa, lda = _matrix_arg(A)
     pb, ldb = _matrix_arg(B)
     r0, r1 = (0, M) if rows is None else rows
-    rc = lib.oracle_gemm_rows(M, N, K, pa, lda, pb, ldb,
-                              C.ctypes.data_as(_dp), max(N, 1),
-                              S.ctypes.data_as(_dp), max(N, 1),
-                              r0, r1, int(threads))
+    if oa == 0 and ob == 0:           # the plain entry point, as pinned
+        rc = lib.oracle_gemm_rows(M, N, K, pa, lda, pb, ldb,
+                                  C.ctypes.data_as(_dp), max(N, 1),
+                                  S.ctypes.data_as(_dp), max(N, 1),
+                                  r0, r1, int(threads))
+    else:
+        rc = lib.oracle_gemm_op_rows(oa, ob, M, N, K, pa, lda, pb, ldb,
+                                     C.ctypes.data_as(_dp), max(N, 1),
+                                     S.ctypes.data_as(_dp), max(N, 1),
+                                     r0, r1, int(threads))
     if rc != 0:
-        raise ValueError(f"oracle_gemm_rows rejected its arguments (rc={rc})")
+        raise ValueError(f"oracle product rejected its arguments (rc={rc})")
     return C, S
 
 
-def gemm_entries(A: np.ndarray, B: np.ndarray, ii, jj, lib=None):
-    """Returns (c, s) for the entries (ii[t], jj[t]) of A x B only."""
+def gemm_entries(A: np.ndarray, B: np.ndarray, ii, jj, lib=None, op_a="N", op_b="N"):
+    """Returns (c, s) for the entries (ii[t], jj[t]) of op(A) x op(B) only."""
     lib = lib or load()
-    M, K = A.shape
-    K2, N = B.shape
-    if K != K2:
-        raise ValueError("inner dimensions differ")
+    oa, ob = _op(op_a), _op(op_b)
+    M, N, K = _shapes(A, B, oa, ob)
     ii = np.ascontiguousarray(ii, dtype=np.int64)
     jj = np.ascontiguousarray(jj, dtype=np.int64)
     if ii.shape != jj.shape or ii.ndim != 1:
@@ -121,11 +151,12 @@ def gemm_entries(A: np.ndarray, B: np.ndarray, ii, jj, lib=None):
     s = np.zeros(ii.shape[0], dtype=np.float64)
     pa, lda = _matrix_arg(A)
     pb, ldb = _matrix_arg(B)
-    rc = lib.oracle_gemm_entries(M, N, K, pa, lda, pb, ldb, ii.shape[0],
-                                 ii.ctypes.data_as(_ip), jj.ctypes.data_as(_ip),
-                                 c.ctypes.data_as(_dp), s.ctypes.data_as(_dp))
+    args = (M, N, K, pa, lda, pb, ldb, ii.shape[0], ii.ctypes.data_as(_ip), jj.ctypes.data_as(_ip),
+            c.ctypes.data_as(_dp), s.ctypes.data_as(_dp))
+    rc = lib.oracle_gemm_entries(*args) if oa == 0 and ob == 0 else \
+        lib.oracle_gemm_op_entries(oa, ob, *args)
     if rc != 0:
-        raise ValueError(f"oracle_gemm_entries rejected its arguments (rc={rc})")
+        raise ValueError(f"oracle entries rejected their arguments (rc={rc})")
     return c, s
 
 

@@ -19,6 +19,9 @@
  *   - same first page, section "Bank Conflict": 32 banks of 4-byte words,
  *     n distinct words in one bank serialise into an n-way conflict, equal
  *     words are a broadcast.
+ *   - the one-volume PMPP notes, deep-learning chapter: the backward pass
+ *     needs the products with a transposed factor, X^T dY and dY W^T, and
+ *     runs them on the same tile kernel; op(A), op(B) below.
  *
  * Readings where the pages are silent (all listed in the design notes):
  *   - general shapes M x K times K x N with row-major leading dimensions
@@ -31,8 +34,9 @@
  *
  * Parity pins (in the CPU tests): exact integer brute force, identity and
  * zero, closed forms, a binary64 library product, linearity, power-of-two
- * scaling, the transpose identity, leading-dimension invariance, and the
- * pages' printed intensity and bank-conflict numbers.  The per-entry and the
+ * scaling, the transpose identity, leading-dimension invariance, transposed
+ * operands against explicitly transposed copies, and the pages' printed
+ * intensity and bank-conflict numbers.  The per-entry and the
  * traffic/bank functions are pinned the same way; no function here is left
  * "parity unpinned".
  *
@@ -51,20 +55,32 @@
 /* One output element: the definition of the product, term by term.         */
 /* ------------------------------------------------------------------------ */
 
-/* c = sum_{k=0}^{K-1} A[i][k] * B[k][j]   and   s = sum_k |A[i][k] * B[k][j]|.
- * Row i of A starts at A + i*lda; row k of B starts at B + k*ldb. */
-static void dot_entry(int64_t K, const float *A, int64_t lda, const float *B,
-                      int64_t ldb, int64_t i, int64_t j, double *c, double *s)
+/* c = sum_{k=0}^{K-1} A[i][k] * B[k][j]   and   s = sum_k |A[i][k] * B[k][j]|,
+ * where element (i, k) of the left factor is A[i*a_rs + k*a_cs] and element
+ * (k, j) of the right factor is B[k*b_rs + j*b_cs].  A row-major matrix with
+ * leading dimension ld has (row stride, column stride) = (ld, 1); its
+ * transpose, read in place, has (1, ld). */
+static void dot_entry(int64_t K, const float *A, int64_t a_rs, int64_t a_cs,
+                      const float *B, int64_t b_rs, int64_t b_cs,
+                      int64_t i, int64_t j, double *c, double *s)
 {
     double acc = 0.0;
     double mag = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-        double prod = (double)A[i * lda + k] * (double)B[k * ldb + j];
+        double prod = (double)A[i * a_rs + k * a_cs] * (double)B[k * b_rs + j * b_cs];
         acc += prod;
         mag += fabs(prod);
     }
     *c = acc;
     *s = mag;
+}
+
+/* Strides of op(X) for a stored row-major X with leading dimension ld:
+ * op 0 uses X as stored, op 1 uses its transpose. */
+static void op_strides(int op, int64_t ld, int64_t *rs, int64_t *cs)
+{
+    if (op == 0) { *rs = ld; *cs = 1; }
+    else         { *rs = 1;  *cs = ld; }
 }
 
 /* ------------------------------------------------------------------------ */
@@ -75,8 +91,8 @@ static void dot_entry(int64_t K, const float *A, int64_t lda, const float *B,
 
 struct rows_job {
     int64_t row_begin, row_end, N, K;
-    const float *A; int64_t lda;
-    const float *B; int64_t ldb;
+    const float *A; int64_t a_rs, a_cs;
+    const float *B; int64_t b_rs, b_cs;
     double *C; int64_t ldc;
     double *S; int64_t lds;
 };
@@ -87,7 +103,8 @@ static void *rows_worker(void *arg)
     for (int64_t i = job->row_begin; i < job->row_end; ++i) {
         for (int64_t j = 0; j < job->N; ++j) {
             double c, s;
-            dot_entry(job->K, job->A, job->lda, job->B, job->ldb, i, j, &c, &s);
+            dot_entry(job->K, job->A, job->a_rs, job->a_cs, job->B, job->b_rs, job->b_cs,
+                      i, j, &c, &s);
             job->C[i * job->ldc + j] = c;
             if (job->S)
                 job->S[i * job->lds + j] = s;
@@ -96,23 +113,32 @@ static void *rows_worker(void *arg)
     return NULL;
 }
 
-/* C (binary64, leading dimension ldc) = A x B; S (optional, may be NULL,
- * leading dimension lds) = sum of |products|.  Rows [row_begin, row_end) of
- * the product only, so a caller can time or check a band of rows.
- * threads <= 1 runs on the calling thread. */
-int oracle_gemm_rows(int64_t M, int64_t N, int64_t K,
-                     const float *A, int64_t lda, const float *B, int64_t ldb,
-                     double *C, int64_t ldc, double *S, int64_t lds,
-                     int64_t row_begin, int64_t row_end, int threads)
+/* C (binary64, leading dimension ldc) = op(A) x op(B); S (optional, may be
+ * NULL, leading dimension lds) = sum of |products|.  op_a = 0: A is stored
+ * M x K (lda >= K); op_a = 1: A is stored K x M (lda >= M) and op(A) is its
+ * transpose.  op_b = 0: B is stored K x N (ldb >= N); op_b = 1: B is stored
+ * N x K (ldb >= K).  Rows [row_begin, row_end) of the product only, so a
+ * caller can time or check a band of rows.  threads <= 1 runs on the
+ * calling thread. */
+int oracle_gemm_op_rows(int op_a, int op_b, int64_t M, int64_t N, int64_t K,
+                        const float *A, int64_t lda, const float *B, int64_t ldb,
+                        double *C, int64_t ldc, double *S, int64_t lds,
+                        int64_t row_begin, int64_t row_end, int threads)
 {
+    if ((op_a != 0 && op_a != 1) || (op_b != 0 && op_b != 1))
+        return ORACLE_BAD_ARG;
     if (M < 0 || N < 0 || K < 0 || row_begin < 0 || row_end > M || row_begin > row_end)
         return ORACLE_BAD_ARG;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    int64_t a_cols = op_a == 0 ? K : M, b_cols = op_b == 0 ? N : K;
+    if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) || ldc < (N > 1 ? N : 1))
         return ORACLE_BAD_ARG;
     if (S && lds < (N > 1 ? N : 1))
         return ORACLE_BAD_ARG;
     if ((row_end > row_begin && N > 0) && (!C || (K > 0 && (!A || !B))))
         return ORACLE_BAD_ARG;
+    int64_t a_rs, a_cs, b_rs, b_cs;
+    op_strides(op_a, lda, &a_rs, &a_cs);
+    op_strides(op_b, ldb, &b_rs, &b_cs);
 
     int64_t rows = row_end - row_begin;
     if (threads < 1)
@@ -130,7 +156,7 @@ int oracle_gemm_rows(int64_t M, int64_t N, int64_t K,
     int64_t per = rows / threads, extra = rows % threads, r = row_begin;
     for (int t = 0; t < threads; ++t) {
         int64_t take = per + (t < extra ? 1 : 0);
-        jobs[t] = (struct rows_job){r, r + take, N, K, A, lda, B, ldb, C, ldc, S, lds};
+        jobs[t] = (struct rows_job){r, r + take, N, K, A, a_rs, a_cs, B, b_rs, b_cs, C, ldc, S, lds};
         r += take;
     }
     int started = 0;
@@ -149,6 +175,16 @@ int oracle_gemm_rows(int64_t M, int64_t N, int64_t K,
     return ORACLE_OK;
 }
 
+/* The plain product C = A x B (both as stored), rows [row_begin, row_end). */
+int oracle_gemm_rows(int64_t M, int64_t N, int64_t K,
+                     const float *A, int64_t lda, const float *B, int64_t ldb,
+                     double *C, int64_t ldc, double *S, int64_t lds,
+                     int64_t row_begin, int64_t row_end, int threads)
+{
+    return oracle_gemm_op_rows(0, 0, M, N, K, A, lda, B, ldb, C, ldc, S, lds,
+                               row_begin, row_end, threads);
+}
+
 int oracle_gemm(int64_t M, int64_t N, int64_t K,
                 const float *A, int64_t lda, const float *B, int64_t ldb,
                 double *C, int64_t ldc, double *S, int64_t lds, int threads)
@@ -156,27 +192,42 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K,
     return oracle_gemm_rows(M, N, K, A, lda, B, ldb, C, ldc, S, lds, 0, M, threads);
 }
 
-/* Selected entries only: out_c[t], out_s[t] for the pair (ii[t], jj[t]).
- * Used where the full product is too large to compute on the host. */
-int oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
-                        const float *A, int64_t lda, const float *B, int64_t ldb,
-                        int64_t count, const int64_t *ii, const int64_t *jj,
-                        double *out_c, double *out_s)
+/* Selected entries only: out_c[t], out_s[t] for the pair (ii[t], jj[t]) of
+ * op(A) x op(B) (op flags as in oracle_gemm_op_rows).  Used where the full
+ * product is too large to compute on the host. */
+int oracle_gemm_op_entries(int op_a, int op_b, int64_t M, int64_t N, int64_t K,
+                           const float *A, int64_t lda, const float *B, int64_t ldb,
+                           int64_t count, const int64_t *ii, const int64_t *jj,
+                           double *out_c, double *out_s)
 {
+    if ((op_a != 0 && op_a != 1) || (op_b != 0 && op_b != 1))
+        return ORACLE_BAD_ARG;
     if (M < 0 || N < 0 || K < 0 || count < 0)
         return ORACLE_BAD_ARG;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1))
+    int64_t a_cols = op_a == 0 ? K : M, b_cols = op_b == 0 ? N : K;
+    if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1))
         return ORACLE_BAD_ARG;
+    int64_t a_rs, a_cs, b_rs, b_cs;
+    op_strides(op_a, lda, &a_rs, &a_cs);
+    op_strides(op_b, ldb, &b_rs, &b_cs);
     for (int64_t t = 0; t < count; ++t) {
         if (ii[t] < 0 || ii[t] >= M || jj[t] < 0 || jj[t] >= N)
             return ORACLE_BAD_ARG;
         double c, s;
-        dot_entry(K, A, lda, B, ldb, ii[t], jj[t], &c, &s);
+        dot_entry(K, A, a_rs, a_cs, B, b_rs, b_cs, ii[t], jj[t], &c, &s);
         out_c[t] = c;
         if (out_s)
             out_s[t] = s;
     }
     return ORACLE_OK;
+}
+
+int oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
+                        const float *A, int64_t lda, const float *B, int64_t ldb,
+                        int64_t count, const int64_t *ii, const int64_t *jj,
+                        double *out_c, double *out_s)
+{
+    return oracle_gemm_op_entries(0, 0, M, N, K, A, lda, B, ldb, count, ii, jj, out_c, out_s);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -202,6 +202,54 @@ def check_entries_rows_threads(lib):
     assert np.array_equal(c, C1[ii, jj]) and np.array_equal(s, S1[ii, jj])
 
 
+def _padded_copy(X, extra, off):
+    rows, cols = X.shape
+    ld = cols + extra
+    buf = np.full(off + rows * ld + 8, np.nan, np.float32)
+    V = buf[off:off + rows * ld].reshape(rows, ld)[:, :cols]
+    V[:] = X
+    return V
+
+
+def check_transposed_operands(lib):
+    """op(A) x op(B) with A and/or B stored transposed (also in NaN-padded,
+    offset storage) equals the plain product of the untransposed matrices bit
+    for bit: the same products are summed in the same k order."""
+    gen = np.random.default_rng(109)
+    for (M, N, K) in ((23, 41, 57), (64, 9, 130), (1, 33, 7)):
+        X = gen.standard_normal((M, K), dtype=np.float32)
+        Y = (2 * gen.random((K, N), dtype=np.float32) - 1).astype(np.float32)
+        C0, S0 = oracle.gemm(X, Y, lib=lib)
+        Xt, Yt = np.ascontiguousarray(X.T), np.ascontiguousarray(Y.T)
+        for (A, B, oa, ob) in ((Xt, Y, "T", "N"), (X, Yt, "N", "T"), (Xt, Yt, "T", "T"),
+                               (_padded_copy(Xt, 3, 1), _padded_copy(Yt, 5, 2), "T", "T"),
+                               (_padded_copy(Xt, 1, 0), Y, "T", "N")):
+            C, S = oracle.gemm(A, B, op_a=oa, op_b=ob, threads=3, lib=lib)
+            assert np.array_equal(C, C0) and np.array_equal(S, S0), (M, N, K, oa, ob)
+            ii = gen.integers(0, M, 50)
+            jj = gen.integers(0, N, 50)
+            c, s2 = oracle.gemm_entries(A, B, ii, jj, op_a=oa, op_b=ob, lib=lib)
+            assert np.array_equal(c, C0[ii, jj]) and np.array_equal(s2, S0[ii, jj])
+
+
+def check_transposed_bruteforce(lib):
+    """Integer inputs, tiny shapes, every op combination: exact equality with
+    Python-int brute force on the transposes built element by element."""
+    gen = np.random.default_rng(110)
+    for (M, N, K) in ((2, 3, 4), (5, 1, 3), (3, 7, 2), (6, 4, 9)):
+        for oa in ("N", "T"):
+            for ob in ("N", "T"):
+                A = _ints(gen, M, K, -7, 7) if oa == "N" else _ints(gen, K, M, -7, 7)
+                B = _ints(gen, K, N, -7, 7) if ob == "N" else _ints(gen, N, K, -7, 7)
+                opA = [[int(A[i][k]) if oa == "N" else int(A[k][i]) for k in range(K)] for i in range(M)]
+                opB = [[int(B[k][j]) if ob == "N" else int(B[j][k]) for j in range(N)] for k in range(K)]
+                Ce, Se = _py_product(np.array(opA, dtype=np.float32).reshape(M, K),
+                                     np.array(opB, dtype=np.float32).reshape(K, N))
+                C, S = oracle.gemm(A, B, op_a=oa, op_b=ob, lib=lib)
+                assert np.array_equal(C, np.array(Ce, dtype=np.float64).reshape(M, N)), (oa, ob, M, N, K)
+                assert np.array_equal(S, np.array(Se, dtype=np.float64).reshape(M, N)), (oa, ob, M, N, K)
+
+
 # ------------------------------------------------------ traffic bookkeeping --
 
 def check_naive_intensity(lib):
@@ -302,6 +350,7 @@ ALL_CHECKS = [
     check_bruteforce_tiny, check_bruteforce_tile_straddling, check_identity_and_zero,
     check_closed_forms, check_library_float64, check_linearity_and_scaling,
     check_transpose_identity, check_padded_views, check_entries_rows_threads,
+    check_transposed_operands, check_transposed_bruteforce,
     check_naive_intensity, check_tiled_intensity_and_traffic, check_tiled_traffic_ragged,
     check_naive_roofline_context, check_bank_model,
 ]

@@ -34,6 +34,7 @@ EDGE_SHAPES = [
     (15, 17, 33), (31, 33, 63), (63, 65, 127), (65, 63, 3), (127, 129, 255),
     (129, 127, 257), (255, 257, 129), (257, 255, 1009), (33, 1009, 7),
     (257, 511, 65), (511, 257, 33), (300, 200, 2),
+    (4097, 31, 40), (17, 4099, 33), (520, 530, 64),
 ]
 
 

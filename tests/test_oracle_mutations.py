@@ -17,8 +17,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "gemm_oracle.c")
 
 MUTANTS = {
-    "transposed_B_index": ("(double)B[k * ldb + j]", "(double)B[j * ldb + k]"),
-    "A_uses_ldb": ("(double)A[i * lda + k]", "(double)A[i * ldb + k]"),
+    "transposed_B_index": ("(double)B[k * b_rs + j * b_cs]", "(double)B[j * b_rs + k * b_cs]"),
+    "A_uses_B_stride": ("(double)A[i * a_rs + k * a_cs]", "(double)A[i * b_rs + k * a_cs]"),
+    "transpose_op_ignored": ("else         { *rs = 1;  *cs = ld; }", "else         { *rs = ld; *cs = 1; }"),
+    "op_flags_swapped": ("op_strides(op_a, lda, &a_rs, &a_cs);\n    op_strides(op_b, ldb, &b_rs, &b_cs);\n\n    int64_t rows",
+                         "op_strides(op_b, lda, &a_rs, &a_cs);\n    op_strides(op_a, ldb, &b_rs, &b_cs);\n\n    int64_t rows"),
+    "entries_op_ignored": ("op_strides(op_a, lda, &a_rs, &a_cs);\n    op_strides(op_b, ldb, &b_rs, &b_cs);\n    for",
+                           "op_strides(0, lda, &a_rs, &a_cs);\n    op_strides(0, ldb, &b_rs, &b_cs);\n    for"),
     "dropped_first_term": ("for (int64_t k = 0; k < K; ++k) {\n        double prod",
                            "for (int64_t k = 1; k < K; ++k) {\n        double prod"),
     "dropped_last_term": ("for (int64_t k = 0; k < K; ++k) {\n        double prod",
