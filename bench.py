@@ -17,6 +17,9 @@ Extra modes (used for counter runs under rocprofv3):
     --copy-probe-mib N  first run one device-to-device copy of N MiB, the
                         reference for scaling HBM byte counters
     --no-cpu-baseline   skip the oracle timing
+    --op XY             time gemm_f32_op with op(A) = X, op(B) = Y (N or T):
+                        the transposed factor is stored transposed, with a
+                        compact leading dimension
 """
 from __future__ import annotations
 
@@ -62,18 +65,18 @@ def recorded_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(A, B, w, budget_s: float = 12.0):
+def cpu_baseline(A, B, w, op_a="N", op_b="N", budget_s: float = 12.0):
     """The oracle as it is, on all host cores, over a band of output rows."""
     import oracle
     cores = len(os.sched_getaffinity(0))
     rows = min(cores, w.M)                  # one row per thread to size the sample
     t0 = time.perf_counter()
-    oracle.gemm(A.view, B.view, threads=cores, rows=(0, rows))
+    oracle.gemm(A.view, B.view, threads=cores, rows=(0, rows), op_a=op_a, op_b=op_b)
     probe = time.perf_counter() - t0
     rows = max(rows, min(w.M, int(rows * budget_s / max(probe, 1e-3))))
     rows -= rows % cores if rows > cores else 0
     t0 = time.perf_counter()
-    oracle.gemm(A.view, B.view, threads=cores, rows=(0, rows))
+    oracle.gemm(A.view, B.view, threads=cores, rows=(0, rows), op_a=op_a, op_b=op_b)
     dt = time.perf_counter() - t0
     flop = 2.0 * rows * w.N * w.K
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
@@ -92,6 +95,7 @@ def main(argv=None) -> int:
     ap.add_argument("--ladder", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="NN", choices=["NN", "TN", "NT", "TT"])
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -110,13 +114,23 @@ def main(argv=None) -> int:
         return 2
     torch.cuda.set_device(0)
     w = inputs.WORKLOADS[args.workload]
-    A, B = inputs.operands(w)
+    op_a, op_b = args.op[0], args.op[1]
+    if args.op == "NN":
+        A, B = inputs.operands(w)
+        lda, ldb = w.lda, w.ldb
+    else:       # the transposed factor is stored transposed (compact rows)
+        ga, gb = inputs.rng(w.index, 0), inputs.rng(w.index, 1)
+        A = inputs.padded(inputs.random_matrix(ga, w.K, w.M, w.dist), w.M, w.offset) if op_a == "T" \
+            else inputs.padded(inputs.random_matrix(ga, w.M, w.K, w.dist), w.lda, w.offset)
+        B = inputs.padded(inputs.random_matrix(gb, w.N, w.K, w.dist), w.K, w.offset) if op_b == "T" \
+            else inputs.padded(inputs.random_matrix(gb, w.K, w.N, w.dist), w.ldb, w.offset)
+        lda, ldb = A.ld, B.ld
     dev = torch.device("cuda:0")
     a = torch.from_numpy(A.buf).to(dev)
     b = torch.from_numpy(B.buf).to(dev)
     c = torch.empty(w.offset + w.M * w.ldc + 64, dtype=torch.float32, device=dev)
-    call_args = (w.M, w.N, w.K, a.data_ptr() + 4 * w.offset, w.lda,
-                 b.data_ptr() + 4 * w.offset, w.ldb, c.data_ptr() + 4 * w.offset, w.ldc)
+    call_args = (w.M, w.N, w.K, a.data_ptr() + 4 * w.offset, lda,
+                 b.data_ptr() + 4 * w.offset, ldb, c.data_ptr() + 4 * w.offset, w.ldc)
     flop = 2.0 * w.M * w.N * w.K
 
     if args.copy_probe_mib:
@@ -130,7 +144,9 @@ def main(argv=None) -> int:
         del src, dst
 
     def one(v):
-        if v is None:
+        if args.op != "NN":
+            binding.gemm_f32_op(op_a, op_b, *call_args)
+        elif v is None:
             binding.gemm_f32(*call_args)
         else:
             binding.gemm_f32_variant(v, *call_args)
@@ -180,16 +196,17 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb,
-                   "ldc": w.ldc, "view_offset_floats": w.offset, "values": w.dist,
-                   "entry_point": "gemm_f32" if args.variant is None else f"gemm_f32_variant({args.variant})",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "lda": lda, "ldb": ldb,
+                   "ldc": w.ldc, "view_offset_floats": w.offset, "values": w.dist, "op": args.op,
+                   "entry_point": (f"gemm_f32_op({op_a},{op_b})" if args.op != "NN" else
+                                   "gemm_f32" if args.variant is None else f"gemm_f32_variant({args.variant})"),
                    "kernel": kernel_name, "percent_of_peak": round(100 * value / PEAK_FP32_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
-                     "traffic": recorded_traffic(w.name) if args.variant is None else None},
+                     "traffic": recorded_traffic(w.name) if args.variant is None and args.op == "NN" else None},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(A, B, w)
+        line["cpu_baseline"] = cpu_baseline(A, B, w, op_a, op_b)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -65,6 +65,7 @@ extern "C" {
 #define GEMM_F32_ERR_TOO_LARGE       6  /* M, N or K >= 2^31, or the grid would not fit */
 #define GEMM_F32_ERR_LAUNCH          7  /* the HIP runtime rejected the launch       */
 #define GEMM_F32_ERR_DEVICE          8  /* no usable current HIP device              */
+#define GEMM_F32_ERR_INVALID_OP      9  /* op_a or op_b is neither N nor T           */
 
 /* Kernel ladder.  Each rung computes the same product; each is tested against
  * the oracle and against the rung below it.
@@ -105,6 +106,35 @@ int gemm_f32_variant(int variant,
                      const float *B, int64_t ldb,
                      float *C, int64_t ldc,
                      void *stream);
+
+/* Products with a transposed factor: C = op(A) x op(B), C still M x N.
+ *
+ * The one-volume PMPP notes (deep-learning chapter, backward pass) need the
+ * weight gradient X^T dY and the input gradient dY W^T besides the forward
+ * product, and run all three on the same tile kernel; so does this entry
+ * point (the MFMA rung, with each factor's LDS tile kept in the orientation
+ * in which it is stored).
+ *   op_a == GEMM_F32_OP_N: A is stored M x K, element (i,k) at A[i*lda + k],
+ *                          lda >= max(1, K)
+ *   op_a == GEMM_F32_OP_T: A is stored K x M, element (i,k) of op(A) at
+ *                          A[k*lda + i], lda >= max(1, M)
+ *   op_b == GEMM_F32_OP_N: B is stored K x N, element (k,j) at B[k*ldb + j],
+ *                          ldb >= max(1, N)
+ *   op_b == GEMM_F32_OP_T: B is stored N x K, element (k,j) of op(B) at
+ *                          B[j*ldb + k], ldb >= max(1, K)
+ * C, ownership, streams, errors and accuracy are as for gemm_f32; an op
+ * other than N or T returns GEMM_F32_ERR_INVALID_OP.  For a given M, N, K
+ * the k-summation order does not depend on the ops, so op(A) = A^T gives
+ * the same bits as gemm_f32 on an explicitly transposed copy.
+ */
+#define GEMM_F32_OP_N 0
+#define GEMM_F32_OP_T 1
+int gemm_f32_op(int op_a, int op_b,
+                int64_t M, int64_t N, int64_t K,
+                const float *A, int64_t lda,
+                const float *B, int64_t ldb,
+                float *C, int64_t ldc,
+                void *stream);
 
 /* Number of ladder rungs (variants 0 .. n-1). */
 int gemm_f32_num_variants(void);

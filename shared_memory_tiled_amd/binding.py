@@ -27,6 +27,7 @@ _lock = threading.Lock()
 
 OK = 0
 VARIANTS = {"naive": 0, "tiled": 1, "regblock": 2, "mfma": 3}
+OPS = {"N": 0, "T": 1, 0: 0, 1: 1}
 DIAGNOSTIC_BASE = 16
 
 
@@ -55,6 +56,8 @@ def load_library():
         lib.gemm_f32.restype = ctypes.c_int
         lib.gemm_f32_variant.argtypes = [ctypes.c_int] + sig
         lib.gemm_f32_variant.restype = ctypes.c_int
+        lib.gemm_f32_op.argtypes = [ctypes.c_int, ctypes.c_int] + sig
+        lib.gemm_f32_op.restype = ctypes.c_int
         lib.gemm_f32_num_variants.argtypes = []
         lib.gemm_f32_num_variants.restype = ctypes.c_int
         lib.gemm_f32_num_diagnostic_variants.argtypes = []
@@ -105,6 +108,15 @@ def gemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> N
                                 _addr(C), ldc, _stream(stream)))
 
 
+def gemm_f32_op(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
+    """C = op(A) x op(B), op 'N' (as stored) or 'T' (stored transposed)."""
+    lib = load_library()
+    oa = OPS.get(op_a, op_a) if not isinstance(op_a, int) else op_a
+    ob = OPS.get(op_b, op_b) if not isinstance(op_b, int) else op_b
+    _check(lib.gemm_f32_op(int(oa), int(ob), M, N, K, _addr(A), lda, _addr(B), ldb,
+                           _addr(C), ldc, _stream(stream)))
+
+
 def gemm_f32_num_variants() -> int:
     return load_library().gemm_f32_num_variants()
 
@@ -131,12 +143,14 @@ def _ld(t: torch.Tensor) -> int:
 
 
 def gemm(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
-         variant=None, stream=None) -> torch.Tensor:
-    """Tensor form: returns ``out`` (allocated if None) = A @ B.  Row-major
-    views with a leading dimension (``stride(0)``) and a storage offset are
-    passed through as they are."""
-    M, K = A.shape
-    K2, N = B.shape
+         variant=None, stream=None, op_a="N", op_b="N") -> torch.Tensor:
+    """Tensor form: returns ``out`` (allocated if None) = op(A) @ op(B).  A
+    and B are the stored row-major tensors (with op 'T', A is K x M and B is
+    N x K); views with a leading dimension (``stride(0)``) and a storage
+    offset are passed through as they are.  ``variant`` selects a ladder
+    rung and requires op 'N' for both factors."""
+    M, K = A.shape if op_a in ("N", 0) else A.shape[::-1]
+    K2, N = B.shape if op_b in ("N", 0) else B.shape[::-1]
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
     if out is None:
@@ -144,7 +158,11 @@ def gemm(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
     if tuple(out.shape) != (M, N):
         raise ValueError("out has the wrong shape")
     args = (M, N, K, A, _ld(A), B, _ld(B), out, _ld(out))
-    if variant is None:
+    if op_a not in ("N", 0) or op_b not in ("N", 0):
+        if variant is not None:
+            raise ValueError("transposed factors run on the default kernel only")
+        gemm_f32_op(op_a, op_b, *args, stream=stream)
+    elif variant is None:
         gemm_f32(*args, stream=stream)
     else:
         gemm_f32_variant(variant, *args, stream=stream)

@@ -36,6 +36,8 @@ const Diagnostic kDiagnostics[] = {
     {"mfma256x256_bk16_w2x4_direct", 3, 8},
     {"mfma256x256_bk32_w4x2_direct", 3, 9},
     {"mfma256x256_bk32_w2x4_direct_swz32", 3, 10},
+    {"mfma256x256_bk32_w2x4_direct_g4", 3, 11},
+    {"mfma256x256_bk32_w2x4_direct_g16", 3, 12},
 };
 constexpr int kNumDiagnostics = (int)(sizeof(kDiagnostics) / sizeof(kDiagnostics[0]));
 
@@ -52,16 +54,24 @@ bool extent_fits(int64_t rows, int64_t cols, int64_t ld) {
     return !__builtin_add_overflow(last, cols, &last);
 }
 
-int validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
-             int64_t ldb, const float* C, int64_t ldc) {
+// op_a / op_b: 0 = the factor as stored, 1 = its transpose (A stored K x M,
+// B stored N x K).
+int validate(int op_a, int op_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+             const float* B, int64_t ldb, const float* C, int64_t ldc) {
+    if ((op_a != GEMM_F32_OP_N && op_a != GEMM_F32_OP_T) ||
+        (op_b != GEMM_F32_OP_N && op_b != GEMM_F32_OP_T))
+        return GEMM_F32_ERR_INVALID_OP;
     if (M < 0 || N < 0 || K < 0) return GEMM_F32_ERR_INVALID_DIM;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    const int64_t a_rows = op_a ? K : M, a_cols = op_a ? M : K;
+    const int64_t b_rows = op_b ? N : K, b_cols = op_b ? K : N;
+    if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) || ldc < (N > 1 ? N : 1))
         return GEMM_F32_ERR_INVALID_LD;
     if (M == 0 || N == 0) return GEMM_F32_OK;           // nothing is read or written
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return GEMM_F32_ERR_NULL_PTR;
     if (misaligned(C) || (K > 0 && (misaligned(A) || misaligned(B)))) return GEMM_F32_ERR_MISALIGNED;
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_F32_ERR_TOO_LARGE;
-    if (!extent_fits(M, K, lda) || !extent_fits(K, N, ldb) || !extent_fits(M, N, ldc))
+    if (!extent_fits(a_rows, a_cols, lda) || !extent_fits(b_rows, b_cols, ldb) ||
+        !extent_fits(M, N, ldc))
         return GEMM_F32_ERR_TOO_LARGE;
     // every launch uses at most one block per 16 x 16 outputs and at most 1024
     // threads per block; keep the grid below 2^32 work-items
@@ -70,9 +80,9 @@ int validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const
     return GEMM_F32_OK;
 }
 
-int run(int rung, int config, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
-        const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
-    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+int run(int rung, int config, int op_a, int op_b, int64_t M, int64_t N, int64_t K, const float* A,
+        int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+    const int st = validate(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc);
     if (st != GEMM_F32_OK) return st;
     if (M == 0 || N == 0) return GEMM_F32_OK;
     int dev = -1;
@@ -84,9 +94,12 @@ int run(int rung, int config, int64_t M, int64_t N, int64_t K, const float* A, i
         case 0: e = launch_naive(p, s); break;
         case 1: e = launch_tiled(p, s, config); break;
         case 2: e = launch_regblock(p, s, config); break;
-        default: e = launch_mfma(p, s, config < 0 ? mfma_pick_config(p.M, p.N, p.K) : config); break;
+        default:
+            e = launch_mfma(p, s, config < 0 ? mfma_pick_config(p.M, p.N, p.K) : config, op_a, op_b);
+            break;
     }
     if (e == hipErrorInvalidValue) return GEMM_F32_ERR_TOO_LARGE;
+    if (e == hipErrorNotSupported) return GEMM_F32_ERR_INVALID_OP;
     return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
 }
 
@@ -97,7 +110,13 @@ using namespace gemmf32;
 
 extern "C" int gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                         const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
-    return run(3, -1, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return run(3, -1, GEMM_F32_OP_N, GEMM_F32_OP_N, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+extern "C" int gemm_f32_op(int op_a, int op_b, int64_t M, int64_t N, int64_t K, const float* A,
+                           int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                           void* stream) {
+    return run(3, -1, op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 extern "C" int gemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const float* A,
@@ -105,12 +124,13 @@ extern "C" int gemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, co
                                 void* stream) {
     if (variant >= 0 && variant < kNumRungs) {
         const int config = variant == 1 ? 4 : (variant == 2 ? 0 : -1);   // rung defaults
-        return run(variant, config, M, N, K, A, lda, B, ldb, C, ldc, stream);
+        return run(variant, config, GEMM_F32_OP_N, GEMM_F32_OP_N, M, N, K, A, lda, B, ldb, C, ldc,
+                   stream);
     }
     const int d = variant - kDiagBase;
     if (d >= 0 && d < kNumDiagnostics)
-        return run(kDiagnostics[d].rung, kDiagnostics[d].config, M, N, K, A, lda, B, ldb, C, ldc,
-                   stream);
+        return run(kDiagnostics[d].rung, kDiagnostics[d].config, GEMM_F32_OP_N, GEMM_F32_OP_N, M, N,
+                   K, A, lda, B, ldb, C, ldc, stream);
     return GEMM_F32_ERR_INVALID_VARIANT;
 }
 
@@ -137,6 +157,7 @@ extern "C" const char* gemm_f32_status_string(int status) {
         case GEMM_F32_ERR_TOO_LARGE: return "problem too large for the kernel index range or grid";
         case GEMM_F32_ERR_LAUNCH: return "kernel launch rejected by the HIP runtime";
         case GEMM_F32_ERR_DEVICE: return "no usable current HIP device";
+        case GEMM_F32_ERR_INVALID_OP: return "invalid op: op_a and op_b must be GEMM_F32_OP_N or GEMM_F32_OP_T";
         default: return "unknown status";
     }
 }

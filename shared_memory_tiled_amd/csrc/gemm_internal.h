@@ -9,6 +9,8 @@ namespace gemmf32 {
 
 // One product C = A x B on row-major binary32 matrices (see gemm_f32.h).
 // Sizes were validated by the entry point: 0 < M, N < 2^31, 0 <= K < 2^31.
+// For the MFMA kernels A and/or B may be stored transposed (see mfma.hip);
+// the other kernels take them as stored.
 struct GemmArgs {
     int M, N, K;
     const float* A; int64_t lda;
@@ -62,7 +64,7 @@ __device__ __forceinline__ void store4_guarded(float* __restrict__ base, int r, 
 hipError_t launch_naive(const GemmArgs& p, hipStream_t s);
 hipError_t launch_tiled(const GemmArgs& p, hipStream_t s, int pad);
 hipError_t launch_regblock(const GemmArgs& p, hipStream_t s, int config);
-hipError_t launch_mfma(const GemmArgs& p, hipStream_t s, int config);
+hipError_t launch_mfma(const GemmArgs& p, hipStream_t s, int config, int op_a, int op_b);
 
 // Number of MFMA / register-blocked tile configurations and their names.
 int mfma_num_configs();

@@ -8,6 +8,8 @@
 // FMAs.  The pages use matrix units only with 16-bit inputs (PMPP one-volume
 // notes, deep-learning chapter: the FC layer is a GEMM on tensor cores); the
 // fp32 matrix instruction is this library's reading for an fp32 product.
+// The same chapter runs the backward products X^T dY and dY W^T on the same
+// tile kernel; here either factor may be stored transposed (op(A), op(B)).
 //
 // v_mfma_f32_32x32x2_f32: D(32x32) += A(32x2) B(2x32) per wave, 16 passes.
 // Lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32]; accumulator
@@ -15,19 +17,25 @@
 //
 // The order of the k terms inside a phase is free (the sum is the same up
 // to rounding), so for each group of 8 k values lane half h = l / 32 feeds
-// k = kg + 4h + s to the s-th of four instructions.  A lane's four A
-// operands are then contiguous and come from LDS in one 128-bit read.
+// k = kg + 4h + s to the s-th of four instructions.  A lane's four operands
+// of one factor are then four consecutive k values of one row of op(X).
+// The k order depends only on the tile shape, never on how a factor is
+// stored, so op(A) = A^T gives the same bits as A stored untransposed.
 //
-// LDS layout per stage (two stages, one barrier per phase):
-//   A: BM rows x BK k, m-major as in global memory.  Register-staged
-//      kernels pad each row by 4 words (row stride BK + 4): the 16 rows that
-//      one 128-bit read touches per LDS cycle then start on 16 different
-//      4-bank groups.  Direct-copy kernels cannot pad (one copy instruction
-//      fills 1 KB contiguously), so they permute the 16-byte chunks of each
-//      row by an XOR with the row index instead, to the same effect.
-//   B: BK rows x BN n, k-major as in global memory, row stride BN + 8.  A
-//      lane reads one word; the two lane halves read rows 4 apart, and the
-//      8-word pad puts those two 32-word runs in different banks.
+// Each factor is an MN x K matrix (MN = M for A, N for B) stored either
+// k-contiguous (element (mn, k) at X[mn ld + k]: A as stored, B stored
+// transposed) or mn-contiguous (X[k ld + mn]: B as stored, A stored
+// transposed).  Its LDS tile keeps the stored orientation:
+//   k-contiguous: MN rows of BK k values.  A lane's four k values are one
+//      128-bit read.  Register-staged kernels pad rows by 4 words (row
+//      stride BK + 4): the 16 rows one 128-bit read touches per LDS cycle
+//      then start on 16 different 4-bank groups.  Direct-copy kernels cannot
+//      pad (one copy instruction fills 1 KB contiguously), so they permute
+//      the 16-byte chunks of each row by an XOR with the row index instead.
+//   mn-contiguous: BK rows of MN values, row stride MN + 8.  A lane reads
+//      its four k values as four words; the two lane halves read rows 4
+//      apart, and the 8-word pad puts those two 32-word runs in different
+//      banks.
 // The bank rule is the first page's ("Bank Conflict": n distinct words in
 // one bank serialise), measured on gfx950 rather than assumed: 128-bit LDS
 // reads are served 16 lanes at a time from 64 banks.  A swizzle laid out for
@@ -44,7 +52,7 @@
 // Block -> tile mapping: gfx950 hands consecutive workgroups to its eight
 // XCDs in turn, and each XCD has its own L2.  The block index is remapped so
 // each XCD walks a contiguous run of tiles, and tiles are ordered in groups
-// of GROUP_M tile rows so that the blocks resident on one XCD at a time
+// of group_m tile rows so that the blocks resident on one XCD at a time
 // share A row panels and B column panels in that XCD's L2.
 #include "gemm_internal.h"
 
@@ -64,40 +72,100 @@ __device__ __forceinline__ int xcd_contiguous(int b, int nblocks) {
     const int x = b % kXcds, local = b / kXcds;
     return x * per + min(x, extra) + local;
 }
+
+// Where one factor lives: stored matrix, leading dimension, extent along mn
+// (M or N) and along k.
+struct Factor {
+    const float* X;
+    int64_t ld;
+    int mn_ext, k_ext;
+};
+
+// One factor's tile: MNT x BK values of op(X) per stage, copied by NT
+// threads (NW waves).  KC: the factor is stored k-contiguous.
+template <int MNT, int BK, bool KC, bool DIRECT, int SWZ_BANKS, int NT, int NW>
+struct OperandTile {
+    static constexpr int STRIDE = KC ? (DIRECT ? BK : BK + 4) : MNT + 8;
+    static constexpr int WORDS = KC ? MNT * STRIDE : BK * STRIDE;    // per stage
+    static constexpr int CPR = KC ? BK / 4 : MNT / 4;   // 16-byte chunks per stored row
+    static constexpr int CHUNKS = MNT * BK / 4 / NT;    // copy chunks per thread
+    static constexpr int ROWS_PER_SWEEP = SWZ_BANKS / BK;
+    static constexpr int COPIES = !DIRECT ? 0 : (KC ? MNT * BK / 256 / NW : BK / NW);
+    static_assert(CHUNKS * NT * 4 == MNT * BK, "copy split");
+    static_assert(!DIRECT || (KC ? ((MNT * BK / 256) % NW == 0 && (BK == 16 || BK == 32))
+                                 : (MNT == 256 && BK % NW == 0)),
+                  "direct-copy tile shape");
+
+    // Stored (row, col) of copy chunk q: rows are mn (KC) or k (MC).
+    __device__ static int chunk_row(int q) { return q / CPR; }
+    __device__ static int chunk_col(int q) { return (q % CPR) * 4; }
+    // Physical position of 16-byte chunk lc in k-contiguous row r.
+    __device__ static int phys(int r, int lc) {
+        return (KC && DIRECT) ? (lc ^ ((r / ROWS_PER_SWEEP) % (BK / 4))) : lc;
+    }
+    // LDS word of the chunk that starts at stored (row, col), col % 4 == 0.
+    __device__ static int word(int row, int col) {
+        return KC ? row * STRIDE + 4 * phys(row, col / 4) : row * STRIDE + col;
+    }
+    // op(X)[mn0 + r][k0 + c .. c+3] as stored chunk, with ghost zeros.
+    __device__ static floatx4 ghost_load(const Factor& f, int mn0, int k0, int row, int col) {
+        return KC ? load4_ghost(f.X, mn0 + row, f.mn_ext, k0 + col, f.k_ext, f.ld)
+                  : load4_ghost(f.X, k0 + row, f.k_ext, mn0 + col, f.mn_ext, f.ld);
+    }
+    // Element offset of stored (row, col) of the phase-0 tile; a phase adds
+    // phase_step(k0).
+    __device__ static int64_t offset(const Factor& f, int mn0, int row, int col) {
+        return KC ? (int64_t)(mn0 + row) * f.ld + col : (int64_t)row * f.ld + mn0 + col;
+    }
+    __device__ static int64_t phase_step(const Factor& f, int k0) {
+        return KC ? (int64_t)k0 : (int64_t)k0 * f.ld;
+    }
+    // Four k values (k = kg + 4h + s, s = 0..3) of row mn of op(X).
+    __device__ static floatx4 fragment(const float* stage, int mn, int kg, int h) {
+        if constexpr (KC) {
+            return *reinterpret_cast<const floatx4*>(&stage[word(mn, kg + 4 * h)]);
+        } else {
+            floatx4 v;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) v[s] = stage[(kg + 4 * h + s) * STRIDE + mn];
+            return v;
+        }
+    }
+    // Direct copy j of a wave: the stored rows it fills, and lane l's source.
+    //   KC: rows R0 .. R0 + 64/CPR - 1 with R0 = (w + j NW) 64/CPR; lane l
+    //       fills physical chunk l % CPR of row R0 + l / CPR.
+    //   MC: row w + j NW; lane l fills columns 4l .. 4l + 3.
+    __device__ static int copy_first_row(int wave, int j) {
+        return KC ? (wave + j * NW) * (64 / CPR) : wave + j * NW;
+    }
+    __device__ static int64_t copy_offset(const Factor& f, int mn0, int wave, int j, int lane) {
+        if constexpr (KC) {
+            const int r = copy_first_row(wave, j) + lane / CPR;
+            return (int64_t)(mn0 + r) * f.ld + 4 * phys(r, lane % CPR);   // XOR is its own inverse
+        } else {
+            return (int64_t)copy_first_row(wave, j) * f.ld + mn0 + 4 * lane;
+        }
+    }
+};
 }  // namespace
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool DIRECT, int SWZ_BANKS>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool DIRECT, int SWZ_BANKS,
+          bool TRANS_A, bool TRANS_B>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
 void gemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
-    constexpr int NT = WAVES_M * WAVES_N * 64;
     constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int NT = NW * 64;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;     // wave tile
     constexpr int FM = WM / 32, FN = WN / 32;               // 32x32 blocks per wave
-    // A rows: padded by 4 words, or (DIRECT) unpadded with the 16-byte chunks
-    // of a row permuted by an XOR of the row index, see a_chunk() below.
-    constexpr int SA = DIRECT ? BK : BK + 4, SB = BN + 8;
-    constexpr int CPR = BK / 4;                 // 16-byte chunks per A row
-    // rows of the A tile that fit in one sweep of SWZ_BANKS 4-byte banks
-    constexpr int ROWS_PER_BANK_CYCLE = SWZ_BANKS / BK;
-    constexpr int A_STAGE = BM * SA, B_STAGE = BK * SB;
-    constexpr int A_CHUNKS = BM * BK / 4 / NT, B_CHUNKS = BK * BN / 4 / NT;
     static_assert(WM % 32 == 0 && WN % 32 == 0 && BK % 8 == 0, "tile shape");
-    static_assert(A_CHUNKS * NT * 4 == BM * BK && B_CHUNKS * NT * 4 == BK * BN, "copy split");
-    static_assert(!DIRECT || (BN == 256 && (BK == 16 || BK == 32) && (BM * BK / 256) % NW == 0 &&
-                              BK % NW == 0), "direct-to-LDS copy shape");
-    __shared__ __attribute__((aligned(16))) float lds[2 * (A_STAGE + B_STAGE)];
-
-    // Physical 16-byte chunk of logical chunk lc in A-tile row r.  With the
-    // XOR, the eight rows a 128-bit access touches per LDS cycle (32 banks,
-    // 8 lanes) read eight different bank groups, and the eight chunks a
-    // 1 KB direct copy writes per cycle do too -- the swizzle of the first
-    // page's "Bank Conflict" section, on 16-byte chunks instead of words.
-    auto a_chunk = [](int r, int lc) {
-        return DIRECT ? (lc ^ ((r / ROWS_PER_BANK_CYCLE) % CPR)) : lc;
-    };
+    using TA = OperandTile<BM, BK, !TRANS_A, DIRECT, SWZ_BANKS, NT, NW>;
+    using TB = OperandTile<BN, BK, TRANS_B, DIRECT, SWZ_BANKS, NT, NW>;
+    constexpr int STAGE = TA::WORDS + TB::WORDS;
+    __shared__ __attribute__((aligned(16))) float lds[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int li = lane & 31, lh = lane >> 5;
 
@@ -111,114 +179,103 @@ void gemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     const int m0 = (first_m + in_g % gm) * BM;
     const int n0 = (in_g / gm) * BN;
 
-    // Per-thread element offsets of this thread's copy chunks (phase 0); a
-    // phase adds k0 to the A offsets and k0 * ldb to the B offsets.  (Not
-    // used by the direct-copy kernels.)
-    int64_t a_off[A_CHUNKS], b_off[B_CHUNKS];
-#pragma unroll
-    for (int u = 0; u < (DIRECT ? 0 : A_CHUNKS); ++u) {
-        const int q = tid + u * NT;
-        a_off[u] = (int64_t)(m0 + q / (BK / 4)) * p.lda + (q % (BK / 4)) * 4;
-    }
-#pragma unroll
-    for (int u = 0; u < (DIRECT ? 0 : B_CHUNKS); ++u) {
-        const int q = tid + u * NT;
-        b_off[u] = (int64_t)(q / (BN / 4)) * p.ldb + n0 + (q % (BN / 4)) * 4;
-    }
+    const Factor fa{p.A, p.lda, p.M, p.K};
+    const Factor fb{p.B, p.ldb, p.N, p.K};
     // Interior tiles skip the ghost checks: the test is uniform over the
-    // block, so the branch below never diverges within a wave.
+    // block, so the branches below never diverge within a wave.
     const bool tile_inside = (m0 + BM <= p.M) && (n0 + BN <= p.N);
 
-    floatx4 ra[A_CHUNKS], rb[B_CHUNKS];
+    // --- register-staged copies (not used by the direct-copy kernels) ---
+    int64_t a_off[DIRECT ? 1 : TA::CHUNKS], b_off[DIRECT ? 1 : TB::CHUNKS];
+    floatx4 ra[DIRECT ? 1 : TA::CHUNKS], rb[DIRECT ? 1 : TB::CHUNKS];
+    if constexpr (!DIRECT) {
+#pragma unroll
+        for (int u = 0; u < TA::CHUNKS; ++u) {
+            const int q = tid + u * NT;
+            a_off[u] = TA::offset(fa, m0, TA::chunk_row(q), TA::chunk_col(q));
+        }
+#pragma unroll
+        for (int u = 0; u < TB::CHUNKS; ++u) {
+            const int q = tid + u * NT;
+            b_off[u] = TB::offset(fb, n0, TB::chunk_row(q), TB::chunk_col(q));
+        }
+    }
     auto load_tiles = [&](int k0) {
-        if (!DIRECT && tile_inside && k0 + BK <= p.K) {
-            const float* __restrict__ a = p.A + k0;
-            const float* __restrict__ b = p.B + (int64_t)k0 * p.ldb;
+        if constexpr (!DIRECT) {
+            if (tile_inside && k0 + BK <= p.K) {
+                const float* a = p.A + TA::phase_step(fa, k0);
+                const float* b = p.B + TB::phase_step(fb, k0);
 #pragma unroll
-            for (int u = 0; u < A_CHUNKS; ++u) __builtin_memcpy(&ra[u], a + a_off[u], 16);
+                for (int u = 0; u < TA::CHUNKS; ++u) __builtin_memcpy(&ra[u], a + a_off[u], 16);
 #pragma unroll
-            for (int u = 0; u < B_CHUNKS; ++u) __builtin_memcpy(&rb[u], b + b_off[u], 16);
-            return;
-        }
+                for (int u = 0; u < TB::CHUNKS; ++u) __builtin_memcpy(&rb[u], b + b_off[u], 16);
+                return;
+            }
 #pragma unroll
-        for (int u = 0; u < A_CHUNKS; ++u) {
-            const int q = tid + u * NT;
-            const int r = q / (BK / 4), c = (q % (BK / 4)) * 4;
-            ra[u] = load4_ghost(p.A, m0 + r, p.M, k0 + c, p.K, p.lda);
-        }
+            for (int u = 0; u < TA::CHUNKS; ++u) {
+                const int q = tid + u * NT;
+                ra[u] = TA::ghost_load(fa, m0, k0, TA::chunk_row(q), TA::chunk_col(q));
+            }
 #pragma unroll
-        for (int u = 0; u < B_CHUNKS; ++u) {
-            const int q = tid + u * NT;
-            const int r = q / (BN / 4), c = (q % (BN / 4)) * 4;
-            rb[u] = load4_ghost(p.B, k0 + r, p.K, n0 + c, p.N, p.ldb);
+            for (int u = 0; u < TB::CHUNKS; ++u) {
+                const int q = tid + u * NT;
+                rb[u] = TB::ghost_load(fb, n0, k0, TB::chunk_row(q), TB::chunk_col(q));
+            }
         }
     };
-    // Direct copies global -> LDS (global_load_lds_dwordx4): each wave
-    // instruction writes 1 KB of LDS contiguously, lane l at byte 16 l.  A:
-    // instruction j of wave w fills rows R0 .. R0 + 64/CPR - 1 with
-    // R0 = (w + j NW) 64/CPR; B: instruction j of wave w fills row w + j NW.
-    constexpr int A_DIRECT = DIRECT ? BM * BK / 256 / NW : 0;
-    constexpr int B_DIRECT = DIRECT ? BK / NW : 0;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    int64_t a_doff[A_DIRECT > 0 ? A_DIRECT : 1], b_doff[B_DIRECT > 0 ? B_DIRECT : 1];
-    if constexpr (DIRECT) {
+    auto store_tiles = [&](int buf) {
+        if constexpr (!DIRECT) {
+            float* as = lds + buf * STAGE;
+            float* bs = as + TA::WORDS;
 #pragma unroll
-        for (int j = 0; j < A_DIRECT; ++j) {
-            const int r = (wave_u + j * NW) * (64 / CPR) + lane / CPR;
-            const int lc = a_chunk(r, lane % CPR);       // the XOR is its own inverse
-            a_doff[j] = (int64_t)(m0 + r) * p.lda + 4 * lc;
+            for (int u = 0; u < TA::CHUNKS; ++u) {
+                const int q = tid + u * NT;
+                *reinterpret_cast<floatx4*>(&as[TA::word(TA::chunk_row(q), TA::chunk_col(q))]) = ra[u];
+            }
+#pragma unroll
+            for (int u = 0; u < TB::CHUNKS; ++u) {
+                const int q = tid + u * NT;
+                *reinterpret_cast<floatx4*>(&bs[TB::word(TB::chunk_row(q), TB::chunk_col(q))]) = rb[u];
+            }
         }
-#pragma unroll
-        for (int j = 0; j < B_DIRECT; ++j)
-            b_doff[j] = (int64_t)(wave_u + j * NW) * p.ldb + n0 + 4 * lane;
-    }
-    auto direct_tiles = [&](int k0, int buf) {
-        float* as = lds + buf * (A_STAGE + B_STAGE);
-        float* bs = as + A_STAGE;
-        const float* a = p.A + k0;
-        const float* b = p.B + (int64_t)k0 * p.ldb;
-#pragma unroll
-        for (int j = 0; j < A_DIRECT; ++j)
-            copy16_global_to_lds(a + a_doff[j], as + (wave_u + j * NW) * (64 / CPR) * SA);
-#pragma unroll
-        for (int j = 0; j < B_DIRECT; ++j)
-            copy16_global_to_lds(b + b_doff[j], bs + (wave_u + j * NW) * SB);
     };
 
+    // --- direct copies global -> LDS ---
+    int64_t a_doff[TA::COPIES > 0 ? TA::COPIES : 1], b_doff[TB::COPIES > 0 ? TB::COPIES : 1];
+    if constexpr (DIRECT) {
+#pragma unroll
+        for (int j = 0; j < TA::COPIES; ++j) a_doff[j] = TA::copy_offset(fa, m0, wave_u, j, lane);
+#pragma unroll
+        for (int j = 0; j < TB::COPIES; ++j) b_doff[j] = TB::copy_offset(fb, n0, wave_u, j, lane);
+    }
+    auto direct_tiles = [&](int k0, int buf) {
+        float* as = lds + buf * STAGE;
+        float* bs = as + TA::WORDS;
+        const float* a = p.A + TA::phase_step(fa, k0);
+        const float* b = p.B + TB::phase_step(fb, k0);
+#pragma unroll
+        for (int j = 0; j < TA::COPIES; ++j)
+            copy16_global_to_lds(a + a_doff[j], as + TA::copy_first_row(wave_u, j) * TA::STRIDE);
+#pragma unroll
+        for (int j = 0; j < TB::COPIES; ++j)
+            copy16_global_to_lds(b + b_doff[j], bs + TB::copy_first_row(wave_u, j) * TB::STRIDE);
+    };
     // Ghost phases of the direct-copy kernels: load and store chunk by chunk
     // (no registers held across the math; these phases are rare).
     auto ghost_tiles_now = [&](int k0, int buf) {
-        float* as = lds + buf * (A_STAGE + B_STAGE);
-        float* bs = as + A_STAGE;
+        float* as = lds + buf * STAGE;
+        float* bs = as + TA::WORDS;
 #pragma unroll
-        for (int u = 0; u < A_CHUNKS; ++u) {
+        for (int u = 0; u < TA::CHUNKS; ++u) {
             const int q = tid + u * NT;
-            const int r = q / (BK / 4), c = (q % (BK / 4)) * 4;
-            *reinterpret_cast<floatx4*>(&as[r * SA + 4 * a_chunk(r, c / 4)]) =
-                load4_ghost(p.A, m0 + r, p.M, k0 + c, p.K, p.lda);
+            const int r = TA::chunk_row(q), c = TA::chunk_col(q);
+            *reinterpret_cast<floatx4*>(&as[TA::word(r, c)]) = TA::ghost_load(fa, m0, k0, r, c);
         }
 #pragma unroll
-        for (int u = 0; u < B_CHUNKS; ++u) {
+        for (int u = 0; u < TB::CHUNKS; ++u) {
             const int q = tid + u * NT;
-            const int r = q / (BN / 4), c = (q % (BN / 4)) * 4;
-            *reinterpret_cast<floatx4*>(&bs[r * SB + c]) = load4_ghost(p.B, k0 + r, p.K, n0 + c, p.N, p.ldb);
-        }
-    };
-
-    auto store_tiles = [&](int buf) {
-        float* as = lds + buf * (A_STAGE + B_STAGE);
-        float* bs = as + A_STAGE;
-#pragma unroll
-        for (int u = 0; u < A_CHUNKS; ++u) {
-            const int q = tid + u * NT;
-            const int r = q / (BK / 4), c = (q % (BK / 4)) * 4;
-            *reinterpret_cast<floatx4*>(&as[r * SA + 4 * a_chunk(r, c / 4)]) = ra[u];
-        }
-#pragma unroll
-        for (int u = 0; u < B_CHUNKS; ++u) {
-            const int q = tid + u * NT;
-            const int r = q / (BN / 4), c = (q % (BN / 4)) * 4;
-            *reinterpret_cast<floatx4*>(&bs[r * SB + c]) = rb[u];
+            const int r = TB::chunk_row(q), c = TB::chunk_col(q);
+            *reinterpret_cast<floatx4*>(&bs[TB::word(r, c)]) = TB::ghost_load(fb, n0, k0, r, c);
         }
     };
 
@@ -233,7 +290,7 @@ void gemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     const int phases = ceil_div(p.K, BK);
     // A phase is copied directly into LDS when it lies wholly inside the
     // matrices; ghost phases go through registers (load4_ghost + LDS store).
-    auto direct_ok = [&](int k0) { return DIRECT && tile_inside && k0 + BK <= p.K; };
+    auto direct_ok = [&](int k0) { return tile_inside && k0 + BK <= p.K; };
     if (phases > 0) {
         if constexpr (DIRECT) {
             if (direct_ok(0)) direct_tiles(0, 0);
@@ -256,23 +313,15 @@ void gemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         } else if (more) {
             load_tiles((ph + 1) * BK);
         }
-        const float* as = lds + cur * (A_STAGE + B_STAGE);
-        const float* bs = as + A_STAGE;
+        const float* as = lds + cur * STAGE;
+        const float* bs = as + TA::WORDS;
 #pragma unroll
         for (int kg = 0; kg < BK; kg += 8) {
-            floatx4 a[FM];
-            float b[FN][4];
+            floatx4 a[FM], b[FN];
 #pragma unroll
-            for (int f = 0; f < FM; ++f)
-            {
-                const int r = wm * WM + f * 32 + li;
-                a[f] = *reinterpret_cast<const floatx4*>(&as[r * SA + 4 * a_chunk(r, kg / 4 + lh)]);
-            }
+            for (int f = 0; f < FM; ++f) a[f] = TA::fragment(as, wm * WM + f * 32 + li, kg, lh);
 #pragma unroll
-            for (int f = 0; f < FN; ++f)
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    b[f][s] = bs[(kg + 4 * lh + s) * SB + wn * WN + f * 32 + li];
+            for (int f = 0; f < FN; ++f) b[f] = TB::fragment(bs, wn * WN + f * 32 + li, kg, lh);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -304,37 +353,53 @@ void gemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
 }
 
 namespace {
+using LaunchFn = hipError_t (*)(const GemmArgs&, hipStream_t, int, int, int, unsigned);
+
 struct MfmaConfig {
     const char* name;
-    int bm, bn, threads;
-    hipError_t (*launch)(const GemmArgs&, hipStream_t, int, int, int, unsigned);
+    int bm, bn, threads, group_m;
+    LaunchFn launch[4];          // by 2 op_a + op_b; null: op pair not built for this config
 };
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool DIRECT = false, int SWZ = 64>
-hipError_t launch_cfg(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool DIRECT, int SWZ, bool TRA, bool TRB>
+hipError_t launch_one(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
                       unsigned blocks) {
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, WAVES_M, WAVES_N, DIRECT, SWZ>), dim3(blocks),
-                       dim3(WAVES_M * WAVES_N * 64), 0, s, p, tiles_m, tiles_n, group_m);
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, WAVES_M, WAVES_N, DIRECT, SWZ, TRA, TRB>),
+                       dim3(blocks), dim3(WAVES_M * WAVES_N * 64), 0, s, p, tiles_m, tiles_n, group_m);
     return hipGetLastError();
 }
 
+// NN only (diagnostic layouts) or all four op combinations.
+#define NN_ONLY(BM, BN, BK, WM, WN, D, S) \
+    {launch_one<BM, BN, BK, WM, WN, D, S, false, false>, nullptr, nullptr, nullptr}
+#define ALL_OPS(BM, BN, BK, WM, WN, D, S)                    \
+    {launch_one<BM, BN, BK, WM, WN, D, S, false, false>,     \
+     launch_one<BM, BN, BK, WM, WN, D, S, false, true>,      \
+     launch_one<BM, BN, BK, WM, WN, D, S, true, false>,      \
+     launch_one<BM, BN, BK, WM, WN, D, S, true, true>}
+
 const MfmaConfig kConfigs[] = {
-    // register-staged copies (global -> VGPR -> LDS), padded A rows
-    {"mfma256x256_bk16_w2x2", 256, 256, 256, launch_cfg<256, 256, 16, 2, 2>},
-    {"mfma128x128_bk16_w2x2", 128, 128, 256, launch_cfg<128, 128, 16, 2, 2>},
-    {"mfma256x128_bk16_w2x2", 256, 128, 256, launch_cfg<256, 128, 16, 2, 2>},
-    {"mfma128x128_bk32_w2x2", 128, 128, 256, launch_cfg<128, 128, 32, 2, 2>},
-    {"mfma64x64_bk16_w2x2", 64, 64, 256, launch_cfg<64, 64, 16, 2, 2>},
-    {"mfma256x256_bk32_w2x4", 256, 256, 512, launch_cfg<256, 256, 32, 2, 4>},
-    {"mfma128x256_bk16_w2x2", 128, 256, 256, launch_cfg<128, 256, 16, 2, 2>},
-    // direct copies (global -> LDS), XOR-swizzled A rows
-    {"mfma256x256_bk32_w2x4_direct", 256, 256, 512, launch_cfg<256, 256, 32, 2, 4, true, 64>},
-    {"mfma256x256_bk16_w2x4_direct", 256, 256, 512, launch_cfg<256, 256, 16, 2, 4, true, 64>},
-    {"mfma256x256_bk32_w4x2_direct", 256, 256, 512, launch_cfg<256, 256, 32, 4, 2, true, 64>},
+    // register-staged copies (global -> VGPR -> LDS), padded k-contiguous rows
+    {"mfma256x256_bk16_w2x2", 256, 256, 256, 8, NN_ONLY(256, 256, 16, 2, 2, false, 64)},
+    {"mfma128x128_bk16_w2x2", 128, 128, 256, 8, ALL_OPS(128, 128, 16, 2, 2, false, 64)},
+    {"mfma256x128_bk16_w2x2", 256, 128, 256, 8, NN_ONLY(256, 128, 16, 2, 2, false, 64)},
+    {"mfma128x128_bk32_w2x2", 128, 128, 256, 8, NN_ONLY(128, 128, 32, 2, 2, false, 64)},
+    {"mfma64x64_bk16_w2x2", 64, 64, 256, 8, ALL_OPS(64, 64, 16, 2, 2, false, 64)},
+    {"mfma256x256_bk32_w2x4", 256, 256, 512, 8, NN_ONLY(256, 256, 32, 2, 4, false, 64)},
+    {"mfma128x256_bk16_w2x2", 128, 256, 256, 8, NN_ONLY(128, 256, 16, 2, 2, false, 64)},
+    // direct copies (global -> LDS), XOR-swizzled k-contiguous rows
+    {"mfma256x256_bk32_w2x4_direct", 256, 256, 512, 8, ALL_OPS(256, 256, 32, 2, 4, true, 64)},
+    {"mfma256x256_bk16_w2x4_direct", 256, 256, 512, 8, NN_ONLY(256, 256, 16, 2, 4, true, 64)},
+    {"mfma256x256_bk32_w4x2_direct", 256, 256, 512, 8, NN_ONLY(256, 256, 32, 4, 2, true, 64)},
     // the same swizzle laid out for a 32-bank LDS: kept to show, in the bank
     // conflict counter, that gfx950 serves 128-bit reads from 64 banks
-    {"mfma256x256_bk32_w2x4_direct_swz32", 256, 256, 512, launch_cfg<256, 256, 32, 2, 4, true, 32>},
+    {"mfma256x256_bk32_w2x4_direct_swz32", 256, 256, 512, 8, NN_ONLY(256, 256, 32, 2, 4, true, 32)},
+    // the default with tile-row groups of 4 and 16 instead of 8 (L2 reuse)
+    {"mfma256x256_bk32_w2x4_direct_g4", 256, 256, 512, 4, NN_ONLY(256, 256, 32, 2, 4, true, 64)},
+    {"mfma256x256_bk32_w2x4_direct_g16", 256, 256, 512, 16, NN_ONLY(256, 256, 32, 2, 4, true, 64)},
 };
+#undef NN_ONLY
+#undef ALL_OPS
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 }  // namespace
 
@@ -344,7 +409,8 @@ const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConf
 // Largest tile that still gives every CU at least one workgroup: 256 x 256
 // with eight waves (two per SIMD, so one wave's barrier or LDS wait is
 // covered by the other's matrix instructions) and direct global -> LDS
-// copies once there are 256 such tiles.
+// copies once there are 256 such tiles.  Every picked configuration is built
+// for all four op combinations.
 int mfma_pick_config(int M, int N, int /*K*/) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
@@ -353,14 +419,16 @@ int mfma_pick_config(int M, int N, int /*K*/) {
     return 4;
 }
 
-// Returns hipErrorInvalidValue when the grid would exceed the launch limits.
-hipError_t launch_mfma(const GemmArgs& p, hipStream_t s, int config) {
+// hipErrorInvalidValue: the grid would exceed the launch limits.
+// hipErrorNotSupported: this configuration is not built for the op pair.
+hipError_t launch_mfma(const GemmArgs& p, hipStream_t s, int config, int op_a, int op_b) {
     const MfmaConfig& c = kConfigs[(config >= 0 && config < kNumConfigs) ? config : 0];
+    const LaunchFn fn = c.launch[2 * (op_a ? 1 : 0) + (op_b ? 1 : 0)];
+    if (fn == nullptr) return hipErrorNotSupported;
     const int tiles_m = ceil_div(p.M, c.bm), tiles_n = ceil_div(p.N, c.bn);
     const int64_t blocks = (int64_t)tiles_m * tiles_n;
     if (blocks * c.threads > 0xFFFFFFFFll || blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    const int group_m = 8;
-    return c.launch(p, s, tiles_m, tiles_n, group_m, (unsigned)blocks);
+    return fn(p, s, tiles_m, tiles_n, c.group_m, (unsigned)blocks);
 }
 
 }  // namespace gemmf32

@@ -117,6 +117,24 @@ def test_validation_without_launch(lib, args, code):
         assert lib.gemm_f32_variant(v, M, N, K, A, lda, B, ldb, C, ldc, None) == want
 
 
+@pytest.mark.parametrize("op_a,op_b,args,code", [
+    (2, 0, (4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_OP"),
+    (0, -1, (4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_OP"),
+    (1, 0, (8, 4, 3, FAKE, 7, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_LD"),    # A^T: lda >= M
+    (1, 0, (8, 4, 3, FAKE, 8, FAKE, 4, FAKE, 4), "GEMM_F32_OK_IF_NO_GPU"),
+    (0, 1, (4, 6, 9, FAKE, 9, FAKE, 8, FAKE, 6), "GEMM_F32_ERR_INVALID_LD"),    # B^T: ldb >= K
+    (1, 1, (4, 6, 9, FAKE, 3, FAKE, 9, FAKE, 6), "GEMM_F32_ERR_INVALID_LD"),
+    (1, 1, (4, 6, 9, FAKE + 1, 4, FAKE, 9, FAKE, 6), "GEMM_F32_ERR_MISALIGNED"),
+    (1, 0, (-1, 6, 9, FAKE, 4, FAKE, 6, FAKE, 6), "GEMM_F32_ERR_INVALID_DIM"),
+    (1, 1, (0, 6, 9, None, 1, None, 9, None, 6), "GEMM_F32_OK"),
+])
+def test_op_validation_without_launch(lib, op_a, op_b, args, code):
+    if code == "GEMM_F32_OK_IF_NO_GPU":
+        return      # valid arguments: would launch (covered by the GPU tests)
+    want = declared_codes()[code]
+    assert lib.gemm_f32_op(op_a, op_b, *args, None) == want
+
+
 def test_unknown_variant(lib):
     code = declared_codes()["GEMM_F32_ERR_INVALID_VARIANT"]
     for v in (4, 15, -1, 16 + lib.gemm_f32_num_diagnostic_variants(), 1000):
