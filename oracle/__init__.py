@@ -20,6 +20,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gemm_oracle.c")
+_SOURCES = [_SRC, os.path.join(_HERE, "transpose_oracle.c")]
 _LIB = os.path.join(_HERE, "libgemm_oracle.so")
 
 _i64 = ctypes.c_int64
@@ -30,13 +31,19 @@ _ip = ctypes.POINTER(ctypes.c_int64)
 _lib = None
 
 
-def build(src: str = _SRC, out: str = _LIB) -> str:
-    """Compile the oracle into a shared library (gcc, strict IEEE arithmetic).
-    The library is written under a temporary name and renamed into place, so
+def build(src: str | None = None, out: str = _LIB, replace: dict | None = None) -> str:
+    """Compile the oracle sources into one shared library (gcc, strict IEEE
+    arithmetic).  ``replace`` maps a source's base name to another file to
+    compile in its place (``src`` is the same for gemm_oracle.c).  The
+    library is written under a temporary name and renamed into place, so
     concurrent builders never expose a partly written file."""
+    replace = dict(replace or {})
+    if src is not None:
+        replace["gemm_oracle.c"] = src
+    sources = [replace.get(os.path.basename(s), s) for s in _SOURCES]
     tmp = f"{out}.tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
-           "-shared", "-fPIC", "-pthread", "-o", tmp, src, "-lm"]
+           "-shared", "-fPIC", "-pthread", "-o", tmp, *sources, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -70,6 +77,10 @@ def load(path: str | None = None):
     lib.oracle_tiled_traffic.restype = ctypes.c_int
     lib.oracle_bank_conflict_degree.argtypes = [_i64, _ip, _i64]
     lib.oracle_bank_conflict_degree.restype = _i64
+    lib.oracle_transpose.argtypes = [_i64, _i64, _fp, _i64, _fp, _i64]
+    lib.oracle_transpose.restype = ctypes.c_int
+    lib.oracle_sectors_touched.argtypes = [_i64, _ip, _i64, _i64]
+    lib.oracle_sectors_touched.restype = _i64
     if path is None:
         _lib = lib
     return lib
@@ -180,3 +191,36 @@ def bank_conflict_degree(word_addrs, banks: int = 32, lib=None) -> int:
     lib = lib or load()
     w = np.ascontiguousarray(word_addrs, dtype=np.int64)
     return int(lib.oracle_bank_conflict_degree(w.shape[0], w.ctypes.data_as(_ip), banks))
+
+
+def transpose_into(X: np.ndarray, out: np.ndarray, lib=None) -> None:
+    """Writes the transpose of the 2-D float32 view X into the 2-D view out
+    (shape X.shape[::-1]); words of out's buffer outside the view are left as
+    they are."""
+    lib = lib or load()
+    rows, cols = X.shape
+    if out.shape != (cols, rows) or out.dtype != np.float32:
+        raise ValueError("out must be a float32 view of shape X.shape[::-1]")
+    px, ldx = _matrix_arg(X)
+    po, ldo = _matrix_arg(out)
+    rc = lib.oracle_transpose(rows, cols, px, ldx, po, ldo)
+    if rc != 0:
+        raise ValueError("oracle_transpose rejected its arguments")
+
+
+def transpose(X: np.ndarray, lib=None) -> np.ndarray:
+    """The transpose of the 2-D float32 view X as a new compact array."""
+    out = np.zeros(X.shape[::-1], dtype=np.float32)
+    transpose_into(X, out, lib=lib)
+    return out
+
+
+def sectors_touched(byte_addrs, width: int, sector_bytes: int = 32, lib=None) -> int:
+    """Distinct aligned sectors touched when lane l reads `width` bytes at
+    byte address byte_addrs[l]."""
+    lib = lib or load()
+    a = np.ascontiguousarray(byte_addrs, dtype=np.int64)
+    n = int(lib.oracle_sectors_touched(a.shape[0], a.ctypes.data_as(_ip), width, sector_bytes))
+    if n < 0:
+        raise ValueError("oracle_sectors_touched rejected its arguments")
+    return n

@@ -346,13 +346,58 @@ def check_bank_model(lib):
     assert oracle.bank_conflict_degree(np.full(32, ty * 32 + k), lib=lib) == g["tiled_product_reads"]  # As[ty][k]
 
 
+# --------------------------------------------------------------- transpose --
+
+def check_transpose(lib):
+    """The transpose against brute force on tiny shapes, numpy's transpose,
+    and the involution (transposing twice gives the input back bit for bit),
+    in padded, offset storage whose padding must stay untouched."""
+    gen = np.random.default_rng(111)
+    for rows, cols in ((1, 1), (1, 7), (5, 1), (3, 4), (4, 3)):
+        X = gen.standard_normal((rows, cols), dtype=np.float32)
+        T = oracle.transpose(X, lib=lib)
+        for r in range(rows):
+            for c in range(cols):
+                assert T[c, r] == X[r, c], (rows, cols, r, c)
+    for rows, cols in ((37, 53), (64, 33), (129, 257)):
+        X = gen.standard_normal((rows, cols), dtype=np.float32)
+        T = oracle.transpose(X, lib=lib)
+        assert np.array_equal(T, X.T)
+        assert np.array_equal(oracle.transpose(T, lib=lib), X)
+        Xp = _padded_copy(X, 3, 1)
+        buf = np.full(1 + cols * (rows + 5) + 8, 7.5, np.float32)
+        Tv = buf[1:1 + cols * (rows + 5)].reshape(cols, rows + 5)[:, :rows]
+        oracle.transpose_into(Xp, Tv, lib=lib)
+        assert np.array_equal(Tv, X.T)
+        mask = np.ones(buf.shape, bool)
+        for c in range(cols):
+            mask[1 + c * (rows + 5): 1 + c * (rows + 5) + rows] = False
+        assert np.all(buf[mask] == 7.5)
+
+
+def check_sector_model(lib):
+    """The first page's coalescing numbers: 32 lanes of 4-byte floats touch
+    128 bytes of 32-byte sectors when aligned, 160 bytes when shifted by one
+    float, and 1024 bytes when the lanes are 32 bytes apart."""
+    g = _golden()["coalescing_sectors"]
+    sb, n, w = g["sector_bytes"], g["lanes"], g["float_bytes"]
+    lanes = np.arange(n, dtype=np.int64)
+    assert oracle.sectors_touched(lanes * w, w, sb, lib=lib) * sb == g["aligned_bytes"]
+    assert oracle.sectors_touched(lanes * w + w, w, sb, lib=lib) * sb == g["shifted_one_float_bytes"]
+    assert oracle.sectors_touched(lanes * 32, w, sb, lib=lib) * sb == g["stride_32_bytes"]
+    assert oracle.sectors_touched(lanes * 64, w, sb, lib=lib) * sb == g["stride_32_bytes"]
+    # a repeated address is one access, a straddling one counts both sectors
+    assert oracle.sectors_touched(np.zeros(n, np.int64), w, sb, lib=lib) == 1
+    assert oracle.sectors_touched(np.array([30], np.int64), 4, sb, lib=lib) == 2
+
+
 ALL_CHECKS = [
     check_bruteforce_tiny, check_bruteforce_tile_straddling, check_identity_and_zero,
     check_closed_forms, check_library_float64, check_linearity_and_scaling,
     check_transpose_identity, check_padded_views, check_entries_rows_threads,
     check_transposed_operands, check_transposed_bruteforce,
     check_naive_intensity, check_tiled_intensity_and_traffic, check_tiled_traffic_ragged,
-    check_naive_roofline_context, check_bank_model,
+    check_naive_roofline_context, check_bank_model, check_transpose, check_sector_model,
 ]
 
 

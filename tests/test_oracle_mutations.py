@@ -15,6 +15,7 @@ import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "gemm_oracle.c")
+TRANSPOSE_SRC = os.path.join(ROOT, "oracle", "transpose_oracle.c")
 
 MUTANTS = {
     "transposed_B_index": ("(double)B[k * b_rs + j * b_cs]", "(double)B[j * b_rs + k * b_cs]"),
@@ -38,18 +39,30 @@ MUTANTS = {
     "traffic_B_tile_transposed": ("if (k < K && col < N) out[1]++; else out[3]++;",
                                   "if (k < N && col < K) out[1]++; else out[3]++;"),
     "bank_broadcast_counted": ("if (!seen)\n                distinct++;", "distinct++;"),
+    # transpose_oracle.c
+    "transpose_not_transposed": ("out[c * ld_out + r] = in[r * ld_in + c];",
+                                 "out[r * ld_out + c] = in[r * ld_in + c];"),
+    "transpose_wrong_in_ld": ("out[c * ld_out + r] = in[r * ld_in + c];",
+                              "out[c * ld_out + r] = in[r * cols + c];"),
+    "transpose_drops_last_row": ("for (int64_t r = 0; r < rows; ++r)\n        for (int64_t c = 0; c < cols; ++c)",
+                                 "for (int64_t r = 0; r < rows - 1; ++r)\n        for (int64_t c = 0; c < cols; ++c)"),
+    "sectors_end_byte_ignored": ("s <= (addr[l] + width - 1) / sector_bytes", "s <= addr[l] / sector_bytes"),
+    "sectors_duplicates_counted": ("if (!dup)\n                seen[n++] = s;", "seen[n++] = s;"),
 }
+TRANSPOSE_MUTANTS = {"transpose_not_transposed", "transpose_wrong_in_ld", "transpose_drops_last_row",
+                     "sectors_end_byte_ignored", "sectors_duplicates_counted"}
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_mutant(name, tmp_path):
     old, new = MUTANTS[name]
-    text = open(SRC).read()
+    src = TRANSPOSE_SRC if name in TRANSPOSE_MUTANTS else SRC
+    text = open(src).read()
     assert text.count(old) == 1, f"mutation anchor for {name} not unique/found"
     mutant_src = tmp_path / "mutant.c"
     mutant_src.write_text(text.replace(old, new))
     lib = str(tmp_path / "libmutant.so")
-    oracle.build(src=str(mutant_src), out=lib)
+    oracle.build(out=lib, replace={os.path.basename(src): str(mutant_src)})
     proc = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_pins.py"), lib],
                           cwd=ROOT, capture_output=True, text=True, timeout=300,
                           env={**os.environ, "PYTHONPATH": ROOT})
