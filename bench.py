@@ -17,6 +17,8 @@ Extra modes (used for counter runs under rocprofv3):
     --copy-probe-mib N  first run one device-to-device copy of N MiB, the
                         reference for scaling HBM byte counters
     --no-cpu-baseline   skip the oracle timing
+    --row transpose     time transpose_f32 on the workload's A matrix instead
+                        (metric GB/s moved, bound HBM)
     --op XY             time gemm_f32_op with op(A) = X, op(B) = Y (N or T):
                         the transposed factor is stored transposed, with a
                         compact leading dimension
@@ -85,6 +87,86 @@ def cpu_baseline(A, B, w, op_a="N", op_b="N", budget_s: float = 12.0):
                       f"triple loop, {cores} threads"}
 
 
+def bench_transpose(args, w) -> int:
+    """transpose_f32 of the workload's A matrix (M x K, leading dimension lda)
+    into an M-column output; bytes moved = 2 x 4 M K per launch."""
+    import torch
+
+    from shared_memory_tiled_amd import binding, inputs
+
+    A, _ = inputs.operands(w)
+    dev = torch.device("cuda:0")
+    a = torch.from_numpy(A.buf).to(dev)
+    out = torch.empty(w.K * w.M + 64, dtype=torch.float32, device=dev)
+    variant = None if args.variant is None else args.variant
+    targs = (w.M, w.K, a.data_ptr() + 4 * w.offset, w.lda, out.data_ptr(), w.M)
+    moved = 2.0 * 4 * w.M * w.K
+
+    def one():
+        if variant is None:
+            binding.transpose_f32(*targs)
+        else:
+            binding.transpose_f32_variant(variant, *targs)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, e0.elapsed_time(e1) / steps
+
+    if args.ladder:
+        for v in range(binding.transpose_f32_num_variants()):
+            variant = v
+            _, ms = timed(one, args.steps, 1)
+            print(json.dumps({"row": "transpose", "variant": v, "name": binding.transpose_f32_variant_name(v),
+                              "workload": w.name, "ms_per_launch": round(ms, 4),
+                              "GB_per_s": round(moved / ms / 1e6, 1)}), flush=True)
+        return 0
+    wall, ms = timed(one, args.steps, args.warmup)
+    # the same bytes through a plain device copy, for reference
+    src = a[w.offset:w.offset + w.M * w.lda]
+    dst = torch.empty_like(src)
+    _, copy_ms = timed(lambda: dst.copy_(src), args.steps, args.warmup)
+    achieved = moved / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "fp32 shared-tile transpose GB/s (bytes read + written) on MI355X",
+        "value": round(moved * args.steps / wall / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} A matrix", "rows": w.M, "cols": w.K, "ld_in": w.lda,
+                   "ld_out": w.M, "view_offset_floats": w.offset,
+                   "kernel": ("auto: " + binding.transpose_f32_variant_name(6 if (4 * w.lda) % 4096 == 0 or (4 * w.M) % 4096 == 0 else 4))
+                   if variant is None else binding.transpose_f32_variant_name(variant),
+                   "device_copy_same_bytes_GB_per_s": round(2.0 * 4 * w.M * w.lda / (copy_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        reps = 0
+        import numpy as np
+        buf = np.zeros((w.K, w.M), dtype=np.float32)
+        while time.perf_counter() - t0 < 10.0:
+            oracle.transpose_into(A.view, buf)
+            reps += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(moved * reps / dt / 1e9, 2), "unit": "GB/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"{reps} full {w.M}x{w.K} transposes in {dt:.2f} s, one thread"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +178,7 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--op", default="NN", choices=["NN", "TN", "NT", "TT"])
+    ap.add_argument("--row", default="gemm", choices=["gemm", "transpose"])
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -113,7 +196,20 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n}), flush=True)
+        del src, dst
+
     w = inputs.WORKLOADS[args.workload]
+    if args.row == "transpose":
+        return bench_transpose(args, w)
     op_a, op_b = args.op[0], args.op[1]
     if args.op == "NN":
         A, B = inputs.operands(w)
@@ -132,16 +228,6 @@ def main(argv=None) -> int:
     call_args = (w.M, w.N, w.K, a.data_ptr() + 4 * w.offset, lda,
                  b.data_ptr() + 4 * w.offset, ldb, c.data_ptr() + 4 * w.offset, w.ldc)
     flop = 2.0 * w.M * w.N * w.K
-
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n}), flush=True)
-        del src, dst
 
     def one(v):
         if args.op != "NN":

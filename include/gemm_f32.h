@@ -150,6 +150,35 @@ int gemm_f32_num_diagnostic_variants(void);
 /* Static, NUL-terminated description of a status code. */
 const char *gemm_f32_status_string(int status);
 
+/* Shared-tile transpose: out = in^T, binary32, row-major.
+ *
+ * The first page's "Bank Conflict" section transposes through a tile held
+ * in shared memory -- read rows of `in` and write rows of `out`, both
+ * coalesced, reading the tile by columns in between -- and uses it to show
+ * bank conflicts and their cures (padding, XOR swizzle).
+ *   in  is rows x cols, element (r, c) at in[r*ld_in + c],   ld_in  >= max(1, cols)
+ *   out is cols x rows, element (c, r) at out[c*ld_out + r], ld_out >= max(1, rows)
+ * out[c*ld_out + r] = in[r*ld_in + c] exactly; words of out outside the
+ * cols x rows window are never written.  Device pointers, caller-owned, 4-byte
+ * aligned; out must not overlap in.  rows or cols == 0 is a no-op.  Status
+ * codes, streams and asynchrony as for gemm_f32 (GEMM_F32_ERR_INVALID_LD for
+ * a too-small leading dimension, GEMM_F32_ERR_INVALID_VARIANT for an unknown
+ * variant).
+ * Variants: 0 naive (no LDS), 1 [32][32] tile (the page's kernel), 2 [32][33]
+ * padded tile, 3 XOR-swizzled [32][32] tile, 4 64 x 64 tile with 128-bit
+ * global and LDS accesses and an LDS layout conflict free on gfx950, 5 the
+ * same with 128 x 128 tiles, 6 variant 4 with tiles handed out in diagonal
+ * order.  transpose_f32 uses 6 when a leading dimension is a multiple of
+ * 4 KB (concurrent tiles would otherwise crowd the same memory channels),
+ * else 4.
+ */
+int transpose_f32(int64_t rows, int64_t cols, const float *in, int64_t ld_in,
+                  float *out, int64_t ld_out, void *stream);
+int transpose_f32_variant(int variant, int64_t rows, int64_t cols, const float *in,
+                          int64_t ld_in, float *out, int64_t ld_out, void *stream);
+int transpose_f32_num_variants(void);
+const char *transpose_f32_variant_name(int variant);   /* NULL if unknown */
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,8 @@ _BINDING_NAMES = {
     "gemm_f32", "gemm_f32_variant", "gemm_f32_num_variants",
     "gemm_f32_variant_name", "gemm_f32_status_string", "gemm", "GemmError",
     "gemm_f32_num_diagnostic_variants", "DIAGNOSTIC_BASE", "gemm_f32_op", "OPS",
+    "transpose_f32", "transpose_f32_variant", "transpose_f32_num_variants",
+    "transpose_f32_variant_name", "transpose",
     "VARIANTS", "load_library", "library_path",
 }
 

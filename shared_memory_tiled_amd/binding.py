@@ -66,6 +66,15 @@ def load_library():
         lib.gemm_f32_variant_name.restype = ctypes.c_char_p
         lib.gemm_f32_status_string.argtypes = [ctypes.c_int]
         lib.gemm_f32_status_string.restype = ctypes.c_char_p
+        tsig = [_i64, _i64, _vp, _i64, _vp, _i64, _vp]
+        lib.transpose_f32.argtypes = tsig
+        lib.transpose_f32.restype = ctypes.c_int
+        lib.transpose_f32_variant.argtypes = [ctypes.c_int] + tsig
+        lib.transpose_f32_variant.restype = ctypes.c_int
+        lib.transpose_f32_num_variants.argtypes = []
+        lib.transpose_f32_num_variants.restype = ctypes.c_int
+        lib.transpose_f32_variant_name.argtypes = [ctypes.c_int]
+        lib.transpose_f32_variant_name.restype = ctypes.c_char_p
         _lib = lib
         return lib
 
@@ -166,4 +175,41 @@ def gemm(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
         gemm_f32(*args, stream=stream)
     else:
         gemm_f32_variant(variant, *args, stream=stream)
+    return out
+
+
+def transpose_f32(rows, cols, src, ld_in, dst, ld_out, stream=None) -> None:
+    """dst (cols x rows) = src (rows x cols) transposed; see gemm_f32.h."""
+    lib = load_library()
+    _check(lib.transpose_f32(rows, cols, _addr(src), ld_in, _addr(dst), ld_out, _stream(stream)))
+
+
+def transpose_f32_variant(variant, rows, cols, src, ld_in, dst, ld_out, stream=None) -> None:
+    lib = load_library()
+    _check(lib.transpose_f32_variant(int(variant), rows, cols, _addr(src), ld_in, _addr(dst), ld_out,
+                                     _stream(stream)))
+
+
+def transpose_f32_num_variants() -> int:
+    return load_library().transpose_f32_num_variants()
+
+
+def transpose_f32_variant_name(variant: int) -> str | None:
+    name = load_library().transpose_f32_variant_name(int(variant))
+    return name.decode() if name is not None else None
+
+
+def transpose(X: torch.Tensor, out: torch.Tensor | None = None, variant=None, stream=None) -> torch.Tensor:
+    """Tensor form: returns ``out`` (allocated if None) = X^T for a 2-D
+    float32 row-major CUDA tensor (views with a leading dimension allowed)."""
+    rows, cols = X.shape
+    if out is None:
+        out = torch.empty((cols, rows), dtype=torch.float32, device=X.device)
+    if tuple(out.shape) != (cols, rows):
+        raise ValueError("out has the wrong shape")
+    args = (rows, cols, X, _ld(X), out, _ld(out))
+    if variant is None:
+        transpose_f32(*args, stream=stream)
+    else:
+        transpose_f32_variant(variant, *args, stream=stream)
     return out

@@ -161,3 +161,57 @@ extern "C" const char* gemm_f32_status_string(int status) {
         default: return "unknown status";
     }
 }
+
+// ---------------------------------------------------------------- transpose
+
+namespace {
+constexpr int kTransposeAuto = -1;
+
+// The default transpose: 64 x 64 tiles with 128-bit accesses, handed out in
+// diagonal order when a leading dimension is a multiple of 4 KB.  With such
+// strides, tiles handed out row by row make concurrent blocks touch addresses
+// equal modulo a large power of two (the same HBM channels); the diagonal
+// order spreads them.  With other strides the row-by-row order is kept, since
+// it lets concurrent blocks share input rows.
+int pick_transpose(int64_t ld_in, int64_t ld_out) {
+    const bool pow2ish = ((ld_in * 4) % 4096 == 0) || ((ld_out * 4) % 4096 == 0);
+    return pow2ish ? 6 : 4;
+}
+
+int run_transpose(int variant, int64_t rows, int64_t cols, const float* in, int64_t ld_in, float* out,
+                  int64_t ld_out, void* stream) {
+    if (variant != kTransposeAuto && (variant < 0 || variant >= transpose_num_variants()))
+        return GEMM_F32_ERR_INVALID_VARIANT;
+    if (rows < 0 || cols < 0) return GEMM_F32_ERR_INVALID_DIM;
+    if (ld_in < (cols > 1 ? cols : 1) || ld_out < (rows > 1 ? rows : 1)) return GEMM_F32_ERR_INVALID_LD;
+    if (rows == 0 || cols == 0) return GEMM_F32_OK;
+    if (in == nullptr || out == nullptr) return GEMM_F32_ERR_NULL_PTR;
+    if (misaligned(in) || misaligned(out)) return GEMM_F32_ERR_MISALIGNED;
+    if (rows > INT_MAX || cols > INT_MAX || !extent_fits(rows, cols, ld_in) ||
+        !extent_fits(cols, rows, ld_out))
+        return GEMM_F32_ERR_TOO_LARGE;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_F32_ERR_DEVICE;
+    if (variant == kTransposeAuto) variant = pick_transpose(ld_in, ld_out);
+    const hipError_t e = launch_transpose(variant, (int)rows, (int)cols, in, ld_in, out, ld_out,
+                                          reinterpret_cast<hipStream_t>(stream));
+    if (e == hipErrorInvalidValue) return GEMM_F32_ERR_TOO_LARGE;
+    return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
+}
+}  // namespace
+
+extern "C" int transpose_f32(int64_t rows, int64_t cols, const float* in, int64_t ld_in, float* out,
+                             int64_t ld_out, void* stream) {
+    return run_transpose(kTransposeAuto, rows, cols, in, ld_in, out, ld_out, stream);
+}
+
+extern "C" int transpose_f32_variant(int variant, int64_t rows, int64_t cols, const float* in,
+                                     int64_t ld_in, float* out, int64_t ld_out, void* stream) {
+    return run_transpose(variant, rows, cols, in, ld_in, out, ld_out, stream);
+}
+
+extern "C" int transpose_f32_num_variants(void) { return transpose_num_variants(); }
+
+extern "C" const char* transpose_f32_variant_name(int variant) {
+    return transpose_variant_name(variant);
+}

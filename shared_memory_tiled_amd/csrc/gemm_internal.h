@@ -66,6 +66,12 @@ hipError_t launch_tiled(const GemmArgs& p, hipStream_t s, int pad);
 hipError_t launch_regblock(const GemmArgs& p, hipStream_t s, int config);
 hipError_t launch_mfma(const GemmArgs& p, hipStream_t s, int config, int op_a, int op_b);
 
+// Shared-tile transpose (transpose.hip): out (cols x rows) = in^T.
+hipError_t launch_transpose(int variant, int rows, int cols, const float* in, int64_t ld_in,
+                            float* out, int64_t ld_out, hipStream_t s);
+int transpose_num_variants();
+const char* transpose_variant_name(int v);
+
 // Number of MFMA / register-blocked tile configurations and their names.
 int mfma_num_configs();
 const char* mfma_config_name(int config);

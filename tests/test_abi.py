@@ -145,3 +145,31 @@ def test_python_errors_are_raised(binding):
     with pytest.raises(binding.GemmError) as e:
         binding.gemm_f32(-1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, stream=0)
     assert e.value.status == declared_codes()["GEMM_F32_ERR_INVALID_DIM"]
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_DIM"),
+    ((4, -1, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_DIM"),
+    ((4, 6, FAKE, 5, FAKE, 4), "GEMM_F32_ERR_INVALID_LD"),
+    ((4, 6, FAKE, 6, FAKE, 3), "GEMM_F32_ERR_INVALID_LD"),
+    ((4, 6, None, 6, FAKE, 4), "GEMM_F32_ERR_NULL_PTR"),
+    ((4, 6, FAKE, 6, None, 4), "GEMM_F32_ERR_NULL_PTR"),
+    ((4, 6, FAKE + 2, 6, FAKE, 4), "GEMM_F32_ERR_MISALIGNED"),
+    ((2**31, 6, FAKE, 6, FAKE, 2**31), "GEMM_F32_ERR_TOO_LARGE"),
+    ((0, 6, None, 6, None, 1), "GEMM_F32_OK"),
+    ((6, 0, None, 1, None, 6), "GEMM_F32_OK"),
+])
+def test_transpose_validation_without_launch(lib, args, code):
+    want = declared_codes()[code]
+    assert lib.transpose_f32(*args, None) == want
+    for v in range(lib.transpose_f32_num_variants()):
+        assert lib.transpose_f32_variant(v, *args, None) == want
+
+
+def test_transpose_variants(binding, lib):
+    n = binding.transpose_f32_num_variants()
+    names = [binding.transpose_f32_variant_name(v) for v in range(n)]
+    assert n == 7 and all(names) and len(set(names)) == n
+    assert binding.transpose_f32_variant_name(n) is None
+    code = declared_codes()["GEMM_F32_ERR_INVALID_VARIANT"]
+    assert lib.transpose_f32_variant(n, 4, 4, FAKE, 4, FAKE, 4, None) == code

@@ -89,3 +89,57 @@ def test_register_path_a_stores(bk, expected):
     cpr = bk // 4
     words = [(q // cpr) * (bk + 4) + 4 * (q % cpr) for q in range(64)]
     assert degree(words, 4, 32, 8) == expected
+
+
+# ------------------------------------------------------- transpose layouts --
+
+def tile32_column_read(pad, swizzle):
+    """The page's transpose kernel reads its tile by columns: for output row
+    ty, lanes tx = 0..31 read tile[tx][ty] (lanes 32..63 do row ty + 1)."""
+    s = 32 + pad
+    return [tx * s + ((ty ^ tx) if swizzle else ty) for ty in (5, 6) for tx in range(32)]
+
+
+def test_tile32_column_reads():
+    # the page's own numbers on its 32-bank model ...
+    assert degree(tile32_column_read(0, False)[:32], 1, 32, 32) == 32
+    assert degree(tile32_column_read(1, False)[:32], 1, 32, 32) == 1
+    assert degree(tile32_column_read(0, True)[:32], 1, 32, 32) == 1
+    # ... and on gfx950's 64 banks: the unpadded column read is 16-way
+    assert degree(tile32_column_read(0, False), 1, 64, 32) == 16
+    assert degree(tile32_column_read(1, False), 1, 64, 32) == 1
+    assert degree(tile32_column_read(0, True), 1, 64, 32) == 1
+
+
+def tvec_word(T, c, chunk):
+    return c * T + 4 * (chunk ^ ((c >> 2) & 7))
+
+
+@pytest.mark.parametrize("T", [64, 128])
+def test_tile_vec_layout(T):
+    """The T x T transposes: 128-bit stores of register-transposed 4 x 4
+    blocks and 128-bit reads, all conflict free under the measured
+    geometries; the layout is a bijection onto the T^2 words."""
+    nb = T // 4
+    for p in range(nb * nb // 256):
+        for w in range(4):
+            for e in range(4):
+                stores = []
+                for t in range(64 * w, 64 * w + 64):
+                    b = t + 256 * p
+                    stores.append(tvec_word(T, 4 * (b % nb) + e, b // nb))
+                assert degree(stores, 4, 32, 8) == 1
+    for u in range(T * T // 1024):
+        for w in range(4):
+            reads = [tvec_word(T, (t + 256 * u) // nb, (t + 256 * u) % nb) for t in range(64 * w, 64 * w + 64)]
+            assert degree(reads, 4, 64, 16) == 1
+    words = sorted(tvec_word(T, c, k) + e for c in range(T) for k in range(nb) for e in range(4))
+    assert words == list(range(T * T))
+
+
+def test_scalar_pair_stores_would_conflict():
+    """Why the 64 x 64 kernel avoids scalar LDS stores: paired into one
+    instruction, two words 64 apart fall into the same one of 64 banks."""
+    lanes = [r for r in range(32)]
+    words = [w for r in lanes for w in (r, r + 64)]
+    assert oracle.bank_conflict_degree(words, 64) == 2
