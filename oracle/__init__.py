@@ -20,7 +20,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gemm_oracle.c")
-_SOURCES = [_SRC, os.path.join(_HERE, "transpose_oracle.c")]
+_SOURCES = [_SRC, os.path.join(_HERE, "transpose_oracle.c"), os.path.join(_HERE, "reduce_oracle.c")]
 _LIB = os.path.join(_HERE, "libgemm_oracle.so")
 
 _i64 = ctypes.c_int64
@@ -55,7 +55,9 @@ def load(path: str | None = None):
     if path is None and _lib is not None:
         return _lib
     p = path or _LIB
-    if not os.path.exists(p):
+    stale = path is None and os.path.exists(p) and \
+        max(os.path.getmtime(src) for src in _SOURCES) > os.path.getmtime(p)
+    if not os.path.exists(p) or stale:
         build(out=p)
     lib = ctypes.CDLL(p)
     lib.oracle_gemm_op_rows.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _fp, _i64,
@@ -81,6 +83,12 @@ def load(path: str | None = None):
     lib.oracle_transpose.restype = ctypes.c_int
     lib.oracle_sectors_touched.argtypes = [_i64, _ip, _i64, _i64]
     lib.oracle_sectors_touched.restype = _i64
+    lib.oracle_sum.argtypes = [_i64, _fp, _dp, _dp]
+    lib.oracle_sum.restype = ctypes.c_int
+    lib.oracle_tree_counts.argtypes = [_i64, _i64, ctypes.c_int, _ip]
+    lib.oracle_tree_counts.restype = ctypes.c_int
+    lib.oracle_reduce_passes.argtypes = [_i64, _i64, _ip, _i64]
+    lib.oracle_reduce_passes.restype = _i64
     if path is None:
         _lib = lib
     return lib
@@ -224,3 +232,35 @@ def sectors_touched(byte_addrs, width: int, sector_bytes: int = 32, lib=None) ->
     if n < 0:
         raise ValueError("oracle_sectors_touched rejected its arguments")
     return n
+
+
+def reduce_sum(x: np.ndarray, lib=None):
+    """(sum, sum of |x|) of a 1-D float32 array, in binary64, index order."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    s = ctypes.c_double()
+    a = ctypes.c_double()
+    ptr = x.ctypes.data_as(_fp) if x.size else ctypes.cast(ctypes.c_void_p(0), _fp)
+    rc = lib.oracle_sum(x.size, ptr, ctypes.byref(s), ctypes.byref(a))
+    if rc != 0:
+        raise ValueError("oracle_sum rejected its arguments")
+    return s.value, a.value
+
+
+def tree_counts(block: int, warp: int, version: int, lib=None) -> dict:
+    """Steps, additions and active-warp steps of one block's tree reduction."""
+    lib = lib or load()
+    out = (ctypes.c_int64 * 3)()
+    if lib.oracle_tree_counts(block, warp, version, out) != 0:
+        raise ValueError("oracle_tree_counts rejected its arguments")
+    return {"steps": out[0], "adds": out[1], "warp_steps": out[2]}
+
+
+def reduce_passes(n: int, per_block: int, lib=None):
+    """(launches, sizes after each launch) of the multi-pass scheme."""
+    lib = lib or load()
+    sizes = (ctypes.c_int64 * 64)()
+    k = int(lib.oracle_reduce_passes(n, per_block, sizes, 64))
+    if k < 0:
+        raise ValueError("oracle_reduce_passes rejected its arguments")
+    return k, [sizes[i] for i in range(k + 1)]

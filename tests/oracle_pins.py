@@ -391,6 +391,55 @@ def check_sector_model(lib):
     assert oracle.sectors_touched(np.array([30], np.int64), 4, sb, lib=lib) == 2
 
 
+# --------------------------------------------------------------- reduction --
+
+def check_sum(lib):
+    """The binary64 sum: exact on integers (closed form and int64 sums), on
+    the empty array +0, and within n 2^-53 sum|x| of the exact sum of floats
+    (math.fsum); sum|x| likewise."""
+    gen = np.random.default_rng(112)
+    s, a = oracle.reduce_sum(np.zeros(0, np.float32), lib=lib)
+    assert s == 0.0 and not math.copysign(1.0, s) < 0 and a == 0.0
+    n = 100_000
+    ramp = np.arange(1, n + 1, dtype=np.float32)
+    s, a = oracle.reduce_sum(ramp, lib=lib)
+    assert s == n * (n + 1) // 2 and a == s
+    for size in (1, 7, 1000, 65537):
+        xi = gen.integers(-3, 4, size)
+        s, a = oracle.reduce_sum(xi.astype(np.float32), lib=lib)
+        assert s == float(xi.sum()) and a == float(np.abs(xi).sum())
+    for size in (17, 4096, 300001):
+        x = gen.standard_normal(size, dtype=np.float32)
+        s, a = oracle.reduce_sum(x, lib=lib)
+        exact = math.fsum(x.astype(np.float64).tolist())
+        assert abs(s - exact) <= size * 2.0**-53 * a
+        assert abs(a - math.fsum(np.abs(x).astype(np.float64).tolist())) <= size * 2.0**-53 * a
+        assert a > 0
+
+
+def check_tree_bookkeeping(lib):
+    """The page's tree counts: 8 steps and 255 additions for 256 elements in
+    both versions, and 47 (version 0) against 12 (version 1) warp steps with
+    32-thread warps; a tree over N values always does N - 1 additions."""
+    g = _golden()["reduction"]
+    for version, key in ((0, "warp_steps_version0"), (1, "warp_steps_version1")):
+        t = oracle.tree_counts(g["block"], g["warp"], version, lib=lib)
+        assert t["steps"] == g["steps"] and t["adds"] == g["adds"] and t["warp_steps"] == g[key]
+    for b in (2, 8, 64, 1024):
+        for version in (0, 1):
+            t = oracle.tree_counts(b, 64, version, lib=lib)
+            assert t["adds"] == b - 1 and t["steps"] == int(math.log2(b))
+
+
+def check_multipass(lib):
+    """2^24 values, 256 per block: 65,536 -> 256 -> 1, three launches."""
+    g = _golden()["reduction"]
+    k, sizes = oracle.reduce_passes(g["multipass_n"], g["multipass_per_block"], lib=lib)
+    assert k == g["multipass_launches"] and sizes == g["multipass_sizes"]
+    assert oracle.reduce_passes(1, 256, lib=lib)[0] == 0
+    assert oracle.reduce_passes(257, 256, lib=lib) == (2, [257, 2, 1])
+
+
 ALL_CHECKS = [
     check_bruteforce_tiny, check_bruteforce_tile_straddling, check_identity_and_zero,
     check_closed_forms, check_library_float64, check_linearity_and_scaling,
@@ -398,6 +447,7 @@ ALL_CHECKS = [
     check_transposed_operands, check_transposed_bruteforce,
     check_naive_intensity, check_tiled_intensity_and_traffic, check_tiled_traffic_ragged,
     check_naive_roofline_context, check_bank_model, check_transpose, check_sector_model,
+    check_sum, check_tree_bookkeeping, check_multipass,
 ]
 
 

@@ -49,6 +49,19 @@ MUTANTS = {
     "sectors_end_byte_ignored": ("s <= (addr[l] + width - 1) / sector_bytes", "s <= addr[l] / sector_bytes"),
     "sectors_duplicates_counted": ("if (!dup)\n                seen[n++] = s;", "seen[n++] = s;"),
 }
+MUTANTS.update({
+    # reduce_oracle.c
+    "sum_skips_first": ("for (int64_t i = 0; i < n; ++i) {\n        s += (double)x[i];",
+                        "for (int64_t i = 1; i < n; ++i) {\n        s += (double)x[i];"),
+    "sum_single_precision": ("double s = 0.0, a = 0.0;", "float s = 0.0f; double a = 0.0;"),
+    "sum_abs_missing": ("a += fabs((double)x[i]);", "a += (double)x[i];"),
+    "tree_v0_condition": ("(tid % (2 * s) == 0)", "(tid % s == 0)"),
+    "tree_counts_threads_not_warps": ("warps_here += any;", "warps_here += 1;"),
+    "passes_floor_division": ("n = (n + per_block - 1) / per_block;", "n = n / per_block;"),
+})
+REDUCE_MUTANTS = {"sum_skips_first", "sum_single_precision", "sum_abs_missing", "tree_v0_condition",
+                  "tree_counts_threads_not_warps", "passes_floor_division"}
+REDUCE_SRC = os.path.join(ROOT, "oracle", "reduce_oracle.c")
 TRANSPOSE_MUTANTS = {"transpose_not_transposed", "transpose_wrong_in_ld", "transpose_drops_last_row",
                      "sectors_end_byte_ignored", "sectors_duplicates_counted"}
 
@@ -56,7 +69,7 @@ TRANSPOSE_MUTANTS = {"transpose_not_transposed", "transpose_wrong_in_ld", "trans
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_mutant(name, tmp_path):
     old, new = MUTANTS[name]
-    src = TRANSPOSE_SRC if name in TRANSPOSE_MUTANTS else SRC
+    src = TRANSPOSE_SRC if name in TRANSPOSE_MUTANTS else REDUCE_SRC if name in REDUCE_MUTANTS else SRC
     text = open(src).read()
     assert text.count(old) == 1, f"mutation anchor for {name} not unique/found"
     mutant_src = tmp_path / "mutant.c"
