@@ -19,6 +19,8 @@ Extra modes (used for counter runs under rocprofv3):
     --no-cpu-baseline   skip the oracle timing
     --row transpose     time transpose_f32 on the workload's A matrix instead
                         (metric GB/s moved, bound HBM)
+    --row reduce        time reduce_sum_f32 on --n uniform[-1,1) values
+                        (default 2^28; metric GB/s read, bound HBM)
     --op XY             time gemm_f32_op with op(A) = X, op(B) = Y (N or T):
                         the transposed factor is stored transposed, with a
                         compact leading dimension
@@ -85,6 +87,80 @@ def cpu_baseline(A, B, w, op_a="N", op_b="N", budget_s: float = 12.0):
             "sample": f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} product "
                       f"({rows * w.N} outputs, {flop:.3e} FLOP) in {dt:.2f} s, binary64 "
                       f"triple loop, {cores} threads"}
+
+
+def _timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, e0.elapsed_time(e1) / steps
+
+
+def bench_reduce(args) -> int:
+    """reduce_sum_f32 over n uniform[-1,1) floats resident in HBM; bytes read
+    = 4 n per launch (the partials are a few KB)."""
+    import numpy as np
+    import torch
+
+    from shared_memory_tiled_amd import binding, inputs
+
+    n = args.n
+    x_host = inputs.random_matrix(inputs.rng(100, 0), 1, n, "uniform").reshape(-1)
+    x = torch.from_numpy(x_host).cuda()
+    out = torch.empty(1, device="cuda")
+    read = 4.0 * n
+
+    def make(v):
+        vv = binding.REDUCE_DEFAULT if v is None else v
+        wsb = binding.reduce_sum_f32_workspace_size(vv, n)
+        ws = torch.empty(max(wsb // 4, 1), device="cuda")
+        if v is None:
+            return lambda: binding.reduce_sum_f32(n, x, out, ws, wsb)
+        return lambda: binding.reduce_sum_f32_variant(v, n, x, out, ws, wsb)
+
+    if args.ladder:
+        for v in range(binding.reduce_sum_f32_num_variants()):
+            _, ms = _timed(make(v), args.steps, 1)
+            print(json.dumps({"row": "reduce", "variant": v, "name": binding.reduce_sum_f32_variant_name(v),
+                              "n": n, "ms_per_launch": round(ms, 4), "GB_per_s": round(read / ms / 1e6, 1)}),
+                  flush=True)
+        return 0
+    wall, ms = _timed(make(args.variant), args.steps, args.warmup)
+    _, torch_ms = _timed(lambda: torch.sum(x), args.steps, args.warmup)
+    achieved = read / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "fp32 sum reduction GB/s (bytes read) on MI355X",
+        "value": round(read * args.steps / wall / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"sum of {n} uniform[-1,1) floats", "n": n,
+                   "kernel": binding.reduce_sum_f32_variant_name(binding.REDUCE_DEFAULT if args.variant is None
+                                                                 else args.variant),
+                   "torch_sum_same_data_GB_per_s": round(read / (torch_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10.0:
+            oracle.reduce_sum(x_host)
+            reps += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(read * reps / dt / 1e9, 2), "unit": "GB/s", "cores": 1,
+                                "kind": "oracle", "sample": f"{reps} full sums of {n} values in {dt:.2f} s, one thread"}
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 def bench_transpose(args, w) -> int:
@@ -178,7 +254,8 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--op", default="NN", choices=["NN", "TN", "NT", "TT"])
-    ap.add_argument("--row", default="gemm", choices=["gemm", "transpose"])
+    ap.add_argument("--row", default="gemm", choices=["gemm", "transpose", "reduce"])
+    ap.add_argument("--n", type=int, default=2 ** 28, help="values summed by --row reduce")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -207,6 +284,8 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n}), flush=True)
         del src, dst
 
+    if args.row == "reduce":
+        return bench_reduce(args)
     w = inputs.WORKLOADS[args.workload]
     if args.row == "transpose":
         return bench_transpose(args, w)

@@ -66,6 +66,7 @@ extern "C" {
 #define GEMM_F32_ERR_LAUNCH          7  /* the HIP runtime rejected the launch       */
 #define GEMM_F32_ERR_DEVICE          8  /* no usable current HIP device              */
 #define GEMM_F32_ERR_INVALID_OP      9  /* op_a or op_b is neither N nor T           */
+#define GEMM_F32_ERR_WORKSPACE      10  /* workspace smaller than required            */
 
 /* Kernel ladder.  Each rung computes the same product; each is tested against
  * the oracle and against the rung below it.
@@ -178,6 +179,38 @@ int transpose_f32_variant(int variant, int64_t rows, int64_t cols, const float *
                           int64_t ld_in, float *out, int64_t ld_out, void *stream);
 int transpose_f32_num_variants(void);
 const char *transpose_f32_variant_name(int variant);   /* NULL if unknown */
+
+/* Sum reduction: *out = x[0] + ... + x[n-1], binary32.
+ *
+ * The first page's "Reduction" section folds an array into one value with a
+ * tree in shared memory, improves the tree step by step (interleaved, then
+ * sequential addressing, then warp shuffles for the last steps, then one
+ * atomic per block), and reduces large arrays in several passes (each block
+ * folds its values to one partial, then the partials are folded again).
+ *   x          device pointer to n floats (4-byte aligned), read only
+ *   out        device pointer to one float, overwritten (+0 when n == 0)
+ *   workspace  device memory of at least reduce_sum_f32_workspace_size()
+ *              bytes for the partials (NULL allowed when that size is 0);
+ *              owned by the caller, contents undefined after the call; it
+ *              must not overlap x or out
+ * The summation order depends on the variant and on n only, except for
+ * variant 3, whose block sums are added by float atomics in arrival order:
+ * its last bits may vary from run to run.  The error is bounded by
+ * (longest sequential chain + tree depth) * 2^-24 * sum |x_i|; the result is
+ * exact when every partial sum is an integer below 2^24 in magnitude.
+ * Variants: 0 interleaved tree (tid % 2s), 1 sequential addressing (tid < s),
+ * 2 sequential + wave shuffles for the last six steps, 3 one atomic add per
+ * block, 4 grid-stride 128-bit loads + wave shuffles + a one-block second
+ * pass (the default).  Statuses as for gemm_f32, plus
+ * GEMM_F32_ERR_WORKSPACE.
+ */
+int64_t reduce_sum_f32_workspace_size(int variant, int64_t n);   /* bytes; -1 if invalid */
+int reduce_sum_f32(int64_t n, const float *x, float *out,
+                   void *workspace, int64_t workspace_bytes, void *stream);
+int reduce_sum_f32_variant(int variant, int64_t n, const float *x, float *out,
+                           void *workspace, int64_t workspace_bytes, void *stream);
+int reduce_sum_f32_num_variants(void);
+const char *reduce_sum_f32_variant_name(int variant);  /* NULL if unknown */
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,8 @@ _BINDING_NAMES = {
     "gemm_f32_num_diagnostic_variants", "DIAGNOSTIC_BASE", "gemm_f32_op", "OPS",
     "transpose_f32", "transpose_f32_variant", "transpose_f32_num_variants",
     "transpose_f32_variant_name", "transpose",
+    "reduce_sum_f32", "reduce_sum_f32_variant", "reduce_sum_f32_num_variants",
+    "reduce_sum_f32_variant_name", "reduce_sum_f32_workspace_size", "reduce_sum",
     "VARIANTS", "load_library", "library_path",
 }
 

@@ -75,6 +75,17 @@ def load_library():
         lib.transpose_f32_num_variants.restype = ctypes.c_int
         lib.transpose_f32_variant_name.argtypes = [ctypes.c_int]
         lib.transpose_f32_variant_name.restype = ctypes.c_char_p
+        lib.reduce_sum_f32_workspace_size.argtypes = [ctypes.c_int, _i64]
+        lib.reduce_sum_f32_workspace_size.restype = _i64
+        rsig = [_i64, _vp, _vp, _vp, _i64, _vp]
+        lib.reduce_sum_f32.argtypes = rsig
+        lib.reduce_sum_f32.restype = ctypes.c_int
+        lib.reduce_sum_f32_variant.argtypes = [ctypes.c_int] + rsig
+        lib.reduce_sum_f32_variant.restype = ctypes.c_int
+        lib.reduce_sum_f32_num_variants.argtypes = []
+        lib.reduce_sum_f32_num_variants.restype = ctypes.c_int
+        lib.reduce_sum_f32_variant_name.argtypes = [ctypes.c_int]
+        lib.reduce_sum_f32_variant_name.restype = ctypes.c_char_p
         _lib = lib
         return lib
 
@@ -212,4 +223,49 @@ def transpose(X: torch.Tensor, out: torch.Tensor | None = None, variant=None, st
         transpose_f32(*args, stream=stream)
     else:
         transpose_f32_variant(variant, *args, stream=stream)
+    return out
+
+
+REDUCE_DEFAULT = 4
+
+
+def reduce_sum_f32_workspace_size(variant: int, n: int) -> int:
+    return load_library().reduce_sum_f32_workspace_size(int(variant), int(n))
+
+
+def reduce_sum_f32(n, x, out, workspace, workspace_bytes, stream=None) -> None:
+    """*out = sum of x[0 .. n-1] (device pointers); see gemm_f32.h."""
+    lib = load_library()
+    _check(lib.reduce_sum_f32(n, _addr(x), _addr(out), _addr(workspace), workspace_bytes, _stream(stream)))
+
+
+def reduce_sum_f32_variant(variant, n, x, out, workspace, workspace_bytes, stream=None) -> None:
+    lib = load_library()
+    _check(lib.reduce_sum_f32_variant(int(variant), n, _addr(x), _addr(out), _addr(workspace),
+                                      workspace_bytes, _stream(stream)))
+
+
+def reduce_sum_f32_num_variants() -> int:
+    return load_library().reduce_sum_f32_num_variants()
+
+
+def reduce_sum_f32_variant_name(variant: int) -> str | None:
+    name = load_library().reduce_sum_f32_variant_name(int(variant))
+    return name.decode() if name is not None else None
+
+
+def reduce_sum(x: torch.Tensor, variant=None, stream=None) -> torch.Tensor:
+    """Tensor form: a one-element float32 CUDA tensor holding the sum of the
+    contiguous float32 tensor x; the workspace is allocated with torch."""
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 tensor")
+    n = x.numel()
+    v = REDUCE_DEFAULT if variant is None else int(variant)
+    out = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws_bytes = reduce_sum_f32_workspace_size(v, n)
+    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=x.device)
+    if variant is None:
+        reduce_sum_f32(n, x, out, ws, ws_bytes, stream=stream)
+    else:
+        reduce_sum_f32_variant(v, n, x, out, ws, ws_bytes, stream=stream)
     return out

@@ -158,6 +158,7 @@ extern "C" const char* gemm_f32_status_string(int status) {
         case GEMM_F32_ERR_LAUNCH: return "kernel launch rejected by the HIP runtime";
         case GEMM_F32_ERR_DEVICE: return "no usable current HIP device";
         case GEMM_F32_ERR_INVALID_OP: return "invalid op: op_a and op_b must be GEMM_F32_OP_N or GEMM_F32_OP_T";
+        case GEMM_F32_ERR_WORKSPACE: return "workspace smaller than reduce_sum_f32_workspace_size()";
         default: return "unknown status";
     }
 }
@@ -215,3 +216,47 @@ extern "C" int transpose_f32_num_variants(void) { return transpose_num_variants(
 extern "C" const char* transpose_f32_variant_name(int variant) {
     return transpose_variant_name(variant);
 }
+
+// ---------------------------------------------------------------- reduction
+
+namespace {
+constexpr int kReduceDefault = 4;
+
+int run_reduce(int variant, int64_t n, const float* x, float* out, void* workspace, int64_t ws_bytes,
+               void* stream) {
+    if (variant < 0 || variant >= reduce_num_variants()) return GEMM_F32_ERR_INVALID_VARIANT;
+    if (n < 0 || ws_bytes < 0) return GEMM_F32_ERR_INVALID_DIM;
+    if (out == nullptr || (n > 0 && x == nullptr)) return GEMM_F32_ERR_NULL_PTR;
+    if (misaligned(out) || (n > 0 && misaligned(x))) return GEMM_F32_ERR_MISALIGNED;
+    if (n > ((int64_t)1 << 39)) return GEMM_F32_ERR_TOO_LARGE;
+    const int64_t need = 4 * reduce_workspace_floats(variant, n);
+    if (ws_bytes < need) return GEMM_F32_ERR_WORKSPACE;
+    if (need > 0 && workspace == nullptr) return GEMM_F32_ERR_NULL_PTR;
+    if (need > 0 && misaligned(workspace)) return GEMM_F32_ERR_MISALIGNED;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_F32_ERR_DEVICE;
+    const hipError_t e = launch_reduce(variant, n, x, out, static_cast<float*>(workspace),
+                                       reinterpret_cast<hipStream_t>(stream));
+    if (e == hipErrorInvalidValue) return GEMM_F32_ERR_TOO_LARGE;
+    return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
+}
+}  // namespace
+
+extern "C" int64_t reduce_sum_f32_workspace_size(int variant, int64_t n) {
+    if (variant < 0 || variant >= reduce_num_variants() || n < 0) return -1;
+    return 4 * reduce_workspace_floats(variant, n);
+}
+
+extern "C" int reduce_sum_f32(int64_t n, const float* x, float* out, void* workspace,
+                              int64_t workspace_bytes, void* stream) {
+    return run_reduce(kReduceDefault, n, x, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int reduce_sum_f32_variant(int variant, int64_t n, const float* x, float* out,
+                                      void* workspace, int64_t workspace_bytes, void* stream) {
+    return run_reduce(variant, n, x, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int reduce_sum_f32_num_variants(void) { return reduce_num_variants(); }
+
+extern "C" const char* reduce_sum_f32_variant_name(int variant) { return reduce_variant_name(variant); }

@@ -72,6 +72,12 @@ hipError_t launch_transpose(int variant, int rows, int cols, const float* in, in
 int transpose_num_variants();
 const char* transpose_variant_name(int v);
 
+// Sum reduction (reduce.hip): *out = sum of x[0 .. n-1].
+hipError_t launch_reduce(int variant, int64_t n, const float* x, float* out, float* ws, hipStream_t s);
+int64_t reduce_workspace_floats(int variant, int64_t n);
+int reduce_num_variants();
+const char* reduce_variant_name(int v);
+
 // Number of MFMA / register-blocked tile configurations and their names.
 int mfma_num_configs();
 const char* mfma_config_name(int config);

@@ -173,3 +173,33 @@ def test_transpose_variants(binding, lib):
     assert binding.transpose_f32_variant_name(n) is None
     code = declared_codes()["GEMM_F32_ERR_INVALID_VARIANT"]
     assert lib.transpose_f32_variant(n, 4, 4, FAKE, 4, FAKE, 4, None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, FAKE, FAKE, FAKE, 4096), "GEMM_F32_ERR_INVALID_DIM"),
+    ((10, FAKE, None, FAKE, 4096), "GEMM_F32_ERR_NULL_PTR"),
+    ((10, None, FAKE, FAKE, 4096), "GEMM_F32_ERR_NULL_PTR"),
+    ((10, FAKE + 2, FAKE, FAKE, 4096), "GEMM_F32_ERR_MISALIGNED"),
+    ((10**6, FAKE, FAKE, FAKE, 4), "GEMM_F32_ERR_WORKSPACE"),
+    ((10**6, FAKE, FAKE, None, 10**8), "GEMM_F32_ERR_NULL_PTR"),
+    ((2**40, FAKE, FAKE, FAKE, 2**45), "GEMM_F32_ERR_TOO_LARGE"),
+])
+def test_reduce_validation_without_launch(lib, args, code):
+    want = declared_codes()[code]
+    n, x, out, ws, wsb = args
+    for v in (0, 1, 2, 4):
+        assert lib.reduce_sum_f32_variant(v, n, x, out, ws, wsb, None) == want, v
+
+
+def test_reduce_workspace_sizes(binding, lib):
+    # the page's multi-pass sizes: 2^24 values -> 65,536 + 256 partials kept
+    assert binding.reduce_sum_f32_workspace_size(1, 2**24) == 4 * (65536 + 256)
+    assert binding.reduce_sum_f32_workspace_size(0, 256) == 0
+    assert binding.reduce_sum_f32_workspace_size(2, 257) == 4 * 2
+    assert binding.reduce_sum_f32_workspace_size(3, 10**9) == 0
+    assert binding.reduce_sum_f32_workspace_size(4, 1) == 4 * 1024
+    assert binding.reduce_sum_f32_workspace_size(9, 10) == -1
+    assert binding.reduce_sum_f32_workspace_size(1, -1) == -1
+    n = binding.reduce_sum_f32_num_variants()
+    names = [binding.reduce_sum_f32_variant_name(v) for v in range(n)]
+    assert n == 5 and all(names) and len(set(names)) == n and binding.reduce_sum_f32_variant_name(n) is None
