@@ -20,13 +20,15 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gemm_oracle.c")
-_SOURCES = [_SRC, os.path.join(_HERE, "transpose_oracle.c"), os.path.join(_HERE, "reduce_oracle.c")]
+_SOURCES = [_SRC, os.path.join(_HERE, "transpose_oracle.c"), os.path.join(_HERE, "reduce_oracle.c"),
+            os.path.join(_HERE, "gemm16_oracle.c")]
 _LIB = os.path.join(_HERE, "libgemm_oracle.so")
 
 _i64 = ctypes.c_int64
 _fp = ctypes.POINTER(ctypes.c_float)
 _dp = ctypes.POINTER(ctypes.c_double)
 _ip = ctypes.POINTER(ctypes.c_int64)
+_hp = ctypes.POINTER(ctypes.c_uint16)
 
 _lib = None
 
@@ -89,6 +91,14 @@ def load(path: str | None = None):
     lib.oracle_tree_counts.restype = ctypes.c_int
     lib.oracle_reduce_passes.argtypes = [_i64, _i64, _ip, _i64]
     lib.oracle_reduce_passes.restype = _i64
+    lib.oracle_decode16_array.argtypes = [ctypes.c_int, _i64, _hp, _dp]
+    lib.oracle_decode16_array.restype = ctypes.c_int
+    lib.oracle_gemm16_rows.argtypes = [ctypes.c_int, _i64, _i64, _i64, _hp, _i64, _hp, _i64,
+                                       _dp, _i64, _dp, _i64, _i64, _i64, ctypes.c_int]
+    lib.oracle_gemm16_rows.restype = ctypes.c_int
+    lib.oracle_gemm16_entries.argtypes = [ctypes.c_int, _i64, _i64, _i64, _hp, _i64, _hp, _i64,
+                                          _i64, _ip, _ip, _dp, _dp]
+    lib.oracle_gemm16_entries.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -264,3 +274,84 @@ def reduce_passes(n: int, per_block: int, lib=None):
     if k < 0:
         raise ValueError("oracle_reduce_passes rejected its arguments")
     return k, [sizes[i] for i in range(k + 1)]
+
+
+FORMATS16 = {"bf16": 0, "f16": 1}
+
+
+def _fmt16(fmt) -> int:
+    if fmt in FORMATS16:
+        return FORMATS16[fmt]
+    if fmt in (0, 1):
+        return int(fmt)
+    raise ValueError(f"16-bit format must be 'bf16' or 'f16', not {fmt!r}")
+
+
+def _matrix16_arg(X: np.ndarray):
+    """(pointer, leading dimension) of a 2-D uint16 row-major (possibly
+    padded) view holding 16-bit patterns."""
+    if X.dtype != np.uint16 or X.ndim != 2:
+        raise TypeError("16-bit oracle operands must be 2-D uint16 arrays of bit patterns")
+    if X.size == 0:
+        return ctypes.cast(ctypes.c_void_p(X.ctypes.data), _hp), max(X.shape[1], 1)
+    if X.shape[1] > 1 and X.strides[1] != 2:
+        raise ValueError("oracle operands need unit column stride")
+    if X.strides[0] % 2:
+        raise ValueError("row stride must be a whole number of elements")
+    ld = X.strides[0] // 2 if X.shape[0] > 1 else max(X.shape[1], 1)
+    return X.ctypes.data_as(_hp), max(ld, X.shape[1], 1)
+
+
+def decode16(fmt, bits, lib=None) -> np.ndarray:
+    """Values (binary64) of an array of 16-bit patterns."""
+    lib = lib or load()
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.zeros(b.shape, dtype=np.float64)
+    if b.size and lib.oracle_decode16_array(_fmt16(fmt), b.size, b.ctypes.data_as(_hp),
+                                            out.ctypes.data_as(_dp)) != 0:
+        raise ValueError("oracle_decode16_array rejected its arguments")
+    return out
+
+
+def gemm16(fmt, A: np.ndarray, B: np.ndarray, threads: int = 1, rows=None, lib=None):
+    """Returns (C, S) in binary64 for 16-bit A (M x K) and B (K x N) given as
+    uint16 bit patterns of format ``fmt`` ('bf16' or 'f16')."""
+    lib = lib or load()
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    C = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    pa, lda = _matrix16_arg(A)
+    pb, ldb = _matrix16_arg(B)
+    r0, r1 = (0, M) if rows is None else rows
+    rc = lib.oracle_gemm16_rows(_fmt16(fmt), M, N, K, pa, lda, pb, ldb,
+                                C.ctypes.data_as(_dp), max(N, 1), S.ctypes.data_as(_dp), max(N, 1),
+                                r0, r1, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle 16-bit product rejected its arguments (rc={rc})")
+    return C, S
+
+
+def gemm16_entries(fmt, A: np.ndarray, B: np.ndarray, ii, jj, lib=None):
+    """Returns (c, s) for the entries (ii[t], jj[t]) of the 16-bit product."""
+    lib = lib or load()
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    if ii.shape != jj.shape or ii.ndim != 1:
+        raise ValueError("ii and jj must be 1-D of equal length")
+    c = np.zeros(ii.shape[0], dtype=np.float64)
+    s = np.zeros(ii.shape[0], dtype=np.float64)
+    pa, lda = _matrix16_arg(A)
+    pb, ldb = _matrix16_arg(B)
+    rc = lib.oracle_gemm16_entries(_fmt16(fmt), M, N, K, pa, lda, pb, ldb, ii.shape[0],
+                                   ii.ctypes.data_as(_ip), jj.ctypes.data_as(_ip),
+                                   c.ctypes.data_as(_dp), s.ctypes.data_as(_dp))
+    if rc != 0:
+        raise ValueError(f"oracle 16-bit entries rejected their arguments (rc={rc})")
+    return c, s

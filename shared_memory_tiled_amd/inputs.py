@@ -20,6 +20,11 @@ general sizes with leading dimensions):
 
 "uniform[-1,1)" is 2u - 1 with u drawn as binary32 on the 2^-24 grid, which
 is exact in binary32 and never reaches +1.
+
+The mixed-precision product takes the same workloads in a 16-bit format
+(bfloat16 or binary16): the binary32 data above rounded to the format,
+nearest-even, and held as uint16 bit patterns; pads and guards hold the
+format's quiet NaN.
 """
 from __future__ import annotations
 
@@ -156,3 +161,49 @@ def sample_pairs(M: int, N: int, count: int, gen: np.random.Generator,
             ii.append(i)
             jj.append(j)
     return np.asarray(ii, dtype=np.int64), np.asarray(jj, dtype=np.int64)
+
+
+# 16-bit formats: name -> quiet-NaN pattern used for padding.
+NAN16 = {"bf16": np.uint16(0x7FC0), "f16": np.uint16(0x7E00)}
+
+
+def to16(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Bit patterns (uint16) of the binary32 array ``x`` rounded to ``fmt``,
+    nearest-even.  binary16 uses numpy's conversion; for bfloat16 the lower
+    half of each binary32 pattern is rounded away (finite inputs only)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if fmt == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    if fmt == "bf16":
+        if not np.all(np.isfinite(x)):
+            raise ValueError("bfloat16 rounding here takes finite values only")
+        bits = x.view(np.uint32).astype(np.uint64)
+        return ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16).astype(np.uint16)
+    raise ValueError(f"unknown 16-bit format {fmt!r}")
+
+
+def padded16(bits: np.ndarray, ld: int, offset: int, fmt: str, guard: int = GUARD_WORDS) -> Padded:
+    """Copy the uint16 matrix ``bits`` into a padded uint16 buffer whose pad
+    and guard elements hold the format's quiet NaN."""
+    rows, cols = bits.shape
+    if ld < max(cols, 1):
+        raise ValueError("leading dimension smaller than the column count")
+    buf = np.empty(offset + rows * ld + guard, dtype=np.uint16)
+    buf[:] = NAN16[fmt]
+    p = Padded(buf, rows, cols, ld, offset)
+    if rows:
+        p.view[:, :] = bits
+    return p
+
+
+def operands16(w: Workload, fmt: str, dist: str | None = None, offset: int | None = None):
+    """(A, B) of workload ``w`` rounded to ``fmt``, as padded uint16 host
+    buffers with the workload's leading dimensions (in elements), and the
+    binary32 data they were rounded from (dense)."""
+    d = dist or w.dist
+    off = w.offset if offset is None else offset
+    sa, sb = (2, 3) if d == "int" else (0, 1)
+    A32 = random_matrix(rng(w.index, sa), w.M, w.K, d)
+    B32 = random_matrix(rng(w.index, sb), w.K, w.N, d)
+    return (padded16(to16(A32, fmt), w.lda, off, fmt), padded16(to16(B32, fmt), w.ldb, off, fmt),
+            A32, B32)

@@ -439,6 +439,140 @@ def check_multipass(lib):
     assert oracle.reduce_passes(1, 256, lib=lib)[0] == 0
     assert oracle.reduce_passes(257, 256, lib=lib) == (2, [257, 2, 1])
 
+# ------------------------------------------- 16-bit inputs, fp32 result --
+
+def _widen16(bits, fmt):
+    """binary32 values of 16-bit patterns by numpy's own decoding: binary16
+    through numpy's float16, bfloat16 as the upper half of a binary32."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    if fmt == "f16":
+        with np.errstate(invalid="ignore"):
+            return bits.view(np.float16).astype(np.float32)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _encode_exact16(x, fmt):
+    """Patterns of values that are exact in the format (checked)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if fmt == "f16":
+        b = x.astype(np.float16).view(np.uint16)
+    else:
+        w = x.view(np.uint32)
+        assert np.all((w & 0xFFFF) == 0)
+        b = (w >> 16).astype(np.uint16)
+    assert np.array_equal(_widen16(b, fmt), x)
+    return b
+
+
+def _finite16(gen, shape, fmt):
+    """Random finite 16-bit patterns (every sign, exponent and fraction)."""
+    b = gen.integers(0, 65536, size=shape).astype(np.uint16)
+    exp_all_ones = (b & 0x7F80) == 0x7F80 if fmt == "bf16" else (b & 0x7C00) == 0x7C00
+    b[exp_all_ones] &= np.uint16(0xBFFF)         # clear the top exponent bit
+    return b
+
+
+def check_decode16_all_patterns(lib):
+    """Every one of the 65,536 patterns of both formats decodes to numpy's
+    value for it (NaN to NaN, each zero with its sign), and a few values the
+    formats' definitions fix: 1, the largest finite and the smallest
+    subnormal of each."""
+    b = np.arange(65536, dtype=np.uint16)
+    for fmt in ("f16", "bf16"):
+        got = oracle.decode16(fmt, b, lib=lib)
+        with np.errstate(invalid="ignore"):
+            ref = _widen16(b, fmt).astype(np.float64)
+        assert np.array_equal(got, ref, equal_nan=True), fmt
+        assert np.array_equal(np.signbit(got), np.signbit(ref)), fmt
+    known = {("f16", 0x3C00): 1.0, ("f16", 0x7BFF): 65504.0, ("f16", 0x0001): 2.0**-24,
+             ("f16", 0x0400): 2.0**-14, ("f16", 0xC000): -2.0,
+             ("bf16", 0x3F80): 1.0, ("bf16", 0x7F7F): (2 - 2.0**-7) * 2.0**127,
+             ("bf16", 0x0001): 2.0**-133, ("bf16", 0x0080): 2.0**-126, ("bf16", 0xC000): -2.0}
+    for (fmt, bits), v in known.items():
+        assert oracle.decode16(fmt, np.array([bits], np.uint16), lib=lib)[0] == v, (fmt, hex(bits))
+
+
+def check_gemm16_equals_fp32_oracle(lib):
+    """Random finite patterns of both formats, at tile-straddling shapes and in
+    padded offset views: the 16-bit product equals the fp32 oracle on the same
+    values widened to binary32, bit for bit, for C and S; row bands, thread
+    counts and single entries agree with the full product."""
+    gen = np.random.default_rng(120)
+    for fmt in ("bf16", "f16"):
+        for (M, N, K) in ((1, 1, 1), (17, 33, 65), (64, 31, 129), (33, 64, 0)):
+            A = _finite16(gen, (M, K), fmt)
+            B = _finite16(gen, (K, N), fmt)
+            C, S = oracle.gemm16(fmt, A, B, lib=lib)
+            C32, S32 = oracle.gemm(_widen16(A, fmt), _widen16(B, fmt), lib=lib)
+            assert np.array_equal(C, C32) and np.array_equal(S, S32), (fmt, M, N, K)
+            # padded views with an odd element offset
+            Ap = np.full(3 + M * (K + 5) + 7, 0x7E00, np.uint16)
+            Av = Ap[3:3 + M * (K + 5)].reshape(M, K + 5)[:, :K]
+            Av[:, :] = A
+            Bp = np.full(1 + K * (N + 2) + 7, 0x7E00, np.uint16)
+            Bv = Bp[1:1 + K * (N + 2)].reshape(K, N + 2)[:, :N] if K else B
+            if K:
+                Bv[:, :] = B
+            Cv, Sv = oracle.gemm16(fmt, Av, Bv, threads=3, lib=lib)
+            assert np.array_equal(Cv, C) and np.array_equal(Sv, S), (fmt, M, N, K)
+            if M > 2 and N:
+                Cb, _ = oracle.gemm16(fmt, A, B, rows=(1, M - 1), lib=lib)
+                assert np.array_equal(Cb[1:M - 1], C[1:M - 1]) and np.all(Cb[0] == 0)
+                ii = gen.integers(0, M, 20)
+                jj = gen.integers(0, N, 20)
+                c, sv = oracle.gemm16_entries(fmt, Av, Bv, ii, jj, lib=lib)
+                assert np.array_equal(c, C[ii, jj]) and np.array_equal(sv, S[ii, jj])
+
+
+def check_gemm16_bruteforce(lib):
+    """Integers -9..9 (exact in both formats), every M, N in {1, 2, 3, 5, 8}
+    and K in {0, 1, 2, 3, 5, 8}: exact equality with Python-int brute force."""
+    gen = np.random.default_rng(121)
+    sizes = [1, 2, 3, 5, 8]
+    for fmt in ("bf16", "f16"):
+        for M, N, K in itertools.product(sizes, sizes, [0] + sizes):
+            A = _ints(gen, M, K, -9, 9)
+            B = _ints(gen, K, N, -9, 9)
+            C, S = oracle.gemm16(fmt, _encode_exact16(A, fmt), _encode_exact16(B, fmt), lib=lib)
+            Ce, Se = _py_product(A, B)
+            assert np.array_equal(C, np.array(Ce, dtype=np.float64).reshape(M, N)), (fmt, M, N, K)
+            assert np.array_equal(S, np.array(Se, dtype=np.float64).reshape(M, N)), (fmt, M, N, K)
+
+
+def check_gemm16_extremes(lib):
+    """The formats' range ends inside the product: binary16's largest finite
+    value 65504 squared and summed K times, its smallest subnormal 2^-24
+    squared (2^-48 per term, far below binary16 but exact in the sum);
+    bfloat16's largest finite times 2^-126 and its smallest subnormal 2^-133
+    times 2^100; all-ones gives K; signs of mixed terms."""
+    K = 37
+    for fmt, big, tiny, one, exp in (("f16", 0x7BFF, 0x0001, 0x3C00, None),
+                                     ("bf16", 0x7F7F, 0x0001, 0x3F80, (0x0080, 0x71 << 7))):
+        A = np.full((2, K), one, np.uint16)
+        B = np.full((K, 3), one, np.uint16)
+        C, S = oracle.gemm16(fmt, A, B, lib=lib)
+        assert np.all(C == K) and np.all(S == K)
+        if fmt == "f16":
+            A[0, :] = big
+            B[:, 0] = big
+            A[1, :] = tiny
+            B[:, 1] = tiny
+            C, _ = oracle.gemm16(fmt, A, B, lib=lib)
+            assert C[0, 0] == K * 65504.0**2 and C[1, 1] == K * 2.0**-48 and C[0, 1] == K * 65504.0 * 2.0**-24
+        else:
+            A[0, :] = big
+            B[:, 0] = exp[0]                      # 2^-126
+            A[1, :] = tiny                        # 2^-133
+            B[:, 1] = exp[1]                      # 2^(0x71 - 127) = 2^-14
+            C, _ = oracle.gemm16(fmt, A, B, lib=lib)
+            assert C[0, 0] == K * (2 - 2.0**-7) * 2.0 and C[1, 1] == K * 2.0**-147
+        A = np.full((1, 4), one, np.uint16)
+        A[0, 1] |= np.uint16(0x8000)              # -1
+        B = np.full((4, 1), one, np.uint16)
+        B[3, 0] |= np.uint16(0x8000)
+        C, S = oracle.gemm16(fmt, A, B, lib=lib)
+        assert C[0, 0] == 0.0 and S[0, 0] == 4.0     # 1 - 1 + 1 - 1
+
 
 ALL_CHECKS = [
     check_bruteforce_tiny, check_bruteforce_tile_straddling, check_identity_and_zero,
@@ -448,6 +582,8 @@ ALL_CHECKS = [
     check_naive_intensity, check_tiled_intensity_and_traffic, check_tiled_traffic_ragged,
     check_naive_roofline_context, check_bank_model, check_transpose, check_sector_model,
     check_sum, check_tree_bookkeeping, check_multipass,
+    check_decode16_all_patterns, check_gemm16_equals_fp32_oracle, check_gemm16_bruteforce,
+    check_gemm16_extremes,
 ]
 
 

@@ -1,7 +1,7 @@
 """Plants plausible mistakes in copies of the oracle (on the CPU) and checks
 that the pins catch every one of them.
 
-Each mutant is a textual edit of ``oracle/gemm_oracle.c`` compiled into a
+Each mutant is a textual edit of one oracle source compiled into a
 temporary library; the pin battery runs in a subprocess (a mutant may read out
 of bounds) and must report at least one failure or die.
 """
@@ -62,6 +62,21 @@ MUTANTS.update({
 REDUCE_MUTANTS = {"sum_skips_first", "sum_single_precision", "sum_abs_missing", "tree_v0_condition",
                   "tree_counts_threads_not_warps", "passes_floor_division"}
 REDUCE_SRC = os.path.join(ROOT, "oracle", "reduce_oracle.c")
+MUTANTS.update({
+    # gemm16_oracle.c
+    "bf16_bias_off": ("v = ldexp(1.0 + f / 128.0, e - 127);", "v = ldexp(1.0 + f / 128.0, e - 126);"),
+    "f16_subnormal_as_normal": ("v = ldexp((double)f, -24);", "v = ldexp(1.0 + f / 1024.0, -14);"),
+    "f16_fraction_width": ("v = ldexp(1.0 + f / 1024.0, e - 15);", "v = ldexp(1.0 + f / 512.0, e - 15);"),
+    "decode16_sign_ignored": ("return neg ? -v : v;", "return v;"),
+    "gemm16_drops_last_term": ("for (int64_t k = 0; k < K; ++k) {\n        const double prod",
+                               "for (int64_t k = 0; k < K - 1; ++k) {\n        const double prod"),
+    "gemm16_B_uses_lda": ("val[B[k * ldb + j]]", "val[B[k * lda + j]]"),
+    "gemm16_format_ignored": ("double *val = decode_table(format);\n    int64_t rows",
+                              "double *val = decode_table(FMT_BF16);\n    int64_t rows"),
+})
+GEMM16_MUTANTS = {"bf16_bias_off", "f16_subnormal_as_normal", "f16_fraction_width", "decode16_sign_ignored",
+                  "gemm16_drops_last_term", "gemm16_B_uses_lda", "gemm16_format_ignored"}
+GEMM16_SRC = os.path.join(ROOT, "oracle", "gemm16_oracle.c")
 TRANSPOSE_MUTANTS = {"transpose_not_transposed", "transpose_wrong_in_ld", "transpose_drops_last_row",
                      "sectors_end_byte_ignored", "sectors_duplicates_counted"}
 
@@ -69,7 +84,8 @@ TRANSPOSE_MUTANTS = {"transpose_not_transposed", "transpose_wrong_in_ld", "trans
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_mutant(name, tmp_path):
     old, new = MUTANTS[name]
-    src = TRANSPOSE_SRC if name in TRANSPOSE_MUTANTS else REDUCE_SRC if name in REDUCE_MUTANTS else SRC
+    src = TRANSPOSE_SRC if name in TRANSPOSE_MUTANTS else REDUCE_SRC if name in REDUCE_MUTANTS else \
+        GEMM16_SRC if name in GEMM16_MUTANTS else SRC
     text = open(src).read()
     assert text.count(old) == 1, f"mutation anchor for {name} not unique/found"
     mutant_src = tmp_path / "mutant.c"
