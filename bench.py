@@ -21,6 +21,9 @@ Extra modes (used for counter runs under rocprofv3):
                         (metric GB/s moved, bound HBM)
     --row reduce        time reduce_sum_f32 on --n uniform[-1,1) values
                         (default 2^28; metric GB/s read, bound HBM)
+    --row mixed         time gemm_mixed on the workload rounded to --format
+                        (bf16 or f16; binary32 result; metric TFLOP/s against
+                        the 16-bit matrix peak)
     --op XY             time gemm_f32_op with op(A) = X, op(B) = Y (N or T):
                         the transposed factor is stored transposed, with a
                         compact leading dimension
@@ -40,11 +43,11 @@ if ROOT not in sys.path:
 
 PEAK_FP32_TFLOPS = 157.3        # MI355X published dense fp32 (vector and matrix)
 PEAK_HBM_GBS = 8000.0
+PEAK_16BIT_TFLOPS = 2500.0      # MI355X published dense bf16 / fp16 matrix peak
 DEFAULT_WORKLOAD = "square8192"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mfma_square8192_hbm_traffic.txt")
 KERNEL_SOURCES = ["shared_memory_tiled_amd/csrc/mfma.hip",
-                  "shared_memory_tiled_amd/csrc/gemm_internal.h",
-                  "shared_memory_tiled_amd/csrc/api.hip"]
+                  "shared_memory_tiled_amd/csrc/gemm_internal.h"]
 
 
 def source_digest() -> str:
@@ -163,6 +166,88 @@ def bench_reduce(args) -> int:
     return 0
 
 
+def cpu_baseline16(fmt, A, B, w, budget_s: float = 10.0):
+    """The 16-bit oracle as it is, on all host cores, over a band of rows."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    rows = min(cores, w.M)
+    t0 = time.perf_counter()
+    oracle.gemm16(fmt, A.view, B.view, threads=cores, rows=(0, rows))
+    probe = time.perf_counter() - t0
+    rows = max(rows, min(w.M, int(rows * budget_s / max(probe, 1e-3))))
+    rows -= rows % cores if rows > cores else 0
+    t0 = time.perf_counter()
+    oracle.gemm16(fmt, A.view, B.view, threads=cores, rows=(0, rows))
+    dt = time.perf_counter() - t0
+    flop = 2.0 * rows * w.N * w.K
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} {fmt} product "
+                      f"({rows * w.N} outputs, {flop:.3e} FLOP) in {dt:.2f} s, binary64 "
+                      f"triple loop, {cores} threads"}
+
+
+def bench_mixed(args, w) -> int:
+    """gemm_mixed on the workload's data rounded to 16 bits (bf16 or f16),
+    binary32 result; 2 M N K FLOP per launch against the 16-bit matrix peak."""
+    import numpy as np
+    import torch
+
+    from shared_memory_tiled_amd import binding, inputs
+
+    fmt = args.format
+    A, B, _, _ = inputs.operands16(w, fmt)
+    dev = torch.device("cuda:0")
+    a = torch.from_numpy(A.buf.view(np.int16)).to(dev)
+    b = torch.from_numpy(B.buf.view(np.int16)).to(dev)
+    c = torch.empty(w.offset + w.M * w.ldc + 64, dtype=torch.float32, device=dev)
+    call_args = (fmt, w.M, w.N, w.K, a.data_ptr() + 2 * w.offset, w.lda, b.data_ptr() + 2 * w.offset,
+                 w.ldb, c.data_ptr() + 4 * w.offset, w.ldc)
+    flop = 2.0 * w.M * w.N * w.K
+
+    def make(v):
+        if v is None:
+            return lambda: binding.gemm_mixed(*call_args)
+        return lambda: binding.gemm_mixed_variant(v, *call_args)
+
+    if args.ladder:
+        for v in range(binding.gemm_mixed_num_variants()):
+            _, ms = _timed(make(v), args.steps, 2)
+            print(json.dumps({"row": "mixed", "format": fmt, "variant": v,
+                              "name": binding.gemm_mixed_variant_name(v), "workload": w.name,
+                              "ms_per_launch": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
+                              "frac_of_peak": round(flop / ms / 1e9 / PEAK_16BIT_TFLOPS, 4)}), flush=True)
+        return 0
+    wall, ms = _timed(make(args.variant), args.steps, args.warmup)
+    achieved = flop / (ms * 1e-3) / 1e12
+    # the kernel gemm_mixed picks: 256 x 256 tiles once there are 256 of them
+    tiles256 = -(-w.M // 256) * -(-w.N // 256)
+    tiles128 = -(-w.M // 128) * -(-w.N // 128)
+    picked = 0 if tiles256 >= 256 else 2 if tiles128 >= 256 else 3
+    config = {"workload": f"{w.name} rounded to {fmt}", "M": w.M, "N": w.N, "K": w.K, "lda": w.lda,
+              "ldb": w.ldb, "ldc": w.ldc, "view_offset_elements": w.offset, "values": w.dist,
+              "format": fmt, "result": "f32",
+              "kernel": binding.gemm_mixed_variant_name(picked if args.variant is None else args.variant)}
+    if w.offset == 0 and w.lda == w.K and w.ldb == w.N:
+        dt = torch.bfloat16 if fmt == "bf16" else torch.float16
+        at = a[:w.M * w.K].view(dt).view(w.M, w.K)
+        bt = b[:w.K * w.N].view(dt).view(w.K, w.N)
+        _, tms = _timed(lambda: torch.matmul(at, bt), args.steps, args.warmup)
+        config["torch_matmul_same_inputs_16bit_out_TFLOPs"] = round(flop / tms / 1e9, 1)
+    line = {
+        "metric": f"{fmt} x {fmt} -> f32 GEMM TFLOP/s on MI355X",
+        "value": round(flop * args.steps / wall / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": fmt,
+        "data": "synthetic", "config": config,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_16BIT_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_16BIT_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline16(fmt, A, B, w)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_transpose(args, w) -> int:
     """transpose_f32 of the workload's A matrix (M x K, leading dimension lda)
     into an M-column output; bytes moved = 2 x 4 M K per launch."""
@@ -254,7 +339,8 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--op", default="NN", choices=["NN", "TN", "NT", "TT"])
-    ap.add_argument("--row", default="gemm", choices=["gemm", "transpose", "reduce"])
+    ap.add_argument("--row", default="gemm", choices=["gemm", "transpose", "reduce", "mixed"])
+    ap.add_argument("--format", default="bf16", choices=["bf16", "f16"], help="16-bit format of --row mixed")
     ap.add_argument("--n", type=int, default=2 ** 28, help="values summed by --row reduce")
     args = ap.parse_args(argv)
 
@@ -289,6 +375,8 @@ def main(argv=None) -> int:
     w = inputs.WORKLOADS[args.workload]
     if args.row == "transpose":
         return bench_transpose(args, w)
+    if args.row == "mixed":
+        return bench_mixed(args, w)
     op_a, op_b = args.op[0], args.op[1]
     if args.op == "NN":
         A, B = inputs.operands(w)

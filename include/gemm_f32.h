@@ -67,6 +67,7 @@ extern "C" {
 #define GEMM_F32_ERR_DEVICE          8  /* no usable current HIP device              */
 #define GEMM_F32_ERR_INVALID_OP      9  /* op_a or op_b is neither N nor T           */
 #define GEMM_F32_ERR_WORKSPACE      10  /* workspace smaller than required            */
+#define GEMM_F32_ERR_INVALID_FORMAT 11  /* 16-bit input format unknown                */
 
 /* Kernel ladder.  Each rung computes the same product; each is tested against
  * the oracle and against the rung below it.
@@ -211,6 +212,47 @@ int reduce_sum_f32_variant(int variant, int64_t n, const float *x, float *out,
                            void *workspace, int64_t workspace_bytes, void *stream);
 int reduce_sum_f32_num_variants(void);
 const char *reduce_sum_f32_variant_name(int variant);  /* NULL if unknown */
+
+/* Mixed-precision product: C (binary32) = A x B with A and B in a 16-bit
+ * format, accumulated in binary32.
+ *
+ * The one-volume PMPP notes ("PMPP 단권화", deep-learning chapter, "FC Layer
+ * = GEMM" and "Mixed Precision") run the fully connected layer as a matrix
+ * product on matrix units that take FP16 or BF16 inputs and accumulate in
+ * FP32; BF16 keeps FP32's exponent range, FP16 does not.
+ *   format   GEMM_MIXED_BF16 (bfloat16: 1 sign, 8 exponent, 7 fraction bits)
+ *            or GEMM_MIXED_F16 (IEEE binary16: 1 sign, 5 exponent, 10
+ *            fraction bits); both factors use the same format
+ *   A        M x K, element (i, k) at A[i*lda + k], lda >= max(1, K), 16-bit
+ *            patterns, 2-byte aligned
+ *   B        K x N, element (k, j) at B[k*ldb + j], ldb >= max(1, N), same
+ *   C        M x N binary32, element (i, j) at C[i*ldc + j], ldc >= max(1, N),
+ *            4-byte aligned
+ * Leading dimensions count elements.  C[i*ldc + j] = sum_k a_ik b_kj: every
+ * product of two 16-bit values is exact in binary32, the sum is accumulated
+ * in binary32 (the accuracy bound of gemm_f32 applies, measured against the
+ * exact product of the 16-bit values), and the result is bit exact whenever
+ * every partial sum is an integer below 2^24 in magnitude.  Rounding binary32
+ * data to 16 bits is the caller's step, before the call.  Overwrite, window,
+ * K == 0, empty-size, ownership, stream and error rules as for gemm_f32; an
+ * unknown format returns GEMM_F32_ERR_INVALID_FORMAT.  Operands whose bases
+ * are 4-byte aligned with even leading dimensions use vector loads; others
+ * are served by element-wise loads (correct, slower).
+ * gemm_mixed picks the tile shape for the problem; gemm_mixed_variant runs
+ * tile configuration `variant` (0 .. gemm_mixed_num_variants() - 1, named by
+ * gemm_mixed_variant_name).
+ */
+#define GEMM_MIXED_BF16 0
+#define GEMM_MIXED_F16  1
+
+int gemm_mixed(int format, int64_t M, int64_t N, int64_t K,
+               const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+               float *C, int64_t ldc, void *stream);
+int gemm_mixed_variant(int variant, int format, int64_t M, int64_t N, int64_t K,
+                       const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                       float *C, int64_t ldc, void *stream);
+int gemm_mixed_num_variants(void);
+const char *gemm_mixed_variant_name(int variant);   /* NULL if unknown */
 
 #ifdef __cplusplus
 }

@@ -86,6 +86,15 @@ def load_library():
         lib.reduce_sum_f32_num_variants.restype = ctypes.c_int
         lib.reduce_sum_f32_variant_name.argtypes = [ctypes.c_int]
         lib.reduce_sum_f32_variant_name.restype = ctypes.c_char_p
+        msig = [ctypes.c_int] + sig
+        lib.gemm_mixed.argtypes = msig
+        lib.gemm_mixed.restype = ctypes.c_int
+        lib.gemm_mixed_variant.argtypes = [ctypes.c_int] + msig
+        lib.gemm_mixed_variant.restype = ctypes.c_int
+        lib.gemm_mixed_num_variants.argtypes = []
+        lib.gemm_mixed_num_variants.restype = ctypes.c_int
+        lib.gemm_mixed_variant_name.argtypes = [ctypes.c_int]
+        lib.gemm_mixed_variant_name.restype = ctypes.c_char_p
         _lib = lib
         return lib
 
@@ -268,4 +277,68 @@ def reduce_sum(x: torch.Tensor, variant=None, stream=None) -> torch.Tensor:
         reduce_sum_f32(n, x, out, ws, ws_bytes, stream=stream)
     else:
         reduce_sum_f32_variant(v, n, x, out, ws, ws_bytes, stream=stream)
+    return out
+
+
+FORMATS = {"bf16": 0, "f16": 1}
+_FORMAT_OF_DTYPE = {torch.bfloat16: 0, torch.float16: 1}
+
+
+def _format(fmt) -> int:
+    if isinstance(fmt, str):
+        return FORMATS[fmt]
+    return int(fmt)
+
+
+def gemm_mixed(fmt, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
+    """C (binary32) = A x B for 16-bit A and B of format ``fmt`` ('bf16' or
+    'f16'); leading dimensions in elements; see gemm_f32.h."""
+    lib = load_library()
+    _check(lib.gemm_mixed(_format(fmt), M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc,
+                          _stream(stream)))
+
+
+def gemm_mixed_variant(variant, fmt, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
+    lib = load_library()
+    _check(lib.gemm_mixed_variant(int(variant), _format(fmt), M, N, K, _addr(A), lda, _addr(B), ldb,
+                                  _addr(C), ldc, _stream(stream)))
+
+
+def gemm_mixed_num_variants() -> int:
+    return load_library().gemm_mixed_num_variants()
+
+
+def gemm_mixed_variant_name(variant: int) -> str | None:
+    name = load_library().gemm_mixed_variant_name(int(variant))
+    return name.decode() if name is not None else None
+
+
+def _ld16(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.dtype not in _FORMAT_OF_DTYPE:
+        raise TypeError("16-bit factors must be 2-D bfloat16 or float16 tensors")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("matrices must be row-major (unit column stride)")
+    return max(t.stride(0) if t.shape[0] > 1 else t.shape[1], t.shape[1], 1)
+
+
+def gemm16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None, variant=None,
+           stream=None) -> torch.Tensor:
+    """Tensor form: returns ``out`` (float32, allocated if None) = A @ B for
+    bfloat16 or float16 CUDA tensors A (M x K) and B (K x N) of one dtype;
+    views with a leading dimension and a storage offset pass through."""
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same 16-bit dtype")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    args = (_FORMAT_OF_DTYPE[A.dtype], M, N, K, A, _ld16(A), B, _ld16(B), out, _ld(out))
+    if variant is None:
+        gemm_mixed(*args, stream=stream)
+    else:
+        gemm_mixed_variant(variant, *args, stream=stream)
     return out

@@ -159,6 +159,7 @@ extern "C" const char* gemm_f32_status_string(int status) {
         case GEMM_F32_ERR_DEVICE: return "no usable current HIP device";
         case GEMM_F32_ERR_INVALID_OP: return "invalid op: op_a and op_b must be GEMM_F32_OP_N or GEMM_F32_OP_T";
         case GEMM_F32_ERR_WORKSPACE: return "workspace smaller than reduce_sum_f32_workspace_size()";
+        case GEMM_F32_ERR_INVALID_FORMAT: return "unknown 16-bit format: use GEMM_MIXED_BF16 or GEMM_MIXED_F16";
         default: return "unknown status";
     }
 }
@@ -260,3 +261,51 @@ extern "C" int reduce_sum_f32_variant(int variant, int64_t n, const float* x, fl
 extern "C" int reduce_sum_f32_num_variants(void) { return reduce_num_variants(); }
 
 extern "C" const char* reduce_sum_f32_variant_name(int variant) { return reduce_variant_name(variant); }
+
+// ---------------------------------------------------------- mixed precision
+
+namespace {
+constexpr int kMixedAuto = -1;
+
+bool misaligned2(const void* ptr) { return ((uintptr_t)ptr & 1u) != 0; }
+
+int run_mixed(int config, int format, int64_t M, int64_t N, int64_t K, const uint16_t* A,
+              int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+    if (config != kMixedAuto && (config < 0 || config >= mixed_num_configs()))
+        return GEMM_F32_ERR_INVALID_VARIANT;
+    if (format != GEMM_MIXED_BF16 && format != GEMM_MIXED_F16) return GEMM_F32_ERR_INVALID_FORMAT;
+    if (M < 0 || N < 0 || K < 0) return GEMM_F32_ERR_INVALID_DIM;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+        return GEMM_F32_ERR_INVALID_LD;
+    if (M == 0 || N == 0) return GEMM_F32_OK;
+    if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return GEMM_F32_ERR_NULL_PTR;
+    if (misaligned(C) || (K > 0 && (misaligned2(A) || misaligned2(B)))) return GEMM_F32_ERR_MISALIGNED;
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_F32_ERR_TOO_LARGE;
+    if (!extent_fits(M, K, lda) || !extent_fits(K, N, ldb) || !extent_fits(M, N, ldc))
+        return GEMM_F32_ERR_TOO_LARGE;
+    const int64_t blocks16 = ((M + 15) / 16) * ((N + 15) / 16);
+    if (blocks16 > (int64_t)0xFFFFFFFF / 256) return GEMM_F32_ERR_TOO_LARGE;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_F32_ERR_DEVICE;
+    const Gemm16Args p{(int)M, (int)N, (int)K, A, lda, B, ldb, C, ldc};
+    if (config == kMixedAuto) config = mixed_pick_config(p.M, p.N, p.K);
+    const hipError_t e = launch_mixed(p, reinterpret_cast<hipStream_t>(stream), format, config);
+    if (e == hipErrorInvalidValue) return GEMM_F32_ERR_TOO_LARGE;
+    return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
+}
+}  // namespace
+
+extern "C" int gemm_mixed(int format, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                          const uint16_t* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+    return run_mixed(kMixedAuto, format, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+extern "C" int gemm_mixed_variant(int variant, int format, int64_t M, int64_t N, int64_t K,
+                                  const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                  float* C, int64_t ldc, void* stream) {
+    return run_mixed(variant, format, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+extern "C" int gemm_mixed_num_variants(void) { return mixed_num_configs(); }
+
+extern "C" const char* gemm_mixed_variant_name(int variant) { return mixed_config_name(variant); }

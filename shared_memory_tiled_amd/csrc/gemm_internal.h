@@ -23,6 +23,16 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (int)(((int64_t)a + b - 1) / b); }
 
+// gfx950 deals consecutive workgroups to its eight XCDs in turn, and each XCD
+// has its own L2.  This maps block b to a logical tile index so that each XCD
+// walks one contiguous run of the nblocks tiles.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_contiguous(int b, int nblocks) {
+    const int per = nblocks / kXcds, extra = nblocks % kXcds;
+    const int x = b % kXcds, local = b / kXcds;
+    return x * per + min(x, extra) + local;
+}
+
 // Four consecutive floats of row `r` starting at column `c` of a row-major
 // matrix with `rows` x `cols` valid entries and leading dimension `ld`.
 // Slots outside the matrix read as +0 (ghost elements) and are never loaded.
@@ -71,6 +81,20 @@ hipError_t launch_transpose(int variant, int rows, int cols, const float* in, in
                             float* out, int64_t ld_out, hipStream_t s);
 int transpose_num_variants();
 const char* transpose_variant_name(int v);
+
+// Mixed-precision product (mfma16.hip): C (binary32) = A x B with A and B
+// holding 16-bit patterns of one format (0 bfloat16, 1 binary16), row-major,
+// leading dimensions in elements.  Validated like GemmArgs.
+struct Gemm16Args {
+    int M, N, K;
+    const uint16_t* A; int64_t lda;
+    const uint16_t* B; int64_t ldb;
+    float* C; int64_t ldc;
+};
+hipError_t launch_mixed(const Gemm16Args& p, hipStream_t s, int format, int config);
+int mixed_num_configs();
+const char* mixed_config_name(int config);
+int mixed_pick_config(int M, int N, int K);
 
 // Sum reduction (reduce.hip): *out = sum of x[0 .. n-1].
 hipError_t launch_reduce(int variant, int64_t n, const float* x, float* out, float* ws, hipStream_t s);

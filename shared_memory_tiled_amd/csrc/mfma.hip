@@ -59,18 +59,11 @@
 namespace gemmf32 {
 
 namespace {
-constexpr int kXcds = 8;
 
 // One lane's 16 bytes from global memory straight into LDS: the wave's 64
 // lanes fill 1 KB starting at `dst` (wave-uniform), lane l at byte 16 l.
 __device__ __forceinline__ void copy16_global_to_lds(const float* src, float* dst) {
     __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-}
-
-__device__ __forceinline__ int xcd_contiguous(int b, int nblocks) {
-    const int per = nblocks / kXcds, extra = nblocks % kXcds;
-    const int x = b % kXcds, local = b / kXcds;
-    return x * per + min(x, extra) + local;
 }
 
 // Where one factor lives: stored matrix, leading dimension, extent along mn

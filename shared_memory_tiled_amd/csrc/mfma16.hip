@@ -1,0 +1,399 @@
+// mfma16.hip -- the mixed-precision product: bfloat16 or binary16 inputs,
+// binary32 accumulation and result, on gfx950's 16-bit matrix instructions.
+//
+// The one-volume PMPP notes ("PMPP 단권화", deep-learning chapter) run the
+// fully connected layer as a matrix product on matrix units that take FP16 or
+// BF16 inputs and accumulate in FP32 ("FC Layer = GEMM", "Mixed Precision").
+// This is that product with the tiled structure of the fp32 kernels: per
+// phase a block stages an A tile and a B tile in LDS, ghost zeros past the
+// matrix edges, double-buffered stages and one barrier per phase, a guarded
+// store of the binary32 accumulators.
+//
+// v_mfma_f32_32x32x16_{bf16,f16}: D(32x32) += A(32x16) B(16x32) per wave.
+// Lane l supplies eight values of row l % 32 of A and eight of column l % 32
+// of B, the same eight k for both factors; accumulator register r of lane l
+// holds D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], as for the fp32
+// instruction.  Which k a lane half holds is free as long as both factors
+// agree, so in the s-th 16-deep step of a phase lane half h takes
+// k = 16 s + 8 h + 0..7: each lane's operand of either factor is then eight
+// consecutive k of one row, one 128-bit LDS read.
+//
+// LDS layout: both tiles k-contiguous, one 128-byte row of BK = 64 values per
+// output row (A) or column (B).  The 16-byte chunk c of row r sits at chunk
+// position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 4)) & 7 (the first page's XOR
+// swizzle, on 16-byte chunks).  Fragment reads: 16 lanes per LDS cycle read
+// rows R .. R+15 at one chunk; a row pair spans the 64 banks and f gives the
+// eight row pairs eight different chunk positions.  B stores (below): 8 lanes
+// per cycle write rows 4l + j, l = 0..7, at one chunk; f gives those eight
+// rows eight different positions as well.
+//
+// A (M x K, k-contiguous in memory) is copied as stored: straight from global
+// memory into LDS (global_load_lds_dwordx4, each wave instruction fills 1 KB,
+// 8 rows) in interior phases of the large tiles, else with 128-bit loads
+// through registers.  B (K x N, n-contiguous in memory) has to become
+// k-contiguous: each thread loads a block of 8 k rows x 4 n (eight 64-bit
+// loads; the lanes of a wave cover consecutive n of one k row), transposes it
+// in registers and writes four 128-bit LDS rows of 8 k values.
+//
+// Vector loads need 4-byte alignment (gfx9 runs global memory in unaligned
+// mode; a dword-aligned multi-dword load is legal): operands whose base is
+// only 2-byte aligned, or whose leading dimension is odd, take the same
+// kernels with element-wise 16-bit loads.
+#include "gemm_internal.h"
+
+#include <type_traits>
+
+namespace gemmf32 {
+
+namespace {
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+constexpr int kBK = 64;          // k values per phase = one 128-byte LDS row
+constexpr int kCPR = kBK / 8;    // 16-byte chunks per LDS row
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 4)) & 7; }
+// Element offset, inside a tile stage, of logical chunk c of row r.
+__device__ __forceinline__ int lds_elem(int r, int c) { return r * kBK + 8 * (c ^ swz(r)); }
+
+// One lane's 16 bytes from global memory straight into LDS: the wave's 64
+// lanes fill 1 KB starting at `dst` (wave-uniform), lane l at byte 16 l.
+__device__ __forceinline__ void copy16_to_lds(const uint16_t* src, uint16_t* dst) {
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+template <int FMT>
+__device__ __forceinline__ floatx16 mfma16(u32x4 a, u32x4 b, floatx16 c) {
+    if constexpr (FMT == 0)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a),
+                                                      __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+}
+
+// Eight consecutive elements of row r from column c of a rows x cols matrix
+// (leading dimension ld); slots outside the matrix are +0 and never loaded.
+template <bool VEC>
+__device__ __forceinline__ u32x4 load8_ghost(const uint16_t* __restrict__ base, int r, int rows, int c,
+                                             int cols, int64_t ld) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < rows) {
+        const uint16_t* q = base + (int64_t)r * ld + c;
+        if (VEC && c + 8 <= cols) {
+            __builtin_memcpy(&v, q, 16);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (c + e < cols) v[e >> 1] |= (unsigned)q[e] << (16 * (e & 1));
+        }
+    }
+    return v;
+}
+
+// Four consecutive elements of row r from column c, ghost zeros as above.
+template <bool VEC>
+__device__ __forceinline__ u32x2 load4_ghost16(const uint16_t* __restrict__ base, int r, int rows, int c,
+                                               int cols, int64_t ld) {
+    u32x2 v = {0u, 0u};
+    if (r < rows) {
+        const uint16_t* q = base + (int64_t)r * ld + c;
+        if (VEC && c + 4 <= cols) {
+            __builtin_memcpy(&v, q, 8);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (c + e < cols) v[e >> 1] |= (unsigned)q[e] << (16 * (e & 1));
+        }
+    }
+    return v;
+}
+
+// Column j (0..3) of an 8 x 4 block held as eight rows of four 16-bit values,
+// as one 128-bit row of eight values (row i in element i).
+__device__ __forceinline__ u32x4 block_column(const u32x2 (&v)[8], int j) {
+    u32x4 t;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const unsigned lo = v[2 * q][j >> 1], hi = v[2 * q + 1][j >> 1];
+        t[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+    return t;
+}
+}  // namespace
+
+template <int FMT, int BM, int BN, int WAVES_M, int WAVES_N, bool DIRECT, bool VEC>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
+void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int NT = NW * 64;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
+    constexpr int FM = WM / 32, FN = WN / 32;             // 32 x 32 blocks per wave
+    constexpr int A_CHUNKS = BM * kCPR / NT;              // register-staged A chunks per thread
+    constexpr int NB4 = BN / 4;                           // 4-wide n blocks per k row of B
+    constexpr int B_BLOCKS = (kBK / 8) * NB4 / NT;        // 8 x 4 blocks of B per thread
+    constexpr int A_COPIES = BM / 8 / NW;                 // direct 1 KB copies per wave
+    constexpr int STAGE = (BM + BN) * kBK;                // 16-bit elements per stage
+    static_assert(WM % 32 == 0 && WN % 32 == 0, "tile shape");
+    static_assert(A_CHUNKS * NT == BM * kCPR && B_BLOCKS * NT == (kBK / 8) * NB4, "copy split");
+    static_assert(!DIRECT || (VEC && A_COPIES * NW * 8 == BM), "direct copy split");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int li = lane & 31, lh = lane >> 5;
+
+    // tile of this block: XCD-contiguous runs, in groups of group_m tile rows
+    const int logical = xcd_contiguous((int)blockIdx.x, tiles_m * tiles_n);
+    const int group_size = group_m * tiles_n;
+    const int g = logical / group_size;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int in_g = logical - g * group_size;
+    const int m0 = (first_m + in_g % gm) * BM;
+    const int n0 = (in_g / gm) * BN;
+    // Interior tiles with vector-aligned operands run their full phases on
+    // straight-line loads (no ghost checks); edge tiles and a ragged last
+    // phase take the ghost-zero loads.  The test is uniform over the block.
+    const bool fast_tile = VEC && (m0 + BM <= p.M) && (n0 + BN <= p.N);
+
+    // ---- A through registers (every phase when !DIRECT; ghost phases otherwise)
+    u32x4 ra[A_CHUNKS];
+    auto load_a_fast = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < A_CHUNKS; ++u) {
+            const int q = tid + u * NT, r = q / kCPR, c = q % kCPR;
+            __builtin_memcpy(&ra[u], p.A + (int64_t)(m0 + r) * p.lda + k0 + 8 * c, 16);
+        }
+    };
+    auto load_a_ghost = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < A_CHUNKS; ++u) {
+            const int q = tid + u * NT, r = q / kCPR, c = q % kCPR;
+            ra[u] = load8_ghost<VEC>(p.A, m0 + r, p.M, k0 + 8 * c, p.K, p.lda);
+        }
+    };
+    auto store_a = [&](int buf) {
+        uint16_t* as = lds + buf * STAGE;
+#pragma unroll
+        for (int u = 0; u < A_CHUNKS; ++u) {
+            const int q = tid + u * NT;
+            *reinterpret_cast<u32x4*>(&as[lds_elem(q / kCPR, q % kCPR)]) = ra[u];
+        }
+    };
+    // Direct copy j of this wave fills LDS rows R .. R+7, R = 8 (wave + j NW);
+    // lane l writes physical chunk l % 8 of row R + l / 8, so it reads the
+    // logical chunk (l % 8) ^ f(row) of global row m0 + row.
+    int64_t a_doff[DIRECT ? A_COPIES : 1];
+    if constexpr (DIRECT) {
+#pragma unroll
+        for (int j = 0; j < A_COPIES; ++j) {
+            const int row = 8 * (wave_u + j * NW) + lane / 8;
+            a_doff[j] = (int64_t)(m0 + row) * p.lda + 8 * ((lane % 8) ^ swz(row));
+        }
+    }
+    auto direct_a = [&](int k0, int buf) {
+        if constexpr (DIRECT) {
+            uint16_t* as = lds + buf * STAGE;
+            const uint16_t* a = p.A + k0;
+#pragma unroll
+            for (int j = 0; j < A_COPIES; ++j)
+                copy16_to_lds(a + a_doff[j], as + 8 * (wave_u + j * NW) * kBK);
+        }
+    };
+
+    // ---- B: 8 x 4 blocks, q = tid + u NT: n block q % NB4, k block q / NB4
+    u32x2 rb[B_BLOCKS][8];
+    auto load_b_fast = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < B_BLOCKS; ++u) {
+            const int q = tid + u * NT, nb = q % NB4, kb = q / NB4;
+            const uint16_t* b = p.B + (int64_t)(k0 + 8 * kb) * p.ldb + n0 + 4 * nb;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) __builtin_memcpy(&rb[u][i], b + i * p.ldb, 8);
+        }
+    };
+    auto load_b_ghost = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < B_BLOCKS; ++u) {
+            const int q = tid + u * NT, nb = q % NB4, kb = q / NB4;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                rb[u][i] = load4_ghost16<VEC>(p.B, k0 + 8 * kb + i, p.K, n0 + 4 * nb, p.N, p.ldb);
+        }
+    };
+    auto store_b = [&](int buf) {
+        uint16_t* bs = lds + buf * STAGE + BM * kBK;
+#pragma unroll
+        for (int u = 0; u < B_BLOCKS; ++u) {
+            const int q = tid + u * NT, nb = q % NB4, kb = q / NB4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x4*>(&bs[lds_elem(4 * nb + j, kb)]) = block_column(rb[u], j);
+        }
+    };
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    auto math = [&](int buf) {
+        const uint16_t* as = lds + buf * STAGE;
+        const uint16_t* bs = as + BM * kBK;
+#pragma unroll
+        for (int s = 0; s < kBK / 16; ++s) {
+            u32x4 a[FM], b[FN];
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+                a[f] = *reinterpret_cast<const u32x4*>(&as[lds_elem(wm * WM + f * 32 + li, 2 * s + lh)]);
+#pragma unroll
+            for (int f = 0; f < FN; ++f)
+                b[f] = *reinterpret_cast<const u32x4*>(&bs[lds_elem(wn * WN + f * 32 + li, 2 * s + lh)]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<FMT>(a[i], b[j], acc[i][j]);
+        }
+    };
+    // The direct copies write LDS behind the compiler's back: wait for them,
+    // and tell the compiler that LDS changed across the barrier.
+    auto end_phase = [&]() {
+        if constexpr (DIRECT) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if constexpr (DIRECT) asm volatile("" ::: "memory");
+    };
+    // Tiles of the phase starting at k0 into stage buf, FAST (interior, full
+    // phase) or with ghost zeros, issued now and stored by finish_tiles.
+    auto start_tiles = [&](int k0, int buf, auto fast) {
+        if constexpr (decltype(fast)::value) {
+            if constexpr (DIRECT) direct_a(k0, buf);
+            else load_a_fast(k0);
+            load_b_fast(k0);
+        } else {
+            load_a_ghost(k0);
+            load_b_ghost(k0);
+        }
+    };
+    auto finish_tiles = [&](int buf, auto fast) {
+        if constexpr (!(DIRECT && decltype(fast)::value)) store_a(buf);
+        store_b(buf);
+    };
+    // One phase on stage ph & 1 while the next phase's tiles (PF: 0 none,
+    // 1 fast, 2 ghost) go to the other stage.
+    auto phase = [&](int ph, auto pf) {
+        constexpr int PF = decltype(pf)::value;
+        const int cur = ph & 1, k_next = (ph + 1) * kBK;
+        if constexpr (PF == 1) start_tiles(k_next, cur ^ 1, std::true_type{});
+        if constexpr (PF == 2) start_tiles(k_next, cur ^ 1, std::false_type{});
+        // keep the next phase's loads ahead of the math, so their latency
+        // hides behind it (the scheduler would otherwise sink them to their use)
+        if constexpr (PF != 0) __builtin_amdgcn_sched_barrier(0);
+        math(cur);
+        // and keep their use (B's transpose, the LDS stores) after the math
+        if constexpr (PF != 0) __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PF == 1) finish_tiles(cur ^ 1, std::true_type{});
+        if constexpr (PF == 2) finish_tiles(cur ^ 1, std::false_type{});
+        end_phase();
+    };
+    using none = std::integral_constant<int, 0>;
+    using fast = std::integral_constant<int, 1>;
+    using ghost = std::integral_constant<int, 2>;
+
+    const int phases = ceil_div(p.K, kBK);
+    const int full = fast_tile ? p.K / kBK : 0;      // phases loaded straight (no ghosts)
+    if (phases > 0) {
+        if (full > 0) {
+            start_tiles(0, 0, std::true_type{});
+            finish_tiles(0, std::true_type{});
+        } else {
+            start_tiles(0, 0, std::false_type{});
+            finish_tiles(0, std::false_type{});
+        }
+    }
+    end_phase();
+    int ph = 0;
+    for (; ph + 1 < full; ++ph) phase(ph, fast{});          // next phase full: the hot loop
+    for (; ph + 1 < phases; ++ph) phase(ph, ghost{});       // next phase ragged or edge tile
+    if (ph < phases) phase(ph, none{});
+
+    // Guarded store: register r of lane (li, lh) is row 8 (r/4) + 4 lh + r%4.
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn * WN + j * 32 + li;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
+            }
+        }
+}
+
+namespace {
+using Launch16 = hipError_t (*)(const Gemm16Args&, hipStream_t, int, int, int, unsigned);
+
+template <int FMT, int BM, int BN, int WAVES_M, int WAVES_N, bool DIRECT, bool VEC>
+hipError_t launch16(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                    unsigned blocks) {
+    hipLaunchKernelGGL((gemm16_kernel<FMT, BM, BN, WAVES_M, WAVES_N, DIRECT, VEC>), dim3(blocks),
+                       dim3(WAVES_M * WAVES_N * 64), 0, s, p, tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+}
+
+struct MixedConfig {
+    const char* name;
+    int bm, bn, group_m;
+    Launch16 launch[2][2];        // [format][vector loads]
+};
+
+// Misaligned operands use the element-wise kernel of the same tile shape
+// (never direct copies).
+#define MIXED(BM, BN, WM, WN, D)                                                                \
+    {{launch16<0, BM, BN, WM, WN, false, false>, launch16<0, BM, BN, WM, WN, D, true>},        \
+     {launch16<1, BM, BN, WM, WN, false, false>, launch16<1, BM, BN, WM, WN, D, true>}}
+
+const MixedConfig kMixed[] = {
+    {"mixed256x256_bk64_w2x4_directA", 256, 256, 8, MIXED(256, 256, 2, 4, true)},
+    {"mixed256x256_bk64_w2x4", 256, 256, 8, MIXED(256, 256, 2, 4, false)},
+    {"mixed128x128_bk64_w2x2", 128, 128, 8, MIXED(128, 128, 2, 2, false)},
+    {"mixed64x64_bk64_w1x2", 64, 64, 8, MIXED(64, 64, 1, 2, false)},
+};
+#undef MIXED
+constexpr int kNumMixed = (int)(sizeof(kMixed) / sizeof(kMixed[0]));
+}  // namespace
+
+int mixed_num_configs() { return kNumMixed; }
+const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed[c].name : nullptr; }
+
+// The largest tile that still gives every CU a workgroup.
+int mixed_pick_config(int M, int N, int /*K*/) {
+    const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
+    const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
+    if (t256 >= 256) return 0;
+    if (t128 >= 256) return 2;
+    return 3;
+}
+
+// hipErrorInvalidValue: the grid would exceed the launch limits.
+hipError_t launch_mixed(const Gemm16Args& p, hipStream_t s, int format, int config) {
+    const MixedConfig& c = kMixed[(config >= 0 && config < kNumMixed) ? config : 0];
+    // vector loads: 4-byte aligned bases and even leading dimensions
+    const bool vec = ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 3) == 0 &&
+                     (p.lda % 2) == 0 && (p.ldb % 2) == 0;
+    const int tiles_m = ceil_div(p.M, c.bm), tiles_n = ceil_div(p.N, c.bn);
+    const int64_t blocks = (int64_t)tiles_m * tiles_n;
+    if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    return c.launch[format ? 1 : 0][vec ? 1 : 0](p, s, tiles_m, tiles_n, c.group_m, (unsigned)blocks);
+}
+
+}  // namespace gemmf32

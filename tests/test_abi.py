@@ -16,11 +16,13 @@ def _header_text():
 
 
 def declared_functions():
-    return sorted(set(re.findall(r"\b(gemm_f32\w*)\s*\(", _header_text())))
+    """Every function the header declares (return type at the line start)."""
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int64_t|int|char|void)\s*\*?\s*(\w+)\s*\(",
+                                 _header_text(), flags=re.M)))
 
 
 def declared_codes():
-    return {m[0]: int(m[1]) for m in re.findall(r"#define\s+(GEMM_F32_\w+)\s+(-?\d+)", _header_text())}
+    return {m[0]: int(m[1]) for m in re.findall(r"#define\s+(GEMM_\w+)\s+(-?\d+)", _header_text())}
 
 
 @pytest.fixture(scope="module")
@@ -42,8 +44,9 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, n), f"{n} declared in gemm_f32.h but not exported"
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "shared_memory_tiled_amd", "libgemm_f32.so")],
                          capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (gemm_f32\w*)$", out, flags=re.M))
+    exported = set(re.findall(r"\bT ([A-Za-z]\w*)$", out, flags=re.M))    # C names (no _Z, _init)
     assert exported == set(names), exported ^ set(names)
+    assert {"transpose_f32", "reduce_sum_f32", "gemm_mixed", "gemm_mixed_variant"} <= set(names)
 
 
 def test_library_is_independent_of_the_oracle():
@@ -198,6 +201,43 @@ def test_reduce_workspace_sizes(binding, lib):
     assert binding.reduce_sum_f32_workspace_size(2, 257) == 4 * 2
     assert binding.reduce_sum_f32_workspace_size(3, 10**9) == 0
     assert binding.reduce_sum_f32_workspace_size(4, 1) == 4 * 1024
+
+
+@pytest.mark.parametrize("args,code", [
+    ((2, 4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_FORMAT"),
+    ((-1, 4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_FORMAT"),
+    ((0, -1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_DIM"),
+    ((1, 4, 4, -3, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_DIM"),
+    ((0, 4, 4, 8, FAKE, 7, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_LD"),
+    ((1, 4, 6, 4, FAKE, 4, FAKE, 5, FAKE, 6), "GEMM_F32_ERR_INVALID_LD"),
+    ((0, 4, 6, 4, FAKE, 4, FAKE, 6, FAKE, 5), "GEMM_F32_ERR_INVALID_LD"),
+    ((0, 4, 4, 4, None, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_NULL_PTR"),
+    ((1, 4, 4, 4, FAKE, 4, None, 4, FAKE, 4), "GEMM_F32_ERR_NULL_PTR"),
+    ((0, 4, 4, 4, FAKE, 4, FAKE, 4, None, 4), "GEMM_F32_ERR_NULL_PTR"),
+    ((0, 4, 4, 4, FAKE + 1, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_MISALIGNED"),   # 16-bit: 2-byte alignment
+    ((1, 4, 4, 4, FAKE, 4, FAKE + 3, 4, FAKE, 4), "GEMM_F32_ERR_MISALIGNED"),
+    ((0, 4, 4, 4, FAKE, 4, FAKE, 4, FAKE + 2, 4), "GEMM_F32_ERR_MISALIGNED"),   # C is binary32
+    ((0, 2**31, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_TOO_LARGE"),
+    ((1, 4, 4, 4, FAKE, 2**62, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_TOO_LARGE"),
+    ((0, 0, 4, 4, None, 4, None, 4, None, 4), "GEMM_F32_OK"),          # empty: no launch
+    ((1, 4, 0, 4, None, 4, None, 1, None, 1), "GEMM_F32_OK"),
+])
+def test_mixed_validation_without_launch(lib, args, code):
+    want = declared_codes()[code]
+    assert lib.gemm_mixed(*args, None) == want
+    for v in range(lib.gemm_mixed_num_variants()):
+        assert lib.gemm_mixed_variant(v, *args, None) == want
+
+
+def test_mixed_variants(binding, lib):
+    n = binding.gemm_mixed_num_variants()
+    names = [binding.gemm_mixed_variant_name(v) for v in range(n)]
+    assert n >= 3 and all(names) and len(set(names)) == n
+    assert binding.gemm_mixed_variant_name(n) is None and binding.gemm_mixed_variant_name(-1) is None
+    code = declared_codes()["GEMM_F32_ERR_INVALID_VARIANT"]
+    assert lib.gemm_mixed_variant(n, 0, 4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, None) == code
+    assert declared_codes()["GEMM_MIXED_BF16"] == binding.FORMATS["bf16"] == 0
+    assert declared_codes()["GEMM_MIXED_F16"] == binding.FORMATS["f16"] == 1
     assert binding.reduce_sum_f32_workspace_size(9, 10) == -1
     assert binding.reduce_sum_f32_workspace_size(1, -1) == -1
     n = binding.reduce_sum_f32_num_variants()
