@@ -7,7 +7,7 @@
 // (PMPP chapter 5 notes, section 5.4): with K = 0 there are no phases and
 // every output is the initial +0; with M = 0 or N = 0 there is no output.
 #include "gemm_f32.h"
-#include "gemm_internal.h"
+#include "launch.h"
 
 #include <limits.h>
 

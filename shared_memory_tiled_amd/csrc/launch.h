@@ -1,0 +1,50 @@
+// launch.h -- host-side declarations of the kernel launchers and their
+// configuration tables, shared by the kernel translation units and api.hip
+// (not part of the public interface).  Device code lives in the .hip files and
+// in gemm_internal.h.
+#pragma once
+
+#include "gemm_internal.h"
+
+namespace gemmf32 {
+
+// Launchers (asynchronous; return the launch status of the HIP runtime).
+hipError_t launch_naive(const GemmArgs& p, hipStream_t s);
+hipError_t launch_tiled(const GemmArgs& p, hipStream_t s, int pad);
+hipError_t launch_regblock(const GemmArgs& p, hipStream_t s, int config);
+hipError_t launch_mfma(const GemmArgs& p, hipStream_t s, int config, int op_a, int op_b);
+
+// Shared-tile transpose (transpose.hip): out (cols x rows) = in^T.
+hipError_t launch_transpose(int variant, int rows, int cols, const float* in, int64_t ld_in,
+                            float* out, int64_t ld_out, hipStream_t s);
+int transpose_num_variants();
+const char* transpose_variant_name(int v);
+
+// Mixed-precision product (mfma16.hip): C (binary32) = A x B with A and B
+// holding 16-bit patterns of one format (0 bfloat16, 1 binary16), row-major,
+// leading dimensions in elements.  Validated like GemmArgs.
+struct Gemm16Args {
+    int M, N, K;
+    const uint16_t* A; int64_t lda;
+    const uint16_t* B; int64_t ldb;
+    float* C; int64_t ldc;
+};
+hipError_t launch_mixed(const Gemm16Args& p, hipStream_t s, int format, int config);
+int mixed_num_configs();
+const char* mixed_config_name(int config);
+int mixed_pick_config(int M, int N, int K);
+
+// Sum reduction (reduce.hip): *out = sum of x[0 .. n-1].
+hipError_t launch_reduce(int variant, int64_t n, const float* x, float* out, float* ws, hipStream_t s);
+int64_t reduce_workspace_floats(int variant, int64_t n);
+int reduce_num_variants();
+const char* reduce_variant_name(int v);
+
+// Number of MFMA / register-blocked tile configurations and their names.
+int mfma_num_configs();
+const char* mfma_config_name(int config);
+int mfma_pick_config(int M, int N, int K);
+int regblock_num_configs();
+const char* regblock_config_name(int config);
+
+}  // namespace gemmf32

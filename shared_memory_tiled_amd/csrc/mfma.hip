@@ -54,7 +54,7 @@
 // each XCD walks a contiguous run of tiles, and tiles are ordered in groups
 // of group_m tile rows so that the blocks resident on one XCD at a time
 // share A row panels and B column panels in that XCD's L2.
-#include "gemm_internal.h"
+#include "launch.h"
 
 namespace gemmf32 {
 

@@ -39,7 +39,7 @@
 // mode; a dword-aligned multi-dword load is legal): operands whose base is
 // only 2-byte aligned, or whose leading dimension is odd, take the same
 // kernels with element-wise 16-bit loads.
-#include "gemm_internal.h"
+#include "launch.h"
 
 #include <type_traits>
 
@@ -63,6 +63,40 @@ __device__ __forceinline__ int lds_elem(int r, int c) { return r * kBK + 8 * (c 
 // lanes fill 1 KB starting at `dst` (wave-uniform), lane l at byte 16 l.
 __device__ __forceinline__ void copy16_to_lds(const uint16_t* src, uint16_t* dst) {
     __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Four 16-bit values through ds_read_b64_tr_b16.  Within each group of 16
+// lanes, value e of lane i is element i % 4 of the 8 bytes addressed by lane
+// 4 e + i / 4.  So if lane j of a group addresses row kb + j / 4, columns
+// nb + 4 (j % 4) .. +3 of a row-major tile, lane i receives the column
+// nb + i, rows kb .. kb + 3: four consecutive k of one n.
+//
+// Issued as inline assembly: the compiler would otherwise wait for every
+// outstanding global -> LDS copy before the first such read (it cannot tell
+// that the copies fill the other stage).  The "memory" clobber keeps the
+// reads in order with the barriers; wait_tied() below is their wait.
+__device__ __forceinline__ u32x2 read_tr16(uint32_t lds_byte_addr) {
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(lds_byte_addr) : "memory");
+    return v;
+}
+
+// Waits for all outstanding LDS reads; the fragments pass through the wait
+// as operands, so no use of them can be scheduled before it.
+template <int N>
+__device__ __forceinline__ void wait_tied(u32x4 (&b)[N]) {
+    static_assert(N == 1 || N == 2 || N == 4, "fragment count");
+    if constexpr (N == 1) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]) : : "memory");
+    if constexpr (N == 2) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]) : : "memory");
+    if constexpr (N == 4)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : : "memory");
+}
+
+// Byte address inside LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 template <int FMT>
@@ -112,9 +146,11 @@ __device__ __forceinline__ u32x2 load4_ghost16(const uint16_t* __restrict__ base
     return v;
 }
 
-// Column j (0..3) of an 8 x 4 block held as eight rows of four 16-bit values,
-// as one 128-bit row of eight values (row i in element i).
-__device__ __forceinline__ u32x4 block_column(const u32x2 (&v)[8], int j) {
+// Column j of an 8 x W block (W = 4 or 8) held as eight rows of W 16-bit
+// values (u32x2 or u32x4 each), as one 128-bit row of eight values (row i in
+// element i).
+template <typename Row>
+__device__ __forceinline__ u32x4 block_column(const Row (&v)[8], int j) {
     u32x4 t;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -125,7 +161,12 @@ __device__ __forceinline__ u32x4 block_column(const u32x2 (&v)[8], int j) {
 }
 }  // namespace
 
-template <int FMT, int BM, int BN, int WAVES_M, int WAVES_N, bool DIRECT, bool VEC>
+// BTR: B is copied into LDS as stored (k rows of n values, straight from
+// global memory like A) and its fragments are read with ds_read_b64_tr_b16.
+// The 16-byte chunk c of B row r sits at chunk position c ^ 4 (r % 4): the
+// 32 lanes of one transposed read cover rows kb .. kb+3 and 32 consecutive n
+// (four chunks), 16 distinct chunk positions, all 64 banks once.
+template <int FMT, int BM, int BN, int WAVES_M, int WAVES_N, bool DIRECT, bool VEC, bool BTR>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
 void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     constexpr int NW = WAVES_M * WAVES_N;
@@ -133,12 +174,19 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
     constexpr int FM = WM / 32, FN = WN / 32;             // 32 x 32 blocks per wave
     constexpr int A_CHUNKS = BM * kCPR / NT;              // register-staged A chunks per thread
-    constexpr int NB4 = BN / 4;                           // 4-wide n blocks per k row of B
-    constexpr int B_BLOCKS = (kBK / 8) * NB4 / NT;        // 8 x 4 blocks of B per thread
+    // B is moved in blocks of 8 k rows x BW n: BW = 8 (128-bit loads) when the
+    // blocks divide evenly among the threads, else BW = 4 (64-bit loads)
+    constexpr int BW = ((kBK / 8) * (BN / 8)) % NT == 0 ? 8 : 4;
+    constexpr int NBW = BN / BW;                          // n blocks per k-block row of B
+    constexpr int B_BLOCKS = (kBK / 8) * NBW / NT;        // 8 x BW blocks of B per thread
     constexpr int A_COPIES = BM / 8 / NW;                 // direct 1 KB copies per wave
+    constexpr int CPRB = BN / 8;                          // BTR: 16-byte chunks per B row
+    constexpr int B_COPIES = kBK * BN * 2 / 1024 / NW;    // BTR: direct 1 KB copies per wave
+    static_assert(!BTR || (DIRECT && CPRB >= 16 && 64 % CPRB == 0 && B_COPIES * NW * 1024 == kBK * BN * 2),
+                  "transposed-read B tile");
     constexpr int STAGE = (BM + BN) * kBK;                // 16-bit elements per stage
     static_assert(WM % 32 == 0 && WN % 32 == 0, "tile shape");
-    static_assert(A_CHUNKS * NT == BM * kCPR && B_BLOCKS * NT == (kBK / 8) * NB4, "copy split");
+    static_assert(A_CHUNKS * NT == BM * kCPR && B_BLOCKS * NT == (kBK / 8) * NBW, "copy split");
     static_assert(!DIRECT || (VEC && A_COPIES * NW * 8 == BM), "direct copy split");
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
 
@@ -207,35 +255,95 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
         }
     };
 
-    // ---- B: 8 x 4 blocks, q = tid + u NT: n block q % NB4, k block q / NB4
-    u32x2 rb[B_BLOCKS][8];
+    // ---- B: 8 x BW blocks, q = tid + u NT: n block q % NBW, k block q / NBW
+    using BRow = typename std::conditional<BW == 8, u32x4, u32x2>::type;
+    BRow rb[BTR ? 1 : B_BLOCKS][8];
     auto load_b_fast = [&](int k0) {
 #pragma unroll
         for (int u = 0; u < B_BLOCKS; ++u) {
-            const int q = tid + u * NT, nb = q % NB4, kb = q / NB4;
-            const uint16_t* b = p.B + (int64_t)(k0 + 8 * kb) * p.ldb + n0 + 4 * nb;
+            const int q = tid + u * NT, nb = q % NBW, kb = q / NBW;
+            const uint16_t* b = p.B + (int64_t)(k0 + 8 * kb) * p.ldb + n0 + BW * nb;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) __builtin_memcpy(&rb[u][i], b + i * p.ldb, 8);
+            for (int i = 0; i < 8; ++i) __builtin_memcpy(&rb[u][i], b + i * p.ldb, 2 * BW);
         }
     };
     auto load_b_ghost = [&](int k0) {
 #pragma unroll
         for (int u = 0; u < B_BLOCKS; ++u) {
-            const int q = tid + u * NT, nb = q % NB4, kb = q / NB4;
+            const int q = tid + u * NT, nb = q % NBW, kb = q / NBW;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                rb[u][i] = load4_ghost16<VEC>(p.B, k0 + 8 * kb + i, p.K, n0 + 4 * nb, p.N, p.ldb);
+            for (int i = 0; i < 8; ++i) {
+                if constexpr (BW == 8)
+                    rb[u][i] = load8_ghost<VEC>(p.B, k0 + 8 * kb + i, p.K, n0 + 8 * nb, p.N, p.ldb);
+                else
+                    rb[u][i] = load4_ghost16<VEC>(p.B, k0 + 8 * kb + i, p.K, n0 + 4 * nb, p.N, p.ldb);
+            }
         }
     };
+    // Row n = BW nb + j of the LDS tile gets column j of the block.  With
+    // BW = 8 the eight lanes of one store cycle write rows 8 l + j, with
+    // BW = 4 rows 4 l + j: f spreads both over eight chunk positions.
     auto store_b = [&](int buf) {
         uint16_t* bs = lds + buf * STAGE + BM * kBK;
 #pragma unroll
         for (int u = 0; u < B_BLOCKS; ++u) {
-            const int q = tid + u * NT, nb = q % NB4, kb = q / NB4;
+            const int q = tid + u * NT, nb = q % NBW, kb = q / NBW;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<u32x4*>(&bs[lds_elem(4 * nb + j, kb)]) = block_column(rb[u], j);
+            for (int j = 0; j < BW; ++j)
+                *reinterpret_cast<u32x4*>(&bs[lds_elem(BW * nb + j, kb)]) = block_column(rb[u], j);
         }
+    };
+
+    // ---- BTR: B as stored.  Element offset of chunk c of B row r:
+    auto b_elem = [](int r, int c) { return r * BN + 8 * (c ^ (4 * (r & 3))); };
+    // Direct copy j of this wave fills B rows R .. R + 64/CPRB - 1 with
+    // R = (64/CPRB) (wave + j NW); lane l writes physical chunk l % CPRB of
+    // row R + l / CPRB.
+    int64_t b_doff[BTR ? B_COPIES : 1];
+    if constexpr (BTR) {
+#pragma unroll
+        for (int j = 0; j < B_COPIES; ++j) {
+            const int row = (64 / CPRB) * (wave_u + j * NW) + lane / CPRB;
+            b_doff[j] = (int64_t)row * p.ldb + n0 + 8 * ((lane % CPRB) ^ (4 * (row & 3)));
+        }
+    }
+    auto direct_b = [&](int k0, int buf) {
+        if constexpr (BTR) {
+            uint16_t* bs = lds + buf * STAGE + BM * kBK;
+            const uint16_t* b = p.B + (int64_t)k0 * p.ldb;
+#pragma unroll
+            for (int j = 0; j < B_COPIES; ++j)
+                copy16_to_lds(b + b_doff[j], bs + (64 / CPRB) * (wave_u + j * NW) * BN);
+        }
+    };
+    // Ghost phases of a BTR kernel: B rows loaded and stored chunk by chunk
+    // (no registers held across the math; these phases are rare).
+    auto ghost_b_now = [&](int k0, int buf) {
+        if constexpr (BTR) {
+            uint16_t* bs = lds + buf * STAGE + BM * kBK;
+#pragma unroll
+            for (int u = 0; u < kBK * CPRB / NT; ++u) {
+                const int q = tid + u * NT, r = q / CPRB, c = q % CPRB;
+                *reinterpret_cast<u32x4*>(&bs[b_elem(r, c)]) =
+                    load8_ghost<VEC>(p.B, k0 + r, p.K, n0 + 8 * c, p.N, p.ldb);
+            }
+        }
+    };
+    // Transposed fragment of B: lane (g = lane / 16, j = lane % 16) addresses
+    // row 16 s + 8 (g / 2) + 4 r + j / 4, column n + 16 (g % 2) + 4 (j % 4)
+    // for reads r = 0, 1 (k 0..3 and 4..7 of its lane half).
+    const int tr_g = lane >> 4, tr_j = lane & 15;
+    auto read_b_tr = [&](const uint16_t* bs, int s, int f) {
+        const int n = wn * WN + f * 32 + 16 * (tr_g & 1) + 4 * (tr_j & 3);
+        u32x4 out;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int row = 16 * s + 8 * (tr_g >> 1) + 4 * r + (tr_j >> 2);
+            const u32x2 v = read_tr16(lds_addr(bs + b_elem(row, n >> 3) + 4 * ((n >> 2) & 1)));
+            out[2 * r] = v[0];
+            out[2 * r + 1] = v[1];
+        }
+        return out;
     };
 
     floatx16 acc[FM][FN];
@@ -246,22 +354,54 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    auto math = [&](int buf) {
+    // The fragments of 16-deep step s are read while the matrix instructions
+    // of step s - 1 run (two register sets), so LDS latency hides behind them.
+    auto read_frags = [&](const uint16_t* as, const uint16_t* bs, int s, u32x4 (&a)[FM], u32x4 (&b)[FN]) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+            a[f] = *reinterpret_cast<const u32x4*>(&as[lds_elem(wm * WM + f * 32 + li, 2 * s + lh)]);
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+            if constexpr (BTR) b[f] = read_b_tr(bs, s, f);
+            else b[f] = *reinterpret_cast<const u32x4*>(&bs[lds_elem(wn * WN + f * 32 + li, 2 * s + lh)]);
+        }
+    };
+    // One wave per SIMD (128 x 128 wave tiles, accumulators in AGPRs): the
+    // next step's fragment reads and the next stage's B stores are placed
+    // among the matrix instructions explicitly.
+    constexpr bool PIPE = FM * FN >= 16;
+    // before_last() runs just before the last step's matrix instructions
+    // (the next stage's stores: they write the other LDS stage).
+    auto math = [&](int buf, auto&& before_last) {
         const uint16_t* as = lds + buf * STAGE;
         const uint16_t* bs = as + BM * kBK;
+        u32x4 a[2][FM], b[2][FN];
+        read_frags(as, bs, 0, a[0], b[0]);
 #pragma unroll
         for (int s = 0; s < kBK / 16; ++s) {
-            u32x4 a[FM], b[FN];
-#pragma unroll
-            for (int f = 0; f < FM; ++f)
-                a[f] = *reinterpret_cast<const u32x4*>(&as[lds_elem(wm * WM + f * 32 + li, 2 * s + lh)]);
-#pragma unroll
-            for (int f = 0; f < FN; ++f)
-                b[f] = *reinterpret_cast<const u32x4*>(&bs[lds_elem(wn * WN + f * 32 + li, 2 * s + lh)]);
+            // this step's transposed reads were issued one step ago
+            if constexpr (BTR) wait_tied(b[s & 1]);
+            if (s + 1 < kBK / 16) {
+                read_frags(as, bs, s + 1, a[(s + 1) & 1], b[(s + 1) & 1]);
+                // keep the reads ahead of this step's matrix instructions
+                if constexpr (PIPE) __builtin_amdgcn_sched_barrier(0);
+            } else {
+                before_last();
+            }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<FMT>(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<FMT>(a[s & 1][i], b[s & 1][j], acc[i][j]);
+        }
+        if constexpr (PIPE && !BTR) {
+            // last step: one LDS store after each of the first matrix
+            // instructions, the transposes in between
+#pragma unroll
+            for (int t = 0; t < B_BLOCKS * BW; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            }
         }
     };
     // The direct copies write LDS behind the compiler's back: wait for them,
@@ -277,15 +417,17 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
         if constexpr (decltype(fast)::value) {
             if constexpr (DIRECT) direct_a(k0, buf);
             else load_a_fast(k0);
-            load_b_fast(k0);
+            if constexpr (BTR) direct_b(k0, buf);
+            else load_b_fast(k0);
         } else {
             load_a_ghost(k0);
-            load_b_ghost(k0);
+            if constexpr (BTR) ghost_b_now(k0, buf);
+            else load_b_ghost(k0);
         }
     };
     auto finish_tiles = [&](int buf, auto fast) {
         if constexpr (!(DIRECT && decltype(fast)::value)) store_a(buf);
-        store_b(buf);
+        if constexpr (!BTR) store_b(buf);
     };
     // One phase on stage ph & 1 while the next phase's tiles (PF: 0 none,
     // 1 fast, 2 ghost) go to the other stage.
@@ -297,11 +439,17 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
         // keep the next phase's loads ahead of the math, so their latency
         // hides behind it (the scheduler would otherwise sink them to their use)
         if constexpr (PF != 0) __builtin_amdgcn_sched_barrier(0);
-        math(cur);
-        // and keep their use (B's transpose, the LDS stores) after the math
-        if constexpr (PF != 0) __builtin_amdgcn_sched_barrier(0);
-        if constexpr (PF == 1) finish_tiles(cur ^ 1, std::true_type{});
-        if constexpr (PF == 2) finish_tiles(cur ^ 1, std::false_type{});
+        if constexpr (PIPE && PF == 1) {
+            // the stores of the next stage go in among the last step's
+            // matrix instructions
+            math(cur, [&]() { finish_tiles(cur ^ 1, std::true_type{}); });
+        } else {
+            math(cur, []() {});
+            // keep the loads' use (B's transpose, the LDS stores) after the math
+            if constexpr (PF != 0) __builtin_amdgcn_sched_barrier(0);
+            if constexpr (PF == 1) finish_tiles(cur ^ 1, std::true_type{});
+            if constexpr (PF == 2) finish_tiles(cur ^ 1, std::false_type{});
+        }
         end_phase();
     };
     using none = std::integral_constant<int, 0>;
@@ -342,10 +490,10 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
 namespace {
 using Launch16 = hipError_t (*)(const Gemm16Args&, hipStream_t, int, int, int, unsigned);
 
-template <int FMT, int BM, int BN, int WAVES_M, int WAVES_N, bool DIRECT, bool VEC>
+template <int FMT, int BM, int BN, int WAVES_M, int WAVES_N, bool DIRECT, bool VEC, bool BTR>
 hipError_t launch16(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
                     unsigned blocks) {
-    hipLaunchKernelGGL((gemm16_kernel<FMT, BM, BN, WAVES_M, WAVES_N, DIRECT, VEC>), dim3(blocks),
+    hipLaunchKernelGGL((gemm16_kernel<FMT, BM, BN, WAVES_M, WAVES_N, DIRECT, VEC, BTR>), dim3(blocks),
                        dim3(WAVES_M * WAVES_N * 64), 0, s, p, tiles_m, tiles_n, group_m);
     return hipGetLastError();
 }
@@ -358,15 +506,19 @@ struct MixedConfig {
 
 // Misaligned operands use the element-wise kernel of the same tile shape
 // (never direct copies).
-#define MIXED(BM, BN, WM, WN, D)                                                                \
-    {{launch16<0, BM, BN, WM, WN, false, false>, launch16<0, BM, BN, WM, WN, D, true>},        \
-     {launch16<1, BM, BN, WM, WN, false, false>, launch16<1, BM, BN, WM, WN, D, true>}}
+#define MIXED(BM, BN, WM, WN, D, T)                                                                  \
+    {{launch16<0, BM, BN, WM, WN, false, false, false>, launch16<0, BM, BN, WM, WN, D, true, T>},   \
+     {launch16<1, BM, BN, WM, WN, false, false, false>, launch16<1, BM, BN, WM, WN, D, true, T>}}
 
 const MixedConfig kMixed[] = {
-    {"mixed256x256_bk64_w2x4_directA", 256, 256, 8, MIXED(256, 256, 2, 4, true)},
-    {"mixed256x256_bk64_w2x4", 256, 256, 8, MIXED(256, 256, 2, 4, false)},
-    {"mixed128x128_bk64_w2x2", 128, 128, 8, MIXED(128, 128, 2, 2, false)},
-    {"mixed64x64_bk64_w1x2", 64, 64, 8, MIXED(64, 64, 1, 2, false)},
+    {"mixed256x256_bk64_w2x4_directA", 256, 256, 8, MIXED(256, 256, 2, 4, true, false)},
+    {"mixed256x256_bk64_w2x4", 256, 256, 8, MIXED(256, 256, 2, 4, false, false)},
+    {"mixed128x128_bk64_w2x2", 128, 128, 8, MIXED(128, 128, 2, 2, false, false)},
+    {"mixed64x64_bk64_w1x2", 64, 64, 8, MIXED(64, 64, 1, 2, false, false)},
+    {"mixed256x256_bk64_w2x2_directA", 256, 256, 8, MIXED(256, 256, 2, 2, true, false)},
+    {"mixed256x256_bk64_w2x2_directAB", 256, 256, 8, MIXED(256, 256, 2, 2, true, true)},
+    {"mixed256x256_bk64_w2x4_directAB", 256, 256, 8, MIXED(256, 256, 2, 4, true, true)},
+    {"mixed128x128_bk64_w2x2_directAB", 128, 128, 8, MIXED(128, 128, 2, 2, true, true)},
 };
 #undef MIXED
 constexpr int kNumMixed = (int)(sizeof(kMixed) / sizeof(kMixed[0]));
@@ -375,12 +527,13 @@ constexpr int kNumMixed = (int)(sizeof(kMixed) / sizeof(kMixed[0]));
 int mixed_num_configs() { return kNumMixed; }
 const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed[c].name : nullptr; }
 
-// The largest tile that still gives every CU a workgroup.
+// The largest tile that still gives every CU a workgroup, with both factors
+// copied straight into LDS.
 int mixed_pick_config(int M, int N, int /*K*/) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
-    if (t256 >= 256) return 0;
-    if (t128 >= 256) return 2;
+    if (t256 >= 256) return 6;
+    if (t128 >= 256) return 7;
     return 3;
 }
 

@@ -12,7 +12,7 @@
 // On wave64 a 16 x 16 workgroup is four waves, each covering four rows of
 // sixteen outputs: the B read of a wave is four copies of 16 consecutive
 // floats and the A read is four broadcast addresses.
-#include "gemm_internal.h"
+#include "launch.h"
 
 namespace gemmf32 {
 

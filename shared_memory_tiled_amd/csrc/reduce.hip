@@ -21,7 +21,7 @@
 //                     (deterministic; bound by HBM reads)
 // Versions 0-2 and 4 write partials to the caller's workspace; every version
 // is deterministic except 3.
-#include "gemm_internal.h"
+#include "launch.h"
 
 namespace gemmf32 {
 

@@ -25,7 +25,7 @@
 //  * per k step a thread reads 16 floats from LDS for 64 fused multiply-adds
 //    (1 byte of LDS per FMA).  Packed FP32 is disabled for this library, so
 //    the VALU ceiling is half of the chip's fp32 peak.
-#include "gemm_internal.h"
+#include "launch.h"
 
 namespace gemmf32 {
 

@@ -19,7 +19,7 @@
 //    PAD words; PAD = 4 keeps each row 16-byte aligned for the 128-bit LDS
 //    stores.  PAD = 0 and PAD = 1 are built as diagnostic variants so that
 //    the LDS bank-conflict counter can compare the layouts.
-#include "gemm_internal.h"
+#include "launch.h"
 
 namespace gemmf32 {
 

@@ -22,7 +22,7 @@
 //   6 tile64_vec_diag  tile64_vec with tiles handed out in diagonal order
 // Every variant guards each element against the matrix edges; nothing is
 // read or written outside `rows x cols` (in) and `cols x rows` (out).
-#include "gemm_internal.h"
+#include "launch.h"
 
 namespace gemmf32 {
 
