@@ -143,3 +143,64 @@ def test_scalar_pair_stores_would_conflict():
     lanes = [r for r in range(32)]
     words = [w for r in lanes for w in (r, r + 64)]
     assert oracle.bank_conflict_degree(words, 64) == 2
+
+
+# ---- the mixed-precision kernels (16-bit elements; words are 4 bytes) ----
+
+def swz16(r):
+    """Chunk XOR of the 16-bit tiles' k-contiguous rows (128 bytes, 8 chunks)."""
+    return ((r >> 1) ^ (r >> 4)) & 7
+
+
+def test_mixed_fragment_reads_conflict_free():
+    """128-bit fragment reads of the k-contiguous 16-bit tiles: lane (i, h)
+    reads row R + i, chunk 2 s + h; 16 lanes per cycle over 64 banks."""
+    for R in range(0, 256, 32):
+        for s in range(4):
+            words = [(R + i) * 32 + 4 * ((2 * s + h) ^ swz16(R + i)) for h in (0, 1) for i in range(32)]
+            assert degree(words, 4, 64, 16) == 1, (R, s)
+    # without the swizzle, 16 rows of 128 bytes put one chunk in two places
+    plain = [(i) * 32 + 4 * h for h in (0, 1) for i in range(32)]
+    assert degree(plain, 4, 64, 16) == 8
+
+
+@pytest.mark.parametrize("bw,threads,bn", [(4, 512, 256), (8, 256, 256), (4, 256, 128), (4, 128, 64)])
+def test_mixed_b_transposed_stores_conflict_free(bw, threads, bn):
+    """Register-path B stores: thread q writes rows bw nb + j (j < bw) at chunk
+    kb, nb = q % (bn / bw), kb = q / (bn / bw); 128-bit stores are served
+    8 lanes per cycle over 32 banks."""
+    nbw = bn // bw
+    for w0 in range(0, threads, 64):
+        for j in range(bw):
+            words = []
+            for q in range(w0, w0 + 64):
+                nb, kb = q % nbw, q // nbw
+                if kb >= 8:
+                    continue
+                row = bw * nb + j
+                words.append(row * 32 + 4 * (kb ^ swz16(row)))
+            if words:
+                assert degree(words, 4, 32, 8) == 1, (w0, j)
+
+
+@pytest.mark.parametrize("bn", [128, 256])
+def test_mixed_transposed_b_reads_conflict_free(bn):
+    """ds_read_b64_tr_b16 reads of the k-major B tile (rows of bn values,
+    chunk c of row r at c ^ 4 (r % 4)): lane (g, j) reads 8 bytes at row
+    16 s + 8 (g / 2) + 4 r + j / 4, column nf + 16 (g % 2) + 4 (j % 4).
+    Taken as 32 lanes per cycle over 64 banks, every cycle is conflict free;
+    without the XOR the four rows of a group would collide 4 ways."""
+    def words(s, r, nf, xor):
+        out = []
+        for lane in range(64):
+            g, j = lane >> 4, lane & 15
+            row = 16 * s + 8 * (g >> 1) + 4 * r + (j >> 2)
+            n = nf + 16 * (g & 1) + 4 * (j & 3)
+            c = (n >> 3) ^ (4 * (row & 3) if xor else 0)
+            out.append((row * bn + 8 * c + 4 * ((n >> 2) & 1)) // 2)
+        return out
+    for nf in range(0, bn, 32):
+        for s in range(4):
+            for r in range(2):
+                assert degree(words(s, r, nf, True), 2, 64, 32) == 1, (nf, s, r)
+    assert degree(words(0, 0, 0, False), 2, 64, 32) == 4
