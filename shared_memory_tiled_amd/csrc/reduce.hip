@@ -14,10 +14,11 @@
 //   3 atomic          version 2 per block, then one float atomic add per
 //                     block into *out (single pass; the order of the adds
 //                     varies from run to run, so the last bits can too)
-//   4 grid_vec        gfx950 layout: a fixed grid of 1024 blocks walks the
-//                     array with 128-bit loads into four accumulators per
-//                     thread, folds waves by shuffles and blocks through LDS,
-//                     and a second one-block launch folds the 1024 partials
+//   4 grid_vec        gfx950 layout: a fixed grid of 2048 blocks walks the
+//                     array with nontemporal 128-bit loads (streamed data
+//                     that is read once) into four accumulators per thread,
+//                     folds waves by shuffles and blocks through LDS, and a
+//                     second one-block launch folds the 2048 partials
 //                     (deterministic; bound by HBM reads)
 // Versions 0-2 and 4 write partials to the caller's workspace; every version
 // is deterministic except 3.
@@ -28,7 +29,7 @@ namespace gemmf32 {
 namespace {
 
 constexpr int kBlock = 256;          // threads per block, values per block (versions 0-3)
-constexpr int kGridBlocks = 1024;    // version 4: blocks of the first pass
+constexpr int kGridBlocks = 2048;    // version 4: blocks of the first pass
 
 // One wave's 64 values folded into lane 0 by shuffles (offsets 32 .. 1).
 __device__ __forceinline__ float wave_sum(float v) {
@@ -75,6 +76,10 @@ __global__ __launch_bounds__(kBlock) void reduce_block_kernel(int64_t n, const f
 
 __global__ void zero_one_kernel(float* out) { *out = 0.0f; }
 
+// Four floats at 4-byte alignment (a dword-aligned 128-bit load is legal on
+// gfx9, which runs global memory in unaligned mode).
+typedef float floatx4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 // Version 4, first pass: a grid-stride walk over 16-byte chunks.
 __global__ __launch_bounds__(kBlock) void reduce_grid_vec_kernel(int64_t n, const float* in, float* part) {
     __shared__ float wave_part[kBlock / 64];
@@ -83,8 +88,7 @@ __global__ __launch_bounds__(kBlock) void reduce_grid_vec_kernel(int64_t n, cons
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
     for (int64_t c = (int64_t)blockIdx.x * kBlock + tid; c < chunks; c += stride) {
-        floatx4 v;
-        __builtin_memcpy(&v, in + 4 * c, 16);          // 4-byte alignment suffices on gfx9
+        const floatx4_a4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4_a4*>(in + 4 * c));
         a0 += v[0];
         a1 += v[1];
         a2 += v[2];
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(kBlock) void reduce_grid_vec_kernel(int64_t n, cons
     if (tid == 0) part[blockIdx.x] = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
 }
 
-// Version 4, second pass: one block folds `count` (<= 4 * kBlock) partials.
+// Version 4, second pass: one block folds `count` partials.
 __global__ __launch_bounds__(kBlock) void reduce_final_kernel(int count, const float* part, float* out) {
     __shared__ float wave_part[kBlock / 64];
     const int tid = threadIdx.x;

@@ -200,7 +200,7 @@ def test_reduce_workspace_sizes(binding, lib):
     assert binding.reduce_sum_f32_workspace_size(0, 256) == 0
     assert binding.reduce_sum_f32_workspace_size(2, 257) == 4 * 2
     assert binding.reduce_sum_f32_workspace_size(3, 10**9) == 0
-    assert binding.reduce_sum_f32_workspace_size(4, 1) == 4 * 1024
+    assert binding.reduce_sum_f32_workspace_size(4, 1) == 4 * 2048
 
 
 @pytest.mark.parametrize("args,code", [

@@ -29,8 +29,11 @@ def chain_bound(variant: int, n: int) -> float:
         return 8 * passes + 1
     if variant == 3:                         # tree of 256, then atomics block by block
         return 8 + math.ceil(n / 256) + 1
-    stride = 1024 * 256                      # grid_vec: 1024 blocks of 256 threads
-    return math.ceil(n / 4 / stride) + 26
+    # grid_vec: 2048 blocks of 256 threads; per thread a sequential run of
+    # chunks (+1 for the tail), 2 + 6 + 2 levels to the block partial, then
+    # 8 partials per thread, 6 + 2 levels in the second pass
+    stride = 2048 * 256
+    return math.ceil(n / 4 / stride) + 1 + 10 + 16
 
 
 def gpu_sum(x: np.ndarray, variant, dev_x=None) -> float:
