@@ -170,9 +170,11 @@ const char *gemm_f32_status_string(int status);
  * padded tile, 3 XOR-swizzled [32][32] tile, 4 64 x 64 tile with 128-bit
  * global and LDS accesses and an LDS layout conflict free on gfx950, 5 the
  * same with 128 x 128 tiles, 6 variant 4 with tiles handed out in diagonal
- * order.  transpose_f32 uses 6 when a leading dimension is a multiple of
- * 4 KB (concurrent tiles would otherwise crowd the same memory channels),
- * else 4.
+ * order, 7 and 8 variants 6 and 4 with nontemporal global loads and stores.
+ * transpose_f32 uses 6 (with leading dimensions near a multiple of 4 KB,
+ * tiles handed out row by row crowd the same memory channels), and 7 for
+ * inputs of 256 MiB or more (larger than the last-level cache) whose leading
+ * dimension is a multiple of 4 KB.
  */
 int transpose_f32(int64_t rows, int64_t cols, const float *in, int64_t ld_in,
                   float *out, int64_t ld_out, void *stream);

@@ -170,14 +170,17 @@ namespace {
 constexpr int kTransposeAuto = -1;
 
 // The default transpose: 64 x 64 tiles with 128-bit accesses, handed out in
-// diagonal order when a leading dimension is a multiple of 4 KB.  With such
-// strides, tiles handed out row by row make concurrent blocks touch addresses
-// equal modulo a large power of two (the same HBM channels); the diagonal
-// order spreads them.  With other strides the row-by-row order is kept, since
-// it lets concurrent blocks share input rows.
-int pick_transpose(int64_t ld_in, int64_t ld_out) {
+// diagonal order (measured as fast as or faster than row order on every
+// shape tried: with strides near a multiple of 4 KB, tiles handed out row by
+// row make concurrent blocks touch addresses equal modulo a large power of
+// two, the same HBM channels).  Inputs of 256 MiB or more (larger than the
+// last-level cache) with a leading dimension that is a multiple of 4 KB use
+// nontemporal accesses, which measured faster there; elsewhere the
+// measurements were mixed, and the cached form is kept.
+int pick_transpose(int64_t rows, int64_t cols, int64_t ld_in, int64_t ld_out) {
     const bool pow2ish = ((ld_in * 4) % 4096 == 0) || ((ld_out * 4) % 4096 == 0);
-    return pow2ish ? 6 : 4;
+    const bool big = rows * cols * 4 >= ((int64_t)256 << 20);
+    return (pow2ish && big) ? 7 : 6;
 }
 
 int run_transpose(int variant, int64_t rows, int64_t cols, const float* in, int64_t ld_in, float* out,
@@ -194,7 +197,7 @@ int run_transpose(int variant, int64_t rows, int64_t cols, const float* in, int6
         return GEMM_F32_ERR_TOO_LARGE;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_F32_ERR_DEVICE;
-    if (variant == kTransposeAuto) variant = pick_transpose(ld_in, ld_out);
+    if (variant == kTransposeAuto) variant = pick_transpose(rows, cols, ld_in, ld_out);
     const hipError_t e = launch_transpose(variant, (int)rows, (int)cols, in, ld_in, out, ld_out,
                                           reinterpret_cast<hipStream_t>(stream));
     if (e == hipErrorInvalidValue) return GEMM_F32_ERR_TOO_LARGE;

@@ -20,6 +20,9 @@
 //                    conflict free on gfx950's LDS (see the kernel).
 //   5 tile128_vec    the same with a 128 x 128 tile (512-byte row segments)
 //   6 tile64_vec_diag  tile64_vec with tiles handed out in diagonal order
+//   7 tile64_vec_diag_nt, 8 tile64_vec_nt  variants 6 and 4 with nontemporal
+//                    global loads and stores (for arrays larger than the last
+//                    level cache, where every byte is moved once anyway)
 // Every variant guards each element against the matrix edges; nothing is
 // read or written outside `rows x cols` (in) and `cols x rows` (out).
 #include "launch.h"
@@ -76,9 +79,13 @@ __device__ __forceinline__ int tvec_word(int c, int chunk) {
     return c * T + 4 * (chunk ^ ((c >> 2) & 7));
 }
 
+// Four floats at 4-byte alignment (a dword-aligned 128-bit access is legal on
+// gfx9, which runs global memory in unaligned mode).
+typedef float floatx4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 // T x T tile (T = 64 or 128), 256 threads; each thread transposes
-// (T/4)^2 / 256 blocks of 4 x 4.
-template <int T, bool DIAGONAL>
+// (T/4)^2 / 256 blocks of 4 x 4.  NT: nontemporal global accesses.
+template <int T, bool DIAGONAL, bool NT>
 __global__ __launch_bounds__(256) void transpose_tile_vec_kernel(int rows, int cols, const float* in,
                                                                  int64_t ld_in, float* out,
                                                                  int64_t ld_out, int tiles_c) {
@@ -110,7 +117,9 @@ __global__ __launch_bounds__(256) void transpose_tile_vec_kernel(int rows, int c
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 4 * i + e;
-            if (inside) __builtin_memcpy(&v[e], in + (int64_t)(r0 + r) * ld_in + c0 + 4 * j, 16);
+            const float* src = in + (int64_t)(r0 + r) * ld_in + c0 + 4 * j;
+            if (inside && NT) v[e] = __builtin_nontemporal_load(reinterpret_cast<const floatx4_a4*>(src));
+            else if (inside) __builtin_memcpy(&v[e], src, 16);
             else v[e] = load4_ghost(in, r0 + r, rows, c0 + 4 * j, cols, ld_in);   // zeros never reach out
         }
 #pragma unroll
@@ -126,19 +135,22 @@ __global__ __launch_bounds__(256) void transpose_tile_vec_kernel(int rows, int c
         const int q = tid + 256 * u;
         const int c = q / NB, k = q % NB;
         const floatx4 w = *reinterpret_cast<const floatx4*>(&tile[tvec_word<T>(c, k)]);
-        if (inside) __builtin_memcpy(out + (int64_t)(c0 + c) * ld_out + r0 + 4 * k, &w, 16);
+        float* dst = out + (int64_t)(c0 + c) * ld_out + r0 + 4 * k;
+        if (inside && NT) __builtin_nontemporal_store(floatx4_a4(w), reinterpret_cast<floatx4_a4*>(dst));
+        else if (inside) __builtin_memcpy(dst, &w, 16);
         else store4_guarded(out, c0 + c, cols, r0 + 4 * k, rows, ld_out, w);
     }
 }
 
 }  // namespace
 
-int transpose_num_variants() { return 7; }
+int transpose_num_variants() { return 9; }
 
 const char* transpose_variant_name(int v) {
-    static const char* const names[] = {"naive", "tile32", "tile32_pad", "tile32_swizzle",
-                                        "tile64_vec", "tile128_vec", "tile64_vec_diag"};
-    return (v >= 0 && v < 7) ? names[v] : nullptr;
+    static const char* const names[] = {"naive",           "tile32",         "tile32_pad",
+                                        "tile32_swizzle",  "tile64_vec",     "tile128_vec",
+                                        "tile64_vec_diag", "tile64_vec_diag_nt", "tile64_vec_nt"};
+    return (v >= 0 && v < 9) ? names[v] : nullptr;
 }
 
 hipError_t launch_transpose(int variant, int rows, int cols, const float* in, int64_t ld_in,
@@ -167,16 +179,24 @@ hipError_t launch_transpose(int variant, int rows, int cols, const float* in, in
                                in, ld_in, out, ld_out, tiles_c);
             break;
         case 5:
-            hipLaunchKernelGGL((transpose_tile_vec_kernel<128, false>), grid, dim3(256), 0, s, rows, cols,
-                               in, ld_in, out, ld_out, tiles_c);
+            hipLaunchKernelGGL((transpose_tile_vec_kernel<128, false, false>), grid, dim3(256), 0, s, rows,
+                               cols, in, ld_in, out, ld_out, tiles_c);
             break;
         case 6:
-            hipLaunchKernelGGL((transpose_tile_vec_kernel<64, true>), grid, dim3(256), 0, s, rows, cols,
-                               in, ld_in, out, ld_out, tiles_c);
+            hipLaunchKernelGGL((transpose_tile_vec_kernel<64, true, false>), grid, dim3(256), 0, s, rows,
+                               cols, in, ld_in, out, ld_out, tiles_c);
+            break;
+        case 7:
+            hipLaunchKernelGGL((transpose_tile_vec_kernel<64, true, true>), grid, dim3(256), 0, s, rows,
+                               cols, in, ld_in, out, ld_out, tiles_c);
+            break;
+        case 8:
+            hipLaunchKernelGGL((transpose_tile_vec_kernel<64, false, true>), grid, dim3(256), 0, s, rows,
+                               cols, in, ld_in, out, ld_out, tiles_c);
             break;
         default:
-            hipLaunchKernelGGL((transpose_tile_vec_kernel<64, false>), grid, dim3(256), 0, s, rows, cols,
-                               in, ld_in, out, ld_out, tiles_c);
+            hipLaunchKernelGGL((transpose_tile_vec_kernel<64, false, false>), grid, dim3(256), 0, s, rows,
+                               cols, in, ld_in, out, ld_out, tiles_c);
             break;
     }
     return hipGetLastError();

@@ -172,7 +172,7 @@ def test_transpose_validation_without_launch(lib, args, code):
 def test_transpose_variants(binding, lib):
     n = binding.transpose_f32_num_variants()
     names = [binding.transpose_f32_variant_name(v) for v in range(n)]
-    assert n == 7 and all(names) and len(set(names)) == n
+    assert n == 9 and all(names) and len(set(names)) == n
     assert binding.transpose_f32_variant_name(n) is None
     code = declared_codes()["GEMM_F32_ERR_INVALID_VARIANT"]
     assert lib.transpose_f32_variant(n, 4, 4, FAKE, 4, FAKE, 4, None) == code
