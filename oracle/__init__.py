@@ -96,9 +96,13 @@ def load(path: str | None = None):
     lib.oracle_gemm16_rows.argtypes = [ctypes.c_int, _i64, _i64, _i64, _hp, _i64, _hp, _i64,
                                        _dp, _i64, _dp, _i64, _i64, _i64, ctypes.c_int]
     lib.oracle_gemm16_rows.restype = ctypes.c_int
+    lib.oracle_gemm16_op_rows.argtypes = [ctypes.c_int, ctypes.c_int] + lib.oracle_gemm16_rows.argtypes
+    lib.oracle_gemm16_op_rows.restype = ctypes.c_int
     lib.oracle_gemm16_entries.argtypes = [ctypes.c_int, _i64, _i64, _i64, _hp, _i64, _hp, _i64,
                                           _i64, _ip, _ip, _dp, _dp]
     lib.oracle_gemm16_entries.restype = ctypes.c_int
+    lib.oracle_gemm16_op_entries.argtypes = [ctypes.c_int, ctypes.c_int] + lib.oracle_gemm16_entries.argtypes
+    lib.oracle_gemm16_op_entries.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -313,34 +317,33 @@ def decode16(fmt, bits, lib=None) -> np.ndarray:
     return out
 
 
-def gemm16(fmt, A: np.ndarray, B: np.ndarray, threads: int = 1, rows=None, lib=None):
-    """Returns (C, S) in binary64 for 16-bit A (M x K) and B (K x N) given as
-    uint16 bit patterns of format ``fmt`` ('bf16' or 'f16')."""
+def gemm16(fmt, A: np.ndarray, B: np.ndarray, threads: int = 1, rows=None, lib=None,
+           op_a="N", op_b="N"):
+    """Returns (C, S) in binary64 for op(A) x op(B), 16-bit factors given as
+    uint16 bit patterns of format ``fmt`` ('bf16' or 'f16').  A and B are
+    the STORED matrices (with op 'T', A is K x M and B is N x K)."""
     lib = lib or load()
-    M, K = A.shape
-    K2, N = B.shape
-    if K != K2:
-        raise ValueError("inner dimensions differ")
+    oa, ob = _op(op_a), _op(op_b)
+    M, N, K = _shapes(A, B, oa, ob)
     C = np.zeros((M, N), dtype=np.float64)
     S = np.zeros((M, N), dtype=np.float64)
     pa, lda = _matrix16_arg(A)
     pb, ldb = _matrix16_arg(B)
     r0, r1 = (0, M) if rows is None else rows
-    rc = lib.oracle_gemm16_rows(_fmt16(fmt), M, N, K, pa, lda, pb, ldb,
-                                C.ctypes.data_as(_dp), max(N, 1), S.ctypes.data_as(_dp), max(N, 1),
-                                r0, r1, int(threads))
+    args = (_fmt16(fmt), M, N, K, pa, lda, pb, ldb,
+            C.ctypes.data_as(_dp), max(N, 1), S.ctypes.data_as(_dp), max(N, 1), r0, r1, int(threads))
+    rc = lib.oracle_gemm16_rows(*args) if oa == 0 and ob == 0 else lib.oracle_gemm16_op_rows(oa, ob, *args)
     if rc != 0:
         raise ValueError(f"oracle 16-bit product rejected its arguments (rc={rc})")
     return C, S
 
 
-def gemm16_entries(fmt, A: np.ndarray, B: np.ndarray, ii, jj, lib=None):
-    """Returns (c, s) for the entries (ii[t], jj[t]) of the 16-bit product."""
+def gemm16_entries(fmt, A: np.ndarray, B: np.ndarray, ii, jj, lib=None, op_a="N", op_b="N"):
+    """Returns (c, s) for the entries (ii[t], jj[t]) of the 16-bit product
+    op(A) x op(B)."""
     lib = lib or load()
-    M, K = A.shape
-    K2, N = B.shape
-    if K != K2:
-        raise ValueError("inner dimensions differ")
+    oa, ob = _op(op_a), _op(op_b)
+    M, N, K = _shapes(A, B, oa, ob)
     ii = np.ascontiguousarray(ii, dtype=np.int64)
     jj = np.ascontiguousarray(jj, dtype=np.int64)
     if ii.shape != jj.shape or ii.ndim != 1:
@@ -349,9 +352,9 @@ def gemm16_entries(fmt, A: np.ndarray, B: np.ndarray, ii, jj, lib=None):
     s = np.zeros(ii.shape[0], dtype=np.float64)
     pa, lda = _matrix16_arg(A)
     pb, ldb = _matrix16_arg(B)
-    rc = lib.oracle_gemm16_entries(_fmt16(fmt), M, N, K, pa, lda, pb, ldb, ii.shape[0],
-                                   ii.ctypes.data_as(_ip), jj.ctypes.data_as(_ip),
-                                   c.ctypes.data_as(_dp), s.ctypes.data_as(_dp))
+    args = (_fmt16(fmt), M, N, K, pa, lda, pb, ldb, ii.shape[0], ii.ctypes.data_as(_ip),
+            jj.ctypes.data_as(_ip), c.ctypes.data_as(_dp), s.ctypes.data_as(_dp))
+    rc = lib.oracle_gemm16_entries(*args) if oa == 0 and ob == 0 else lib.oracle_gemm16_op_entries(oa, ob, *args)
     if rc != 0:
         raise ValueError(f"oracle 16-bit entries rejected their arguments (rc={rc})")
     return c, s

@@ -12,6 +12,8 @@
  *     matrix units that take FP16 or BF16 inputs and accumulate in FP32; in
  *     "Mixed Precision", BF16 has the exponent range of FP32, while FP16's
  *     narrow range is what loss scaling works around;
+ *   - same chapter: the backward pass needs the products with a transposed
+ *     factor (X^T dY, dY W^T); op(A), op(B) below, as in gemm_oracle.c;
  *   - same notes, reduction chapter, numerical remarks: sums of 16-bit values
  *     risk overflow, hence an FP32 accumulator;
  *   - the two formats as they are defined.  binary16 (IEEE 754-2008): sign
@@ -90,13 +92,15 @@ static double *decode_table(int format)
 }
 
 /* c = sum_{k<K} a(i,k) b(k,j), s = sum_k |a(i,k) b(k,j)|, with a(i,k) =
- * value of A[i*lda + k] and b(k,j) = value of B[k*ldb + j]. */
-static void dot16(const double *val, int64_t K, const uint16_t *A, int64_t lda,
-                  const uint16_t *B, int64_t ldb, int64_t i, int64_t j, double *c, double *s)
+ * value of A[i*a_rs + k*a_cs] and b(k,j) = value of B[k*b_rs + j*b_cs]: a
+ * factor used as stored has strides (ld, 1), its transpose (1, ld). */
+static void dot16(const double *val, int64_t K, const uint16_t *A, int64_t a_rs, int64_t a_cs,
+                  const uint16_t *B, int64_t b_rs, int64_t b_cs, int64_t i, int64_t j,
+                  double *c, double *s)
 {
     double acc = 0.0, mag = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-        const double prod = val[A[i * lda + k]] * val[B[k * ldb + j]];
+        const double prod = val[A[i * a_rs + k * a_cs]] * val[B[k * b_rs + j * b_cs]];
         acc += prod;
         mag += fabs(prod);
     }
@@ -107,8 +111,8 @@ static void dot16(const double *val, int64_t K, const uint16_t *A, int64_t lda,
 struct rows16_job {
     const double *val;
     int64_t row_begin, row_end, N, K;
-    const uint16_t *A; int64_t lda;
-    const uint16_t *B; int64_t ldb;
+    const uint16_t *A; int64_t a_rs, a_cs;
+    const uint16_t *B; int64_t b_rs, b_cs;
     double *C; int64_t ldc;
     double *S; int64_t lds;
 };
@@ -119,7 +123,7 @@ static void *rows16_worker(void *arg)
     for (int64_t i = job->row_begin; i < job->row_end; ++i)
         for (int64_t j = 0; j < job->N; ++j) {
             double c, s;
-            dot16(job->val, job->K, job->A, job->lda, job->B, job->ldb, i, j, &c, &s);
+            dot16(job->val, job->K, job->A, job->a_rs, job->a_cs, job->B, job->b_rs, job->b_cs, i, j, &c, &s);
             job->C[i * job->ldc + j] = c;
             if (job->S)
                 job->S[i * job->lds + j] = s;
@@ -127,25 +131,41 @@ static void *rows16_worker(void *arg)
     return NULL;
 }
 
-/* C (binary64, leading dimension ldc) = A x B for 16-bit A (M x K, lda >= K)
- * and B (K x N, ldb >= N) of the given format; S (optional) = sum of
- * |products|.  Rows [row_begin, row_end) only; threads split the rows, each
- * element computed by one thread with the same code. */
-int oracle_gemm16_rows(int format, int64_t M, int64_t N, int64_t K,
-                       const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
-                       double *C, int64_t ldc, double *S, int64_t lds,
-                       int64_t row_begin, int64_t row_end, int threads)
+/* Strides of op(X) for a stored row-major X with leading dimension ld: op 0
+ * uses X as stored, op 1 its transpose. */
+static void op16_strides(int op, int64_t ld, int64_t *rs, int64_t *cs)
+{
+    if (op == 0) { *rs = ld; *cs = 1; }
+    else         { *rs = 1;  *cs = ld; }
+}
+
+/* C (binary64, leading dimension ldc) = op(A) x op(B) for 16-bit factors of
+ * the given format.  op_a = 0: A stored M x K (lda >= K); op_a = 1: A stored
+ * K x M (lda >= M).  op_b = 0: B stored K x N (ldb >= N); op_b = 1: B stored
+ * N x K (ldb >= K).  S (optional) = sum of |products|.  Rows [row_begin,
+ * row_end) only; threads split the rows, each element computed by one thread
+ * with the same code. */
+int oracle_gemm16_op_rows(int op_a, int op_b, int format, int64_t M, int64_t N, int64_t K,
+                          const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                          double *C, int64_t ldc, double *S, int64_t lds,
+                          int64_t row_begin, int64_t row_end, int threads)
 {
     if (format != FMT_BF16 && format != FMT_F16)
         return ORACLE_BAD_ARG;
+    if ((op_a != 0 && op_a != 1) || (op_b != 0 && op_b != 1))
+        return ORACLE_BAD_ARG;
     if (M < 0 || N < 0 || K < 0 || row_begin < 0 || row_end > M || row_begin > row_end)
         return ORACLE_BAD_ARG;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    const int64_t a_cols = op_a == 0 ? K : M, b_cols = op_b == 0 ? N : K;
+    if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) || ldc < (N > 1 ? N : 1))
         return ORACLE_BAD_ARG;
     if (S && lds < (N > 1 ? N : 1))
         return ORACLE_BAD_ARG;
     if ((row_end > row_begin && N > 0) && (!C || (K > 0 && (!A || !B))))
         return ORACLE_BAD_ARG;
+    int64_t a_rs, a_cs, b_rs, b_cs;
+    op16_strides(op_a, lda, &a_rs, &a_cs);
+    op16_strides(op_b, ldb, &b_rs, &b_cs);
     double *val = decode_table(format);
     int64_t rows = row_end - row_begin;
     if (threads < 1)
@@ -163,7 +183,7 @@ int oracle_gemm16_rows(int format, int64_t M, int64_t N, int64_t K,
     int64_t per = rows / threads, extra = rows % threads, r = row_begin;
     for (int t = 0; t < threads; ++t) {
         int64_t take = per + (t < extra ? 1 : 0);
-        jobs[t] = (struct rows16_job){val, r, r + take, N, K, A, lda, B, ldb, C, ldc, S, lds};
+        jobs[t] = (struct rows16_job){val, r, r + take, N, K, A, a_rs, a_cs, B, b_rs, b_cs, C, ldc, S, lds};
         r += take;
     }
     int started = 0;
@@ -183,29 +203,53 @@ int oracle_gemm16_rows(int format, int64_t M, int64_t N, int64_t K,
     return ORACLE_OK;
 }
 
-/* Selected entries (ii[t], jj[t]) of A x B only, for shapes too large for
- * the full product on the host. */
-int oracle_gemm16_entries(int format, int64_t M, int64_t N, int64_t K,
-                          const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
-                          int64_t count, const int64_t *ii, const int64_t *jj,
-                          double *out_c, double *out_s)
+/* The plain product A x B (both as stored), rows [row_begin, row_end). */
+int oracle_gemm16_rows(int format, int64_t M, int64_t N, int64_t K,
+                       const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                       double *C, int64_t ldc, double *S, int64_t lds,
+                       int64_t row_begin, int64_t row_end, int threads)
+{
+    return oracle_gemm16_op_rows(0, 0, format, M, N, K, A, lda, B, ldb, C, ldc, S, lds,
+                                 row_begin, row_end, threads);
+}
+
+/* Selected entries (ii[t], jj[t]) of op(A) x op(B) only (op flags as in
+ * oracle_gemm16_op_rows), for shapes too large for the full product. */
+int oracle_gemm16_op_entries(int op_a, int op_b, int format, int64_t M, int64_t N, int64_t K,
+                             const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                             int64_t count, const int64_t *ii, const int64_t *jj,
+                             double *out_c, double *out_s)
 {
     if (format != FMT_BF16 && format != FMT_F16)
         return ORACLE_BAD_ARG;
+    if ((op_a != 0 && op_a != 1) || (op_b != 0 && op_b != 1))
+        return ORACLE_BAD_ARG;
     if (M < 0 || N < 0 || K < 0 || count < 0)
         return ORACLE_BAD_ARG;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1))
+    const int64_t a_cols = op_a == 0 ? K : M, b_cols = op_b == 0 ? N : K;
+    if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1))
         return ORACLE_BAD_ARG;
     if (count > 0 && (!ii || !jj || !out_c || !out_s || (K > 0 && (!A || !B))))
         return ORACLE_BAD_ARG;
     for (int64_t t = 0; t < count; ++t)
         if (ii[t] < 0 || ii[t] >= M || jj[t] < 0 || jj[t] >= N)
             return ORACLE_BAD_ARG;
+    int64_t a_rs, a_cs, b_rs, b_cs;
+    op16_strides(op_a, lda, &a_rs, &a_cs);
+    op16_strides(op_b, ldb, &b_rs, &b_cs);
     double *val = decode_table(format);
     if (!val)
         return ORACLE_BAD_ARG;
     for (int64_t t = 0; t < count; ++t)
-        dot16(val, K, A, lda, B, ldb, ii[t], jj[t], &out_c[t], &out_s[t]);
+        dot16(val, K, A, a_rs, a_cs, B, b_rs, b_cs, ii[t], jj[t], &out_c[t], &out_s[t]);
     free(val);
     return ORACLE_OK;
+}
+
+int oracle_gemm16_entries(int format, int64_t M, int64_t N, int64_t K,
+                          const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                          int64_t count, const int64_t *ii, const int64_t *jj,
+                          double *out_c, double *out_s)
+{
+    return oracle_gemm16_op_entries(0, 0, format, M, N, K, A, lda, B, ldb, count, ii, jj, out_c, out_s);
 }

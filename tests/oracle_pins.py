@@ -574,6 +574,42 @@ def check_gemm16_extremes(lib):
         assert C[0, 0] == 0.0 and S[0, 0] == 4.0     # 1 - 1 + 1 - 1
 
 
+def check_gemm16_transposed_operands(lib):
+    """op(A) and op(B) for every op pair and both formats: bit equality with
+    the plain 16-bit product on explicitly transposed copies (C and S), in
+    padded odd-offset views, for full products, row bands and entries; and
+    exact integer brute force for the logical factors."""
+    gen = np.random.default_rng(122)
+    for fmt in ("bf16", "f16"):
+        for (M, N, K) in ((1, 1, 1), (17, 33, 65), (64, 31, 129)):
+            A = _finite16(gen, (M, K), fmt)
+            B = _finite16(gen, (K, N), fmt)
+            C, S = oracle.gemm16(fmt, A, B, lib=lib)
+            for op_a, op_b in (("T", "N"), ("N", "T"), ("T", "T")):
+                As = np.ascontiguousarray(A.T) if op_a == "T" else A
+                Bs = np.ascontiguousarray(B.T) if op_b == "T" else B
+                Ap = np.full(3 + As.shape[0] * (As.shape[1] + 5) + 7, 0x7E00, np.uint16)
+                Av = Ap[3:3 + As.shape[0] * (As.shape[1] + 5)].reshape(As.shape[0], As.shape[1] + 5)[:, :As.shape[1]]
+                Av[:, :] = As
+                Co, So = oracle.gemm16(fmt, Av, Bs, threads=3, lib=lib, op_a=op_a, op_b=op_b)
+                assert np.array_equal(Co, C) and np.array_equal(So, S), (fmt, M, N, K, op_a, op_b)
+                ii = gen.integers(0, M, 15)
+                jj = gen.integers(0, N, 15)
+                c, sv = oracle.gemm16_entries(fmt, Av, Bs, ii, jj, lib=lib, op_a=op_a, op_b=op_b)
+                assert np.array_equal(c, C[ii, jj]) and np.array_equal(sv, S[ii, jj]), (fmt, op_a, op_b)
+    for fmt in ("bf16", "f16"):
+        for (M, N, K) in ((2, 3, 5), (5, 1, 8), (8, 5, 3)):
+            Ai = _ints(gen, M, K, -9, 9)
+            Bi = _ints(gen, K, N, -9, 9)
+            Ce, _ = _py_product(Ai, Bi)
+            for op_a, op_b in (("T", "N"), ("N", "T"), ("T", "T")):
+                As = np.ascontiguousarray(Ai.T) if op_a == "T" else Ai
+                Bs = np.ascontiguousarray(Bi.T) if op_b == "T" else Bi
+                Co, _ = oracle.gemm16(fmt, _encode_exact16(As, fmt), _encode_exact16(Bs, fmt), lib=lib,
+                                      op_a=op_a, op_b=op_b)
+                assert np.array_equal(Co, np.array(Ce, dtype=np.float64).reshape(M, N)), (fmt, op_a, op_b)
+
+
 ALL_CHECKS = [
     check_bruteforce_tiny, check_bruteforce_tile_straddling, check_identity_and_zero,
     check_closed_forms, check_library_float64, check_linearity_and_scaling,
@@ -583,7 +619,7 @@ ALL_CHECKS = [
     check_naive_roofline_context, check_bank_model, check_transpose, check_sector_model,
     check_sum, check_tree_bookkeeping, check_multipass,
     check_decode16_all_patterns, check_gemm16_equals_fp32_oracle, check_gemm16_bruteforce,
-    check_gemm16_extremes,
+    check_gemm16_extremes, check_gemm16_transposed_operands,
 ]
 
 

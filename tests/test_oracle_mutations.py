@@ -70,12 +70,19 @@ MUTANTS.update({
     "decode16_sign_ignored": ("return neg ? -v : v;", "return v;"),
     "gemm16_drops_last_term": ("for (int64_t k = 0; k < K; ++k) {\n        const double prod",
                                "for (int64_t k = 0; k < K - 1; ++k) {\n        const double prod"),
-    "gemm16_B_uses_lda": ("val[B[k * ldb + j]]", "val[B[k * lda + j]]"),
+    "gemm16_B_uses_lda": ("val[B[k * b_rs + j * b_cs]]", "val[B[k * a_rs + j * b_cs]]"),
     "gemm16_format_ignored": ("double *val = decode_table(format);\n    int64_t rows",
                               "double *val = decode_table(FMT_BF16);\n    int64_t rows"),
+    "gemm16_transpose_ignored": ("    else         { *rs = 1;  *cs = ld; }\n}\n\n/* C (binary64",
+                                 "    else         { *rs = ld; *cs = 1; }\n}\n\n/* C (binary64"),
+    "gemm16_op_flags_swapped": ("op16_strides(op_a, lda, &a_rs, &a_cs);\n    op16_strides(op_b, ldb, &b_rs, &b_cs);\n    double *val = decode_table(format);\n    int64_t rows",
+                                "op16_strides(op_b, lda, &a_rs, &a_cs);\n    op16_strides(op_a, ldb, &b_rs, &b_cs);\n    double *val = decode_table(format);\n    int64_t rows"),
+    "gemm16_entries_op_ignored": ("op16_strides(op_a, lda, &a_rs, &a_cs);\n    op16_strides(op_b, ldb, &b_rs, &b_cs);\n    double *val = decode_table(format);\n    if (!val)",
+                                  "op16_strides(0, lda, &a_rs, &a_cs);\n    op16_strides(0, ldb, &b_rs, &b_cs);\n    double *val = decode_table(format);\n    if (!val)"),
 })
 GEMM16_MUTANTS = {"bf16_bias_off", "f16_subnormal_as_normal", "f16_fraction_width", "decode16_sign_ignored",
-                  "gemm16_drops_last_term", "gemm16_B_uses_lda", "gemm16_format_ignored"}
+                  "gemm16_drops_last_term", "gemm16_B_uses_lda", "gemm16_format_ignored",
+                  "gemm16_transpose_ignored", "gemm16_op_flags_swapped", "gemm16_entries_op_ignored"}
 GEMM16_SRC = os.path.join(ROOT, "oracle", "gemm16_oracle.c")
 TRANSPOSE_MUTANTS = {"transpose_not_transposed", "transpose_wrong_in_ld", "transpose_drops_last_row",
                      "sectors_end_byte_ignored", "sectors_duplicates_counted"}
