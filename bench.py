@@ -23,7 +23,7 @@ Extra modes (used for counter runs under rocprofv3):
                         (default 2^28; metric GB/s read, bound HBM)
     --row mixed         time gemm_mixed on the workload rounded to --format
                         (bf16 or f16; binary32 result; metric TFLOP/s against
-                        the 16-bit matrix peak)
+                        the 16-bit matrix peak); with --op, gemm_mixed_op
     --op XY             time gemm_f32_op with op(A) = X, op(B) = Y (N or T):
                         the transposed factor is stored transposed, with a
                         compact leading dimension
@@ -166,18 +166,18 @@ def bench_reduce(args) -> int:
     return 0
 
 
-def cpu_baseline16(fmt, A, B, w, budget_s: float = 10.0):
+def cpu_baseline16(fmt, A, B, w, budget_s: float = 10.0, op_a="N", op_b="N"):
     """The 16-bit oracle as it is, on all host cores, over a band of rows."""
     import oracle
     cores = len(os.sched_getaffinity(0))
     rows = min(cores, w.M)
     t0 = time.perf_counter()
-    oracle.gemm16(fmt, A.view, B.view, threads=cores, rows=(0, rows))
+    oracle.gemm16(fmt, A.view, B.view, threads=cores, rows=(0, rows), op_a=op_a, op_b=op_b)
     probe = time.perf_counter() - t0
     rows = max(rows, min(w.M, int(rows * budget_s / max(probe, 1e-3))))
     rows -= rows % cores if rows > cores else 0
     t0 = time.perf_counter()
-    oracle.gemm16(fmt, A.view, B.view, threads=cores, rows=(0, rows))
+    oracle.gemm16(fmt, A.view, B.view, threads=cores, rows=(0, rows), op_a=op_a, op_b=op_b)
     dt = time.perf_counter() - t0
     flop = 2.0 * rows * w.N * w.K
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
@@ -195,16 +195,27 @@ def bench_mixed(args, w) -> int:
     from shared_memory_tiled_amd import binding, inputs
 
     fmt = args.format
+    op_a, op_b = args.op[0], args.op[1]
     A, B, _, _ = inputs.operands16(w, fmt)
+    lda, ldb = w.lda, w.ldb
+    if args.op != "NN":     # the transposed factor is stored transposed (compact rows)
+        if op_a == "T":
+            A = inputs.padded16(np.ascontiguousarray(A.view.T), w.M, w.offset, fmt)
+            lda = w.M
+        if op_b == "T":
+            B = inputs.padded16(np.ascontiguousarray(B.view.T), w.K, w.offset, fmt)
+            ldb = w.K
     dev = torch.device("cuda:0")
     a = torch.from_numpy(A.buf.view(np.int16)).to(dev)
     b = torch.from_numpy(B.buf.view(np.int16)).to(dev)
     c = torch.empty(w.offset + w.M * w.ldc + 64, dtype=torch.float32, device=dev)
-    call_args = (fmt, w.M, w.N, w.K, a.data_ptr() + 2 * w.offset, w.lda, b.data_ptr() + 2 * w.offset,
-                 w.ldb, c.data_ptr() + 4 * w.offset, w.ldc)
+    call_args = (fmt, w.M, w.N, w.K, a.data_ptr() + 2 * w.offset, lda, b.data_ptr() + 2 * w.offset,
+                 ldb, c.data_ptr() + 4 * w.offset, w.ldc)
     flop = 2.0 * w.M * w.N * w.K
 
     def make(v):
+        if args.op != "NN":
+            return lambda: binding.gemm_mixed_op(op_a, op_b, *call_args)
         if v is None:
             return lambda: binding.gemm_mixed(*call_args)
         return lambda: binding.gemm_mixed_variant(v, *call_args)
@@ -223,11 +234,12 @@ def bench_mixed(args, w) -> int:
     tiles256 = -(-w.M // 256) * -(-w.N // 256)
     tiles128 = -(-w.M // 128) * -(-w.N // 128)
     picked = 6 if tiles256 >= 256 else 7 if tiles128 >= 256 else 3
-    config = {"workload": f"{w.name} rounded to {fmt}", "M": w.M, "N": w.N, "K": w.K, "lda": w.lda,
-              "ldb": w.ldb, "ldc": w.ldc, "view_offset_elements": w.offset, "values": w.dist,
-              "format": fmt, "result": "f32",
-              "kernel": binding.gemm_mixed_variant_name(picked if args.variant is None else args.variant)}
-    if w.offset == 0 and w.lda == w.K and w.ldb == w.N:
+    config = {"workload": f"{w.name} rounded to {fmt}", "M": w.M, "N": w.N, "K": w.K, "lda": lda,
+              "ldb": ldb, "ldc": w.ldc, "view_offset_elements": w.offset, "values": w.dist,
+              "format": fmt, "result": "f32", "op": args.op,
+              "kernel": (f"gemm_mixed_op({op_a},{op_b})" if args.op != "NN" else
+                         binding.gemm_mixed_variant_name(picked if args.variant is None else args.variant))}
+    if args.op == "NN" and w.offset == 0 and w.lda == w.K and w.ldb == w.N:
         dt = torch.bfloat16 if fmt == "bf16" else torch.float16
         at = a[:w.M * w.K].view(dt).view(w.M, w.K)
         bt = b[:w.K * w.N].view(dt).view(w.K, w.N)
@@ -243,7 +255,7 @@ def bench_mixed(args, w) -> int:
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_16BIT_TFLOPS, 4), "traffic": None},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline16(fmt, A, B, w)
+        line["cpu_baseline"] = cpu_baseline16(fmt, A, B, w, op_a=op_a, op_b=op_b)
     print(json.dumps(line), flush=True)
     return 0
 

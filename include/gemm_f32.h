@@ -256,6 +256,21 @@ int gemm_mixed_variant(int variant, int format, int64_t M, int64_t N, int64_t K,
 int gemm_mixed_num_variants(void);
 const char *gemm_mixed_variant_name(int variant);   /* NULL if unknown */
 
+/* C (binary32) = op(A) x op(B) for 16-bit factors, either one stored
+ * transposed: the backward-pass products X^T dY and dY W^T of the same
+ * deep-learning chapter ("Backward"), in mixed precision.
+ *   op_a = GEMM_F32_OP_N: A stored M x K (lda >= max(1, K));
+ *   op_a = GEMM_F32_OP_T: A stored K x M (lda >= max(1, M)), op(A) = A^T;
+ *   op_b = GEMM_F32_OP_N: B stored K x N (ldb >= max(1, N));
+ *   op_b = GEMM_F32_OP_T: B stored N x K (ldb >= max(1, K)), op(B) = B^T.
+ * Everything else as for gemm_mixed (formats, alignment, accuracy, errors;
+ * GEMM_F32_ERR_INVALID_OP for another op value).  The factors are read in
+ * place; for a given M, N and K the result has the same bits whichever way
+ * the factors are stored. */
+int gemm_mixed_op(int op_a, int op_b, int format, int64_t M, int64_t N, int64_t K,
+                  const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                  float *C, int64_t ldc, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -91,6 +91,8 @@ def load_library():
         lib.gemm_mixed.restype = ctypes.c_int
         lib.gemm_mixed_variant.argtypes = [ctypes.c_int] + msig
         lib.gemm_mixed_variant.restype = ctypes.c_int
+        lib.gemm_mixed_op.argtypes = [ctypes.c_int, ctypes.c_int] + msig
+        lib.gemm_mixed_op.restype = ctypes.c_int
         lib.gemm_mixed_num_variants.argtypes = []
         lib.gemm_mixed_num_variants.restype = ctypes.c_int
         lib.gemm_mixed_variant_name.argtypes = [ctypes.c_int]
@@ -304,6 +306,16 @@ def gemm_mixed_variant(variant, fmt, M, N, K, A, lda, B, ldb, C, ldc, stream=Non
                                   _addr(C), ldc, _stream(stream)))
 
 
+def gemm_mixed_op(op_a, op_b, fmt, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
+    """C (binary32) = op(A) x op(B) for 16-bit factors, op 'N' (as stored) or
+    'T' (stored transposed: A is K x M, B is N x K); see gemm_f32.h."""
+    lib = load_library()
+    oa = OPS.get(op_a, op_a) if not isinstance(op_a, int) else op_a
+    ob = OPS.get(op_b, op_b) if not isinstance(op_b, int) else op_b
+    _check(lib.gemm_mixed_op(int(oa), int(ob), _format(fmt), M, N, K, _addr(A), lda, _addr(B), ldb,
+                             _addr(C), ldc, _stream(stream)))
+
+
 def gemm_mixed_num_variants() -> int:
     return load_library().gemm_mixed_num_variants()
 
@@ -322,14 +334,16 @@ def _ld16(t: torch.Tensor) -> int:
 
 
 def gemm16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None, variant=None,
-           stream=None) -> torch.Tensor:
-    """Tensor form: returns ``out`` (float32, allocated if None) = A @ B for
-    bfloat16 or float16 CUDA tensors A (M x K) and B (K x N) of one dtype;
-    views with a leading dimension and a storage offset pass through."""
+           stream=None, op_a="N", op_b="N") -> torch.Tensor:
+    """Tensor form: returns ``out`` (float32, allocated if None) = op(A) @
+    op(B) for bfloat16 or float16 CUDA tensors of one dtype.  A and B are the
+    stored row-major tensors (with op 'T', A is K x M and B is N x K); views
+    with a leading dimension and a storage offset pass through.  ``variant``
+    selects a tile configuration and requires op 'N' for both factors."""
     if A.dtype != B.dtype:
         raise TypeError("A and B must have the same 16-bit dtype")
-    M, K = A.shape
-    K2, N = B.shape
+    M, K = A.shape if op_a in ("N", 0) else A.shape[::-1]
+    K2, N = B.shape if op_b in ("N", 0) else B.shape[::-1]
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
     if out is None:
@@ -337,7 +351,11 @@ def gemm16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None, va
     if tuple(out.shape) != (M, N):
         raise ValueError("out has the wrong shape")
     args = (_FORMAT_OF_DTYPE[A.dtype], M, N, K, A, _ld16(A), B, _ld16(B), out, _ld(out))
-    if variant is None:
+    if op_a not in ("N", 0) or op_b not in ("N", 0):
+        if variant is not None:
+            raise ValueError("transposed factors run on the default kernels only")
+        gemm_mixed_op(op_a, op_b, *args, stream=stream)
+    elif variant is None:
         gemm_mixed(*args, stream=stream)
     else:
         gemm_mixed_variant(variant, *args, stream=stream)

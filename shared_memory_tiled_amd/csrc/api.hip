@@ -272,27 +272,39 @@ constexpr int kMixedAuto = -1;
 
 bool misaligned2(const void* ptr) { return ((uintptr_t)ptr & 1u) != 0; }
 
-int run_mixed(int config, int format, int64_t M, int64_t N, int64_t K, const uint16_t* A,
-              int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+// config: a gemm_mixed variant (kMixedAuto: picked for the shape); with a
+// transposed factor (op_a or op_b = 1) only kMixedAuto, on the op kernels.
+int run_mixed(int config, int op_a, int op_b, int format, int64_t M, int64_t N, int64_t K,
+              const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc,
+              void* stream) {
+    if ((op_a != GEMM_F32_OP_N && op_a != GEMM_F32_OP_T) || (op_b != GEMM_F32_OP_N && op_b != GEMM_F32_OP_T))
+        return GEMM_F32_ERR_INVALID_OP;
     if (config != kMixedAuto && (config < 0 || config >= mixed_num_configs()))
         return GEMM_F32_ERR_INVALID_VARIANT;
     if (format != GEMM_MIXED_BF16 && format != GEMM_MIXED_F16) return GEMM_F32_ERR_INVALID_FORMAT;
     if (M < 0 || N < 0 || K < 0) return GEMM_F32_ERR_INVALID_DIM;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    const int64_t a_rows = op_a ? K : M, a_cols = op_a ? M : K;
+    const int64_t b_rows = op_b ? N : K, b_cols = op_b ? K : N;
+    if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) || ldc < (N > 1 ? N : 1))
         return GEMM_F32_ERR_INVALID_LD;
     if (M == 0 || N == 0) return GEMM_F32_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return GEMM_F32_ERR_NULL_PTR;
     if (misaligned(C) || (K > 0 && (misaligned2(A) || misaligned2(B)))) return GEMM_F32_ERR_MISALIGNED;
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_F32_ERR_TOO_LARGE;
-    if (!extent_fits(M, K, lda) || !extent_fits(K, N, ldb) || !extent_fits(M, N, ldc))
+    if (!extent_fits(a_rows, a_cols, lda) || !extent_fits(b_rows, b_cols, ldb) || !extent_fits(M, N, ldc))
         return GEMM_F32_ERR_TOO_LARGE;
     const int64_t blocks16 = ((M + 15) / 16) * ((N + 15) / 16);
     if (blocks16 > (int64_t)0xFFFFFFFF / 256) return GEMM_F32_ERR_TOO_LARGE;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_F32_ERR_DEVICE;
     const Gemm16Args p{(int)M, (int)N, (int)K, A, lda, B, ldb, C, ldc};
-    if (config == kMixedAuto) config = mixed_pick_config(p.M, p.N, p.K);
-    const hipError_t e = launch_mixed(p, reinterpret_cast<hipStream_t>(stream), format, config);
+    hipError_t e;
+    if (op_a || op_b) {
+        e = launch_mixed_op(p, reinterpret_cast<hipStream_t>(stream), format, op_a, op_b);
+    } else {
+        if (config == kMixedAuto) config = mixed_pick_config(p.M, p.N, p.K);
+        e = launch_mixed(p, reinterpret_cast<hipStream_t>(stream), format, config);
+    }
     if (e == hipErrorInvalidValue) return GEMM_F32_ERR_TOO_LARGE;
     return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
 }
@@ -300,13 +312,18 @@ int run_mixed(int config, int format, int64_t M, int64_t N, int64_t K, const uin
 
 extern "C" int gemm_mixed(int format, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                           const uint16_t* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
-    return run_mixed(kMixedAuto, format, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return run_mixed(kMixedAuto, GEMM_F32_OP_N, GEMM_F32_OP_N, format, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+extern "C" int gemm_mixed_op(int op_a, int op_b, int format, int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                             int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+    return run_mixed(kMixedAuto, op_a, op_b, format, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 extern "C" int gemm_mixed_variant(int variant, int format, int64_t M, int64_t N, int64_t K,
                                   const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                   float* C, int64_t ldc, void* stream) {
-    return run_mixed(variant, format, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return run_mixed(variant, GEMM_F32_OP_N, GEMM_F32_OP_N, format, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 extern "C" int gemm_mixed_num_variants(void) { return mixed_num_configs(); }

@@ -33,6 +33,10 @@ hipError_t launch_mixed(const Gemm16Args& p, hipStream_t s, int format, int conf
 int mixed_num_configs();
 const char* mixed_config_name(int config);
 int mixed_pick_config(int M, int N, int K);
+// op(A) x op(B) with either factor stored transposed (op 1): A stored K x M,
+// B stored N x K; validated like GemmArgs with the leading dimensions of the
+// stored matrices.
+hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b);
 
 // Sum reduction (reduce.hip): *out = sum of x[0 .. n-1].
 hipError_t launch_reduce(int variant, int64_t n, const float* x, float* out, float* ws, hipStream_t s);

@@ -487,6 +487,211 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
         }
 }
 
+// ---------------------------------------------------------------------------
+// op(A) x op(B): the backward-pass products (X^T dY, dY W^T) in mixed
+// precision.  Each factor is an MN x K matrix of op(X) (MN = M for A, N for
+// B) stored either
+//   KC, k-contiguous (A as stored, B stored transposed): the LDS tile holds
+//       MNT rows of 64 k (128 bytes), chunk c of row r at c ^ f(r), and a
+//       lane's fragment is one 128-bit read, as for A in gemm16_kernel;
+//   MC, mn-contiguous (B as stored, A stored transposed): the tile holds 64 k
+//       rows of MNT values, chunk c of row r at c ^ 4 (r % 4), and a lane's
+//       fragment is two ds_read_b64_tr_b16 reads, as for B in gemm16_kernel.
+// Interior phases copy both tiles straight from global memory into LDS;
+// ghost phases load chunk by chunk with zeros outside the matrix, into the
+// same layout.  The k order (k = 16 s + 8 h + e for element e of lane half h
+// in step s) does not depend on how a factor is stored, so every op pair
+// gives the bits of gemm_mixed on explicitly transposed copies.
+template <int MNT, bool KC, int NW>
+struct Tile16 {
+    static constexpr int ELEMS = MNT * kBK;                  // per stage
+    static constexpr int CPR = KC ? kBK / 8 : MNT / 8;       // 16-byte chunks per stored row
+    static constexpr int ROWS = KC ? MNT : kBK;              // stored rows per stage
+    static constexpr int ROW_LEN = KC ? kBK : MNT;
+    static constexpr int COPIES = ELEMS * 2 / 1024 / NW;     // direct 1 KB copies per wave
+    static constexpr int ROWS_PER_COPY = 64 / CPR;
+    static_assert(KC || (CPR >= 16 && 64 % CPR == 0), "mn-contiguous tile width");
+    static_assert(COPIES * NW * 1024 == ELEMS * 2, "direct copy split");
+
+    __device__ static int phys(int r, int c) { return KC ? (c ^ swz(r)) : (c ^ (4 * (r & 3))); }
+    __device__ static int elem(int r, int c) { return r * ROW_LEN + 8 * phys(r, c); }
+    // Global element offset of stored (row, col) of the tile at mn0, relative
+    // to the phase's k0 (added separately: k0 for KC, k0 * ld for MC).
+    __device__ static int64_t offset(int64_t ld, int mn0, int row, int col) {
+        return KC ? (int64_t)(mn0 + row) * ld + col : (int64_t)row * ld + mn0 + col;
+    }
+    __device__ static int64_t phase_step(int64_t ld, int k0) { return KC ? (int64_t)k0 : (int64_t)k0 * ld; }
+    // Eight stored values of (row, 8 c) with ghost zeros.
+    template <bool VEC>
+    __device__ static u32x4 ghost(const uint16_t* X, int64_t ld, int mn0, int mn_ext, int k0, int k_ext,
+                                  int row, int c) {
+        return KC ? load8_ghost<VEC>(X, mn0 + row, mn_ext, k0 + 8 * c, k_ext, ld)
+                  : load8_ghost<VEC>(X, k0 + row, k_ext, mn0 + 8 * c, mn_ext, ld);
+    }
+    // Fragment of op(X) rows mb .. mb + 31, 16-deep step s (see gemm16_kernel).
+    __device__ static u32x4 fragment(const uint16_t* t, int mb, int s, int lane) {
+        if constexpr (KC) {
+            return *reinterpret_cast<const u32x4*>(&t[elem(mb + (lane & 31), 2 * s + (lane >> 5))]);
+        } else {
+            const int g = lane >> 4, j = lane & 15;
+            const int mn = mb + 16 * (g & 1) + 4 * (j & 3);
+            u32x4 out;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int row = 16 * s + 8 * (g >> 1) + 4 * r + (j >> 2);
+                const u32x2 v = read_tr16(lds_addr(t + elem(row, mn >> 3) + 4 * ((mn >> 2) & 1)));
+                out[2 * r] = v[0];
+                out[2 * r + 1] = v[1];
+            }
+            return out;
+        }
+    }
+};
+
+template <int FMT, int BM, int BN, int WAVES_M, int WAVES_N, bool KCA, bool KCB, bool VEC>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
+void gemm16_op_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int NT = NW * 64;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int FM = WM / 32, FN = WN / 32;
+    using TA = Tile16<BM, KCA, NW>;
+    using TB = Tile16<BN, KCB, NW>;
+    constexpr int STAGE = TA::ELEMS + TB::ELEMS;
+    static_assert(WM % 32 == 0 && WN % 32 == 0, "tile shape");
+    static_assert((TA::ROWS * TA::CPR) % NT == 0 && (TB::ROWS * TB::CPR) % NT == 0, "ghost split");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int li = lane & 31, lh = lane >> 5;
+    const int logical = xcd_contiguous((int)blockIdx.x, tiles_m * tiles_n);
+    const int group_size = group_m * tiles_n;
+    const int g = logical / group_size;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int in_g = logical - g * group_size;
+    const int m0 = (first_m + in_g % gm) * BM;
+    const int n0 = (in_g / gm) * BN;
+    const bool fast_tile = VEC && (m0 + BM <= p.M) && (n0 + BN <= p.N);
+
+    // direct copy j of this wave fills stored rows R .. R + ROWS_PER_COPY - 1,
+    // R = ROWS_PER_COPY (wave + j NW); lane l writes physical chunk l % CPR of
+    // row R + l / CPR, so it reads the logical chunk of that position
+    int64_t a_doff[VEC ? TA::COPIES : 1], b_doff[VEC ? TB::COPIES : 1];
+    if constexpr (VEC) {
+#pragma unroll
+        for (int j = 0; j < TA::COPIES; ++j) {
+            const int row = TA::ROWS_PER_COPY * (wave_u + j * NW) + lane / TA::CPR;
+            a_doff[j] = TA::offset(p.lda, m0, row, 8 * TA::phys(row, lane % TA::CPR));
+        }
+#pragma unroll
+        for (int j = 0; j < TB::COPIES; ++j) {
+            const int row = TB::ROWS_PER_COPY * (wave_u + j * NW) + lane / TB::CPR;
+            b_doff[j] = TB::offset(p.ldb, n0, row, 8 * TB::phys(row, lane % TB::CPR));
+        }
+    }
+    auto direct_tiles = [&](int k0, int buf) {
+        if constexpr (VEC) {
+            uint16_t* as = lds + buf * STAGE;
+            uint16_t* bs = as + TA::ELEMS;
+            const uint16_t* a = p.A + TA::phase_step(p.lda, k0);
+            const uint16_t* b = p.B + TB::phase_step(p.ldb, k0);
+#pragma unroll
+            for (int j = 0; j < TA::COPIES; ++j)
+                copy16_to_lds(a + a_doff[j], as + TA::ROWS_PER_COPY * (wave_u + j * NW) * TA::ROW_LEN);
+#pragma unroll
+            for (int j = 0; j < TB::COPIES; ++j)
+                copy16_to_lds(b + b_doff[j], bs + TB::ROWS_PER_COPY * (wave_u + j * NW) * TB::ROW_LEN);
+        }
+    };
+    // ghost phases: loaded and stored chunk by chunk (no registers held
+    // across the math; these phases are rare in interior tiles)
+    auto ghost_tiles_now = [&](int k0, int buf) {
+        uint16_t* as = lds + buf * STAGE;
+        uint16_t* bs = as + TA::ELEMS;
+#pragma unroll
+        for (int u = 0; u < TA::ROWS * TA::CPR / NT; ++u) {
+            const int q = tid + u * NT, r = q / TA::CPR, c = q % TA::CPR;
+            *reinterpret_cast<u32x4*>(&as[TA::elem(r, c)]) =
+                TA::template ghost<VEC>(p.A, p.lda, m0, p.M, k0, p.K, r, c);
+        }
+#pragma unroll
+        for (int u = 0; u < TB::ROWS * TB::CPR / NT; ++u) {
+            const int q = tid + u * NT, r = q / TB::CPR, c = q % TB::CPR;
+            *reinterpret_cast<u32x4*>(&bs[TB::elem(r, c)]) =
+                TB::template ghost<VEC>(p.B, p.ldb, n0, p.N, k0, p.K, r, c);
+        }
+    };
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    auto read_frags = [&](const uint16_t* as, const uint16_t* bs, int s, u32x4 (&a)[FM], u32x4 (&b)[FN]) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f) a[f] = TA::fragment(as, wm * WM + f * 32, s, lane);
+#pragma unroll
+        for (int f = 0; f < FN; ++f) b[f] = TB::fragment(bs, wn * WN + f * 32, s, lane);
+    };
+    auto math = [&](int buf) {
+        const uint16_t* as = lds + buf * STAGE;
+        const uint16_t* bs = as + TA::ELEMS;
+        u32x4 a[2][FM], b[2][FN];
+        read_frags(as, bs, 0, a[0], b[0]);
+#pragma unroll
+        for (int s = 0; s < kBK / 16; ++s) {
+            // this step's transposed reads were issued one step ago
+            if constexpr (!KCA) wait_tied(a[s & 1]);
+            if constexpr (!KCB) wait_tied(b[s & 1]);
+            if (s + 1 < kBK / 16) read_frags(as, bs, s + 1, a[(s + 1) & 1], b[(s + 1) & 1]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<FMT>(a[s & 1][i], b[s & 1][j], acc[i][j]);
+        }
+    };
+    auto end_phase = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        asm volatile("" ::: "memory");
+    };
+
+    const int phases = ceil_div(p.K, kBK);
+    const int full = fast_tile ? p.K / kBK : 0;       // phases copied straight (no ghosts)
+    if (phases > 0) {
+        if (full > 0) direct_tiles(0, 0);
+        else ghost_tiles_now(0, 0);
+    }
+    end_phase();
+    for (int ph = 0; ph < phases; ++ph) {
+        const int cur = ph & 1, k_next = (ph + 1) * kBK;
+        if (ph + 1 < full) direct_tiles(k_next, cur ^ 1);
+        else if (ph + 1 < phases) ghost_tiles_now(k_next, cur ^ 1);
+        // keep the next phase's copies ahead of the math
+        __builtin_amdgcn_sched_barrier(0);
+        math(cur);
+        end_phase();
+    }
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn * WN + j * 32 + li;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
+            }
+        }
+}
+
 namespace {
 using Launch16 = hipError_t (*)(const Gemm16Args&, hipStream_t, int, int, int, unsigned);
 
@@ -522,7 +727,50 @@ const MixedConfig kMixed[] = {
 };
 #undef MIXED
 constexpr int kNumMixed = (int)(sizeof(kMixed) / sizeof(kMixed[0]));
+
+// op kernels, chosen by tile, op pair and load path
+template <int FMT, int BM, int BN, int WM, int WN, bool KCA, bool KCB, bool VEC>
+hipError_t launch16_op(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                       unsigned blocks) {
+    hipLaunchKernelGGL((gemm16_op_kernel<FMT, BM, BN, WM, WN, KCA, KCB, VEC>), dim3(blocks), dim3(WM * WN * 64),
+                       0, s, p, tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+}
+template <int FMT, int BM, int BN, int WM, int WN>
+Launch16 op_launcher(int op_a, int op_b, bool vec) {
+    // op 0 = factor as stored: A k-contiguous, B mn-contiguous; op 1 the reverse
+    const int key = 4 * op_a + 2 * op_b + (vec ? 1 : 0);
+    switch (key) {
+        case 0: return launch16_op<FMT, BM, BN, WM, WN, true, false, false>;
+        case 1: return launch16_op<FMT, BM, BN, WM, WN, true, false, true>;
+        case 2: return launch16_op<FMT, BM, BN, WM, WN, true, true, false>;
+        case 3: return launch16_op<FMT, BM, BN, WM, WN, true, true, true>;
+        case 4: return launch16_op<FMT, BM, BN, WM, WN, false, false, false>;
+        case 5: return launch16_op<FMT, BM, BN, WM, WN, false, false, true>;
+        case 6: return launch16_op<FMT, BM, BN, WM, WN, false, true, false>;
+        default: return launch16_op<FMT, BM, BN, WM, WN, false, true, true>;
+    }
+}
 }  // namespace
+
+// op(A) x op(B): 256 x 256 tiles of eight waves once there are 256 of them,
+// else 128 x 128 tiles of four waves.  A and B are the stored matrices;
+// vector loads (and the direct copies) need 4-byte aligned bases and even
+// leading dimensions, as for gemm_mixed.
+hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b) {
+    const bool vec = ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 3) == 0 &&
+                     (p.lda % 2) == 0 && (p.ldb % 2) == 0;
+    const int64_t t256 = (int64_t)ceil_div(p.M, 256) * ceil_div(p.N, 256);
+    const bool big = t256 >= 256;
+    const int tile = big ? 256 : 128;
+    const int tiles_m = ceil_div(p.M, tile), tiles_n = ceil_div(p.N, tile);
+    const int64_t blocks = (int64_t)tiles_m * tiles_n;
+    if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    Launch16 fn;
+    if (big) fn = format ? op_launcher<1, 256, 256, 2, 4>(op_a, op_b, vec) : op_launcher<0, 256, 256, 2, 4>(op_a, op_b, vec);
+    else fn = format ? op_launcher<1, 128, 128, 2, 2>(op_a, op_b, vec) : op_launcher<0, 128, 128, 2, 2>(op_a, op_b, vec);
+    return fn(p, s, tiles_m, tiles_n, 8, (unsigned)blocks);
+}
 
 int mixed_num_configs() { return kNumMixed; }
 const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed[c].name : nullptr; }

@@ -243,3 +243,18 @@ def test_mixed_variants(binding, lib):
     n = binding.reduce_sum_f32_num_variants()
     names = [binding.reduce_sum_f32_variant_name(v) for v in range(n)]
     assert n == 5 and all(names) and len(set(names)) == n and binding.reduce_sum_f32_variant_name(n) is None
+
+
+@pytest.mark.parametrize("op_a,op_b,args,code", [
+    (2, 0, (0, 4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_OP"),
+    (0, -1, (0, 4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_OP"),
+    (1, 0, (0, 8, 4, 3, FAKE, 7, FAKE, 4, FAKE, 4), "GEMM_F32_ERR_INVALID_LD"),     # A^T: lda >= M
+    (0, 1, (1, 4, 6, 9, FAKE, 9, FAKE, 8, FAKE, 6), "GEMM_F32_ERR_INVALID_LD"),     # B^T: ldb >= K
+    (1, 1, (0, 4, 6, 9, FAKE, 3, FAKE, 9, FAKE, 6), "GEMM_F32_ERR_INVALID_LD"),
+    (1, 1, (5, 4, 6, 9, FAKE, 4, FAKE, 9, FAKE, 6), "GEMM_F32_ERR_INVALID_FORMAT"),
+    (1, 1, (0, 4, 6, 9, FAKE + 1, 4, FAKE, 9, FAKE, 6), "GEMM_F32_ERR_MISALIGNED"),
+    (1, 0, (1, -1, 6, 9, FAKE, 4, FAKE, 6, FAKE, 6), "GEMM_F32_ERR_INVALID_DIM"),
+    (1, 1, (0, 0, 6, 9, None, 1, None, 9, None, 6), "GEMM_F32_OK"),
+])
+def test_mixed_op_validation_without_launch(lib, op_a, op_b, args, code):
+    assert lib.gemm_mixed_op(op_a, op_b, *args, None) == declared_codes()[code]
