@@ -27,6 +27,10 @@ Extra modes (used for counter runs under rocprofv3):
     --op XY             time gemm_f32_op with op(A) = X, op(B) = Y (N or T):
                         the transposed factor is stored transposed, with a
                         compact leading dimension
+    --all-workloads     gemm_f32 at each of the five workloads: one JSON line
+                        per workload with the median and best launch time
+                        (HIP events around every launch), then the oracle's
+                        time on this host (see bench_all_workloads)
 """
 from __future__ import annotations
 
@@ -349,6 +353,95 @@ def bench_transpose(args, w) -> int:
     return 0
 
 
+# Timed launches per workload: many for the microsecond-scale small products,
+# fewer for the large ones.
+WORKLOAD_LAUNCHES = {"square256": 200, "square1000": 50, "square4096": 20,
+                     "rect8192x4096x2048_padded": 20, "square8192": 10}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def bench_all_workloads(args) -> int:
+    """gemm_f32 (the default kernel) at every workload, then the oracle.
+
+    GPU: 3 warm-up launches, then a HIP event before the first launch and
+    after every launch on the launch stream; the median and best of the
+    per-launch times give TFLOP/s and the fraction of the fp32 peak.
+    Oracle, on this host, unchanged: the full product at square256 and
+    square1000 on one thread and on all cores, at square4096 on all cores;
+    at the two largest workloads the 4096 sampled entries plus edge entries
+    that the parity tests check (one thread), with the full product's time
+    extrapolated from that rate and labelled as such."""
+    import statistics
+
+    import torch
+
+    from shared_memory_tiled_amd import binding, inputs
+
+    cores = len(os.sched_getaffinity(0))
+    dev = torch.device("cuda:0")
+    for name, launches in WORKLOAD_LAUNCHES.items():
+        w = inputs.WORKLOADS[name]
+        A, B = inputs.operands(w)
+        a = torch.from_numpy(A.buf).to(dev)
+        b = torch.from_numpy(B.buf).to(dev)
+        c = torch.empty(w.offset + w.M * w.ldc + 64, dtype=torch.float32, device=dev)
+        call = (w.M, w.N, w.K, a.data_ptr() + 4 * w.offset, w.lda,
+                b.data_ptr() + 4 * w.offset, w.ldb, c.data_ptr() + 4 * w.offset, w.ldc)
+        for _ in range(3):
+            binding.gemm_f32(*call)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()       # the stream the library launches on
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
+        ev[0].record(stream)
+        for i in range(launches):
+            binding.gemm_f32(*call)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(launches)]
+        flop = 2.0 * w.M * w.N * w.K
+        med, best = statistics.median(ms), min(ms)
+        line = {"workload": name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb,
+                "ldc": w.ldc, "view_offset_floats": w.offset, "values": w.dist,
+                "launches": launches, "median_ms": round(med, 5), "best_ms": round(best, 5),
+                "tflops_median": round(flop / med / 1e9, 3), "tflops_best": round(flop / best / 1e9, 3),
+                "percent_of_peak_median": round(100 * flop / med / 1e9 / PEAK_FP32_TFLOPS, 2)}
+        del a, b, c
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            import oracle
+            cpu = {"cores": cores, "cpu": cpu_model()}
+            if not w.sampled:
+                for threads in (1, cores):
+                    t0 = time.perf_counter()
+                    oracle.gemm(A.view, B.view, threads=threads)
+                    cpu[f"full_s_{threads}_threads"] = round(time.perf_counter() - t0, 3)
+            elif name == "square4096":
+                t0 = time.perf_counter()
+                oracle.gemm(A.view, B.view, threads=cores)
+                cpu[f"full_s_{cores}_threads"] = round(time.perf_counter() - t0, 3)
+            else:
+                ii, jj = inputs.sample_pairs(w.M, w.N, 4096, inputs.rng(w.index, 4))
+                t0 = time.perf_counter()
+                oracle.gemm_entries(A.view, B.view, ii, jj)
+                dt = time.perf_counter() - t0
+                cpu["sample_entries"] = int(ii.shape[0])
+                cpu["sample_s_1_thread"] = round(dt, 3)
+                cpu["full_s_1_thread_extrapolated"] = round(dt * w.M * w.N / ii.shape[0], 1)
+            line["oracle"] = cpu
+        print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,6 +456,7 @@ def main(argv=None) -> int:
     ap.add_argument("--row", default="gemm", choices=["gemm", "transpose", "reduce", "mixed"])
     ap.add_argument("--format", default="bf16", choices=["bf16", "f16"], help="16-bit format of --row mixed")
     ap.add_argument("--n", type=int, default=2 ** 28, help="values summed by --row reduce")
+    ap.add_argument("--all-workloads", action="store_true")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -391,6 +485,8 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n}), flush=True)
         del src, dst
 
+    if args.all_workloads:
+        return bench_all_workloads(args)
     if args.row == "reduce":
         return bench_reduce(args)
     w = inputs.WORKLOADS[args.workload]

@@ -18,5 +18,6 @@ def test_help_lists_modes():
     proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
                           capture_output=True, text=True, timeout=120)
     assert proc.returncode == 0
-    for flag in ("--steps", "--warmup", "--ladder", "--op", "--copy-probe-mib", "--row", "--format"):
+    for flag in ("--steps", "--warmup", "--ladder", "--op", "--copy-probe-mib", "--row", "--format",
+                 "--all-workloads"):
         assert flag in proc.stdout
