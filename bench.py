@@ -3,8 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one C = A x B call through the C ABI (gemm_f32, the default
-kernel) on seeded synthetic operands already resident in HBM.  W untimed
-steps, then exactly K timed steps between two device synchronisations.  One
+kernel) on seeded synthetic operands already resident in HBM.  The step runs
+untimed for --settle-s seconds (default 0.3: the clock ramps up after the
+idle spell of input generation), then W untimed steps, then exactly K timed
+steps between two device synchronisations.  One
 JSON line is printed with the metric (TFLOP/s = 2MNK per step / seconds),
 the roofline of the kernel (algorithmic FLOP per launch over the average
 launch time from HIP events on the launch stream, against the chip's
@@ -96,8 +98,33 @@ def cpu_baseline(A, B, w, op_a="N", op_b="N", budget_s: float = 12.0):
                       f"triple loop, {cores} threads"}
 
 
+# Untimed run of the step, in seconds, before its warm-up steps.  After an
+# idle spell (host-side input generation) the GPU's clock ramps back up over
+# some tens of milliseconds: measured, a 4096^3 product's launches speed up
+# by about 20 % over their first 25 ms, and a step of a fraction of a
+# millisecond would otherwise be timed entirely on that ramp.
+SETTLE_S = 0.3
+
+
+def settle(fn, seconds=None) -> int:
+    """Runs fn untimed for `seconds` (default SETTLE_S) of wall time; returns
+    the number of calls."""
+    import torch
+    seconds = SETTLE_S if seconds is None else seconds
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def _timed(fn, steps, warmup):
     import torch
+    settle(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -147,7 +174,8 @@ def bench_reduce(args) -> int:
     line = {
         "metric": "fp32 sum reduction GB/s (bytes read) on MI355X",
         "value": round(read * args.steps / wall / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "steps": args.steps, "warmup": args.warmup, "settle_s": SETTLE_S,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"sum of {n} uniform[-1,1) floats", "n": n,
                    "kernel": binding.reduce_sum_f32_variant_name(binding.REDUCE_DEFAULT if args.variant is None
@@ -252,7 +280,8 @@ def bench_mixed(args, w) -> int:
     line = {
         "metric": f"{fmt} x {fmt} -> f32 GEMM TFLOP/s on MI355X",
         "value": round(flop * args.steps / wall / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "steps": args.steps, "warmup": args.warmup, "settle_s": SETTLE_S,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": fmt,
         "data": "synthetic", "config": config,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_16BIT_TFLOPS,
@@ -294,19 +323,7 @@ def bench_transpose(args, w) -> int:
         else:
             binding.transpose_f32_variant(variant, *targs)
 
-    def timed(fn, steps, warmup):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0, e0.elapsed_time(e1) / steps
+    timed = _timed
 
     if args.ladder:
         for v in range(binding.transpose_f32_num_variants()):
@@ -325,7 +342,8 @@ def bench_transpose(args, w) -> int:
     line = {
         "metric": "fp32 shared-tile transpose GB/s (bytes read + written) on MI355X",
         "value": round(moved * args.steps / wall / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "steps": args.steps, "warmup": args.warmup, "settle_s": SETTLE_S,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name} A matrix", "rows": w.M, "cols": w.K, "ld_in": w.lda,
@@ -397,6 +415,7 @@ def bench_all_workloads(args) -> int:
         c = torch.empty(w.offset + w.M * w.ldc + 64, dtype=torch.float32, device=dev)
         call = (w.M, w.N, w.K, a.data_ptr() + 4 * w.offset, w.lda,
                 b.data_ptr() + 4 * w.offset, w.ldb, c.data_ptr() + 4 * w.offset, w.ldc)
+        settle(lambda: binding.gemm_f32(*call))
         for _ in range(3):
             binding.gemm_f32(*call)
         torch.cuda.synchronize()
@@ -457,7 +476,10 @@ def main(argv=None) -> int:
     ap.add_argument("--format", default="bf16", choices=["bf16", "f16"], help="16-bit format of --row mixed")
     ap.add_argument("--n", type=int, default=2 ** 28, help="values summed by --row reduce")
     ap.add_argument("--all-workloads", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="untimed run of each timed step, in seconds, before its warm-up steps")
     args = ap.parse_args(argv)
+    globals()["SETTLE_S"] = max(0.0, args.settle_s)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -522,20 +544,7 @@ def main(argv=None) -> int:
             binding.gemm_f32_variant(v, *call_args)
 
     def timed(v, steps, warmup):
-        for _ in range(warmup):
-            one(v)
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()      # the stream the library launches on
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(steps):
-            one(v)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return wall, e0.elapsed_time(e1) / steps
+        return _timed(lambda: one(v), steps, warmup)
 
     if args.ladder:
         variants = list(range(binding.gemm_f32_num_variants())) + \
@@ -560,6 +569,7 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
