@@ -265,7 +265,7 @@ def bench_mixed(args, w) -> int:
     # the kernel gemm_mixed picks: 256 x 256 tiles once there are 256 of them
     tiles256 = -(-w.M // 256) * -(-w.N // 256)
     tiles128 = -(-w.M // 128) * -(-w.N // 128)
-    picked = 6 if tiles256 >= 256 else 7 if tiles128 >= 256 else 3
+    picked = 8 if tiles256 >= 256 else 7 if tiles128 >= 256 else 3
     config = {"workload": f"{w.name} rounded to {fmt}", "M": w.M, "N": w.N, "K": w.K, "lda": lda,
               "ldb": ldb, "ldc": w.ldc, "view_offset_elements": w.offset, "values": w.dist,
               "format": fmt, "result": "f32", "op": args.op,

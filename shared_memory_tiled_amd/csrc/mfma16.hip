@@ -42,6 +42,7 @@
 #include "launch.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace gemmf32 {
 
@@ -144,6 +145,30 @@ __device__ __forceinline__ u32x2 load4_ghost16(const uint16_t* __restrict__ base
         }
     }
     return v;
+}
+
+// 16 bytes of LDS at a byte address.
+__device__ __forceinline__ u32x4 lds_read128(uint32_t lds_byte_addr) {
+    typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+    return *(lds_u32x4*)(uintptr_t)lds_byte_addr;
+}
+
+// read_tr16 with a compile-time byte offset in the instruction.
+__device__ __forceinline__ u32x2 read_tr16_off(uint32_t lds_byte_addr, int off) {
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_byte_addr), "i"(off) : "memory");
+    return v;
+}
+
+template <typename F, int... Q>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Q...>) {
+    (f(std::integral_constant<int, Q>{}), ...);
+}
+// f(std::integral_constant<int, q>{}) for q = 0 .. N - 1, in order: every
+// index is a compile-time constant, so arrays indexed by it stay in registers.
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+    unroll_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 // Column j of an 8 x W block (W = 4 or 8) held as eight rows of W 16-bit
@@ -488,6 +513,234 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
 }
 
 // ---------------------------------------------------------------------------
+// The scheduled kernel: 256 x 256 tiles of full phases (M and N multiples of
+// 256, K of 64, vector-aligned operands), four waves of 128 x 128, one per
+// SIMD, with every instruction of the K loop placed in program order.  Same
+// LDS layouts and the same k order as gemm16_kernel (so the same bits), but:
+//  * Each step issues its 16 matrix instructions one at a time, with the next
+//    step's fragment reads (two after each of the first six) and the copies
+//    of the next phase (one after each odd one) between them, so the reads'
+//    latency and the copies' issue hide behind matrix work.  Scheduling
+//    barriers keep the compiler from regrouping them.
+//  * The last step's matrix instructions of each phase run after the
+//    barrier, on fragments read before it, while the next phase's first
+//    fragments are read: the SIMD has matrix work across the barrier.
+//  * The copies of phase ph + 1 are issued between the barriers that end
+//    phases ph - 1 and ph (eight with the deferred step, eight with step 0),
+//    a whole phase ahead of their use.  They are buffer loads into LDS: base
+//    and extent in a resource, the per-lane offset in a register, the phase's
+//    k in the scalar offset, so they cost no vector instruction.
+//  * Fragment read addresses are computed once per lane (A per fragment and
+//    step; B per fragment, with the step and half as an instruction offset);
+//    a phase only adds the stage offset.
+// LDS: stage st of A at byte 32768 st, of B at byte 65536 + 32768 st.
+template <int FMT>
+__global__ __launch_bounds__(256)
+void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
+    constexpr int BM = 256, BN = 256, NW = 4, WM = 128, WN = 128, FM = 4, FN = 4;
+    constexpr int CPRB = BN / 8;                          // 16-byte chunks per B row
+    constexpr int A_COPIES = BM / 8 / NW;                 // 1 KB copies per wave and phase
+    constexpr int B_COPIES = kBK * BN * 2 / 1024 / NW;
+    constexpr int NCOPY = A_COPIES + B_COPIES;
+    constexpr int A_ST = BM * kBK, B_BASE = 2 * BM * kBK, B_ST = kBK * BN;   // elements
+    static_assert(A_ST * 2 == 32768 && B_ST * 2 == 32768 && NCOPY == 16, "stage layout");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BM + BN) * kBK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave_u / 2, wn = wave_u % 2;
+    const int li = lane & 31, lh = lane >> 5;
+    const int tr_g = lane >> 4, tr_j = lane & 15;
+
+    const int logical = xcd_contiguous((int)blockIdx.x, tiles_m * tiles_n);
+    const int group_size = group_m * tiles_n;
+    const int g = logical / group_size;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int in_g = logical - g * group_size;
+    const int m0 = (first_m + in_g % gm) * BM;
+    const int n0 = (in_g / gm) * BN;
+
+    // Copy j of this wave: A rows 8 (wave + j NW) .. +7 (lane l: chunk
+    // l % 8 ^ f(row) of row l / 8), B rows 2 (wave + (j - 8) NW) .. +1 (lane
+    // l: chunk l % 32 ^ 4 (row % 4) of row l / 32).  Byte offsets from the
+    // operand base at k = 0 (the launcher keeps both extents below 2^31).
+    uint32_t doff[NCOPY];
+#pragma unroll
+    for (int j = 0; j < A_COPIES; ++j) {
+        const int row = 8 * (wave_u + j * NW) + lane / 8;
+        doff[j] = 2u * (uint32_t)((m0 + row) * p.lda + 8 * ((lane % 8) ^ swz(row)));
+    }
+#pragma unroll
+    for (int j = 0; j < B_COPIES; ++j) {
+        const int row = (64 / CPRB) * (wave_u + j * NW) + lane / CPRB;
+        doff[A_COPIES + j] = 2u * (uint32_t)(row * p.ldb + n0 + 8 * ((lane % CPRB) ^ (4 * (row & 3))));
+    }
+    constexpr int kRawBufferWord3 = 0x00020000;
+    const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.A), (short)0, (int)(2 * (int64_t)p.M * p.lda), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.B), (short)0, (int)(2 * (int64_t)p.K * p.ldb), kRawBufferWord3);
+    auto copy = [&](int j, int k0, int buf) __attribute__((always_inline)) {
+        if (j < A_COPIES)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_a, (__attribute__((address_space(3))) void*)(lds + buf * A_ST + 8 * (wave_u + j * NW) * kBK),
+                16, (int)doff[j], 2 * k0, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_b,
+                (__attribute__((address_space(3))) void*)(lds + B_BASE + buf * B_ST +
+                                                          (64 / CPRB) * (wave_u + (j - A_COPIES) * NW) * BN),
+                16, (int)doff[j], 2 * k0 * (int)p.ldb, 0, 0);
+    };
+
+    // Fragment addresses in bytes for stage 0.  A: fragment f of step s, the
+    // 128-bit read of gemm16_kernel.  B: fragment f at step 0, k 0..3 of the
+    // lane half; step s adds 16 rows (8192 bytes), k 4..7 four rows (2048).
+    auto b_elem = [](int r, int c) __attribute__((always_inline)) { return r * BN + 8 * (c ^ (4 * (r & 3))); };
+    uint32_t aaddr[FM][kBK / 16], baddr[FN];
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int st = 0; st < kBK / 16; ++st)
+            aaddr[f][st] = lds_addr(lds) + 2 * lds_elem(wm * WM + f * 32 + li, 2 * st + lh);
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+        const int n = wn * WN + f * 32 + 16 * (tr_g & 1) + 4 * (tr_j & 3);
+        const int row0 = 8 * (tr_g >> 1) + (tr_j >> 2);
+        baddr[f] = lds_addr(lds + B_BASE) + 2 * (b_elem(row0, n >> 3) + 4 * ((n >> 2) & 1));
+    }
+
+    u32x4 a[2][FM], b[2][FN];
+    // Read i of step s from stage buf into fragment set t: i < 4 fragment i
+    // of A, else half (i - 4) % 2 of fragment (i - 4) / 2 of B.
+    auto read_op = [&](int buf, int s, int t, int i) __attribute__((always_inline)) {
+        const uint32_t soff = (uint32_t)buf * 32768u;
+        if (i < FM) {
+            a[t][i] = lds_read128(aaddr[i][s] + soff);
+        } else {
+            const int f = (i - FM) / 2, r = (i - FM) % 2;
+            const u32x2 v = read_tr16_off(baddr[f] + soff, 8192 * s + 2048 * r);
+            b[t][f][2 * r] = v[0];
+            b[t][f][2 * r + 1] = v[1];
+        }
+    };
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // One step: the 16 matrix instructions on fragment set t (if MM); after
+    // the q-th, reads of step rs from stage rbuf into set t ^ 1 (two after
+    // each of the first six, if R) and, after each odd one, copy CB + q / 2
+    // (while below CE) of the phase at k_copy into stage cbuf.
+    auto step = [&](auto mm, int t, auto reads, int rbuf, int rs, auto cb, auto ce, int k_copy,
+                    int cbuf) __attribute__((always_inline)) {
+        constexpr bool MM = decltype(mm)::value;
+        constexpr bool R = decltype(reads)::value;
+        constexpr int CB = decltype(cb)::value, CE = decltype(ce)::value;
+        unroll<FM * FN>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            if constexpr (MM) {
+                acc[q / FN][q % FN] = mfma16<FMT>(a[t][q / FN], b[t][q % FN], acc[q / FN][q % FN]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (R && q < 6) {
+                read_op(rbuf, rs, t ^ 1, 2 * q);
+                read_op(rbuf, rs, t ^ 1, 2 * q + 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (q % 2 == 1 && CB + q / 2 < CE) {
+                copy(CB + q / 2, k_copy, cbuf);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    };
+    // The fragments of set t are complete (the tied wait also keeps the
+    // compiler from adding a wait of its own that would cover later reads).
+    auto wait_set = [&](int t) __attribute__((always_inline)) {
+        wait_tied(a[t]);
+        wait_tied(b[t]);
+    };
+    // This wave's copies have landed; then the barrier makes every wave's
+    // copies visible and releases the stage that was read.
+    auto barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        asm volatile("" ::: "memory");
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    using c0 = std::integral_constant<int, 0>;
+    using c8 = std::integral_constant<int, 8>;
+    using c16 = std::integral_constant<int, 16>;
+    // Steps 0..2 of the phase on stage cur (step 0's fragments already read)
+    // and the wait for step 3's; copies 8..15 of the phase at k_copy into
+    // stage cbuf with step 0 if WC.
+    auto steps012 = [&](int cur, auto wc, int k_copy, int cbuf) __attribute__((always_inline)) {
+        constexpr bool WC = decltype(wc)::value;
+        wait_set(0);
+        if constexpr (WC) step(yes{}, 0, yes{}, cur, 1, c8{}, c16{}, k_copy, cbuf);
+        else step(yes{}, 0, yes{}, cur, 1, c0{}, c0{}, 0, 0);
+        wait_set(1);
+        step(yes{}, 1, yes{}, cur, 2, c0{}, c0{}, 0, 0);
+        wait_set(0);
+        step(yes{}, 0, yes{}, cur, 3, c0{}, c0{}, 0, 0);
+        wait_set(1);
+    };
+
+    // Stage ph & 1 holds phase ph.  Between the barriers that end phases
+    // ph - 1 and ph run the deferred last step of phase ph - 1 (with copies
+    // 0..7 of phase ph + 1 and the first reads of phase ph) and steps 0..2 of
+    // phase ph (copies 8..15 with step 0).
+    const int P = p.K / kBK;
+#pragma unroll
+    for (int j = 0; j < NCOPY; ++j) copy(j, 0, 0);
+    barrier();
+#pragma unroll
+    for (int i = 0; i < 12; ++i) read_op(0, 0, 0, i);
+    if (P > 1) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) copy(j, kBK, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int ph = 0;
+    for (; ph + 2 < P; ++ph) {
+        const int cur = ph & 1;
+        steps012(cur, yes{}, (ph + 1) * kBK, cur ^ 1);
+        barrier();
+        step(yes{}, 1, yes{}, cur ^ 1, 0, c0{}, c8{}, (ph + 2) * kBK, cur);
+    }
+    if (ph + 1 < P) {
+        const int cur = ph & 1;
+        steps012(cur, yes{}, (ph + 1) * kBK, cur ^ 1);
+        barrier();
+        step(yes{}, 1, yes{}, cur ^ 1, 0, c0{}, c0{}, 0, 0);
+        ++ph;
+    }
+    steps012(ph & 1, no{}, 0, 0);
+    step(yes{}, 1, no{}, 0, 0, c0{}, c0{}, 0, 0);
+
+    // Guarded store (full tiles: the guard never fails).  Register r of lane
+    // (li, lh) is row 8 (r / 4) + 4 lh + r % 4 of its 32 x 32 block.
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn * WN + j * 32 + li;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // op(A) x op(B): the backward-pass products (X^T dY, dY W^T) in mixed
 // precision.  Each factor is an MN x K matrix of op(X) (MN = M for A, N for
 // B) stored either
@@ -715,6 +968,24 @@ struct MixedConfig {
     {{launch16<0, BM, BN, WM, WN, false, false, false>, launch16<0, BM, BN, WM, WN, D, true, T>},   \
      {launch16<1, BM, BN, WM, WN, false, false, false>, launch16<1, BM, BN, WM, WN, D, true, T>}}
 
+// The scheduled kernel takes full 256 x 256 tiles, K a multiple of 64,
+// vector-aligned operands and operand extents below 2^31 bytes (its copies
+// use 32-bit offsets); anything else runs configuration 6 (the 8-wave
+// direct-copy kernel: same tiles, same k order, same bits).
+bool sched_fits(const Gemm16Args& p) {
+    const bool vec = ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 3) == 0 &&
+                     (p.lda % 2) == 0 && (p.ldb % 2) == 0;
+    return vec && p.M % 256 == 0 && p.N % 256 == 0 && p.K % kBK == 0 && p.K > 0 &&
+           2 * (int64_t)p.M * p.lda < (1ll << 31) && 2 * (int64_t)p.K * p.ldb < (1ll << 31);
+}
+template <int FMT>
+hipError_t launch_sched(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                        unsigned blocks) {
+    if (!sched_fits(p)) return launch16<FMT, 256, 256, 2, 4, true, true, true>(p, s, tiles_m, tiles_n, group_m, blocks);
+    hipLaunchKernelGGL(gemm16_sched_kernel<FMT>, dim3(blocks), dim3(256), 0, s, p, tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+}
+
 const MixedConfig kMixed[] = {
     {"mixed256x256_bk64_w2x4_directA", 256, 256, 8, MIXED(256, 256, 2, 4, true, false)},
     {"mixed256x256_bk64_w2x4", 256, 256, 8, MIXED(256, 256, 2, 4, false, false)},
@@ -724,6 +995,10 @@ const MixedConfig kMixed[] = {
     {"mixed256x256_bk64_w2x2_directAB", 256, 256, 8, MIXED(256, 256, 2, 2, true, true)},
     {"mixed256x256_bk64_w2x4_directAB", 256, 256, 8, MIXED(256, 256, 2, 4, true, true)},
     {"mixed128x128_bk64_w2x2_directAB", 128, 128, 8, MIXED(128, 128, 2, 2, true, true)},
+    // misaligned operands: the element-wise 8-wave kernel, as for 6
+    {"mixed256x256_bk64_w4_sched", 256, 256, 8,
+     {{launch16<0, 256, 256, 2, 4, false, false, false>, launch_sched<0>},
+      {launch16<1, 256, 256, 2, 4, false, false, false>, launch_sched<1>}}},
 };
 #undef MIXED
 constexpr int kNumMixed = (int)(sizeof(kMixed) / sizeof(kMixed[0]));
@@ -776,11 +1051,12 @@ int mixed_num_configs() { return kNumMixed; }
 const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed[c].name : nullptr; }
 
 // The largest tile that still gives every CU a workgroup, with both factors
-// copied straight into LDS.
+// copied straight into LDS; for 256 x 256 tiles the scheduled kernel (which
+// itself runs configuration 6 on problems it does not take).
 int mixed_pick_config(int M, int N, int /*K*/) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
-    if (t256 >= 256) return 6;
+    if (t256 >= 256) return 8;
     if (t128 >= 256) return 7;
     return 3;
 }

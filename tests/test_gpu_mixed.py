@@ -100,6 +100,46 @@ def test_mixed_every_variant(fmt):
                 check(prob, prob.run(variant=v), dist, f"variant {v} {M}x{N}x{K} {dist}")
 
 
+SCHED = 8          # the scheduled 4-wave kernel (full 256 x 256 tiles, K % 64 == 0)
+SCHED_SHAPES = [(256, 256, 64), (256, 512, 128), (512, 256, 192), (768, 1024, 320), (1024, 1024, 1024),
+                (512, 768, 4160)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_mixed_scheduled_kernel(fmt):
+    """The scheduled kernel on shapes it takes: one, two, three and more
+    phases (its prologue, tail and main-loop paths) and long K; integer data
+    exactly, float data within the bound, and the same bits as the 8-wave
+    kernel of configuration 6 (same tiles, same k order)."""
+    assert binding.gemm_mixed_variant_name(SCHED) == "mixed256x256_bk64_w4_sched"
+    for (M, N, K) in SCHED_SHAPES:
+        for dist in ("int", "uniform"):
+            gen = np.random.default_rng([M, N, K, len(fmt), len(dist)])
+            prob, _, _ = make(fmt, M, N, K, dist, gen)
+            say(f"mixed {fmt} scheduled {M}x{N}x{K} {dist}")
+            C = prob.run(variant=SCHED)
+            check(prob, C, dist, f"scheduled {fmt} {M}x{N}x{K} {dist}")
+            ref6 = prob.run(variant=6).view.copy()
+            assert np.array_equal(C.view.view(np.uint32), ref6.view(np.uint32)), (fmt, M, N, K, dist)
+            del prob
+
+
+def test_mixed_scheduled_kernel_padded_and_fallback():
+    """Padded leading dimensions (still taken by the scheduled kernel), and
+    shapes it does not take (ragged tiles, ragged K, 2-byte-offset views),
+    which run configuration 6 instead: same bits either way."""
+    gen = np.random.default_rng(123)
+    cases = [(512, 512, 256, 0, (8, 16, 3)), (520, 512, 256, 0, (0, 0, 0)), (512, 512, 200, 0, (0, 0, 0)),
+             (512, 512, 256, 1, (2, 2, 2))]
+    for (M, N, K, offset, pad) in cases:
+        prob, _, _ = make("bf16", M, N, K, "uniform", gen, offset, pad)
+        say(f"mixed scheduled/fallback {M}x{N}x{K} offset={offset} pad={pad}")
+        C = prob.run(variant=SCHED)
+        check(prob, C, "uniform", f"scheduled/fallback {M}x{N}x{K}")
+        ref6 = prob.run(variant=6).view.copy()
+        assert np.array_equal(C.view.view(np.uint32), ref6.view(np.uint32)), (M, N, K, offset, pad)
+
+
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_mixed_load_paths_agree_bitwise(fmt):
     """The vector and element-wise load paths sum in the same order: the

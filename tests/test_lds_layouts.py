@@ -204,3 +204,51 @@ def test_mixed_transposed_b_reads_conflict_free(bn):
             for r in range(2):
                 assert degree(words(s, r, nf, True), 2, 64, 32) == 1, (nf, s, r)
     assert degree(words(0, 0, 0, False), 2, 64, 32) == 4
+
+
+def test_scheduled_mixed_kernel_addresses():
+    """The scheduled 16-bit kernel computes its fragment addresses once per
+    lane and adds only the stage offset and an instruction offset per read.
+    Restated here: for every wave, lane, fragment, step, half and stage the
+    decomposed address equals the full layout formula (A rows of 64 values,
+    chunk c of row r at c ^ f(r); B rows of 256 values, chunk c of row r at
+    c ^ 4 (r % 4)), the instruction offset fits its 16 bits, and the four
+    tiles (A and B, two stages) are disjoint and fill 128 KB."""
+    BK, BM, BN = 64, 256, 256
+    A_ST, B_BASE, B_ST = BM * BK, 2 * BM * BK, BK * BN          # elements
+
+    def swz(r):
+        return ((r >> 1) ^ (r >> 4)) & 7
+
+    def lds_elem(r, c):
+        return r * BK + 8 * (c ^ swz(r))
+
+    def b_elem(r, c):
+        return r * BN + 8 * (c ^ (4 * (r & 3)))
+
+    seen_a, seen_b = set(), set()
+    for wave in range(4):
+        wm, wn = wave // 2, wave % 2
+        for lane in range(64):
+            li, lh, g, j = lane & 31, lane >> 5, lane >> 4, lane & 15
+            for f in range(4):
+                n = wn * 128 + f * 32 + 16 * (g & 1) + 4 * (j & 3)
+                row0 = 8 * (g >> 1) + (j >> 2)
+                baddr = 2 * (B_BASE + b_elem(row0, n >> 3) + 4 * ((n >> 2) & 1))
+                for s in range(BK // 16):
+                    aaddr = 2 * lds_elem(wm * 128 + f * 32 + li, 2 * s + lh)
+                    for stage in (0, 1):
+                        a_full = 2 * (stage * A_ST + lds_elem(wm * 128 + f * 32 + li, 2 * s + lh))
+                        assert aaddr + 32768 * stage == a_full
+                        seen_a.add(a_full // 16)
+                        for r in (0, 1):
+                            off = 8192 * s + 2048 * r
+                            assert 0 <= off < 1 << 16
+                            row = 16 * s + 8 * (g >> 1) + 4 * r + (j >> 2)
+                            b_full = 2 * (B_BASE + stage * B_ST + b_elem(row, n >> 3) + 4 * ((n >> 2) & 1))
+                            assert baddr + 32768 * stage + off == b_full
+                            seen_b.add(b_full // 8)
+    # every 16-byte A chunk and every 8-byte B piece of both stages is read
+    assert seen_a == set(range(2 * A_ST * 2 // 16))
+    assert seen_b == set(range(B_BASE * 2 // 8, (B_BASE + 2 * B_ST) * 2 // 8))
+    assert (B_BASE + 2 * B_ST) * 2 == 128 * 1024
