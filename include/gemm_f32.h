@@ -242,7 +242,12 @@ const char *reduce_sum_f32_variant_name(int variant);  /* NULL if unknown */
  * are served by element-wise loads (correct, slower).
  * gemm_mixed picks the tile shape for the problem; gemm_mixed_variant runs
  * tile configuration `variant` (0 .. gemm_mixed_num_variants() - 1, named by
- * gemm_mixed_variant_name).
+ * gemm_mixed_variant_name).  The scheduled configuration
+ * (mixed256x256_bk64_w4_sched, gemm_mixed's choice once there are 256 tiles
+ * of 256 x 256) takes M and N multiples of 256, K a multiple of 64, 4-byte
+ * aligned operands with even leading dimensions and operands under 2^31
+ * bytes; other problems given to it run mixed256x256_bk64_w2x4_directAB,
+ * which has the same tiles and summation order (the same bits).
  */
 #define GEMM_MIXED_BF16 0
 #define GEMM_MIXED_F16  1
