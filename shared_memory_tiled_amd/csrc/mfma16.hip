@@ -56,7 +56,7 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 constexpr int kBK = 64;          // k values per phase = one 128-byte LDS row
 constexpr int kCPR = kBK / 8;    // 16-byte chunks per LDS row
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 4)) & 7; }
+__host__ __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 4)) & 7; }
 // Element offset, inside a tile stage, of logical chunk c of row r.
 __device__ __forceinline__ int lds_elem(int r, int c) { return r * kBK + 8 * (c ^ swz(r)); }
 
@@ -165,7 +165,9 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Q..
     (f(std::integral_constant<int, Q>{}), ...);
 }
 // f(std::integral_constant<int, q>{}) for q = 0 .. N - 1, in order: every
-// index is a compile-time constant, so arrays indexed by it stay in registers.
+// index is a compile-time constant, so arrays indexed by it stay in registers
+// (a loop under #pragma unroll is unrolled only after the pass that would
+// have kept them there).
 template <int N, typename F>
 __device__ __forceinline__ void unroll(F&& f) {
     unroll_seq(f, std::make_integer_sequence<int, N>{});
@@ -514,11 +516,12 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
 
 // ---------------------------------------------------------------------------
 // The scheduled kernel: 256 x 256 tiles of full phases (M and N multiples of
-// 256, K of 64, vector-aligned operands), four waves of 128 x 128, one per
-// SIMD, with every instruction of the K loop placed in program order.  Same
-// LDS layouts and the same k order as gemm16_kernel (so the same bits), but:
+// 256, K of 64, vector-aligned operands under 2^31 bytes each), four waves of
+// 128 x 128, one per SIMD, with every instruction of the K loop placed in
+// program order.  Same LDS layouts and the same k order as the kernels above
+// (so the same bits), but:
 //  * Each step issues its 16 matrix instructions one at a time, with the next
-//    step's fragment reads (two after each of the first six) and the copies
+//    step's fragment reads (two after each of the first ones) and the copies
 //    of the next phase (one after each odd one) between them, so the reads'
 //    latency and the copies' issue hide behind matrix work.  Scheduling
 //    barriers keep the compiler from regrouping them.
@@ -530,21 +533,56 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
 //    a whole phase ahead of their use.  They are buffer loads into LDS: base
 //    and extent in a resource, the per-lane offset in a register, the phase's
 //    k in the scalar offset, so they cost no vector instruction.
-//  * Fragment read addresses are computed once per lane (A per fragment and
-//    step; B per fragment, with the step and half as an instruction offset);
-//    a phase only adds the stage offset.
-// LDS: stage st of A at byte 32768 st, of B at byte 65536 + 32768 st.
-template <int FMT>
+//  * Fragment read addresses are computed once per lane; a phase only adds
+//    the stage offset.
+// With two waves per SIMD (the kernels above) the waves of a SIMD drift
+// apart within a phase and the younger one runs alone, its latencies
+// exposed, while the older one waits at the barrier.
+//
+// Each factor's tile is one of two kinds (see gemm16_op_kernel):
+//   KC (k-contiguous: A as stored, B stored transposed): 256 rows of 64 k,
+//      chunk c of row r at c ^ f(r); a fragment is one 128-bit read; a copy
+//      fills 8 rows;
+//   MC (mn-contiguous: B as stored, A stored transposed): 64 k rows of 256
+//      values, chunk c of row r at c ^ 4 (r % 4); a fragment is two
+//      ds_read_b64_tr_b16 reads; a copy fills 2 rows.
+// Both are 32 KB per stage: LDS holds A's stages at bytes 0 and 32768, B's at
+// 65536 and 98304.
+template <bool KC>
+struct SchedTile {
+    static constexpr int MNT = 256, NW = 4;
+    static constexpr int READS = KC ? 4 : 8;      // LDS reads per step for 4 fragments
+    // Copy j (0..7) of wave w: element offset, inside the tile stage, of the
+    // first LDS element it fills, and lane l's stored (row, 8-value chunk).
+    __host__ __device__ static int copy_dst(int w, int j) {
+        return KC ? 8 * (w + j * NW) * kBK : 2 * (w + j * NW) * MNT;
+    }
+    // Byte offset of lane l's 16 bytes of copy j from the stored matrix's base
+    // at k = 0 (mn0: the tile's first row or column of op(X)).
+    __host__ __device__ static uint32_t copy_src(int w, int j, int lane, int mn0, int64_t ld) {
+        if constexpr (KC) {
+            const int row = 8 * (w + j * NW) + lane / 8;
+            return 2u * (uint32_t)((mn0 + row) * ld + 8 * ((lane % 8) ^ swz(row)));
+        } else {
+            const int row = 2 * (w + j * NW) + lane / 32;
+            return 2u * (uint32_t)(row * ld + mn0 + 8 * ((lane % 32) ^ (4 * (row & 3))));
+        }
+    }
+    // Byte offset of the phase at k0 from the phase at 0.
+    __host__ __device__ static int phase_bytes(int k0, int64_t ld) { return KC ? 2 * k0 : 2 * k0 * (int)ld; }
+};
+
+template <int FMT, bool KCA, bool KCB>
 __global__ __launch_bounds__(256)
 void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     constexpr int BM = 256, BN = 256, NW = 4, WM = 128, WN = 128, FM = 4, FN = 4;
-    constexpr int CPRB = BN / 8;                          // 16-byte chunks per B row
-    constexpr int A_COPIES = BM / 8 / NW;                 // 1 KB copies per wave and phase
-    constexpr int B_COPIES = kBK * BN * 2 / 1024 / NW;
-    constexpr int NCOPY = A_COPIES + B_COPIES;
-    constexpr int A_ST = BM * kBK, B_BASE = 2 * BM * kBK, B_ST = kBK * BN;   // elements
-    static_assert(A_ST * 2 == 32768 && B_ST * 2 == 32768 && NCOPY == 16, "stage layout");
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BM + BN) * kBK];
+    using TA = SchedTile<KCA>;
+    using TB = SchedTile<KCB>;
+    constexpr int TILE = 256 * kBK;                       // elements per tile stage
+    constexpr int A_COPIES = 8, NCOPY = 16;               // 1 KB copies per wave and phase
+    constexpr int NREAD = TA::READS + TB::READS;          // LDS reads per step
+    static_assert(TILE * 2 == 32768 && NREAD <= 16, "stage layout");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[4 * TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -562,69 +600,82 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     const int m0 = (first_m + in_g % gm) * BM;
     const int n0 = (in_g / gm) * BN;
 
-    // Copy j of this wave: A rows 8 (wave + j NW) .. +7 (lane l: chunk
-    // l % 8 ^ f(row) of row l / 8), B rows 2 (wave + (j - 8) NW) .. +1 (lane
-    // l: chunk l % 32 ^ 4 (row % 4) of row l / 32).  Byte offsets from the
-    // operand base at k = 0 (the launcher keeps both extents below 2^31).
+    // Copies 0..7 fill A's tile, 8..15 B's (byte offsets: the launcher keeps
+    // both operands below 2^31 bytes).
     uint32_t doff[NCOPY];
 #pragma unroll
     for (int j = 0; j < A_COPIES; ++j) {
-        const int row = 8 * (wave_u + j * NW) + lane / 8;
-        doff[j] = 2u * (uint32_t)((m0 + row) * p.lda + 8 * ((lane % 8) ^ swz(row)));
-    }
-#pragma unroll
-    for (int j = 0; j < B_COPIES; ++j) {
-        const int row = (64 / CPRB) * (wave_u + j * NW) + lane / CPRB;
-        doff[A_COPIES + j] = 2u * (uint32_t)(row * p.ldb + n0 + 8 * ((lane % CPRB) ^ (4 * (row & 3))));
+        doff[j] = TA::copy_src(wave_u, j, lane, m0, p.lda);
+        doff[A_COPIES + j] = TB::copy_src(wave_u, j, lane, n0, p.ldb);
     }
     constexpr int kRawBufferWord3 = 0x00020000;
+    const int64_t a_rows = KCA ? p.M : p.K, b_rows = KCB ? p.N : p.K;
     const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.A), (short)0, (int)(2 * (int64_t)p.M * p.lda), kRawBufferWord3);
+        const_cast<uint16_t*>(p.A), (short)0, (int)(2 * a_rows * p.lda), kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.B), (short)0, (int)(2 * (int64_t)p.K * p.ldb), kRawBufferWord3);
+        const_cast<uint16_t*>(p.B), (short)0, (int)(2 * b_rows * p.ldb), kRawBufferWord3);
     auto copy = [&](int j, int k0, int buf) __attribute__((always_inline)) {
-        if (j < A_COPIES)
+        if (j < A_COPIES) {
+            const int soff = TA::phase_bytes(k0, p.lda);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc_a, (__attribute__((address_space(3))) void*)(lds + buf * A_ST + 8 * (wave_u + j * NW) * kBK),
-                16, (int)doff[j], 2 * k0, 0, 0);
-        else
+                rsrc_a, (__attribute__((address_space(3))) void*)(lds + buf * TILE + TA::copy_dst(wave_u, j)), 16,
+                (int)doff[j], soff, 0, 0);
+        } else {
+            const int soff = TB::phase_bytes(k0, p.ldb);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc_b,
-                (__attribute__((address_space(3))) void*)(lds + B_BASE + buf * B_ST +
-                                                          (64 / CPRB) * (wave_u + (j - A_COPIES) * NW) * BN),
-                16, (int)doff[j], 2 * k0 * (int)p.ldb, 0, 0);
+                (__attribute__((address_space(3))) void*)(lds + (2 + buf) * TILE + TB::copy_dst(wave_u, j - A_COPIES)),
+                16, (int)doff[j], soff, 0, 0);
+        }
     };
 
-    // Fragment addresses in bytes for stage 0.  A: fragment f of step s, the
-    // 128-bit read of gemm16_kernel.  B: fragment f at step 0, k 0..3 of the
-    // lane half; step s adds 16 rows (8192 bytes), k 4..7 four rows (2048).
-    auto b_elem = [](int r, int c) __attribute__((always_inline)) { return r * BN + 8 * (c ^ (4 * (r & 3))); };
-    uint32_t aaddr[FM][kBK / 16], baddr[FN];
+    // Fragment addresses in bytes for stage 0 of the tile at element `base`:
+    // KC, fragment f of step s (the 128-bit read of gemm16_kernel's A); MC,
+    // fragment f at step 0, k 0..3 of the lane half (step s adds 16 rows, 8192
+    // bytes, k 4..7 four rows, 2048: instruction offsets).
+    auto mc_elem = [](int r, int c) __attribute__((always_inline)) { return r * 256 + 8 * (c ^ (4 * (r & 3))); };
+    auto frag_addr = [&](auto kc, int base, int mn, int s) __attribute__((always_inline)) -> uint32_t {
+        if constexpr (decltype(kc)::value) {
+            return lds_addr(lds + base) + 2u * lds_elem(mn + li, 2 * s + lh);
+        } else {
+            const int n = mn + 16 * (tr_g & 1) + 4 * (tr_j & 3);
+            const int row0 = 8 * (tr_g >> 1) + (tr_j >> 2);
+            return lds_addr(lds + base) + 2u * (mc_elem(row0, n >> 3) + 4 * ((n >> 2) & 1));
+        }
+    };
+    constexpr int SA = KCA ? kBK / 16 : 1, SB = KCB ? kBK / 16 : 1;
+    uint32_t aaddr[FM][SA], baddr[FN][SB];
 #pragma unroll
     for (int f = 0; f < FM; ++f)
 #pragma unroll
-        for (int st = 0; st < kBK / 16; ++st)
-            aaddr[f][st] = lds_addr(lds) + 2 * lds_elem(wm * WM + f * 32 + li, 2 * st + lh);
+        for (int st = 0; st < SA; ++st)
+            aaddr[f][st] = frag_addr(std::integral_constant<bool, KCA>{}, 0, wm * WM + f * 32, st);
 #pragma unroll
-    for (int f = 0; f < FN; ++f) {
-        const int n = wn * WN + f * 32 + 16 * (tr_g & 1) + 4 * (tr_j & 3);
-        const int row0 = 8 * (tr_g >> 1) + (tr_j >> 2);
-        baddr[f] = lds_addr(lds + B_BASE) + 2 * (b_elem(row0, n >> 3) + 4 * ((n >> 2) & 1));
-    }
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int st = 0; st < SB; ++st)
+            baddr[f][st] = frag_addr(std::integral_constant<bool, KCB>{}, 2 * TILE, wn * WN + f * 32, st);
 
     u32x4 a[2][FM], b[2][FN];
-    // Read i of step s from stage buf into fragment set t: i < 4 fragment i
-    // of A, else half (i - 4) % 2 of fragment (i - 4) / 2 of B.
+    // Read i (0 .. READS - 1) of one factor's fragments of step s, from the
+    // stage at soff bytes, into x: KC, fragment i; MC, half i % 2 of fragment
+    // i / 2.
+    auto read_one = [&](auto kc, u32x4 (&x)[4], const auto& addr, uint32_t soff, int s,
+                        int i) __attribute__((always_inline)) {
+        if constexpr (decltype(kc)::value) {
+            x[i] = lds_read128(addr[i][s] + soff);
+        } else {
+            const int f = i / 2, r = i % 2;
+            const u32x2 v = read_tr16_off(addr[f][0] + soff, 8192 * s + 2048 * r);
+            x[f][2 * r] = v[0];
+            x[f][2 * r + 1] = v[1];
+        }
+    };
+    // Read i of step s from stage buf into set t: A's reads first, then B's.
     auto read_op = [&](int buf, int s, int t, int i) __attribute__((always_inline)) {
         const uint32_t soff = (uint32_t)buf * 32768u;
-        if (i < FM) {
-            a[t][i] = lds_read128(aaddr[i][s] + soff);
-        } else {
-            const int f = (i - FM) / 2, r = (i - FM) % 2;
-            const u32x2 v = read_tr16_off(baddr[f] + soff, 8192 * s + 2048 * r);
-            b[t][f][2 * r] = v[0];
-            b[t][f][2 * r + 1] = v[1];
-        }
+        if (i < TA::READS) read_one(std::integral_constant<bool, KCA>{}, a[t], aaddr, soff, s, i);
+        else read_one(std::integral_constant<bool, KCB>{}, b[t], baddr, soff, s, i - TA::READS);
     };
     floatx16 acc[FM][FN];
 #pragma unroll
@@ -635,9 +686,9 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // One step: the 16 matrix instructions on fragment set t (if MM); after
-    // the q-th, reads of step rs from stage rbuf into set t ^ 1 (two after
-    // each of the first six, if R) and, after each odd one, copy CB + q / 2
-    // (while below CE) of the phase at k_copy into stage cbuf.
+    // the q-th, reads 2q and 2q + 1 of step rs from stage rbuf into set t ^ 1
+    // (if R) and, after each odd one, copy CB + q / 2 (while below CE) of the
+    // phase at k_copy into stage cbuf.
     auto step = [&](auto mm, int t, auto reads, int rbuf, int rs, auto cb, auto ce, int k_copy,
                     int cbuf) __attribute__((always_inline)) {
         constexpr bool MM = decltype(mm)::value;
@@ -649,7 +700,7 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
                 acc[q / FN][q % FN] = mfma16<FMT>(a[t][q / FN], b[t][q % FN], acc[q / FN][q % FN]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (R && q < 6) {
+            if constexpr (R && 2 * q < NREAD) {
                 read_op(rbuf, rs, t ^ 1, 2 * q);
                 read_op(rbuf, rs, t ^ 1, 2 * q + 1);
                 __builtin_amdgcn_sched_barrier(0);
@@ -702,7 +753,7 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     for (int j = 0; j < NCOPY; ++j) copy(j, 0, 0);
     barrier();
 #pragma unroll
-    for (int i = 0; i < 12; ++i) read_op(0, 0, 0, i);
+    for (int i = 0; i < NREAD; ++i) read_op(0, 0, 0, i);
     if (P > 1) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) copy(j, kBK, 1);
@@ -969,23 +1020,33 @@ struct MixedConfig {
      {launch16<1, BM, BN, WM, WN, false, false, false>, launch16<1, BM, BN, WM, WN, D, true, T>}}
 
 // The scheduled kernel takes full 256 x 256 tiles, K a multiple of 64,
-// vector-aligned operands and operand extents below 2^31 bytes (its copies
-// use 32-bit offsets); anything else runs configuration 6 (the 8-wave
-// direct-copy kernel: same tiles, same k order, same bits).
-bool sched_fits(const Gemm16Args& p) {
+// vector-aligned operands and operands below 2^31 bytes (its copies use
+// 32-bit offsets); anything else runs the 8-wave kernel of the same tile
+// (gemm16_kernel, configuration 6, or gemm16_op_kernel): same tiles, same k
+// order, same bits.  op_a / op_b: 1 if that factor is stored transposed.
+bool sched_fits(const Gemm16Args& p, int op_a, int op_b) {
     const bool vec = ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 3) == 0 &&
                      (p.lda % 2) == 0 && (p.ldb % 2) == 0;
+    const int64_t a_rows = op_a ? p.K : p.M, b_rows = op_b ? p.N : p.K;
     return vec && p.M % 256 == 0 && p.N % 256 == 0 && p.K % kBK == 0 && p.K > 0 &&
-           2 * (int64_t)p.M * p.lda < (1ll << 31) && 2 * (int64_t)p.K * p.ldb < (1ll << 31);
+           2 * a_rows * p.lda < (1ll << 31) && 2 * b_rows * p.ldb < (1ll << 31);
 }
-// Tile-row groups: 4 for the scheduled kernel, 8 for configuration 6 (each
-// the fastest measured at 8192^3).
-template <int FMT>
-hipError_t launch_sched(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
-                        unsigned blocks) {
-    if (!sched_fits(p)) return launch16<FMT, 256, 256, 2, 4, true, true, true>(p, s, tiles_m, tiles_n, 8, blocks);
-    hipLaunchKernelGGL(gemm16_sched_kernel<FMT>, dim3(blocks), dim3(256), 0, s, p, tiles_m, tiles_n, group_m);
+template <int FMT, bool KCA, bool KCB>
+hipError_t launch_sched_kernel(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                               unsigned blocks) {
+    hipLaunchKernelGGL((gemm16_sched_kernel<FMT, KCA, KCB>), dim3(blocks), dim3(256), 0, s, p, tiles_m, tiles_n,
+                       group_m);
     return hipGetLastError();
+}
+// Tile-row groups: 4 for the scheduled kernel, 8 for the 8-wave kernel (each
+// the fastest measured at 8192^3).
+constexpr int kSchedGroupM = 4, kDirectGroupM = 8;
+template <int FMT>
+hipError_t launch_sched(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int /*group_m*/,
+                        unsigned blocks) {
+    if (!sched_fits(p, 0, 0))
+        return launch16<FMT, 256, 256, 2, 4, true, true, true>(p, s, tiles_m, tiles_n, kDirectGroupM, blocks);
+    return launch_sched_kernel<FMT, true, false>(p, s, tiles_m, tiles_n, kSchedGroupM, blocks);
 }
 
 const MixedConfig kMixed[] = {
@@ -998,7 +1059,7 @@ const MixedConfig kMixed[] = {
     {"mixed256x256_bk64_w2x4_directAB", 256, 256, 8, MIXED(256, 256, 2, 4, true, true)},
     {"mixed128x128_bk64_w2x2_directAB", 128, 128, 8, MIXED(128, 128, 2, 2, true, true)},
     // misaligned operands: the element-wise 8-wave kernel, as for 6
-    {"mixed256x256_bk64_w4_sched", 256, 256, 4,
+    {"mixed256x256_bk64_w4_sched", 256, 256, kSchedGroupM,
      {{launch16<0, 256, 256, 2, 4, false, false, false>, launch_sched<0>},
       {launch16<1, 256, 256, 2, 4, false, false, false>, launch_sched<1>}}},
 };
@@ -1030,10 +1091,11 @@ Launch16 op_launcher(int op_a, int op_b, bool vec) {
 }
 }  // namespace
 
-// op(A) x op(B): 256 x 256 tiles of eight waves once there are 256 of them,
-// else 128 x 128 tiles of four waves.  A and B are the stored matrices;
-// vector loads (and the direct copies) need 4-byte aligned bases and even
-// leading dimensions, as for gemm_mixed.
+// op(A) x op(B): 256 x 256 tiles once there are 256 of them (the scheduled
+// kernel where it fits, else eight waves of gemm16_op_kernel), else 128 x 128
+// tiles of four waves.  A and B are the stored matrices; vector loads (and
+// the direct copies) need 4-byte aligned bases and even leading dimensions,
+// as for gemm_mixed.
 hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b) {
     const bool vec = ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 3) == 0 &&
                      (p.lda % 2) == 0 && (p.ldb % 2) == 0;
@@ -1043,10 +1105,23 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
     const int tiles_m = ceil_div(p.M, tile), tiles_n = ceil_div(p.N, tile);
     const int64_t blocks = (int64_t)tiles_m * tiles_n;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    if (big && sched_fits(p, op_a, op_b)) {
+        // A k-contiguous unless stored transposed; B the reverse
+        const int key = 2 * op_a + op_b;
+        Launch16 fn;
+        if (format) {
+            fn = key == 0 ? launch_sched_kernel<1, true, false> : key == 1 ? launch_sched_kernel<1, true, true>
+               : key == 2 ? launch_sched_kernel<1, false, false> : launch_sched_kernel<1, false, true>;
+        } else {
+            fn = key == 0 ? launch_sched_kernel<0, true, false> : key == 1 ? launch_sched_kernel<0, true, true>
+               : key == 2 ? launch_sched_kernel<0, false, false> : launch_sched_kernel<0, false, true>;
+        }
+        return fn(p, s, tiles_m, tiles_n, kSchedGroupM, (unsigned)blocks);
+    }
     Launch16 fn;
     if (big) fn = format ? op_launcher<1, 256, 256, 2, 4>(op_a, op_b, vec) : op_launcher<0, 256, 256, 2, 4>(op_a, op_b, vec);
     else fn = format ? op_launcher<1, 128, 128, 2, 2>(op_a, op_b, vec) : op_launcher<0, 128, 128, 2, 2>(op_a, op_b, vec);
-    return fn(p, s, tiles_m, tiles_n, 8, (unsigned)blocks);
+    return fn(p, s, tiles_m, tiles_n, kDirectGroupM, (unsigned)blocks);
 }
 
 int mixed_num_configs() { return kNumMixed; }

@@ -89,9 +89,11 @@ def test_mixed_op_edge_shapes(ops, dist):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_mixed_op_bitwise_equal_to_plain(fmt):
-    """For 128- and 256-wide tiles, ragged edges and a ghost k phase, every
+    """For 128- and 256-wide tiles, ragged edges and a ghost k phase, and
+    full tiles of the scheduled kernel with one, two and three phases, every
     op pair gives gemm_mixed's bits on the explicitly transposed factors."""
-    for (M, N, K) in ((520, 530, 200), (1000, 1000, 1000), (4096, 4160, 264)):
+    for (M, N, K) in ((520, 530, 200), (1000, 1000, 1000), (4096, 4160, 264), (4096, 4096, 128), (4096, 4352, 64),
+                      (4352, 4096, 192)):
         gen = np.random.default_rng([M, N, K, len(fmt)])
         A, B = logical16(gen, fmt, M, N, K, "uniform")
         plain = OpProblem(fmt, "N", "N", A, B).run(plain=True).view.copy()
@@ -120,6 +122,25 @@ def test_mixed_op_square8192_sampled(ops):
     check_padding_untouched(C)
     del prob
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("ops", OPS, ids=lambda o: o[0] + o[1])
+def test_mixed_op_scheduled_exact(ops):
+    """Full 256 x 256 tiles (the scheduled kernel for every op pair) with
+    integer data: bit exact against the full oracle, both formats."""
+    op_a, op_b = ops
+    M, N, K = 4096, 4096, 192
+    for fmt in FORMATS:
+        gen = np.random.default_rng([M, N, K, len(fmt), len(op_a + op_b)])
+        A, B = logical16(gen, fmt, M, N, K, "int")
+        prob = OpProblem(fmt, op_a, op_b, as_stored(op_a, A), as_stored(op_b, B))
+        say(f"mixed op scheduled {op_a}{op_b} {fmt} {M}x{N}x{K} int")
+        C = prob.run()
+        Cref, _ = oracle.gemm16(fmt, prob.A.view, prob.B.view, threads=16, op_a=op_a, op_b=op_b)
+        check_exact(C.view, Cref, f"scheduled {op_a}{op_b} {fmt}")
+        check_padding_untouched(C)
+        del prob
+        torch.cuda.empty_cache()
 
 
 def test_mixed_op_tensor_form():
