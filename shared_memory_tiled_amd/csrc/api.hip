@@ -38,6 +38,8 @@ const Diagnostic kDiagnostics[] = {
     {"mfma256x256_bk32_w2x4_direct_swz32", 3, 10},
     {"mfma256x256_bk32_w2x4_direct_g4", 3, 11},
     {"mfma256x256_bk32_w2x4_direct_g16", 3, 12},
+    {"mfma64x64_bk16_w2x2_k4", 3, 13},
+    {"mfma64x64_bk32_w2x2_k4", 3, 14},
 };
 constexpr int kNumDiagnostics = (int)(sizeof(kDiagnostics) / sizeof(kDiagnostics[0]));
 

@@ -345,6 +345,183 @@ void gemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         }
 }
 
+// Small products: KS groups of four waves share one output tile and split its
+// phases between them (round r: group g takes phase r KS + g), each group
+// with its own double-buffered LDS stages and register-staged copies (as the
+// kernel above with !DIRECT).  A problem with few tiles then still has KS
+// waves per SIMD to hide each other's latencies.  At the end the groups'
+// accumulators meet in LDS and group 0 adds them in group order, so the
+// result is deterministic; its rounding differs from the one-group kernels
+// (each group sums its own phases first), within the same bound.
+template <int BM, int BN, int BK, int KS, bool TRANS_A, bool TRANS_B>
+__global__ __launch_bounds__(256 * KS)
+void gemm_mfma_splitk_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
+    constexpr int NWG = 4, NTG = NWG * 64;                  // waves and threads per group
+    constexpr int WM = BM / 2, WN = BN / 2;                 // 2 x 2 waves per group
+    constexpr int FM = WM / 32, FN = WN / 32;
+    static_assert(WM % 32 == 0 && WN % 32 == 0 && BK % 8 == 0 && KS >= 2, "tile shape");
+    using TA = OperandTile<BM, BK, !TRANS_A, false, 64, NTG, NWG>;
+    using TB = OperandTile<BN, BK, TRANS_B, false, 64, NTG, NWG>;
+    constexpr int STAGE = TA::WORDS + TB::WORDS;
+    constexpr int GROUP_WORDS = 2 * STAGE;
+    constexpr int RED_WORDS = (KS - 1) * BM * BN;           // partial tiles of groups 1 .. KS-1
+    constexpr int LDS_WORDS = KS * GROUP_WORDS > RED_WORDS ? KS * GROUP_WORDS : RED_WORDS;
+    __shared__ __attribute__((aligned(16))) float lds[LDS_WORDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int kg = __builtin_amdgcn_readfirstlane(tid / NTG);     // group (wave-uniform)
+    const int gtid = tid % NTG;
+    const int gw = gtid >> 6;                                     // wave within the group
+    const int wm = gw / 2, wn = gw % 2;
+    const int li = lane & 31, lh = lane >> 5;
+
+    const int logical = xcd_contiguous((int)blockIdx.x, tiles_m * tiles_n);
+    const int group_size = group_m * tiles_n;
+    const int g = logical / group_size;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int in_g = logical - g * group_size;
+    const int m0 = (first_m + in_g % gm) * BM;
+    const int n0 = (in_g / gm) * BN;
+
+    const Factor fa{p.A, p.lda, p.M, p.K};
+    const Factor fb{p.B, p.ldb, p.N, p.K};
+    const bool tile_inside = (m0 + BM <= p.M) && (n0 + BN <= p.N);
+    float* glds = lds + kg * GROUP_WORDS;
+
+    int64_t a_off[TA::CHUNKS], b_off[TB::CHUNKS];
+#pragma unroll
+    for (int u = 0; u < TA::CHUNKS; ++u) {
+        const int q = gtid + u * NTG;
+        a_off[u] = TA::offset(fa, m0, TA::chunk_row(q), TA::chunk_col(q));
+    }
+#pragma unroll
+    for (int u = 0; u < TB::CHUNKS; ++u) {
+        const int q = gtid + u * NTG;
+        b_off[u] = TB::offset(fb, n0, TB::chunk_row(q), TB::chunk_col(q));
+    }
+    floatx4 ra[TA::CHUNKS], rb[TB::CHUNKS];
+    auto load_tiles = [&](int k0) {
+        if (tile_inside && k0 + BK <= p.K) {
+            const float* a = p.A + TA::phase_step(fa, k0);
+            const float* b = p.B + TB::phase_step(fb, k0);
+#pragma unroll
+            for (int u = 0; u < TA::CHUNKS; ++u) __builtin_memcpy(&ra[u], a + a_off[u], 16);
+#pragma unroll
+            for (int u = 0; u < TB::CHUNKS; ++u) __builtin_memcpy(&rb[u], b + b_off[u], 16);
+            return;
+        }
+#pragma unroll
+        for (int u = 0; u < TA::CHUNKS; ++u) {
+            const int q = gtid + u * NTG;
+            ra[u] = TA::ghost_load(fa, m0, k0, TA::chunk_row(q), TA::chunk_col(q));
+        }
+#pragma unroll
+        for (int u = 0; u < TB::CHUNKS; ++u) {
+            const int q = gtid + u * NTG;
+            rb[u] = TB::ghost_load(fb, n0, k0, TB::chunk_row(q), TB::chunk_col(q));
+        }
+    };
+    auto store_tiles = [&](int buf) {
+        float* as = glds + buf * STAGE;
+        float* bs = as + TA::WORDS;
+#pragma unroll
+        for (int u = 0; u < TA::CHUNKS; ++u) {
+            const int q = gtid + u * NTG;
+            *reinterpret_cast<floatx4*>(&as[TA::word(TA::chunk_row(q), TA::chunk_col(q))]) = ra[u];
+        }
+#pragma unroll
+        for (int u = 0; u < TB::CHUNKS; ++u) {
+            const int q = gtid + u * NTG;
+            *reinterpret_cast<floatx4*>(&bs[TB::word(TB::chunk_row(q), TB::chunk_col(q))]) = rb[u];
+        }
+    };
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int phases = ceil_div(p.K, BK);
+    const int rounds = ceil_div(phases, KS);
+    // Every wave runs every round (one barrier each); a group whose phase of
+    // the round lies past K only skips its copies and its math.
+    if (kg < phases) {
+        load_tiles(kg * BK);
+        store_tiles(0);
+    }
+    __syncthreads();
+    for (int r = 0; r < rounds; ++r) {
+        const int cur = r & 1;
+        const int ph = r * KS + kg, ph_next = ph + KS;
+        if (ph_next < phases) load_tiles(ph_next * BK);
+        if (ph < phases) {
+            const float* as = glds + cur * STAGE;
+            const float* bs = as + TA::WORDS;
+#pragma unroll
+            for (int kk = 0; kk < BK; kk += 8) {
+                floatx4 a[FM], b[FN];
+#pragma unroll
+                for (int f = 0; f < FM; ++f) a[f] = TA::fragment(as, wm * WM + f * 32 + li, kk, lh);
+#pragma unroll
+                for (int f = 0; f < FN; ++f) b[f] = TB::fragment(bs, wn * WN + f * 32 + li, kk, lh);
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
+            }
+        }
+        if (ph_next < phases) store_tiles(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Groups 1 .. KS-1 leave their partial tiles in LDS (register r of lane l
+    // of wave w at word ((g - 1) NWG + w) FM FN 16 64 + (i FN + j) 16 64 + 64 r
+    // + l: consecutive lanes, consecutive words); group 0 adds them in order.
+    constexpr int PER_WAVE = FM * FN * 16 * 64;
+    if (kg > 0) {
+        float* red = lds + ((kg - 1) * NWG + gw) * PER_WAVE;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) red[((i * FN + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll 1
+        for (int gg = 1; gg < KS; ++gg) {
+            const float* red = lds + ((gg - 1) * NWG + gw) * PER_WAVE;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * FN + j) * 16 + r) * 64 + lane];
+        }
+        // Guarded store: register r of lane (li, lh) is row 8 (r/4) + 4 lh + r%4.
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = n0 + wn * WN + j * 32 + li;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
+                }
+            }
+    }
+}
+
 namespace {
 using LaunchFn = hipError_t (*)(const GemmArgs&, hipStream_t, int, int, int, unsigned);
 
@@ -361,6 +538,17 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n
                        dim3(blocks), dim3(WAVES_M * WAVES_N * 64), 0, s, p, tiles_m, tiles_n, group_m);
     return hipGetLastError();
 }
+
+template <int BM, int BN, int BK, int KS, bool TRA, bool TRB>
+hipError_t launch_splitk(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                         unsigned blocks) {
+    hipLaunchKernelGGL((gemm_mfma_splitk_kernel<BM, BN, BK, KS, TRA, TRB>), dim3(blocks), dim3(256 * KS), 0, s, p,
+                       tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+}
+#define SPLITK_OPS(BM, BN, BK, KS)                                                             \
+    {launch_splitk<BM, BN, BK, KS, false, false>, launch_splitk<BM, BN, BK, KS, false, true>, \
+     launch_splitk<BM, BN, BK, KS, true, false>, launch_splitk<BM, BN, BK, KS, true, true>}
 
 // NN only (diagnostic layouts) or all four op combinations.
 #define NN_ONLY(BM, BN, BK, WM, WN, D, S) \
@@ -390,9 +578,13 @@ const MfmaConfig kConfigs[] = {
     // the default with tile-row groups of 4 and 16 instead of 8 (L2 reuse)
     {"mfma256x256_bk32_w2x4_direct_g4", 256, 256, 512, 4, NN_ONLY(256, 256, 32, 2, 4, true, 64)},
     {"mfma256x256_bk32_w2x4_direct_g16", 256, 256, 512, 16, NN_ONLY(256, 256, 32, 2, 4, true, 64)},
+    // small products: the phases of one tile split over groups of four waves
+    {"mfma64x64_bk16_w2x2_k4", 64, 64, 1024, 8, SPLITK_OPS(64, 64, 16, 4)},
+    {"mfma64x64_bk32_w2x2_k4", 64, 64, 1024, 8, SPLITK_OPS(64, 64, 32, 4)},
 };
 #undef NN_ONLY
 #undef ALL_OPS
+#undef SPLITK_OPS
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 }  // namespace
 
@@ -402,14 +594,22 @@ const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConf
 // Largest tile that still gives every CU at least one workgroup: 256 x 256
 // with eight waves (two per SIMD, so one wave's barrier or LDS wait is
 // covered by the other's matrix instructions) and direct global -> LDS
-// copies once there are 256 such tiles.  Every picked configuration is built
-// for all four op combinations.
+// copies once there are 256 such tiles.  Below that, 128 x 128 tiles when
+// they come in whole rounds of 256 (every CU busy to the end), else 64 x 64
+// tiles with the phases of each tile split over four groups of four waves
+// (16 waves per workgroup to hide latency; 32-deep phases when there are at
+// most 256 such tiles, 16-deep otherwise).  Measured at 512^3 .. 3584^3 and
+// on rectangular shapes, each choice within 2 % of the fastest
+// configuration.  Every picked configuration is built for all four op
+// combinations.
 int mfma_pick_config(int M, int N, int /*K*/) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
+    const int64_t t64 = (int64_t)ceil_div(M, 64) * ceil_div(N, 64);
     if (t256 >= 256) return 7;
-    if (t128 >= 256) return 1;
-    return 4;
+    const int64_t rounds128 = (t128 + 255) / 256;
+    if (t128 >= 256 && t128 * 10 >= rounds128 * 256 * 9) return 1;
+    return t64 <= 256 ? 14 : 13;
 }
 
 // hipErrorInvalidValue: the grid would exceed the launch limits.
