@@ -72,9 +72,10 @@ def transposed_copy(t: torch.Tensor) -> torch.Tensor:
     return t.t().contiguous()
 
 
-# One shape per tile configuration the default path picks (64x64, 128x128,
-# 256x256 direct copies), plus ragged edges and a ghost k phase for the last.
-SAME_BITS_SHAPES = [(300, 200, 130), (2100, 2050, 300), (4096, 4096, 512), (4100, 4097, 515)]
+# One shape per tile configuration the default path picks (64x64 split over
+# four wave groups with 32- and 16-deep phases, 128x128, 256x256 direct
+# copies), plus ragged edges and a ghost k phase for the last.
+SAME_BITS_SHAPES = [(300, 200, 130), (2100, 2050, 300), (2048, 2048, 96), (4096, 4096, 512), (4100, 4097, 515)]
 
 
 @pytest.mark.parametrize("shape", SAME_BITS_SHAPES, ids=lambda s: "x".join(map(str, s)))
