@@ -18,22 +18,27 @@
 // k = 16 s + 8 h + 0..7: each lane's operand of either factor is then eight
 // consecutive k of one row, one 128-bit LDS read.
 //
-// LDS layout: both tiles k-contiguous, one 128-byte row of BK = 64 values per
-// output row (A) or column (B).  The 16-byte chunk c of row r sits at chunk
+// LDS layouts.  k-contiguous tiles: one 128-byte row of BK = 64 values per
+// output row (A) or column (B), the 16-byte chunk c of row r at chunk
 // position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 4)) & 7 (the first page's XOR
-// swizzle, on 16-byte chunks).  Fragment reads: 16 lanes per LDS cycle read
-// rows R .. R+15 at one chunk; a row pair spans the 64 banks and f gives the
-// eight row pairs eight different chunk positions.  B stores (below): 8 lanes
-// per cycle write rows 4l + j, l = 0..7, at one chunk; f gives those eight
-// rows eight different positions as well.
+// swizzle, on 16-byte chunks); a fragment is one 128-bit read, 16 lanes per
+// LDS cycle reading rows R .. R+15 at one chunk (a row pair spans the 64
+// banks and f gives the eight row pairs eight different positions).
+// mn-contiguous tiles (a factor copied as stored with n, or m, along its
+// rows): 64 k rows of the tile's columns, chunk c of row r at c ^ 4 (r % 4),
+// read transposed with ds_read_b64_tr_b16 (see read_tr16).
 //
-// A (M x K, k-contiguous in memory) is copied as stored: straight from global
-// memory into LDS (global_load_lds_dwordx4, each wave instruction fills 1 KB,
-// 8 rows) in interior phases of the large tiles, else with 128-bit loads
-// through registers.  B (K x N, n-contiguous in memory) has to become
-// k-contiguous: each thread loads a block of 8 k rows x 4 n (eight 64-bit
-// loads; the lanes of a wave cover consecutive n of one k row), transposes it
-// in registers and writes four 128-bit LDS rows of 8 k values.
+// Kernels.  gemm16_kernel: A (M x K, k-contiguous in memory) is copied as
+// stored, straight from global memory into LDS in interior phases of the
+// large tiles (global_load_lds_dwordx4, each wave instruction fills 1 KB),
+// else with 128-bit loads through registers; B (K x N) is either copied as
+// stored into an mn-contiguous tile (the direct-copy configurations) or
+// transposed through registers into k-contiguous rows (each thread loads a
+// block of 8 k rows x 8 or 4 n and writes 128-bit LDS rows of 8 k values; 8
+// lanes per store cycle write rows 4l + j, which f spreads over eight
+// positions).  gemm16_sched_kernel: full 256 x 256 tiles on four waves with
+// an explicit instruction order, the default for large problems.
+// gemm16_op_kernel: either factor stored transposed.
 //
 // Vector loads need 4-byte alignment (gfx9 runs global memory in unaligned
 // mode; a dword-aligned multi-dword load is legal): operands whose base is
