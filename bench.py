@@ -262,10 +262,7 @@ def bench_mixed(args, w) -> int:
         return 0
     wall, ms = _timed(make(args.variant), args.steps, args.warmup)
     achieved = flop / (ms * 1e-3) / 1e12
-    # the kernel gemm_mixed picks: 256 x 256 tiles once there are 256 of them
-    tiles256 = -(-w.M // 256) * -(-w.N // 256)
-    tiles128 = -(-w.M // 128) * -(-w.N // 128)
-    picked = 8 if tiles256 >= 256 else 7 if tiles128 >= 256 else 3
+    picked = binding.gemm_mixed_default_variant(w.M, w.N, w.K)     # the configuration gemm_mixed runs
     config = {"workload": f"{w.name} rounded to {fmt}", "M": w.M, "N": w.N, "K": w.K, "lda": lda,
               "ldb": ldb, "ldc": w.ldc, "view_offset_elements": w.offset, "values": w.dist,
               "format": fmt, "result": "f32", "op": args.op,
@@ -431,6 +428,7 @@ def bench_all_workloads(args) -> int:
         med, best = statistics.median(ms), min(ms)
         line = {"workload": name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb,
                 "ldc": w.ldc, "view_offset_floats": w.offset, "values": w.dist,
+                "kernel": binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(w.M, w.N, w.K)),
                 "launches": launches, "median_ms": round(med, 5), "best_ms": round(best, 5),
                 "tflops_median": round(flop / med / 1e9, 3), "tflops_best": round(flop / best / 1e9, 3),
                 "percent_of_peak_median": round(100 * flop / med / 1e9 / PEAK_FP32_TFLOPS, 2)}
@@ -561,7 +559,8 @@ def main(argv=None) -> int:
     wall, ms_event = timed(args.variant, args.steps, args.warmup)
     value = flop * args.steps / wall / 1e12
     achieved = flop / (ms_event * 1e-3) / 1e12
-    kernel_name = binding.gemm_f32_variant_name(3 if args.variant is None else args.variant)
+    kernel_name = binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(w.M, w.N, w.K)
+                                                if args.variant is None else args.variant)
     line = {
         "metric": "fp32 GEMM TFLOP/s and % of MI355X fp32 peak at N=4096/8192",
         "value": round(value, 3),

@@ -149,6 +149,12 @@ const char *gemm_f32_variant_name(int variant);
 /* Number of diagnostic variants (numbered from 16). */
 int gemm_f32_num_diagnostic_variants(void);
 
+/* The diagnostic variant whose configuration gemm_f32 and gemm_f32_op run
+ * for an M x N x K product (the choice depends on M and N only), or -1 for
+ * sizes that are negative or above INT_MAX.  Launches nothing, needs no
+ * device; for callers that want to know which kernel a call will use. */
+int gemm_f32_default_variant(int64_t M, int64_t N, int64_t K);
+
 /* Static, NUL-terminated description of a status code. */
 const char *gemm_f32_status_string(int status);
 
@@ -260,6 +266,11 @@ int gemm_mixed_variant(int variant, int format, int64_t M, int64_t N, int64_t K,
                        float *C, int64_t ldc, void *stream);
 int gemm_mixed_num_variants(void);
 const char *gemm_mixed_variant_name(int variant);   /* NULL if unknown */
+/* The configuration gemm_mixed runs for an M x N x K product (depends on M
+ * and N only; the scheduled configuration hands problems it does not take to
+ * its 8-wave fallback, as described above), or -1 for sizes that are negative
+ * or above INT_MAX.  Launches nothing, needs no device. */
+int gemm_mixed_default_variant(int64_t M, int64_t N, int64_t K);
 
 /* C (binary32) = op(A) x op(B) for 16-bit factors, either one stored
  * transposed: the backward-pass products X^T dY and dY W^T of the same

@@ -66,6 +66,8 @@ def load_library():
         lib.gemm_f32_variant_name.restype = ctypes.c_char_p
         lib.gemm_f32_status_string.argtypes = [ctypes.c_int]
         lib.gemm_f32_status_string.restype = ctypes.c_char_p
+        lib.gemm_f32_default_variant.argtypes = [_i64, _i64, _i64]
+        lib.gemm_f32_default_variant.restype = ctypes.c_int
         tsig = [_i64, _i64, _vp, _i64, _vp, _i64, _vp]
         lib.transpose_f32.argtypes = tsig
         lib.transpose_f32.restype = ctypes.c_int
@@ -95,6 +97,8 @@ def load_library():
         lib.gemm_mixed_op.restype = ctypes.c_int
         lib.gemm_mixed_num_variants.argtypes = []
         lib.gemm_mixed_num_variants.restype = ctypes.c_int
+        lib.gemm_mixed_default_variant.argtypes = [_i64, _i64, _i64]
+        lib.gemm_mixed_default_variant.restype = ctypes.c_int
         lib.gemm_mixed_variant_name.argtypes = [ctypes.c_int]
         lib.gemm_mixed_variant_name.restype = ctypes.c_char_p
         _lib = lib
@@ -154,6 +158,12 @@ def gemm_f32_num_variants() -> int:
 
 def gemm_f32_num_diagnostic_variants() -> int:
     return load_library().gemm_f32_num_diagnostic_variants()
+
+
+def gemm_f32_default_variant(M, N, K) -> int:
+    """The diagnostic variant whose configuration gemm_f32 runs for M x N x K
+    (-1 for invalid sizes); no device needed."""
+    return int(load_library().gemm_f32_default_variant(M, N, K))
 
 
 def gemm_f32_variant_name(variant: int) -> str | None:
@@ -318,6 +328,12 @@ def gemm_mixed_op(op_a, op_b, fmt, M, N, K, A, lda, B, ldb, C, ldc, stream=None)
 
 def gemm_mixed_num_variants() -> int:
     return load_library().gemm_mixed_num_variants()
+
+
+def gemm_mixed_default_variant(M, N, K) -> int:
+    """The configuration gemm_mixed runs for M x N x K (-1 for invalid
+    sizes); no device needed."""
+    return int(load_library().gemm_mixed_default_variant(M, N, K))
 
 
 def gemm_mixed_variant_name(variant: int) -> str | None:

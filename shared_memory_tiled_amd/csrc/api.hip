@@ -147,6 +147,14 @@ extern "C" const char* gemm_f32_variant_name(int variant) {
     return nullptr;
 }
 
+extern "C" int gemm_f32_default_variant(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return -1;
+    const int config = mfma_pick_config((int)M, (int)N, (int)K);
+    for (int d = 0; d < kNumDiagnostics; ++d)
+        if (kDiagnostics[d].rung == 3 && kDiagnostics[d].config == config) return kDiagBase + d;
+    return -1;
+}
+
 extern "C" const char* gemm_f32_status_string(int status) {
     switch (status) {
         case GEMM_F32_OK: return "ok";
@@ -331,3 +339,8 @@ extern "C" int gemm_mixed_variant(int variant, int format, int64_t M, int64_t N,
 extern "C" int gemm_mixed_num_variants(void) { return mixed_num_configs(); }
 
 extern "C" const char* gemm_mixed_variant_name(int variant) { return mixed_config_name(variant); }
+
+extern "C" int gemm_mixed_default_variant(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return -1;
+    return mixed_pick_config((int)M, (int)N, (int)K);
+}

@@ -258,3 +258,38 @@ def test_mixed_variants(binding, lib):
 ])
 def test_mixed_op_validation_without_launch(lib, op_a, op_b, args, code):
     assert lib.gemm_mixed_op(op_a, op_b, *args, None) == declared_codes()[code]
+
+
+def test_default_variant_choices(binding):
+    """The configuration the default entry points run, by problem size (no
+    device needed): 256 x 256 tiles once there are 256 of them, 128 x 128
+    tiles when they fill whole rounds of 256 blocks, else 64 x 64 tiles whose
+    phases are split over four wave groups (32-deep phases for at most 256
+    tiles); for the 16-bit product the scheduled kernel, 128 x 128 direct
+    copies or 64 x 64 tiles.  Invalid sizes give -1."""
+    f32 = {
+        (8192, 8192, 8192): "mfma256x256_bk32_w2x4_direct",
+        (4096, 4096, 4096): "mfma256x256_bk32_w2x4_direct",
+        (8192, 4096, 2048): "mfma256x256_bk32_w2x4_direct",
+        (2048, 2048, 2048): "mfma128x128_bk16_w2x2",
+        (4096, 2048, 1024): "mfma128x128_bk16_w2x2",
+        (2560, 2560, 2560): "mfma64x64_bk16_w2x2_k4",
+        (3000, 3000, 3000): "mfma64x64_bk16_w2x2_k4",
+        (1000, 1000, 1000): "mfma64x64_bk32_w2x2_k4",
+        (256, 256, 256): "mfma64x64_bk32_w2x2_k4",
+        (1, 1, 1): "mfma64x64_bk32_w2x2_k4",
+    }
+    for (M, N, K), name in f32.items():
+        v = binding.gemm_f32_default_variant(M, N, K)
+        assert binding.gemm_f32_variant_name(v) == name, (M, N, K, v)
+    mixed = {
+        (8192, 8192, 8192): "mixed256x256_bk64_w4_sched",
+        (4096, 4096, 64): "mixed256x256_bk64_w4_sched",
+        (2048, 2048, 2048): "mixed128x128_bk64_w2x2_directAB",
+        (1000, 1000, 1000): "mixed64x64_bk64_w1x2",
+    }
+    for (M, N, K), name in mixed.items():
+        assert binding.gemm_mixed_variant_name(binding.gemm_mixed_default_variant(M, N, K)) == name, (M, N, K)
+    for bad in ((-1, 5, 5), (5, -1, 5), (5, 5, -1), (1 << 31, 5, 5)):
+        assert binding.gemm_f32_default_variant(*bad) == -1
+        assert binding.gemm_mixed_default_variant(*bad) == -1
