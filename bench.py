@@ -290,15 +290,6 @@ def bench_mixed(args, w) -> int:
     return 0
 
 
-def transpose_auto_variant(w) -> int:
-    """The variant transpose_f32 picks for the workload's A matrix (for the
-    label only): diagonal tile order, with nontemporal accesses for inputs of
-    256 MiB or more whose leading dimension is a multiple of 4 KB."""
-    pow2 = (4 * w.lda) % 4096 == 0 or (4 * w.M) % 4096 == 0
-    big = 4 * w.M * w.K >= 256 << 20
-    return 7 if (pow2 and big) else 6
-
-
 def bench_transpose(args, w) -> int:
     """transpose_f32 of the workload's A matrix (M x K, leading dimension lda)
     into an M-column output; bytes moved = 2 x 4 M K per launch."""
@@ -345,7 +336,8 @@ def bench_transpose(args, w) -> int:
         "data": "synthetic",
         "config": {"workload": f"{w.name} A matrix", "rows": w.M, "cols": w.K, "ld_in": w.lda,
                    "ld_out": w.M, "view_offset_floats": w.offset,
-                   "kernel": ("auto: " + binding.transpose_f32_variant_name(transpose_auto_variant(w)))
+                   "kernel": ("auto: " + binding.transpose_f32_variant_name(
+                       binding.transpose_f32_default_variant(w.M, w.K, w.lda, w.M)))
                    if variant is None else binding.transpose_f32_variant_name(variant),
                    "device_copy_same_bytes_GB_per_s": round(2.0 * 4 * w.M * w.lda / (copy_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

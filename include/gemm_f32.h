@@ -176,11 +176,14 @@ const char *gemm_f32_status_string(int status);
  * padded tile, 3 XOR-swizzled [32][32] tile, 4 64 x 64 tile with 128-bit
  * global and LDS accesses and an LDS layout conflict free on gfx950, 5 the
  * same with 128 x 128 tiles, 6 variant 4 with tiles handed out in diagonal
- * order, 7 and 8 variants 6 and 4 with nontemporal global loads and stores.
- * transpose_f32 uses 6 (with leading dimensions near a multiple of 4 KB,
- * tiles handed out row by row crowd the same memory channels), and 7 for
- * inputs of 256 MiB or more (larger than the last-level cache) whose leading
- * dimension is a multiple of 4 KB.
+ * order, 7 and 8 variants 6 and 4 with nontemporal global loads and stores,
+ * 9 and 10 variant 6 and its 128 x 128 form with nontemporal stores only.
+ * transpose_f32 uses 9 when the 64 x 64 tile grid is square or the input
+ * holds 128 MiB or more, else 6 (diagonal order: with leading dimensions
+ * near a multiple of 4 KB, tiles handed out row by row crowd the same memory
+ * channels; nontemporal stores keep the caches for the input);
+ * transpose_f32_default_variant names that choice (-1 for negative sizes or
+ * sizes above INT_MAX), launching nothing.
  */
 int transpose_f32(int64_t rows, int64_t cols, const float *in, int64_t ld_in,
                   float *out, int64_t ld_out, void *stream);
@@ -188,6 +191,7 @@ int transpose_f32_variant(int variant, int64_t rows, int64_t cols, const float *
                           int64_t ld_in, float *out, int64_t ld_out, void *stream);
 int transpose_f32_num_variants(void);
 const char *transpose_f32_variant_name(int variant);   /* NULL if unknown */
+int transpose_f32_default_variant(int64_t rows, int64_t cols, int64_t ld_in, int64_t ld_out);
 
 /* Sum reduction: *out = x[0] + ... + x[n-1], binary32.
  *

@@ -16,7 +16,7 @@ _BINDING_NAMES = {
     "reduce_sum_f32", "reduce_sum_f32_variant", "reduce_sum_f32_num_variants",
     "reduce_sum_f32_variant_name", "reduce_sum_f32_workspace_size", "reduce_sum",
     "gemm_mixed", "gemm_mixed_variant", "gemm_mixed_op", "gemm_mixed_num_variants", "gemm_mixed_variant_name",
-    "gemm_f32_default_variant", "gemm_mixed_default_variant",
+    "gemm_f32_default_variant", "gemm_mixed_default_variant", "transpose_f32_default_variant",
     "gemm16", "FORMATS",
     "VARIANTS", "load_library", "library_path",
 }

@@ -77,6 +77,8 @@ def load_library():
         lib.transpose_f32_num_variants.restype = ctypes.c_int
         lib.transpose_f32_variant_name.argtypes = [ctypes.c_int]
         lib.transpose_f32_variant_name.restype = ctypes.c_char_p
+        lib.transpose_f32_default_variant.argtypes = [_i64, _i64, _i64, _i64]
+        lib.transpose_f32_default_variant.restype = ctypes.c_int
         lib.reduce_sum_f32_workspace_size.argtypes = [ctypes.c_int, _i64]
         lib.reduce_sum_f32_workspace_size.restype = _i64
         rsig = [_i64, _vp, _vp, _vp, _i64, _vp]
@@ -224,6 +226,11 @@ def transpose_f32_variant(variant, rows, cols, src, ld_in, dst, ld_out, stream=N
 
 def transpose_f32_num_variants() -> int:
     return load_library().transpose_f32_num_variants()
+
+
+def transpose_f32_default_variant(rows, cols, ld_in, ld_out) -> int:
+    """The variant transpose_f32 runs for these sizes (-1 for invalid ones)."""
+    return int(load_library().transpose_f32_default_variant(rows, cols, ld_in, ld_out))
 
 
 def transpose_f32_variant_name(variant: int) -> str | None:

@@ -84,8 +84,9 @@ __device__ __forceinline__ int tvec_word(int c, int chunk) {
 typedef float floatx4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // T x T tile (T = 64 or 128), 256 threads; each thread transposes
-// (T/4)^2 / 256 blocks of 4 x 4.  NT: nontemporal global accesses.
-template <int T, bool DIAGONAL, bool NT>
+// (T/4)^2 / 256 blocks of 4 x 4.  NT: nontemporal global loads and stores;
+// NTS: nontemporal stores only (the loads keep the input cacheable).
+template <int T, bool DIAGONAL, bool NT, bool NTS = NT>
 __global__ __launch_bounds__(256) void transpose_tile_vec_kernel(int rows, int cols, const float* in,
                                                                  int64_t ld_in, float* out,
                                                                  int64_t ld_out, int tiles_c) {
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256) void transpose_tile_vec_kernel(int rows, int c
         const int c = q / NB, k = q % NB;
         const floatx4 w = *reinterpret_cast<const floatx4*>(&tile[tvec_word<T>(c, k)]);
         float* dst = out + (int64_t)(c0 + c) * ld_out + r0 + 4 * k;
-        if (inside && NT) __builtin_nontemporal_store(floatx4_a4(w), reinterpret_cast<floatx4_a4*>(dst));
+        if (inside && NTS) __builtin_nontemporal_store(floatx4_a4(w), reinterpret_cast<floatx4_a4*>(dst));
         else if (inside) __builtin_memcpy(dst, &w, 16);
         else store4_guarded(out, c0 + c, cols, r0 + 4 * k, rows, ld_out, w);
     }
@@ -144,18 +145,19 @@ __global__ __launch_bounds__(256) void transpose_tile_vec_kernel(int rows, int c
 
 }  // namespace
 
-int transpose_num_variants() { return 9; }
+int transpose_num_variants() { return 11; }
 
 const char* transpose_variant_name(int v) {
     static const char* const names[] = {"naive",           "tile32",         "tile32_pad",
                                         "tile32_swizzle",  "tile64_vec",     "tile128_vec",
-                                        "tile64_vec_diag", "tile64_vec_diag_nt", "tile64_vec_nt"};
-    return (v >= 0 && v < 9) ? names[v] : nullptr;
+                                        "tile64_vec_diag", "tile64_vec_diag_nt", "tile64_vec_nt",
+                                        "tile64_vec_diag_ntstore", "tile128_vec_diag_ntstore"};
+    return (v >= 0 && v < 11) ? names[v] : nullptr;
 }
 
 hipError_t launch_transpose(int variant, int rows, int cols, const float* in, int64_t ld_in,
                             float* out, int64_t ld_out, hipStream_t s) {
-    const int tile = (variant >= 1 && variant <= 3) ? 32 : (variant == 5 ? 128 : 64);
+    const int tile = (variant >= 1 && variant <= 3) ? 32 : ((variant == 5 || variant == 10) ? 128 : 64);
     const int tiles_c = ceil_div(cols, tile);
     const int64_t blocks = (int64_t)tiles_c * ceil_div(rows, tile);
     const int64_t threads = (variant >= 1 && variant <= 3) ? 1024 : 256;
@@ -192,6 +194,14 @@ hipError_t launch_transpose(int variant, int rows, int cols, const float* in, in
             break;
         case 8:
             hipLaunchKernelGGL((transpose_tile_vec_kernel<64, false, true>), grid, dim3(256), 0, s, rows,
+                               cols, in, ld_in, out, ld_out, tiles_c);
+            break;
+        case 9:
+            hipLaunchKernelGGL((transpose_tile_vec_kernel<64, true, false, true>), grid, dim3(256), 0, s, rows,
+                               cols, in, ld_in, out, ld_out, tiles_c);
+            break;
+        case 10:
+            hipLaunchKernelGGL((transpose_tile_vec_kernel<128, true, false, true>), grid, dim3(256), 0, s, rows,
                                cols, in, ld_in, out, ld_out, tiles_c);
             break;
         default:

@@ -172,7 +172,7 @@ def test_transpose_validation_without_launch(lib, args, code):
 def test_transpose_variants(binding, lib):
     n = binding.transpose_f32_num_variants()
     names = [binding.transpose_f32_variant_name(v) for v in range(n)]
-    assert n == 9 and all(names) and len(set(names)) == n
+    assert n == 11 and all(names) and len(set(names)) == n
     assert binding.transpose_f32_variant_name(n) is None
     code = declared_codes()["GEMM_F32_ERR_INVALID_VARIANT"]
     assert lib.transpose_f32_variant(n, 4, 4, FAKE, 4, FAKE, 4, None) == code
@@ -293,3 +293,15 @@ def test_default_variant_choices(binding):
     for bad in ((-1, 5, 5), (5, -1, 5), (5, 5, -1), (1 << 31, 5, 5)):
         assert binding.gemm_f32_default_variant(*bad) == -1
         assert binding.gemm_mixed_default_variant(*bad) == -1
+
+
+def test_transpose_default_variant(binding):
+    """transpose_f32's choice: nontemporal stores (9) for a square 64 x 64 tile
+    grid or an input of 128 MiB or more, else cached stores (6)."""
+    name = lambda r, c, li, lo: binding.transpose_f32_variant_name(binding.transpose_f32_default_variant(r, c, li, lo))
+    assert name(8192, 8192, 8192, 8192) == "tile64_vec_diag_ntstore"
+    assert name(4096, 4096, 4096, 4096) == "tile64_vec_diag_ntstore"
+    assert name(12000, 6000, 6000, 12000) == "tile64_vec_diag_ntstore"
+    assert name(8192, 2048, 2056, 8192) == "tile64_vec_diag"
+    assert name(300, 200, 200, 300) == "tile64_vec_diag"
+    assert binding.transpose_f32_default_variant(-1, 5, 5, 5) == -1
