@@ -52,7 +52,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_16BIT_TFLOPS = 2500.0      # MI355X published dense bf16 / fp16 matrix peak
 DEFAULT_WORKLOAD = "square8192"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mfma_square8192_hbm_traffic.txt")
-KERNEL_SOURCES = ["shared_memory_tiled_amd/csrc/mfma.hip",
+KERNEL_SOURCES = ["shared_memory_tiled_amd/csrc/mfma_sched.hip",
                   "shared_memory_tiled_amd/csrc/gemm_internal.h"]
 
 

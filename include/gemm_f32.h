@@ -81,9 +81,11 @@ extern "C" {
  *      outputs per thread in registers, two LDS buffers and one barrier per
  *      phase, next tile prefetched into registers during the current phase
  *   3  MFMA: v_mfma_f32_32x32x2_f32 matrix-core contraction on double-
- *      buffered LDS tiles; large problems use 256 x 256 tiles, eight waves
- *      and direct global-to-LDS copies into an XOR-swizzled layout (the
- *      default)
+ *      buffered LDS tiles (the default).  Large problems use 256 x 256 tiles
+ *      with direct global-to-LDS copies into an XOR-swizzled layout: on four
+ *      waves with a fixed instruction order when M and N are multiples of
+ *      256 and K of 32 (and each stored factor is under 2 GiB), else on
+ *      eight waves; both give the same bits
  * Variants numbered from 16 up are diagnostic layouts of the same rungs, kept
  * so that their hardware counters can be compared; see
  * gemm_f32_variant_name().
@@ -150,9 +152,11 @@ const char *gemm_f32_variant_name(int variant);
 int gemm_f32_num_diagnostic_variants(void);
 
 /* The diagnostic variant whose configuration gemm_f32 and gemm_f32_op run
- * for an M x N x K product (the choice depends on M and N only), or -1 for
- * sizes that are negative or above INT_MAX.  Launches nothing, needs no
- * device; for callers that want to know which kernel a call will use. */
+ * for an M x N x K product (the choice depends on the sizes only; the
+ * four-wave configuration hands a stored factor of 2 GiB or more to the
+ * eight-wave kernel), or -1 for sizes that are
+ * negative or above INT_MAX.  Launches nothing, needs no device; for callers
+ * that want to know which kernel a call will use. */
 int gemm_f32_default_variant(int64_t M, int64_t N, int64_t K);
 
 /* Static, NUL-terminated description of a status code. */

@@ -40,6 +40,9 @@ const Diagnostic kDiagnostics[] = {
     {"mfma256x256_bk32_w2x4_direct_g16", 3, 12},
     {"mfma64x64_bk16_w2x2_k4", 3, 13},
     {"mfma64x64_bk32_w2x2_k4", 3, 14},
+    {"mfma256x256_bk32_w2x4_direct_mi16", 3, 15},
+    {"mfma256x256_bk32_w2x2_sched", 3, 16},
+    {"mfma256x256_bk32_w2x2_sched_g4", 3, 17},
 };
 constexpr int kNumDiagnostics = (int)(sizeof(kDiagnostics) / sizeof(kDiagnostics[0]));
 

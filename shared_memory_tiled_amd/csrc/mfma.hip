@@ -56,6 +56,8 @@
 // share A row panels and B column panels in that XCD's L2.
 #include "launch.h"
 
+#include <type_traits>
+
 namespace gemmf32 {
 
 namespace {
@@ -75,10 +77,13 @@ struct Factor {
 };
 
 // One factor's tile: MNT x BK values of op(X) per stage, copied by NT
-// threads (NW waves).  KC: the factor is stored k-contiguous.
-template <int MNT, int BK, bool KC, bool DIRECT, int SWZ_BANKS, int NT, int NW>
+// threads (NW waves).  KC: the factor is stored k-contiguous.  MC_PAD: the
+// pad of an mn-contiguous row (8 words when two lane groups read rows 4
+// apart, 4 words when four lane groups do: their 16-word runs then start 16
+// banks apart).
+template <int MNT, int BK, bool KC, bool DIRECT, int SWZ_BANKS, int NT, int NW, int MC_PAD = 8>
 struct OperandTile {
-    static constexpr int STRIDE = KC ? (DIRECT ? BK : BK + 4) : MNT + 8;
+    static constexpr int STRIDE = KC ? (DIRECT ? BK : BK + 4) : MNT + MC_PAD;
     static constexpr int WORDS = KC ? MNT * STRIDE : BK * STRIDE;    // per stage
     static constexpr int CPR = KC ? BK / 4 : MNT / 4;   // 16-byte chunks per stored row
     static constexpr int CHUNKS = MNT * BK / 4 / NT;    // copy chunks per thread
@@ -142,17 +147,29 @@ struct OperandTile {
 };
 }  // namespace
 
+// MI: the matrix instruction, v_mfma_f32_32x32x2_f32 (32) or
+// v_mfma_f32_16x16x4_f32 (16).  The 16x16 form does the same work per cycle
+// with a quarter of the accumulator block per instruction: lane l supplies
+// A[l % 16][l / 16] and B[l / 16][l % 16], and accumulator register r holds
+// D[4 (l / 16) + r][l % 16].  For each group of 16 k values the lane group
+// g = l / 16 feeds k = kg + 4g + s to the s-th of four instructions, so a
+// lane again reads four consecutive k values of one row.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool DIRECT, int SWZ_BANKS,
-          bool TRANS_A, bool TRANS_B>
+          bool TRANS_A, bool TRANS_B, int MI = 32>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
 void gemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int NT = NW * 64;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;     // wave tile
-    constexpr int FM = WM / 32, FN = WN / 32;               // 32x32 blocks per wave
-    static_assert(WM % 32 == 0 && WN % 32 == 0 && BK % 8 == 0, "tile shape");
-    using TA = OperandTile<BM, BK, !TRANS_A, DIRECT, SWZ_BANKS, NT, NW>;
-    using TB = OperandTile<BN, BK, TRANS_B, DIRECT, SWZ_BANKS, NT, NW>;
+    constexpr int FM = WM / MI, FN = WN / MI;               // MI x MI blocks per wave
+    constexpr int KG = MI == 32 ? 8 : 16;                   // k values per group of four instructions
+    constexpr int NACC = MI == 32 ? 16 : 4;                 // accumulator registers per block
+    using Acc = std::conditional_t<MI == 32, floatx16, floatx4>;
+    static_assert(MI == 32 || MI == 16, "matrix instruction");
+    static_assert(WM % MI == 0 && WN % MI == 0 && BK % KG == 0, "tile shape");
+    constexpr int MC_PAD = MI == 32 ? 8 : 4;
+    using TA = OperandTile<BM, BK, !TRANS_A, DIRECT, SWZ_BANKS, NT, NW, MC_PAD>;
+    using TB = OperandTile<BN, BK, TRANS_B, DIRECT, SWZ_BANKS, NT, NW, MC_PAD>;
     constexpr int STAGE = TA::WORDS + TB::WORDS;
     __shared__ __attribute__((aligned(16))) float lds[2 * STAGE];
 
@@ -160,7 +177,7 @@ void gemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     const int lane = tid & 63, wave = tid >> 6;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    const int li = lane & 31, lh = lane >> 5;
+    const int li = lane & (MI - 1), lh = lane / MI;       // row in block, lane group
 
     // tile of this block
     const int logical = xcd_contiguous((int)blockIdx.x, tiles_m * tiles_n);
@@ -272,13 +289,13 @@ void gemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         }
     };
 
-    floatx16 acc[FM][FN];
+    Acc acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < NACC; ++r) acc[i][j][r] = 0.0f;
 
     const int phases = ceil_div(p.K, BK);
     // A phase is copied directly into LDS when it lies wholly inside the
@@ -309,19 +326,23 @@ void gemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         const float* as = lds + cur * STAGE;
         const float* bs = as + TA::WORDS;
 #pragma unroll
-        for (int kg = 0; kg < BK; kg += 8) {
+        for (int kg = 0; kg < BK; kg += KG) {
             floatx4 a[FM], b[FN];
 #pragma unroll
-            for (int f = 0; f < FM; ++f) a[f] = TA::fragment(as, wm * WM + f * 32 + li, kg, lh);
+            for (int f = 0; f < FM; ++f) a[f] = TA::fragment(as, wm * WM + f * MI + li, kg, lh);
 #pragma unroll
-            for (int f = 0; f < FN; ++f) b[f] = TB::fragment(bs, wn * WN + f * 32 + li, kg, lh);
+            for (int f = 0; f < FN; ++f) b[f] = TB::fragment(bs, wn * WN + f * MI + li, kg, lh);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < FN; ++j) {
+                        if constexpr (MI == 32)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
+                    }
         }
         if (!DIRECT && more) store_tiles(cur ^ 1);
         // The direct copies write LDS behind the compiler's back: wait for
@@ -331,15 +352,17 @@ void gemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         if constexpr (DIRECT) asm volatile("" ::: "memory");
     }
 
-    // Guarded store: register r of lane (li, lh) is row 8 (r/4) + 4 lh + r%4.
+    // Guarded store: register r of lane (li, lh) is row 8 (r/4) + 4 lh + r%4
+    // of its 32x32 block, or row 4 lh + r of its 16x16 block.
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn * WN + j * 32 + li;
+            const int col = n0 + wn * WN + j * MI + li;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            for (int r = 0; r < NACC; ++r) {
+                const int row = m0 + wm * WM + i * MI +
+                                (MI == 32 ? 8 * (r >> 2) + 4 * lh + (r & 3) : 4 * lh + r);
                 if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
             }
         }
@@ -531,10 +554,11 @@ struct MfmaConfig {
     LaunchFn launch[4];          // by 2 op_a + op_b; null: op pair not built for this config
 };
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool DIRECT, int SWZ, bool TRA, bool TRB>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool DIRECT, int SWZ, bool TRA, bool TRB,
+          int MI = 32>
 hipError_t launch_one(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
                       unsigned blocks) {
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, WAVES_M, WAVES_N, DIRECT, SWZ, TRA, TRB>),
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, WAVES_M, WAVES_N, DIRECT, SWZ, TRA, TRB, MI>),
                        dim3(blocks), dim3(WAVES_M * WAVES_N * 64), 0, s, p, tiles_m, tiles_n, group_m);
     return hipGetLastError();
 }
@@ -550,6 +574,18 @@ hipError_t launch_splitk(const GemmArgs& p, hipStream_t s, int tiles_m, int tile
     {launch_splitk<BM, BN, BK, KS, false, false>, launch_splitk<BM, BN, BK, KS, false, true>, \
      launch_splitk<BM, BN, BK, KS, true, false>, launch_splitk<BM, BN, BK, KS, true, true>}
 
+// The four-wave scheduled kernel where it takes the problem, else the
+// eight-wave 256 x 256 direct-copy kernel.
+template <bool TRA, bool TRB>
+hipError_t launch_sched_or_direct(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                                  unsigned blocks) {
+    if (sched_f32_fits(p, TRA, TRB)) return launch_sched_f32(p, s, TRA, TRB, group_m);
+    return launch_one<256, 256, 32, 2, 4, true, 64, TRA, TRB>(p, s, tiles_m, tiles_n, 8, blocks);
+}
+#define SCHED_OPS                                                                      \
+    {launch_sched_or_direct<false, false>, launch_sched_or_direct<false, true>,          \
+     launch_sched_or_direct<true, false>, launch_sched_or_direct<true, true>}
+
 // NN only (diagnostic layouts) or all four op combinations.
 #define NN_ONLY(BM, BN, BK, WM, WN, D, S) \
     {launch_one<BM, BN, BK, WM, WN, D, S, false, false>, nullptr, nullptr, nullptr}
@@ -558,6 +594,11 @@ hipError_t launch_splitk(const GemmArgs& p, hipStream_t s, int tiles_m, int tile
      launch_one<BM, BN, BK, WM, WN, D, S, false, true>,      \
      launch_one<BM, BN, BK, WM, WN, D, S, true, false>,      \
      launch_one<BM, BN, BK, WM, WN, D, S, true, true>}
+#define ALL_OPS_MI16(BM, BN, BK, WM, WN, D, S)                   \
+    {launch_one<BM, BN, BK, WM, WN, D, S, false, false, 16>,     \
+     launch_one<BM, BN, BK, WM, WN, D, S, false, true, 16>,      \
+     launch_one<BM, BN, BK, WM, WN, D, S, true, false, 16>,      \
+     launch_one<BM, BN, BK, WM, WN, D, S, true, true, 16>}
 
 const MfmaConfig kConfigs[] = {
     // register-staged copies (global -> VGPR -> LDS), padded k-contiguous rows
@@ -581,9 +622,16 @@ const MfmaConfig kConfigs[] = {
     // small products: the phases of one tile split over groups of four waves
     {"mfma64x64_bk16_w2x2_k4", 64, 64, 1024, 8, SPLITK_OPS(64, 64, 16, 4)},
     {"mfma64x64_bk32_w2x2_k4", 64, 64, 1024, 8, SPLITK_OPS(64, 64, 32, 4)},
+    // the 256 x 256 direct-copy tile on v_mfma_f32_16x16x4_f32
+    {"mfma256x256_bk32_w2x4_direct_mi16", 256, 256, 512, 8, ALL_OPS_MI16(256, 256, 32, 2, 4, true, 64)},
+    // four waves of 128 x 128, instruction order fixed by the kernel
+    {"mfma256x256_bk32_w2x2_sched", 256, 256, 256, 8, SCHED_OPS},
+    {"mfma256x256_bk32_w2x2_sched_g4", 256, 256, 256, 4, SCHED_OPS},
 };
 #undef NN_ONLY
 #undef ALL_OPS
+#undef ALL_OPS_MI16
+#undef SCHED_OPS
 #undef SPLITK_OPS
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 }  // namespace
@@ -592,9 +640,12 @@ int mfma_num_configs() { return kNumConfigs; }
 const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConfigs[c].name : nullptr; }
 
 // Largest tile that still gives every CU at least one workgroup: 256 x 256
-// with eight waves (two per SIMD, so one wave's barrier or LDS wait is
-// covered by the other's matrix instructions) and direct global -> LDS
-// copies once there are 256 such tiles.  Below that, 128 x 128 tiles when
+// once there are 256 such tiles -- on four waves with a fixed instruction
+// order (mfma_sched.hip) when M and N are multiples of 256 and K of 32 (the
+// launcher falls back to the eight-wave kernel for stored factors of 2 GiB
+// or more), else on eight waves (two per SIMD, so one wave's
+// barrier or LDS wait is covered by the other's matrix instructions) with
+// direct global -> LDS copies and ghost phases at the edges.  Below that, 128 x 128 tiles when
 // they come in whole rounds of 256 (every CU busy to the end), else 64 x 64
 // tiles with the phases of each tile split over four groups of four waves
 // (16 waves per workgroup to hide latency; 32-deep phases when there are at
@@ -602,11 +653,11 @@ const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConf
 // on rectangular shapes, each choice within 2 % of the fastest
 // configuration.  Every picked configuration is built for all four op
 // combinations.
-int mfma_pick_config(int M, int N, int /*K*/) {
+int mfma_pick_config(int M, int N, int K) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
     const int64_t t64 = (int64_t)ceil_div(M, 64) * ceil_div(N, 64);
-    if (t256 >= 256) return 7;
+    if (t256 >= 256) return (M % 256 == 0 && N % 256 == 0 && K % 32 == 0 && K > 0) ? 16 : 7;
     const int64_t rounds128 = (t128 + 255) / 256;
     if (t128 >= 256 && t128 * 10 >= rounds128 * 256 * 9) return 1;
     return t64 <= 256 ? 14 : 13;

@@ -1,0 +1,350 @@
+// mfma_sched.hip -- rung 3 on four waves with an explicit instruction order.
+//
+// The tiled product of the pages' shared-memory chapter (PMPP chapter 5
+// notes, sections 5.4-5.5: per phase every thread of a block copies part of
+// an A and a B tile into shared memory, a barrier, the multiply-adds from the
+// tiles, a barrier) on full 256 x 256 output tiles, 32 k values per phase,
+// two LDS stages so the copies of the next phase overlap the math of the
+// current one.
+//
+// Four waves in 2 x 2, each owning a 128 x 128 block of C as 4 x 4 blocks of
+// 32 x 32 (v_mfma_f32_32x32x2_f32, 256 accumulator registers per lane).  A
+// wave tile of 128 x 128 reads 256 values of LDS per k for 32768 products,
+// against 192 for 16384 on the eight-wave 128 x 64 tiles of the other
+// kernels: a third less LDS traffic per flop.  With one wave per SIMD no
+// second wave covers a wait, so the kernel places every instruction itself:
+// a step is the 64 matrix instructions of 8 k values; while one step's
+// fragments feed the matrix core, the next step's are read from LDS (eight
+// 128-bit reads after the first eight instructions) and every eighth
+// instruction is followed by one 1 KB global -> LDS copy of the next phase.
+// Copies 0..7 of a phase are issued in the last step of the phase before the
+// previous one, after the barrier, and 8..15 in step 0 of the previous phase,
+// so every copy has three steps to land before the barrier that ends that
+// phase.
+//
+// LDS tiles (per stage, 32 KB each):
+//   k-contiguous factor (A as stored, B stored transposed): 256 rows of 32
+//     floats (128 bytes).  Chunk c (16 bytes) of row r sits at position
+//     c ^ ((r / 2) mod 8): the 16 rows one 128-bit read cycle touches (two
+//     per 64-bank sweep) land on 16 different 4-bank groups.  A copy fills 8
+//     rows.  Lane l of a wave reads row 32 f + l % 32, k = kg + 4 (l / 32)
+//     .. + 3 for block f: its four values of instruction s = 0..3.
+//   mn-contiguous factor (B as stored, A stored transposed): 32 k rows of
+//     256 floats (1 KB, one copy each), unpadded.  Lane l reads the 128-bit
+//     run of columns 4 (l % 32) .. + 3 of k row kg + 4 (l / 32) + s: one
+//     value for each of the wave's four blocks, so block f of this factor
+//     covers the columns 4 c + f (c = 0..31) of the wave's 128-wide span.
+//     Sixteen lanes of one read cycle cover 256 consecutive bytes: no bank
+//     conflict, and four reads per step instead of sixteen 32-bit ones.
+// A block's k order (instruction s of group kg takes k = kg + s and
+// kg + 4 + s) is that of the eight-wave kernels, so both give the same bits.
+#include "launch.h"
+
+#include <type_traits>
+#include <utility>
+
+namespace gemmf32 {
+
+namespace {
+
+constexpr int kSBK = 32;                 // k values per phase
+constexpr int kSTile = 256 * kSBK;       // floats per tile stage
+constexpr int kStageBytes = 4 * kSTile;  // 32 KB
+
+__host__ __device__ constexpr int sched_swz(int r) { return (r >> 1) & 7; }
+
+template <typename F, int... Q>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Q...>) {
+    (f(std::integral_constant<int, Q>{}), ...);
+}
+// f(std::integral_constant<int, q>{}) for q = 0 .. N - 1, in order, each q a
+// compile-time constant (so the arrays it indexes stay in registers).
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+    unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// 16 bytes of LDS at a byte address.
+__device__ __forceinline__ floatx4 lds_read128(uint32_t lds_byte_addr) {
+    typedef const __attribute__((address_space(3))) floatx4 lds_floatx4;
+    return *(lds_floatx4*)(uintptr_t)lds_byte_addr;
+}
+
+// Byte address inside LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Waits for all outstanding LDS reads; the fragments pass through the wait
+// as operands, so no use of them is scheduled before it (and the compiler
+// adds no wait of its own that would also cover reads issued later).
+__device__ __forceinline__ void wait_tied(floatx4 (&x)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : : "memory");
+}
+
+// One factor's tile.  KC: stored k-contiguous.
+template <bool KC>
+struct SchedTileF32 {
+    // First float, inside the tile stage, that copy j (0..7) of wave w fills.
+    __host__ __device__ static int copy_dst(int w, int j) {
+        return KC ? 8 * (w + 4 * j) * kSBK : (w + 4 * j) * 256;
+    }
+    // Byte offset of lane l's 16 bytes of copy j from the stored matrix's
+    // base at k = 0 (mn0: the tile's first row or column of op(X)).
+    __host__ __device__ static uint32_t copy_src(int w, int j, int lane, int mn0, int64_t ld) {
+        if constexpr (KC) {
+            const int row = 8 * (w + 4 * j) + lane / 8;
+            return 4u * (uint32_t)((mn0 + row) * ld + 4 * ((lane % 8) ^ sched_swz(row)));
+        } else {
+            const int row = w + 4 * j;
+            return 4u * (uint32_t)(row * ld + mn0 + 4 * lane);
+        }
+    }
+    // Byte offset of the phase at k0 from the phase at 0.
+    __host__ __device__ static int phase_bytes(int k0, int64_t ld) { return KC ? 4 * k0 : 4 * k0 * (int)ld; }
+    // LDS byte offset, inside stage 0 of this factor, of lane (li, lh)'s read
+    // i (0..3) of step s for the wave whose 128-wide span starts at mn:
+    //   KC: block i's row mn + 32 i + li, logical chunk 2 s + lh;
+    //   MC: k row 8 s + 4 lh + i, columns mn + 4 li .. + 3.
+    // Either way a per-lane base plus a compile-time part (4096 i for KC, as
+    // the swizzle of row mn + 32 i + li depends on li only; 8192 s + 1024 i
+    // for MC).
+    __host__ __device__ static uint32_t read_base(int mn, int s, int li, int lh) {
+        return KC ? 4u * (uint32_t)((mn + li) * kSBK + 4 * ((2 * s + lh) ^ sched_swz(li)))
+                  : 4u * (uint32_t)(4 * lh * 256 + mn + 4 * li);
+    }
+    __host__ __device__ static constexpr uint32_t read_imm(int s, int i) {
+        return KC ? 4096u * (uint32_t)i : 8192u * (uint32_t)s + 1024u * (uint32_t)i;
+    }
+};
+
+// Operand of block f for instruction e from a lane's four reads x: KC, value
+// e of read f; MC, value f of read e.
+template <bool KC>
+__device__ __forceinline__ float operand(const floatx4 (&x)[4], int f, int e) {
+    return KC ? x[f][e] : x[e][f];
+}
+
+template <bool KCA, bool KCB>
+__global__ __launch_bounds__(256)
+void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
+    constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
+    using TA = SchedTileF32<KCA>;
+    using TB = SchedTileF32<KCB>;
+    constexpr int A_COPIES = 8, NCOPY = 16, NREAD = 8;
+    // A stage 0, A stage 1, B stage 0, B stage 1.
+    __shared__ __attribute__((aligned(16))) float lds[4 * kSTile];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave_u / 2, wn = wave_u % 2;
+    const int li = lane & 31, lh = lane >> 5;
+
+    const int logical = xcd_contiguous((int)blockIdx.x, tiles_m * tiles_n);
+    const int group_size = group_m * tiles_n;
+    const int g = logical / group_size;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int in_g = logical - g * group_size;
+    const int m0 = (first_m + in_g % gm) * BM;
+    const int n0 = (in_g / gm) * BN;
+
+    // Copies 0..7 fill A's tile, 8..15 B's (byte offsets: the launcher keeps
+    // both stored matrices below 2^31 bytes).
+    uint32_t doff[NCOPY];
+#pragma unroll
+    for (int j = 0; j < A_COPIES; ++j) {
+        doff[j] = TA::copy_src(wave_u, j, lane, m0, p.lda);
+        doff[A_COPIES + j] = TB::copy_src(wave_u, j, lane, n0, p.ldb);
+    }
+    constexpr int kRawBufferWord3 = 0x00020000;
+    const int64_t a_rows = KCA ? p.M : p.K, b_rows = KCB ? p.N : p.K;
+    const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.A), (short)0, (int)(4 * a_rows * p.lda), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.B), (short)0, (int)(4 * b_rows * p.ldb), kRawBufferWord3);
+    auto copy = [&](int j, int k0, int buf) __attribute__((always_inline)) {
+        if (j < A_COPIES) {
+            const int soff = TA::phase_bytes(k0, p.lda);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_a, (__attribute__((address_space(3))) void*)(lds + buf * kSTile + TA::copy_dst(wave_u, j)), 16,
+                (int)doff[j], soff, 0, 0);
+        } else {
+            const int soff = TB::phase_bytes(k0, p.ldb);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_b,
+                (__attribute__((address_space(3))) void*)(lds + (2 + buf) * kSTile + TB::copy_dst(wave_u, j - A_COPIES)),
+                16, (int)doff[j], soff, 0, 0);
+        }
+    };
+
+    // Per-lane read bases (stage 0): KC needs one per step, MC one in all.
+    constexpr int SA = KCA ? 4 : 1, SB = KCB ? 4 : 1;
+    uint32_t abase[SA], bbase[SB];
+    const uint32_t lds0 = lds_addr(lds);
+#pragma unroll
+    for (int s = 0; s < SA; ++s) abase[s] = lds0 + TA::read_base(wm * WM, s, li, lh);
+#pragma unroll
+    for (int s = 0; s < SB; ++s) bbase[s] = lds0 + 2u * kStageBytes + TB::read_base(wn * WN, s, li, lh);
+
+    floatx4 a[2][4], b[2][4];
+    // Read i (0..7) of step s from stage buf into set t: A's four first.
+    auto read_op = [&](int buf, int s, int t, int i) __attribute__((always_inline)) {
+        const uint32_t soff = (uint32_t)buf * (uint32_t)kStageBytes;
+        if (i < 4) a[t][i] = lds_read128(abase[KCA ? s : 0] + soff + TA::read_imm(s, i));
+        else b[t][i - 4] = lds_read128(bbase[KCB ? s : 0] + soff + TB::read_imm(s, i - 4));
+    };
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // One step: the 64 matrix instructions on fragment set t (instruction q:
+    // e = q / 16, block (q / 4 % 4, q % 4)); after the q-th (q < 8), read q of
+    // step rs from stage rbuf into set t ^ 1 (if R) and, after every eighth,
+    // copy CB + q / 8 (while below CE) of the phase at k_copy into stage cbuf.
+    auto step = [&](int t, auto reads, int rbuf, int rs, auto cb, auto ce, int k_copy,
+                    int cbuf) __attribute__((always_inline)) {
+        constexpr bool R = decltype(reads)::value;
+        constexpr int CB = decltype(cb)::value, CE = decltype(ce)::value;
+        unroll<64>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            constexpr int e = q / 16, i = (q / 4) % 4, j = q % 4;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(operand<KCA>(a[t], i, e),
+                                                             operand<KCB>(b[t], j, e), acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (R && q < NREAD) {
+                read_op(rbuf, rs, t ^ 1, q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (q % 8 == 7 && CB + q / 8 < CE) {
+                copy(CB + q / 8, k_copy, cbuf);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    };
+    auto wait_set = [&](int t) __attribute__((always_inline)) {
+        wait_tied(a[t]);
+        wait_tied(b[t]);
+    };
+    // This wave's copies have landed; then the barrier makes every wave's
+    // copies visible and releases the stage that was read.
+    auto barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        asm volatile("" ::: "memory");
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    using c0 = std::integral_constant<int, 0>;
+    using c8 = std::integral_constant<int, 8>;
+    using c16 = std::integral_constant<int, 16>;
+    // Steps 0..2 of the phase on stage cur (step 0's fragments already read)
+    // and the wait for step 3's; copies 8..15 of the phase at k_copy into
+    // stage cbuf with step 0 if WC.
+    auto steps012 = [&](int cur, auto wc, int k_copy, int cbuf) __attribute__((always_inline)) {
+        constexpr bool WC = decltype(wc)::value;
+        wait_set(0);
+        if constexpr (WC) step(0, yes{}, cur, 1, c8{}, c16{}, k_copy, cbuf);
+        else step(0, yes{}, cur, 1, c0{}, c0{}, 0, 0);
+        wait_set(1);
+        step(1, yes{}, cur, 2, c0{}, c0{}, 0, 0);
+        wait_set(0);
+        step(0, yes{}, cur, 3, c0{}, c0{}, 0, 0);
+        wait_set(1);
+    };
+
+    // Stage ph & 1 holds phase ph.  Between the barriers that end phases
+    // ph - 1 and ph run the deferred last step of phase ph - 1 (with copies
+    // 0..7 of phase ph + 1 and the first reads of phase ph) and steps 0..2 of
+    // phase ph (copies 8..15 with step 0).
+    const int P = p.K / kSBK;
+#pragma unroll
+    for (int j = 0; j < NCOPY; ++j) copy(j, 0, 0);
+    barrier();
+#pragma unroll
+    for (int i = 0; i < NREAD; ++i) read_op(0, 0, 0, i);
+    if (P > 1) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) copy(j, kSBK, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int ph = 0;
+    for (; ph + 2 < P; ++ph) {
+        const int cur = ph & 1;
+        steps012(cur, yes{}, (ph + 1) * kSBK, cur ^ 1);
+        barrier();
+        step(1, yes{}, cur ^ 1, 0, c0{}, c8{}, (ph + 2) * kSBK, cur);
+    }
+    if (ph + 1 < P) {
+        const int cur = ph & 1;
+        steps012(cur, yes{}, (ph + 1) * kSBK, cur ^ 1);
+        barrier();
+        step(1, yes{}, cur ^ 1, 0, c0{}, c0{}, 0, 0);
+        ++ph;
+    }
+    steps012(ph & 1, no{}, 0, 0);
+    step(1, no{}, 0, 0, c0{}, c0{}, 0, 0);
+
+    // Store (the launcher passes full tiles only).  Register r of lane
+    // (li, lh) is row rho = 8 (r / 4) + 4 lh + r % 4 and column li of its
+    // 32 x 32 block; block (i, j) of a k-contiguous A holds rows 32 i + rho of
+    // the wave's span, of an mn-contiguous A rows 4 rho + i; likewise for B's
+    // columns.  With B mn-contiguous the four blocks j of one row are four
+    // adjacent columns: one 128-bit store.
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int rho = 8 * (r >> 2) + 4 * lh + (r & 3);
+            const int row = m0 + wm * WM + (KCA ? 32 * i + rho : 4 * rho + i);
+            float* crow = p.C + (int64_t)row * p.ldc + n0 + wn * WN;
+            if constexpr (!KCB) {
+                const floatx4 v = {acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
+                *reinterpret_cast<floatx4*>(crow + 4 * li) = v;
+            } else {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) crow[32 * j + li] = acc[i][j][r];
+            }
+        }
+}
+
+template <bool KCA, bool KCB>
+hipError_t launch_sched_f32_kernel(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                                   unsigned blocks) {
+    hipLaunchKernelGGL((gemm_f32_sched_kernel<KCA, KCB>), dim3(blocks), dim3(256), 0, s, p, tiles_m, tiles_n,
+                       group_m);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Any leading dimension and dword alignment will do: gfx9 runs memory in
+// unaligned-access mode, so the 16-byte copies and stores need only the
+// 4-byte alignment the entry points check.
+bool sched_f32_fits(const GemmArgs& p, int op_a, int op_b) {
+    if (p.M % 256 != 0 || p.N % 256 != 0 || p.K % kSBK != 0 || p.K <= 0) return false;
+    // A stored M x K (op N) or K x M (op T); B stored K x N or N x K.  Byte
+    // offsets of both stay below 2^31.
+    const int64_t a_rows = op_a ? p.K : p.M, b_rows = op_b ? p.N : p.K;
+    const int64_t lim = (int64_t)1 << 31;
+    return 4 * a_rows * p.lda < lim && 4 * b_rows * p.ldb < lim;
+}
+
+hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m) {
+    const int tiles_m = p.M / 256, tiles_n = p.N / 256;
+    const unsigned blocks = (unsigned)((int64_t)tiles_m * tiles_n);
+    switch (2 * (op_a ? 1 : 0) + (op_b ? 1 : 0)) {
+        case 0: return launch_sched_f32_kernel<true, false>(p, s, tiles_m, tiles_n, group_m, blocks);
+        case 1: return launch_sched_f32_kernel<true, true>(p, s, tiles_m, tiles_n, group_m, blocks);
+        case 2: return launch_sched_f32_kernel<false, false>(p, s, tiles_m, tiles_n, group_m, blocks);
+        default: return launch_sched_f32_kernel<false, true>(p, s, tiles_m, tiles_n, group_m, blocks);
+    }
+}
+
+}  // namespace gemmf32

@@ -1,0 +1,125 @@
+"""The four-wave scheduled fp32 kernel, which gemm_f32 and gemm_f32_op run
+when M and N are multiples of 256 and K of 32 (with 256 or more tiles).
+
+Checked against the oracle (every entry on a K = 32 problem, sampled entries
+on longer ones; exact on integer inputs) for all four op pairs, on aligned
+and on padded, dword-offset operands, and bit for bit against the eight-wave
+256 x 256 kernel on explicitly transposed copies: both sum every entry's k
+terms in the same order."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_support import check_close, check_exact, check_padding_untouched, say
+from shared_memory_tiled_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+OPS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
+SCHED = "mfma256x256_bk32_w2x2_sched"
+EIGHT_WAVE = "mfma256x256_bk32_w2x4_direct"
+
+
+def variant_number(name):
+    for d in range(binding.gemm_f32_num_diagnostic_variants()):
+        if binding.gemm_f32_variant_name(binding.DIAGNOSTIC_BASE + d) == name:
+            return binding.DIAGNOSTIC_BASE + d
+    raise KeyError(name)
+
+
+def stored_shape(op, rows, cols):
+    return (rows, cols) if op == "N" else (cols, rows)
+
+
+class Problem:
+    """op(A) x op(B) on padded device buffers (pad words NaN, C sentinels)."""
+
+    def __init__(self, op_a, op_b, M, N, K, dist, seed, offset=0, pad=(0, 0, 0)):
+        self.op_a, self.op_b, self.M, self.N, self.K = op_a, op_b, M, N, K
+        gen = np.random.default_rng(seed)
+        ar, ac = stored_shape(op_a, M, K)
+        br, bc = stored_shape(op_b, K, N)
+        self.A = inputs.padded(inputs.random_matrix(gen, ar, ac, dist), ac + pad[0], offset)
+        self.B = inputs.padded(inputs.random_matrix(gen, br, bc, dist), bc + pad[1], offset)
+        self.ldc, self.offset = N + pad[2], offset
+        self.A_dev = torch.from_numpy(self.A.buf).cuda()
+        self.B_dev = torch.from_numpy(self.B.buf).cuda()
+        self.C_init = inputs.padded_output(M, N, self.ldc, offset)
+        self.C_dev = torch.from_numpy(self.C_init.buf).cuda()
+
+    def run(self):
+        self.C_dev.copy_(torch.from_numpy(self.C_init.buf))
+        binding.gemm_f32_op(self.op_a, self.op_b, self.M, self.N, self.K,
+                            self.A_dev.data_ptr() + 4 * self.A.offset, self.A.ld,
+                            self.B_dev.data_ptr() + 4 * self.B.offset, self.B.ld,
+                            self.C_dev.data_ptr() + 4 * self.offset, self.ldc)
+        torch.cuda.synchronize()
+        return inputs.Padded(self.C_dev.cpu().numpy(), self.M, self.N, self.ldc, self.offset)
+
+    def eight_wave_bits(self):
+        """The eight-wave kernel on dense op(A), op(B) copies."""
+        a = torch.from_numpy(np.ascontiguousarray(self.A.view if self.op_a == "N" else self.A.view.T)).cuda()
+        b = torch.from_numpy(np.ascontiguousarray(self.B.view if self.op_b == "N" else self.B.view.T)).cuda()
+        out = binding.gemm(a, b, variant=variant_number(EIGHT_WAVE))
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+
+def test_scheduled_kernel_is_the_default_for_full_tiles():
+    for shape in [(4096, 4096, 32), (4096, 4352, 96), (8192, 8192, 8192)]:
+        assert binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(*shape)) == SCHED
+    for shape in [(4096, 4096, 33), (4100, 4096, 64), (4096, 4097, 64)]:
+        assert binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(*shape)) == EIGHT_WAVE
+
+
+@pytest.mark.parametrize("ops", OPS, ids=lambda o: o[0] + o[1])
+@pytest.mark.parametrize("dist", ["int", "uniform"])
+def test_scheduled_full_oracle(ops, dist):
+    """K = 32 (one phase, the prologue and the peeled last steps only) and
+    K = 64 (two phases) against the whole oracle product."""
+    op_a, op_b = ops
+    for K in (32, 64):
+        prob = Problem(op_a, op_b, 4096, 4096, K, dist, [K, len(op_a + op_b), dist == "int", ord(op_a[0])])
+        Cref, S = oracle.gemm(prob.A.view, prob.B.view, op_a=op_a, op_b=op_b, threads=8)
+        say(f"sched full oracle {op_a}{op_b} {dist} K={K}")
+        C = prob.run()
+        check_padding_untouched(C)
+        what = f"sched {op_a}{op_b} {dist} K={K}"
+        if dist == "int":
+            check_exact(C.view, Cref, what)
+        else:
+            check_close(C.view, Cref, S, what)
+        assert np.array_equal(C.view, prob.eight_wave_bits()), what + ": bits differ from the eight-wave kernel"
+
+
+SAMPLED = [
+    # shape, offset, (pad A, pad B, pad C): aligned, then dword-offset and padded
+    ((4096, 4352, 96), 0, (0, 0, 0)),
+    ((4352, 4096, 544), 1, (3, 5, 7)),
+    ((4096, 4096, 256), 3, (1, 2, 1)),
+]
+
+
+@pytest.mark.parametrize("ops", OPS, ids=lambda o: o[0] + o[1])
+@pytest.mark.parametrize("case", SAMPLED, ids=lambda c: "x".join(map(str, c[0])) + f"_off{c[1]}")
+@pytest.mark.parametrize("dist", ["int", "uniform"])
+def test_scheduled_sampled(ops, case, dist):
+    op_a, op_b = ops
+    (M, N, K), offset, pad = case
+    prob = Problem(op_a, op_b, M, N, K, dist, [M, N, K, offset, len(op_a + op_b), dist == "int"],
+                   offset, pad)
+    ii, jj = inputs.sample_pairs(M, N, 4096, np.random.default_rng([M, N, K, 5]))
+    cref, sref = oracle.gemm_entries(prob.A.view, prob.B.view, ii, jj, op_a=op_a, op_b=op_b)
+    say(f"sched sampled {op_a}{op_b} {dist} {(M, N, K)} offset={offset} pad={pad}")
+    C = prob.run()
+    check_padding_untouched(C)
+    what = f"sched {op_a}{op_b} {dist} {(M, N, K)} offset {offset}"
+    if dist == "int":
+        check_exact(C.view[ii, jj], cref, what)
+    else:
+        check_close(C.view[ii, jj], cref, sref, what)
+    assert np.all(np.isfinite(C.view))
+    assert np.array_equal(C.view, prob.eight_wave_bits()), what + ": bits differ from the eight-wave kernel"
