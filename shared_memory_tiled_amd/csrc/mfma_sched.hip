@@ -189,11 +189,24 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     for (int s = 0; s < SB; ++s) bbase[s] = lds0 + 2u * kStageBytes + TB::read_base(wn * WN, s, li, lh);
 
     floatx4 a[2][4], b[2][4];
-    // Read i (0..7) of step s from stage buf into set t: A's four first.
-    auto read_op = [&](int buf, int s, int t, int i) __attribute__((always_inline)) {
-        const uint32_t soff = (uint32_t)buf * (uint32_t)kStageBytes;
-        if (i < 4) a[t][i] = lds_read128(abase[KCA ? s : 0] + soff + TA::read_imm(s, i));
-        else b[t][i - 4] = lds_read128(bbase[KCB ? s : 0] + soff + TB::read_imm(s, i - 4));
+    // Read i (0..7) of step s into set t, A's four first, from the stage the
+    // bases point at: step and read index go into the instruction's offset
+    // field.  The bases move to the other stage once per phase (flip_stage),
+    // so the loop holds 2..8 vector ALU instructions per phase besides the
+    // matrix ones, not one per read: each placed between two matrix
+    // instructions was measured to cost the matrix core about 14 cycles
+    // (scalar ones cost nothing).
+    auto read_op = [&](int s, int t, int i) __attribute__((always_inline)) {
+        if (i < 4) a[t][i] = lds_read128(abase[KCA ? s : 0] + TA::read_imm(s, i));
+        else b[t][i - 4] = lds_read128(bbase[KCB ? s : 0] + TB::read_imm(s, i - 4));
+    };
+    // Point the read bases at the other stage (from stage cur to cur ^ 1).
+    auto flip_stage = [&](int cur) __attribute__((always_inline)) {
+        const uint32_t d = cur ? (uint32_t)-kStageBytes : (uint32_t)kStageBytes;
+#pragma unroll
+        for (int s = 0; s < SA; ++s) abase[s] += d;
+#pragma unroll
+        for (int s = 0; s < SB; ++s) bbase[s] += d;
     };
 
     floatx16 acc[FM][FN];
@@ -206,9 +219,9 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
 
     // One step: the 64 matrix instructions on fragment set t (instruction q:
     // e = q / 16, block (q / 4 % 4, q % 4)); after the q-th (q < 8), read q of
-    // step rs from stage rbuf into set t ^ 1 (if R) and, after every eighth,
+    // step rs into set t ^ 1 (if R) and, after every eighth,
     // copy CB + q / 8 (while below CE) of the phase at k_copy into stage cbuf.
-    auto step = [&](int t, auto reads, int rbuf, int rs, auto cb, auto ce, int k_copy,
+    auto step = [&](int t, auto reads, int rs, auto cb, auto ce, int k_copy,
                     int cbuf) __attribute__((always_inline)) {
         constexpr bool R = decltype(reads)::value;
         constexpr int CB = decltype(cb)::value, CE = decltype(ce)::value;
@@ -219,7 +232,7 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
                                                              operand<KCB>(b[t], j, e), acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (R && q < NREAD) {
-                read_op(rbuf, rs, t ^ 1, q);
+                read_op(rs, t ^ 1, q);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (q % 8 == 7 && CB + q / 8 < CE) {
@@ -244,31 +257,32 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     using c0 = std::integral_constant<int, 0>;
     using c8 = std::integral_constant<int, 8>;
     using c16 = std::integral_constant<int, 16>;
-    // Steps 0..2 of the phase on stage cur (step 0's fragments already read)
-    // and the wait for step 3's; copies 8..15 of the phase at k_copy into
-    // stage cbuf with step 0 if WC.
-    auto steps012 = [&](int cur, auto wc, int k_copy, int cbuf) __attribute__((always_inline)) {
+    // Steps 0..2 of the phase (step 0's fragments already read) and the wait
+    // for step 3's; copies 8..15 of the phase at k_copy into stage cbuf with
+    // step 0 if WC.
+    auto steps012 = [&](auto wc, int k_copy, int cbuf) __attribute__((always_inline)) {
         constexpr bool WC = decltype(wc)::value;
         wait_set(0);
-        if constexpr (WC) step(0, yes{}, cur, 1, c8{}, c16{}, k_copy, cbuf);
-        else step(0, yes{}, cur, 1, c0{}, c0{}, 0, 0);
+        if constexpr (WC) step(0, yes{}, 1, c8{}, c16{}, k_copy, cbuf);
+        else step(0, yes{}, 1, c0{}, c0{}, 0, 0);
         wait_set(1);
-        step(1, yes{}, cur, 2, c0{}, c0{}, 0, 0);
+        step(1, yes{}, 2, c0{}, c0{}, 0, 0);
         wait_set(0);
-        step(0, yes{}, cur, 3, c0{}, c0{}, 0, 0);
+        step(0, yes{}, 3, c0{}, c0{}, 0, 0);
         wait_set(1);
     };
 
     // Stage ph & 1 holds phase ph.  Between the barriers that end phases
     // ph - 1 and ph run the deferred last step of phase ph - 1 (with copies
-    // 0..7 of phase ph + 1 and the first reads of phase ph) and steps 0..2 of
-    // phase ph (copies 8..15 with step 0).
+    // 0..7 of phase ph + 1 and the first reads of phase ph, the read bases
+    // already on its stage) and steps 0..2 of phase ph (copies 8..15 with
+    // step 0).
     const int P = p.K / kSBK;
 #pragma unroll
     for (int j = 0; j < NCOPY; ++j) copy(j, 0, 0);
     barrier();
 #pragma unroll
-    for (int i = 0; i < NREAD; ++i) read_op(0, 0, 0, i);
+    for (int i = 0; i < NREAD; ++i) read_op(0, 0, i);
     if (P > 1) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) copy(j, kSBK, 1);
@@ -277,19 +291,23 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     int ph = 0;
     for (; ph + 2 < P; ++ph) {
         const int cur = ph & 1;
-        steps012(cur, yes{}, (ph + 1) * kSBK, cur ^ 1);
+        steps012(yes{}, (ph + 1) * kSBK, cur ^ 1);
+        flip_stage(cur);
+        __builtin_amdgcn_sched_barrier(0);
         barrier();
-        step(1, yes{}, cur ^ 1, 0, c0{}, c8{}, (ph + 2) * kSBK, cur);
+        step(1, yes{}, 0, c0{}, c8{}, (ph + 2) * kSBK, cur);
     }
     if (ph + 1 < P) {
         const int cur = ph & 1;
-        steps012(cur, yes{}, (ph + 1) * kSBK, cur ^ 1);
+        steps012(yes{}, (ph + 1) * kSBK, cur ^ 1);
+        flip_stage(cur);
+        __builtin_amdgcn_sched_barrier(0);
         barrier();
-        step(1, yes{}, cur ^ 1, 0, c0{}, c0{}, 0, 0);
+        step(1, yes{}, 0, c0{}, c0{}, 0, 0);
         ++ph;
     }
-    steps012(ph & 1, no{}, 0, 0);
-    step(1, no{}, 0, 0, c0{}, c0{}, 0, 0);
+    steps012(no{}, 0, 0);
+    step(1, no{}, 0, c0{}, c0{}, 0, 0);
 
     // Store (the launcher passes full tiles only).  Register r of lane
     // (li, lh) is row rho = 8 (r / 4) + 4 lh + r % 4 and column li of its
