@@ -523,8 +523,8 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
 // The scheduled kernel: 256 x 256 tiles of full phases (M and N multiples of
 // 256, K of 64, vector-aligned operands under 2^31 bytes each), four waves of
 // 128 x 128, one per SIMD, with every instruction of the K loop placed in
-// program order.  Same LDS layouts and the same k order as the kernels above
-// (so the same bits), but:
+// program order.  Same LDS layouts as the kernels above except for the
+// k-contiguous swizzle (below), and the same k order (so the same bits), but:
 //  * Each step issues its 16 matrix instructions one at a time, with the next
 //    step's fragment reads (two after each of the first ones) and the copies
 //    of the next phase (one after each odd one) between them, so the reads'
@@ -538,21 +538,30 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
 //    a whole phase ahead of their use.  They are buffer loads into LDS: base
 //    and extent in a resource, the per-lane offset in a register, the phase's
 //    k in the scalar offset, so they cost no vector instruction.
-//  * Fragment read addresses are computed once per lane; a phase only adds
-//    the stage offset.
+//  * Fragment read addresses are a per-lane base plus a compile-time offset
+//    (step, fragment), and the bases move to the other stage once per phase:
+//    besides the matrix instructions the loop holds only those 8 vector adds
+//    per phase.  A vector ALU instruction between two matrix instructions
+//    costs the matrix core about 14 cycles (measured on the fp32 kernel),
+//    a lot against a 32-cycle instruction; scalar ones cost nothing.
 // With two waves per SIMD (the kernels above) the waves of a SIMD drift
 // apart within a phase and the younger one runs alone, its latencies
 // exposed, while the older one waits at the barrier.
 //
 // Each factor's tile is one of two kinds (see gemm16_op_kernel):
 //   KC (k-contiguous: A as stored, B stored transposed): 256 rows of 64 k,
-//      chunk c of row r at c ^ f(r); a fragment is one 128-bit read; a copy
-//      fills 8 rows;
+//      chunk c of row r at c ^ ((r / 2) mod 8) (the 16 rows one read cycle
+//      touches, two per 64-bank sweep, on 16 different 4-bank groups; for
+//      the rows 32 f + l % 32 a lane reads, the permutation depends on l
+//      only, so fragment f is a compile-time offset); a fragment is one
+//      128-bit read; a copy fills 8 rows;
 //   MC (mn-contiguous: B as stored, A stored transposed): 64 k rows of 256
 //      values, chunk c of row r at c ^ 4 (r % 4); a fragment is two
 //      ds_read_b64_tr_b16 reads; a copy fills 2 rows.
 // Both are 32 KB per stage: LDS holds A's stages at bytes 0 and 32768, B's at
 // 65536 and 98304.
+__host__ __device__ __forceinline__ constexpr int sched_swz(int r) { return (r >> 1) & 7; }
+
 template <bool KC>
 struct SchedTile {
     static constexpr int MNT = 256, NW = 4;
@@ -567,7 +576,7 @@ struct SchedTile {
     __host__ __device__ static uint32_t copy_src(int w, int j, int lane, int mn0, int64_t ld) {
         if constexpr (KC) {
             const int row = 8 * (w + j * NW) + lane / 8;
-            return 2u * (uint32_t)((mn0 + row) * ld + 8 * ((lane % 8) ^ swz(row)));
+            return 2u * (uint32_t)((mn0 + row) * ld + 8 * ((lane % 8) ^ sched_swz(row)));
         } else {
             const int row = 2 * (w + j * NW) + lane / 32;
             return 2u * (uint32_t)(row * ld + mn0 + 8 * ((lane % 32) ^ (4 * (row & 3))));
@@ -634,53 +643,58 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
         }
     };
 
-    // Fragment addresses in bytes for stage 0 of the tile at element `base`:
-    // KC, fragment f of step s (the 128-bit read of gemm16_kernel's A); MC,
-    // fragment f at step 0, k 0..3 of the lane half (step s adds 16 rows, 8192
-    // bytes, k 4..7 four rows, 2048: instruction offsets).
+    // Per-lane read bases in bytes for stage 0 of the tile at element `base`
+    // (the wave's span starting at mn), four per factor: KC, base x serves
+    // step x (row mn + l % 32, logical chunk 2 x + l / 32; fragment f adds 32
+    // rows, 4096 bytes); MC, base x serves fragment x (k 0..3 of the lane
+    // group at step 0; step s adds 16 rows, 8192 bytes, k 4..7 four rows,
+    // 2048).  All the rest is an instruction offset.
     auto mc_elem = [](int r, int c) __attribute__((always_inline)) { return r * 256 + 8 * (c ^ (4 * (r & 3))); };
-    auto frag_addr = [&](auto kc, int base, int mn, int s) __attribute__((always_inline)) -> uint32_t {
+    auto frag_base = [&](auto kc, int base, int mn, int x) __attribute__((always_inline)) -> uint32_t {
         if constexpr (decltype(kc)::value) {
-            return lds_addr(lds + base) + 2u * lds_elem(mn + li, 2 * s + lh);
+            return lds_addr(lds + base) + 2u * ((mn + li) * kBK + 8 * ((2 * x + lh) ^ sched_swz(li)));
         } else {
-            const int n = mn + 16 * (tr_g & 1) + 4 * (tr_j & 3);
+            const int n = mn + 32 * x + 16 * (tr_g & 1) + 4 * (tr_j & 3);
             const int row0 = 8 * (tr_g >> 1) + (tr_j >> 2);
             return lds_addr(lds + base) + 2u * (mc_elem(row0, n >> 3) + 4 * ((n >> 2) & 1));
         }
     };
-    constexpr int SA = KCA ? kBK / 16 : 1, SB = KCB ? kBK / 16 : 1;
-    uint32_t aaddr[FM][SA], baddr[FN][SB];
+    static_assert(kBK / 16 == 4 && FM == 4 && FN == 4, "four read bases per factor");
+    uint32_t abase[4], bbase[4];
 #pragma unroll
-    for (int f = 0; f < FM; ++f)
-#pragma unroll
-        for (int st = 0; st < SA; ++st)
-            aaddr[f][st] = frag_addr(std::integral_constant<bool, KCA>{}, 0, wm * WM + f * 32, st);
-#pragma unroll
-    for (int f = 0; f < FN; ++f)
-#pragma unroll
-        for (int st = 0; st < SB; ++st)
-            baddr[f][st] = frag_addr(std::integral_constant<bool, KCB>{}, 2 * TILE, wn * WN + f * 32, st);
+    for (int x = 0; x < 4; ++x) {
+        abase[x] = frag_base(std::integral_constant<bool, KCA>{}, 0, wm * WM, x);
+        bbase[x] = frag_base(std::integral_constant<bool, KCB>{}, 2 * TILE, wn * WN, x);
+    }
 
     u32x4 a[2][FM], b[2][FN];
-    // Read i (0 .. READS - 1) of one factor's fragments of step s, from the
-    // stage at soff bytes, into x: KC, fragment i; MC, half i % 2 of fragment
-    // i / 2.
-    auto read_one = [&](auto kc, u32x4 (&x)[4], const auto& addr, uint32_t soff, int s,
+    // Read i (0 .. READS - 1) of one factor's fragments of step s into x: KC,
+    // fragment i; MC, half i % 2 of fragment i / 2.
+    auto read_one = [&](auto kc, u32x4 (&x)[4], const uint32_t (&base)[4], int s,
                         int i) __attribute__((always_inline)) {
         if constexpr (decltype(kc)::value) {
-            x[i] = lds_read128(addr[i][s] + soff);
+            x[i] = lds_read128(base[s] + 4096u * (uint32_t)i);
         } else {
             const int f = i / 2, r = i % 2;
-            const u32x2 v = read_tr16_off(addr[f][0] + soff, 8192 * s + 2048 * r);
+            const u32x2 v = read_tr16_off(base[f], 8192 * s + 2048 * r);
             x[f][2 * r] = v[0];
             x[f][2 * r + 1] = v[1];
         }
     };
-    // Read i of step s from stage buf into set t: A's reads first, then B's.
-    auto read_op = [&](int buf, int s, int t, int i) __attribute__((always_inline)) {
-        const uint32_t soff = (uint32_t)buf * 32768u;
-        if (i < TA::READS) read_one(std::integral_constant<bool, KCA>{}, a[t], aaddr, soff, s, i);
-        else read_one(std::integral_constant<bool, KCB>{}, b[t], baddr, soff, s, i - TA::READS);
+    // Read i of step s into set t, from the stage the bases point at: A's
+    // reads first, then B's.
+    auto read_op = [&](int s, int t, int i) __attribute__((always_inline)) {
+        if (i < TA::READS) read_one(std::integral_constant<bool, KCA>{}, a[t], abase, s, i);
+        else read_one(std::integral_constant<bool, KCB>{}, b[t], bbase, s, i - TA::READS);
+    };
+    // Point the read bases at the other stage (from stage cur to cur ^ 1).
+    auto flip_stage = [&](int cur) __attribute__((always_inline)) {
+        const uint32_t d = cur ? (uint32_t)-32768 : 32768u;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            abase[x] += d;
+            bbase[x] += d;
+        }
     };
     floatx16 acc[FM][FN];
 #pragma unroll
@@ -694,7 +708,7 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     // the q-th, reads 2q and 2q + 1 of step rs from stage rbuf into set t ^ 1
     // (if R) and, after each odd one, copy CB + q / 2 (while below CE) of the
     // phase at k_copy into stage cbuf.
-    auto step = [&](auto mm, int t, auto reads, int rbuf, int rs, auto cb, auto ce, int k_copy,
+    auto step = [&](auto mm, int t, auto reads, int rs, auto cb, auto ce, int k_copy,
                     int cbuf) __attribute__((always_inline)) {
         constexpr bool MM = decltype(mm)::value;
         constexpr bool R = decltype(reads)::value;
@@ -706,8 +720,8 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (R && 2 * q < NREAD) {
-                read_op(rbuf, rs, t ^ 1, 2 * q);
-                read_op(rbuf, rs, t ^ 1, 2 * q + 1);
+                read_op(rs, t ^ 1, 2 * q);
+                read_op(rs, t ^ 1, 2 * q + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (q % 2 == 1 && CB + q / 2 < CE) {
@@ -734,31 +748,32 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     using c0 = std::integral_constant<int, 0>;
     using c8 = std::integral_constant<int, 8>;
     using c16 = std::integral_constant<int, 16>;
-    // Steps 0..2 of the phase on stage cur (step 0's fragments already read)
-    // and the wait for step 3's; copies 8..15 of the phase at k_copy into
-    // stage cbuf with step 0 if WC.
-    auto steps012 = [&](int cur, auto wc, int k_copy, int cbuf) __attribute__((always_inline)) {
+    // Steps 0..2 of the phase (step 0's fragments already read) and the wait
+    // for step 3's; copies 8..15 of the phase at k_copy into stage cbuf with
+    // step 0 if WC.
+    auto steps012 = [&](auto wc, int k_copy, int cbuf) __attribute__((always_inline)) {
         constexpr bool WC = decltype(wc)::value;
         wait_set(0);
-        if constexpr (WC) step(yes{}, 0, yes{}, cur, 1, c8{}, c16{}, k_copy, cbuf);
-        else step(yes{}, 0, yes{}, cur, 1, c0{}, c0{}, 0, 0);
+        if constexpr (WC) step(yes{}, 0, yes{}, 1, c8{}, c16{}, k_copy, cbuf);
+        else step(yes{}, 0, yes{}, 1, c0{}, c0{}, 0, 0);
         wait_set(1);
-        step(yes{}, 1, yes{}, cur, 2, c0{}, c0{}, 0, 0);
+        step(yes{}, 1, yes{}, 2, c0{}, c0{}, 0, 0);
         wait_set(0);
-        step(yes{}, 0, yes{}, cur, 3, c0{}, c0{}, 0, 0);
+        step(yes{}, 0, yes{}, 3, c0{}, c0{}, 0, 0);
         wait_set(1);
     };
 
     // Stage ph & 1 holds phase ph.  Between the barriers that end phases
     // ph - 1 and ph run the deferred last step of phase ph - 1 (with copies
-    // 0..7 of phase ph + 1 and the first reads of phase ph) and steps 0..2 of
-    // phase ph (copies 8..15 with step 0).
+    // 0..7 of phase ph + 1 and the first reads of phase ph, the read bases
+    // already on its stage) and steps 0..2 of phase ph (copies 8..15 with
+    // step 0).
     const int P = p.K / kBK;
 #pragma unroll
     for (int j = 0; j < NCOPY; ++j) copy(j, 0, 0);
     barrier();
 #pragma unroll
-    for (int i = 0; i < NREAD; ++i) read_op(0, 0, 0, i);
+    for (int i = 0; i < NREAD; ++i) read_op(0, 0, i);
     if (P > 1) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) copy(j, kBK, 1);
@@ -767,19 +782,23 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     int ph = 0;
     for (; ph + 2 < P; ++ph) {
         const int cur = ph & 1;
-        steps012(cur, yes{}, (ph + 1) * kBK, cur ^ 1);
+        steps012(yes{}, (ph + 1) * kBK, cur ^ 1);
+        flip_stage(cur);
+        __builtin_amdgcn_sched_barrier(0);
         barrier();
-        step(yes{}, 1, yes{}, cur ^ 1, 0, c0{}, c8{}, (ph + 2) * kBK, cur);
+        step(yes{}, 1, yes{}, 0, c0{}, c8{}, (ph + 2) * kBK, cur);
     }
     if (ph + 1 < P) {
         const int cur = ph & 1;
-        steps012(cur, yes{}, (ph + 1) * kBK, cur ^ 1);
+        steps012(yes{}, (ph + 1) * kBK, cur ^ 1);
+        flip_stage(cur);
+        __builtin_amdgcn_sched_barrier(0);
         barrier();
-        step(yes{}, 1, yes{}, cur ^ 1, 0, c0{}, c0{}, 0, 0);
+        step(yes{}, 1, yes{}, 0, c0{}, c0{}, 0, 0);
         ++ph;
     }
-    steps012(ph & 1, no{}, 0, 0);
-    step(yes{}, 1, no{}, 0, 0, c0{}, c0{}, 0, 0);
+    steps012(no{}, 0, 0);
+    step(yes{}, 1, no{}, 0, c0{}, c0{}, 0, 0);
 
     // Guarded store (full tiles: the guard never fails).  Register r of lane
     // (li, lh) is row 8 (r / 4) + 4 lh + r % 4 of its 32 x 32 block.

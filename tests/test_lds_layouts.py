@@ -207,24 +207,39 @@ def test_mixed_transposed_b_reads_conflict_free(bn):
 
 
 def test_scheduled_mixed_kernel_addresses():
-    """The scheduled 16-bit kernel computes its fragment addresses once per
-    lane and adds only the stage offset and an instruction offset per read.
-    Restated here: for every wave, lane, fragment, step, half and stage the
-    decomposed address equals the full layout formula (A rows of 64 values,
-    chunk c of row r at c ^ f(r); B rows of 256 values, chunk c of row r at
-    c ^ 4 (r % 4)), the instruction offset fits its 16 bits, and the four
-    tiles (A and B, two stages) are disjoint and fill 128 KB."""
+    """The scheduled 16-bit kernel keeps four read bases per factor and adds
+    only an instruction offset per read; the bases move to the other stage
+    once per phase.  Restated here: for every wave, lane, fragment, step, half
+    and stage the decomposed address equals the full layout formula (A rows
+    of 64 values, chunk c of row r at c ^ ((r / 2) mod 8); B rows of 256
+    values, chunk c of row r at c ^ 4 (r % 4)), the instruction offset fits
+    its 16 bits, the k-contiguous reads are conflict free, the copies put
+    chunk c of row r where the reads expect it, and the four tiles (A and B,
+    two stages) are disjoint and fill 128 KB."""
     BK, BM, BN = 64, 256, 256
     A_ST, B_BASE, B_ST = BM * BK, 2 * BM * BK, BK * BN          # elements
 
-    def swz(r):
-        return ((r >> 1) ^ (r >> 4)) & 7
+    def sswz(r):
+        return (r >> 1) & 7
 
-    def lds_elem(r, c):
-        return r * BK + 8 * (c ^ swz(r))
+    def kc_elem(r, c):
+        return r * BK + 8 * (c ^ sswz(r))
 
     def b_elem(r, c):
         return r * BN + 8 * (c ^ (4 * (r & 3)))
+
+    # the k-contiguous copies: copy j of wave w fills rows 8 (w + 4 j) ..,
+    # lane l physical chunk l % 8 of row 8 (w + 4 j) + l / 8 from logical
+    # chunk (l % 8) ^ sswz(row)
+    filled = {}
+    for w in range(4):
+        for j in range(8):
+            for lane in range(64):
+                row = 8 * (w + 4 * j) + lane // 8
+                dst = 8 * (w + 4 * j) * BK + 8 * lane
+                filled[dst] = (row, (lane % 8) ^ sswz(row))
+    assert sorted(filled) == list(range(0, A_ST, 8))
+    assert all(kc_elem(r, c) == d for d, (r, c) in filled.items())
 
     seen_a, seen_b = set(), set()
     for wave in range(4):
@@ -236,10 +251,10 @@ def test_scheduled_mixed_kernel_addresses():
                 row0 = 8 * (g >> 1) + (j >> 2)
                 baddr = 2 * (B_BASE + b_elem(row0, n >> 3) + 4 * ((n >> 2) & 1))
                 for s in range(BK // 16):
-                    aaddr = 2 * lds_elem(wm * 128 + f * 32 + li, 2 * s + lh)
+                    abase = 2 * ((wm * 128 + li) * BK + 8 * ((2 * s + lh) ^ sswz(li)))
                     for stage in (0, 1):
-                        a_full = 2 * (stage * A_ST + lds_elem(wm * 128 + f * 32 + li, 2 * s + lh))
-                        assert aaddr + 32768 * stage == a_full
+                        a_full = 2 * (stage * A_ST + kc_elem(wm * 128 + f * 32 + li, 2 * s + lh))
+                        assert abase + 32768 * stage + 4096 * f == a_full
                         seen_a.add(a_full // 16)
                         for r in (0, 1):
                             off = 8192 * s + 2048 * r
@@ -252,6 +267,12 @@ def test_scheduled_mixed_kernel_addresses():
     assert seen_a == set(range(2 * A_ST * 2 // 16))
     assert seen_b == set(range(B_BASE * 2 // 8, (B_BASE + 2 * B_ST) * 2 // 8))
     assert (B_BASE + 2 * B_ST) * 2 == 128 * 1024
+    # k-contiguous fragment reads: 16 lanes per cycle, 64 banks
+    for f in range(4):
+        for s in range(4):
+            for lh in (0, 1):
+                words = [kc_elem(f * 32 + li, 2 * s + lh) // 2 for li in range(32)]
+                assert degree(words, 4, 64, 16) == 1
 
 
 def sched_f32_swz(r):
