@@ -83,9 +83,9 @@ extern "C" {
  *   3  MFMA: v_mfma_f32_32x32x2_f32 matrix-core contraction on double-
  *      buffered LDS tiles (the default).  Large problems use 256 x 256 tiles
  *      with direct global-to-LDS copies into an XOR-swizzled layout: on four
- *      waves with a fixed instruction order when M and N are multiples of
- *      256 and K of 32 (and each stored factor is under 2 GiB), else on
- *      eight waves; both give the same bits
+ *      waves with a fixed instruction order when K is a multiple of 32 and
+ *      M and N of 4 (and each stored factor is under 2 GiB), else on eight
+ *      waves; both give the same bits
  * Variants numbered from 16 up are diagnostic layouts of the same rungs, kept
  * so that their hardware counters can be compared; see
  * gemm_f32_variant_name().

@@ -641,7 +641,7 @@ const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConf
 
 // Largest tile that still gives every CU at least one workgroup: 256 x 256
 // once there are 256 such tiles -- on four waves with a fixed instruction
-// order (mfma_sched.hip) when M and N are multiples of 256 and K of 32 (the
+// order (mfma_sched.hip) when K is a multiple of 32 and M and N of 4 (the
 // launcher falls back to the eight-wave kernel for stored factors of 2 GiB
 // or more), else on eight waves (two per SIMD, so one wave's
 // barrier or LDS wait is covered by the other's matrix instructions) with
@@ -657,7 +657,7 @@ int mfma_pick_config(int M, int N, int K) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
     const int64_t t64 = (int64_t)ceil_div(M, 64) * ceil_div(N, 64);
-    if (t256 >= 256) return (M % 256 == 0 && N % 256 == 0 && K % 32 == 0 && K > 0) ? 16 : 7;
+    if (t256 >= 256) return (K % 32 == 0 && K > 0 && M % 4 == 0 && N % 4 == 0) ? 16 : 7;
     const int64_t rounds128 = (t128 + 255) / 256;
     if (t128 >= 256 && t128 * 10 >= rounds128 * 256 * 9) return 1;
     return t64 <= 256 ? 14 : 13;

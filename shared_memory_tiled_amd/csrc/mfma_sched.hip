@@ -3,7 +3,8 @@
 // The tiled product of the pages' shared-memory chapter (PMPP chapter 5
 // notes, sections 5.4-5.5: per phase every thread of a block copies part of
 // an A and a B tile into shared memory, a barrier, the multiply-adds from the
-// tiles, a barrier) on full 256 x 256 output tiles, 32 k values per phase,
+// tiles, a barrier, and a guarded store at the edges) on 256 x 256 output
+// tiles, 32 k values per phase (K a multiple of 32),
 // two LDS stages so the copies of the next phase overlap the math of the
 // current one.
 //
@@ -159,11 +160,18 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         doff[A_COPIES + j] = TB::copy_src(wave_u, j, lane, n0, p.ldb);
     }
     constexpr int kRawBufferWord3 = 0x00020000;
-    const int64_t a_rows = KCA ? p.M : p.K, b_rows = KCB ? p.N : p.K;
+    // Each descriptor ends exactly at its stored matrix's last element.  An
+    // edge tile's copies past the last row read +0 without touching memory;
+    // past the last column of an mn-contiguous factor they read the next
+    // row (or +0 past the end), which only ever meets C entries outside the
+    // matrix, never stored.  K is a multiple of 32, and an mn-contiguous
+    // factor's extent a multiple of 4, so no 16-byte chunk straddles an edge.
+    const int64_t a_rows = KCA ? p.M : p.K, a_cols = KCA ? p.K : p.M;
+    const int64_t b_rows = KCB ? p.N : p.K, b_cols = KCB ? p.K : p.N;
     const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(p.A), (short)0, (int)(4 * a_rows * p.lda), kRawBufferWord3);
+        const_cast<float*>(p.A), (short)0, (int)(4 * ((a_rows - 1) * p.lda + a_cols)), kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(p.B), (short)0, (int)(4 * b_rows * p.ldb), kRawBufferWord3);
+        const_cast<float*>(p.B), (short)0, (int)(4 * ((b_rows - 1) * p.ldb + b_cols)), kRawBufferWord3);
     auto copy = [&](int j, int k0, int buf) __attribute__((always_inline)) {
         if (j < A_COPIES) {
             const int soff = TA::phase_bytes(k0, p.lda);
@@ -309,25 +317,28 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     steps012(no{}, 0, 0);
     step(1, no{}, 0, c0{}, c0{}, 0, 0);
 
-    // Store (the launcher passes full tiles only).  Register r of lane
-    // (li, lh) is row rho = 8 (r / 4) + 4 lh + r % 4 and column li of its
-    // 32 x 32 block; block (i, j) of a k-contiguous A holds rows 32 i + rho of
-    // the wave's span, of an mn-contiguous A rows 4 rho + i; likewise for B's
-    // columns.  With B mn-contiguous the four blocks j of one row are four
-    // adjacent columns: one 128-bit store.
+    // Guarded store.  Register r of lane (li, lh) is row rho = 8 (r / 4) +
+    // 4 lh + r % 4 and column li of its 32 x 32 block; block (i, j) of a
+    // k-contiguous A holds rows 32 i + rho of the wave's span, of an
+    // mn-contiguous A rows 4 rho + i; likewise for B's columns.  With B
+    // mn-contiguous the four blocks j of one row are four adjacent columns:
+    // one 128-bit store (N is a multiple of 4, so all four are in or out).
+    const int col0 = n0 + wn * WN;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int rho = 8 * (r >> 2) + 4 * lh + (r & 3);
             const int row = m0 + wm * WM + (KCA ? 32 * i + rho : 4 * rho + i);
-            float* crow = p.C + (int64_t)row * p.ldc + n0 + wn * WN;
+            if (row >= p.M) continue;
+            float* crow = p.C + (int64_t)row * p.ldc + col0;
             if constexpr (!KCB) {
                 const floatx4 v = {acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
-                *reinterpret_cast<floatx4*>(crow + 4 * li) = v;
+                if (col0 + 4 * li < p.N) *reinterpret_cast<floatx4*>(crow + 4 * li) = v;
             } else {
 #pragma unroll
-                for (int j = 0; j < FN; ++j) crow[32 * j + li] = acc[i][j][r];
+                for (int j = 0; j < FN; ++j)
+                    if (col0 + 32 * j + li < p.N) crow[32 * j + li] = acc[i][j][r];
             }
         }
 }
@@ -342,20 +353,21 @@ hipError_t launch_sched_f32_kernel(const GemmArgs& p, hipStream_t s, int tiles_m
 
 }  // namespace
 
-// Any leading dimension and dword alignment will do: gfx9 runs memory in
-// unaligned-access mode, so the 16-byte copies and stores need only the
-// 4-byte alignment the entry points check.
+// K a multiple of 32 and M, N multiples of 4 (edge tiles run whole, see the
+// descriptors above).  Any leading dimension and dword alignment will do:
+// gfx9 runs memory in unaligned-access mode, so the 16-byte copies and
+// stores need only the 4-byte alignment the entry points check.
 bool sched_f32_fits(const GemmArgs& p, int op_a, int op_b) {
-    if (p.M % 256 != 0 || p.N % 256 != 0 || p.K % kSBK != 0 || p.K <= 0) return false;
+    if (p.K % kSBK != 0 || p.K <= 0 || p.M % 4 != 0 || p.N % 4 != 0) return false;
     // A stored M x K (op N) or K x M (op T); B stored K x N or N x K.  Byte
-    // offsets of both stay below 2^31.
+    // offsets, edge tiles' overhang included, stay below 2^31.
     const int64_t a_rows = op_a ? p.K : p.M, b_rows = op_b ? p.N : p.K;
     const int64_t lim = (int64_t)1 << 31;
-    return 4 * a_rows * p.lda < lim && 4 * b_rows * p.ldb < lim;
+    return 4 * (a_rows + 256) * p.lda < lim && 4 * (b_rows + 256) * p.ldb < lim;
 }
 
 hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m) {
-    const int tiles_m = p.M / 256, tiles_n = p.N / 256;
+    const int tiles_m = ceil_div(p.M, 256), tiles_n = ceil_div(p.N, 256);
     const unsigned blocks = (unsigned)((int64_t)tiles_m * tiles_n);
     switch (2 * (op_a ? 1 : 0) + (op_b ? 1 : 0)) {
         case 0: return launch_sched_f32_kernel<true, false>(p, s, tiles_m, tiles_n, group_m, blocks);

@@ -263,7 +263,7 @@ def test_mixed_op_validation_without_launch(lib, op_a, op_b, args, code):
 def test_default_variant_choices(binding):
     """The configuration the default entry points run, by problem size (no
     device needed): 256 x 256 tiles once there are 256 of them (on four
-    scheduled waves when M and N are multiples of 256 and K of 32, else on
+    scheduled waves when K is a multiple of 32 and M and N of 4, else on
     eight), 128 x 128 tiles when they fill whole rounds of 256 blocks, else
     64 x 64 tiles whose phases are split over four wave groups (32-deep
     phases for at most 256 tiles); for the 16-bit product the scheduled
@@ -277,6 +277,8 @@ def test_default_variant_choices(binding):
         (4096, 4096, 48): "mfma256x256_bk32_w2x4_direct",
         (4100, 4097, 515): "mfma256x256_bk32_w2x4_direct",
         (4352, 4096, 4096): "mfma256x256_bk32_w2x2_sched",
+        (4100, 4104, 4096): "mfma256x256_bk32_w2x2_sched",
+        (4098, 4096, 64): "mfma256x256_bk32_w2x4_direct",
         (4096, 4097, 4096): "mfma256x256_bk32_w2x4_direct",
         (4096, 4096, 0): "mfma256x256_bk32_w2x4_direct",
         (2048, 2048, 2048): "mfma128x128_bk16_w2x2",

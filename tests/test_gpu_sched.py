@@ -1,5 +1,6 @@
 """The four-wave scheduled fp32 kernel, which gemm_f32 and gemm_f32_op run
-when M and N are multiples of 256 and K of 32 (with 256 or more tiles).
+when K is a multiple of 32 and M and N of 4 (with 256 or more 256 x 256
+tiles; edge tiles run whole and store only what lies inside C).
 
 Checked against the oracle (every entry on a K = 32 problem, sampled entries
 on longer ones; exact on integer inputs) for all four op pairs, on aligned
@@ -68,10 +69,10 @@ class Problem:
         return out.cpu().numpy()
 
 
-def test_scheduled_kernel_is_the_default_for_full_tiles():
-    for shape in [(4096, 4096, 32), (4096, 4352, 96), (8192, 8192, 8192)]:
+def test_scheduled_kernel_is_the_default_for_its_shapes():
+    for shape in [(4096, 4096, 32), (4096, 4352, 96), (8192, 8192, 8192), (4100, 4132, 64)]:
         assert binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(*shape)) == SCHED
-    for shape in [(4096, 4096, 33), (4100, 4096, 64), (4096, 4097, 64)]:
+    for shape in [(4096, 4096, 33), (4098, 4096, 64), (4096, 4097, 64)]:
         assert binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(*shape)) == EIGHT_WAVE
 
 
@@ -79,15 +80,16 @@ def test_scheduled_kernel_is_the_default_for_full_tiles():
 @pytest.mark.parametrize("dist", ["int", "uniform"])
 def test_scheduled_full_oracle(ops, dist):
     """K = 32 (one phase, the prologue and the peeled last steps only) and
-    K = 64 (two phases) against the whole oracle product."""
+    K = 64 (two phases) against the whole oracle product, on full tiles and
+    with edge tiles in both dimensions (M and N not multiples of 256)."""
     op_a, op_b = ops
-    for K in (32, 64):
-        prob = Problem(op_a, op_b, 4096, 4096, K, dist, [K, len(op_a + op_b), dist == "int", ord(op_a[0])])
+    for (M, N, K) in ((4096, 4096, 32), (4096, 4096, 64), (4100, 4132, 32), (4356, 4004, 64)):
+        prob = Problem(op_a, op_b, M, N, K, dist, [M, N, K, len(op_a + op_b), dist == "int", ord(op_a[0])])
         Cref, S = oracle.gemm(prob.A.view, prob.B.view, op_a=op_a, op_b=op_b, threads=8)
-        say(f"sched full oracle {op_a}{op_b} {dist} K={K}")
+        say(f"sched full oracle {op_a}{op_b} {dist} {(M, N, K)}")
         C = prob.run()
         check_padding_untouched(C)
-        what = f"sched {op_a}{op_b} {dist} K={K}"
+        what = f"sched {op_a}{op_b} {dist} {(M, N, K)}"
         if dist == "int":
             check_exact(C.view, Cref, what)
         else:
@@ -100,6 +102,9 @@ SAMPLED = [
     ((4096, 4352, 96), 0, (0, 0, 0)),
     ((4352, 4096, 544), 1, (3, 5, 7)),
     ((4096, 4096, 256), 3, (1, 2, 1)),
+    # edge tiles: M and N not multiples of 256, padded and dword-offset
+    ((4132, 4356, 160), 1, (3, 5, 7)),
+    ((4500, 3996, 96), 0, (0, 0, 0)),
 ]
 
 
