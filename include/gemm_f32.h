@@ -81,11 +81,13 @@ extern "C" {
  *      outputs per thread in registers, two LDS buffers and one barrier per
  *      phase, next tile prefetched into registers during the current phase
  *   3  MFMA: v_mfma_f32_32x32x2_f32 matrix-core contraction on double-
- *      buffered LDS tiles (the default).  Large problems use 256 x 256 tiles
- *      with direct global-to-LDS copies into an XOR-swizzled layout: on four
- *      waves with a fixed instruction order when K is a multiple of 32 and
- *      M and N of 4 (and each stored factor is under 2 GiB), else on eight
- *      waves; both give the same bits
+ *      buffered LDS tiles (the default).  The tile follows from how full the
+ *      last round of 256 workgroups would run: 256 x 256 tiles with direct
+ *      global-to-LDS copies into an XOR-swizzled layout (on four waves with
+ *      a fixed instruction order when K is a multiple of 32 and M and N of 4
+ *      and each stored factor is under 2 GiB, else on eight waves; both give
+ *      the same bits), else 128 x 128 tiles, else 64 x 64 tiles whose phases
+ *      are split over four groups of four waves
  * Variants numbered from 16 up are diagnostic layouts of the same rungs, kept
  * so that their hardware counters can be compared; see
  * gemm_f32_variant_name().

@@ -639,27 +639,31 @@ constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 int mfma_num_configs() { return kNumConfigs; }
 const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConfigs[c].name : nullptr; }
 
-// Largest tile that still gives every CU at least one workgroup: 256 x 256
-// once there are 256 such tiles -- on four waves with a fixed instruction
-// order (mfma_sched.hip) when K is a multiple of 32 and M and N of 4 (the
-// launcher falls back to the eight-wave kernel for stored factors of 2 GiB
-// or more), else on eight waves (two per SIMD, so one wave's
-// barrier or LDS wait is covered by the other's matrix instructions) with
-// direct global -> LDS copies and ghost phases at the edges.  Below that, 128 x 128 tiles when
-// they come in whole rounds of 256 (every CU busy to the end), else 64 x 64
-// tiles with the phases of each tile split over four groups of four waves
-// (16 waves per workgroup to hide latency; 32-deep phases when there are at
-// most 256 such tiles, 16-deep otherwise).  Measured at 512^3 .. 3584^3 and
-// on rectangular shapes, each choice within 2 % of the fastest
-// configuration.  Every picked configuration is built for all four op
-// combinations.
+// Tile choice by how full the last round of 256 workgroups (one per CU)
+// runs.  256 x 256 tiles when there are at least 256 of them and their last
+// round is at least 80 % full (75 % when 128 x 128 tiles would not fill
+// theirs to 90 % either) -- on four waves with a fixed instruction order
+// (mfma_sched.hip) when K is a multiple of 32 and M and N of 4 (the launcher
+// falls back to the eight-wave kernel for stored factors of 2 GiB or more),
+// else on eight waves (two per SIMD, so one wave's barrier or LDS wait is
+// covered by the other's matrix instructions) with direct global -> LDS
+// copies and ghost phases at the edges.  Else 128 x 128 tiles when at least
+// 256 of them fill their rounds to 90 %, else 64 x 64 tiles with the phases
+// of each tile split over four groups of four waves (16 waves per workgroup
+// to hide latency; 32-deep phases when there are at most 256 such tiles,
+// 16-deep otherwise).  A shape just past a round (4100^2: 289 tiles of 256,
+// the second round nearly empty) runs faster on smaller tiles: 107 against
+// 76 TFLOP/s there, 119 against 91 at 6000^3.  Every picked configuration
+// is built for all four op combinations.
 int mfma_pick_config(int M, int N, int K) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
     const int64_t t64 = (int64_t)ceil_div(M, 64) * ceil_div(N, 64);
-    if (t256 >= 256) return (K % 32 == 0 && K > 0 && M % 4 == 0 && N % 4 == 0) ? 16 : 7;
-    const int64_t rounds128 = (t128 + 255) / 256;
-    if (t128 >= 256 && t128 * 10 >= rounds128 * 256 * 9) return 1;
+    const int64_t slots256 = (t256 + 255) / 256 * 256, slots128 = (t128 + 255) / 256 * 256;
+    const bool fill128 = t128 * 10 >= slots128 * 9;
+    if (t256 >= 256 && (t256 * 10 >= slots256 * 8 || (t256 * 4 >= slots256 * 3 && !fill128)))
+        return (K % 32 == 0 && K > 0 && M % 4 == 0 && N % 4 == 0) ? 16 : 7;
+    if (t128 >= 256 && fill128) return 1;
     return t64 <= 256 ? 14 : 13;
 }
 

@@ -1,6 +1,7 @@
 """The four-wave scheduled fp32 kernel, which gemm_f32 and gemm_f32_op run
-when K is a multiple of 32 and M and N of 4 (with 256 or more 256 x 256
-tiles; edge tiles run whole and store only what lies inside C).
+when K is a multiple of 32 and M and N of 4 and the 256 x 256 tiles fill
+their last round of 256 to at least 80 % (edge tiles run whole and store
+only what lies inside C).
 
 Checked against the oracle (every entry on a K = 32 problem, sampled entries
 on longer ones; exact on integer inputs) for all four op pairs, on aligned
@@ -70,9 +71,9 @@ class Problem:
 
 
 def test_scheduled_kernel_is_the_default_for_its_shapes():
-    for shape in [(4096, 4096, 32), (4096, 4352, 96), (8192, 8192, 8192), (4100, 4132, 64)]:
+    for shape in [(4096, 4096, 32), (4096, 8192, 96), (8192, 8192, 8192), (4100, 6200, 32), (4356, 5800, 64)]:
         assert binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(*shape)) == SCHED
-    for shape in [(4096, 4096, 33), (4098, 4096, 64), (4096, 4097, 64)]:
+    for shape in [(4096, 4096, 33), (8194, 8192, 64), (8192, 8193, 64)]:
         assert binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(*shape)) == EIGHT_WAVE
 
 
@@ -83,7 +84,7 @@ def test_scheduled_full_oracle(ops, dist):
     K = 64 (two phases) against the whole oracle product, on full tiles and
     with edge tiles in both dimensions (M and N not multiples of 256)."""
     op_a, op_b = ops
-    for (M, N, K) in ((4096, 4096, 32), (4096, 4096, 64), (4100, 4132, 32), (4356, 4004, 64)):
+    for (M, N, K) in ((4096, 4096, 32), (4096, 4096, 64), (4100, 6200, 32), (4356, 5800, 64)):
         prob = Problem(op_a, op_b, M, N, K, dist, [M, N, K, len(op_a + op_b), dist == "int", ord(op_a[0])])
         Cref, S = oracle.gemm(prob.A.view, prob.B.view, op_a=op_a, op_b=op_b, threads=8)
         say(f"sched full oracle {op_a}{op_b} {dist} {(M, N, K)}")
@@ -99,12 +100,12 @@ def test_scheduled_full_oracle(ops, dist):
 
 SAMPLED = [
     # shape, offset, (pad A, pad B, pad C): aligned, then dword-offset and padded
-    ((4096, 4352, 96), 0, (0, 0, 0)),
-    ((4352, 4096, 544), 1, (3, 5, 7)),
+    ((4096, 8192, 96), 0, (0, 0, 0)),
+    ((8192, 4096, 544), 1, (3, 5, 7)),
     ((4096, 4096, 256), 3, (1, 2, 1)),
     # edge tiles: M and N not multiples of 256, padded and dword-offset
-    ((4132, 4356, 160), 1, (3, 5, 7)),
-    ((4500, 3996, 96), 0, (0, 0, 0)),
+    ((4100, 6200, 160), 1, (3, 5, 7)),
+    ((6396, 4100, 96), 0, (0, 0, 0)),
 ]
 
 
