@@ -43,6 +43,8 @@ const Diagnostic kDiagnostics[] = {
     {"mfma256x256_bk32_w2x4_direct_mi16", 3, 15},
     {"mfma256x256_bk32_w2x2_sched", 3, 16},
     {"mfma256x256_bk32_w2x2_sched_g4", 3, 17},
+    {"mfma128x128_bk32_w2x2_sched", 3, 18},
+    {"mfma128x128_bk32_w2x2_sched_g16", 3, 19},
 };
 constexpr int kNumDiagnostics = (int)(sizeof(kDiagnostics) / sizeof(kDiagnostics[0]));
 

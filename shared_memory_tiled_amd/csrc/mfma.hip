@@ -579,12 +579,23 @@ hipError_t launch_splitk(const GemmArgs& p, hipStream_t s, int tiles_m, int tile
 template <bool TRA, bool TRB>
 hipError_t launch_sched_or_direct(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
                                   unsigned blocks) {
-    if (sched_f32_fits(p, TRA, TRB)) return launch_sched_f32(p, s, TRA, TRB, group_m);
+    if (sched_f32_fits(p, TRA, TRB)) return launch_sched_f32(p, s, TRA, TRB, group_m, 256);
     return launch_one<256, 256, 32, 2, 4, true, 64, TRA, TRB>(p, s, tiles_m, tiles_n, 8, blocks);
 }
 #define SCHED_OPS                                                                      \
     {launch_sched_or_direct<false, false>, launch_sched_or_direct<false, true>,          \
      launch_sched_or_direct<true, false>, launch_sched_or_direct<true, true>}
+// The same schedule on 128 x 128 tiles, else the register-staged 128 x 128
+// kernel.
+template <bool TRA, bool TRB>
+hipError_t launch_sched128_or_staged(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                                     unsigned blocks) {
+    if (sched_f32_fits(p, TRA, TRB)) return launch_sched_f32(p, s, TRA, TRB, group_m, 128);
+    return launch_one<128, 128, 16, 2, 2, false, 64, TRA, TRB>(p, s, tiles_m, tiles_n, 8, blocks);
+}
+#define SCHED128_OPS                                                                         \
+    {launch_sched128_or_staged<false, false>, launch_sched128_or_staged<false, true>,          \
+     launch_sched128_or_staged<true, false>, launch_sched128_or_staged<true, true>}
 
 // NN only (diagnostic layouts) or all four op combinations.
 #define NN_ONLY(BM, BN, BK, WM, WN, D, S) \
@@ -627,11 +638,14 @@ const MfmaConfig kConfigs[] = {
     // four waves of 128 x 128, instruction order fixed by the kernel
     {"mfma256x256_bk32_w2x2_sched", 256, 256, 256, 8, SCHED_OPS},
     {"mfma256x256_bk32_w2x2_sched_g4", 256, 256, 256, 4, SCHED_OPS},
+    {"mfma128x128_bk32_w2x2_sched", 128, 128, 256, 8, SCHED128_OPS},
+    {"mfma128x128_bk32_w2x2_sched_g16", 128, 128, 256, 16, SCHED128_OPS},
 };
 #undef NN_ONLY
 #undef ALL_OPS
 #undef ALL_OPS_MI16
 #undef SCHED_OPS
+#undef SCHED128_OPS
 #undef SPLITK_OPS
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 }  // namespace
@@ -639,32 +653,33 @@ constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 int mfma_num_configs() { return kNumConfigs; }
 const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConfigs[c].name : nullptr; }
 
-// Tile choice by how full the last round of 256 workgroups (one per CU)
-// runs.  256 x 256 tiles when there are at least 256 of them and their last
-// round is at least 80 % full (75 % when 128 x 128 tiles would not fill
-// theirs to 90 % either) -- on four waves with a fixed instruction order
-// (mfma_sched.hip) when K is a multiple of 32 and M and N of 4 (the launcher
-// falls back to the eight-wave kernel for stored factors of 2 GiB or more),
-// else on eight waves (two per SIMD, so one wave's barrier or LDS wait is
-// covered by the other's matrix instructions) with direct global -> LDS
-// copies and ghost phases at the edges.  Else 128 x 128 tiles when at least
-// 256 of them fill their rounds to 90 %, else 64 x 64 tiles with the phases
-// of each tile split over four groups of four waves (16 waves per workgroup
-// to hide latency; 32-deep phases when there are at most 256 such tiles,
-// 16-deep otherwise).  A shape just past a round (4100^2: 289 tiles of 256,
-// the second round nearly empty) runs faster on smaller tiles: 107 against
-// 76 TFLOP/s there, 119 against 91 at 6000^3.  Every picked configuration
-// is built for all four op combinations.
+// Tile choice.  Shapes the four-wave schedule takes (mfma_sched.hip: K a
+// multiple of 32, M and N of 4): 256 x 256 tiles when there are at least
+// 256 of them and their rounds of 256 workgroups (one per CU) run at least
+// 95 % full, else its 128 x 128 tiles (two workgroups per CU) when there are
+// at least 128, else the split-phase 64 x 64 tiles.  Other shapes: 256 x
+// 256 tiles on eight waves (direct copies, ghost phases at the edges) when
+// their rounds run at least 80 % full (75 % when 128 x 128 tiles would not
+// fill theirs to 90 % either), else register-staged 128 x 128 tiles when at
+// least 256 of them fill their rounds to 90 %, else 64 x 64 tiles with the
+// phases of each tile split over four groups of four waves (16 waves per
+// workgroup to hide latency; 32-deep phases when there are at most 256 such
+// tiles, 16-deep otherwise).  Every picked configuration is built for all
+// four op combinations.
 int mfma_pick_config(int M, int N, int K) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
     const int64_t t64 = (int64_t)ceil_div(M, 64) * ceil_div(N, 64);
     const int64_t slots256 = (t256 + 255) / 256 * 256, slots128 = (t128 + 255) / 256 * 256;
+    const int small = t64 <= 256 ? 14 : 13;
+    if (K % 32 == 0 && K > 0 && M % 4 == 0 && N % 4 == 0) {
+        if (t256 >= 256 && t256 * 20 >= slots256 * 19) return 16;
+        return t128 >= 128 ? 18 : small;
+    }
     const bool fill128 = t128 * 10 >= slots128 * 9;
-    if (t256 >= 256 && (t256 * 10 >= slots256 * 8 || (t256 * 4 >= slots256 * 3 && !fill128)))
-        return (K % 32 == 0 && K > 0 && M % 4 == 0 && N % 4 == 0) ? 16 : 7;
+    if (t256 >= 256 && (t256 * 10 >= slots256 * 8 || (t256 * 4 >= slots256 * 3 && !fill128))) return 7;
     if (t128 >= 256 && fill128) return 1;
-    return t64 <= 256 ? 14 : 13;
+    return small;
 }
 
 // hipErrorInvalidValue: the grid would exceed the launch limits.

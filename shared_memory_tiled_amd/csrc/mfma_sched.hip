@@ -49,8 +49,6 @@ namespace gemmf32 {
 namespace {
 
 constexpr int kSBK = 32;                 // k values per phase
-constexpr int kSTile = 256 * kSBK;       // floats per tile stage
-constexpr int kStageBytes = 4 * kSTile;  // 32 KB
 
 __host__ __device__ constexpr int sched_swz(int r) { return (r >> 1) & 7; }
 
@@ -65,10 +63,15 @@ __device__ __forceinline__ void unroll(F&& f) {
     unroll_seq(f, std::make_integer_sequence<int, N>{});
 }
 
-// 16 bytes of LDS at a byte address.
+// 16 and 8 bytes of LDS at a byte address.
 __device__ __forceinline__ floatx4 lds_read128(uint32_t lds_byte_addr) {
     typedef const __attribute__((address_space(3))) floatx4 lds_floatx4;
     return *(lds_floatx4*)(uintptr_t)lds_byte_addr;
+}
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ floatx2 lds_read64(uint32_t lds_byte_addr) {
+    typedef const __attribute__((address_space(3))) floatx2 lds_floatx2;
+    return *(lds_floatx2*)(uintptr_t)lds_byte_addr;
 }
 
 // Byte address inside LDS of a pointer into a __shared__ array.
@@ -83,12 +86,21 @@ __device__ __forceinline__ void wait_tied(floatx4 (&x)[4]) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : : "memory");
 }
 
-// One factor's tile.  KC: stored k-contiguous.
-template <bool KC>
+// One factor's tile: MNT (256 or 128) rows or columns of op(X) by 32 k per
+// stage; each wave holds F (4 or 2) blocks of 32 of it.  KC: stored
+// k-contiguous.
+template <bool KC, int MNT, int F>
 struct SchedTileF32 {
-    // First float, inside the tile stage, that copy j (0..7) of wave w fills.
+    static_assert((MNT == 256 || MNT == 128) && (F == 4 || F == 2), "tile shape");
+    static constexpr int WORDS = MNT * kSBK;              // floats per stage
+    static constexpr int COPIES = MNT / 32;               // 1 KB copies per wave and phase
+    static constexpr int RPC = KC ? 8 : 256 / MNT;        // stored rows per copy
+    static constexpr int READS = KC ? F : 4;              // LDS reads per step
+    static constexpr bool IS_KC = KC;
+    static constexpr int FV = F;
+    // First float, inside the tile stage, that copy j of wave w fills.
     __host__ __device__ static int copy_dst(int w, int j) {
-        return KC ? 8 * (w + 4 * j) * kSBK : (w + 4 * j) * 256;
+        return KC ? 8 * (w + 4 * j) * kSBK : RPC * (w + 4 * j) * MNT;
     }
     // Byte offset of lane l's 16 bytes of copy j from the stored matrix's
     // base at k = 0 (mn0: the tile's first row or column of op(X)).
@@ -97,25 +109,26 @@ struct SchedTileF32 {
             const int row = 8 * (w + 4 * j) + lane / 8;
             return 4u * (uint32_t)((mn0 + row) * ld + 4 * ((lane % 8) ^ sched_swz(row)));
         } else {
-            const int row = w + 4 * j;
-            return 4u * (uint32_t)(row * ld + mn0 + 4 * lane);
+            constexpr int LPR = 64 / RPC;                   // lanes per stored row
+            const int row = RPC * (w + 4 * j) + lane / LPR;
+            return 4u * (uint32_t)(row * ld + mn0 + 4 * (lane % LPR));
         }
     }
     // Byte offset of the phase at k0 from the phase at 0.
     __host__ __device__ static int phase_bytes(int k0, int64_t ld) { return KC ? 4 * k0 : 4 * k0 * (int)ld; }
     // LDS byte offset, inside stage 0 of this factor, of lane (li, lh)'s read
-    // i (0..3) of step s for the wave whose 128-wide span starts at mn:
-    //   KC: block i's row mn + 32 i + li, logical chunk 2 s + lh;
-    //   MC: k row 8 s + 4 lh + i, columns mn + 4 li .. + 3.
+    // i of step s for the wave whose span of 32 F starts at mn:
+    //   KC: block i's row mn + 32 i + li, logical chunk 2 s + lh (128 bits);
+    //   MC: k row 8 s + 4 lh + i, columns mn + F li .. + F - 1 (F values).
     // Either way a per-lane base plus a compile-time part (4096 i for KC, as
-    // the swizzle of row mn + 32 i + li depends on li only; 8192 s + 1024 i
+    // the swizzle of row mn + 32 i + li depends on li only; 4 MNT (8 s + i)
     // for MC).
     __host__ __device__ static uint32_t read_base(int mn, int s, int li, int lh) {
         return KC ? 4u * (uint32_t)((mn + li) * kSBK + 4 * ((2 * s + lh) ^ sched_swz(li)))
-                  : 4u * (uint32_t)(4 * lh * 256 + mn + 4 * li);
+                  : 4u * (uint32_t)(4 * lh * MNT + mn + F * li);
     }
     __host__ __device__ static constexpr uint32_t read_imm(int s, int i) {
-        return KC ? 4096u * (uint32_t)i : 8192u * (uint32_t)s + 1024u * (uint32_t)i;
+        return KC ? 4096u * (uint32_t)i : 4u * MNT * (uint32_t)(8 * s + i);
     }
 };
 
@@ -126,15 +139,22 @@ __device__ __forceinline__ float operand(const floatx4 (&x)[4], int f, int e) {
     return KC ? x[f][e] : x[e][f];
 }
 
-template <bool KCA, bool KCB>
+// FM x FN blocks of 32 x 32 per wave, 2 x 2 waves: 256 x 256 tiles (FM =
+// FN = 4) or 128 x 128 (FM = FN = 2).
+template <int FM, int FN, bool KCA, bool KCB>
 __global__ __launch_bounds__(256)
 void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
-    constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
-    using TA = SchedTileF32<KCA>;
-    using TB = SchedTileF32<KCB>;
-    constexpr int A_COPIES = 8, NCOPY = 16, NREAD = 8;
+    constexpr int WM = 32 * FM, WN = 32 * FN, BM = 2 * WM, BN = 2 * WN;
+    using TA = SchedTileF32<KCA, BM, FM>;
+    using TB = SchedTileF32<KCB, BN, FN>;
+    constexpr int A_COPIES = TA::COPIES, NCOPY = TA::COPIES + TB::COPIES, HALF = NCOPY / 2;
+    constexpr int NREAD = TA::READS + TB::READS;
+    constexpr int NMFMA = 4 * FM * FN;                    // matrix instructions per step
+    constexpr int CSTRIDE = NMFMA / HALF;                 // a copy after every CSTRIDE-th of them
+    static_assert(NCOPY % 2 == 0 && NREAD <= NMFMA && CSTRIDE >= 1, "schedule");
+    constexpr int A_ST = TA::WORDS, B_ST = TB::WORDS;
     // A stage 0, A stage 1, B stage 0, B stage 1.
-    __shared__ __attribute__((aligned(16))) float lds[4 * kSTile];
+    __shared__ __attribute__((aligned(16))) float lds[2 * (A_ST + B_ST)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -176,13 +196,13 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         if (j < A_COPIES) {
             const int soff = TA::phase_bytes(k0, p.lda);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc_a, (__attribute__((address_space(3))) void*)(lds + buf * kSTile + TA::copy_dst(wave_u, j)), 16,
+                rsrc_a, (__attribute__((address_space(3))) void*)(lds + buf * A_ST + TA::copy_dst(wave_u, j)), 16,
                 (int)doff[j], soff, 0, 0);
         } else {
             const int soff = TB::phase_bytes(k0, p.ldb);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc_b,
-                (__attribute__((address_space(3))) void*)(lds + (2 + buf) * kSTile + TB::copy_dst(wave_u, j - A_COPIES)),
+                (__attribute__((address_space(3))) void*)(lds + 2 * A_ST + buf * B_ST + TB::copy_dst(wave_u, j - A_COPIES)),
                 16, (int)doff[j], soff, 0, 0);
         }
     };
@@ -194,7 +214,7 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
     for (int s = 0; s < SA; ++s) abase[s] = lds0 + TA::read_base(wm * WM, s, li, lh);
 #pragma unroll
-    for (int s = 0; s < SB; ++s) bbase[s] = lds0 + 2u * kStageBytes + TB::read_base(wn * WN, s, li, lh);
+    for (int s = 0; s < SB; ++s) bbase[s] = lds0 + 8u * A_ST + TB::read_base(wn * WN, s, li, lh);
 
     floatx4 a[2][4], b[2][4];
     // Read i (0..7) of step s into set t, A's four first, from the stage the
@@ -204,17 +224,31 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     // matrix ones, not one per read: each placed between two matrix
     // instructions was measured to cost the matrix core about 14 cycles
     // (scalar ones cost nothing).
+    // An mn-contiguous read of F = 2 values fills the first two of each
+    // fragment slot (the operand picks only those).
+    auto read_one = [&](auto tile, floatx4 (&x)[4], uint32_t base, int s, int i) __attribute__((always_inline)) {
+        using T = decltype(tile);
+        const uint32_t addr = base + T::read_imm(s, i);
+        if constexpr (T::IS_KC || T::FV == 4) {
+            x[i] = lds_read128(addr);
+        } else {
+            const floatx2 v = lds_read64(addr);
+            x[i][0] = v[0];
+            x[i][1] = v[1];
+        }
+    };
     auto read_op = [&](int s, int t, int i) __attribute__((always_inline)) {
-        if (i < 4) a[t][i] = lds_read128(abase[KCA ? s : 0] + TA::read_imm(s, i));
-        else b[t][i - 4] = lds_read128(bbase[KCB ? s : 0] + TB::read_imm(s, i - 4));
+        if (i < TA::READS) read_one(TA{}, a[t], abase[KCA ? s : 0], s, i);
+        else read_one(TB{}, b[t], bbase[KCB ? s : 0], s, i - TA::READS);
     };
     // Point the read bases at the other stage (from stage cur to cur ^ 1).
     auto flip_stage = [&](int cur) __attribute__((always_inline)) {
-        const uint32_t d = cur ? (uint32_t)-kStageBytes : (uint32_t)kStageBytes;
+        const uint32_t da = cur ? (uint32_t)(-4 * A_ST) : (uint32_t)(4 * A_ST);
+        const uint32_t db = cur ? (uint32_t)(-4 * B_ST) : (uint32_t)(4 * B_ST);
 #pragma unroll
-        for (int s = 0; s < SA; ++s) abase[s] += d;
+        for (int s = 0; s < SA; ++s) abase[s] += da;
 #pragma unroll
-        for (int s = 0; s < SB; ++s) bbase[s] += d;
+        for (int s = 0; s < SB; ++s) bbase[s] += db;
     };
 
     floatx16 acc[FM][FN];
@@ -225,17 +259,18 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // One step: the 64 matrix instructions on fragment set t (instruction q:
-    // e = q / 16, block (q / 4 % 4, q % 4)); after the q-th (q < 8), read q of
-    // step rs into set t ^ 1 (if R) and, after every eighth,
-    // copy CB + q / 8 (while below CE) of the phase at k_copy into stage cbuf.
+    // One step: the 4 FM FN matrix instructions on fragment set t
+    // (instruction q: e = q / (FM FN), block (q / FN % FM, q % FN)); after the
+    // q-th (q < NREAD), read q of step rs into set t ^ 1 (if R) and, after
+    // every CSTRIDE-th, copy CB + q / CSTRIDE (while below CE) of the phase at
+    // k_copy into stage cbuf.
     auto step = [&](int t, auto reads, int rs, auto cb, auto ce, int k_copy,
                     int cbuf) __attribute__((always_inline)) {
         constexpr bool R = decltype(reads)::value;
         constexpr int CB = decltype(cb)::value, CE = decltype(ce)::value;
-        unroll<64>([&](auto qc) __attribute__((always_inline)) {
+        unroll<NMFMA>([&](auto qc) __attribute__((always_inline)) {
             constexpr int q = decltype(qc)::value;
-            constexpr int e = q / 16, i = (q / 4) % 4, j = q % 4;
+            constexpr int e = q / (FM * FN), i = (q / FN) % FM, j = q % FN;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(operand<KCA>(a[t], i, e),
                                                              operand<KCB>(b[t], j, e), acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -243,8 +278,8 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
                 read_op(rs, t ^ 1, q);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (q % 8 == 7 && CB + q / 8 < CE) {
-                copy(CB + q / 8, k_copy, cbuf);
+            if constexpr (q % CSTRIDE == CSTRIDE - 1 && CB + q / CSTRIDE < CE) {
+                copy(CB + q / CSTRIDE, k_copy, cbuf);
                 __builtin_amdgcn_sched_barrier(0);
             }
         });
@@ -263,15 +298,15 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     using yes = std::true_type;
     using no = std::false_type;
     using c0 = std::integral_constant<int, 0>;
-    using c8 = std::integral_constant<int, 8>;
-    using c16 = std::integral_constant<int, 16>;
+    using cH = std::integral_constant<int, HALF>;
+    using cN = std::integral_constant<int, NCOPY>;
     // Steps 0..2 of the phase (step 0's fragments already read) and the wait
     // for step 3's; copies 8..15 of the phase at k_copy into stage cbuf with
     // step 0 if WC.
     auto steps012 = [&](auto wc, int k_copy, int cbuf) __attribute__((always_inline)) {
         constexpr bool WC = decltype(wc)::value;
         wait_set(0);
-        if constexpr (WC) step(0, yes{}, 1, c8{}, c16{}, k_copy, cbuf);
+        if constexpr (WC) step(0, yes{}, 1, cH{}, cN{}, k_copy, cbuf);
         else step(0, yes{}, 1, c0{}, c0{}, 0, 0);
         wait_set(1);
         step(1, yes{}, 2, c0{}, c0{}, 0, 0);
@@ -303,7 +338,7 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         flip_stage(cur);
         __builtin_amdgcn_sched_barrier(0);
         barrier();
-        step(1, yes{}, 0, c0{}, c8{}, (ph + 2) * kSBK, cur);
+        step(1, yes{}, 0, c0{}, cH{}, (ph + 2) * kSBK, cur);
     }
     if (ph + 1 < P) {
         const int cur = ph & 1;
@@ -320,21 +355,28 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     // Guarded store.  Register r of lane (li, lh) is row rho = 8 (r / 4) +
     // 4 lh + r % 4 and column li of its 32 x 32 block; block (i, j) of a
     // k-contiguous A holds rows 32 i + rho of the wave's span, of an
-    // mn-contiguous A rows 4 rho + i; likewise for B's columns.  With B
-    // mn-contiguous the four blocks j of one row are four adjacent columns:
-    // one 128-bit store (N is a multiple of 4, so all four are in or out).
+    // mn-contiguous A rows FM rho + i; likewise for B's columns.  With B
+    // mn-contiguous the FN blocks j of one row are FN adjacent columns: one
+    // 128- or 64-bit store (N is a multiple of 4, so all are in or out).
     const int col0 = n0 + wn * WN;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int rho = 8 * (r >> 2) + 4 * lh + (r & 3);
-            const int row = m0 + wm * WM + (KCA ? 32 * i + rho : 4 * rho + i);
+            const int row = m0 + wm * WM + (KCA ? 32 * i + rho : FM * rho + i);
             if (row >= p.M) continue;
             float* crow = p.C + (int64_t)row * p.ldc + col0;
             if constexpr (!KCB) {
-                const floatx4 v = {acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
-                if (col0 + 4 * li < p.N) *reinterpret_cast<floatx4*>(crow + 4 * li) = v;
+                if (col0 + FN * li < p.N) {
+                    if constexpr (FN == 4) {
+                        const floatx4 v = {acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
+                        *reinterpret_cast<floatx4*>(crow + 4 * li) = v;
+                    } else {
+                        const floatx2 v = {acc[i][0][r], acc[i][1][r]};
+                        *reinterpret_cast<floatx2*>(crow + 2 * li) = v;
+                    }
+                }
             } else {
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
@@ -343,14 +385,26 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         }
 }
 
-template <bool KCA, bool KCB>
+template <int F, bool KCA, bool KCB>
 hipError_t launch_sched_f32_kernel(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
                                    unsigned blocks) {
-    hipLaunchKernelGGL((gemm_f32_sched_kernel<KCA, KCB>), dim3(blocks), dim3(256), 0, s, p, tiles_m, tiles_n,
+    hipLaunchKernelGGL((gemm_f32_sched_kernel<F, F, KCA, KCB>), dim3(blocks), dim3(256), 0, s, p, tiles_m, tiles_n,
                        group_m);
     return hipGetLastError();
 }
 
+template <int F>
+hipError_t launch_sched_f32_tile(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m) {
+    constexpr int T = 64 * F;
+    const int tiles_m = ceil_div(p.M, T), tiles_n = ceil_div(p.N, T);
+    const unsigned blocks = (unsigned)((int64_t)tiles_m * tiles_n);
+    switch (2 * (op_a ? 1 : 0) + (op_b ? 1 : 0)) {
+        case 0: return launch_sched_f32_kernel<F, true, false>(p, s, tiles_m, tiles_n, group_m, blocks);
+        case 1: return launch_sched_f32_kernel<F, true, true>(p, s, tiles_m, tiles_n, group_m, blocks);
+        case 2: return launch_sched_f32_kernel<F, false, false>(p, s, tiles_m, tiles_n, group_m, blocks);
+        default: return launch_sched_f32_kernel<F, false, true>(p, s, tiles_m, tiles_n, group_m, blocks);
+    }
+}
 }  // namespace
 
 // K a multiple of 32 and M, N multiples of 4 (edge tiles run whole, see the
@@ -366,15 +420,9 @@ bool sched_f32_fits(const GemmArgs& p, int op_a, int op_b) {
     return 4 * (a_rows + 256) * p.lda < lim && 4 * (b_rows + 256) * p.ldb < lim;
 }
 
-hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m) {
-    const int tiles_m = ceil_div(p.M, 256), tiles_n = ceil_div(p.N, 256);
-    const unsigned blocks = (unsigned)((int64_t)tiles_m * tiles_n);
-    switch (2 * (op_a ? 1 : 0) + (op_b ? 1 : 0)) {
-        case 0: return launch_sched_f32_kernel<true, false>(p, s, tiles_m, tiles_n, group_m, blocks);
-        case 1: return launch_sched_f32_kernel<true, true>(p, s, tiles_m, tiles_n, group_m, blocks);
-        case 2: return launch_sched_f32_kernel<false, false>(p, s, tiles_m, tiles_n, group_m, blocks);
-        default: return launch_sched_f32_kernel<false, true>(p, s, tiles_m, tiles_n, group_m, blocks);
-    }
+hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m, int tile) {
+    return tile == 128 ? launch_sched_f32_tile<2>(p, s, op_a, op_b, group_m)
+                       : launch_sched_f32_tile<4>(p, s, op_a, op_b, group_m);
 }
 
 }  // namespace gemmf32

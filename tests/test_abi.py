@@ -262,31 +262,34 @@ def test_mixed_op_validation_without_launch(lib, op_a, op_b, args, code):
 
 def test_default_variant_choices(binding):
     """The configuration the default entry points run, by problem size (no
-    device needed): 256 x 256 tiles when there are at least 256 of them and
-    their last round of 256 is at least 80 % full (on four scheduled waves
-    when K is a multiple of 32 and M and N of 4, else on eight), 128 x 128
-    tiles when at least 256 of them fill their rounds to 90 %, else 64 x 64
-    tiles whose phases are split over four wave groups (32-deep phases for
-    at most 256 tiles); for the 16-bit product the scheduled kernel, 128 x
-    128 direct copies or 64 x 64 tiles.  Invalid sizes give -1."""
+    device needed).  Shapes the four-wave schedule takes (K a multiple of 32,
+    M and N of 4): its 256 x 256 tiles when at least 256 of them fill their
+    rounds of 256 to 95 %, else its 128 x 128 tiles when there are at least
+    128, else the split-phase 64 x 64 tiles.  Other shapes: eight-wave 256 x
+    256 tiles when their rounds run at least 80 % full (75 % when 128 x 128
+    tiles would not fill theirs to 90 %), register-staged 128 x 128 tiles
+    when at least 256 of them fill their rounds to 90 %, else the split-phase
+    tiles (32-deep phases for at most 256 tiles).  For the 16-bit product the
+    scheduled kernel, 128 x 128 direct copies or 64 x 64 tiles.  Invalid
+    sizes give -1."""
     f32 = {
         (8192, 8192, 8192): "mfma256x256_bk32_w2x2_sched",
         (4096, 4096, 4096): "mfma256x256_bk32_w2x2_sched",
         (8192, 4096, 2048): "mfma256x256_bk32_w2x2_sched",
         (4096, 4096, 32): "mfma256x256_bk32_w2x2_sched",
-        (8200, 8200, 8192): "mfma256x256_bk32_w2x2_sched",       # 1089 tiles: 85 % of 5 rounds
-        (4100, 6200, 4096): "mfma256x256_bk32_w2x2_sched",       # 425 tiles: 83 % of 2 rounds
+        (7940, 8132, 32): "mfma256x256_bk32_w2x2_sched",         # 1024 tiles with edges
+        (8200, 8200, 8192): "mfma128x128_bk32_w2x2_sched",       # 1089 tiles of 256: 85 % of 5 rounds
+        (4100, 4104, 4096): "mfma128x128_bk32_w2x2_sched",
+        (4000, 5000, 4096): "mfma128x128_bk32_w2x2_sched",
+        (2048, 2048, 2048): "mfma128x128_bk32_w2x2_sched",
+        (1536, 1536, 1536): "mfma128x128_bk32_w2x2_sched",       # 144 tiles of 128
+        (1024, 1024, 1024): "mfma64x64_bk32_w2x2_k4",            # 64 tiles of 128
         (4096, 4096, 48): "mfma256x256_bk32_w2x4_direct",
         (8193, 8190, 96): "mfma256x256_bk32_w2x4_direct",
         (4096, 4096, 0): "mfma256x256_bk32_w2x4_direct",
-        (4100, 4104, 4096): "mfma64x64_bk16_w2x2_k4",            # 289 tiles of 256, 1089 of 128
-        (4352, 4096, 4096): "mfma64x64_bk16_w2x2_k4",
+        (6000, 6000, 6000): "mfma128x128_bk16_w2x2",             # K % 32 = 16; 2209 of 128 (96 %)
+        (3840, 2048, 100): "mfma128x128_bk16_w2x2",
         (4100, 4097, 515): "mfma64x64_bk16_w2x2_k4",
-        (6000, 6000, 6000): "mfma128x128_bk16_w2x2",             # 576 of 256 (75 %), 2209 of 128 (96 %)
-        (4000, 5000, 4096): "mfma128x128_bk16_w2x2",
-        (2048, 2048, 2048): "mfma128x128_bk16_w2x2",
-        (4096, 2048, 1024): "mfma128x128_bk16_w2x2",
-        (2560, 2560, 2560): "mfma64x64_bk16_w2x2_k4",
         (3000, 3000, 3000): "mfma64x64_bk16_w2x2_k4",
         (1000, 1000, 1000): "mfma64x64_bk32_w2x2_k4",
         (256, 256, 256): "mfma64x64_bk32_w2x2_k4",

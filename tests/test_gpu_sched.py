@@ -1,13 +1,15 @@
-"""The four-wave scheduled fp32 kernel, which gemm_f32 and gemm_f32_op run
-when K is a multiple of 32 and M and N of 4 and the 256 x 256 tiles fill
-their last round of 256 to at least 80 % (edge tiles run whole and store
-only what lies inside C).
+"""The four-wave scheduled fp32 kernel on 256 x 256 and 128 x 128 tiles,
+which gemm_f32 and gemm_f32_op run when K is a multiple of 32 and M and N of
+4 (the 256 x 256 form when its tiles fill their rounds of 256 workgroups to
+95 %, else the 128 x 128 form when there are at least 128 such tiles; edge
+tiles run whole and store only what lies inside C).
 
-Checked against the oracle (every entry on a K = 32 problem, sampled entries
-on longer ones; exact on integer inputs) for all four op pairs, on aligned
-and on padded, dword-offset operands, and bit for bit against the eight-wave
-256 x 256 kernel on explicitly transposed copies: both sum every entry's k
-terms in the same order."""
+Checked against the oracle (every entry on short-K problems, sampled
+entries on longer ones; exact on integer inputs) for all four op pairs, on
+aligned and on padded, dword-offset operands, and bit for bit against the
+kernel of the same tile size that other shapes use (eight-wave 256 x 256,
+register-staged 128 x 128) on explicitly transposed copies: all sum every
+entry's k terms in the same order."""
 from __future__ import annotations
 
 import numpy as np
@@ -21,8 +23,11 @@ from shared_memory_tiled_amd import binding, inputs
 pytestmark = pytest.mark.gpu
 
 OPS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
-SCHED = "mfma256x256_bk32_w2x2_sched"
-EIGHT_WAVE = "mfma256x256_bk32_w2x4_direct"
+# kernel -> (its configuration, the same-tile kernel it must match bit for bit)
+KERNELS = {
+    "tile256": ("mfma256x256_bk32_w2x2_sched", "mfma256x256_bk32_w2x4_direct"),
+    "tile128": ("mfma128x128_bk32_w2x2_sched", "mfma128x128_bk16_w2x2"),
+}
 
 
 def variant_number(name):
@@ -61,71 +66,90 @@ class Problem:
         torch.cuda.synchronize()
         return inputs.Padded(self.C_dev.cpu().numpy(), self.M, self.N, self.ldc, self.offset)
 
-    def eight_wave_bits(self):
-        """The eight-wave kernel on dense op(A), op(B) copies."""
+    def reference_bits(self, name):
+        """The named configuration on dense op(A), op(B) copies."""
         a = torch.from_numpy(np.ascontiguousarray(self.A.view if self.op_a == "N" else self.A.view.T)).cuda()
         b = torch.from_numpy(np.ascontiguousarray(self.B.view if self.op_b == "N" else self.B.view.T)).cuda()
-        out = binding.gemm(a, b, variant=variant_number(EIGHT_WAVE))
+        out = binding.gemm(a, b, variant=variant_number(name))
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
 
-def test_scheduled_kernel_is_the_default_for_its_shapes():
-    for shape in [(4096, 4096, 32), (4096, 8192, 96), (8192, 8192, 8192), (4100, 6200, 32), (4356, 5800, 64)]:
-        assert binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(*shape)) == SCHED
+def default_name(M, N, K):
+    return binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(M, N, K))
+
+
+def test_scheduled_kernels_are_the_default_for_their_shapes():
+    for shape in [(4096, 4096, 32), (4096, 8192, 96), (8192, 8192, 8192), (7940, 8132, 32), (8132, 7940, 64)]:
+        assert default_name(*shape) == KERNELS["tile256"][0], shape
+    for shape in [(2048, 2048, 32), (1500, 2044, 64), (2052, 3000, 96), (4100, 6200, 160), (8200, 8200, 64)]:
+        assert default_name(*shape) == KERNELS["tile128"][0], shape
     for shape in [(4096, 4096, 33), (8194, 8192, 64), (8192, 8193, 64)]:
-        assert binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(*shape)) == EIGHT_WAVE
+        assert default_name(*shape) == KERNELS["tile256"][1], shape
+
+
+FULL = {
+    # K = 32 (one phase: prologue and the peeled last steps only), K = 64
+    # (two phases) and more; full tiles and edge tiles in both dimensions
+    "tile256": [(4096, 4096, 32), (4096, 4096, 64), (7940, 8132, 32)],
+    "tile128": [(2048, 2048, 32), (1500, 2044, 64), (2052, 3000, 96)],
+}
 
 
 @pytest.mark.parametrize("ops", OPS, ids=lambda o: o[0] + o[1])
 @pytest.mark.parametrize("dist", ["int", "uniform"])
-def test_scheduled_full_oracle(ops, dist):
-    """K = 32 (one phase, the prologue and the peeled last steps only) and
-    K = 64 (two phases) against the whole oracle product, on full tiles and
-    with edge tiles in both dimensions (M and N not multiples of 256)."""
+@pytest.mark.parametrize("kernel", sorted(KERNELS))
+def test_scheduled_full_oracle(kernel, ops, dist):
+    """Every entry against the oracle product."""
     op_a, op_b = ops
-    for (M, N, K) in ((4096, 4096, 32), (4096, 4096, 64), (4100, 6200, 32), (4356, 5800, 64)):
+    name, same_tile = KERNELS[kernel]
+    for (M, N, K) in FULL[kernel]:
+        assert default_name(M, N, K) == name
         prob = Problem(op_a, op_b, M, N, K, dist, [M, N, K, len(op_a + op_b), dist == "int", ord(op_a[0])])
         Cref, S = oracle.gemm(prob.A.view, prob.B.view, op_a=op_a, op_b=op_b, threads=8)
-        say(f"sched full oracle {op_a}{op_b} {dist} {(M, N, K)}")
+        say(f"sched full oracle {kernel} {op_a}{op_b} {dist} {(M, N, K)}")
         C = prob.run()
         check_padding_untouched(C)
-        what = f"sched {op_a}{op_b} {dist} {(M, N, K)}"
+        what = f"sched {kernel} {op_a}{op_b} {dist} {(M, N, K)}"
         if dist == "int":
             check_exact(C.view, Cref, what)
         else:
             check_close(C.view, Cref, S, what)
-        assert np.array_equal(C.view, prob.eight_wave_bits()), what + ": bits differ from the eight-wave kernel"
+        assert np.array_equal(C.view, prob.reference_bits(same_tile)), what + ": bits differ from " + same_tile
 
 
 SAMPLED = [
-    # shape, offset, (pad A, pad B, pad C): aligned, then dword-offset and padded
-    ((4096, 8192, 96), 0, (0, 0, 0)),
-    ((8192, 4096, 544), 1, (3, 5, 7)),
-    ((4096, 4096, 256), 3, (1, 2, 1)),
-    # edge tiles: M and N not multiples of 256, padded and dword-offset
-    ((4100, 6200, 160), 1, (3, 5, 7)),
-    ((6396, 4100, 96), 0, (0, 0, 0)),
+    # kernel, shape, offset, (pad A, pad B, pad C): aligned, then dword-offset and padded
+    ("tile256", (4096, 8192, 96), 0, (0, 0, 0)),
+    ("tile256", (8192, 4096, 544), 1, (3, 5, 7)),
+    ("tile256", (4096, 4096, 256), 3, (1, 2, 1)),
+    ("tile256", (7940, 8132, 160), 1, (3, 5, 7)),
+    ("tile256", (8132, 7940, 96), 0, (0, 0, 0)),
+    ("tile128", (3000, 7000, 1024), 0, (0, 0, 0)),
+    ("tile128", (5000, 5004, 128), 1, (3, 5, 7)),
+    ("tile128", (4100, 6200, 160), 3, (1, 2, 1)),
 ]
 
 
 @pytest.mark.parametrize("ops", OPS, ids=lambda o: o[0] + o[1])
-@pytest.mark.parametrize("case", SAMPLED, ids=lambda c: "x".join(map(str, c[0])) + f"_off{c[1]}")
+@pytest.mark.parametrize("case", SAMPLED, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + f"_off{c[2]}")
 @pytest.mark.parametrize("dist", ["int", "uniform"])
 def test_scheduled_sampled(ops, case, dist):
     op_a, op_b = ops
-    (M, N, K), offset, pad = case
+    kernel, (M, N, K), offset, pad = case
+    name, same_tile = KERNELS[kernel]
+    assert default_name(M, N, K) == name
     prob = Problem(op_a, op_b, M, N, K, dist, [M, N, K, offset, len(op_a + op_b), dist == "int"],
                    offset, pad)
     ii, jj = inputs.sample_pairs(M, N, 4096, np.random.default_rng([M, N, K, 5]))
     cref, sref = oracle.gemm_entries(prob.A.view, prob.B.view, ii, jj, op_a=op_a, op_b=op_b)
-    say(f"sched sampled {op_a}{op_b} {dist} {(M, N, K)} offset={offset} pad={pad}")
+    say(f"sched sampled {kernel} {op_a}{op_b} {dist} {(M, N, K)} offset={offset} pad={pad}")
     C = prob.run()
     check_padding_untouched(C)
-    what = f"sched {op_a}{op_b} {dist} {(M, N, K)} offset {offset}"
+    what = f"sched {kernel} {op_a}{op_b} {dist} {(M, N, K)} offset {offset}"
     if dist == "int":
         check_exact(C.view[ii, jj], cref, what)
     else:
         check_close(C.view[ii, jj], cref, sref, what)
     assert np.all(np.isfinite(C.view))
-    assert np.array_equal(C.view, prob.eight_wave_bits()), what + ": bits differ from the eight-wave kernel"
+    assert np.array_equal(C.view, prob.reference_bits(same_tile)), what + ": bits differ from " + same_tile

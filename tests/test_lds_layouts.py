@@ -279,26 +279,30 @@ def sched_f32_swz(r):
     return (r >> 1) & 7
 
 
+@pytest.mark.parametrize("mnt,f", [(256, 4), (128, 2)], ids=["tile256", "tile128"])
 @pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
-def test_scheduled_fp32_kernel_layout(kc):
-    """The four-wave fp32 kernel: each factor tile is 256 rows of 32 floats
-    (k-contiguous, chunk c of row r at c ^ ((r / 2) mod 8), a copy fills 8
-    rows) or 32 k rows of 256 floats (mn-contiguous, a copy fills one row).
-    Restated here, the copies of all four waves are simulated into a map from
-    LDS word to the (mn, k) element they bring, then every lane's reads (per-
-    lane base + compile-time offset + stage) must deliver the operands of its
-    instructions: for block f and instruction e of step s, the value of
-    op(X)[mn][k] with k = 8 s + 4 (lane / 32) + e and mn = 32 f + lane % 32
-    (k-contiguous) or 4 (lane % 32) + f (mn-contiguous) inside the wave's
-    128-wide span.  Reads are conflict free (16 lanes per cycle, 64 banks)
-    and the instruction offsets fit their 16 bits."""
-    TILE = 256 * 32                                      # floats per stage
+def test_scheduled_fp32_kernel_layout(kc, mnt, f):
+    """The four-wave fp32 kernel on MNT x MNT tiles (two waves along each
+    dimension, F = MNT / 64 blocks of 32 per wave): each factor tile is MNT
+    rows of 32 floats (k-contiguous, chunk c of row r at c ^ ((r / 2) mod 8),
+    a copy fills 8 rows) or 32 k rows of MNT floats (mn-contiguous, a copy
+    fills 256 / MNT rows).  Restated here, the copies of all four waves are
+    simulated into a map from LDS word to the (mn, k) element they bring,
+    then every lane's reads (per-lane base + compile-time offset) must
+    deliver the operands of its instructions: for block b and instruction e
+    of step s, op(X)[mn][k] with k = 8 s + 4 (lane / 32) + e and mn = 32 b +
+    lane % 32 (k-contiguous) or F (lane % 32) + b (mn-contiguous) inside the
+    wave's span of 32 F.  Reads are conflict free (128-bit: 16 lanes per
+    cycle; 64-bit: 32) and the instruction offsets fit their 16 bits."""
+    TILE = mnt * 32                                      # floats per stage
+    rpc = 8 if kc else 256 // mnt                        # stored rows per copy
+    lpr = 64 // rpc                                      # lanes per stored row
 
-    def copy_map(kc):
+    def copy_map():
         """LDS word (stage 0, relative to the tile) -> (mn, k)."""
         where = {}
         for w in range(4):
-            for j in range(8):
+            for j in range(mnt // 32):
                 for lane in range(64):
                     if kc:
                         row = 8 * (w + 4 * j) + lane // 8
@@ -307,38 +311,37 @@ def test_scheduled_fp32_kernel_layout(kc):
                         for e in range(4):
                             where[dst + e] = (row, src_k + e)
                     else:
-                        row = w + 4 * j
-                        dst = row * 256 + 4 * lane
+                        row = rpc * (w + 4 * j) + lane // lpr
+                        dst = rpc * (w + 4 * j) * mnt + 4 * lane
                         for e in range(4):
-                            where[dst + e] = (4 * lane + e, row)
+                            where[dst + e] = (4 * (lane % lpr) + e, row)
         assert sorted(where) == list(range(TILE))        # the copies fill the tile exactly once
         return where
 
-    def read_base(kc, mn, s, li, lh):                    # bytes, as the kernel computes it
+    def read_base(mn, s, li, lh):                        # bytes, as the kernel computes it
         if kc:
             return 4 * ((mn + li) * 32 + 4 * ((2 * s + lh) ^ sched_f32_swz(li)))
-        return 4 * (4 * lh * 256 + mn + 4 * li)
+        return 4 * (4 * lh * mnt + mn + f * li)
 
-    def read_imm(kc, s, i):
-        return 4096 * i if kc else 8192 * s + 1024 * i
+    def read_imm(s, i):
+        return 4096 * i if kc else 4 * mnt * (8 * s + i)
 
-    where = copy_map(kc)
-    for span in (0, 128):                   # the wave's 128-wide span of the tile
+    width = 4 if kc else f                               # floats per read
+    where = copy_map()
+    for span in (0, 32 * f):                             # the wave's span of the tile
         for s in range(4):
-            for i in range(4):
-                assert 0 <= read_imm(kc, s, i) < 1 << 16
+            for i in range(f if kc else 4):
+                assert 0 <= read_imm(s, i) < 1 << 16
                 words = []
                 for lane in range(64):
                     li, lh = lane & 31, lane >> 5
-                    addr = read_base(kc, span, s, li, lh) + read_imm(kc, s, i)
-                    assert addr % 16 == 0 and 0 <= addr and addr + 16 <= 4 * TILE
+                    addr = read_base(span, s, li, lh) + read_imm(s, i)
+                    assert addr % (4 * width) == 0 and 0 <= addr and addr + 4 * width <= 4 * TILE
                     words.append(addr // 4)
-                    got = [where[addr // 4 + e] for e in range(4)]
+                    got = [where[addr // 4 + e] for e in range(width)]
                     if kc:      # read i = block i, values e = instructions
                         want = [(span + 32 * i + li, 8 * s + 4 * lh + e) for e in range(4)]
                     else:       # read i = instruction i, values e = blocks
-                        want = [(span + 4 * li + e, 8 * s + 4 * lh + i) for e in range(4)]
+                        want = [(span + f * li + e, 8 * s + 4 * lh + i) for e in range(f)]
                     assert got == want, (span, s, i, lane)
-                assert degree(words, 4, 64, 16) == 1
-    # A's two stages, then B's: four 32 KB tiles fill 128 KB.
-    assert 4 * TILE * 4 == 128 * 1024
+                assert degree(words, width, 64, 16 if width == 4 else 32) == 1
