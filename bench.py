@@ -33,6 +33,11 @@ Extra modes (used for counter runs under rocprofv3):
                         per workload with the median and best launch time
                         (HIP events around every launch), then the oracle's
                         time on this host (see bench_all_workloads)
+    --shape-sweep       the tile choice on 25 shapes (512^3 .. 8192^3,
+                        rectangular and awkward ones): TFLOP/s of the default
+                        configuration, of every candidate configuration and
+                        of torch.matmul (hipBLASLt, for context), one JSON
+                        line per shape (see bench_shape_sweep)
 """
 from __future__ import annotations
 
@@ -366,6 +371,61 @@ WORKLOAD_LAUNCHES = {"square256": 200, "square1000": 50, "square4096": 20,
                      "rect8192x4096x2048_padded": 20, "square8192": 10}
 
 
+SWEEP_SHAPES = ([(n, n, n) for n in (512, 768, 1024, 1536, 2048, 2560, 3072, 3584, 4096, 4352, 4608, 5120,
+                                      6144, 7168, 8192)] +
+                [(4100, 4100, 4096), (4000, 5000, 4096), (6000, 6000, 6000), (8200, 8200, 4096),
+                 (8192, 4096, 2048), (2048, 8192, 4096), (16384, 1024, 4096), (1024, 16384, 2048),
+                 (5000, 3000, 2000), (3000, 7000, 1024)])
+SWEEP_CANDIDATES = ["mfma64x64_bk32_w2x2_k4", "mfma64x64_bk16_w2x2_k4", "mfma128x128_bk16_w2x2",
+                    "mfma128x128_bk32_w2x2_sched", "mfma256x256_bk32_w2x4_direct",
+                    "mfma256x256_bk32_w2x2_sched"]
+
+
+def bench_shape_sweep(args) -> int:
+    """For each shape (uniform[-1,1) operands, compact leading dimensions):
+    the configuration gemm_f32 picks and the TFLOP/s of every candidate
+    configuration through gemm_f32_variant, each run untimed for 0.1 s and
+    then timed over 10 launches with HIP events on the launch stream, plus
+    torch.matmul on the same operands (fp32, TF32 off) for context."""
+    import torch
+
+    from shared_memory_tiled_amd import binding
+
+    torch.backends.cuda.matmul.allow_tf32 = False
+    number = {binding.gemm_f32_variant_name(binding.DIAGNOSTIC_BASE + d): binding.DIAGNOSTIC_BASE + d
+              for d in range(binding.gemm_f32_num_diagnostic_variants())}
+
+    def tflops(fn, flop, reps=10):
+        settle(fn, 0.1)
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return flop / (e0.elapsed_time(e1) / reps) / 1e9
+
+    gen = torch.Generator(device="cuda").manual_seed(20261202)
+    for (M, N, K) in SWEEP_SHAPES:
+        X = torch.rand((M, K), device="cuda", generator=gen) * 2 - 1
+        Y = torch.rand((K, N), device="cuda", generator=gen) * 2 - 1
+        out = torch.empty((M, N), device="cuda")
+        flop = 2.0 * M * N * K
+        default = binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(M, N, K))
+        res = {c: round(tflops(lambda: binding.gemm(X, Y, out, variant=number[c]), flop), 1)
+               for c in SWEEP_CANDIDATES}
+        best = max(res, key=res.get)
+        line = {"M": M, "N": N, "K": K, "default": default,
+                "default_tflops": round(tflops(lambda: binding.gemm(X, Y, out), flop), 1),
+                "best": best, "best_tflops": res[best], "candidates_tflops": res,
+                "torch_matmul_tflops": round(tflops(lambda: torch.matmul(X, Y, out=out), flop), 1)}
+        line["default_over_best"] = round(line["default_tflops"] / res[best], 3)
+        print(json.dumps(line), flush=True)
+        del X, Y, out
+    return 0
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -466,6 +526,7 @@ def main(argv=None) -> int:
     ap.add_argument("--format", default="bf16", choices=["bf16", "f16"], help="16-bit format of --row mixed")
     ap.add_argument("--n", type=int, default=2 ** 28, help="values summed by --row reduce")
     ap.add_argument("--all-workloads", action="store_true")
+    ap.add_argument("--shape-sweep", action="store_true")
     ap.add_argument("--settle-s", type=float, default=SETTLE_S,
                     help="untimed run of each timed step, in seconds, before its warm-up steps")
     args = ap.parse_args(argv)
@@ -499,6 +560,8 @@ def main(argv=None) -> int:
 
     if args.all_workloads:
         return bench_all_workloads(args)
+    if args.shape_sweep:
+        return bench_shape_sweep(args)
     if args.row == "reduce":
         return bench_reduce(args)
     w = inputs.WORKLOADS[args.workload]

@@ -19,5 +19,5 @@ def test_help_lists_modes():
                           capture_output=True, text=True, timeout=120)
     assert proc.returncode == 0
     for flag in ("--steps", "--warmup", "--ladder", "--op", "--copy-probe-mib", "--row", "--format",
-                 "--all-workloads"):
+                 "--all-workloads", "--shape-sweep"):
         assert flag in proc.stdout
