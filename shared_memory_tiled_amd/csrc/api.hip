@@ -45,6 +45,7 @@ const Diagnostic kDiagnostics[] = {
     {"mfma256x256_bk32_w2x2_sched_g4", 3, 17},
     {"mfma128x128_bk32_w2x2_sched", 3, 18},
     {"mfma128x128_bk32_w2x2_sched_g16", 3, 19},
+    {"mfma64x64_bk32_w1x1_k4_sched", 3, 20},
 };
 constexpr int kNumDiagnostics = (int)(sizeof(kDiagnostics) / sizeof(kDiagnostics[0]));
 

@@ -54,6 +54,11 @@ int mfma_pick_config(int M, int N, int K);
 // (op 1: factor stored transposed; tile 256 or 128).
 bool sched_f32_fits(const GemmArgs& p, int op_a, int op_b);
 hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m, int tile);
+// Four waves splitting the phases of one 64 x 64 tile (mfma_sched.hip):
+// whether it takes the problem (K, M and N multiples of 4, stored factors
+// below 2^31 bytes), and its launcher.
+bool ksplit_f32_fits(const GemmArgs& p, int op_a, int op_b);
+hipError_t launch_ksplit_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m);
 int regblock_num_configs();
 const char* regblock_config_name(int config);
 

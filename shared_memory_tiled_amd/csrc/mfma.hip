@@ -597,6 +597,18 @@ hipError_t launch_sched128_or_staged(const GemmArgs& p, hipStream_t s, int tiles
     {launch_sched128_or_staged<false, false>, launch_sched128_or_staged<false, true>,          \
      launch_sched128_or_staged<true, false>, launch_sched128_or_staged<true, true>}
 
+// Four waves splitting the phases of a 64 x 64 tile, else the split-phase
+// kernel with four groups of four waves.
+template <bool TRA, bool TRB>
+hipError_t launch_ksplit_or_splitk(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                                   unsigned blocks) {
+    if (ksplit_f32_fits(p, TRA, TRB)) return launch_ksplit_f32(p, s, TRA, TRB, group_m);
+    return launch_splitk<64, 64, 32, 4, TRA, TRB>(p, s, tiles_m, tiles_n, group_m, blocks);
+}
+#define KSPLIT_OPS                                                                       \
+    {launch_ksplit_or_splitk<false, false>, launch_ksplit_or_splitk<false, true>,          \
+     launch_ksplit_or_splitk<true, false>, launch_ksplit_or_splitk<true, true>}
+
 // NN only (diagnostic layouts) or all four op combinations.
 #define NN_ONLY(BM, BN, BK, WM, WN, D, S) \
     {launch_one<BM, BN, BK, WM, WN, D, S, false, false>, nullptr, nullptr, nullptr}
@@ -640,6 +652,8 @@ const MfmaConfig kConfigs[] = {
     {"mfma256x256_bk32_w2x2_sched_g4", 256, 256, 256, 4, SCHED_OPS},
     {"mfma128x128_bk32_w2x2_sched", 128, 128, 256, 8, SCHED128_OPS},
     {"mfma128x128_bk32_w2x2_sched_g16", 128, 128, 256, 16, SCHED128_OPS},
+    // four waves, each the whole 64 x 64 tile over every fourth phase
+    {"mfma64x64_bk32_w1x1_k4_sched", 64, 64, 1024, 8, KSPLIT_OPS},
 };
 #undef NN_ONLY
 #undef ALL_OPS
@@ -647,6 +661,7 @@ const MfmaConfig kConfigs[] = {
 #undef SCHED_OPS
 #undef SCHED128_OPS
 #undef SPLITK_OPS
+#undef KSPLIT_OPS
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 }  // namespace
 
@@ -660,26 +675,65 @@ const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConf
 // at least 128, else the split-phase 64 x 64 tiles.  Other shapes: 256 x
 // 256 tiles on eight waves (direct copies, ghost phases at the edges) when
 // their rounds run at least 80 % full (75 % when 128 x 128 tiles would not
-// fill theirs to 90 % either), else register-staged 128 x 128 tiles when at
-// least 256 of them fill their rounds to 90 %, else 64 x 64 tiles with the
-// phases of each tile split over four groups of four waves (16 waves per
-// workgroup to hide latency; 32-deep phases when there are at most 256 such
-// tiles, 16-deep otherwise).  Every picked configuration is built for all
-// four op combinations.
+// fill theirs to 90 %), else register-staged 128 x 128 tiles when at least
+// 256 of them fill their rounds to 90 %, else 64 x 64 tiles with the phases
+// of each tile split over four groups of four waves (16 waves per workgroup
+// to hide latency; 32-deep phases when there are at most 256 such tiles,
+// 16-deep otherwise).
+//
+// Then, for K of at least 512 and K, M and N multiples of 4, the 64 x 64
+// tiles whose four waves split the phases (mfma_sched.hip) replace that
+// choice when a cost model gives them the shorter time.  The model charges
+// each round of 256 tiles the tile's work at a kernel's measured fraction
+// of the matrix-core peak plus a fixed cost per tile (first copies, final
+// store): four-wave 256 x 256 0.985 and 11 us, 128 x 128 0.975 and 5.3 us,
+// eight-wave 256 x 256 0.92 and 11 us, register-staged 128 x 128 0.85 and
+// 5.3 us, 64 x 64 with split phases 0.914 and 3 us (fitted to 31 shapes
+// from 512^3 to 8192^3; below K = 512 the fixed cost of the 64 x 64 tiles
+// is not captured well enough: there they only replace the split-phase
+// tiles, from K = 384, three phases per wave).  Every picked configuration
+// is built for all four op combinations.
+namespace {
+// Modelled time (ns) of a configuration: rounds x (tile work / efficiency
+// + fixed cost); tile work at the per-CU peak of 2 x 64 x 64 x K flops per
+// 64 x 64 tile at 614.5 GFLOP/s, 13.33 ns per k.
+double model_ns(int config, int M, int N, int K) {
+    int tile, rel;
+    double eff, fixed;
+    switch (config) {
+        case 16: tile = 256; rel = 16; eff = 0.985; fixed = 11000; break;
+        case 18: tile = 128; rel = 4; eff = 0.975; fixed = 5300; break;
+        case 7: tile = 256; rel = 16; eff = 0.92; fixed = 11000; break;
+        case 1: tile = 128; rel = 4; eff = 0.85; fixed = 5300; break;
+        case 20: tile = 64; rel = 1; eff = 0.914; fixed = 3000; break;
+        default: return 1e300;                    // the split-phase 64 x 64 tiles: never kept over 20
+    }
+    const int64_t tiles = (int64_t)ceil_div(M, tile) * ceil_div(N, tile);
+    const double rounds = (double)((tiles + 255) / 256);
+    return rounds * (rel * 13.33 * K / eff + fixed);
+}
+}  // namespace
+
 int mfma_pick_config(int M, int N, int K) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
     const int64_t t64 = (int64_t)ceil_div(M, 64) * ceil_div(N, 64);
     const int64_t slots256 = (t256 + 255) / 256 * 256, slots128 = (t128 + 255) / 256 * 256;
     const int small = t64 <= 256 ? 14 : 13;
+    int pick;
     if (K % 32 == 0 && K > 0 && M % 4 == 0 && N % 4 == 0) {
-        if (t256 >= 256 && t256 * 20 >= slots256 * 19) return 16;
-        return t128 >= 128 ? 18 : small;
+        if (t256 >= 256 && t256 * 20 >= slots256 * 19) pick = 16;
+        else pick = t128 >= 128 ? 18 : small;
+    } else {
+        const bool fill128 = t128 * 10 >= slots128 * 9;
+        if (t256 >= 256 && (t256 * 10 >= slots256 * 8 || (t256 * 4 >= slots256 * 3 && !fill128))) pick = 7;
+        else if (t128 >= 256 && fill128) pick = 1;
+        else pick = small;
     }
-    const bool fill128 = t128 * 10 >= slots128 * 9;
-    if (t256 >= 256 && (t256 * 10 >= slots256 * 8 || (t256 * 4 >= slots256 * 3 && !fill128))) return 7;
-    if (t128 >= 256 && fill128) return 1;
-    return small;
+    const bool split_fits = K % 4 == 0 && M % 4 == 0 && N % 4 == 0;
+    if (split_fits && ((pick == small && K >= 384) || (K >= 512 && model_ns(20, M, N, K) < model_ns(pick, M, N, K))))
+        pick = 20;
+    return pick;
 }
 
 // hipErrorInvalidValue: the grid would exceed the launch limits.

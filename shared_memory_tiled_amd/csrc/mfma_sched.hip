@@ -86,12 +86,13 @@ __device__ __forceinline__ void wait_tied(floatx4 (&x)[4]) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : : "memory");
 }
 
-// One factor's tile: MNT (256 or 128) rows or columns of op(X) by 32 k per
-// stage; each wave holds F (4 or 2) blocks of 32 of it.  KC: stored
-// k-contiguous.
+// One factor's tile: MNT (256, 128 or 64) rows or columns of op(X) by 32 k
+// per stage; each wave holds F (4 or 2) blocks of 32 of it.  KC: stored
+// k-contiguous.  Copy j of wave w: one of the 4 MNT / 32 copies of a stage,
+// dealt to four waves in turn.
 template <bool KC, int MNT, int F>
 struct SchedTileF32 {
-    static_assert((MNT == 256 || MNT == 128) && (F == 4 || F == 2), "tile shape");
+    static_assert((MNT == 256 || MNT == 128 || MNT == 64) && (F == 4 || F == 2), "tile shape");
     static constexpr int WORDS = MNT * kSBK;              // floats per stage
     static constexpr int COPIES = MNT / 32;               // 1 KB copies per wave and phase
     static constexpr int RPC = KC ? 8 : 256 / MNT;        // stored rows per copy
@@ -112,6 +113,16 @@ struct SchedTileF32 {
             constexpr int LPR = 64 / RPC;                   // lanes per stored row
             const int row = RPC * (w + 4 * j) + lane / LPR;
             return 4u * (uint32_t)(row * ld + mn0 + 4 * (lane % LPR));
+        }
+    }
+    // k of lane l's 16 bytes of copy j of wave w, relative to the phase's
+    // first k.
+    __host__ __device__ static int copy_k(int w, int j, int lane) {
+        if constexpr (KC) {
+            const int row = 8 * (w + 4 * j) + lane / 8;
+            return 4 * ((lane % 8) ^ sched_swz(row));
+        } else {
+            return RPC * (w + 4 * j) + lane / (64 / RPC);
         }
     }
     // Byte offset of the phase at k0 from the phase at 0.
@@ -328,7 +339,7 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     for (int i = 0; i < NREAD; ++i) read_op(0, 0, i);
     if (P > 1) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) copy(j, kSBK, 1);
+        for (int j = 0; j < HALF; ++j) copy(j, kSBK, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
     int ph = 0;
@@ -385,6 +396,284 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         }
 }
 
+// Small products: 64 x 64 tiles, one per workgroup, whose four waves each
+// compute the whole tile over every fourth phase (wave w: phases w, w + 4,
+// ...) from two LDS stages of their own, which only that wave copies into
+// and reads.  The waves never wait for each other before the end, where
+// their four partial tiles meet in LDS and are added in wave order (so the
+// result is deterministic; its rounding differs from the one-wave-per-block
+// kernels, within the same bound).  Per wave the schedule above on a 64 x
+// 64 wave tile (2 x 2 blocks): 16 matrix instructions per step, the 16 1 KB
+// copies of a phase after every second of them in two steps, and one wait
+// for the wave's own copies where the kernel above has its barrier.
+//
+// K need only be a multiple of 4: the phases are aligned to the end of K,
+// phase g covering k = K - 32 (P - g) .. + 31 for P = ceil(K / 32) phases,
+// so only phase 0 can reach below k = 0, and its lanes there are pointed
+// past the end of their descriptor and copy zeros.
+template <bool KCA, bool KCB>
+__global__ __launch_bounds__(256)
+void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
+    constexpr int FM = 2, FN = 2, BM = 64, BN = 64;
+    using TA = SchedTileF32<KCA, BM, FM>;
+    using TB = SchedTileF32<KCB, BN, FN>;
+    constexpr int A_COPIES = 4 * TA::COPIES, NCOPY = A_COPIES + 4 * TB::COPIES, HALF = NCOPY / 2;
+    constexpr int NREAD = TA::READS + TB::READS;
+    constexpr int NMFMA = 4 * FM * FN;
+    constexpr int CSTRIDE = NMFMA / HALF;
+    static_assert(NCOPY == 16 && NREAD <= NMFMA && CSTRIDE == 2, "schedule");
+    constexpr int A_ST = TA::WORDS, B_ST = TB::WORDS;
+    constexpr int WAVE_WORDS = 2 * (A_ST + B_ST);            // A stage 0, 1, B stage 0, 1
+    constexpr int PART_WORDS = FM * FN * 16 * 64;            // one wave's partial tile
+    static_assert(PART_WORDS <= WAVE_WORDS, "partials reuse the stages");
+    __shared__ __attribute__((aligned(16))) float lds[4 * WAVE_WORDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, lh = lane >> 5;
+
+    const int logical = xcd_contiguous((int)blockIdx.x, tiles_m * tiles_n);
+    const int group_size = group_m * tiles_n;
+    const int g = logical / group_size;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int in_g = logical - g * group_size;
+    const int m0 = (first_m + in_g % gm) * BM;
+    const int n0 = (in_g / gm) * BN;
+
+    // This wave's phases: local phase lp is phase 4 lp + w, at k0 = kof(lp).
+    const int nph = ceil_div(p.K, kSBK);
+    const int kbase = p.K - kSBK * nph;                      // -31 .. 0
+    const int P = nph > w ? (nph - 1 - w) / 4 + 1 : 0;
+    auto kof = [&](int lp) __attribute__((always_inline)) { return kbase + kSBK * (4 * lp + w); };
+
+    // Copy j < 8 fills A's tile, j >= 8 B's; within a factor copy j is copy
+    // j / 4 of "wave" j % 4 of the shared layout, so one wave covers it all.
+    uint32_t doff[NCOPY];
+#pragma unroll
+    for (int j = 0; j < A_COPIES; ++j) {
+        doff[j] = TA::copy_src(j % 4, j / 4, lane, m0, p.lda);
+        doff[A_COPIES + j] = TB::copy_src(j % 4, j / 4, lane, n0, p.ldb);
+    }
+    constexpr int kRawBufferWord3 = 0x00020000;
+    constexpr uint32_t kPastEnd = 0x80000000u;               // beyond any descriptor here
+    // Descriptors end exactly at each stored matrix's last element: rows
+    // past the edge (of the tile, or k >= K of an mn-contiguous factor) read
+    // +0; columns past the last one of an mn-contiguous factor read the next
+    // row, which only meets C entries outside the matrix.
+    const int64_t a_rows = KCA ? p.M : p.K, a_cols = KCA ? p.K : p.M;
+    const int64_t b_rows = KCB ? p.N : p.K, b_cols = KCB ? p.K : p.N;
+    const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.A), (short)0, (int)(4 * ((a_rows - 1) * p.lda + a_cols)), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.B), (short)0, (int)(4 * ((b_rows - 1) * p.ldb + b_cols)), kRawBufferWord3);
+    float* const wl = lds + w * WAVE_WORDS;
+    auto copy_at = [&](int j, uint32_t voff, int soff, int buf) __attribute__((always_inline)) {
+        if (j < A_COPIES) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_a, (__attribute__((address_space(3))) void*)(wl + buf * A_ST + TA::copy_dst(j % 4, j / 4)),
+                16, (int)voff, soff, 0, 0);
+        } else {
+            const int jb = j - A_COPIES;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_b,
+                (__attribute__((address_space(3))) void*)(wl + 2 * A_ST + buf * B_ST + TB::copy_dst(jb % 4, jb / 4)),
+                16, (int)voff, soff, 0, 0);
+        }
+    };
+    auto copy = [&](int j, int k0, int buf) __attribute__((always_inline)) {
+        copy_at(j, doff[j], j < A_COPIES ? TA::phase_bytes(k0, p.lda) : TB::phase_bytes(k0, p.ldb), buf);
+    };
+    // The wave's first phase (k0 <= 0 only for phase 0), into stage 0: the
+    // phase offset goes into each lane's offset, and lanes whose k is
+    // negative point past the end.
+    auto copy_first = [&]() __attribute__((always_inline)) {
+        const int k0 = kof(0);
+#pragma unroll
+        for (int j = 0; j < NCOPY; ++j) {
+            const bool is_a = j < A_COPIES;
+            const int jj = is_a ? j : j - A_COPIES;
+            const int kl = is_a ? TA::copy_k(jj % 4, jj / 4, lane) : TB::copy_k(jj % 4, jj / 4, lane);
+            const int pb = is_a ? TA::phase_bytes(k0, p.lda) : TB::phase_bytes(k0, p.ldb);
+            copy_at(j, k0 + kl >= 0 ? doff[j] + (uint32_t)pb : kPastEnd, 0, 0);
+        }
+    };
+
+    constexpr int SA = KCA ? 4 : 1, SB = KCB ? 4 : 1;
+    uint32_t abase[SA], bbase[SB];
+    const uint32_t wl0 = lds_addr(wl);
+#pragma unroll
+    for (int s = 0; s < SA; ++s) abase[s] = wl0 + TA::read_base(0, s, li, lh);
+#pragma unroll
+    for (int s = 0; s < SB; ++s) bbase[s] = wl0 + 8u * A_ST + TB::read_base(0, s, li, lh);
+
+    floatx4 a[2][4], b[2][4];
+    auto read_one = [&](auto tile, floatx4 (&x)[4], uint32_t base, int s, int i) __attribute__((always_inline)) {
+        using T = decltype(tile);
+        const uint32_t addr = base + T::read_imm(s, i);
+        if constexpr (T::IS_KC) {
+            x[i] = lds_read128(addr);
+        } else {
+            const floatx2 v = lds_read64(addr);
+            x[i][0] = v[0];
+            x[i][1] = v[1];
+        }
+    };
+    auto read_op = [&](int s, int t, int i) __attribute__((always_inline)) {
+        if (i < TA::READS) read_one(TA{}, a[t], abase[KCA ? s : 0], s, i);
+        else read_one(TB{}, b[t], bbase[KCB ? s : 0], s, i - TA::READS);
+    };
+    auto flip_stage = [&](int cur) __attribute__((always_inline)) {
+        const uint32_t da = cur ? (uint32_t)(-4 * A_ST) : (uint32_t)(4 * A_ST);
+        const uint32_t db = cur ? (uint32_t)(-4 * B_ST) : (uint32_t)(4 * B_ST);
+#pragma unroll
+        for (int s = 0; s < SA; ++s) abase[s] += da;
+#pragma unroll
+        for (int s = 0; s < SB; ++s) bbase[s] += db;
+    };
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    auto step = [&](int t, auto reads, int rs, auto cb, auto ce, int k_copy,
+                    int cbuf) __attribute__((always_inline)) {
+        constexpr bool R = decltype(reads)::value;
+        constexpr int CB = decltype(cb)::value, CE = decltype(ce)::value;
+        unroll<NMFMA>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            constexpr int e = q / (FM * FN), i = (q / FN) % FM, j = q % FN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(operand<KCA>(a[t], i, e),
+                                                             operand<KCB>(b[t], j, e), acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (R && q < NREAD) {
+                read_op(rs, t ^ 1, q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (q % CSTRIDE == CSTRIDE - 1 && CB + q / CSTRIDE < CE) {
+                copy(CB + q / CSTRIDE, k_copy, cbuf);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    };
+    auto wait_set = [&](int t) __attribute__((always_inline)) {
+        wait_tied(a[t]);
+        wait_tied(b[t]);
+    };
+    // This wave's copies have landed (no other wave reads its stages).
+    auto wait_copies = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    using c0 = std::integral_constant<int, 0>;
+    using cH = std::integral_constant<int, HALF>;
+    using cN = std::integral_constant<int, NCOPY>;
+    auto steps012 = [&](auto wc, int k_copy, int cbuf) __attribute__((always_inline)) {
+        constexpr bool WC = decltype(wc)::value;
+        wait_set(0);
+        if constexpr (WC) step(0, yes{}, 1, cH{}, cN{}, k_copy, cbuf);
+        else step(0, yes{}, 1, c0{}, c0{}, 0, 0);
+        wait_set(1);
+        step(1, yes{}, 2, c0{}, c0{}, 0, 0);
+        wait_set(0);
+        step(0, yes{}, 3, c0{}, c0{}, 0, 0);
+        wait_set(1);
+    };
+
+    // Stage lp & 1 holds local phase lp; the order of the kernel above.
+    if (P > 0) {
+        copy_first();
+        wait_copies();
+#pragma unroll
+        for (int i = 0; i < NREAD; ++i) read_op(0, 0, i);
+        if (P > 1) {
+#pragma unroll
+            for (int j = 0; j < HALF; ++j) copy(j, kof(1), 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        int lp = 0;
+        for (; lp + 2 < P; ++lp) {
+            const int cur = lp & 1;
+            steps012(yes{}, kof(lp + 1), cur ^ 1);
+            flip_stage(cur);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_copies();
+            step(1, yes{}, 0, c0{}, cH{}, kof(lp + 2), cur);
+        }
+        if (lp + 1 < P) {
+            const int cur = lp & 1;
+            steps012(yes{}, kof(lp + 1), cur ^ 1);
+            flip_stage(cur);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_copies();
+            step(1, yes{}, 0, c0{}, c0{}, 0, 0);
+        }
+        steps012(no{}, 0, 0);
+        step(1, no{}, 0, c0{}, c0{}, 0, 0);
+    }
+
+    // Partial tiles: register r of block (i, j) of lane l of wave v at word
+    // v PART_WORDS + ((2 i + j) 16 + r) 64 + l.  Wave v then adds, in wave
+    // order, block row i = v / 2, registers 8 (v % 2) .. + 7 of both blocks
+    // j, and stores them: register r of lane (li, lh) is row rho = 8 (r / 4)
+    // + 4 lh + r % 4 of its block (tile row 32 i + rho for a k-contiguous A,
+    // 2 rho + i for an mn-contiguous one) and column li (32 j + li, or 2 li +
+    // j: then the two blocks' values are adjacent columns, one 64-bit store;
+    // N is a multiple of 4, so both are in or out).
+    __syncthreads();
+    {
+        float* part = lds + w * PART_WORDS;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) part[((i * FN + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    const int bi = w >> 1, r0 = 8 * (w & 1);
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+        const int r = r0 + rr;
+        float v[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const float* q = lds + ((bi * FN + j) * 16 + r) * 64 + lane;
+            v[j] = q[0];
+#pragma unroll
+            for (int u = 1; u < 4; ++u) v[j] += q[u * PART_WORDS];
+        }
+        const int rho = 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int row = m0 + (KCA ? 32 * bi + rho : FM * rho + bi);
+        if (row >= p.M) continue;
+        float* crow = p.C + (int64_t)row * p.ldc + n0;
+        if constexpr (!KCB) {
+            if (n0 + 2 * li < p.N) {
+                const floatx2 x = {v[0], v[1]};
+                *reinterpret_cast<floatx2*>(crow + 2 * li) = x;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                if (n0 + 32 * j + li < p.N) crow[32 * j + li] = v[j];
+        }
+    }
+}
+
+template <bool KCA, bool KCB>
+hipError_t launch_ksplit_f32_kernel(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                                    unsigned blocks) {
+    hipLaunchKernelGGL((gemm_f32_ksplit_kernel<KCA, KCB>), dim3(blocks), dim3(256), 0, s, p, tiles_m, tiles_n,
+                       group_m);
+    return hipGetLastError();
+}
+
 template <int F, bool KCA, bool KCB>
 hipError_t launch_sched_f32_kernel(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
                                    unsigned blocks) {
@@ -418,6 +707,26 @@ bool sched_f32_fits(const GemmArgs& p, int op_a, int op_b) {
     const int64_t a_rows = op_a ? p.K : p.M, b_rows = op_b ? p.N : p.K;
     const int64_t lim = (int64_t)1 << 31;
     return 4 * (a_rows + 256) * p.lda < lim && 4 * (b_rows + 256) * p.ldb < lim;
+}
+
+// K, M and N multiples of 4 (see the descriptors of the kernel), stored
+// factors below 2^31 bytes with a tile's overhang.
+bool ksplit_f32_fits(const GemmArgs& p, int op_a, int op_b) {
+    if (p.K % 4 != 0 || p.K <= 0 || p.M % 4 != 0 || p.N % 4 != 0) return false;
+    const int64_t a_rows = op_a ? p.K : p.M, b_rows = op_b ? p.N : p.K;
+    const int64_t lim = (int64_t)1 << 31;
+    return 4 * (a_rows + 256) * p.lda < lim && 4 * (b_rows + 256) * p.ldb < lim;
+}
+
+hipError_t launch_ksplit_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m) {
+    const int tiles_m = ceil_div(p.M, 64), tiles_n = ceil_div(p.N, 64);
+    const unsigned blocks = (unsigned)((int64_t)tiles_m * tiles_n);
+    switch (2 * (op_a ? 1 : 0) + (op_b ? 1 : 0)) {
+        case 0: return launch_ksplit_f32_kernel<true, false>(p, s, tiles_m, tiles_n, group_m, blocks);
+        case 1: return launch_ksplit_f32_kernel<true, true>(p, s, tiles_m, tiles_n, group_m, blocks);
+        case 2: return launch_ksplit_f32_kernel<false, false>(p, s, tiles_m, tiles_n, group_m, blocks);
+        default: return launch_ksplit_f32_kernel<false, true>(p, s, tiles_m, tiles_n, group_m, blocks);
+    }
 }
 
 hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m, int tile) {

@@ -269,7 +269,11 @@ def test_default_variant_choices(binding):
     256 tiles when their rounds run at least 80 % full (75 % when 128 x 128
     tiles would not fill theirs to 90 %), register-staged 128 x 128 tiles
     when at least 256 of them fill their rounds to 90 %, else the split-phase
-    tiles (32-deep phases for at most 256 tiles).  For the 16-bit product the
+    tiles (32-deep phases for at most 256 tiles).  Then, with K, M and N
+    multiples of 4, the 64 x 64 tiles whose four waves split the phases where
+    a cost model of rounds, efficiency and fixed cost per tile gives them the
+    shorter time (K >= 512), or in place of the split-phase tiles (K >= 384).
+    For the 16-bit product the
     scheduled kernel, 128 x 128 direct copies or 64 x 64 tiles.  Invalid
     sizes give -1."""
     f32 = {
@@ -279,19 +283,27 @@ def test_default_variant_choices(binding):
         (4096, 4096, 32): "mfma256x256_bk32_w2x2_sched",
         (7940, 8132, 32): "mfma256x256_bk32_w2x2_sched",         # 1024 tiles with edges
         (8200, 8200, 8192): "mfma128x128_bk32_w2x2_sched",       # 1089 tiles of 256: 85 % of 5 rounds
-        (4100, 4104, 4096): "mfma128x128_bk32_w2x2_sched",
+        (4100, 4104, 4096): "mfma64x64_bk32_w1x1_k4_sched",       # 4225 tiles of 64: 16.5 rounds
         (4000, 5000, 4096): "mfma128x128_bk32_w2x2_sched",
         (2048, 2048, 2048): "mfma128x128_bk32_w2x2_sched",
-        (1536, 1536, 1536): "mfma128x128_bk32_w2x2_sched",       # 144 tiles of 128
-        (1024, 1024, 1024): "mfma64x64_bk32_w2x2_k4",            # 64 tiles of 128
+        (6144, 6144, 6144): "mfma128x128_bk32_w2x2_sched",
+        (7168, 7168, 7168): "mfma128x128_bk32_w2x2_sched",
+        (3000, 3000, 384): "mfma128x128_bk32_w2x2_sched",        # K < 512: no cost model
+        (1536, 1536, 1536): "mfma64x64_bk32_w1x1_k4_sched",       # 144 tiles of 128, 576 of 64
+        (3072, 3072, 3072): "mfma64x64_bk32_w1x1_k4_sched",       # 2304 tiles of 64: 9 full rounds
+        (1024, 1024, 1024): "mfma64x64_bk32_w1x1_k4_sched",
         (4096, 4096, 48): "mfma256x256_bk32_w2x4_direct",
         (8193, 8190, 96): "mfma256x256_bk32_w2x4_direct",
         (4096, 4096, 0): "mfma256x256_bk32_w2x4_direct",
-        (6000, 6000, 6000): "mfma128x128_bk16_w2x2",             # K % 32 = 16; 2209 of 128 (96 %)
+        (6000, 6000, 6000): "mfma64x64_bk32_w1x1_k4_sched",       # K % 32 = 16, K % 4 = 0
+        (5000, 3000, 2000): "mfma64x64_bk32_w1x1_k4_sched",
         (3840, 2048, 100): "mfma128x128_bk16_w2x2",
-        (4100, 4097, 515): "mfma64x64_bk16_w2x2_k4",
-        (3000, 3000, 3000): "mfma64x64_bk16_w2x2_k4",
-        (1000, 1000, 1000): "mfma64x64_bk32_w2x2_k4",
+        (4100, 4097, 515): "mfma64x64_bk16_w2x2_k4",              # K % 4 = 3
+        (3000, 3000, 3000): "mfma64x64_bk32_w1x1_k4_sched",
+        (1000, 1000, 1000): "mfma64x64_bk32_w1x1_k4_sched",
+        (1000, 2000, 500): "mfma64x64_bk32_w1x1_k4_sched",        # in place of the split-phase tiles
+        (1000, 1000, 380): "mfma64x64_bk32_w2x2_k4",              # K < 384
+        (1002, 1000, 1000): "mfma64x64_bk32_w2x2_k4",             # M % 4 = 2
         (256, 256, 256): "mfma64x64_bk32_w2x2_k4",
         (1, 1, 1): "mfma64x64_bk32_w2x2_k4",
     }
