@@ -87,7 +87,14 @@ extern "C" {
  *      a fixed instruction order when K is a multiple of 32 and M and N of 4
  *      and each stored factor is under 2 GiB, else on eight waves; both give
  *      the same bits), else 128 x 128 tiles, else 64 x 64 tiles whose phases
- *      are split over four groups of four waves
+ *      are split over four groups of four waves.  With K, M and N multiples
+ *      of 4, 64 x 64 tiles whose four waves each run the whole tile over
+ *      every fourth phase (partial tiles added in wave order, so results are
+ *      deterministic and the same for every op pair) replace that choice
+ *      where a cost model of rounds, per-kernel efficiency and fixed cost
+ *      per tile gives them the shorter time (K >= 512), or in place of the
+ *      split-phase tiles (K >= 384).  gemm_f32_default_variant() names the
+ *      configuration a shape runs.
  * Variants numbered from 16 up are diagnostic layouts of the same rungs, kept
  * so that their hardware counters can be compared; see
  * gemm_f32_variant_name().
