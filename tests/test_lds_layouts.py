@@ -279,11 +279,14 @@ def sched_f32_swz(r):
     return (r >> 1) & 7
 
 
-@pytest.mark.parametrize("mnt,f", [(256, 4), (128, 2)], ids=["tile256", "tile128"])
+@pytest.mark.parametrize("mnt,f", [(256, 4), (128, 2), (64, 2)], ids=["tile256", "tile128", "ksplit64"])
 @pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
 def test_scheduled_fp32_kernel_layout(kc, mnt, f):
     """The four-wave fp32 kernel on MNT x MNT tiles (two waves along each
-    dimension, F = MNT / 64 blocks of 32 per wave): each factor tile is MNT
+    dimension, F = MNT / 64 blocks of 32 per wave), and the k-split kernel's
+    64 x 64 tile (MNT = 64, F = 2: one wave issues all eight copies of a
+    factor, copy j as copy j / 4 of wave j % 4 below, and reads the whole
+    tile from its own stages): each factor tile is MNT
     rows of 32 floats (k-contiguous, chunk c of row r at c ^ ((r / 2) mod 8),
     a copy fills 8 rows) or 32 k rows of MNT floats (mn-contiguous, a copy
     fills 256 / MNT rows).  Restated here, the copies of all four waves are
@@ -328,7 +331,7 @@ def test_scheduled_fp32_kernel_layout(kc, mnt, f):
 
     width = 4 if kc else f                               # floats per read
     where = copy_map()
-    for span in (0, 32 * f):                             # the wave's span of the tile
+    for span in ((0, 32 * f) if 32 * f < mnt else (0,)):  # the wave's span of the tile
         for s in range(4):
             for i in range(f if kc else 4):
                 assert 0 <= read_imm(s, i) < 1 << 16
@@ -345,3 +348,52 @@ def test_scheduled_fp32_kernel_layout(kc, mnt, f):
                         want = [(span + f * li + e, 8 * s + 4 * lh + i) for e in range(f)]
                     assert got == want, (span, s, i, lane)
                 assert degree(words, width, 64, 16 if width == 4 else 32) == 1
+
+
+@pytest.mark.parametrize("K", [4, 8, 28, 32, 36, 60, 64, 96, 100, 124, 128, 132, 260, 388, 516, 1000, 1024])
+def test_ksplit_phase_partition_and_first_phase_mask(K):
+    """The k-split kernel's phases, restated: P = ceil(K / 32) phases aligned
+    to the end of K (phase g at k0 = K - 32 P + 32 g), wave w taking phases
+    w, w + 4, ... (P_w of them).  Every phase is taken by exactly one wave;
+    only phase 0 reaches below k = 0; the lanes a copy of phase 0 points past
+    the descriptor are exactly those whose 4 values (k-contiguous chunk) or
+    row (mn-contiguous) lie below k = 0; and over all phases every k in
+    0 .. K - 1 of a row (column) is copied exactly once, none at k >= K."""
+    assert K % 4 == 0
+    P = -(-K // 32)
+    kbase = K - 32 * P
+    assert -32 < kbase <= 0
+    owner = {}
+    for w in range(4):
+        Pw = (P - 1 - w) // 4 + 1 if P > w else 0
+        for lp in range(Pw):
+            g = 4 * lp + w
+            assert g not in owner
+            owner[g] = w
+    assert sorted(owner) == list(range(P))
+    for kc in (True, False):
+        for row_or_col in range(64):          # one stored row (KC) or one column (MC) of the tile
+            seen = []
+            for g in range(P):
+                k0 = kbase + 32 * g
+                for j in range(8):            # copy j of the wave: copy j // 4 of "wave" j % 4
+                    w_, j_ = j % 4, j // 4
+                    for lane in range(64):
+                        if kc:
+                            row = 8 * (w_ + 4 * j_) + lane // 8
+                            if row != row_or_col:
+                                continue
+                            kl = 4 * ((lane % 8) ^ sched_f32_swz(row))
+                            ks = [k0 + kl + e for e in range(4)]
+                        else:
+                            if 4 * (lane % 16) > row_or_col or row_or_col >= 4 * (lane % 16) + 4:
+                                continue
+                            kl = 4 * (w_ + 4 * j_) + lane // 16
+                            ks = [k0 + kl]
+                        masked = g == 0 and k0 + kl < 0
+                        assert masked == (min(ks) < 0), (kc, g, j, lane)
+                        assert max(ks) < 0 or min(ks) >= 0     # a chunk never straddles k = 0
+                        assert max(ks) < K
+                        if not masked:
+                            seen.extend(ks)
+            assert sorted(seen) == list(range(K)), (kc, row_or_col)
