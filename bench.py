@@ -44,6 +44,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -61,11 +62,21 @@ KERNEL_SOURCES = ["shared_memory_tiled_amd/csrc/mfma_sched.hip",
                   "shared_memory_tiled_amd/csrc/gemm_internal.h"]
 
 
+def source_code(text: str) -> str:
+    """The code of a C++ source without its comments and with whitespace
+    runs collapsed (the kernel sources hold no string literals with // or
+    /*), so that an edit of a comment leaves the digest unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(source_code(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

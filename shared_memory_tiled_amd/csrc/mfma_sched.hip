@@ -3,10 +3,12 @@
 // The tiled product of the pages' shared-memory chapter (PMPP chapter 5
 // notes, sections 5.4-5.5: per phase every thread of a block copies part of
 // an A and a B tile into shared memory, a barrier, the multiply-adds from the
-// tiles, a barrier, and a guarded store at the edges) on 256 x 256 output
-// tiles, 32 k values per phase (K a multiple of 32),
-// two LDS stages so the copies of the next phase overlap the math of the
-// current one.
+// tiles, a barrier, and a guarded store at the edges) on 256 x 256 (or 128 x
+// 128) output tiles, 32 k values per phase (K a multiple of 32), two LDS
+// stages so the copies of the next phase overlap the math of the current
+// one.  Further down, the same schedule on 64 x 64 tiles whose four waves
+// each take every fourth phase of the whole tile (gemm_f32_ksplit_kernel,
+// K a multiple of 4).
 //
 // Four waves in 2 x 2, each owning a 128 x 128 block of C as 4 x 4 blocks of
 // 32 x 32 (v_mfma_f32_32x32x2_f32, 256 accumulator registers per lane).  A
