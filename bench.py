@@ -37,7 +37,8 @@ Extra modes (used for counter runs under rocprofv3):
                         rectangular and awkward ones): TFLOP/s of the default
                         configuration, of every candidate configuration and
                         of torch.matmul (hipBLASLt, for context), one JSON
-                        line per shape (see bench_shape_sweep)
+                        line per shape (see bench_shape_sweep); with --row
+                        mixed, of gemm_mixed in --format
 """
 from __future__ import annotations
 
@@ -394,19 +395,39 @@ SWEEP_CANDIDATES = ["mfma64x64_bk32_w2x2_k4", "mfma64x64_bk16_w2x2_k4", "mfma64x
                     "mfma256x256_bk32_w2x2_sched"]
 
 
+MIXED_SWEEP_CANDIDATES = ["mixed64x64_bk64_w1x2", "mixed128x128_bk64_w2x2_directAB",
+                          "mixed256x256_bk64_w2x4_directAB", "mixed256x256_bk64_w4_sched"]
+
+
 def bench_shape_sweep(args) -> int:
     """For each shape (uniform[-1,1) operands, compact leading dimensions):
     the configuration gemm_f32 picks and the TFLOP/s of every candidate
     configuration through gemm_f32_variant, each run untimed for 0.1 s and
     then timed over 10 launches with HIP events on the launch stream, plus
-    torch.matmul on the same operands (fp32, TF32 off) for context."""
+    torch.matmul on the same operands (fp32, TF32 off) for context.  With
+    --row mixed the same for gemm_mixed on operands rounded to --format
+    (binary32 result), against torch.matmul in that format (16-bit result)."""
     import torch
 
     from shared_memory_tiled_amd import binding
 
     torch.backends.cuda.matmul.allow_tf32 = False
-    number = {binding.gemm_f32_variant_name(binding.DIAGNOSTIC_BASE + d): binding.DIAGNOSTIC_BASE + d
-              for d in range(binding.gemm_f32_num_diagnostic_variants())}
+    mixed = args.row == "mixed"
+    if mixed:
+        dtype = torch.bfloat16 if args.format == "bf16" else torch.float16
+        number = {binding.gemm_mixed_variant_name(v): v for v in range(binding.gemm_mixed_num_variants())}
+        candidates = MIXED_SWEEP_CANDIDATES
+        default_name = lambda M, N, K: binding.gemm_mixed_variant_name(binding.gemm_mixed_default_variant(M, N, K))
+        run = lambda X, Y, out, v=None: binding.gemm16(X, Y, out, variant=v)
+        context = lambda X, Y, out: torch.matmul(X, Y)
+    else:
+        dtype = torch.float32
+        number = {binding.gemm_f32_variant_name(binding.DIAGNOSTIC_BASE + d): binding.DIAGNOSTIC_BASE + d
+                  for d in range(binding.gemm_f32_num_diagnostic_variants())}
+        candidates = SWEEP_CANDIDATES
+        default_name = lambda M, N, K: binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(M, N, K))
+        run = lambda X, Y, out, v=None: binding.gemm(X, Y, out, variant=v)
+        context = lambda X, Y, out: torch.matmul(X, Y, out=out)
 
     def tflops(fn, flop, reps=10):
         settle(fn, 0.1)
@@ -421,18 +442,16 @@ def bench_shape_sweep(args) -> int:
 
     gen = torch.Generator(device="cuda").manual_seed(20261202)
     for (M, N, K) in SWEEP_SHAPES:
-        X = torch.rand((M, K), device="cuda", generator=gen) * 2 - 1
-        Y = torch.rand((K, N), device="cuda", generator=gen) * 2 - 1
+        X = (torch.rand((M, K), device="cuda", generator=gen) * 2 - 1).to(dtype)
+        Y = (torch.rand((K, N), device="cuda", generator=gen) * 2 - 1).to(dtype)
         out = torch.empty((M, N), device="cuda")
         flop = 2.0 * M * N * K
-        default = binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(M, N, K))
-        res = {c: round(tflops(lambda: binding.gemm(X, Y, out, variant=number[c]), flop), 1)
-               for c in SWEEP_CANDIDATES}
+        res = {c: round(tflops(lambda: run(X, Y, out, number[c]), flop), 1) for c in candidates}
         best = max(res, key=res.get)
-        line = {"M": M, "N": N, "K": K, "default": default,
-                "default_tflops": round(tflops(lambda: binding.gemm(X, Y, out), flop), 1),
+        line = {"M": M, "N": N, "K": K, "dtype": str(dtype).replace("torch.", ""), "default": default_name(M, N, K),
+                "default_tflops": round(tflops(lambda: run(X, Y, out), flop), 1),
                 "best": best, "best_tflops": res[best], "candidates_tflops": res,
-                "torch_matmul_tflops": round(tflops(lambda: torch.matmul(X, Y, out=out), flop), 1)}
+                "torch_matmul_tflops": round(tflops(lambda: context(X, Y, out), flop), 1)}
         line["default_over_best"] = round(line["default_tflops"] / res[best], 3)
         print(json.dumps(line), flush=True)
         del X, Y, out

@@ -266,11 +266,13 @@ const char *reduce_sum_f32_variant_name(int variant);  /* NULL if unknown */
  * gemm_mixed picks the tile shape for the problem; gemm_mixed_variant runs
  * tile configuration `variant` (0 .. gemm_mixed_num_variants() - 1, named by
  * gemm_mixed_variant_name).  The scheduled configuration
- * (mixed256x256_bk64_w4_sched, gemm_mixed's choice once there are 256 tiles
- * of 256 x 256) takes M and N multiples of 256, K a multiple of 64, 4-byte
- * aligned operands with even leading dimensions and operands under 2^31
- * bytes; other problems given to it run mixed256x256_bk64_w2x4_directAB,
- * which has the same tiles and summation order (the same bits).
+ * (mixed256x256_bk64_w4_sched, gemm_mixed's choice once there are 128 tiles
+ * of 256 x 256) takes K a multiple of 64, N even (M too for A stored
+ * transposed in gemm_mixed_op, and not N for B stored transposed),
+ * 4-byte aligned operands with even leading dimensions and operands under
+ * 2^31 bytes; edge tiles run whole and store only inside C.  Other problems
+ * given to it run mixed256x256_bk64_w2x4_directAB, which has the same tiles
+ * and summation order (the same bits).
  */
 #define GEMM_MIXED_BF16 0
 #define GEMM_MIXED_F16  1
@@ -283,8 +285,8 @@ int gemm_mixed_variant(int variant, int format, int64_t M, int64_t N, int64_t K,
                        float *C, int64_t ldc, void *stream);
 int gemm_mixed_num_variants(void);
 const char *gemm_mixed_variant_name(int variant);   /* NULL if unknown */
-/* The configuration gemm_mixed runs for an M x N x K product (depends on M
- * and N only; the scheduled configuration hands problems it does not take to
+/* The configuration gemm_mixed runs for an M x N x K product (the scheduled
+ * configuration hands problems it does not take to
  * its 8-wave fallback, as described above), or -1 for sizes that are negative
  * or above INT_MAX.  Launches nothing, needs no device. */
 int gemm_mixed_default_variant(int64_t M, int64_t N, int64_t K);

@@ -36,8 +36,9 @@
 // transposed through registers into k-contiguous rows (each thread loads a
 // block of 8 k rows x 8 or 4 n and writes 128-bit LDS rows of 8 k values; 8
 // lanes per store cycle write rows 4l + j, which f spreads over eight
-// positions).  gemm16_sched_kernel: full 256 x 256 tiles on four waves with
-// an explicit instruction order, the default for large problems.
+// positions).  gemm16_sched_kernel: 256 x 256 tiles (edge tiles run whole)
+// on four waves with an explicit instruction order, the default for large
+// problems.
 // gemm16_op_kernel: either factor stored transposed.
 //
 // Vector loads need 4-byte alignment (gfx9 runs global memory in unaligned
@@ -623,11 +624,21 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
         doff[A_COPIES + j] = TB::copy_src(wave_u, j, lane, n0, p.ldb);
     }
     constexpr int kRawBufferWord3 = 0x00020000;
-    const int64_t a_rows = KCA ? p.M : p.K, b_rows = KCB ? p.N : p.K;
+    // Each descriptor ends exactly at its stored matrix's last element.  An
+    // edge tile's copies past the last row read +0 without touching memory;
+    // past the last column of an mn-contiguous factor they read the next
+    // row (or +0 past the end), which only ever meets C entries outside the
+    // matrix, never stored.  K is a multiple of 64.  A 16-byte chunk across
+    // the end of an mn-contiguous factor's last row reads its dwords up to
+    // the descriptor's end and zeros past it (the range check is per dword;
+    // checked on MI355X); the factor's width is even, so no dword straddles
+    // that end.
+    const int64_t a_rows = KCA ? p.M : p.K, a_cols = KCA ? p.K : p.M;
+    const int64_t b_rows = KCB ? p.N : p.K, b_cols = KCB ? p.K : p.N;
     const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.A), (short)0, (int)(2 * a_rows * p.lda), kRawBufferWord3);
+        const_cast<uint16_t*>(p.A), (short)0, (int)(2 * ((a_rows - 1) * p.lda + a_cols)), kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.B), (short)0, (int)(2 * b_rows * p.ldb), kRawBufferWord3);
+        const_cast<uint16_t*>(p.B), (short)0, (int)(2 * ((b_rows - 1) * p.ldb + b_cols)), kRawBufferWord3);
     auto copy = [&](int j, int k0, int buf) __attribute__((always_inline)) {
         if (j < A_COPIES) {
             const int soff = TA::phase_bytes(k0, p.lda);
@@ -800,8 +811,9 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     steps012(no{}, 0, 0);
     step(yes{}, 1, no{}, 0, c0{}, c0{}, 0, 0);
 
-    // Guarded store (full tiles: the guard never fails).  Register r of lane
-    // (li, lh) is row 8 (r / 4) + 4 lh + r % 4 of its 32 x 32 block.
+    // Guarded store (edge tiles run whole and store only what lies inside
+    // C).  Register r of lane (li, lh) is row 8 (r / 4) + 4 lh + r % 4 of its
+    // 32 x 32 block.
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -1043,17 +1055,20 @@ struct MixedConfig {
     {{launch16<0, BM, BN, WM, WN, false, false, false>, launch16<0, BM, BN, WM, WN, D, true, T>},   \
      {launch16<1, BM, BN, WM, WN, false, false, false>, launch16<1, BM, BN, WM, WN, D, true, T>}}
 
-// The scheduled kernel takes full 256 x 256 tiles, K a multiple of 64,
-// vector-aligned operands and operands below 2^31 bytes (its copies use
-// 32-bit offsets); anything else runs the 8-wave kernel of the same tile
+// The scheduled kernel takes K a multiple of 64, an mn-contiguous factor's
+// width (M for A stored transposed, N for B as stored) even,
+// vector-aligned operands and operands below 2^31 bytes with a tile's
+// overhang (its copies use 32-bit offsets); edge tiles run whole (see its
+// descriptors).  Anything else runs the 8-wave kernel of the same tile
 // (gemm16_kernel, configuration 6, or gemm16_op_kernel): same tiles, same k
 // order, same bits.  op_a / op_b: 1 if that factor is stored transposed.
 bool sched_fits(const Gemm16Args& p, int op_a, int op_b) {
     const bool vec = ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 3) == 0 &&
                      (p.lda % 2) == 0 && (p.ldb % 2) == 0;
     const int64_t a_rows = op_a ? p.K : p.M, b_rows = op_b ? p.N : p.K;
-    return vec && p.M % 256 == 0 && p.N % 256 == 0 && p.K % kBK == 0 && p.K > 0 &&
-           2 * a_rows * p.lda < (1ll << 31) && 2 * b_rows * p.ldb < (1ll << 31);
+    const bool widths = (op_a == 0 || p.M % 2 == 0) && (op_b != 0 || p.N % 2 == 0);
+    return vec && widths && p.K % kBK == 0 && p.K > 0 && p.M > 0 && p.N > 0 &&
+           2 * (a_rows + 256) * p.lda < (1ll << 31) && 2 * (b_rows + 256) * p.ldb < (1ll << 31);
 }
 template <int FMT, bool KCA, bool KCB>
 hipError_t launch_sched_kernel(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
@@ -1115,7 +1130,7 @@ Launch16 op_launcher(int op_a, int op_b, bool vec) {
 }
 }  // namespace
 
-// op(A) x op(B): 256 x 256 tiles once there are 256 of them (the scheduled
+// op(A) x op(B): 256 x 256 tiles once there are 128 of them (the scheduled
 // kernel where it fits, else eight waves of gemm16_op_kernel), else 128 x 128
 // tiles of four waves.  A and B are the stored matrices; vector loads (and
 // the direct copies) need 4-byte aligned bases and even leading dimensions,
@@ -1124,7 +1139,7 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
     const bool vec = ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 3) == 0 &&
                      (p.lda % 2) == 0 && (p.ldb % 2) == 0;
     const int64_t t256 = (int64_t)ceil_div(p.M, 256) * ceil_div(p.N, 256);
-    const bool big = t256 >= 256;
+    const bool big = t256 >= 128;
     const int tile = big ? 256 : 128;
     const int tiles_m = ceil_div(p.M, tile), tiles_n = ceil_div(p.N, tile);
     const int64_t blocks = (int64_t)tiles_m * tiles_n;
@@ -1151,14 +1166,17 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
 int mixed_num_configs() { return kNumMixed; }
 const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed[c].name : nullptr; }
 
-// The largest tile that still gives every CU a workgroup, with both factors
-// copied straight into LDS; for 256 x 256 tiles the scheduled kernel (which
-// itself runs configuration 6 on problems it does not take).
-int mixed_pick_config(int M, int N, int /*K*/) {
+// 256 x 256 tiles on the scheduled kernel (which itself runs configuration
+// 6 on problems it does not take) from 128 of them, half the CUs: measured,
+// 144 such tiles (3072^3) still beat 576 of 128 x 128 by 40 %.  Else 128 x
+// 128 tiles with both factors copied straight into LDS from 128 of them
+// (64 for K of at least 2048), else 64 x 64 tiles (measured: 1536^3 346
+// against 276 TFLOP/s, 1024^3 141 against 156).
+int mixed_pick_config(int M, int N, int K) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
-    if (t256 >= 256) return 8;
-    if (t128 >= 256) return 7;
+    if (t256 >= 128) return 8;
+    if (t128 >= 128 || (t128 >= 64 && K >= 2048)) return 7;
     return 3;
 }
 

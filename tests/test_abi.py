@@ -274,7 +274,8 @@ def test_default_variant_choices(binding):
     a cost model of rounds, efficiency and fixed cost per tile gives them the
     shorter time (K >= 512), or in place of the split-phase tiles (K >= 384).
     For the 16-bit product the
-    scheduled kernel, 128 x 128 direct copies or 64 x 64 tiles.  Invalid
+    scheduled kernel from 128 tiles of 256 x 256, 128 x 128 direct copies
+    from 128 tiles of those (64 for K >= 2048), else 64 x 64 tiles.  Invalid
     sizes give -1."""
     f32 = {
         (8192, 8192, 8192): "mfma256x256_bk32_w2x2_sched",
@@ -313,7 +314,13 @@ def test_default_variant_choices(binding):
     mixed = {
         (8192, 8192, 8192): "mixed256x256_bk64_w4_sched",
         (4096, 4096, 64): "mixed256x256_bk64_w4_sched",
+        (3072, 3072, 3072): "mixed256x256_bk64_w4_sched",         # 144 tiles of 256
+        (4100, 4100, 4096): "mixed256x256_bk64_w4_sched",         # edge tiles, N even
+        (2560, 2560, 2560): "mixed128x128_bk64_w2x2_directAB",    # 100 tiles of 256, 400 of 128
         (2048, 2048, 2048): "mixed128x128_bk64_w2x2_directAB",
+        (1536, 1536, 1536): "mixed128x128_bk64_w2x2_directAB",    # 144 tiles of 128
+        (1024, 1024, 4096): "mixed128x128_bk64_w2x2_directAB",    # 64 tiles of 128, K >= 2048
+        (1024, 1024, 1024): "mixed64x64_bk64_w1x2",
         (1000, 1000, 1000): "mixed64x64_bk64_w1x2",
     }
     for (M, N, K), name in mixed.items():

@@ -152,3 +152,27 @@ def test_mixed_op_tensor_form():
     torch.cuda.synchronize()
     Cref, S = oracle.gemm16("bf16", A, B)
     check_close(C.cpu().numpy(), Cref, S, "tensor form TT")
+
+
+@pytest.mark.parametrize("ops", OPS, ids=lambda o: o[0] + o[1])
+def test_mixed_op_scheduled_edge_tiles(ops):
+    """144 tiles of 256 x 256 with edge tiles (the scheduled kernel from 128
+    such tiles) and integer data: bit exact against the full oracle and the
+    bits of gemm_mixed on explicitly transposed copies.  Widths 3004 and
+    2996 put a chunk across the end of an mn-contiguous factor's last row
+    (zeros past it); with M (N) odd and even leading dimensions, A stored
+    transposed (B as stored) runs the 8-wave kernel instead: the same bits."""
+    op_a, op_b = ops
+    for fmt in FORMATS:
+        for (M, N, K, pad) in ((3000, 3000, 128, (0, 0, 0)), (3004, 2996, 192, (0, 0, 0)),
+                               (3003, 2995, 64, (1, 1, 0))):
+            gen = np.random.default_rng([M, N, K, len(fmt), len(op_a + op_b), 5])
+            A, B = logical16(gen, fmt, M, N, K, "int")
+            prob = OpProblem(fmt, op_a, op_b, as_stored(op_a, A), as_stored(op_b, B), 0, pad)
+            say(f"mixed op scheduled edges {op_a}{op_b} {fmt} {M}x{N}x{K} pad={pad} int")
+            C = prob.run()
+            check_padding_untouched(C)
+            Cref, _ = oracle.gemm16(fmt, prob.A.view, prob.B.view, threads=16, op_a=op_a, op_b=op_b)
+            check_exact(C.view, Cref, f"scheduled edges {op_a}{op_b} {fmt} {M}x{N}x{K}")
+            plain = OpProblem(fmt, "N", "N", A, B).run(plain=True).view
+            assert np.array_equal(C.view.view(np.uint32), plain.view(np.uint32)), (fmt, op_a, op_b, M, N, K)
