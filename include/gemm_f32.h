@@ -267,10 +267,11 @@ const char *reduce_sum_f32_variant_name(int variant);  /* NULL if unknown */
  * tile configuration `variant` (0 .. gemm_mixed_num_variants() - 1, named by
  * gemm_mixed_variant_name).  The scheduled configuration
  * (mixed256x256_bk64_w4_sched, gemm_mixed's choice once there are 128 tiles
- * of 256 x 256) takes K a multiple of 64, N even (M too for A stored
+ * of 256 x 256) takes K a multiple of 8, N even (M too for A stored
  * transposed in gemm_mixed_op, and not N for B stored transposed),
  * 4-byte aligned operands with even leading dimensions and operands under
- * 2^31 bytes; edge tiles run whole and store only inside C.  Other problems
+ * 2^31 bytes; edge tiles run whole and store only inside C, and a last
+ * phase that reaches past K copies zeros there.  Other problems
  * given to it run mixed256x256_bk64_w2x4_directAB, which has the same tiles
  * and summation order (the same bits).
  */

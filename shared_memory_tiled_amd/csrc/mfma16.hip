@@ -583,6 +583,16 @@ struct SchedTile {
             return 2u * (uint32_t)(row * ld + mn0 + 8 * ((lane % 32) ^ (4 * (row & 3))));
         }
     }
+    // k of lane l's 16 bytes of copy j of wave w, relative to the phase's
+    // first k (KC: the first of its 8 values).
+    __host__ __device__ static int copy_k(int w, int j, int lane) {
+        if constexpr (KC) {
+            const int row = 8 * (w + j * NW) + lane / 8;
+            return 8 * ((lane % 8) ^ sched_swz(row));
+        } else {
+            return 2 * (w + j * NW) + lane / 32;
+        }
+    }
     // Byte offset of the phase at k0 from the phase at 0.
     __host__ __device__ static int phase_bytes(int k0, int64_t ld) { return KC ? 2 * k0 : 2 * k0 * (int)ld; }
 };
@@ -628,29 +638,46 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     // edge tile's copies past the last row read +0 without touching memory;
     // past the last column of an mn-contiguous factor they read the next
     // row (or +0 past the end), which only ever meets C entries outside the
-    // matrix, never stored.  K is a multiple of 64.  A 16-byte chunk across
-    // the end of an mn-contiguous factor's last row reads its dwords up to
-    // the descriptor's end and zeros past it (the range check is per dword;
+    // matrix, never stored.  A 16-byte chunk across the end of an
+    // mn-contiguous factor's last row reads its dwords up to the
+    // descriptor's end and zeros past it (the range check is per dword;
     // checked on MI355X); the factor's width is even, so no dword straddles
-    // that end.
+    // that end.  K is a multiple of 8: when the last phase reaches past K,
+    // its rows k >= K of an mn-contiguous factor lie past the end, and its
+    // 16-byte chunks at k >= K of a k-contiguous factor are pointed there
+    // (dlast), so they copy zeros; the 8-wave kernel's ghost phase has the
+    // same zeros, so both still give the same bits.
     const int64_t a_rows = KCA ? p.M : p.K, a_cols = KCA ? p.K : p.M;
     const int64_t b_rows = KCB ? p.N : p.K, b_cols = KCB ? p.K : p.N;
     const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(p.A), (short)0, (int)(2 * ((a_rows - 1) * p.lda + a_cols)), kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(p.B), (short)0, (int)(2 * ((b_rows - 1) * p.ldb + b_cols)), kRawBufferWord3);
-    auto copy = [&](int j, int k0, int buf) __attribute__((always_inline)) {
+    const int P = ceil_div(p.K, kBK);
+    constexpr uint32_t kPastEnd = 0x80000000u;              // beyond any descriptor here
+    uint32_t dlast[NCOPY];
+#pragma unroll
+    for (int j = 0; j < A_COPIES; ++j) {
+        const int ka = (P - 1) * kBK + TA::copy_k(wave_u, j, lane);
+        const int kb = (P - 1) * kBK + TB::copy_k(wave_u, j, lane);
+        dlast[j] = KCA && ka >= p.K ? kPastEnd : doff[j];
+        dlast[A_COPIES + j] = KCB && kb >= p.K ? kPastEnd : doff[A_COPIES + j];
+    }
+    // Copy j of the phase at k0 into stage buf; LAST: the phase is the last.
+    auto copy = [&](int j, int k0, int buf, auto lastc) __attribute__((always_inline)) {
+        constexpr bool LAST = decltype(lastc)::value;
+        const uint32_t voff = LAST ? dlast[j] : doff[j];
         if (j < A_COPIES) {
             const int soff = TA::phase_bytes(k0, p.lda);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc_a, (__attribute__((address_space(3))) void*)(lds + buf * TILE + TA::copy_dst(wave_u, j)), 16,
-                (int)doff[j], soff, 0, 0);
+                (int)voff, soff, 0, 0);
         } else {
             const int soff = TB::phase_bytes(k0, p.ldb);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc_b,
                 (__attribute__((address_space(3))) void*)(lds + (2 + buf) * TILE + TB::copy_dst(wave_u, j - A_COPIES)),
-                16, (int)doff[j], soff, 0, 0);
+                16, (int)voff, soff, 0, 0);
         }
     };
 
@@ -718,9 +745,9 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     // One step: the 16 matrix instructions on fragment set t (if MM); after
     // the q-th, reads 2q and 2q + 1 of step rs from stage rbuf into set t ^ 1
     // (if R) and, after each odd one, copy CB + q / 2 (while below CE) of the
-    // phase at k_copy into stage cbuf.
-    auto step = [&](auto mm, int t, auto reads, int rs, auto cb, auto ce, int k_copy,
-                    int cbuf) __attribute__((always_inline)) {
+    // phase at k_copy into stage cbuf (the last phase if lastc).
+    auto step = [&](auto mm, int t, auto reads, int rs, auto cb, auto ce, int k_copy, int cbuf,
+                    auto lastc) __attribute__((always_inline)) {
         constexpr bool MM = decltype(mm)::value;
         constexpr bool R = decltype(reads)::value;
         constexpr int CB = decltype(cb)::value, CE = decltype(ce)::value;
@@ -736,7 +763,7 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (q % 2 == 1 && CB + q / 2 < CE) {
-                copy(CB + q / 2, k_copy, cbuf);
+                copy(CB + q / 2, k_copy, cbuf, lastc);
                 __builtin_amdgcn_sched_barrier(0);
             }
         });
@@ -760,17 +787,17 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     using c8 = std::integral_constant<int, 8>;
     using c16 = std::integral_constant<int, 16>;
     // Steps 0..2 of the phase (step 0's fragments already read) and the wait
-    // for step 3's; copies 8..15 of the phase at k_copy into stage cbuf with
-    // step 0 if WC.
-    auto steps012 = [&](auto wc, int k_copy, int cbuf) __attribute__((always_inline)) {
+    // for step 3's; copies 8..15 of the phase at k_copy (the last phase if
+    // lastc) into stage cbuf with step 0 if WC.
+    auto steps012 = [&](auto wc, int k_copy, int cbuf, auto lastc) __attribute__((always_inline)) {
         constexpr bool WC = decltype(wc)::value;
         wait_set(0);
-        if constexpr (WC) step(yes{}, 0, yes{}, 1, c8{}, c16{}, k_copy, cbuf);
-        else step(yes{}, 0, yes{}, 1, c0{}, c0{}, 0, 0);
+        if constexpr (WC) step(yes{}, 0, yes{}, 1, c8{}, c16{}, k_copy, cbuf, lastc);
+        else step(yes{}, 0, yes{}, 1, c0{}, c0{}, 0, 0, no{});
         wait_set(1);
-        step(yes{}, 1, yes{}, 2, c0{}, c0{}, 0, 0);
+        step(yes{}, 1, yes{}, 2, c0{}, c0{}, 0, 0, no{});
         wait_set(0);
-        step(yes{}, 0, yes{}, 3, c0{}, c0{}, 0, 0);
+        step(yes{}, 0, yes{}, 3, c0{}, c0{}, 0, 0, no{});
         wait_set(1);
     };
 
@@ -778,38 +805,56 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     // ph - 1 and ph run the deferred last step of phase ph - 1 (with copies
     // 0..7 of phase ph + 1 and the first reads of phase ph, the read bases
     // already on its stage) and steps 0..2 of phase ph (copies 8..15 with
-    // step 0).
-    const int P = p.K / kBK;
+    // step 0).  The copies of phase P - 1 take the last phase's offsets: in
+    // the prologue when P <= 2, else in the loop's final pass (peeled) and
+    // the block after it.
+    if (P == 1) {
 #pragma unroll
-    for (int j = 0; j < NCOPY; ++j) copy(j, 0, 0);
+        for (int j = 0; j < NCOPY; ++j) copy(j, 0, 0, yes{});
+    } else {
+#pragma unroll
+        for (int j = 0; j < NCOPY; ++j) copy(j, 0, 0, no{});
+    }
     barrier();
 #pragma unroll
     for (int i = 0; i < NREAD; ++i) read_op(0, 0, i);
-    if (P > 1) {
+    if (P == 2) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) copy(j, kBK, 1);
+        for (int j = 0; j < 8; ++j) copy(j, kBK, 1, yes{});
+    } else if (P > 2) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) copy(j, kBK, 1, no{});
     }
     __builtin_amdgcn_sched_barrier(0);
     int ph = 0;
-    for (; ph + 2 < P; ++ph) {
+    for (; ph + 3 < P; ++ph) {
         const int cur = ph & 1;
-        steps012(yes{}, (ph + 1) * kBK, cur ^ 1);
+        steps012(yes{}, (ph + 1) * kBK, cur ^ 1, no{});
         flip_stage(cur);
         __builtin_amdgcn_sched_barrier(0);
         barrier();
-        step(yes{}, 1, yes{}, 0, c0{}, c8{}, (ph + 2) * kBK, cur);
+        step(yes{}, 1, yes{}, 0, c0{}, c8{}, (ph + 2) * kBK, cur, no{});
     }
-    if (ph + 1 < P) {
+    if (ph + 2 < P) {                                       // copies 0..7 of the last phase
         const int cur = ph & 1;
-        steps012(yes{}, (ph + 1) * kBK, cur ^ 1);
+        steps012(yes{}, (ph + 1) * kBK, cur ^ 1, no{});
         flip_stage(cur);
         __builtin_amdgcn_sched_barrier(0);
         barrier();
-        step(yes{}, 1, yes{}, 0, c0{}, c0{}, 0, 0);
+        step(yes{}, 1, yes{}, 0, c0{}, c8{}, (ph + 2) * kBK, cur, yes{});
         ++ph;
     }
-    steps012(no{}, 0, 0);
-    step(yes{}, 1, no{}, 0, c0{}, c0{}, 0, 0);
+    if (ph + 1 < P) {                                       // copies 8..15 of the last phase
+        const int cur = ph & 1;
+        steps012(yes{}, (ph + 1) * kBK, cur ^ 1, yes{});
+        flip_stage(cur);
+        __builtin_amdgcn_sched_barrier(0);
+        barrier();
+        step(yes{}, 1, yes{}, 0, c0{}, c0{}, 0, 0, no{});
+        ++ph;
+    }
+    steps012(no{}, 0, 0, no{});
+    step(yes{}, 1, no{}, 0, c0{}, c0{}, 0, 0, no{});
 
     // Guarded store (edge tiles run whole and store only what lies inside
     // C).  Register r of lane (li, lh) is row 8 (r / 4) + 4 lh + r % 4 of its
@@ -1055,7 +1100,7 @@ struct MixedConfig {
     {{launch16<0, BM, BN, WM, WN, false, false, false>, launch16<0, BM, BN, WM, WN, D, true, T>},   \
      {launch16<1, BM, BN, WM, WN, false, false, false>, launch16<1, BM, BN, WM, WN, D, true, T>}}
 
-// The scheduled kernel takes K a multiple of 64, an mn-contiguous factor's
+// The scheduled kernel takes K a multiple of 8, an mn-contiguous factor's
 // width (M for A stored transposed, N for B as stored) even,
 // vector-aligned operands and operands below 2^31 bytes with a tile's
 // overhang (its copies use 32-bit offsets); edge tiles run whole (see its
@@ -1067,7 +1112,7 @@ bool sched_fits(const Gemm16Args& p, int op_a, int op_b) {
                      (p.lda % 2) == 0 && (p.ldb % 2) == 0;
     const int64_t a_rows = op_a ? p.K : p.M, b_rows = op_b ? p.N : p.K;
     const bool widths = (op_a == 0 || p.M % 2 == 0) && (op_b != 0 || p.N % 2 == 0);
-    return vec && widths && p.K % kBK == 0 && p.K > 0 && p.M > 0 && p.N > 0 &&
+    return vec && widths && p.K % 8 == 0 && p.K > 0 && p.M > 0 && p.N > 0 &&
            2 * (a_rows + 256) * p.lda < (1ll << 31) && 2 * (b_rows + 256) * p.ldb < (1ll << 31);
 }
 template <int FMT, bool KCA, bool KCB>

@@ -100,21 +100,24 @@ def test_mixed_every_variant(fmt):
                 check(prob, prob.run(variant=v), dist, f"variant {v} {M}x{N}x{K} {dist}")
 
 
-SCHED = 8          # the scheduled 4-wave kernel (256 x 256 tiles, K % 64 == 0, N even)
+SCHED = 8          # the scheduled 4-wave kernel (256 x 256 tiles, K % 8 == 0, N even)
 SCHED_SHAPES = [(256, 256, 64), (256, 512, 128), (512, 256, 192), (768, 1024, 320), (1024, 1024, 1024),
                 (512, 768, 4160),
                 # edge tiles run whole: ragged M (any), ragged N (even; N % 8 = 4
                 # or 2: the last row's chunk across the end reads zeros past it)
                 (264, 520, 128), (1000, 1000, 1024), (300, 776, 192), (8, 264, 64), (301, 516, 128),
-                (257, 1026, 64)]
+                (257, 1026, 64),
+                # K a multiple of 8, the last phase partial: one, two, three and more phases
+                (256, 256, 8), (512, 512, 72), (512, 256, 136), (264, 520, 200), (300, 776, 1000)]
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_mixed_scheduled_kernel(fmt):
     """The scheduled kernel on shapes it takes: one, two, three and more
-    phases (its prologue, tail and main-loop paths), long K and edge tiles
+    phases (its prologue, tail and main-loop paths), long K, edge tiles
     (rows past M and columns past N copy zeros or feed only unstored C
-    entries; the NaN padding of the operands must not reach C); integer data
+    entries; the NaN padding of the operands must not reach C) and a last
+    phase that reaches past K (its chunks there copy zeros); integer data
     exactly, float data within the bound, and the same bits as the 8-wave
     kernel of configuration 6 (same tiles, same k order)."""
     assert binding.gemm_mixed_variant_name(SCHED) == "mixed256x256_bk64_w4_sched"
@@ -132,10 +135,11 @@ def test_mixed_scheduled_kernel(fmt):
 
 def test_mixed_scheduled_kernel_padded_and_fallback():
     """Padded leading dimensions and ragged M (still taken by the scheduled
-    kernel), and shapes it does not take (odd N, ragged K, 2-byte-offset
-    views), which run configuration 6 instead: same bits either way."""
+    kernel), and shapes it does not take (odd N, K not a multiple of 8,
+    2-byte-offset views), which run configuration 6 instead: same bits
+    either way."""
     gen = np.random.default_rng(123)
-    cases = [(512, 512, 256, 0, (8, 16, 3)), (520, 512, 256, 0, (0, 0, 0)), (512, 512, 200, 0, (0, 0, 0)),
+    cases = [(512, 512, 256, 0, (8, 16, 3)), (520, 512, 256, 0, (0, 0, 0)), (512, 512, 204, 0, (0, 0, 0)),
              (512, 512, 256, 1, (2, 2, 2)), (512, 515, 256, 0, (0, 1, 0)), (520, 264, 256, 0, (8, 16, 3))]
     for (M, N, K, offset, pad) in cases:
         prob, _, _ = make("bf16", M, N, K, "uniform", gen, offset, pad)
