@@ -33,7 +33,7 @@ Extra modes (used for counter runs under rocprofv3):
                         per workload with the median and best launch time
                         (HIP events around every launch), then the oracle's
                         time on this host (see bench_all_workloads)
-    --shape-sweep       the tile choice on 31 shapes (512^3 .. 8192^3,
+    --shape-sweep       the tile choice on 33 shapes (512^3 .. 8192^3,
                         rectangular and awkward ones): TFLOP/s of the default
                         configuration, of every candidate configuration and
                         of torch.matmul (hipBLASLt, for context), one JSON
@@ -388,7 +388,8 @@ SWEEP_SHAPES = ([(n, n, n) for n in (512, 768, 1024, 1536, 2048, 2560, 3072, 358
                 [(4100, 4100, 4096), (4000, 5000, 4096), (6000, 6000, 6000), (8200, 8200, 4096),
                  (8192, 4096, 2048), (2048, 8192, 4096), (16384, 1024, 4096), (1024, 16384, 2048),
                  (5000, 3000, 2000), (3000, 7000, 1024), (1000, 2000, 500), (2048, 2048, 256),
-                 (4096, 4096, 256), (1024, 1024, 4096), (1000, 1000, 1000), (3000, 3000, 384)])
+                 (4096, 4096, 256), (1024, 1024, 4096), (1000, 1000, 1000), (3000, 3000, 384),
+                 (8192, 8192, 8100), (4096, 4096, 4100)])
 SWEEP_CANDIDATES = ["mfma64x64_bk32_w2x2_k4", "mfma64x64_bk16_w2x2_k4", "mfma64x64_bk32_w1x1_k4_sched",
                     "mfma128x128_bk16_w2x2",
                     "mfma128x128_bk32_w2x2_sched", "mfma256x256_bk32_w2x4_direct",

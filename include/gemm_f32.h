@@ -84,7 +84,7 @@ extern "C" {
  *      buffered LDS tiles (the default).  The tile follows from how full the
  *      last round of 256 workgroups would run: 256 x 256 tiles with direct
  *      global-to-LDS copies into an XOR-swizzled layout (on four waves with
- *      a fixed instruction order when K is a multiple of 32 and M and N of 4
+ *      a fixed instruction order when K, M and N are multiples of 4
  *      and each stored factor is under 2 GiB, else on eight waves; both give
  *      the same bits), else 128 x 128 tiles, else 64 x 64 tiles whose phases
  *      are split over four groups of four waves.  With K, M and N multiples
@@ -92,7 +92,7 @@ extern "C" {
  *      every fourth phase (partial tiles added in wave order, so results are
  *      deterministic and the same for every op pair) replace that choice
  *      where a cost model of rounds, per-kernel efficiency and fixed cost
- *      per tile gives them the shorter time (K >= 512), or in place of the
+ *      per tile gives them the shorter time (K >= 448), or in place of the
  *      split-phase tiles (K >= 384).  gemm_f32_default_variant() names the
  *      configuration a shape runs.
  * Variants numbered from 16 up are diagnostic layouts of the same rungs, kept

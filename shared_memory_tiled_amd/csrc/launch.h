@@ -49,8 +49,8 @@ int mfma_num_configs();
 const char* mfma_config_name(int config);
 int mfma_pick_config(int M, int N, int K);
 // Four-wave kernel with an explicit instruction order (mfma_sched.hip) on
-// 256 x 256 or 128 x 128 tiles: whether it takes the problem (K a multiple
-// of 32, M and N of 4, stored factors below 2^31 bytes), and its launcher
+// 256 x 256 or 128 x 128 tiles: whether it takes the problem (K, M and N
+// multiples of 4, stored factors below 2^31 bytes), and its launcher
 // (op 1: factor stored transposed; tile 256 or 128).
 bool sched_f32_fits(const GemmArgs& p, int op_a, int op_b);
 hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m, int tile);

@@ -668,8 +668,8 @@ constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 int mfma_num_configs() { return kNumConfigs; }
 const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConfigs[c].name : nullptr; }
 
-// Tile choice.  Shapes the four-wave schedule takes (mfma_sched.hip: K a
-// multiple of 32, M and N of 4): 256 x 256 tiles when there are at least
+// Tile choice.  Shapes the four-wave schedule takes (mfma_sched.hip: K, M
+// and N multiples of 4): 256 x 256 tiles when there are at least
 // 256 of them and their rounds of 256 workgroups (one per CU) run at least
 // 95 % full, else its 128 x 128 tiles (two workgroups per CU) when there are
 // at least 128, else the split-phase 64 x 64 tiles.  Other shapes: 256 x
@@ -681,7 +681,7 @@ const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConf
 // to hide latency; 32-deep phases when there are at most 256 such tiles,
 // 16-deep otherwise).
 //
-// Then, for K of at least 512 and K, M and N multiples of 4, the 64 x 64
+// Then, for K of at least 448 and K, M and N multiples of 4, the 64 x 64
 // tiles whose four waves split the phases (mfma_sched.hip) replace that
 // choice when a cost model gives them the shorter time.  The model charges
 // each round of 256 tiles the tile's work at a kernel's measured fraction
@@ -689,9 +689,10 @@ const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConf
 // store): four-wave 256 x 256 0.985 and 11 us, 128 x 128 0.975 and 5.3 us,
 // eight-wave 256 x 256 0.92 and 11 us, register-staged 128 x 128 0.85 and
 // 5.3 us, 64 x 64 with split phases 0.914 and 3 us (fitted to 31 shapes
-// from 512^3 to 8192^3; below K = 512 the fixed cost of the 64 x 64 tiles
-// is not captured well enough: there they only replace the split-phase
-// tiles, from K = 384, three phases per wave).  Every picked configuration
+// from 512^3 to 8192^3; below K = 448 the model misjudges them against
+// two co-resident 128 x 128 workgroups per CU, e.g. at 3000 x 3000 x 384:
+// there they only replace the split-phase tiles, from K = 384, three
+// phases per wave).  Every picked configuration
 // is built for all four op combinations.
 namespace {
 // Modelled time (ns) of a configuration: rounds x (tile work / efficiency
@@ -721,7 +722,7 @@ int mfma_pick_config(int M, int N, int K) {
     const int64_t slots256 = (t256 + 255) / 256 * 256, slots128 = (t128 + 255) / 256 * 256;
     const int small = t64 <= 256 ? 14 : 13;
     int pick;
-    if (K % 32 == 0 && K > 0 && M % 4 == 0 && N % 4 == 0) {
+    if (K % 4 == 0 && K > 0 && M % 4 == 0 && N % 4 == 0) {
         if (t256 >= 256 && t256 * 20 >= slots256 * 19) pick = 16;
         else pick = t128 >= 128 ? 18 : small;
     } else {
@@ -731,7 +732,7 @@ int mfma_pick_config(int M, int N, int K) {
         else pick = small;
     }
     const bool split_fits = K % 4 == 0 && M % 4 == 0 && N % 4 == 0;
-    if (split_fits && ((pick == small && K >= 384) || (K >= 512 && model_ns(20, M, N, K) < model_ns(pick, M, N, K))))
+    if (split_fits && ((pick == small && K >= 384) || (K >= 448 && model_ns(20, M, N, K) < model_ns(pick, M, N, K))))
         pick = 20;
     return pick;
 }

@@ -4,7 +4,8 @@
 // notes, sections 5.4-5.5: per phase every thread of a block copies part of
 // an A and a B tile into shared memory, a barrier, the multiply-adds from the
 // tiles, a barrier, and a guarded store at the edges) on 256 x 256 (or 128 x
-// 128) output tiles, 32 k values per phase (K a multiple of 32), two LDS
+// 128) output tiles, 32 k values per phase (K a multiple of 4; a last
+// phase past K copies zeros there), two LDS
 // stages so the copies of the next phase overlap the math of the current
 // one.  Further down, the same schedule on 64 x 64 tiles whose four waves
 // each take every fourth phase of the whole tile (gemm_f32_ksplit_kernel,
@@ -197,26 +198,44 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     // edge tile's copies past the last row read +0 without touching memory;
     // past the last column of an mn-contiguous factor they read the next
     // row (or +0 past the end), which only ever meets C entries outside the
-    // matrix, never stored.  K is a multiple of 32, and an mn-contiguous
-    // factor's extent a multiple of 4, so no 16-byte chunk straddles an edge.
+    // matrix, never stored.  An mn-contiguous factor's extent is a multiple
+    // of 4, so no 16-byte chunk straddles an edge.  K is a multiple of 4:
+    // when the last phase reaches past K, its rows k >= K of an
+    // mn-contiguous factor lie past the end, and its chunks at k >= K of a
+    // k-contiguous factor are pointed there (dlast), so they copy zeros;
+    // the other kernels' ghost phases hold the same zeros, so all still give
+    // the same bits.
     const int64_t a_rows = KCA ? p.M : p.K, a_cols = KCA ? p.K : p.M;
     const int64_t b_rows = KCB ? p.N : p.K, b_cols = KCB ? p.K : p.N;
     const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(p.A), (short)0, (int)(4 * ((a_rows - 1) * p.lda + a_cols)), kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(p.B), (short)0, (int)(4 * ((b_rows - 1) * p.ldb + b_cols)), kRawBufferWord3);
-    auto copy = [&](int j, int k0, int buf) __attribute__((always_inline)) {
+    const int P = ceil_div(p.K, kSBK);
+    constexpr uint32_t kPastEnd = 0x80000000u;              // beyond any descriptor here
+    uint32_t dlast[NCOPY];
+#pragma unroll
+    for (int j = 0; j < A_COPIES; ++j) {
+        const int ka = (P - 1) * kSBK + TA::copy_k(wave_u, j, lane);
+        const int kb = (P - 1) * kSBK + TB::copy_k(wave_u, j, lane);
+        dlast[j] = KCA && ka >= p.K ? kPastEnd : doff[j];
+        dlast[A_COPIES + j] = KCB && kb >= p.K ? kPastEnd : doff[A_COPIES + j];
+    }
+    // Copy j of the phase at k0 into stage buf; LAST: the phase is the last.
+    auto copy = [&](int j, int k0, int buf, auto lastc) __attribute__((always_inline)) {
+        constexpr bool LAST = decltype(lastc)::value;
+        const uint32_t voff = LAST ? dlast[j] : doff[j];
         if (j < A_COPIES) {
             const int soff = TA::phase_bytes(k0, p.lda);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc_a, (__attribute__((address_space(3))) void*)(lds + buf * A_ST + TA::copy_dst(wave_u, j)), 16,
-                (int)doff[j], soff, 0, 0);
+                (int)voff, soff, 0, 0);
         } else {
             const int soff = TB::phase_bytes(k0, p.ldb);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc_b,
                 (__attribute__((address_space(3))) void*)(lds + 2 * A_ST + buf * B_ST + TB::copy_dst(wave_u, j - A_COPIES)),
-                16, (int)doff[j], soff, 0, 0);
+                16, (int)voff, soff, 0, 0);
         }
     };
 
@@ -276,9 +295,9 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     // (instruction q: e = q / (FM FN), block (q / FN % FM, q % FN)); after the
     // q-th (q < NREAD), read q of step rs into set t ^ 1 (if R) and, after
     // every CSTRIDE-th, copy CB + q / CSTRIDE (while below CE) of the phase at
-    // k_copy into stage cbuf.
-    auto step = [&](int t, auto reads, int rs, auto cb, auto ce, int k_copy,
-                    int cbuf) __attribute__((always_inline)) {
+    // k_copy (the last phase if lastc) into stage cbuf.
+    auto step = [&](int t, auto reads, int rs, auto cb, auto ce, int k_copy, int cbuf,
+                    auto lastc) __attribute__((always_inline)) {
         constexpr bool R = decltype(reads)::value;
         constexpr int CB = decltype(cb)::value, CE = decltype(ce)::value;
         unroll<NMFMA>([&](auto qc) __attribute__((always_inline)) {
@@ -292,7 +311,7 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (q % CSTRIDE == CSTRIDE - 1 && CB + q / CSTRIDE < CE) {
-                copy(CB + q / CSTRIDE, k_copy, cbuf);
+                copy(CB + q / CSTRIDE, k_copy, cbuf, lastc);
                 __builtin_amdgcn_sched_barrier(0);
             }
         });
@@ -314,56 +333,74 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     using cH = std::integral_constant<int, HALF>;
     using cN = std::integral_constant<int, NCOPY>;
     // Steps 0..2 of the phase (step 0's fragments already read) and the wait
-    // for step 3's; copies 8..15 of the phase at k_copy into stage cbuf with
-    // step 0 if WC.
-    auto steps012 = [&](auto wc, int k_copy, int cbuf) __attribute__((always_inline)) {
+    // for step 3's; copies HALF.. of the phase at k_copy (the last phase if
+    // lastc) into stage cbuf with step 0 if WC.
+    auto steps012 = [&](auto wc, int k_copy, int cbuf, auto lastc) __attribute__((always_inline)) {
         constexpr bool WC = decltype(wc)::value;
         wait_set(0);
-        if constexpr (WC) step(0, yes{}, 1, cH{}, cN{}, k_copy, cbuf);
-        else step(0, yes{}, 1, c0{}, c0{}, 0, 0);
+        if constexpr (WC) step(0, yes{}, 1, cH{}, cN{}, k_copy, cbuf, lastc);
+        else step(0, yes{}, 1, c0{}, c0{}, 0, 0, no{});
         wait_set(1);
-        step(1, yes{}, 2, c0{}, c0{}, 0, 0);
+        step(1, yes{}, 2, c0{}, c0{}, 0, 0, no{});
         wait_set(0);
-        step(0, yes{}, 3, c0{}, c0{}, 0, 0);
+        step(0, yes{}, 3, c0{}, c0{}, 0, 0, no{});
         wait_set(1);
     };
 
     // Stage ph & 1 holds phase ph.  Between the barriers that end phases
     // ph - 1 and ph run the deferred last step of phase ph - 1 (with copies
-    // 0..7 of phase ph + 1 and the first reads of phase ph, the read bases
-    // already on its stage) and steps 0..2 of phase ph (copies 8..15 with
-    // step 0).
-    const int P = p.K / kSBK;
+    // 0..HALF-1 of phase ph + 1 and the first reads of phase ph, the read
+    // bases already on its stage) and steps 0..2 of phase ph (the other
+    // copies with step 0).  The copies of phase P - 1 take the last phase's
+    // offsets: in the prologue when P <= 2, else in the loop's final pass
+    // (peeled) and the block after it.
+    if (P == 1) {
 #pragma unroll
-    for (int j = 0; j < NCOPY; ++j) copy(j, 0, 0);
+        for (int j = 0; j < NCOPY; ++j) copy(j, 0, 0, yes{});
+    } else {
+#pragma unroll
+        for (int j = 0; j < NCOPY; ++j) copy(j, 0, 0, no{});
+    }
     barrier();
 #pragma unroll
     for (int i = 0; i < NREAD; ++i) read_op(0, 0, i);
-    if (P > 1) {
+    if (P == 2) {
 #pragma unroll
-        for (int j = 0; j < HALF; ++j) copy(j, kSBK, 1);
+        for (int j = 0; j < HALF; ++j) copy(j, kSBK, 1, yes{});
+    } else if (P > 2) {
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) copy(j, kSBK, 1, no{});
     }
     __builtin_amdgcn_sched_barrier(0);
     int ph = 0;
-    for (; ph + 2 < P; ++ph) {
+    for (; ph + 3 < P; ++ph) {
         const int cur = ph & 1;
-        steps012(yes{}, (ph + 1) * kSBK, cur ^ 1);
+        steps012(yes{}, (ph + 1) * kSBK, cur ^ 1, no{});
         flip_stage(cur);
         __builtin_amdgcn_sched_barrier(0);
         barrier();
-        step(1, yes{}, 0, c0{}, cH{}, (ph + 2) * kSBK, cur);
+        step(1, yes{}, 0, c0{}, cH{}, (ph + 2) * kSBK, cur, no{});
     }
-    if (ph + 1 < P) {
+    if (ph + 2 < P) {                                       // copies 0..HALF-1 of the last phase
         const int cur = ph & 1;
-        steps012(yes{}, (ph + 1) * kSBK, cur ^ 1);
+        steps012(yes{}, (ph + 1) * kSBK, cur ^ 1, no{});
         flip_stage(cur);
         __builtin_amdgcn_sched_barrier(0);
         barrier();
-        step(1, yes{}, 0, c0{}, c0{}, 0, 0);
+        step(1, yes{}, 0, c0{}, cH{}, (ph + 2) * kSBK, cur, yes{});
         ++ph;
     }
-    steps012(no{}, 0, 0);
-    step(1, no{}, 0, c0{}, c0{}, 0, 0);
+    if (ph + 1 < P) {                                       // the rest of the last phase's copies
+        const int cur = ph & 1;
+        steps012(yes{}, (ph + 1) * kSBK, cur ^ 1, yes{});
+        flip_stage(cur);
+        __builtin_amdgcn_sched_barrier(0);
+        barrier();
+        step(1, yes{}, 0, c0{}, c0{}, 0, 0, no{});
+        ++ph;
+    }
+    steps012(no{}, 0, 0, no{});
+    step(1, no{}, 0, c0{}, c0{}, 0, 0, no{});
 
     // Guarded store.  Register r of lane (li, lh) is row rho = 8 (r / 4) +
     // 4 lh + r % 4 and column li of its 32 x 32 block; block (i, j) of a
@@ -698,12 +735,12 @@ hipError_t launch_sched_f32_tile(const GemmArgs& p, hipStream_t s, int op_a, int
 }
 }  // namespace
 
-// K a multiple of 32 and M, N multiples of 4 (edge tiles run whole, see the
-// descriptors above).  Any leading dimension and dword alignment will do:
+// K, M and N multiples of 4 (edge tiles and a last phase past K run whole,
+// see the descriptors above).  Any leading dimension and dword alignment will do:
 // gfx9 runs memory in unaligned-access mode, so the 16-byte copies and
 // stores need only the 4-byte alignment the entry points check.
 bool sched_f32_fits(const GemmArgs& p, int op_a, int op_b) {
-    if (p.K % kSBK != 0 || p.K <= 0 || p.M % 4 != 0 || p.N % 4 != 0) return false;
+    if (p.K % 4 != 0 || p.K <= 0 || p.M % 4 != 0 || p.N % 4 != 0) return false;
     // A stored M x K (op N) or K x M (op T); B stored K x N or N x K.  Byte
     // offsets, edge tiles' overhang included, stay below 2^31.
     const int64_t a_rows = op_a ? p.K : p.M, b_rows = op_b ? p.N : p.K;

@@ -262,8 +262,8 @@ def test_mixed_op_validation_without_launch(lib, op_a, op_b, args, code):
 
 def test_default_variant_choices(binding):
     """The configuration the default entry points run, by problem size (no
-    device needed).  Shapes the four-wave schedule takes (K a multiple of 32,
-    M and N of 4): its 256 x 256 tiles when at least 256 of them fill their
+    device needed).  Shapes the four-wave schedule takes (K, M and N
+    multiples of 4): its 256 x 256 tiles when at least 256 of them fill their
     rounds of 256 to 95 %, else its 128 x 128 tiles when there are at least
     128, else the split-phase 64 x 64 tiles.  Other shapes: eight-wave 256 x
     256 tiles when their rounds run at least 80 % full (75 % when 128 x 128
@@ -272,7 +272,7 @@ def test_default_variant_choices(binding):
     tiles (32-deep phases for at most 256 tiles).  Then, with K, M and N
     multiples of 4, the 64 x 64 tiles whose four waves split the phases where
     a cost model of rounds, efficiency and fixed cost per tile gives them the
-    shorter time (K >= 512), or in place of the split-phase tiles (K >= 384).
+    shorter time (K >= 448), or in place of the split-phase tiles (K >= 384).
     For the 16-bit product the
     scheduled kernel from 128 tiles of 256 x 256, 128 x 128 direct copies
     from 128 tiles of those (64 for K >= 2048), else 64 x 64 tiles.  Invalid
@@ -293,12 +293,14 @@ def test_default_variant_choices(binding):
         (1536, 1536, 1536): "mfma64x64_bk32_w1x1_k4_sched",       # 144 tiles of 128, 576 of 64
         (3072, 3072, 3072): "mfma64x64_bk32_w1x1_k4_sched",       # 2304 tiles of 64: 9 full rounds
         (1024, 1024, 1024): "mfma64x64_bk32_w1x1_k4_sched",
-        (4096, 4096, 48): "mfma256x256_bk32_w2x4_direct",
+        (4096, 4096, 48): "mfma256x256_bk32_w2x2_sched",          # K % 32 = 16: last phase past K
         (8193, 8190, 96): "mfma256x256_bk32_w2x4_direct",
         (4096, 4096, 0): "mfma256x256_bk32_w2x4_direct",
-        (6000, 6000, 6000): "mfma64x64_bk32_w1x1_k4_sched",       # K % 32 = 16, K % 4 = 0
-        (5000, 3000, 2000): "mfma64x64_bk32_w1x1_k4_sched",
-        (3840, 2048, 100): "mfma128x128_bk16_w2x2",
+        (6000, 6000, 6000): "mfma128x128_bk32_w2x2_sched",        # K % 32 = 16: last phase past K
+        (5000, 3000, 2000): "mfma128x128_bk32_w2x2_sched",
+        (4608, 4608, 4608): "mfma64x64_bk32_w1x1_k4_sched",       # 5184 tiles of 64: 20.25 rounds
+        (3840, 2048, 100): "mfma128x128_bk32_w2x2_sched",
+        (3840, 2048, 102): "mfma128x128_bk16_w2x2",               # K % 4 = 2
         (4100, 4097, 515): "mfma64x64_bk16_w2x2_k4",              # K % 4 = 3
         (3000, 3000, 3000): "mfma64x64_bk32_w1x1_k4_sched",
         (1000, 1000, 1000): "mfma64x64_bk32_w1x1_k4_sched",

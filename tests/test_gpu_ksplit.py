@@ -1,7 +1,7 @@
 """The 64 x 64 kernel whose four waves split the phases of one tile (each
 wave the whole tile over every fourth 32-deep phase, partial tiles added in
 wave order), which gemm_f32 and gemm_f32_op run for K, M and N multiples of 4
-where its cost model wins (K >= 512) or in place of the split-phase tiles
+where its cost model wins (K >= 448) or in place of the split-phase tiles
 (K >= 384).  Its phases are aligned to the end of K, so with K not a multiple
 of 32 the first phase reaches below k = 0 and those lanes copy zeros.
 
@@ -81,7 +81,7 @@ class Problem:
 
 def test_kernel_is_the_default_for_its_shapes():
     for shape in [(1000, 1000, 1000), (300, 260, 1000), (252, 136, 516), (3072, 3072, 3072),
-                  (6000, 6000, 6000), (1000, 2000, 500), (5000, 3000, 2000)]:
+                  (4608, 4608, 4608), (1000, 2000, 500), (4100, 4104, 4100), (2000, 1000, 996)]:
         assert default_name(*shape) == KS, shape
     for shape in [(1000, 1000, 380), (1002, 1000, 1000), (1000, 1000, 1001), (8192, 8192, 8192),
                   (2048, 2048, 2048)]:
@@ -125,8 +125,8 @@ SAMPLED = [
     # shape, offset, (pad A, pad B, pad C)
     ((1000, 1000, 1000), 1, (3, 5, 7)),
     ((3072, 3072, 3072), 0, (0, 0, 0)),
-    ((6000, 6000, 6000), 3, (1, 2, 1)),
-    ((5000, 3000, 2000), 1, (4, 0, 3)),
+    ((4100, 4104, 4100), 3, (1, 2, 1)),
+    ((2000, 1000, 996), 1, (4, 0, 3)),
 ]
 
 

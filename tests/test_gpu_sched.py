@@ -1,8 +1,9 @@
 """The four-wave scheduled fp32 kernel on 256 x 256 and 128 x 128 tiles,
-which gemm_f32 and gemm_f32_op run when K is a multiple of 32 and M and N of
-4 (the 256 x 256 form when its tiles fill their rounds of 256 workgroups to
-95 %, else the 128 x 128 form when there are at least 128 such tiles; edge
-tiles run whole and store only what lies inside C).
+which gemm_f32 and gemm_f32_op run when K, M and N are multiples of 4 (the
+256 x 256 form when its tiles fill their rounds of 256 workgroups to 95 %,
+else the 128 x 128 form when there are at least 128 such tiles, unless the
+k-split 64 x 64 tiles win the cost model; edge tiles run whole and store only
+what lies inside C, and a last phase that reaches past K copies zeros there).
 
 Checked against the oracle (every entry on short-K problems, sampled
 entries on longer ones; exact on integer inputs) for all four op pairs, on
@@ -80,9 +81,11 @@ def default_name(M, N, K):
 
 
 def test_scheduled_kernels_are_the_default_for_their_shapes():
-    for shape in [(4096, 4096, 32), (4096, 8192, 96), (8192, 8192, 8192), (7940, 8132, 32), (8132, 7940, 64)]:
+    for shape in [(4096, 4096, 32), (4096, 8192, 96), (8192, 8192, 8192), (7940, 8132, 32), (8132, 7940, 64),
+                  (4096, 4096, 100), (4096, 4096, 4), (8192, 8192, 8100)]:
         assert default_name(*shape) == KERNELS["tile256"][0], shape
-    for shape in [(2048, 2048, 32), (1500, 2044, 64), (2052, 3000, 96), (4100, 6200, 160), (8200, 8200, 64)]:
+    for shape in [(2048, 2048, 32), (1500, 2044, 64), (2052, 3000, 96), (4100, 6200, 160), (8200, 8200, 64),
+                  (2048, 2048, 100), (2052, 3000, 4)]:
         assert default_name(*shape) == KERNELS["tile128"][0], shape
     for shape in [(4096, 4096, 33), (8194, 8192, 64), (8192, 8193, 64)]:
         assert default_name(*shape) == KERNELS["tile256"][1], shape
@@ -90,9 +93,12 @@ def test_scheduled_kernels_are_the_default_for_their_shapes():
 
 FULL = {
     # K = 32 (one phase: prologue and the peeled last steps only), K = 64
-    # (two phases) and more; full tiles and edge tiles in both dimensions
-    "tile256": [(4096, 4096, 32), (4096, 4096, 64), (7940, 8132, 32)],
-    "tile128": [(2048, 2048, 32), (1500, 2044, 64), (2052, 3000, 96)],
+    # (two phases) and more; full tiles and edge tiles in both dimensions;
+    # a last phase past K with one (K = 4), two (36) and four (100) phases
+    "tile256": [(4096, 4096, 32), (4096, 4096, 64), (7940, 8132, 32), (4096, 4096, 100), (4096, 4096, 36),
+                (7940, 8132, 4)],
+    "tile128": [(2048, 2048, 32), (1500, 2044, 64), (2052, 3000, 96), (2048, 2048, 100), (1500, 2044, 36),
+                (2052, 3000, 4)],
 }
 
 
@@ -128,6 +134,8 @@ SAMPLED = [
     ("tile128", (3000, 7000, 1024), 0, (0, 0, 0)),
     ("tile128", (5000, 5004, 128), 1, (3, 5, 7)),
     ("tile128", (4100, 6200, 160), 3, (1, 2, 1)),
+    ("tile256", (8192, 4096, 2020), 1, (3, 5, 7)),
+    ("tile128", (3000, 7000, 1020), 0, (0, 0, 0)),
 ]
 
 
