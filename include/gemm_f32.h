@@ -55,7 +55,12 @@
 extern "C" {
 #endif
 
-/* Status codes. */
+/* Status codes.  Every entry point returns one, synchronously, before it
+ * enqueues anything: the host-program habit of the one-volume PMPP notes
+ * ("PMPP 단권화", chapter 2, host program structure), which checks the
+ * status of every runtime call and reports it by name, carried over to the
+ * library's own argument checks.  The codes and their texts
+ * (gemm_f32_status_string) are this library's own. */
 #define GEMM_F32_OK                  0
 #define GEMM_F32_ERR_INVALID_DIM     1  /* M, N or K negative                       */
 #define GEMM_F32_ERR_INVALID_LD      2  /* lda < max(1,K), ldb or ldc < max(1,N)     */
@@ -149,7 +154,11 @@ int gemm_f32_op(int op_a, int op_b,
                 float *C, int64_t ldc,
                 void *stream);
 
-/* Number of ladder rungs (variants 0 .. n-1). */
+/* Introspection.  These calls are this library's own (the pages define no
+ * such interface): they launch nothing, need no device, and exist so that
+ * tests, benchmarks and counter runs can name the kernels they measure.
+ *
+ * Number of ladder rungs (variants 0 .. n-1). */
 int gemm_f32_num_variants(void);
 
 /* Static, NUL-terminated name of a variant, or NULL if it does not exist.
@@ -168,7 +177,9 @@ int gemm_f32_num_diagnostic_variants(void);
  * that want to know which kernel a call will use. */
 int gemm_f32_default_variant(int64_t M, int64_t N, int64_t K);
 
-/* Static, NUL-terminated description of a status code. */
+/* Static, NUL-terminated description of a status code (the by-name report
+ * of the chapter 2 error check cited with the codes above); "unknown status"
+ * for any other number. */
 const char *gemm_f32_status_string(int status);
 
 /* Shared-tile transpose: out = in^T, binary32, row-major.
@@ -224,11 +235,11 @@ int transpose_f32_default_variant(int64_t rows, int64_t cols, int64_t ld_in, int
  * its last bits may vary from run to run.  The error is bounded by
  * (longest sequential chain + tree depth) * 2^-24 * sum |x_i|; the result is
  * exact when every partial sum is an integer below 2^24 in magnitude.
- * Variants: 0 interleaved tree (tid % 2s), 1 sequential addressing (tid < s),
- * 2 sequential + wave shuffles for the last six steps, 3 one atomic add per
- * block, 4 grid-stride 128-bit loads + wave shuffles + a one-block second
- * pass (the default).  Statuses as for gemm_f32, plus
- * GEMM_F32_ERR_WORKSPACE.
+ * Variants: 0 interleaved pairs (the thread owning a pair's left slot adds),
+ * 1 sequential addressing (the lowest-numbered threads add), 2 sequential +
+ * wave shuffles for the last six steps, 3 one atomic add per block, 4
+ * grid-stride 128-bit loads + wave shuffles + a one-block second pass (the
+ * default).  Statuses as for gemm_f32, plus GEMM_F32_ERR_WORKSPACE.
  */
 int64_t reduce_sum_f32_workspace_size(int variant, int64_t n);   /* bytes; -1 if invalid */
 int reduce_sum_f32(int64_t n, const float *x, float *out,

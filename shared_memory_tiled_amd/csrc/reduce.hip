@@ -4,10 +4,11 @@
 // memory and improves it step by step; its multi-pass scheme reduces each
 // block of values to one partial and runs again on the partials until one
 // value is left.  Versions, adapted to gfx950's 64-lane waves:
-//   0 interleaved     tree in LDS, thread tid adds at step s when
-//                     tid % (2s) == 0 (scattered active lanes, a modulo)
-//   1 sequential      tree in LDS, thread tid adds when tid < s (active
-//                     lanes packed at the front, no modulo, no conflicts)
+//   0 interleaved     tree in LDS; at each level the thread owning the
+//                     left slot of a pair adds (a remainder test picks one
+//                     thread in 2, 4, 8, ..., scattered over every wave)
+//   1 sequential      tree in LDS; the lowest-numbered threads add (adders
+//                     packed at the front, whole waves idle, no remainder)
 //   2 wave_shuffle    version 1 until one wave holds the data, then the wave
 //                     folds it in registers with lane shuffles (no LDS
 //                     round trips, no block barriers for the last 6 steps)
@@ -24,6 +25,8 @@
 // is deterministic except 3.
 #include "launch.h"
 
+#include <type_traits>
+
 namespace gemmf32 {
 
 namespace {
@@ -38,35 +41,62 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Versions 0-3: block b reduces values [256 b, 256 b + 256) of `in` (missing
+// The block's tree (versions 0-2).  Level j (j = 0, 1, ...) halves the
+// number of live slots: each of its kBlock >> (j + 1) additions folds one
+// slot into another.  The versions differ only in which thread performs
+// which addition, which decides how the adding threads spread over waves.
+//
+// Interleaved pairs: a live slot at level j is a multiple of 2^j and
+// absorbs the slot 2^j above it; each thread works on its own slot, so the
+// adders are the threads whose index leaves no remainder modulo 2^(j+1) --
+// one in every 2^(j+1), scattered through every wave until the tree is a
+// wave wide.
+struct InterleavedPairs {
+    __device__ static bool adds(int t, int level) { return t % (2 << level) == 0; }
+    __device__ static int partner(int t, int level) { return t + (1 << level); }
+};
+// Sequential pairs: at level j the live slots are the first kBlock >> j, and
+// thread t folds slot t + (kBlock >> (j + 1)) into slot t, so the adders are
+// the lowest-numbered threads and whole waves drop out as the tree narrows.
+struct SequentialPairs {
+    __device__ static int half(int level) { return kBlock >> (level + 1); }
+    __device__ static bool adds(int t, int level) { return t < half(level); }
+    __device__ static int partner(int t, int level) { return t + half(level); }
+};
+
+// Levels 0 .. LEVELS - 1 of the tree over `slots`, one block barrier after
+// each so the next level reads finished sums.
+template <class Pairs, int LEVELS>
+__device__ __forceinline__ void fold_levels(float* slots, int t) {
+    for (int level = 0; level < LEVELS; ++level) {
+        if (Pairs::adds(t, level)) slots[t] += slots[Pairs::partner(t, level)];
+        __syncthreads();
+    }
+}
+
+constexpr int kLevels = 8;                 // log2(kBlock)
+static_assert((1 << kLevels) == kBlock, "tree depth");
+
+// Versions 0-3: block b folds values [256 b, 256 b + 256) of `in` (missing
 // values count as +0) into part[b], or adds it to *out (version 3).
+// Versions 0 and 1 run the whole tree in LDS; 2 and 3 run it until one wave
+// holds the live slots (two levels), then fold that wave in registers.
 template <int VERSION>
 __global__ __launch_bounds__(kBlock) void reduce_block_kernel(int64_t n, const float* in, float* part) {
-    __shared__ float buf[kBlock];
-    const int tid = threadIdx.x;
-    const int64_t i = (int64_t)blockIdx.x * kBlock + tid;
-    buf[tid] = i < n ? in[i] : 0.0f;
+    __shared__ float slots[kBlock];
+    const int t = threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + t;
+    slots[t] = i < n ? in[i] : 0.0f;
     __syncthreads();
-    if constexpr (VERSION == 0) {
-        for (int s = 1; s < kBlock; s *= 2) {
-            if (tid % (2 * s) == 0) buf[tid] += buf[tid + s];
-            __syncthreads();
-        }
-        if (tid == 0) part[blockIdx.x] = buf[0];
-    } else if constexpr (VERSION == 1) {
-        for (int s = kBlock / 2; s > 0; s >>= 1) {
-            if (tid < s) buf[tid] += buf[tid + s];
-            __syncthreads();
-        }
-        if (tid == 0) part[blockIdx.x] = buf[0];
+    if constexpr (VERSION <= 1) {
+        using Pairs = std::conditional_t<VERSION == 0, InterleavedPairs, SequentialPairs>;
+        fold_levels<Pairs, kLevels>(slots, t);
+        if (t == 0) part[blockIdx.x] = slots[0];
     } else {
-        for (int s = kBlock / 2; s >= 64; s >>= 1) {      // until one wave holds the data
-            if (tid < s) buf[tid] += buf[tid + s];
-            __syncthreads();
-        }
-        if (tid < 64) {                                   // wave 0, wave-uniform branch
-            const float v = wave_sum(buf[tid]);
-            if (tid == 0) {
+        fold_levels<SequentialPairs, 2>(slots, t);        // 256 -> 64 live slots
+        if (t < 64) {                                     // wave 0, wave-uniform branch
+            const float v = wave_sum(slots[t]);
+            if (t == 0) {
                 if constexpr (VERSION == 2) part[blockIdx.x] = v;
                 else atomicAdd(part, v);                  // part is *out for version 3
             }
