@@ -27,7 +27,9 @@
  *
  * Memory and ownership: A, B and C are DEVICE pointers on the current HIP
  * device, owned by the caller; the library allocates nothing, keeps no
- * pointer after returning and holds no state.  A and B are read only.  C
+ * pointer after returning and holds no state (the one exception is the
+ * fixed 1 MiB scratch array of reduce_sum_f32_variant_noalloc, a static
+ * device variable, and its address per device).  A and B are read only.  C
  * must not overlap A or B (the result is undefined otherwise).  Pointers need
  * 4-byte alignment only; 16-byte alignment is not required.
  *
@@ -73,6 +75,7 @@ extern "C" {
 #define GEMM_F32_ERR_INVALID_OP      9  /* op_a or op_b is neither N nor T           */
 #define GEMM_F32_ERR_WORKSPACE      10  /* workspace smaller than required            */
 #define GEMM_F32_ERR_INVALID_FORMAT 11  /* 16-bit input format unknown                */
+#define GEMM_F32_ERR_SCRATCH        12  /* partials would exceed the fixed scratch      */
 
 /* Kernel ladder.  Each rung computes the same product; each is tested against
  * the oracle and against the rung below it.
@@ -248,6 +251,30 @@ int reduce_sum_f32_variant(int variant, int64_t n, const float *x, float *out,
                            void *workspace, int64_t workspace_bytes, void *stream);
 int reduce_sum_f32_num_variants(void);
 const char *reduce_sum_f32_variant_name(int variant);  /* NULL if unknown */
+
+/* reduce_sum_f32_variant without a workspace, for callers that cannot
+ * allocate device memory: code under HIP stream capture, serving loops that
+ * must not call the allocator, harnesses that forbid it.  It calls no
+ * allocator (the library's, HIP's or torch's) at any point.
+ *   The partials go to a fixed array of REDUCE_SUM_F32_SCRATCH_BYTES (1 MiB)
+ * that the library holds in the device memory of every GPU it runs on, for
+ * the life of the process.  Its address on a device is looked up on the
+ * first call with that device current.
+ *   Limit: a problem whose partials need more than that scratch, i.e. whose
+ * reduce_sum_f32_workspace_size(variant, n) exceeds
+ * REDUCE_SUM_F32_SCRATCH_BYTES, is rejected with GEMM_F32_ERR_SCRATCH
+ * before anything is enqueued.  Variants 3 and 4 fit for any n; variants
+ * 0-2 need about 4 n / 255 bytes, so they take n up to about 6.7e7.
+ *   Sharing: every call on one GPU uses that GPU's one scratch array, which
+ * keeps the last call's contents.  Calls that overlap on one GPU -- on two
+ * streams, or from two host threads without ordering -- race and give
+ * undefined results.  Calls on one stream are ordered and safe.
+ *   Arguments, results, summation order (the same bits as
+ * reduce_sum_f32_variant for variants 0-2 and 4), statuses and asynchrony
+ * are as for reduce_sum_f32_variant. */
+#define REDUCE_SUM_F32_SCRATCH_BYTES (1 << 20)
+int reduce_sum_f32_variant_noalloc(int variant, int64_t n, const float *x, float *out,
+                                   void *stream);
 
 /* Mixed-precision product: C (binary32) = A x B with A and B in a 16-bit
  * format, accumulated in binary32.

@@ -86,6 +86,8 @@ def load_library():
         lib.reduce_sum_f32.restype = ctypes.c_int
         lib.reduce_sum_f32_variant.argtypes = [ctypes.c_int] + rsig
         lib.reduce_sum_f32_variant.restype = ctypes.c_int
+        lib.reduce_sum_f32_variant_noalloc.argtypes = [ctypes.c_int, _i64, _vp, _vp, _vp]
+        lib.reduce_sum_f32_variant_noalloc.restype = ctypes.c_int
         lib.reduce_sum_f32_num_variants.argtypes = []
         lib.reduce_sum_f32_num_variants.restype = ctypes.c_int
         lib.reduce_sum_f32_variant_name.argtypes = [ctypes.c_int]
@@ -271,6 +273,16 @@ def reduce_sum_f32_variant(variant, n, x, out, workspace, workspace_bytes, strea
     lib = load_library()
     _check(lib.reduce_sum_f32_variant(int(variant), n, _addr(x), _addr(out), _addr(workspace),
                                       workspace_bytes, _stream(stream)))
+
+
+def reduce_sum_f32_variant_noalloc(variant, n, x, out, stream=None) -> None:
+    """reduce_sum_f32_variant with the partials in the library's fixed
+    per-device scratch (no workspace, no allocation)."""
+    lib = load_library()
+    _check(lib.reduce_sum_f32_variant_noalloc(int(variant), n, _addr(x), _addr(out), _stream(stream)))
+
+
+REDUCE_SCRATCH_BYTES = 1 << 20     # REDUCE_SUM_F32_SCRATCH_BYTES
 
 
 def reduce_sum_f32_num_variants() -> int:

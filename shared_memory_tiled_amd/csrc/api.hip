@@ -176,6 +176,8 @@ extern "C" const char* gemm_f32_status_string(int status) {
         case GEMM_F32_ERR_INVALID_OP: return "invalid op: op_a and op_b must be GEMM_F32_OP_N or GEMM_F32_OP_T";
         case GEMM_F32_ERR_WORKSPACE: return "workspace smaller than reduce_sum_f32_workspace_size()";
         case GEMM_F32_ERR_INVALID_FORMAT: return "unknown 16-bit format: use GEMM_MIXED_BF16 or GEMM_MIXED_F16";
+        case GEMM_F32_ERR_SCRATCH:
+            return "partials exceed the library's fixed 1 MiB scratch: use reduce_sum_f32_variant with a workspace";
         default: return "unknown status";
     }
 }
@@ -249,23 +251,34 @@ extern "C" const char* transpose_f32_variant_name(int variant) {
 namespace {
 constexpr int kReduceDefault = 4;
 
-int run_reduce(int variant, int64_t n, const float* x, float* out, void* workspace, int64_t ws_bytes,
-               void* stream) {
+// Checks shared by the reduction entry points (no device needed).
+int check_reduce(int variant, int64_t n, const float* x, const float* out) {
     if (variant < 0 || variant >= reduce_num_variants()) return GEMM_F32_ERR_INVALID_VARIANT;
-    if (n < 0 || ws_bytes < 0) return GEMM_F32_ERR_INVALID_DIM;
+    if (n < 0) return GEMM_F32_ERR_INVALID_DIM;
     if (out == nullptr || (n > 0 && x == nullptr)) return GEMM_F32_ERR_NULL_PTR;
     if (misaligned(out) || (n > 0 && misaligned(x))) return GEMM_F32_ERR_MISALIGNED;
     if (n > ((int64_t)1 << 39)) return GEMM_F32_ERR_TOO_LARGE;
+    return GEMM_F32_OK;
+}
+
+int finish_reduce(hipError_t e) {
+    if (e == hipErrorInvalidValue) return GEMM_F32_ERR_TOO_LARGE;
+    return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
+}
+
+int run_reduce(int variant, int64_t n, const float* x, float* out, void* workspace, int64_t ws_bytes,
+               void* stream) {
+    const int st = check_reduce(variant, n, x, out);
+    if (st != GEMM_F32_OK) return st;
+    if (ws_bytes < 0) return GEMM_F32_ERR_INVALID_DIM;
     const int64_t need = 4 * reduce_workspace_floats(variant, n);
     if (ws_bytes < need) return GEMM_F32_ERR_WORKSPACE;
     if (need > 0 && workspace == nullptr) return GEMM_F32_ERR_NULL_PTR;
     if (need > 0 && misaligned(workspace)) return GEMM_F32_ERR_MISALIGNED;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_F32_ERR_DEVICE;
-    const hipError_t e = launch_reduce(variant, n, x, out, static_cast<float*>(workspace),
-                                       reinterpret_cast<hipStream_t>(stream));
-    if (e == hipErrorInvalidValue) return GEMM_F32_ERR_TOO_LARGE;
-    return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
+    return finish_reduce(launch_reduce(variant, n, x, out, static_cast<float*>(workspace),
+                                       reinterpret_cast<hipStream_t>(stream)));
 }
 }  // namespace
 
@@ -282,6 +295,21 @@ extern "C" int reduce_sum_f32(int64_t n, const float* x, float* out, void* works
 extern "C" int reduce_sum_f32_variant(int variant, int64_t n, const float* x, float* out,
                                       void* workspace, int64_t workspace_bytes, void* stream) {
     return run_reduce(variant, n, x, out, workspace, workspace_bytes, stream);
+}
+
+// The same reduction with the partials in the library's fixed per-device
+// scratch instead of a caller's workspace: nothing is allocated, so callers
+// that cannot allocate (stream capture, allocation-free loops) can use it.
+extern "C" int reduce_sum_f32_variant_noalloc(int variant, int64_t n, const float* x, float* out,
+                                              void* stream) {
+    const int st = check_reduce(variant, n, x, out);
+    if (st != GEMM_F32_OK) return st;
+    if (reduce_workspace_floats(variant, n) > kReduceScratchFloats) return GEMM_F32_ERR_SCRATCH;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_F32_ERR_DEVICE;
+    float* scratch = nullptr;
+    if (reduce_scratch(dev, &scratch) != hipSuccess) return GEMM_F32_ERR_DEVICE;
+    return finish_reduce(launch_reduce(variant, n, x, out, scratch, reinterpret_cast<hipStream_t>(stream)));
 }
 
 extern "C" int reduce_sum_f32_num_variants(void) { return reduce_num_variants(); }

@@ -41,6 +41,12 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
 // Sum reduction (reduce.hip): *out = sum of x[0 .. n-1].
 hipError_t launch_reduce(int variant, int64_t n, const float* x, float* out, float* ws, hipStream_t s);
 int64_t reduce_workspace_floats(int variant, int64_t n);
+// The fixed per-device scratch (reduce.hip) that takes the partials of the
+// entry point for callers that cannot allocate: its size in floats, and its
+// address on `device` (looked up once per device; the device must be
+// current on the first call for it).
+constexpr int64_t kReduceScratchFloats = (int64_t)1 << 18;     // 1 MiB
+hipError_t reduce_scratch(int device, float** ptr);
 int reduce_num_variants();
 const char* reduce_variant_name(int v);
 

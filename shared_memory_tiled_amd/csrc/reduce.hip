@@ -21,10 +21,13 @@
 //                     folds waves by shuffles and blocks through LDS, and a
 //                     second one-block launch folds the 2048 partials
 //                     (deterministic; bound by HBM reads)
-// Versions 0-2 and 4 write partials to the caller's workspace; every version
-// is deterministic except 3.
+// Versions 0-2 and 4 write partials to a workspace: the caller's, or, for
+// callers that cannot allocate, a fixed array in device memory (below);
+// every version is deterministic except 3.
 #include "launch.h"
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 namespace gemmf32 {
@@ -209,6 +212,44 @@ hipError_t launch_reduce(int variant, int64_t n, const float* x, float* out, flo
         dst += blocks;
         m = blocks;
     }
+}
+
+// ------------------------------------------------------------ fixed scratch
+//
+// For callers that cannot allocate device memory (code under stream capture,
+// loops that must not call the allocator): the partials go to this array,
+// which every GPU the library runs on holds for the life of the process.
+// Each device has its own copy at its own address; on the host the name
+// `scratch` is only a symbol, so kernels receive the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept.  Every call on one GPU shares that GPU's copy: calls that
+// overlap on one GPU (two streams, two host threads) race.  Nothing in it
+// needs clearing: every version writes each partial before reading it.
+__device__ __align__(256) float scratch[kReduceScratchFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t reduce_scratch(int device, float** ptr) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    float* p = g_scratch[device].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[device].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            void* addr = nullptr;
+            const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (addr == nullptr) return hipErrorInvalidSymbol;
+            p = static_cast<float*>(addr);
+            g_scratch[device].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 }  // namespace gemmf32

@@ -194,6 +194,44 @@ def test_reduce_validation_without_launch(lib, args, code):
         assert lib.reduce_sum_f32_variant(v, n, x, out, ws, wsb, None) == want, v
 
 
+@pytest.mark.parametrize("args,code", [
+    ((0, -1, FAKE, FAKE), "GEMM_F32_ERR_INVALID_DIM"),
+    ((7, 10, FAKE, FAKE), "GEMM_F32_ERR_INVALID_VARIANT"),
+    ((-1, 10, FAKE, FAKE), "GEMM_F32_ERR_INVALID_VARIANT"),
+    ((1, 10, FAKE, None), "GEMM_F32_ERR_NULL_PTR"),
+    ((2, 10, None, FAKE), "GEMM_F32_ERR_NULL_PTR"),
+    ((4, 10, FAKE + 2, FAKE), "GEMM_F32_ERR_MISALIGNED"),
+    ((4, 2**40, FAKE, FAKE), "GEMM_F32_ERR_TOO_LARGE"),
+    # versions 0-2 keep ~n/255 partials: past 1 MiB of them the fixed scratch
+    # is too small, and the call is refused before anything is enqueued
+    ((0, 2**27, FAKE, FAKE), "GEMM_F32_ERR_SCRATCH"),
+    ((1, 2**27, FAKE, FAKE), "GEMM_F32_ERR_SCRATCH"),
+    ((2, 10**9, FAKE, FAKE), "GEMM_F32_ERR_SCRATCH"),
+])
+def test_reduce_noalloc_validation_without_launch(lib, args, code):
+    assert lib.reduce_sum_f32_variant_noalloc(*args, None) == declared_codes()[code]
+
+
+def test_reduce_noalloc_scratch_limit(binding):
+    """The declared scratch size, and the largest n each tree version takes
+    in it: exactly where the workspace the version needs passes 1 MiB."""
+    text = open(HEADER).read()
+    assert re.search(r"#define\s+REDUCE_SUM_F32_SCRATCH_BYTES\s+\(1 << 20\)", text)
+    limit = binding.REDUCE_SCRATCH_BYTES
+    assert limit == 1 << 20
+    for v in (0, 1, 2):
+        lo, hi = 1, 2**30          # largest n whose workspace fits in the scratch
+        while lo < hi:
+            mid = (lo + hi + 1) // 2
+            if binding.reduce_sum_f32_workspace_size(v, mid) <= limit:
+                lo = mid
+            else:
+                hi = mid - 1
+        assert 6.6e7 < lo < 6.8e7, lo
+    for v in (3, 4):
+        assert binding.reduce_sum_f32_workspace_size(v, 2**39) <= limit
+
+
 def test_reduce_workspace_sizes(binding, lib):
     # the page's multi-pass sizes: 2^24 values -> 65,536 + 256 partials kept
     assert binding.reduce_sum_f32_workspace_size(1, 2**24) == 4 * (65536 + 256)
