@@ -634,19 +634,23 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
         doff[A_COPIES + j] = TB::copy_src(wave_u, j, lane, n0, p.ldb);
     }
     constexpr int kRawBufferWord3 = 0x00020000;
-    // Each descriptor ends exactly at its stored matrix's last element.  An
-    // edge tile's copies past the last row read +0 without touching memory;
-    // past the last column of an mn-contiguous factor they read the next
-    // row (or +0 past the end), which only ever meets C entries outside the
-    // matrix, never stored.  A 16-byte chunk across the end of an
+    // Each descriptor ends exactly at its stored matrix's last element, and
+    // a copy that must bring zeros gets them from a per-lane offset that by
+    // itself lies at or past that end (the scalar offset, which holds the
+    // phase, never decides it).  An edge tile's copies past the last row of
+    // a k-contiguous factor have such offsets in every phase.  Past the last
+    // column of an mn-contiguous factor they read the next row, which only
+    // ever meets C entries outside the matrix, never stored.  The last
+    // phase's copies take their own per-lane offsets (dlast) with the phase
+    // folded in and a scalar offset of 0: K is a multiple of 8, its 16-byte
+    // chunks or rows at k >= K are pointed past the end (kPastEnd), so they
+    // copy zeros, and a chunk of the last row past the last column lies past
+    // the end by its own offset.  A 16-byte chunk across the end of an
     // mn-contiguous factor's last row reads its dwords up to the
     // descriptor's end and zeros past it (the range check is per dword;
     // checked on MI355X); the factor's width is even, so no dword straddles
-    // that end.  K is a multiple of 8: when the last phase reaches past K,
-    // its rows k >= K of an mn-contiguous factor lie past the end, and its
-    // 16-byte chunks at k >= K of a k-contiguous factor are pointed there
-    // (dlast), so they copy zeros; the 8-wave kernel's ghost phase has the
-    // same zeros, so both still give the same bits.
+    // that end.  The 8-wave kernel's ghost phase has the same zeros, so both
+    // still give the same bits.
     const int64_t a_rows = KCA ? p.M : p.K, a_cols = KCA ? p.K : p.M;
     const int64_t b_rows = KCB ? p.N : p.K, b_cols = KCB ? p.K : p.N;
     const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
@@ -655,25 +659,27 @@ void gemm16_sched_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
         const_cast<uint16_t*>(p.B), (short)0, (int)(2 * ((b_rows - 1) * p.ldb + b_cols)), kRawBufferWord3);
     const int P = ceil_div(p.K, kBK);
     constexpr uint32_t kPastEnd = 0x80000000u;              // beyond any descriptor here
+    const int klast = (P - 1) * kBK;                        // the last phase's first k
     uint32_t dlast[NCOPY];
 #pragma unroll
     for (int j = 0; j < A_COPIES; ++j) {
-        const int ka = (P - 1) * kBK + TA::copy_k(wave_u, j, lane);
-        const int kb = (P - 1) * kBK + TB::copy_k(wave_u, j, lane);
-        dlast[j] = KCA && ka >= p.K ? kPastEnd : doff[j];
-        dlast[A_COPIES + j] = KCB && kb >= p.K ? kPastEnd : doff[A_COPIES + j];
+        const int ka = klast + TA::copy_k(wave_u, j, lane);
+        const int kb = klast + TB::copy_k(wave_u, j, lane);
+        dlast[j] = ka >= p.K ? kPastEnd : doff[j] + (uint32_t)TA::phase_bytes(klast, p.lda);
+        dlast[A_COPIES + j] = kb >= p.K ? kPastEnd : doff[A_COPIES + j] + (uint32_t)TB::phase_bytes(klast, p.ldb);
     }
-    // Copy j of the phase at k0 into stage buf; LAST: the phase is the last.
+    // Copy j of the phase at k0 into stage buf; LAST: the phase is the last
+    // (its offsets hold the phase; k0 is not used).
     auto copy = [&](int j, int k0, int buf, auto lastc) __attribute__((always_inline)) {
         constexpr bool LAST = decltype(lastc)::value;
         const uint32_t voff = LAST ? dlast[j] : doff[j];
         if (j < A_COPIES) {
-            const int soff = TA::phase_bytes(k0, p.lda);
+            const int soff = LAST ? 0 : TA::phase_bytes(k0, p.lda);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc_a, (__attribute__((address_space(3))) void*)(lds + buf * TILE + TA::copy_dst(wave_u, j)), 16,
                 (int)voff, soff, 0, 0);
         } else {
-            const int soff = TB::phase_bytes(k0, p.ldb);
+            const int soff = LAST ? 0 : TB::phase_bytes(k0, p.ldb);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc_b,
                 (__attribute__((address_space(3))) void*)(lds + (2 + buf) * TILE + TB::copy_dst(wave_u, j - A_COPIES)),

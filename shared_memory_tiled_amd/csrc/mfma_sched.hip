@@ -118,6 +118,9 @@ struct SchedTileF32 {
             return 4u * (uint32_t)(row * ld + mn0 + 4 * (lane % LPR));
         }
     }
+    // mn-contiguous only: first column, relative to the tile's first one, of
+    // lane l's 16 bytes (the same in every copy).
+    __host__ __device__ static int copy_mn(int lane) { return 4 * (lane % (64 / RPC)); }
     // k of lane l's 16 bytes of copy j of wave w, relative to the phase's
     // first k.
     __host__ __device__ static int copy_k(int w, int j, int lane) {
@@ -194,17 +197,20 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         doff[A_COPIES + j] = TB::copy_src(wave_u, j, lane, n0, p.ldb);
     }
     constexpr int kRawBufferWord3 = 0x00020000;
-    // Each descriptor ends exactly at its stored matrix's last element.  An
-    // edge tile's copies past the last row read +0 without touching memory;
-    // past the last column of an mn-contiguous factor they read the next
-    // row (or +0 past the end), which only ever meets C entries outside the
-    // matrix, never stored.  An mn-contiguous factor's extent is a multiple
-    // of 4, so no 16-byte chunk straddles an edge.  K is a multiple of 4:
-    // when the last phase reaches past K, its rows k >= K of an
-    // mn-contiguous factor lie past the end, and its chunks at k >= K of a
-    // k-contiguous factor are pointed there (dlast), so they copy zeros;
-    // the other kernels' ghost phases hold the same zeros, so all still give
-    // the same bits.
+    // Each descriptor ends exactly at its stored matrix's last element, and
+    // every copy that must bring zeros gets them from a per-lane offset that
+    // by itself lies at or past that end (the scalar offset, which holds the
+    // phase, never decides it).  An edge tile's copies past the last row of
+    // a k-contiguous factor have such offsets in every phase.  Past the last
+    // column of an mn-contiguous factor they read the next row, which only
+    // ever meets C entries outside the matrix, never stored; an
+    // mn-contiguous factor's extent is a multiple of 4, so no 16-byte chunk
+    // straddles an edge.  The last phase's copies take their own per-lane
+    // offsets (dlast) with the phase folded in and a scalar offset of 0:
+    // K is a multiple of 4, and its chunks or rows at k >= K are pointed
+    // past the end (kPastEnd), so they copy zeros, as does the column
+    // overhang of the last row; the other kernels' ghost phases hold the
+    // same zeros, so all still give the same bits.
     const int64_t a_rows = KCA ? p.M : p.K, a_cols = KCA ? p.K : p.M;
     const int64_t b_rows = KCB ? p.N : p.K, b_cols = KCB ? p.K : p.N;
     const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
@@ -213,25 +219,27 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         const_cast<float*>(p.B), (short)0, (int)(4 * ((b_rows - 1) * p.ldb + b_cols)), kRawBufferWord3);
     const int P = ceil_div(p.K, kSBK);
     constexpr uint32_t kPastEnd = 0x80000000u;              // beyond any descriptor here
+    const int klast = (P - 1) * kSBK;                       // the last phase's first k
     uint32_t dlast[NCOPY];
 #pragma unroll
     for (int j = 0; j < A_COPIES; ++j) {
-        const int ka = (P - 1) * kSBK + TA::copy_k(wave_u, j, lane);
-        const int kb = (P - 1) * kSBK + TB::copy_k(wave_u, j, lane);
-        dlast[j] = KCA && ka >= p.K ? kPastEnd : doff[j];
-        dlast[A_COPIES + j] = KCB && kb >= p.K ? kPastEnd : doff[A_COPIES + j];
+        const int ka = klast + TA::copy_k(wave_u, j, lane);
+        const int kb = klast + TB::copy_k(wave_u, j, lane);
+        dlast[j] = ka >= p.K ? kPastEnd : doff[j] + (uint32_t)TA::phase_bytes(klast, p.lda);
+        dlast[A_COPIES + j] = kb >= p.K ? kPastEnd : doff[A_COPIES + j] + (uint32_t)TB::phase_bytes(klast, p.ldb);
     }
-    // Copy j of the phase at k0 into stage buf; LAST: the phase is the last.
+    // Copy j of the phase at k0 into stage buf; LAST: the phase is the last
+    // (its offsets hold the phase; k0 is not used).
     auto copy = [&](int j, int k0, int buf, auto lastc) __attribute__((always_inline)) {
         constexpr bool LAST = decltype(lastc)::value;
         const uint32_t voff = LAST ? dlast[j] : doff[j];
         if (j < A_COPIES) {
-            const int soff = TA::phase_bytes(k0, p.lda);
+            const int soff = LAST ? 0 : TA::phase_bytes(k0, p.lda);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc_a, (__attribute__((address_space(3))) void*)(lds + buf * A_ST + TA::copy_dst(wave_u, j)), 16,
                 (int)voff, soff, 0, 0);
         } else {
-            const int soff = TB::phase_bytes(k0, p.ldb);
+            const int soff = LAST ? 0 : TB::phase_bytes(k0, p.ldb);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc_b,
                 (__attribute__((address_space(3))) void*)(lds + 2 * A_ST + buf * B_ST + TB::copy_dst(wave_u, j - A_COPIES)),
@@ -487,6 +495,20 @@ void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     const int P = nph > w ? (nph - 1 - w) / 4 + 1 : 0;
     auto kof = [&](int lp) __attribute__((always_inline)) { return kbase + kSBK * (4 * lp + w); };
 
+    // Descriptors end exactly at each stored matrix's last element, and a
+    // copy that must bring zeros gets them from a per-lane offset that by
+    // itself lies at or past that end (never from the scalar offset, which
+    // holds the phase): rows of a k-contiguous factor past the tile's edge
+    // have such offsets; the 16-byte chunks of an mn-contiguous factor past
+    // its last column (which would only meet C entries outside the matrix;
+    // its extent is a multiple of 4, so a chunk is wholly in or out) are
+    // pointed past the end (kPastEnd) in every phase; and phase 0's lanes
+    // below k = 0 are pointed there too (copy_first).  Every other lane
+    // addresses an element of the matrix in every phase.
+    const int64_t a_rows = KCA ? p.M : p.K, a_cols = KCA ? p.K : p.M;
+    const int64_t b_rows = KCB ? p.N : p.K, b_cols = KCB ? p.K : p.N;
+    constexpr int kRawBufferWord3 = 0x00020000;
+    constexpr uint32_t kPastEnd = 0x80000000u;               // beyond any descriptor here
     // Copy j < 8 fills A's tile, j >= 8 B's; within a factor copy j is copy
     // j / 4 of "wave" j % 4 of the shared layout, so one wave covers it all.
     uint32_t doff[NCOPY];
@@ -494,15 +516,9 @@ void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     for (int j = 0; j < A_COPIES; ++j) {
         doff[j] = TA::copy_src(j % 4, j / 4, lane, m0, p.lda);
         doff[A_COPIES + j] = TB::copy_src(j % 4, j / 4, lane, n0, p.ldb);
+        if (!KCA && m0 + TA::copy_mn(lane) >= a_cols) doff[j] = kPastEnd;
+        if (!KCB && n0 + TB::copy_mn(lane) >= b_cols) doff[A_COPIES + j] = kPastEnd;
     }
-    constexpr int kRawBufferWord3 = 0x00020000;
-    constexpr uint32_t kPastEnd = 0x80000000u;               // beyond any descriptor here
-    // Descriptors end exactly at each stored matrix's last element: rows
-    // past the edge (of the tile, or k >= K of an mn-contiguous factor) read
-    // +0; columns past the last one of an mn-contiguous factor read the next
-    // row, which only meets C entries outside the matrix.
-    const int64_t a_rows = KCA ? p.M : p.K, a_cols = KCA ? p.K : p.M;
-    const int64_t b_rows = KCB ? p.N : p.K, b_cols = KCB ? p.K : p.N;
     const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(p.A), (short)0, (int)(4 * ((a_rows - 1) * p.lda + a_cols)), kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
@@ -535,7 +551,7 @@ void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
             const int jj = is_a ? j : j - A_COPIES;
             const int kl = is_a ? TA::copy_k(jj % 4, jj / 4, lane) : TB::copy_k(jj % 4, jj / 4, lane);
             const int pb = is_a ? TA::phase_bytes(k0, p.lda) : TB::phase_bytes(k0, p.ldb);
-            copy_at(j, k0 + kl >= 0 ? doff[j] + (uint32_t)pb : kPastEnd, 0, 0);
+            copy_at(j, k0 + kl >= 0 && doff[j] != kPastEnd ? doff[j] + (uint32_t)pb : kPastEnd, 0, 0);
         }
     };
 

@@ -397,3 +397,162 @@ def test_ksplit_phase_partition_and_first_phase_mask(K):
                         if not masked:
                             seen.extend(ks)
             assert sorted(seen) == list(range(K)), (kc, row_or_col)
+
+
+PAST_END = 0x80000000
+
+
+def _f32_copy(kc, mnt, w, j, lane, mn0, ld):
+    """(byte offset at k = 0, k of the lane's first value relative to the
+    phase, first mn index) of lane `lane` of copy j of wave w of a 32-deep
+    fp32 tile stage: the scheduled kernels' copy map, restated."""
+    rpc = 8 if kc else 256 // mnt
+    if kc:
+        row = 8 * (w + 4 * j) + lane // 8
+        kl = 4 * ((lane % 8) ^ sched_f32_swz(row))
+        return 4 * ((mn0 + row) * ld + kl), kl, mn0 + row
+    lpr = 64 // rpc
+    row = rpc * (w + 4 * j) + lane // lpr
+    col = mn0 + 4 * (lane % lpr)
+    return 4 * (row * ld + col), row, col
+
+
+def _check_copy(voff, soff, nrec, width_bytes, wants_zero, in_matrix, what):
+    """The outcome of a buffer copy must not depend on whether the scalar
+    offset takes part in the range check: the per-lane offset is past the
+    end by itself, or the whole chunk lies inside even with the scalar
+    offset added.  Chunks that must bring zeros are past the end; chunks of
+    elements inside the matrix are inside."""
+    assert 0 <= soff
+    past = voff >= nrec
+    inside = voff + soff + width_bytes <= nrec
+    assert past or inside, what
+    if wants_zero:
+        assert past, what
+    if in_matrix:
+        assert inside and not past, what
+
+
+@pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
+@pytest.mark.parametrize("mnt", [256, 128])
+@pytest.mark.parametrize("shape", [(4092, 100, 4100), (1532, 164, 1532), (300, 36, 301), (256, 32, 256)])
+def test_sched_fp32_copies_never_depend_on_the_scalar_offset(kc, mnt, shape):
+    """Four-wave fp32 kernel: one factor of mn extent `ext`, depth K, stored
+    leading dimension ld; every copy of every phase of the first and the last
+    (edge) tile.  Phases before the last take the phase in the scalar offset;
+    the last phase's per-lane offsets hold it (dlast) with a scalar offset of
+    0, and its lanes at k >= K are pointed past the end."""
+    ext, K, ld_mn = shape
+    rows, cols = (ext, K) if kc else (K, ext)
+    ld = max(K + 4, 4) if kc else max(cols, ld_mn)
+    nrec = 4 * ((rows - 1) * ld + cols)
+    P = -(-K // 32)
+    for mn0 in sorted({0, (ext - 1) // mnt * mnt}):
+        for w in range(4):
+            for j in range(mnt // 32):
+                for lane in range(64):
+                    doff, kl, mn = _f32_copy(kc, mnt, w, j, lane, mn0, ld)
+                    for ph in range(P):
+                        k0 = 32 * ph
+                        k = k0 + kl
+                        if ph == P - 1:
+                            voff = PAST_END if k >= K else doff + (4 * k0 if kc else 4 * k0 * ld)
+                            soff = 0
+                        else:
+                            voff, soff = doff, (4 * k0 if kc else 4 * k0 * ld)
+                        if kc:
+                            wants_zero = k >= K or mn >= ext
+                            in_matrix = k + 3 < K and mn < ext
+                        else:
+                            # the column overhang may read another row (it only
+                            # meets outputs outside C) or zeros
+                            wants_zero = k >= K
+                            in_matrix = k < K and mn + 3 < ext
+                        _check_copy(voff, soff, nrec, 16, wants_zero, in_matrix,
+                                    (kc, mnt, shape, mn0, w, j, lane, ph))
+
+
+@pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
+@pytest.mark.parametrize("shape", [(508, 1004, 508), (380, 1004, 384), (64, 36, 64), (100, 4, 100)])
+def test_ksplit_copies_never_depend_on_the_scalar_offset(kc, shape):
+    """k-split fp32 kernel: phases aligned to the end of K, phase 0 copied
+    with the phase folded into the per-lane offsets and a scalar offset of
+    0 (lanes below k = 0 past the end), the others with the phase in the
+    scalar offset; chunks of an mn-contiguous factor past its last column
+    are past the end in every phase."""
+    ext, K, ld_mn = shape
+    rows, cols = (ext, K) if kc else (K, ext)
+    ld = max(K, 4) if kc else max(ld_mn, ext)
+    nrec = 4 * ((rows - 1) * ld + cols)
+    P = -(-K // 32)
+    kbase = K - 32 * P
+    for mn0 in sorted({0, (ext - 1) // 64 * 64}):
+        for j in range(8):                   # the wave's 8 copies of this factor
+            w_, j_ = j % 4, j // 4
+            for lane in range(64):
+                doff, kl, mn = _f32_copy(kc, 64, w_, j_, lane, mn0, ld)
+                if not kc and mn >= ext:
+                    doff = PAST_END
+                for g in range(P):
+                    k0 = kbase + 32 * g
+                    k = k0 + kl
+                    pb = 4 * k0 if kc else 4 * k0 * ld
+                    if g < 4:          # each wave's first phase: copy_first
+                        voff = doff + pb if k >= 0 and doff != PAST_END else PAST_END
+                        soff = 0
+                    else:
+                        voff, soff = doff, pb
+                    if kc:
+                        wants_zero = k < 0 or mn >= ext
+                        in_matrix = k >= 0 and mn < ext
+                    else:
+                        wants_zero = k < 0 or mn >= ext
+                        in_matrix = k >= 0 and mn + 3 < ext
+                    assert k + (3 if kc else 0) < K
+                    _check_copy(voff, soff, nrec, 16, wants_zero, in_matrix, (kc, shape, mn0, j, lane, g))
+
+
+@pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
+@pytest.mark.parametrize("shape", [(3068, 200, 3072), (2814, 72, 2818), (256, 64, 256)])
+def test_sched_mixed_copies_never_depend_on_the_scalar_offset(kc, shape):
+    """Scheduled 16-bit kernel (64-deep phases, 16-byte chunks of 8 values):
+    the same rule as the fp32 kernel.  An mn-contiguous factor's width is
+    only even, so a chunk may straddle its last column: one of the last row
+    straddles the descriptor's end, which is a whole dword, and its dwords
+    past the end copy zeros (the range check is per dword); no other chunk
+    straddles the end."""
+    ext, K, ld_mn = shape
+    rows, cols = (ext, K) if kc else (K, ext)
+    ld = (K + 8) if kc else ld_mn
+    nrec = 2 * ((rows - 1) * ld + cols)
+    assert nrec % 4 == 0
+    P = -(-K // 64)
+    for mn0 in sorted({0, (ext - 1) // 256 * 256}):
+        for w in range(4):
+            for j in range(8):
+                for lane in range(64):
+                    if kc:
+                        row = 8 * (w + 4 * j) + lane // 8
+                        kl = 8 * ((lane % 8) ^ ((row >> 1) & 7))
+                        doff, mn = 2 * ((mn0 + row) * ld + kl), mn0 + row
+                    else:
+                        row = 2 * (w + 4 * j) + lane // 32
+                        col = mn0 + 8 * ((lane % 32) ^ (4 * (row & 3)))
+                        doff, kl, mn = 2 * (row * ld + col), row, col
+                    for ph in range(P):
+                        k0 = 64 * ph
+                        k = k0 + kl
+                        pb = 2 * k0 if kc else 2 * k0 * ld
+                        if ph == P - 1:
+                            voff, soff = (PAST_END if k >= K else doff + pb), 0
+                        else:
+                            voff, soff = doff, pb
+                        what = (kc, shape, mn0, w, j, lane, ph)
+                        if not kc and k < K and mn < ext < mn + 8 and voff < nrec < voff + soff + 16:
+                            # the last row's chunk across the end: whole dwords
+                            assert k == K - 1 and ph == P - 1 and soff == 0, what
+                            assert (nrec - voff) % 4 == 0 and nrec - voff == 2 * (ext - mn), what
+                            continue
+                        wants_zero = k >= K or (kc and mn >= ext)
+                        in_matrix = (k + 7 < K and mn < ext) if kc else (k < K and mn + 7 < ext)
+                        _check_copy(voff, soff, nrec, 16, wants_zero, in_matrix, what)
