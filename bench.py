@@ -4,9 +4,10 @@
 
 A step is one C = A x B call through the C ABI (gemm_f32, the default
 kernel) on seeded synthetic operands already resident in HBM.  The step runs
-untimed for --settle-s seconds (default 0.3: the clock ramps up after the
-idle spell of input generation), then W untimed steps, then exactly K timed
-steps between two device synchronisations.  One
+untimed for --settle-s seconds (default 2 for this headline line, 0.3 for the
+other modes: the clock ramps up after the idle spell of input generation),
+then W untimed steps, then exactly K timed steps between two device
+synchronisations.  One
 JSON line is printed with the metric (TFLOP/s = 2MNK per step / seconds),
 the roofline of the kernel (algorithmic FLOP per launch over the average
 launch time from HIP events on the launch stream, against the chip's
@@ -20,7 +21,12 @@ Extra modes (used for counter runs under rocprofv3):
                         reference for scaling HBM byte counters
     --no-cpu-baseline   skip the oracle timing
     --row transpose     time transpose_f32 on the workload's A matrix instead
-                        (metric GB/s moved, bound HBM)
+                        (metric GB/s moved, bound HBM); the launches cycle
+                        through --rotate copies (default 4: a cold cache),
+                        and the same matrix repeated is reported beside it
+    --variants LIST     with --ladder: only these variant numbers
+    --view-offset N     floats between each allocation and its matrix view
+                        (default: the workload's own)
     --row reduce        time reduce_sum_f32 on --n uniform[-1,1) values
                         (default 2^28; metric GB/s read, bound HBM)
     --row mixed         time gemm_mixed on the workload rounded to --format
@@ -29,8 +35,9 @@ Extra modes (used for counter runs under rocprofv3):
     --op XY             time gemm_f32_op with op(A) = X, op(B) = Y (N or T):
                         the transposed factor is stored transposed, with a
                         compact leading dimension
-    --all-workloads     gemm_f32 at each of the five workloads: one JSON line
-                        per workload with the median and best launch time
+    --all-workloads     gemm_f32 at each of the five workloads (the padded
+                        rect workload also with aligned views, offset 0): one
+                        JSON line per run with the median and best launch time
                         (HIP events around every launch), then the oracle's
                         time on this host (see bench_all_workloads)
     --shape-sweep       the tile choice on 33 shapes (512^3 .. 8192^3,
@@ -121,6 +128,10 @@ def cpu_baseline(A, B, w, op_a="N", op_b="N", budget_s: float = 12.0):
 # by about 20 % over their first 25 ms, and a step of a fraction of a
 # millisecond would otherwise be timed entirely on that ramp.
 SETTLE_S = 0.3
+# The headline line settles longer: its timed region is short (tens of
+# milliseconds), and a longer untimed stretch of the same step keeps the GPU
+# visibly busy to outside utilisation samplers as well.
+HEADLINE_SETTLE_S = 2.0
 
 
 def settle(fn, seconds=None) -> int:
@@ -309,41 +320,66 @@ def bench_mixed(args, w) -> int:
 
 def bench_transpose(args, w) -> int:
     """transpose_f32 of the workload's A matrix (M x K, leading dimension lda)
-    into an M-column output; bytes moved = 2 x 4 M K per launch."""
+    into an M-column output; bytes moved = 2 x 4 M K per launch.
+
+    Cold: the launches cycle through --rotate distinct input/output pairs
+    (copies of the same matrix), so at square8192 (256 MiB in, 256 MiB out)
+    with the default 4 pairs each launch reads a matrix that 1.5 GiB of
+    other traffic has passed since it was last touched -- far more than the
+    256 MB last-level cache holds -- and the rate is an HBM rate.  The same
+    matrix transposed over and over (one pair) is also timed and reported as
+    cache-assisted: its input fits the last-level cache."""
     import torch
 
     from shared_memory_tiled_amd import binding, inputs
 
     A, _ = inputs.operands(w)
     dev = torch.device("cuda:0")
-    a = torch.from_numpy(A.buf).to(dev)
-    out = torch.empty(w.K * w.M + 64, dtype=torch.float32, device=dev)
-    variant = None if args.variant is None else args.variant
-    targs = (w.M, w.K, a.data_ptr() + 4 * w.offset, w.lda, out.data_ptr(), w.M)
+    rotate = max(1, args.rotate)
+    a0 = torch.from_numpy(A.buf).to(dev)
+    ins = [a0] + [a0.clone() for _ in range(rotate - 1)]
+    outs = [torch.empty(w.K * w.M + 64, dtype=torch.float32, device=dev) for _ in range(rotate)]
     moved = 2.0 * 4 * w.M * w.K
+    state = {"variant": args.variant, "i": 0}
 
-    def one():
-        if variant is None:
+    def call(x, y):
+        targs = (w.M, w.K, x.data_ptr() + 4 * w.offset, w.lda, y.data_ptr(), w.M)
+        if state["variant"] is None:
             binding.transpose_f32(*targs)
         else:
-            binding.transpose_f32_variant(variant, *targs)
+            binding.transpose_f32_variant(state["variant"], *targs)
 
-    timed = _timed
+    def one():                        # cold: the next pair in turn
+        i = state["i"] % rotate
+        state["i"] += 1
+        call(ins[i], outs[i])
+
+    def same():                       # cache-assisted: always the first pair
+        call(ins[0], outs[0])
 
     if args.ladder:
         for v in range(binding.transpose_f32_num_variants()):
-            variant = v
-            _, ms = timed(one, args.steps, 1)
+            state["variant"] = v
+            _, ms = _timed(one, args.steps, 1)
             print(json.dumps({"row": "transpose", "variant": v, "name": binding.transpose_f32_variant_name(v),
-                              "workload": w.name, "ms_per_launch": round(ms, 4),
+                              "workload": w.name, "rotate": rotate, "ms_per_launch": round(ms, 4),
                               "GB_per_s": round(moved / ms / 1e6, 1)}), flush=True)
         return 0
-    wall, ms = timed(one, args.steps, args.warmup)
-    # the same bytes through a plain device copy, for reference
-    src = a[w.offset:w.offset + w.M * w.lda]
-    dst = torch.empty_like(src)
-    _, copy_ms = timed(lambda: dst.copy_(src), args.steps, args.warmup)
+    wall, ms = _timed(one, args.steps, args.warmup)
+    _, same_ms = _timed(same, args.steps, args.warmup)
+    # the same bytes through a plain device copy, for reference (rotated too)
+    srcs = [x[w.offset:w.offset + w.M * w.lda] for x in ins]
+    dsts = [torch.empty_like(srcs[0]) for _ in range(rotate)]
+    cstate = {"i": 0}
+
+    def copy_one():
+        i = cstate["i"] % rotate
+        cstate["i"] += 1
+        dsts[i].copy_(srcs[i])
+
+    _, copy_ms = _timed(copy_one, args.steps, args.warmup)
     achieved = moved / (ms * 1e-3) / 1e9
+    copy_bytes = 2.0 * 4 * w.M * w.lda
     line = {
         "metric": "fp32 shared-tile transpose GB/s (bytes read + written) on MI355X",
         "value": round(moved * args.steps / wall / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
@@ -353,18 +389,24 @@ def bench_transpose(args, w) -> int:
         "data": "synthetic",
         "config": {"workload": f"{w.name} A matrix", "rows": w.M, "cols": w.K, "ld_in": w.lda,
                    "ld_out": w.M, "view_offset_floats": w.offset,
+                   "rotate": rotate,
+                   "cache": ("cold: each launch's input last touched "
+                             f"{(rotate - 1) * 2 * 4 * w.M * w.K / 2**20:.0f} MiB of traffic earlier"
+                             if rotate > 1 else "same matrix every launch"),
                    "kernel": ("auto: " + binding.transpose_f32_variant_name(
                        binding.transpose_f32_default_variant(w.M, w.K, w.lda, w.M)))
-                   if variant is None else binding.transpose_f32_variant_name(variant),
-                   "device_copy_same_bytes_GB_per_s": round(2.0 * 4 * w.M * w.lda / (copy_ms * 1e-3) / 1e9, 1)},
+                   if args.variant is None else binding.transpose_f32_variant_name(args.variant),
+                   "cache_assisted_same_matrix_GB_per_s": round(moved / (same_ms * 1e-3) / 1e9, 1),
+                   "device_copy_same_bytes_rotated_GB_per_s": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
     }
     if not args.no_cpu_baseline:
+        import numpy as np
+
         import oracle
         t0 = time.perf_counter()
         reps = 0
-        import numpy as np
         buf = np.zeros((w.K, w.M), dtype=np.float32)
         while time.perf_counter() - t0 < 10.0:
             oracle.transpose_into(A.view, buf)
@@ -487,10 +529,17 @@ def bench_all_workloads(args) -> int:
 
     from shared_memory_tiled_amd import binding, inputs
 
+    import dataclasses
+
     cores = len(os.sched_getaffinity(0))
     dev = torch.device("cuda:0")
+    runs = []
     for name, launches in WORKLOAD_LAUNCHES.items():
         w = inputs.WORKLOADS[name]
+        runs.append((name, launches, w))
+        if w.offset != 0:       # the same shape with aligned views: alignment apart from ld
+            runs.append((name, launches, dataclasses.replace(w, offset=0)))
+    for name, launches, w in runs:
         A, B = inputs.operands(w)
         a = torch.from_numpy(A.buf).to(dev)
         b = torch.from_numpy(B.buf).to(dev)
@@ -519,7 +568,7 @@ def bench_all_workloads(args) -> int:
                 "percent_of_peak_median": round(100 * flop / med / 1e9 / PEAK_FP32_TFLOPS, 2)}
         del a, b, c
         torch.cuda.empty_cache()
-        if not args.no_cpu_baseline:
+        if not args.no_cpu_baseline and w.offset == inputs.WORKLOADS[name].offset:
             import oracle
             cpu = {"cores": cores, "cpu": cpu_model()}
             if not w.sampled:
@@ -560,10 +609,24 @@ def main(argv=None) -> int:
     ap.add_argument("--n", type=int, default=2 ** 28, help="values summed by --row reduce")
     ap.add_argument("--all-workloads", action="store_true")
     ap.add_argument("--shape-sweep", action="store_true")
-    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
-                    help="untimed run of each timed step, in seconds, before its warm-up steps")
+    ap.add_argument("--settle-s", type=float, default=None,
+                    help="untimed run of each timed step, in seconds, before its warm-up steps "
+                         f"(default {SETTLE_S}; {HEADLINE_SETTLE_S} for the headline line)")
+    ap.add_argument("--variants", default=None,
+                    help="with --ladder: comma-separated variant numbers to time (default: all)")
+    ap.add_argument("--view-offset", type=int, default=None,
+                    help="floats between each allocation's start and its matrix view "
+                         "(default: the workload's own)")
+    ap.add_argument("--rotate", type=int, default=4,
+                    help="--row transpose: distinct input/output pairs cycled through, so each "
+                         "launch reads a matrix the last-level cache no longer holds (1: the same "
+                         "matrix every launch)")
     args = ap.parse_args(argv)
-    globals()["SETTLE_S"] = max(0.0, args.settle_s)
+    headline = not (args.all_workloads or args.shape_sweep or args.ladder or args.row != "gemm")
+    if args.settle_s is not None:
+        globals()["SETTLE_S"] = max(0.0, args.settle_s)
+    elif headline:
+        globals()["SETTLE_S"] = HEADLINE_SETTLE_S
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -598,6 +661,9 @@ def main(argv=None) -> int:
     if args.row == "reduce":
         return bench_reduce(args)
     w = inputs.WORKLOADS[args.workload]
+    if args.view_offset is not None:
+        import dataclasses
+        w = dataclasses.replace(w, offset=args.view_offset)
     if args.row == "transpose":
         return bench_transpose(args, w)
     if args.row == "mixed":
@@ -635,6 +701,8 @@ def main(argv=None) -> int:
     if args.ladder:
         variants = list(range(binding.gemm_f32_num_variants())) + \
             [binding.DIAGNOSTIC_BASE + d for d in range(binding.gemm_f32_num_diagnostic_variants())]
+        if args.variants:
+            variants = [int(v) for v in args.variants.split(",")]
         for v in variants:
             steps = max(1, min(args.steps, 3 if v == 0 else args.steps))
             wall, ms = timed(v, steps, 1)
