@@ -101,8 +101,12 @@ extern "C" {
  *      deterministic and the same for every op pair) replace that choice
  *      where a cost model of rounds, per-kernel efficiency and fixed cost
  *      per tile gives them the shorter time (K >= 448), or in place of the
- *      split-phase tiles (K >= 384).  gemm_f32_default_variant() names the
- *      configuration a shape runs.
+ *      split-phase tiles (K >= 384).  Products of at most 1024 output tiles
+ *      of 16 x 16 take small tiles instead (16 x 16 on 8 waves up to 512 of
+ *      them, else 32 x 32 on 4 waves), whose K is split over the waves of
+ *      each block, operands loaded straight into registers for
+ *      v_mfma_f32_16x16x4_f32, partial tiles added in wave order.
+ *      gemm_f32_default_variant() names the configuration a shape runs.
  * Variants numbered from 16 up are diagnostic layouts of the same rungs, kept
  * so that their hardware counters can be compared; see
  * gemm_f32_variant_name().
@@ -179,6 +183,26 @@ int gemm_f32_num_diagnostic_variants(void);
  * negative or above INT_MAX.  Launches nothing, needs no device; for callers
  * that want to know which kernel a call will use. */
 int gemm_f32_default_variant(int64_t M, int64_t N, int64_t K);
+
+/* Measurement helper, this library's own (not part of the product): a loop
+ * of non-packed binary32 fused multiply-adds on the vector ALU -- the
+ * register-blocked rung's instruction -- whose time, measured by the caller,
+ * gives that instruction's issue rate on the device.
+ *   form    0: one operand in a scalar register; 1: all operands in vector
+ *           registers, 16 independent accumulators per lane; 2: an 8 x 8
+ *           outer product of vector registers (the rung's inner step)
+ *   blocks  workgroups of 256 threads (4 waves) to launch, >= 1
+ *   iters   loop trips: each lane does iters x 16 FMAs (forms 0 and 1) or
+ *           (iters / 4) x 64 (form 2)
+ *   out     device pointer to blocks x 256 floats, overwritten (keeps the
+ *           results live)
+ *   stamps  device pointer to blocks x 4 x 4 uint64_t (8-byte aligned): for
+ *           wave w, stamps[4w .. 4w+3] = shader clock counter and 100 MHz
+ *           counter at the start, then at the end of its loop
+ * Enqueue-only on `stream`; statuses as for gemm_f32 (an unknown form gives
+ * GEMM_F32_ERR_INVALID_VARIANT). */
+int gemm_f32_valu_probe(int form, int64_t blocks, int iters, float *out, uint64_t *stamps,
+                        void *stream);
 
 /* Static, NUL-terminated description of a status code (the by-name report
  * of the chapter 2 error check cited with the codes above); "unknown status"

@@ -86,6 +86,8 @@ def load_library():
         lib.reduce_sum_f32.restype = ctypes.c_int
         lib.reduce_sum_f32_variant.argtypes = [ctypes.c_int] + rsig
         lib.reduce_sum_f32_variant.restype = ctypes.c_int
+        lib.gemm_f32_valu_probe.argtypes = [ctypes.c_int, _i64, ctypes.c_int, _vp, _vp, _vp]
+        lib.gemm_f32_valu_probe.restype = ctypes.c_int
         lib.reduce_sum_f32_variant_noalloc.argtypes = [ctypes.c_int, _i64, _vp, _vp, _vp]
         lib.reduce_sum_f32_variant_noalloc.restype = ctypes.c_int
         lib.reduce_sum_f32_num_variants.argtypes = []
@@ -254,6 +256,12 @@ def transpose(X: torch.Tensor, out: torch.Tensor | None = None, variant=None, st
     else:
         transpose_f32_variant(variant, *args, stream=stream)
     return out
+
+
+def gemm_f32_valu_probe(form, blocks, iters, out, stamps, stream=None) -> None:
+    """The vector-ALU FMA loop of the library's measurement helper."""
+    lib = load_library()
+    _check(lib.gemm_f32_valu_probe(int(form), int(blocks), int(iters), _addr(out), _addr(stamps), _stream(stream)))
 
 
 REDUCE_DEFAULT = 4

@@ -46,6 +46,9 @@ const Diagnostic kDiagnostics[] = {
     {"mfma128x128_bk32_w2x2_sched", 3, 18},
     {"mfma128x128_bk32_w2x2_sched_g16", 3, 19},
     {"mfma64x64_bk32_w1x1_k4_sched", 3, 20},
+    {"mfma16x16_w4_small", 3, 21},
+    {"mfma32x32_w4_small", 3, 22},
+    {"mfma16x16_w8_small", 3, 23},
 };
 constexpr int kNumDiagnostics = (int)(sizeof(kDiagnostics) / sizeof(kDiagnostics[0]));
 
@@ -180,6 +183,20 @@ extern "C" const char* gemm_f32_status_string(int status) {
             return "partials exceed the library's fixed 1 MiB scratch: use reduce_sum_f32_variant with a workspace";
         default: return "unknown status";
     }
+}
+
+// A measurement helper: the vector-ALU FMA loop of probe.hip.
+extern "C" int gemm_f32_valu_probe(int form, int64_t blocks, int iters, float* out, uint64_t* stamps,
+                                   void* stream) {
+    if (form < 0 || form > 2) return GEMM_F32_ERR_INVALID_VARIANT;
+    if (blocks < 1 || iters < 0) return GEMM_F32_ERR_INVALID_DIM;
+    if (blocks > 0x7FFFFFFF / 256) return GEMM_F32_ERR_TOO_LARGE;
+    if (out == nullptr || stamps == nullptr) return GEMM_F32_ERR_NULL_PTR;
+    if (misaligned(out) || ((uintptr_t)stamps & 7u) != 0) return GEMM_F32_ERR_MISALIGNED;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_F32_ERR_DEVICE;
+    const hipError_t e = launch_valu_probe(form, (int)blocks, iters, out, stamps, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
 }
 
 // ---------------------------------------------------------------- transpose

@@ -65,6 +65,15 @@ hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b
 // below 2^31 bytes), and its launcher.
 bool ksplit_f32_fits(const GemmArgs& p, int op_a, int op_b);
 hipError_t launch_ksplit_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m);
+// Small products (small.hip): 16 x 16 or 32 x 32 output tiles whose k
+// groups are split over the waves of each block, operands loaded straight
+// into registers (shape 0: 16 x 16 on 4 waves, 1: 32 x 32 on 4 waves, 2: 16
+// x 16 on 8 waves).  Any sizes, leading dimensions and op pair.
+hipError_t launch_small_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int shape);
+// Measurement helper (probe.hip): a loop of non-packed fp32 FMAs on the
+// vector ALU in operand form `form` (0 scalar-register operand, 1 vector
+// registers, 2 8 x 8 outer product), `blocks` blocks of 256 threads.
+hipError_t launch_valu_probe(int form, int blocks, int iters, float* out, uint64_t* stamps, hipStream_t s);
 int regblock_num_configs();
 const char* regblock_config_name(int config);
 

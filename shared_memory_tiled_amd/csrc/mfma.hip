@@ -609,6 +609,16 @@ hipError_t launch_ksplit_or_splitk(const GemmArgs& p, hipStream_t s, int tiles_m
     {launch_ksplit_or_splitk<false, false>, launch_ksplit_or_splitk<false, true>,          \
      launch_ksplit_or_splitk<true, false>, launch_ksplit_or_splitk<true, true>}
 
+// Small output tiles whose k groups are split over the waves of a block
+// (small.hip).
+template <int SHAPE, bool TRA, bool TRB>
+hipError_t launch_small_cfg(const GemmArgs& p, hipStream_t s, int, int, int, unsigned) {
+    return launch_small_f32(p, s, TRA, TRB, SHAPE);
+}
+#define SMALL_OPS(SHAPE)                                                                  \
+    {launch_small_cfg<SHAPE, false, false>, launch_small_cfg<SHAPE, false, true>,          \
+     launch_small_cfg<SHAPE, true, false>, launch_small_cfg<SHAPE, true, true>}
+
 // NN only (diagnostic layouts) or all four op combinations.
 #define NN_ONLY(BM, BN, BK, WM, WN, D, S) \
     {launch_one<BM, BN, BK, WM, WN, D, S, false, false>, nullptr, nullptr, nullptr}
@@ -654,6 +664,10 @@ const MfmaConfig kConfigs[] = {
     {"mfma128x128_bk32_w2x2_sched_g16", 128, 128, 256, 16, SCHED128_OPS},
     // four waves, each the whole 64 x 64 tile over every fourth phase
     {"mfma64x64_bk32_w1x1_k4_sched", 64, 64, 1024, 8, KSPLIT_OPS},
+    // small products: 16 x 16 or 32 x 32 tiles, k groups split over the waves
+    {"mfma16x16_w4_small", 16, 16, 256, 8, SMALL_OPS(0)},
+    {"mfma32x32_w4_small", 32, 32, 256, 8, SMALL_OPS(1)},
+    {"mfma16x16_w8_small", 16, 16, 512, 8, SMALL_OPS(2)},
 };
 #undef NN_ONLY
 #undef ALL_OPS
@@ -662,6 +676,7 @@ const MfmaConfig kConfigs[] = {
 #undef SCHED128_OPS
 #undef SPLITK_OPS
 #undef KSPLIT_OPS
+#undef SMALL_OPS
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 }  // namespace
 
@@ -692,7 +707,9 @@ const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConf
 // from 512^3 to 8192^3; below K = 448 the model misjudges them against
 // two co-resident 128 x 128 workgroups per CU, e.g. at 3000 x 3000 x 384:
 // there they only replace the split-phase tiles, from K = 384, three
-// phases per wave).  Every picked configuration
+// phases per wave).  Last, products of at most 1024 output tiles of 16 x 16
+// take the small-tile kernels (16 x 16 tiles on 8 waves up to 512 such
+// tiles, else 32 x 32 tiles on 4 waves).  Every picked configuration
 // is built for all four op combinations.
 namespace {
 // Modelled time (ns) of a configuration: rounds x (tile work / efficiency
@@ -734,6 +751,15 @@ int mfma_pick_config(int M, int N, int K) {
     const bool split_fits = K % 4 == 0 && M % 4 == 0 && N % 4 == 0;
     if (split_fits && ((pick == small && K >= 384) || (K >= 448 && model_ns(20, M, N, K) < model_ns(pick, M, N, K))))
         pick = 20;
+    // Few output elements: small tiles whose k groups are split over the
+    // waves of a block (small.hip), any shape and K.  Measured kernel times
+    // (256^3: 3.9 us against 8.7 for the split-phase tiles; 512^3: 9.2
+    // against 11.8 for the k-split tiles; 256 x 256 x 1024: 6.9 against
+    // 18.4) put the crossover near 1024 tiles of 16 x 16 (640^3, 1600 such
+    // tiles: the k-split tiles lead, 16.2 against 17.8 us).
+    const int64_t t16 = (int64_t)ceil_div(M, 16) * ceil_div(N, 16);
+    if (t16 <= 512) pick = 23;                   // 16 x 16 tiles, 8 waves
+    else if (t16 <= 1024) pick = 22;             // 32 x 32 tiles, 4 waves
     return pick;
 }
 

@@ -23,8 +23,13 @@
 //    other buffer after them, so one barrier per phase orders both the write
 //    before the next read and the reads before the overwrite two phases on.
 //  * per k step a thread reads 16 floats from LDS for 64 fused multiply-adds
-//    (1 byte of LDS per FMA).  Packed FP32 is disabled for this library, so
-//    the VALU ceiling is half of the chip's fp32 peak.
+//    (1 byte of LDS per FMA), each a v_fmac_f32 with all three operands in
+//    vector registers.  Packed FP32 is disabled for this library; on gfx950
+//    the non-packed form with vector-register operands still issues one
+//    wave64 FMA per SIMD every two cycles (measured: 0.43 per cycle at 8
+//    waves per SIMD, where a form with a scalar-register operand reaches
+//    only half that), so the VALU ceiling of this rung is the chip's fp32
+//    peak, 256 FLOP per clock per CU.
 #include "launch.h"
 
 namespace gemmf32 {

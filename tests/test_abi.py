@@ -311,6 +311,8 @@ def test_default_variant_choices(binding):
     multiples of 4, the 64 x 64 tiles whose four waves split the phases where
     a cost model of rounds, efficiency and fixed cost per tile gives them the
     shorter time (K >= 448), or in place of the split-phase tiles (K >= 384).
+    Last, at most 512 output tiles of 16 x 16 take the 16 x 16 small-tile
+    kernel on 8 waves, at most 1024 the 32 x 32 one on 4 waves, whatever K.
     For the 16-bit product the
     scheduled kernel from 128 tiles of 256 x 256, 128 x 128 direct copies
     from 128 tiles of those (64 for K >= 2048), else 64 x 64 tiles.  Invalid
@@ -345,8 +347,17 @@ def test_default_variant_choices(binding):
         (1000, 2000, 500): "mfma64x64_bk32_w1x1_k4_sched",        # in place of the split-phase tiles
         (1000, 1000, 380): "mfma64x64_bk32_w2x2_k4",              # K < 384
         (1002, 1000, 1000): "mfma64x64_bk32_w2x2_k4",             # M % 4 = 2
-        (256, 256, 256): "mfma64x64_bk32_w2x2_k4",
-        (1, 1, 1): "mfma64x64_bk32_w2x2_k4",
+        (256, 256, 256): "mfma16x16_w8_small",                   # 256 tiles of 16 x 16
+        (1, 1, 1): "mfma16x16_w8_small",
+        (256, 256, 0): "mfma16x16_w8_small",
+        (128, 128, 8192): "mfma16x16_w8_small",
+        (368, 352, 97): "mfma16x16_w8_small",                     # 506 tiles, ragged K
+        (512, 512, 512): "mfma32x32_w4_small",                    # 1024 tiles of 16 x 16
+        (4096, 64, 256): "mfma32x32_w4_small",
+        (500, 400, 257): "mfma32x32_w4_small",
+        (640, 640, 640): "mfma64x64_bk32_w1x1_k4_sched",          # 1600 tiles of 16 x 16
+        (528, 512, 512): "mfma64x64_bk32_w1x1_k4_sched",          # 1056
+        (1000, 1000, 380): "mfma64x64_bk32_w2x2_k4",
     }
     for (M, N, K), name in f32.items():
         v = binding.gemm_f32_default_variant(M, N, K)

@@ -80,7 +80,7 @@ class Problem:
 
 
 def test_kernel_is_the_default_for_its_shapes():
-    for shape in [(1000, 1000, 1000), (300, 260, 1000), (252, 136, 516), (3072, 3072, 3072),
+    for shape in [(1000, 1000, 1000), (560, 548, 1000), (540, 516, 516), (3072, 3072, 3072),
                   (4608, 4608, 4608), (1000, 2000, 500), (4100, 4104, 4100), (2000, 1000, 996)]:
         assert default_name(*shape) == KS, shape
     for shape in [(1000, 1000, 380), (1002, 1000, 1000), (1000, 1000, 1001), (8192, 8192, 8192),
@@ -89,10 +89,12 @@ def test_kernel_is_the_default_for_its_shapes():
 
 
 FULL = [
-    # 5 x 5 tiles with ragged edges and K % 32 = 8 (first phase partial),
-    # 4 x 3 tiles with K % 32 = 4, 16 x 16 tiles with K a multiple of 32
-    (300, 260, 1000),
-    (252, 136, 516),
+    # 9 x 9 tiles with ragged edges and K % 32 = 8 (first phase partial),
+    # 9 x 9 tiles with K % 32 = 4, 16 x 16 tiles with K a multiple of 32
+    # (more than 1024 output tiles of 16 x 16 each, so not the small-tile
+    # kernels)
+    (560, 548, 1000),
+    (540, 516, 516),
     (1000, 1000, 512),
 ]
 
@@ -192,7 +194,7 @@ def test_planted_infinity_stays_in_its_row_or_column(ops, factor):
     stored row before its own, instead of a zero, would carry the infinity to
     row r + 1 (column c + 1)."""
     op_a, op_b = ops
-    M, N, K = 260, 200, 1000                                # K % 32 = 8
+    M, N, K = 580, 520, 1000                                # K % 32 = 8
     assert default_name(M, N, K) == KS
     gen = np.random.default_rng([M, N, K, len(op_a + op_b), ord(factor)])
     a = inputs.random_matrix(gen, *stored_shape(op_a, M, K), "uniform")

@@ -72,12 +72,13 @@ def transposed_copy(t: torch.Tensor) -> torch.Tensor:
     return t.t().contiguous()
 
 
-# One shape per tile configuration the default path picks (64x64 split over
-# four wave groups with 32- and 16-deep phases, 128x128 register-staged,
-# 128x128 and 256x256 on four scheduled waves, 256x256 on eight waves with a
-# ghost k phase, and with ragged edges as well).
-SAME_BITS_SHAPES = [(300, 200, 130), (2100, 2050, 300), (3840, 2048, 100), (2048, 2048, 96), (4096, 4096, 512),
-                    (4096, 4096, 515), (8193, 8190, 99)]
+# One shape per tile configuration the default path picks (16x16 and 32x32
+# small tiles with k groups split over the waves, 64x64 split over four wave
+# groups with 32- and 16-deep phases, 128x128 register-staged, 128x128 and
+# 256x256 on four scheduled waves, 256x256 on eight waves with a ghost k
+# phase, and with ragged edges as well).
+SAME_BITS_SHAPES = [(300, 200, 130), (500, 400, 257), (1000, 1000, 380), (2100, 2050, 300), (3840, 2048, 100),
+                    (2048, 2048, 96), (4096, 4096, 512), (4096, 4096, 515), (8193, 8190, 99)]
 
 
 @pytest.mark.parametrize("shape", SAME_BITS_SHAPES, ids=lambda s: "x".join(map(str, s)))
