@@ -40,6 +40,9 @@ Extra modes (used for counter runs under rocprofv3):
                         JSON line per run with the median and best launch time
                         (HIP events around every launch), then the oracle's
                         time on this host (see bench_all_workloads)
+    --valu-probe        the issue rate of non-packed v_fmac_f32 on the vector
+                        ALU in three operand forms, with the measured clock
+                        (the register-blocked rung's ceiling)
     --shape-sweep       the tile choice on 33 shapes (512^3 .. 8192^3,
                         rectangular and awkward ones): TFLOP/s of the default
                         configuration, of every candidate configuration and
@@ -148,6 +151,38 @@ def settle(fn, seconds=None) -> int:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     return n
+
+
+def graph_ms_per_launch(fn, launches: int, replays: int = 5):
+    """Per-launch time of `fn` when `launches` calls of it are captured in
+    one HIP graph and the graph is replayed: the launches then run back to
+    back on the GPU, with no host in between.  A product of a few
+    microseconds takes less time on the GPU than one call through Python
+    takes on the host, so timing eager calls measures the host.  The graph is
+    replayed untimed for 0.3 s first (steady clock), then `replays` times
+    between HIP events; returns the per-launch times of those replays, in
+    milliseconds.  The library enqueues only kernel launches (no memory
+    operations), which capture as kernel nodes."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(launches):
+            fn()
+    torch.cuda.synchronize()
+    settle(g.replay)
+    out = []
+    stream = torch.cuda.current_stream()
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / launches)
+    del g
+    return out
 
 
 def _timed(fn, steps, warmup):
@@ -445,8 +480,9 @@ MIXED_SWEEP_CANDIDATES = ["mixed64x64_bk64_w1x2", "mixed128x128_bk64_w2x2_direct
 def bench_shape_sweep(args) -> int:
     """For each shape (uniform[-1,1) operands, compact leading dimensions):
     the configuration gemm_f32 picks and the TFLOP/s of every candidate
-    configuration through gemm_f32_variant, each run untimed for 0.1 s and
-    then timed over 10 launches with HIP events on the launch stream, plus
+    configuration through gemm_f32_variant, each as 10 launches captured in
+    a HIP graph, replayed untimed for 0.3 s, then timed over 3 replays (the
+    median per launch; see graph_ms_per_launch), plus
     torch.matmul on the same operands (fp32, TF32 off) for context.  With
     --row mixed the same for gemm_mixed on operands rounded to --format
     (binary32 result), against torch.matmul in that format (16-bit result)."""
@@ -473,15 +509,8 @@ def bench_shape_sweep(args) -> int:
         context = lambda X, Y, out: torch.matmul(X, Y, out=out)
 
     def tflops(fn, flop, reps=10):
-        settle(fn, 0.1)
-        stream = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return flop / (e0.elapsed_time(e1) / reps) / 1e9
+        import statistics
+        return flop / statistics.median(graph_ms_per_launch(fn, reps, replays=3)) / 1e9
 
     gen = torch.Generator(device="cuda").manual_seed(20261202)
     for (M, N, K) in SWEEP_SHAPES:
@@ -501,6 +530,44 @@ def bench_shape_sweep(args) -> int:
     return 0
 
 
+def bench_valu_probe(args) -> int:
+    """The vector-ALU issue rate of the register-blocked rung's instruction
+    (non-packed v_fmac_f32), from the library's measurement helper: each
+    operand form at 4 and 8 waves per SIMD, three runs each, with the clock
+    the loop ran at (shader clock counter against the 100 MHz counter) and
+    the wave64 FMAs issued per SIMD per clock at that clock."""
+    import torch
+
+    from shared_memory_tiled_amd import binding
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 20000
+    forms = {0: "scalar-register operand", 1: "vector registers", 2: "8x8 outer product"}
+    for form, what in forms.items():
+        for wps in (4, 8):
+            blocks = cus * wps                    # 4 waves per block: one per SIMD
+            waves = blocks * 4
+            out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            stamps = torch.zeros(waves * 4, dtype=torch.int64, device="cuda")
+            for rep in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                binding.gemm_f32_valu_probe(form, blocks, iters, out, stamps)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1)
+                t = stamps.view(waves, 4).cpu().double()
+                mhz = float((100.0 * (t[:, 2] - t[:, 0]) / (t[:, 3] - t[:, 1])).mean())
+                fmas = blocks * 256.0 * ((iters // 4) * 64 if form == 2 else iters * 16)
+                per_simd_clk = fmas / 64 / (ms * 1e-3) / (cus * 4) / (mhz * 1e6)
+                print(json.dumps({"valu_probe_form": form, "operands": what, "waves_per_simd": wps, "run": rep,
+                                  "ms": round(ms, 4), "tflops": round(2 * fmas / (ms * 1e-3) / 1e12, 2),
+                                  "clock_mhz": round(mhz), "wave64_fma_per_simd_per_clock": round(per_simd_clk, 4),
+                                  "tflops_at_2400mhz_same_rate": round(per_simd_clk * 64 * 2 * cus * 4 * 2.4e9 / 1e12, 1)}),
+                      flush=True)
+    return 0
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -517,7 +584,11 @@ def bench_all_workloads(args) -> int:
 
     GPU: 3 warm-up launches, then a HIP event before the first launch and
     after every launch on the launch stream; the median and best of the
-    per-launch times give TFLOP/s and the fraction of the fp32 peak.
+    per-launch times give TFLOP/s and the fraction of the fp32 peak.  The
+    same number of launches is also captured in one HIP graph and replayed
+    (graph_ms_per_launch, see graph_ms_per_launch): for the microsecond-scale
+    products the eager launches wait on the host's call rate, the replayed
+    ones run back to back.
     Oracle, on this host, unchanged: the full product at square256 and
     square1000 on one thread and on all cores, at square4096 on all cores;
     at the two largest workloads the 4096 sampled entries plus edge entries
@@ -558,14 +629,23 @@ def bench_all_workloads(args) -> int:
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
         ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(launches)]
+        eager_c = c.clone()
+        graph = graph_ms_per_launch(lambda: binding.gemm_f32(*call), launches)
+        torch.cuda.synchronize()
+        graph_same_bits = bool(torch.equal(c, eager_c))
         flop = 2.0 * w.M * w.N * w.K
         med, best = statistics.median(ms), min(ms)
+        gmed = statistics.median(graph)
         line = {"workload": name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb,
                 "ldc": w.ldc, "view_offset_floats": w.offset, "values": w.dist,
                 "kernel": binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(w.M, w.N, w.K)),
                 "launches": launches, "median_ms": round(med, 5), "best_ms": round(best, 5),
                 "tflops_median": round(flop / med / 1e9, 3), "tflops_best": round(flop / best / 1e9, 3),
-                "percent_of_peak_median": round(100 * flop / med / 1e9 / PEAK_FP32_TFLOPS, 2)}
+                "percent_of_peak_median": round(100 * flop / med / 1e9 / PEAK_FP32_TFLOPS, 2),
+                "graph_ms_per_launch": round(gmed, 5), "graph_tflops": round(flop / gmed / 1e9, 3),
+                "graph_percent_of_peak": round(100 * flop / gmed / 1e9 / PEAK_FP32_TFLOPS, 2),
+                "graph_result_same_bits_as_eager": graph_same_bits}
+        del eager_c
         del a, b, c
         torch.cuda.empty_cache()
         if not args.no_cpu_baseline and w.offset == inputs.WORKLOADS[name].offset:
@@ -608,6 +688,8 @@ def main(argv=None) -> int:
     ap.add_argument("--format", default="bf16", choices=["bf16", "f16"], help="16-bit format of --row mixed")
     ap.add_argument("--n", type=int, default=2 ** 28, help="values summed by --row reduce")
     ap.add_argument("--all-workloads", action="store_true")
+    ap.add_argument("--valu-probe", action="store_true",
+                    help="issue rate of non-packed v_fmac_f32 (the register-blocked rung's instruction)")
     ap.add_argument("--shape-sweep", action="store_true")
     ap.add_argument("--settle-s", type=float, default=None,
                     help="untimed run of each timed step, in seconds, before its warm-up steps "
@@ -622,7 +704,7 @@ def main(argv=None) -> int:
                          "launch reads a matrix the last-level cache no longer holds (1: the same "
                          "matrix every launch)")
     args = ap.parse_args(argv)
-    headline = not (args.all_workloads or args.shape_sweep or args.ladder or args.row != "gemm")
+    headline = not (args.all_workloads or args.shape_sweep or args.ladder or args.valu_probe or args.row != "gemm")
     if args.settle_s is not None:
         globals()["SETTLE_S"] = max(0.0, args.settle_s)
     elif headline:
@@ -654,6 +736,8 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n}), flush=True)
         del src, dst
 
+    if args.valu_probe:
+        return bench_valu_probe(args)
     if args.all_workloads:
         return bench_all_workloads(args)
     if args.shape_sweep:
