@@ -327,7 +327,13 @@ int reduce_sum_f32_variant_noalloc(int variant, int64_t n, const float *x, float
  * are served by element-wise loads (correct, slower).
  * gemm_mixed picks the tile shape for the problem; gemm_mixed_variant runs
  * tile configuration `variant` (0 .. gemm_mixed_num_variants() - 1, named by
- * gemm_mixed_variant_name).  The scheduled configuration
+ * gemm_mixed_variant_name).  Below 128 tiles of 128 x 128 (and below 128 of
+ * 256 x 256) with K a multiple of 8, gemm_mixed and gemm_mixed_op take
+ * 64 x 64 tiles whose four waves each run the whole tile over every fourth
+ * 32-deep phase (mixed64x64_bk32_w4_ksplit, v_mfma_f32_16x16x32; partial
+ * tiles added in wave order, so every op pair gives the same bits); it needs
+ * what the scheduled configuration needs (below), and a problem it does not
+ * take runs the element-wise 64 x 64 kernel.  The scheduled configuration
  * (mixed256x256_bk64_w4_sched, gemm_mixed's choice once there are 128 tiles
  * of 256 x 256) takes K a multiple of 8, N even (M too for A stored
  * transposed in gemm_mixed_op, and not N for B stored transposed),

@@ -28,9 +28,16 @@ FLAGS = ["-O3", f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", "-Wall",
          "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-source extra flags.  mfma16_ksplit.hip: matrix instructions in their
+# vector-register form -- with the accumulators in AGPRs the register
+# allocator copied every accumulator before each matrix instruction of that
+# kernel.
+EXTRA_FLAGS = {"mfma16_ksplit.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
 def _compile(src: str, resource_usage: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if resource_usage:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     proc = subprocess.run(cmd, capture_output=True, text=True)

@@ -37,6 +37,13 @@ int mixed_pick_config(int M, int N, int K);
 // B stored N x K; validated like GemmArgs with the leading dimensions of the
 // stored matrices.
 hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b);
+// 16-bit product on 64 x 64 tiles whose four waves split the phases
+// (mfma16_ksplit.hip): whether it takes the problem (K a multiple of 8, an
+// mn-contiguous factor's width even, vector-aligned operands below 2^31
+// bytes), and its launcher (format 0 bfloat16, 1 binary16; op 1: that factor
+// stored transposed).
+bool ksplit16_fits(const Gemm16Args& p, int op_a, int op_b);
+hipError_t launch_ksplit16(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b);
 
 // Sum reduction (reduce.hip): *out = sum of x[0 .. n-1].
 hipError_t launch_reduce(int variant, int64_t n, const float* x, float* out, float* ws, hipStream_t s);

@@ -45,7 +45,7 @@
 // mode; a dword-aligned multi-dword load is legal): operands whose base is
 // only 2-byte aligned, or whose leading dimension is odd, take the same
 // kernels with element-wise 16-bit loads.
-#include "launch.h"
+#include "mfma16_common.h"
 
 #include <type_traits>
 #include <utility>
@@ -54,10 +54,6 @@ namespace gemmf32 {
 
 namespace {
 
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBK = 64;          // k values per phase = one 128-byte LDS row
 constexpr int kCPR = kBK / 8;    // 16-byte chunks per LDS row
@@ -73,38 +69,6 @@ __device__ __forceinline__ void copy16_to_lds(const uint16_t* src, uint16_t* dst
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// Four 16-bit values through ds_read_b64_tr_b16.  Within each group of 16
-// lanes, value e of lane i is element i % 4 of the 8 bytes addressed by lane
-// 4 e + i / 4.  So if lane j of a group addresses row kb + j / 4, columns
-// nb + 4 (j % 4) .. +3 of a row-major tile, lane i receives the column
-// nb + i, rows kb .. kb + 3: four consecutive k of one n.
-//
-// Issued as inline assembly: the compiler would otherwise wait for every
-// outstanding global -> LDS copy before the first such read (it cannot tell
-// that the copies fill the other stage).  The "memory" clobber keeps the
-// reads in order with the barriers; wait_tied() below is their wait.
-__device__ __forceinline__ u32x2 read_tr16(uint32_t lds_byte_addr) {
-    u32x2 v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(lds_byte_addr) : "memory");
-    return v;
-}
-
-// Waits for all outstanding LDS reads; the fragments pass through the wait
-// as operands, so no use of them can be scheduled before it.
-template <int N>
-__device__ __forceinline__ void wait_tied(u32x4 (&b)[N]) {
-    static_assert(N == 1 || N == 2 || N == 4, "fragment count");
-    if constexpr (N == 1) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]) : : "memory");
-    if constexpr (N == 2) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]) : : "memory");
-    if constexpr (N == 4)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : : "memory");
-}
-
-// Byte address inside LDS of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 template <int FMT>
 __device__ __forceinline__ floatx16 mfma16(u32x4 a, u32x4 b, floatx16 c) {
@@ -151,32 +115,6 @@ __device__ __forceinline__ u32x2 load4_ghost16(const uint16_t* __restrict__ base
         }
     }
     return v;
-}
-
-// 16 bytes of LDS at a byte address.
-__device__ __forceinline__ u32x4 lds_read128(uint32_t lds_byte_addr) {
-    typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
-    return *(lds_u32x4*)(uintptr_t)lds_byte_addr;
-}
-
-// read_tr16 with a compile-time byte offset in the instruction.
-__device__ __forceinline__ u32x2 read_tr16_off(uint32_t lds_byte_addr, int off) {
-    u32x2 v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_byte_addr), "i"(off) : "memory");
-    return v;
-}
-
-template <typename F, int... Q>
-__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Q...>) {
-    (f(std::integral_constant<int, Q>{}), ...);
-}
-// f(std::integral_constant<int, q>{}) for q = 0 .. N - 1, in order: every
-// index is a compile-time constant, so arrays indexed by it stay in registers
-// (a loop under #pragma unroll is unrolled only after the pass that would
-// have kept them there).
-template <int N, typename F>
-__device__ __forceinline__ void unroll(F&& f) {
-    unroll_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 // Column j of an 8 x W block (W = 4 or 8) held as eight rows of W 16-bit
@@ -1139,6 +1077,17 @@ hipError_t launch_sched(const Gemm16Args& p, hipStream_t s, int tiles_m, int til
     return launch_sched_kernel<FMT, true, false>(p, s, tiles_m, tiles_n, kSchedGroupM, blocks);
 }
 
+// Configuration 9 (the k-split kernel, mfma16_ksplit.hip) where it takes
+// the problem; other problems given to it run the 64 x 64 tiles of
+// gemm16_kernel.
+template <int FMT>
+hipError_t launch_ksplit16_cfg(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                               unsigned blocks) {
+    if (!ksplit16_fits(p, 0, 0))
+        return launch16<FMT, 64, 64, 1, 2, false, true, false>(p, s, tiles_m, tiles_n, group_m, blocks);
+    return launch_ksplit16(p, s, FMT, 0, 0);
+}
+
 const MixedConfig kMixed[] = {
     {"mixed256x256_bk64_w2x4_directA", 256, 256, 8, MIXED(256, 256, 2, 4, true, false)},
     {"mixed256x256_bk64_w2x4", 256, 256, 8, MIXED(256, 256, 2, 4, false, false)},
@@ -1152,9 +1101,15 @@ const MixedConfig kMixed[] = {
     {"mixed256x256_bk64_w4_sched", 256, 256, kSchedGroupM,
      {{launch16<0, 256, 256, 2, 4, false, false, false>, launch_sched<0>},
       {launch16<1, 256, 256, 2, 4, false, false, false>, launch_sched<1>}}},
+    // four waves, each the whole 64 x 64 tile over every fourth phase;
+    // misaligned operands: the element-wise 64 x 64 kernel
+    {"mixed64x64_bk32_w4_ksplit", 64, 64, 8,
+     {{launch16<0, 64, 64, 1, 2, false, false, false>, launch_ksplit16_cfg<0>},
+      {launch16<1, 64, 64, 1, 2, false, false, false>, launch_ksplit16_cfg<1>}}},
 };
 #undef MIXED
 constexpr int kNumMixed = (int)(sizeof(kMixed) / sizeof(kMixed[0]));
+constexpr int kKsplitConfig = 9;          // mixed64x64_bk32_w4_ksplit
 
 // op kernels, chosen by tile, op pair and load path
 template <int FMT, int BM, int BN, int WM, int WN, bool KCA, bool KCB, bool VEC>
@@ -1190,6 +1145,8 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
     const bool vec = ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 3) == 0 &&
                      (p.lda % 2) == 0 && (p.ldb % 2) == 0;
     const int64_t t256 = (int64_t)ceil_div(p.M, 256) * ceil_div(p.N, 256);
+    if (mixed_pick_config(p.M, p.N, p.K) == kKsplitConfig && ksplit16_fits(p, op_a, op_b))
+        return launch_ksplit16(p, s, format, op_a, op_b);
     const bool big = t256 >= 128;
     const int tile = big ? 256 : 128;
     const int tiles_m = ceil_div(p.M, tile), tiles_n = ceil_div(p.N, tile);
@@ -1219,14 +1176,18 @@ const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed
 
 // 256 x 256 tiles on the scheduled kernel (which itself runs configuration
 // 6 on problems it does not take) from 128 of them, half the CUs: measured,
-// 144 such tiles (3072^3) still beat 576 of 128 x 128 by 40 %.  Else 128 x
-// 128 tiles with both factors copied straight into LDS from 128 of them
-// (64 for K of at least 2048), else 64 x 64 tiles (measured: 1536^3 346
-// against 276 TFLOP/s, 1024^3 141 against 156).
+// 144 such tiles (3072^3) still beat 576 of 128 x 128 by 40 %.  Else, below
+// 128 tiles of 128 x 128 and with K a multiple of 8, 64 x 64 tiles whose
+// four waves split the phases (mfma16_ksplit.hip; measured bf16: 1024^2 x
+// 4096 479 against 186 TFLOP/s on the 128 x 128 tiles, 1000^3 234 against
+// 53, 1024^3 297 against 160; 1536^3, with 144 tiles of 128 x 128, 321
+// against 339).  Else 128 x 128 tiles with both factors copied straight into
+// LDS from 128 of them (64 for K of at least 2048), else 64 x 64 tiles.
 int mixed_pick_config(int M, int N, int K) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
     if (t256 >= 128) return 8;
+    if (t128 < 128 && K % 8 == 0 && K > 0) return kKsplitConfig;
     if (t128 >= 128 || (t128 >= 64 && K >= 2048)) return 7;
     return 3;
 }

@@ -1,0 +1,81 @@
+// mfma16_common.h -- device helpers shared by the 16-bit (bfloat16 /
+// binary16) kernels: vector types, LDS reads (plain and transposed), waits
+// tied to the registers they complete, and compile-time unrolling (not part
+// of the public interface).
+#pragma once
+
+#include "launch.h"
+
+#include <type_traits>
+#include <utility>
+
+namespace gemmf32 {
+
+namespace {
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+// Four 16-bit values through ds_read_b64_tr_b16.  Within each group of 16
+// lanes, value e of lane i is element i % 4 of the 8 bytes addressed by lane
+// 4 e + i / 4.  So if lane j of a group addresses row kb + j / 4, columns
+// nb + 4 (j % 4) .. +3 of a row-major tile, lane i receives the column
+// nb + i, rows kb .. kb + 3: four consecutive k of one n.
+//
+// Issued as inline assembly: the compiler would otherwise wait for every
+// outstanding global -> LDS copy before the first such read (it cannot tell
+// that the copies fill the other stage).  The "memory" clobber keeps the
+// reads in order with the barriers; wait_tied() below is their wait.
+__device__ __forceinline__ u32x2 read_tr16(uint32_t lds_byte_addr) {
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(lds_byte_addr) : "memory");
+    return v;
+}
+
+// Waits for all outstanding LDS reads; the fragments pass through the wait
+// as operands, so no use of them can be scheduled before it.
+template <int N>
+__device__ __forceinline__ void wait_tied(u32x4 (&b)[N]) {
+    static_assert(N == 1 || N == 2 || N == 4, "fragment count");
+    if constexpr (N == 1) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]) : : "memory");
+    if constexpr (N == 2) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]) : : "memory");
+    if constexpr (N == 4)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : : "memory");
+}
+
+// Byte address inside LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes of LDS at a byte address.
+__device__ __forceinline__ u32x4 lds_read128(uint32_t lds_byte_addr) {
+    typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+    return *(lds_u32x4*)(uintptr_t)lds_byte_addr;
+}
+
+// read_tr16 with a compile-time byte offset in the instruction.
+__device__ __forceinline__ u32x2 read_tr16_off(uint32_t lds_byte_addr, int off) {
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_byte_addr), "i"(off) : "memory");
+    return v;
+}
+
+template <typename F, int... Q>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Q...>) {
+    (f(std::integral_constant<int, Q>{}), ...);
+}
+// f(std::integral_constant<int, q>{}) for q = 0 .. N - 1, in order: every
+// index is a compile-time constant, so arrays indexed by it stay in registers
+// (a loop under #pragma unroll is unrolled only after the pass that would
+// have kept them there).
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+    unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+}  // namespace
+
+}  // namespace gemmf32

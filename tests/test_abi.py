@@ -314,9 +314,10 @@ def test_default_variant_choices(binding):
     Last, at most 512 output tiles of 16 x 16 take the 16 x 16 small-tile
     kernel on 8 waves, at most 1024 the 32 x 32 one on 4 waves, whatever K.
     For the 16-bit product the
-    scheduled kernel from 128 tiles of 256 x 256, 128 x 128 direct copies
-    from 128 tiles of those (64 for K >= 2048), else 64 x 64 tiles.  Invalid
-    sizes give -1."""
+    scheduled kernel from 128 tiles of 256 x 256, else the k-split 64 x 64
+    tiles below 128 tiles of 128 x 128 (K a multiple of 8), else 128 x 128
+    direct copies from 128 tiles of those (64 for K >= 2048), else 64 x 64
+    tiles.  Invalid sizes give -1."""
     f32 = {
         (8192, 8192, 8192): "mfma256x256_bk32_w2x2_sched",
         (4096, 4096, 4096): "mfma256x256_bk32_w2x2_sched",
@@ -370,9 +371,12 @@ def test_default_variant_choices(binding):
         (2560, 2560, 2560): "mixed128x128_bk64_w2x2_directAB",    # 100 tiles of 256, 400 of 128
         (2048, 2048, 2048): "mixed128x128_bk64_w2x2_directAB",
         (1536, 1536, 1536): "mixed128x128_bk64_w2x2_directAB",    # 144 tiles of 128
-        (1024, 1024, 4096): "mixed128x128_bk64_w2x2_directAB",    # 64 tiles of 128, K >= 2048
-        (1024, 1024, 1024): "mixed64x64_bk64_w1x2",
-        (1000, 1000, 1000): "mixed64x64_bk64_w1x2",
+        (1024, 1024, 4096): "mixed64x64_bk32_w4_ksplit",          # 64 tiles of 128: k-split
+        (1024, 1024, 1024): "mixed64x64_bk32_w4_ksplit",
+        (1000, 1000, 1000): "mixed64x64_bk32_w4_ksplit",
+        (512, 512, 8192): "mixed64x64_bk32_w4_ksplit",
+        (1024, 1024, 4092): "mixed128x128_bk64_w2x2_directAB",    # K % 8 = 4: 64 tiles of 128, K >= 2048
+        (1000, 1000, 1001): "mixed64x64_bk64_w1x2",
     }
     for (M, N, K), name in mixed.items():
         assert binding.gemm_mixed_variant_name(binding.gemm_mixed_default_variant(M, N, K)) == name, (M, N, K)

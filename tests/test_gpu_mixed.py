@@ -152,19 +152,34 @@ def test_mixed_scheduled_kernel_padded_and_fallback():
 
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_mixed_load_paths_agree_bitwise(fmt):
-    """The vector and element-wise load paths sum in the same order: the
-    same data at an aligned and at a 2-byte-offset address give the same bits."""
+    """The vector and element-wise load paths of one tile configuration sum
+    in the same order: the same data at an aligned and at a 2-byte-offset
+    address give the same bits, for the configurations the default path
+    picks besides the k-split one (64 x 64, 128 x 128 with direct copies, the
+    scheduled 256 x 256).  The k-split configuration's 16-byte copies need
+    4-byte alignment; a misaligned call given to it runs the element-wise
+    64 x 64 kernel, whose order differs: the default is checked against the
+    oracle at both addresses instead."""
+    names = ("mixed64x64_bk64_w1x2", "mixed128x128_bk64_w2x2_directAB", "mixed256x256_bk64_w4_sched")
+    configs = [v for v in range(binding.gemm_mixed_num_variants()) if binding.gemm_mixed_variant_name(v) in names]
+    assert len(configs) == 3
     for (M, N, K) in ((520, 530, 200), (1000, 1000, 1000), (300, 2100, 776)):
         gen = np.random.default_rng([M, N, K, 7, len(fmt)])
         A32 = inputs.random_matrix(gen, M, K, "uniform")
         B32 = inputs.random_matrix(gen, K, N, "uniform")
-        out = []
+        probs = []
         for offset in (0, 1):
             A = inputs.padded16(inputs.to16(A32, fmt), K, offset, fmt)
             B = inputs.padded16(inputs.to16(B32, fmt), N, offset, fmt)
-            say(f"mixed {fmt} load paths {M}x{N}x{K} offset={offset}")
-            out.append(MixedProblem(fmt, A, B, N).run().view.copy())
-        assert np.array_equal(out[0].view(np.uint32), out[1].view(np.uint32)), (fmt, M, N, K)
+            probs.append(MixedProblem(fmt, A, B, N))
+        for v in configs:
+            say(f"mixed {fmt} load paths {M}x{N}x{K} variant={v}")
+            out = [pr.run(variant=v).view.copy() for pr in probs]
+            assert np.array_equal(out[0].view(np.uint32), out[1].view(np.uint32)), (fmt, M, N, K, v)
+        say(f"mixed {fmt} load paths {M}x{N}x{K} default")
+        ref, S = oracle.gemm16(fmt, probs[0].A.view, probs[0].B.view, threads=8)
+        for pr in probs:
+            check_close(pr.run().view, ref, S, f"{fmt} {M}x{N}x{K} default, offset {pr.A.offset}")
 
 
 @pytest.mark.parametrize("fmt", FORMATS)

@@ -556,3 +556,122 @@ def test_sched_mixed_copies_never_depend_on_the_scalar_offset(kc, shape):
                         wants_zero = k >= K or (kc and mn >= ext)
                         in_matrix = (k + 7 < K and mn < ext) if kc else (k < K and mn + 7 < ext)
                         _check_copy(voff, soff, nrec, 16, wants_zero, in_matrix, what)
+
+
+def ks16_swz(kc, r):
+    return ((r >> 2) & 3) if kc else ((((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2))
+
+
+def ks16_copy(kc, j, lane):
+    """(stored row, logical chunk) that lane `lane` of copy j (0..3) of the
+    16-bit k-split kernel's tile brings: KC rows of 32 k (4 chunks of 8),
+    16 rows per 1 KB copy; MC rows of 64 values (8 chunks), 8 rows per copy."""
+    cpr = 4 if kc else 8
+    row = (64 // cpr) * j + lane // cpr
+    return row, (lane % cpr) ^ ks16_swz(kc, row)
+
+
+def ks16_read_base(kc, f, lane):
+    j, g = lane & 15, lane >> 4
+    if kc:
+        return 64 * j + 16 * (g ^ ks16_swz(True, j))
+    q, jj = j >> 2, j & 3
+    r0 = 8 * g + q
+    return 128 * r0 + 16 * ((2 * f + (jj >> 1)) ^ ks16_swz(False, r0)) + 8 * (jj & 1)
+
+
+def ks16_read_imm(kc, f, i):
+    return 1024 * f if kc else 512 * i
+
+
+@pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
+def test_ksplit16_kernel_layout(kc):
+    """The 16-bit k-split kernel's tile (64 mn x 32 k per stage), restated:
+    the four 1 KB copies fill the stage exactly once; every lane's fragment
+    reads (per-lane base + instruction offset, 128-bit for a k-contiguous
+    tile, two ds_read_b64_tr_b16 for an mn-contiguous one) deliver the
+    operands v_mfma_f32_16x16x32 needs -- for block f, lane l supplies
+    op(X)[16 f + l % 16][8 (l / 16) + e], e = 0..7 -- and the reads are free
+    of bank conflicts on 64 banks (128-bit: 16 lanes per cycle; 64-bit: 32)."""
+    where = {}                                   # LDS element -> (mn, k)
+    for j in range(4):
+        for lane in range(64):
+            row, c = ks16_copy(kc, j, lane)
+            dst = 512 * j + 8 * lane
+            for e in range(8):
+                where[dst + e] = (row, 8 * c + e) if kc else (8 * c + e, row)
+    assert sorted(where) == list(range(64 * 32))
+    for f in range(4):
+        if kc:
+            words = []
+            for lane in range(64):
+                addr = ks16_read_base(True, f, lane) + ks16_read_imm(True, f, 0)
+                assert addr % 16 == 0 and 0 <= addr < 4096 and ks16_read_imm(True, f, 0) < 1 << 16
+                got = [where[addr // 2 + e] for e in range(8)]
+                assert got == [(16 * f + lane % 16, 8 * (lane // 16) + e) for e in range(8)], (f, lane)
+                words.append(addr // 4)
+            assert degree(words, 4, 64, 16) == 1
+        else:
+            vals = {lane: [] for lane in range(64)}
+            for i in range(2):
+                words = []
+                addrs = [ks16_read_base(False, f, lane) + ks16_read_imm(False, f, i) for lane in range(64)]
+                for lane in range(64):
+                    assert addrs[lane] % 8 == 0 and 0 <= addrs[lane] < 4096
+                    words.append(addrs[lane] // 4)
+                # transposed read: in each group of 16 lanes, value e of lane i is
+                # element i % 4 of the 8 bytes that lane 4 e + i // 4 addresses
+                for lane in range(64):
+                    grp, i16 = lane - lane % 16, lane % 16
+                    for e in range(4):
+                        src = addrs[grp + 4 * e + i16 // 4]
+                        vals[lane].append(where[src // 2 + i16 % 4])
+                assert degree(words, 2, 64, 32) == 1
+            for lane in range(64):
+                assert vals[lane] == [(16 * f + lane % 16, 8 * (lane // 16) + e) for e in range(8)], (f, lane)
+
+
+@pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
+@pytest.mark.parametrize("shape", [(1024, 4096, 1024), (100, 1000, 104), (64, 8, 64), (1000, 4104, 1002)])
+def test_ksplit16_copies_never_depend_on_the_scalar_offset(kc, shape):
+    """16-bit k-split kernel: phases of 32 k aligned to the end of K (a
+    multiple of 8), wave w taking phases w, w + 4, ...; each wave's first
+    and last phases take the phase in their per-lane offsets with a scalar
+    offset of 0 (lanes below k = 0 past the end), the others in the scalar
+    offset; chunks of an mn-contiguous factor wholly past its last column
+    are past the end in every phase.  Only a chunk of the mn-contiguous
+    factor's last row across its last column may straddle the descriptor's
+    end, by its per-lane offset alone and by whole dwords (the width is
+    even)."""
+    ext, K, ld_mn = shape
+    assert K % 8 == 0 and ext % 2 == 0
+    rows, cols = (ext, K) if kc else (K, ext)
+    ld = (K + 8) if kc else max(ld_mn, ext)
+    nrec = 2 * ((rows - 1) * ld + cols)
+    P = -(-K // 32)
+    kbase = K - 32 * P
+    for mn0 in sorted({0, (ext - 1) // 64 * 64}):
+        for j in range(4):
+            for lane in range(64):
+                row, c = ks16_copy(kc, j, lane)
+                kl, mn = (8 * c, mn0 + row) if kc else (row, mn0 + 8 * c)
+                doff = 2 * (mn * ld + kl) if kc else 2 * (kl * ld + mn)
+                if not kc and mn >= ext:
+                    doff = PAST_END
+                for g in range(P):
+                    k0 = kbase + 32 * g
+                    k = k0 + kl
+                    pb = 2 * k0 if kc else 2 * k0 * ld
+                    last = g + 4 >= P  # the wave's last phase
+                    if g < 4 or last:  # each wave's first and last phases fold the phase in
+                        voff, soff = (doff + pb if k >= 0 and doff != PAST_END else PAST_END), 0
+                    else:
+                        voff, soff = doff, pb
+                    what = (kc, shape, mn0, j, lane, g)
+                    assert k + (7 if kc else 0) < K, what
+                    if not kc and k >= 0 and mn < ext < mn + 8 and voff < nrec < voff + soff + 16:
+                        assert k == K - 1 and soff == 0 and (nrec - voff) % 4 == 0, what
+                        continue
+                    wants_zero = k < 0 or mn >= ext
+                    in_matrix = k >= 0 and (mn < ext if kc else mn + 7 < ext)
+                    _check_copy(voff, soff, nrec, 16, wants_zero, in_matrix, what)
