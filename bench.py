@@ -40,6 +40,9 @@ Extra modes (used for counter runs under rocprofv3):
                         JSON line per run with the median and best launch time
                         (HIP events around every launch), then the oracle's
                         time on this host (see bench_all_workloads)
+    --lds-probe         one wave reading LDS at chosen offsets, one launch per
+                        case (which lanes one read cycle serves, from the
+                        bank-conflict counter of each dispatch)
     --valu-probe        the issue rate of non-packed v_fmac_f32 on the vector
                         ALU in three operand forms, with the measured clock
                         (the register-blocked rung's ceiling)
@@ -474,7 +477,8 @@ SWEEP_CANDIDATES = ["mfma64x64_bk32_w2x2_k4", "mfma64x64_bk16_w2x2_k4", "mfma64x
 
 
 MIXED_SWEEP_CANDIDATES = ["mixed64x64_bk64_w1x2", "mixed64x64_bk32_w4_ksplit", "mixed128x128_bk64_w2x2_directAB",
-                          "mixed256x256_bk64_w2x4_directAB", "mixed256x256_bk64_w4_sched"]
+                          "mixed256x256_bk64_w2x4_directAB", "mixed256x256_bk64_w4_sched",
+                          "mixed256x256_bk64_w4_wide"]
 
 
 def bench_shape_sweep(args) -> int:
@@ -565,6 +569,57 @@ def bench_valu_probe(args) -> int:
                                   "clock_mhz": round(mhz), "wave64_fma_per_simd_per_clock": round(per_simd_clk, 4),
                                   "tflops_at_2400mhz_same_rate": round(per_simd_clk * 64 * 2 * cus * 4 * 2.4e9 / 1e12, 1)}),
                       flush=True)
+    return 0
+
+
+def lds_probe_cases():
+    """(name, form, 64 byte offsets) of the LDS read probe, in launch order.
+    Pairs: two groups of lanes on the same banks at different addresses,
+    every other lane on one broadcast address in other banks; the pair
+    conflicts if and only if one read cycle serves both groups.
+      128-bit reads (form 2): every pair of 4-lane quads (lanes 4q .. 4q + 3);
+      64-bit reads, plain (form 1) and transposed (form 3): every pair of
+      8-lane groups.
+    Then the k-contiguous tile reads of the 16 x 16 x 32 kernels (lane l:
+    row l % 16, 16-byte chunk l / 16) in three layouts."""
+    cases = [("b128 all lanes on one address", 2, [240] * 64),
+             ("b128 1 KB contiguous", 2, [16 * l for l in range(64)])]
+    for qa in range(16):
+        for qb in range(qa + 1, 16):
+            offs = [240] * 64
+            for i in range(4):
+                offs[4 * qa + i] = 1024 + 16 * i
+                offs[4 * qb + i] = 2048 + 16 * i
+            cases.append((f"b128 quads {qa} {qb}", 2, offs))
+    for form, what in ((1, "b64"), (3, "b64_tr_b16")):
+        for ga in range(8):
+            for gb in range(ga + 1, 8):
+                offs = [248] * 64
+                for i in range(8):
+                    offs[8 * ga + i] = 1024 + 8 * i
+                    offs[8 * gb + i] = 2048 + 8 * i
+                cases.append((f"{what} groups {ga} {gb}", form, offs))
+    rows = lambda pitch, swz: [pitch * (l % 16) + 16 * ((l // 16) ^ swz(l % 16)) for l in range(64)]
+    cases.append(("b128 rows of 64 bytes, chunk c ^ ((r / 4) mod 4)", 2, rows(64, lambda r: (r >> 2) & 3)))
+    cases.append(("b128 rows of 64 bytes, chunk c ^ 2 ((r / 8) mod 2)", 2, rows(64, lambda r: 2 * ((r >> 3) & 1))))
+    cases.append(("b128 rows of 128 bytes, chunk c ^ ((r / 2) mod 8)", 2, rows(128, lambda r: (r >> 1) & 7)))
+    return cases
+
+
+def bench_lds_probe(args) -> int:
+    """Launches the LDS read probe once per case (64 reads per lane each),
+    printing the cases in launch order; the bank-conflict counts come from a
+    profiler run around this command (SQ_LDS_BANK_CONFLICT per dispatch)."""
+    import torch
+
+    from shared_memory_tiled_amd import binding
+
+    out = torch.zeros(64, dtype=torch.int32, device="cuda")
+    for i, (name, form, offs) in enumerate(lds_probe_cases()):
+        t = torch.tensor(offs, dtype=torch.int32, device="cuda")
+        binding.gemm_f32_lds_probe(form, t, 64, out)
+        torch.cuda.synchronize()
+        print(json.dumps({"lds_probe_dispatch": i, "form": form, "case": name}), flush=True)
     return 0
 
 
@@ -688,6 +743,8 @@ def main(argv=None) -> int:
     ap.add_argument("--format", default="bf16", choices=["bf16", "f16"], help="16-bit format of --row mixed")
     ap.add_argument("--n", type=int, default=2 ** 28, help="values summed by --row reduce")
     ap.add_argument("--all-workloads", action="store_true")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="launch the LDS read probe over its lane-grouping cases (for a counter run)")
     ap.add_argument("--valu-probe", action="store_true",
                     help="issue rate of non-packed v_fmac_f32 (the register-blocked rung's instruction)")
     ap.add_argument("--shape-sweep", action="store_true")
@@ -704,7 +761,8 @@ def main(argv=None) -> int:
                          "launch reads a matrix the last-level cache no longer holds (1: the same "
                          "matrix every launch)")
     args = ap.parse_args(argv)
-    headline = not (args.all_workloads or args.shape_sweep or args.ladder or args.valu_probe or args.row != "gemm")
+    headline = not (args.all_workloads or args.shape_sweep or args.ladder or args.valu_probe or args.lds_probe
+                    or args.row != "gemm")
     if args.settle_s is not None:
         globals()["SETTLE_S"] = max(0.0, args.settle_s)
     elif headline:
@@ -738,6 +796,8 @@ def main(argv=None) -> int:
 
     if args.valu_probe:
         return bench_valu_probe(args)
+    if args.lds_probe:
+        return bench_lds_probe(args)
     if args.all_workloads:
         return bench_all_workloads(args)
     if args.shape_sweep:

@@ -204,6 +204,19 @@ int gemm_f32_default_variant(int64_t M, int64_t N, int64_t K);
 int gemm_f32_valu_probe(int form, int64_t blocks, int iters, float *out, uint64_t *stamps,
                         void *stream);
 
+/* Measurement helper, this library's own (not part of the product): one
+ * wave (a single workgroup of 64 threads) reads LDS, lane l at byte offset
+ * offsets[l] of a 64 KB array (masked into it and aligned down to the read's
+ * width), `iters` times; with a profiler's LDS bank-conflict counter per
+ * dispatch, a chosen set of offsets shows which lanes one read cycle serves.
+ *   form     0 ds_read_b32, 1 ds_read_b64, 2 ds_read_b128,
+ *            3 ds_read_b64_tr_b16
+ *   offsets  device pointer to 64 int32 byte offsets (4-byte aligned)
+ *   out      device pointer to 64 uint32, overwritten (keeps the reads live)
+ * Enqueue-only on `stream`; statuses as for gemm_f32 (an unknown form gives
+ * GEMM_F32_ERR_INVALID_VARIANT, iters < 0 GEMM_F32_ERR_INVALID_DIM). */
+int gemm_f32_lds_probe(int form, const int32_t *offsets, int iters, uint32_t *out, void *stream);
+
 /* Static, NUL-terminated description of a status code (the by-name report
  * of the chapter 2 error check cited with the codes above); "unknown status"
  * for any other number. */

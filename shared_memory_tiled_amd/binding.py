@@ -88,6 +88,8 @@ def load_library():
         lib.reduce_sum_f32_variant.restype = ctypes.c_int
         lib.gemm_f32_valu_probe.argtypes = [ctypes.c_int, _i64, ctypes.c_int, _vp, _vp, _vp]
         lib.gemm_f32_valu_probe.restype = ctypes.c_int
+        lib.gemm_f32_lds_probe.argtypes = [ctypes.c_int, _vp, ctypes.c_int, _vp, _vp]
+        lib.gemm_f32_lds_probe.restype = ctypes.c_int
         lib.reduce_sum_f32_variant_noalloc.argtypes = [ctypes.c_int, _i64, _vp, _vp, _vp]
         lib.reduce_sum_f32_variant_noalloc.restype = ctypes.c_int
         lib.reduce_sum_f32_num_variants.argtypes = []
@@ -262,6 +264,13 @@ def gemm_f32_valu_probe(form, blocks, iters, out, stamps, stream=None) -> None:
     """The vector-ALU FMA loop of the library's measurement helper."""
     lib = load_library()
     _check(lib.gemm_f32_valu_probe(int(form), int(blocks), int(iters), _addr(out), _addr(stamps), _stream(stream)))
+
+
+def gemm_f32_lds_probe(form, offsets, iters, out, stream=None) -> None:
+    """The LDS read probe of the library's measurement helper (offsets: 64
+    int32 on the device; out: 64 uint32 or int32 on the device)."""
+    lib = load_library()
+    _check(lib.gemm_f32_lds_probe(int(form), _addr(offsets), int(iters), _addr(out), _stream(stream)))
 
 
 REDUCE_DEFAULT = 4

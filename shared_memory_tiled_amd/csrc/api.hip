@@ -199,6 +199,18 @@ extern "C" int gemm_f32_valu_probe(int form, int64_t blocks, int iters, float* o
     return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
 }
 
+// A measurement helper: the LDS read probe of probe.hip.
+extern "C" int gemm_f32_lds_probe(int form, const int32_t* offsets, int iters, uint32_t* out, void* stream) {
+    if (form < 0 || form > 3) return GEMM_F32_ERR_INVALID_VARIANT;
+    if (iters < 0) return GEMM_F32_ERR_INVALID_DIM;
+    if (offsets == nullptr || out == nullptr) return GEMM_F32_ERR_NULL_PTR;
+    if (misaligned(offsets) || misaligned(out)) return GEMM_F32_ERR_MISALIGNED;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_F32_ERR_DEVICE;
+    const hipError_t e = launch_lds_probe(form, offsets, iters, out, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
+}
+
 // ---------------------------------------------------------------- transpose
 
 namespace {

@@ -44,6 +44,10 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
 // stored transposed).
 bool ksplit16_fits(const Gemm16Args& p, int op_a, int op_b);
 hipError_t launch_ksplit16(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b);
+// The scheduled 256 x 256 kernel on the 16 x 16 x 32 instruction
+// (mfma16_wide.hip); it takes the problems the 32 x 32 x 16 scheduled kernel
+// takes (the caller checks), with tile-row groups of group_m.
+hipError_t launch_wide16(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m);
 
 // Sum reduction (reduce.hip): *out = sum of x[0 .. n-1].
 hipError_t launch_reduce(int variant, int64_t n, const float* x, float* out, float* ws, hipStream_t s);
@@ -81,6 +85,10 @@ hipError_t launch_small_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b
 // vector ALU in operand form `form` (0 scalar-register operand, 1 vector
 // registers, 2 8 x 8 outer product), `blocks` blocks of 256 threads.
 hipError_t launch_valu_probe(int form, int blocks, int iters, float* out, uint64_t* stamps, hipStream_t s);
+// Measurement helper (probe.hip): one wave reading LDS at 64 given byte
+// offsets, `iters` times (form 0 ds_read_b32, 1 ds_read_b64, 2
+// ds_read_b128, 3 ds_read_b64_tr_b16).
+hipError_t launch_lds_probe(int form, const int* offs, int iters, unsigned* out, hipStream_t s);
 int regblock_num_configs();
 const char* regblock_config_name(int config);
 

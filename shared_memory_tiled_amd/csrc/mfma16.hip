@@ -490,7 +490,8 @@ void gemm16_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
 // Each factor's tile is one of two kinds (see gemm16_op_kernel):
 //   KC (k-contiguous: A as stored, B stored transposed): 256 rows of 64 k,
 //      chunk c of row r at c ^ ((r / 2) mod 8) (the 16 rows one read cycle
-//      touches, two per 64-bank sweep, on 16 different 4-bank groups; for
+//      touches -- four 4-lane quads of a half-wave -- on 16 different 4-bank
+//      groups; for
 //      the rows 32 f + l % 32 a lane reads, the permutation depends on l
 //      only, so fragment f is a compile-time offset); a fragment is one
 //      128-bit read; a copy fills 8 rows;
@@ -1088,6 +1089,17 @@ hipError_t launch_ksplit16_cfg(const Gemm16Args& p, hipStream_t s, int tiles_m, 
     return launch_ksplit16(p, s, FMT, 0, 0);
 }
 
+// Configuration 10 (the scheduled kernel on v_mfma_f32_16x16x32,
+// mfma16_wide.hip) where it takes the problem; else the 8-wave kernel, as
+// for configuration 8 (its bits differ: another instruction).
+template <int FMT>
+hipError_t launch_wide_cfg(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int /*group_m*/,
+                           unsigned blocks) {
+    if (!sched_fits(p, 0, 0))
+        return launch16<FMT, 256, 256, 2, 4, true, true, true>(p, s, tiles_m, tiles_n, kDirectGroupM, blocks);
+    return launch_wide16(p, s, FMT, 0, 0, kSchedGroupM);
+}
+
 const MixedConfig kMixed[] = {
     {"mixed256x256_bk64_w2x4_directA", 256, 256, 8, MIXED(256, 256, 2, 4, true, false)},
     {"mixed256x256_bk64_w2x4", 256, 256, 8, MIXED(256, 256, 2, 4, false, false)},
@@ -1106,10 +1118,16 @@ const MixedConfig kMixed[] = {
     {"mixed64x64_bk32_w4_ksplit", 64, 64, 8,
      {{launch16<0, 64, 64, 1, 2, false, false, false>, launch_ksplit16_cfg<0>},
       {launch16<1, 64, 64, 1, 2, false, false, false>, launch_ksplit16_cfg<1>}}},
+    // the scheduled kernel's tiles on v_mfma_f32_16x16x32; misaligned
+    // operands: the element-wise 8-wave kernel, as for 6
+    {"mixed256x256_bk64_w4_wide", 256, 256, kSchedGroupM,
+     {{launch16<0, 256, 256, 2, 4, false, false, false>, launch_wide_cfg<0>},
+      {launch16<1, 256, 256, 2, 4, false, false, false>, launch_wide_cfg<1>}}},
 };
 #undef MIXED
 constexpr int kNumMixed = (int)(sizeof(kMixed) / sizeof(kMixed[0]));
 constexpr int kKsplitConfig = 9;          // mixed64x64_bk32_w4_ksplit
+constexpr int kWideConfig = 10;           // mixed256x256_bk64_w4_wide
 
 // op kernels, chosen by tile, op pair and load path
 template <int FMT, int BM, int BN, int WM, int WN, bool KCA, bool KCB, bool VEC>
@@ -1137,8 +1155,9 @@ Launch16 op_launcher(int op_a, int op_b, bool vec) {
 }  // namespace
 
 // op(A) x op(B): 256 x 256 tiles once there are 128 of them (the scheduled
-// kernel where it fits, else eight waves of gemm16_op_kernel), else 128 x 128
-// tiles of four waves.  A and B are the stored matrices; vector loads (and
+// kernel on v_mfma_f32_16x16x32, mfma16_wide.hip, where it fits, else eight
+// waves of gemm16_op_kernel), else the k-split kernel or 128 x 128 tiles of
+// four waves, as gemm_mixed picks.  A and B are the stored matrices; vector loads (and
 // the direct copies) need 4-byte aligned bases and even leading dimensions,
 // as for gemm_mixed.
 hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b) {
@@ -1152,19 +1171,7 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
     const int tiles_m = ceil_div(p.M, tile), tiles_n = ceil_div(p.N, tile);
     const int64_t blocks = (int64_t)tiles_m * tiles_n;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    if (big && sched_fits(p, op_a, op_b)) {
-        // A k-contiguous unless stored transposed; B the reverse
-        const int key = 2 * op_a + op_b;
-        Launch16 fn;
-        if (format) {
-            fn = key == 0 ? launch_sched_kernel<1, true, false> : key == 1 ? launch_sched_kernel<1, true, true>
-               : key == 2 ? launch_sched_kernel<1, false, false> : launch_sched_kernel<1, false, true>;
-        } else {
-            fn = key == 0 ? launch_sched_kernel<0, true, false> : key == 1 ? launch_sched_kernel<0, true, true>
-               : key == 2 ? launch_sched_kernel<0, false, false> : launch_sched_kernel<0, false, true>;
-        }
-        return fn(p, s, tiles_m, tiles_n, kSchedGroupM, (unsigned)blocks);
-    }
+    if (big && sched_fits(p, op_a, op_b)) return launch_wide16(p, s, format, op_a, op_b, kSchedGroupM);
     Launch16 fn;
     if (big) fn = format ? op_launcher<1, 256, 256, 2, 4>(op_a, op_b, vec) : op_launcher<0, 256, 256, 2, 4>(op_a, op_b, vec);
     else fn = format ? op_launcher<1, 128, 128, 2, 2>(op_a, op_b, vec) : op_launcher<0, 128, 128, 2, 2>(op_a, op_b, vec);
@@ -1174,9 +1181,12 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
 int mixed_num_configs() { return kNumMixed; }
 const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed[c].name : nullptr; }
 
-// 256 x 256 tiles on the scheduled kernel (which itself runs configuration
-// 6 on problems it does not take) from 128 of them, half the CUs: measured,
-// 144 such tiles (3072^3) still beat 576 of 128 x 128 by 40 %.  Else, below
+// 256 x 256 tiles on the scheduled kernel of the 16 x 16 x 32 instruction
+// (configuration 10, which itself runs configuration 6 on problems it does
+// not take) from 128 of them, half the CUs: measured, 144 such tiles
+// (3072^3) still beat 576 of 128 x 128 by 40 %; at 8192^3 it runs bf16 at
+// 1395 TFLOP/s against 1332 for the 32 x 32 x 16 form (configuration 8) on
+// the same box, f16 at 1340 against 1250.  Else, below
 // 128 tiles of 128 x 128 and with K a multiple of 8, 64 x 64 tiles whose
 // four waves split the phases (mfma16_ksplit.hip; measured bf16: 1024^2 x
 // 4096 479 against 186 TFLOP/s on the 128 x 128 tiles, 1000^3 234 against
@@ -1186,7 +1196,7 @@ const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed
 int mixed_pick_config(int M, int N, int K) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
-    if (t256 >= 128) return 8;
+    if (t256 >= 128) return kWideConfig;
     if (t128 < 128 && K % 8 == 0 && K > 0) return kKsplitConfig;
     if (t128 >= 128 || (t128 >= 64 && K >= 2048)) return 7;
     return 3;

@@ -38,11 +38,26 @@ __device__ __forceinline__ u32x2 read_tr16(uint32_t lds_byte_addr) {
 // as operands, so no use of them can be scheduled before it.
 template <int N>
 __device__ __forceinline__ void wait_tied(u32x4 (&b)[N]) {
-    static_assert(N == 1 || N == 2 || N == 4, "fragment count");
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8, "fragment count");
     if constexpr (N == 1) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]) : : "memory");
     if constexpr (N == 2) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]) : : "memory");
     if constexpr (N == 4)
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : : "memory");
+    if constexpr (N == 8)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]), "+v"(b[5]), "+v"(b[6]), "+v"(b[7])
+                     :
+                     : "memory");
+}
+
+// The same for fragments held as 64-bit halves (two transposed reads each).
+__device__ __forceinline__ void wait_tied(u32x2 (&h)[8][2]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(h[0][0]), "+v"(h[0][1]), "+v"(h[1][0]), "+v"(h[1][1]), "+v"(h[2][0]), "+v"(h[2][1]),
+                   "+v"(h[3][0]), "+v"(h[3][1]), "+v"(h[4][0]), "+v"(h[4][1]), "+v"(h[5][0]), "+v"(h[5][1]),
+                   "+v"(h[6][0]), "+v"(h[6][1]), "+v"(h[7][0]), "+v"(h[7][1])
+                 :
+                 : "memory");
 }
 
 // Byte address inside LDS of a pointer into a __shared__ array.
@@ -61,6 +76,19 @@ __device__ __forceinline__ u32x2 read_tr16_off(uint32_t lds_byte_addr, int off) 
     u32x2 v;
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_byte_addr), "i"(off) : "memory");
     return v;
+}
+
+// D = A B + C on one 16 x 16 x 32 block (format 0 bfloat16, 1 binary16):
+// lane l supplies A[l % 16][8 (l / 16) .. + 7] and B[8 (l / 16) .. + 7][l %
+// 16]; accumulator register r holds D[4 (l / 16) + r][l % 16].
+template <int FMT>
+__device__ __forceinline__ floatx4 mfma16x16(u32x4 a, u32x4 b, floatx4 c) {
+    if constexpr (FMT == 0)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                       0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, b), c,
+                                                      0, 0, 0);
 }
 
 template <typename F, int... Q>

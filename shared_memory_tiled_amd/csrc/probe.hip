@@ -1,7 +1,8 @@
-// probe.hip -- a measurement helper, not part of the product: loops of
-// non-packed binary32 fused multiply-adds on the vector ALU, timed by the
-// caller, that give the issue rate of the register-blocked rung's
-// instruction (v_fmac_f32) on gfx950.  Three operand forms:
+// probe.hip -- measurement helpers, not part of the product.
+//
+// 1. Loops of non-packed binary32 fused multiply-adds on the vector ALU,
+// timed by the caller, that give the issue rate of the register-blocked
+// rung's instruction (v_fmac_f32) on gfx950.  Three operand forms:
 //   0  one operand in a scalar register (v_fmac_f32 acc, v_x, s_b)
 //   1  all operands in vector registers (v_fmac_f32 acc, v_x, v_y), 16
 //      independent accumulators per lane
@@ -67,7 +68,57 @@ __global__ __launch_bounds__(256) void valu_probe_kernel(float* out, uint64_t* t
     stamp(t, 1);
 }
 
+// 2. One wave reading LDS: lane l reads `width` bytes at byte offset
+// offs[l] (masked into a 64 KB array and aligned to the width) `iters`
+// times, each read waited for in the same instruction sequence; with the
+// LDS bank-conflict counter per dispatch, a set of offsets tells which lanes
+// one read cycle serves.  Forms: 0 ds_read_b32, 1 ds_read_b64, 2
+// ds_read_b128, 3 ds_read_b64_tr_b16.
+template <int FORM>
+__global__ __launch_bounds__(64) void lds_probe_kernel(const int* __restrict__ offs, int iters,
+                                                       unsigned* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) unsigned lds[16384];          // 64 KB
+    const int t = threadIdx.x;
+    for (int i = t; i < 16384; i += 64) lds[i] = (unsigned)i * 2654435761u;
+    __syncthreads();
+    constexpr uint32_t kMask = FORM == 0 ? 0xFFFCu : FORM == 2 ? 0xFFF0u : 0xFFF8u;
+    const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds +
+                          ((uint32_t)offs[t] & kMask);
+    unsigned acc = 0;
+    for (int i = 0; i < iters; ++i) {
+        if constexpr (FORM == 0) {
+            unsigned v;
+            asm volatile("ds_read_b32 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+            acc += v;
+        } else if constexpr (FORM == 2) {
+            typedef unsigned u4 __attribute__((ext_vector_type(4)));
+            u4 v;
+            asm volatile("ds_read_b128 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+            acc += v[0] ^ v[1] ^ v[2] ^ v[3];
+        } else {
+            typedef unsigned u2 __attribute__((ext_vector_type(2)));
+            u2 v;
+            if constexpr (FORM == 1)
+                asm volatile("ds_read_b64 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+            else
+                asm volatile("ds_read_b64_tr_b16 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+            acc += v[0] ^ v[1];
+        }
+    }
+    out[t] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_lds_probe(int form, const int* offs, int iters, unsigned* out, hipStream_t s) {
+    switch (form) {
+        case 0: hipLaunchKernelGGL(lds_probe_kernel<0>, dim3(1), dim3(64), 0, s, offs, iters, out); break;
+        case 1: hipLaunchKernelGGL(lds_probe_kernel<1>, dim3(1), dim3(64), 0, s, offs, iters, out); break;
+        case 2: hipLaunchKernelGGL(lds_probe_kernel<2>, dim3(1), dim3(64), 0, s, offs, iters, out); break;
+        default: hipLaunchKernelGGL(lds_probe_kernel<3>, dim3(1), dim3(64), 0, s, offs, iters, out); break;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_valu_probe(int form, int blocks, int iters, float* out, uint64_t* stamps, hipStream_t s) {
     switch (form) {

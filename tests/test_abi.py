@@ -212,6 +212,18 @@ def test_reduce_noalloc_validation_without_launch(lib, args, code):
     assert lib.reduce_sum_f32_variant_noalloc(*args, None) == declared_codes()[code]
 
 
+@pytest.mark.parametrize("args,code", [
+    ((4, FAKE, 1, FAKE), "GEMM_F32_ERR_INVALID_VARIANT"),
+    ((-1, FAKE, 1, FAKE), "GEMM_F32_ERR_INVALID_VARIANT"),
+    ((2, FAKE, -1, FAKE), "GEMM_F32_ERR_INVALID_DIM"),
+    ((2, None, 1, FAKE), "GEMM_F32_ERR_NULL_PTR"),
+    ((2, FAKE, 1, None), "GEMM_F32_ERR_NULL_PTR"),
+    ((2, FAKE + 2, 1, FAKE), "GEMM_F32_ERR_MISALIGNED"),
+])
+def test_lds_probe_validation_without_launch(lib, args, code):
+    assert lib.gemm_f32_lds_probe(*args, None) == declared_codes()[code]
+
+
 def test_reduce_noalloc_scratch_limit(binding):
     """The declared scratch size, and the largest n each tree version takes
     in it: exactly where the workspace the version needs passes 1 MiB."""
@@ -364,10 +376,10 @@ def test_default_variant_choices(binding):
         v = binding.gemm_f32_default_variant(M, N, K)
         assert binding.gemm_f32_variant_name(v) == name, (M, N, K, v)
     mixed = {
-        (8192, 8192, 8192): "mixed256x256_bk64_w4_sched",
-        (4096, 4096, 64): "mixed256x256_bk64_w4_sched",
-        (3072, 3072, 3072): "mixed256x256_bk64_w4_sched",         # 144 tiles of 256
-        (4100, 4100, 4096): "mixed256x256_bk64_w4_sched",         # edge tiles, N even
+        (8192, 8192, 8192): "mixed256x256_bk64_w4_wide",
+        (4096, 4096, 64): "mixed256x256_bk64_w4_wide",
+        (3072, 3072, 3072): "mixed256x256_bk64_w4_wide",          # 144 tiles of 256
+        (4100, 4100, 4096): "mixed256x256_bk64_w4_wide",          # edge tiles, N even
         (2560, 2560, 2560): "mixed128x128_bk64_w2x2_directAB",    # 100 tiles of 256, 400 of 128
         (2048, 2048, 2048): "mixed128x128_bk64_w2x2_directAB",
         (1536, 1536, 1536): "mixed128x128_bk64_w2x2_directAB",    # 144 tiles of 128

@@ -34,7 +34,7 @@ FP32_CASES = {
     "mfma128x128_bk32_w2x2_sched": (1532, 1404, 164),
     "mfma64x64_bk32_w1x1_k4_sched": (556, 572, 1004),
 }
-MIXED_CASES = {"mixed256x256_bk64_w4_sched": (3068, 3068, 200)}
+MIXED_CASES = {"mixed256x256_bk64_w4_wide": (3068, 3068, 200)}
 
 
 def stored(op, rows, cols):
@@ -81,7 +81,7 @@ def test_mixed_zero_copies_read_no_guard(kernel, fmt, ops):
     Ab = inputs.to16(inputs.random_matrix(gen, ar, ac, "int"), fmt)
     Bb = inputs.to16(inputs.random_matrix(gen, br, bc, "int"), fmt)
     # even leading dimensions and an offset of two elements keep the
-    # scheduled kernel's 4-byte alignment
+    # scheduled kernels' 4-byte alignment
     A = inputs.padded16(Ab, ac + 4, 2, fmt, guard=GUARD_ROWS * (ac + 4) + 64)
     B = inputs.padded16(Bb, bc + 6, 2, fmt, guard=GUARD_ROWS * (bc + 6) + 64)
     ref, _ = oracle.gemm16(fmt, A.view, B.view, threads=8, op_a=op_a, op_b=op_b)
