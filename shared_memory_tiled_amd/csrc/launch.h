@@ -48,6 +48,9 @@ hipError_t launch_ksplit16(const Gemm16Args& p, hipStream_t s, int format, int o
 // (mfma16_wide.hip); it takes the problems the 32 x 32 x 16 scheduled kernel
 // takes (the caller checks), with tile-row groups of group_m.
 hipError_t launch_wide16(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m);
+// The same product with four 32-deep LDS stages (mfma16_wide4.hip), as
+// stored (A k-contiguous, B mn-contiguous) only.
+hipError_t launch_wide16_4stage(const Gemm16Args& p, hipStream_t s, int format, int group_m);
 
 // Sum reduction (reduce.hip): *out = sum of x[0 .. n-1].
 hipError_t launch_reduce(int variant, int64_t n, const float* x, float* out, float* ws, hipStream_t s);

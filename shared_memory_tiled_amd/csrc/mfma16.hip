@@ -1100,6 +1100,16 @@ hipError_t launch_wide_cfg(const Gemm16Args& p, hipStream_t s, int tiles_m, int 
     return launch_wide16(p, s, FMT, 0, 0, kSchedGroupM);
 }
 
+// Configuration 11 (the four-stage form, mfma16_wide4.hip) where it takes
+// the problem; else the 8-wave kernel, as for configuration 8.
+template <int FMT>
+hipError_t launch_wide4_cfg(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int /*group_m*/,
+                            unsigned blocks) {
+    if (!sched_fits(p, 0, 0))
+        return launch16<FMT, 256, 256, 2, 4, true, true, true>(p, s, tiles_m, tiles_n, kDirectGroupM, blocks);
+    return launch_wide16_4stage(p, s, FMT, kSchedGroupM);
+}
+
 const MixedConfig kMixed[] = {
     {"mixed256x256_bk64_w2x4_directA", 256, 256, 8, MIXED(256, 256, 2, 4, true, false)},
     {"mixed256x256_bk64_w2x4", 256, 256, 8, MIXED(256, 256, 2, 4, false, false)},
@@ -1123,6 +1133,10 @@ const MixedConfig kMixed[] = {
     {"mixed256x256_bk64_w4_wide", 256, 256, kSchedGroupM,
      {{launch16<0, 256, 256, 2, 4, false, false, false>, launch_wide_cfg<0>},
       {launch16<1, 256, 256, 2, 4, false, false, false>, launch_wide_cfg<1>}}},
+    // the same with four 32-deep LDS stages (not picked by default)
+    {"mixed256x256_bk32_w4_wide4stage", 256, 256, kSchedGroupM,
+     {{launch16<0, 256, 256, 2, 4, false, false, false>, launch_wide4_cfg<0>},
+      {launch16<1, 256, 256, 2, 4, false, false, false>, launch_wide4_cfg<1>}}},
 };
 #undef MIXED
 constexpr int kNumMixed = (int)(sizeof(kMixed) / sizeof(kMixed[0]));

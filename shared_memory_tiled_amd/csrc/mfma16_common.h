@@ -60,6 +60,19 @@ __device__ __forceinline__ void wait_tied(u32x2 (&h)[8][2]) {
                  : "memory");
 }
 
+// Keeps fragments alive up to this point (no register of theirs is handed
+// to another value before it).
+template <int N>
+__device__ __forceinline__ void keep_alive(const u32x4 (&b)[N]) {
+    static_assert(N == 8, "fragment count");
+    asm volatile("" ::"v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]), "v"(b[7]));
+}
+__device__ __forceinline__ void keep_alive(const u32x2 (&h)[8][2]) {
+    asm volatile("" ::"v"(h[0][0]), "v"(h[0][1]), "v"(h[1][0]), "v"(h[1][1]), "v"(h[2][0]), "v"(h[2][1]),
+                 "v"(h[3][0]), "v"(h[3][1]), "v"(h[4][0]), "v"(h[4][1]), "v"(h[5][0]), "v"(h[5][1]), "v"(h[6][0]),
+                 "v"(h[6][1]), "v"(h[7][0]), "v"(h[7][1]));
+}
+
 // Byte address inside LDS of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;

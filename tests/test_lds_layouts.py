@@ -819,3 +819,150 @@ def test_wide16_copies_never_depend_on_the_scalar_offset(kc, shape):
                         wants_zero = k >= K or (kc and mn >= ext)
                         in_matrix = (k + 7 < K and mn < ext) if kc else (k < K and mn + 7 < ext)
                         _check_copy(voff, soff, nrec, 16, wants_zero, in_matrix, what)
+
+
+def wide4_copy(kc, w, j, lane):
+    """(LDS byte of the first of the 16 bytes, mn, k relative to the phase)
+    of lane `lane` of copy j (0..3) of wave w of the 16 x 16 x 32 scheduled
+    kernel's four-stage form (32-deep tile stage): KC, 64-byte rows of 32 k with chunk c at
+    c ^ 2 ((r / 8) mod 2), 16 rows per 1 KB copy; MC, pairs of 512-byte k rows
+    1056 bytes apart, one pair per copy, k row kappa in pair (kappa % 4) + 4
+    (kappa / 8), row (kappa / 4) % 2."""
+    q = w + 4 * j
+    if kc:
+        row = 16 * q + lane // 4
+        k = 8 * ((lane % 4) ^ (((row >> 3) & 1) << 1))
+        return 1024 * q + 16 * lane, row, k
+    kappa = 8 * ((q >> 2) & 3) + 4 * (lane // 32) + (q & 3)
+    return 1056 * q + 16 * lane, 8 * (lane % 32), kappa
+
+
+def wide4_read(kc, lane, mn, f, h):
+    """LDS byte a lane addresses for read h of fragment f (the kernel's
+    per-lane base plus its instruction offset, stage 0)."""
+    j, g = lane % 16, lane // 16
+    if kc:
+        return 64 * (mn + j) + 16 * (g ^ (((j >> 3) & 1) << 1)) + 1024 * f
+    return 1056 * (j // 4 + 4 * g) + 2 * (mn + 4 * (j % 4)) + (32 * f + 512 * h)
+
+
+@pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
+def test_wide4_kernel_layout(kc):
+    """The four-stage 16 x 16 x 32 kernel's tile stage (256 mn x 32 k),
+    restated: the 16 copies (4 per wave) fill every (mn, k) exactly once
+    (the MC stage's padding is never written); every lane's fragment reads
+    deliver the operands v_mfma_f32_16x16x32 needs -- for the wave's span at
+    mn, block f, lane l supplies op(X)[mn + 16 f + l % 16][8 (l / 16) + e],
+    e = 0..7; both reads conflict free on 64 banks (128-bit: the measured
+    quad grouping; 64-bit transposed: 32 lanes per cycle); instruction
+    offsets with the largest stage stay below 2^16."""
+    stage = 16384 if kc else 16 * 1056
+    where = {}                                   # LDS byte (even) -> (mn, k)
+    for w in range(4):
+        for j in range(4):
+            for lane in range(64):
+                dst, mn, k = wide4_copy(kc, w, j, lane)
+                for e in range(8):
+                    assert dst + 2 * e not in where
+                    where[dst + 2 * e] = (mn, k + e) if kc else (mn + e, k)
+    assert sorted(set(where.values())) == [(m, k) for m in range(256) for k in range(32)]
+    assert max(where) < stage
+    if not kc:
+        pads = {1056 * m + 1024 + 2 * x for m in range(16) for x in range(16)}
+        assert not pads & set(where)
+    for mn in (0, 128):
+        for f in range(8):
+            imm = 3 * stage + ((1024 * f) if kc else (32 * f + 512))
+            assert imm < 1 << 16
+            if kc:
+                addrs = [wide4_read(True, lane, mn, f, 0) for lane in range(64)]
+                for lane, a in enumerate(addrs):
+                    assert a % 16 == 0
+                    got = [where[a + 2 * e] for e in range(8)]
+                    assert got == [(mn + 16 * f + lane % 16, 8 * (lane // 16) + e) for e in range(8)], (mn, f, lane)
+                assert degree128([a // 4 for a in addrs]) == 1
+            else:
+                vals = {lane: [] for lane in range(64)}
+                for h in range(2):
+                    addrs = [wide4_read(False, lane, mn, f, h) for lane in range(64)]
+                    assert all(a % 8 == 0 for a in addrs)
+                    # in each group of 16 lanes, value e of lane i is element
+                    # i % 4 of the 8 bytes that lane 4 e + i // 4 addresses
+                    for lane in range(64):
+                        grp, i16 = lane - lane % 16, lane % 16
+                        for e in range(4):
+                            vals[lane].append(where[addrs[grp + 4 * e + i16 // 4] + 2 * (i16 % 4)])
+                    assert degree([a // 4 for a in addrs], 2, 64, 32) == 1
+                for lane in range(64):
+                    assert vals[lane] == [(mn + 16 * f + lane % 16, 8 * (lane // 16) + e) for e in range(8)], (mn, f, lane)
+
+
+def wide4_phase_blocks(K):
+    """Block (k0 = 32 b) of each phase position of the four-stage kernel:
+    the last block first, then zero phases (None) up to a multiple of 4
+    phases, then blocks 0 .. KB - 2."""
+    KB = -(-K // 32)
+    P = 4 * (-(-KB // 4))
+    return [KB - 1] + [None] * (P - KB) + list(range(KB - 1))
+
+
+@pytest.mark.parametrize("K", [8, 32, 40, 96, 136, 200, 1000, 8192, 8100])
+def test_wide4_phase_order_covers_k_once(K):
+    """Every k < K is in exactly one phase; the phase count is a multiple
+    of 4; only the first four phases (copied in the prologue) hold the last
+    block or zeros."""
+    blocks = wide4_phase_blocks(K)
+    assert len(blocks) % 4 == 0
+    ks = sorted(32 * b + i for b in blocks if b is not None for i in range(32) if 32 * b + i < K)
+    assert ks == list(range(K))
+    assert all(b is not None and 32 * b + 31 < K for b in blocks[4:])
+
+
+@pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
+@pytest.mark.parametrize("shape", [(3068, 200, 3072), (2814, 72, 2818), (256, 64, 256), (4100, 8, 4100), (520, 1000, 522)])
+def test_wide4_copies_never_depend_on_the_scalar_offset(kc, shape):
+    """Four-stage 16 x 16 x 32 kernel: the prologue's four phases take their
+    block in the per-lane offsets with a scalar offset of 0 (lanes at k >= K
+    and zero phases past the end); every later phase is an interior block
+    copied with its block in the scalar offset, and copies aimed past the
+    last phase re-copy block 0 with a scalar offset of 0.  Only a chunk of
+    the mn-contiguous factor's last row across its last column may straddle
+    the descriptor's end -- by its per-lane offset (scalar offset 0: in the
+    prologue, or a re-copy of block 0 when K <= 32), by whole dwords."""
+    ext, K, ld_mn = shape
+    rows, cols = (ext, K) if kc else (K, ext)
+    ld = (K + 8) if kc else ld_mn
+    nrec = 2 * ((rows - 1) * ld + cols)
+    assert nrec % 4 == 0 and K % 8 == 0
+    blocks = wide4_phase_blocks(K)
+    P = len(blocks)
+    pb = (lambda k0: 2 * k0) if kc else (lambda k0: 2 * k0 * ld)
+    for mn0 in sorted({0, (ext - 1) // 256 * 256}):
+        for w in range(4):
+            for j in range(4):
+                for lane in range(64):
+                    _, mnl, kl = wide4_copy(kc, w, j, lane)
+                    mn = mn0 + mnl
+                    doff = 2 * (mn * ld + kl) if kc else 2 * (kl * ld + mn)
+                    for pos in range(P + 4):                 # the loop also copies 4 positions past the end
+                        b = blocks[pos] if pos < P else 0
+                        k = 32 * b + kl if b is not None else None
+                        if pos < 4:
+                            voff = PAST_END if b is None or k >= K else doff + pb(32 * b)
+                            soff = 0
+                        elif pos < P:
+                            voff, soff = doff, pb(32 * b)
+                        else:
+                            voff, soff = doff, 0
+                        what = (kc, shape, mn0, w, j, lane, pos)
+                        if b is not None and not kc and k < K and mn < ext < mn + 8 and voff < nrec < voff + soff + 16:
+                            assert k == K - 1 and (pos == 0 or pos >= P) and soff == 0, what
+                            assert (nrec - voff) % 4 == 0 and nrec - voff == 2 * (ext - mn), what
+                            continue
+                        if pos >= P:
+                            # never read: only in range or past the end by its own offset
+                            assert voff >= nrec or voff + 16 <= nrec or not kc and voff < nrec, what
+                            continue
+                        wants_zero = b is None or k >= K or (kc and mn >= ext)
+                        in_matrix = b is not None and ((k + 7 < K and mn < ext) if kc else (k < K and mn + 7 < ext))
+                        _check_copy(voff, soff, nrec, 16, wants_zero, in_matrix, what)
