@@ -40,6 +40,8 @@ Extra modes (used for counter runs under rocprofv3):
                         JSON line per run with the median and best launch time
                         (HIP events around every launch), then the oracle's
                         time on this host (see bench_all_workloads)
+    --copy-rate         bytes per clock per CU that 1 KB wave loads bring from
+                        an L2-resident buffer into LDS and into registers
     --lds-probe         one wave reading LDS at chosen offsets, one launch per
                         case (which lanes one read cycle serves, from the
                         bank-conflict counter of each dispatch)
@@ -623,6 +625,41 @@ def bench_lds_probe(args) -> int:
     return 0
 
 
+def bench_copy_rate(args) -> int:
+    """The rate at which each CU brings 1 KB wave loads from an L2-resident
+    buffer, into LDS (the 16-bit kernels' copies) and into registers, from
+    the library's measurement helper: one workgroup of 4 waves per CU, each
+    with its own 64 KB (2 MB per XCD in all), three runs of each mode; bytes
+    per clock per CU from each wave's shader clock cycles."""
+    import statistics
+
+    import torch
+
+    from shared_memory_tiled_amd import binding
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 2000
+    src = torch.randint(0, 1 << 30, (cus * 65536 // 4,), dtype=torch.int32, device="cuda")
+    out = torch.zeros(cus * 256, dtype=torch.int32, device="cuda")
+    cycles = torch.zeros(cus * 4, dtype=torch.int64, device="cuda")
+    nbytes = cus * 4 * iters * 8 * 1024
+    for mode, what in ((0, "into LDS"), (1, "into registers")):
+        binding.gemm_f32_copy_probe(mode, cus, 2, src, out, cycles)       # warm the caches
+        for rep in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            binding.gemm_f32_copy_probe(mode, cus, iters, src, out, cycles)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            cyc = statistics.median(cycles.cpu().tolist())
+            print(json.dumps({"copy_probe_mode": mode, "loads": what, "run": rep, "ms": round(ms, 4),
+                              "TB_per_s_all_CUs": round(nbytes / ms / 1e9, 2),
+                              "bytes_per_clock_per_CU": round(nbytes / cus / cyc, 1),
+                              "clock_GHz": round(cyc / (ms * 1e-3) / 1e9, 3)}), flush=True)
+    return 0
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -743,6 +780,8 @@ def main(argv=None) -> int:
     ap.add_argument("--format", default="bf16", choices=["bf16", "f16"], help="16-bit format of --row mixed")
     ap.add_argument("--n", type=int, default=2 ** 28, help="values summed by --row reduce")
     ap.add_argument("--all-workloads", action="store_true")
+    ap.add_argument("--copy-rate", action="store_true",
+                    help="per-CU rate of 1 KB wave loads from L2 into LDS and into registers")
     ap.add_argument("--lds-probe", action="store_true",
                     help="launch the LDS read probe over its lane-grouping cases (for a counter run)")
     ap.add_argument("--valu-probe", action="store_true",
@@ -762,7 +801,7 @@ def main(argv=None) -> int:
                          "matrix every launch)")
     args = ap.parse_args(argv)
     headline = not (args.all_workloads or args.shape_sweep or args.ladder or args.valu_probe or args.lds_probe
-                    or args.row != "gemm")
+                    or args.copy_rate or args.row != "gemm")
     if args.settle_s is not None:
         globals()["SETTLE_S"] = max(0.0, args.settle_s)
     elif headline:
@@ -798,6 +837,8 @@ def main(argv=None) -> int:
         return bench_valu_probe(args)
     if args.lds_probe:
         return bench_lds_probe(args)
+    if args.copy_rate:
+        return bench_copy_rate(args)
     if args.all_workloads:
         return bench_all_workloads(args)
     if args.shape_sweep:

@@ -217,6 +217,25 @@ int gemm_f32_valu_probe(int form, int64_t blocks, int iters, float *out, uint64_
  * GEMM_F32_ERR_INVALID_VARIANT, iters < 0 GEMM_F32_ERR_INVALID_DIM). */
 int gemm_f32_lds_probe(int form, const int32_t *offsets, int iters, uint32_t *out, void *stream);
 
+/* Measurement helper, this library's own (not part of the product): the
+ * rate at which a CU brings 1 KB wave loads (16 bytes a lane, as the 16-bit
+ * kernels' copies) from an L2-resident buffer, into LDS or into registers.
+ * Each workgroup (4 waves) reads its own 64 KB of src, wave w the 16 KB at
+ * 16 KB w, cycling through it `iters` x 8 times with 8 to 16 loads in flight.
+ *   mode    0: buffer loads into LDS; 1: buffer loads into vector registers
+ *   blocks  workgroups of 256 threads, >= 1 (one per CU for a per-CU rate)
+ *   iters   loop trips, even, >= 0
+ *   src     device pointer, 16-byte aligned, to blocks x 65536 bytes
+ *           (blocks x 64 KB should fit the L2 caches)
+ *   out     device pointer to blocks x 256 uint32, overwritten
+ *   cycles  device pointer to blocks x 4 uint64 (8-byte aligned): each
+ *           wave's shader clock cycles for its loop
+ * Enqueue-only on `stream`; statuses as for gemm_f32 (an unknown mode gives
+ * GEMM_F32_ERR_INVALID_VARIANT, odd or negative iters
+ * GEMM_F32_ERR_INVALID_DIM). */
+int gemm_f32_copy_probe(int mode, int64_t blocks, int iters, const void *src, uint32_t *out, uint64_t *cycles,
+                        void *stream);
+
 /* Static, NUL-terminated description of a status code (the by-name report
  * of the chapter 2 error check cited with the codes above); "unknown status"
  * for any other number. */

@@ -90,6 +90,8 @@ def load_library():
         lib.gemm_f32_valu_probe.restype = ctypes.c_int
         lib.gemm_f32_lds_probe.argtypes = [ctypes.c_int, _vp, ctypes.c_int, _vp, _vp]
         lib.gemm_f32_lds_probe.restype = ctypes.c_int
+        lib.gemm_f32_copy_probe.argtypes = [ctypes.c_int, _i64, ctypes.c_int, _vp, _vp, _vp, _vp]
+        lib.gemm_f32_copy_probe.restype = ctypes.c_int
         lib.reduce_sum_f32_variant_noalloc.argtypes = [ctypes.c_int, _i64, _vp, _vp, _vp]
         lib.reduce_sum_f32_variant_noalloc.restype = ctypes.c_int
         lib.reduce_sum_f32_num_variants.argtypes = []
@@ -271,6 +273,13 @@ def gemm_f32_lds_probe(form, offsets, iters, out, stream=None) -> None:
     int32 on the device; out: 64 uint32 or int32 on the device)."""
     lib = load_library()
     _check(lib.gemm_f32_lds_probe(int(form), _addr(offsets), int(iters), _addr(out), _stream(stream)))
+
+
+def gemm_f32_copy_probe(mode, blocks, iters, src, out, cycles, stream=None) -> None:
+    """The copy-rate probe of the library's measurement helper."""
+    lib = load_library()
+    _check(lib.gemm_f32_copy_probe(int(mode), int(blocks), int(iters), _addr(src), _addr(out), _addr(cycles),
+                                   _stream(stream)))
 
 
 REDUCE_DEFAULT = 4

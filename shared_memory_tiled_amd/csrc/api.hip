@@ -211,6 +211,22 @@ extern "C" int gemm_f32_lds_probe(int form, const int32_t* offsets, int iters, u
     return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
 }
 
+// A measurement helper: the copy-rate probe of probe.hip.
+extern "C" int gemm_f32_copy_probe(int mode, int64_t blocks, int iters, const void* src, uint32_t* out,
+                                   uint64_t* cycles, void* stream) {
+    if (mode < 0 || mode > 1) return GEMM_F32_ERR_INVALID_VARIANT;
+    if (blocks < 1 || iters < 0 || iters % 2 != 0) return GEMM_F32_ERR_INVALID_DIM;
+    if (blocks > 0x7FFFFFFF / 256) return GEMM_F32_ERR_TOO_LARGE;
+    if (src == nullptr || out == nullptr || cycles == nullptr) return GEMM_F32_ERR_NULL_PTR;
+    if (((uintptr_t)src & 15u) != 0 || misaligned(out) || ((uintptr_t)cycles & 7u) != 0)
+        return GEMM_F32_ERR_MISALIGNED;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_F32_ERR_DEVICE;
+    const hipError_t e = launch_copy_probe(mode, (int)blocks, static_cast<const unsigned*>(src), iters, out, cycles,
+                                           reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
+}
+
 // ---------------------------------------------------------------- transpose
 
 namespace {

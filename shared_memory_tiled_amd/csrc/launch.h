@@ -92,6 +92,11 @@ hipError_t launch_valu_probe(int form, int blocks, int iters, float* out, uint64
 // offsets, `iters` times (form 0 ds_read_b32, 1 ds_read_b64, 2
 // ds_read_b128, 3 ds_read_b64_tr_b16).
 hipError_t launch_lds_probe(int form, const int* offs, int iters, unsigned* out, hipStream_t s);
+// Measurement helper (probe.hip): 1 KB wave loads from an L2-resident
+// buffer, into LDS (mode 0) or vector registers (mode 1); `blocks` blocks of
+// 4 waves, each block reading its own 64 KB of src.
+hipError_t launch_copy_probe(int mode, int blocks, const unsigned* src, int iters, unsigned* out, uint64_t* cycles,
+                             hipStream_t s);
 int regblock_num_configs();
 const char* regblock_config_name(int config);
 

@@ -27,7 +27,7 @@
 // against 1399 (one round of tiles, where the latency was already hidden).
 // The 16-bit product needs 32 bytes per clock per CU from L2 at full
 // matrix rate, about what the L2 delivers into LDS under load (measured:
-// 31 bytes per clock per CU), so the copies' timing matters.  The stage of
+// 32.5 bytes per clock per CU), so the copies' timing matters.  The stage of
 // each phase is an instruction offset (the loop is unrolled by the four
 // stages), so the loop holds no vector ALU instruction besides the matrix
 // instructions.

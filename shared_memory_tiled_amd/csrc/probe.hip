@@ -108,7 +108,69 @@ __global__ __launch_bounds__(64) void lds_probe_kernel(const int* __restrict__ o
     out[t] = acc;
 }
 
+// 3. The rate of 1 KB wave copies from an L2-resident buffer per CU: each
+// block (4 waves) reads its own 64 KB window of src, wave w the 16 KB at
+// 16 KB w, in 1 KB wave loads (16 bytes a lane) cycling through the 16 KB,
+// keeping 8 to 16 loads in flight; mode 0 loads into LDS
+// (buffer_load_dwordx4 ... lds, as the 16-bit kernels' copies), mode 1 into
+// vector registers (the loads of one group of eight are consumed while the
+// next group is in flight).  Lane 0 of each wave records the shader clock
+// counter around its loop.
+template <int MODE>
+__global__ __launch_bounds__(256) void copy_probe_kernel(const unsigned* __restrict__ src, int iters,
+                                                         unsigned* __restrict__ out, uint64_t* __restrict__ cycles) {
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) unsigned char lds[32768];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned*>(src) + ((int64_t)blockIdx.x * 65536 + (int64_t)w * 16384) / 4, (short)0, 16384,
+        0x00020000);
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    u4 acc = {0, 0, 0, 0}, v0[8], v1[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v0[j] = v1[j] = u4{0, 0, 0, 0};
+    for (int i = 0; i < iters; i += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            u4 (&cur)[8] = h ? v1 : v0;
+            u4 (&prev)[8] = h ? v0 : v1;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int voff = ((i * 3 + h * 8 + j) % 16) * 1024 + 16 * lane;      // below 16384
+                if constexpr (MODE == 0) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rs, (__attribute__((address_space(3))) void*)(lds + (w * 8 + j) * 1024), 16, voff, 0, 0, 0);
+                } else {
+                    cur[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+                }
+            }
+            if constexpr (MODE == 0) {
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc ^= prev[j];
+            }
+        }
+    }
+    if constexpr (MODE == 1) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc ^= v1[j];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    __syncthreads();
+    out[blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3] ^ lds[threadIdx.x * 16];
+    if (lane == 0) cycles[blockIdx.x * 4 + w] = t1 - t0;
+}
+
 }  // namespace
+
+hipError_t launch_copy_probe(int mode, int blocks, const unsigned* src, int iters, unsigned* out, uint64_t* cycles,
+                             hipStream_t s) {
+    if (mode == 0) hipLaunchKernelGGL(copy_probe_kernel<0>, dim3(blocks), dim3(256), 0, s, src, iters, out, cycles);
+    else hipLaunchKernelGGL(copy_probe_kernel<1>, dim3(blocks), dim3(256), 0, s, src, iters, out, cycles);
+    return hipGetLastError();
+}
 
 hipError_t launch_lds_probe(int form, const int* offs, int iters, unsigned* out, hipStream_t s) {
     switch (form) {

@@ -224,6 +224,21 @@ def test_lds_probe_validation_without_launch(lib, args, code):
     assert lib.gemm_f32_lds_probe(*args, None) == declared_codes()[code]
 
 
+@pytest.mark.parametrize("args,code", [
+    ((2, 1, 2, FAKE, FAKE, FAKE), "GEMM_F32_ERR_INVALID_VARIANT"),
+    ((0, 0, 2, FAKE, FAKE, FAKE), "GEMM_F32_ERR_INVALID_DIM"),
+    ((0, 1, 3, FAKE, FAKE, FAKE), "GEMM_F32_ERR_INVALID_DIM"),
+    ((1, 1, -2, FAKE, FAKE, FAKE), "GEMM_F32_ERR_INVALID_DIM"),
+    ((0, 1, 2, None, FAKE, FAKE), "GEMM_F32_ERR_NULL_PTR"),
+    ((0, 1, 2, FAKE, FAKE, None), "GEMM_F32_ERR_NULL_PTR"),
+    ((0, 1, 2, FAKE + 4, FAKE, FAKE), "GEMM_F32_ERR_MISALIGNED"),
+    ((0, 1, 2, FAKE, FAKE, FAKE + 4), "GEMM_F32_ERR_MISALIGNED"),
+    ((0, 2**31, 2, FAKE, FAKE, FAKE), "GEMM_F32_ERR_TOO_LARGE"),
+])
+def test_copy_probe_validation_without_launch(lib, args, code):
+    assert lib.gemm_f32_copy_probe(*args, None) == declared_codes()[code]
+
+
 def test_reduce_noalloc_scratch_limit(binding):
     """The declared scratch size, and the largest n each tree version takes
     in it: exactly where the workspace the version needs passes 1 MiB."""
