@@ -364,16 +364,20 @@ int reduce_sum_f32_variant_noalloc(int variant, int64_t n, const float *x, float
  * 64 x 64 tiles whose four waves each run the whole tile over every fourth
  * 32-deep phase (mixed64x64_bk32_w4_ksplit, v_mfma_f32_16x16x32; partial
  * tiles added in wave order, so every op pair gives the same bits); it needs
- * what the scheduled configuration needs (below), and a problem it does not
- * take runs the element-wise 64 x 64 kernel.  The scheduled configuration
- * (mixed256x256_bk64_w4_sched, gemm_mixed's choice once there are 128 tiles
- * of 256 x 256) takes K a multiple of 8, N even (M too for A stored
- * transposed in gemm_mixed_op, and not N for B stored transposed),
- * 4-byte aligned operands with even leading dimensions and operands under
- * 2^31 bytes; edge tiles run whole and store only inside C, and a last
- * phase that reaches past K copies zeros there.  Other problems
- * given to it run mixed256x256_bk64_w2x4_directAB, which has the same tiles
- * and summation order (the same bits).
+ * what the scheduled configurations need (below), and a problem it does not
+ * take runs the element-wise 64 x 64 kernel.  The scheduled configurations
+ * -- mixed256x256_bk64_w4_wide (v_mfma_f32_16x16x32; gemm_mixed's and
+ * gemm_mixed_op's choice once there are 128 tiles of 256 x 256),
+ * mixed256x256_bk64_w4_sched (the same schedule on v_mfma_f32_32x32x16) and
+ * mixed256x256_bk32_w4_wide4stage (16x16x32 with four 32-deep LDS stages) --
+ * take K a multiple of 8, N even (M too for A stored transposed in
+ * gemm_mixed_op, and not N for B stored transposed), 4-byte aligned operands
+ * with even leading dimensions and operands under 2^31 bytes; edge tiles run
+ * whole and store only inside C, and k positions past K copy zeros.  Other
+ * problems given to them run mixed256x256_bk64_w2x4_directAB (for the
+ * 32 x 32 x 16 configuration the same tiles and summation order, the same
+ * bits; for the 16 x 16 x 32 ones another instruction, other bits within the
+ * same bound).
  */
 #define GEMM_MIXED_BF16 0
 #define GEMM_MIXED_F16  1
@@ -387,8 +391,8 @@ int gemm_mixed_variant(int variant, int format, int64_t M, int64_t N, int64_t K,
 int gemm_mixed_num_variants(void);
 const char *gemm_mixed_variant_name(int variant);   /* NULL if unknown */
 /* The configuration gemm_mixed runs for an M x N x K product (the scheduled
- * configuration hands problems it does not take to
- * its 8-wave fallback, as described above), or -1 for sizes that are negative
+ * configurations hand problems they do not take to
+ * the 8-wave fallback, as described above), or -1 for sizes that are negative
  * or above INT_MAX.  Launches nothing, needs no device. */
 int gemm_mixed_default_variant(int64_t M, int64_t N, int64_t K);
 
@@ -402,7 +406,12 @@ int gemm_mixed_default_variant(int64_t M, int64_t N, int64_t K);
  * Everything else as for gemm_mixed (formats, alignment, accuracy, errors;
  * GEMM_F32_ERR_INVALID_OP for another op value).  The factors are read in
  * place; for a given M, N and K the result has the same bits whichever way
- * the factors are stored. */
+ * the factors are stored, as long as each storage meets the conditions of
+ * the configuration gemm_mixed picks: from 128 tiles of 256 x 256 on, a
+ * storage that does not (an odd M for A stored transposed, an odd N for B
+ * as stored, an odd leading dimension, a 2-byte aligned base) runs the
+ * 8-wave fallback on v_mfma_f32_32x32x16, whose bits differ within the same
+ * bound. */
 int gemm_mixed_op(int op_a, int op_b, int format, int64_t M, int64_t N, int64_t K,
                   const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                   float *C, int64_t ldc, void *stream);

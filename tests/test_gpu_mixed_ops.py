@@ -161,8 +161,9 @@ def test_mixed_op_scheduled_edge_tiles(ops):
     bits of gemm_mixed on explicitly transposed copies.  Widths 3004 and
     2996 put a chunk across the end of an mn-contiguous factor's last row
     (zeros past it); with M (N) odd and even leading dimensions, A stored
-    transposed (B as stored) runs the 8-wave kernel instead: the same bits.
-    K = 200: the last of four phases reaches past K (zeros there)."""
+    transposed (B as stored) runs the 8-wave kernel instead (on integer data
+    every summation order gives the same exact bits).  K = 200: the last of
+    four phases reaches past K (zeros there)."""
     op_a, op_b = ops
     for fmt in FORMATS:
         for (M, N, K, pad) in ((3000, 3000, 128, (0, 0, 0)), (3004, 2996, 192, (0, 0, 0)),
