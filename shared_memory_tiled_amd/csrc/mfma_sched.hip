@@ -673,50 +673,65 @@ void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         step(1, no{}, 0, c0{}, c0{}, 0, 0);
     }
 
-    // Partial tiles: register r of block (i, j) of lane l of wave v at word
-    // v PART_WORDS + ((2 i + j) 16 + r) 64 + l.  Wave v then adds, in wave
-    // order, block row i = v / 2, registers 8 (v % 2) .. + 7 of both blocks
-    // j, and stores them: register r of lane (li, lh) is row rho = 8 (r / 4)
-    // + 4 lh + r % 4 of its block (tile row 32 i + rho for a k-contiguous A,
-    // 2 rho + i for an mn-contiguous one) and column li (32 j + li, or 2 li +
-    // j: then the two blocks' values are adjacent columns, one 64-bit store;
-    // N is a multiple of 4, so both are in or out).
-    __syncthreads();
+    // Partial tiles.  Wave v adds, in wave order, block row v / 2,
+    // registers 8 (v % 2) .. + 7 of both blocks j (16 values per lane), and
+    // stores them.  Each wave writes its partial into its own stages, which
+    // no other wave reads and which hold no copy in flight after its last
+    // phase (so no barrier is needed before): slot v holds what wave v adds,
+    // as groups g = 2 j + h (registers 8 (v % 2) + 4 h .. + 3 of block (v /
+    // 2, j)), lane l's four values at word v SLOT + 4 (64 g + l): one 128-bit
+    // write or read per group, consecutive lanes on consecutive 16 bytes.
+    // Register r of lane (li, lh) is row rho = 8 (r / 4) + 4 lh + r % 4 of
+    // its block (tile row 32 i + rho for a k-contiguous A, 2 rho + i for an
+    // mn-contiguous one) and column li (32 j + li, or 2 li + j: then the two
+    // blocks' values are adjacent columns, one 64-bit store; N is a multiple
+    // of 4, so both are in or out).
+    constexpr int SLOT = 4 * 4 * 64;
+    static_assert(4 * SLOT <= WAVE_WORDS, "slots fit in the wave's stages");
     {
-        float* part = lds + w * PART_WORDS;
+        float* const mine = lds + w * WAVE_WORDS;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) part[((i * FN + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 8 * (v & 1) + 4 * h;
+                    const floatx4 x = {acc[v >> 1][j][r], acc[v >> 1][j][r + 1], acc[v >> 1][j][r + 2],
+                                       acc[v >> 1][j][r + 3]};
+                    *reinterpret_cast<floatx4*>(mine + v * SLOT + 4 * (64 * (2 * j + h) + lane)) = x;
+                }
     }
     __syncthreads();
     const int bi = w >> 1, r0 = 8 * (w & 1);
+    floatx4 sum[FN][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const floatx4 x =
+                    *reinterpret_cast<const floatx4*>(lds + u * WAVE_WORDS + w * SLOT + 4 * (64 * (2 * j + h) + lane));
+                if (u == 0) sum[j][h] = x;
+                else sum[j][h] += x;
+            }
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
         const int r = r0 + rr;
-        float v[FN];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const float* q = lds + ((bi * FN + j) * 16 + r) * 64 + lane;
-            v[j] = q[0];
-#pragma unroll
-            for (int u = 1; u < 4; ++u) v[j] += q[u * PART_WORDS];
-        }
         const int rho = 8 * (r >> 2) + 4 * lh + (r & 3);
         const int row = m0 + (KCA ? 32 * bi + rho : FM * rho + bi);
         if (row >= p.M) continue;
         float* crow = p.C + (int64_t)row * p.ldc + n0;
         if constexpr (!KCB) {
             if (n0 + 2 * li < p.N) {
-                const floatx2 x = {v[0], v[1]};
+                const floatx2 x = {sum[0][rr >> 2][rr & 3], sum[1][rr >> 2][rr & 3]};
                 *reinterpret_cast<floatx2*>(crow + 2 * li) = x;
             }
         } else {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                if (n0 + 32 * j + li < p.N) crow[32 * j + li] = v[j];
+                if (n0 + 32 * j + li < p.N) crow[32 * j + li] = sum[j][rr >> 2][rr & 3];
         }
     }
 }
