@@ -461,7 +461,7 @@ def bench_transpose(args, w) -> int:
 
 # Timed launches per workload: many for the microsecond-scale small products,
 # fewer for the large ones.
-WORKLOAD_LAUNCHES = {"square256": 200, "square1000": 50, "square4096": 20,
+WORKLOAD_LAUNCHES = {"square256": 200, "square1000": 100, "square4096": 20,
                      "rect8192x4096x2048_padded": 20, "square8192": 10}
 
 
@@ -660,6 +660,61 @@ def bench_copy_rate(args) -> int:
     return 0
 
 
+def bench_ksplit_timeline(args) -> int:
+    """Where the k-split kernel's time goes at a workload it runs (default
+    square1000), from the library's timeline helper: gemm_f32 runs untimed
+    for the settle time, then 20 launches back to back, then -- with no wait
+    in between -- the timeline instantiation of the same kernel, whose
+    result must have gemm_f32's bits.  Per wave (100 MHz real-time counter):
+    start relative to the first wave's start, the wait for its first phase,
+    the phase loop, the time to the barrier before the partial tiles are
+    added, the sum and the store until the stores have completed, and the
+    shader clock over its lifetime.  Medians (and extremes) over all waves."""
+    import statistics
+
+    import torch
+
+    from shared_memory_tiled_amd import binding, inputs
+
+    name = args.workload if args.workload != DEFAULT_WORKLOAD else "square1000"
+    w = inputs.WORKLOADS[name]
+    A, B = inputs.operands(w)
+    a = torch.from_numpy(A.buf).cuda()
+    b = torch.from_numpy(B.buf).cuda()
+    c = torch.empty(w.offset + w.M * w.ldc + 64, dtype=torch.float32, device="cuda")
+    call = (w.M, w.N, w.K, a.data_ptr() + 4 * w.offset, w.lda, b.data_ptr() + 4 * w.offset, w.ldb,
+            c.data_ptr() + 4 * w.offset, w.ldc)
+    handle = torch.cuda.current_stream().cuda_stream
+    blocks = ((w.M + 63) // 64) * ((w.N + 63) // 64)
+    tl = torch.zeros(32 * blocks, dtype=torch.int32, device="cuda")
+    settle(lambda: binding.gemm_f32(*call, handle), args.settle_s)
+    for _ in range(20):
+        binding.gemm_f32(*call, handle)
+    torch.cuda.synchronize()
+    ref = c.clone()
+    for _ in range(20):
+        binding.gemm_f32(*call, handle)
+    binding.gemm_f32_ksplit_timeline(*call, tl, tl.numel(), handle)
+    torch.cuda.synchronize()
+    same_bits = bool(torch.equal(c, ref))
+    rows = tl.view(-1, 8).cpu().numpy().astype("int64") & 0xFFFFFFFF
+    t0 = rows[:, 0].min()
+    us = lambda x: float(x) / 100.0                  # 100 MHz ticks -> microseconds
+    parts = {"start_after_first_wave": rows[:, 0] - t0, "first_phase_wait": rows[:, 1] - rows[:, 0],
+             "phase_loop": rows[:, 2] - rows[:, 1], "to_partial_barrier": rows[:, 3] - rows[:, 2],
+             "sum_and_store": rows[:, 4] - rows[:, 3], "wave_lifetime": rows[:, 4] - rows[:, 0],
+             "end_after_first_wave": rows[:, 4] - t0}
+    clock = rows[:, 5] / ((rows[:, 4] - rows[:, 0]) / 100e6) / 1e9
+    line = {"ksplit_timeline": name, "M": w.M, "N": w.N, "K": w.K, "blocks": blocks, "waves": int(rows.shape[0]),
+            "phases_per_wave": sorted(set(int(x) for x in rows[:, 6])), "same_bits_as_gemm_f32": same_bits,
+            "clock_GHz_median": round(float(statistics.median(clock)), 3)}
+    for k, v in parts.items():
+        line[k + "_us"] = {"min": round(us(v.min()), 2), "median": round(us(statistics.median(v)), 2),
+                           "max": round(us(v.max()), 2)}
+    print(json.dumps(line), flush=True)
+    return 0 if same_bits else 1
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -674,13 +729,14 @@ def cpu_model() -> str:
 def bench_all_workloads(args) -> int:
     """gemm_f32 (the default kernel) at every workload, then the oracle.
 
-    GPU: 3 warm-up launches, then a HIP event before the first launch and
-    after every launch on the launch stream; the median and best of the
-    per-launch times give TFLOP/s and the fraction of the fp32 peak.  The
-    same number of launches is also captured in one HIP graph and replayed
-    (graph_ms_per_launch, see graph_ms_per_launch): for the microsecond-scale
-    products the eager launches wait on the host's call rate, the replayed
-    ones run back to back.
+    GPU: 3 warm-up launches, then the timed launches in ten windows, with a
+    HIP event on the launch stream before the first window and after each
+    (the stream handle is passed to every call; a Python event record after
+    every launch would take longer than the microsecond-scale products); the
+    median and best per-launch time over the windows give TFLOP/s and the
+    fraction of the fp32 peak.  The same number of launches is also captured
+    in one HIP graph and replayed (see graph_ms_per_launch), so that they run
+    back to back with no host in between.
     Oracle, on this host, unchanged: the full product at square256 and
     square1000 on one thread and on all cores, at square4096 on all cores;
     at the two largest workloads the 4096 sampled entries plus edge entries
@@ -709,18 +765,24 @@ def bench_all_workloads(args) -> int:
         c = torch.empty(w.offset + w.M * w.ldc + 64, dtype=torch.float32, device=dev)
         call = (w.M, w.N, w.K, a.data_ptr() + 4 * w.offset, w.lda,
                 b.data_ptr() + 4 * w.offset, w.ldb, c.data_ptr() + 4 * w.offset, w.ldc)
-        settle(lambda: binding.gemm_f32(*call))
-        for _ in range(3):
-            binding.gemm_f32(*call)
-        torch.cuda.synchronize()
         stream = torch.cuda.current_stream()       # the stream the library launches on
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
+        handle = stream.cuda_stream
+        settle(lambda: binding.gemm_f32(*call, handle))
+        for _ in range(3):
+            binding.gemm_f32(*call, handle)
+        torch.cuda.synchronize()
+        # ten windows of launches between events: a Python event record after
+        # every launch takes longer than a microsecond-scale kernel
+        per = max(1, launches // 10)
+        windows = launches // per
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(windows + 1)]
         ev[0].record(stream)
-        for i in range(launches):
-            binding.gemm_f32(*call)
+        for i in range(windows):
+            for _ in range(per):
+                binding.gemm_f32(*call, handle)
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(launches)]
+        ms = [ev[i].elapsed_time(ev[i + 1]) / per for i in range(windows)]
         eager_c = c.clone()
         graph = graph_ms_per_launch(lambda: binding.gemm_f32(*call), launches)
         torch.cuda.synchronize()
@@ -731,7 +793,7 @@ def bench_all_workloads(args) -> int:
         line = {"workload": name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb,
                 "ldc": w.ldc, "view_offset_floats": w.offset, "values": w.dist,
                 "kernel": binding.gemm_f32_variant_name(binding.gemm_f32_default_variant(w.M, w.N, w.K)),
-                "launches": launches, "median_ms": round(med, 5), "best_ms": round(best, 5),
+                "launches": launches, "launches_per_window": per, "median_ms": round(med, 5), "best_ms": round(best, 5),
                 "tflops_median": round(flop / med / 1e9, 3), "tflops_best": round(flop / best / 1e9, 3),
                 "percent_of_peak_median": round(100 * flop / med / 1e9 / PEAK_FP32_TFLOPS, 2),
                 "graph_ms_per_launch": round(gmed, 5), "graph_tflops": round(flop / gmed / 1e9, 3),
@@ -780,6 +842,8 @@ def main(argv=None) -> int:
     ap.add_argument("--format", default="bf16", choices=["bf16", "f16"], help="16-bit format of --row mixed")
     ap.add_argument("--n", type=int, default=2 ** 28, help="values summed by --row reduce")
     ap.add_argument("--all-workloads", action="store_true")
+    ap.add_argument("--ksplit-timeline", action="store_true",
+                    help="per-wave timeline of the k-split kernel at --workload (default square1000)")
     ap.add_argument("--copy-rate", action="store_true",
                     help="per-CU rate of 1 KB wave loads from L2 into LDS and into registers")
     ap.add_argument("--lds-probe", action="store_true",
@@ -801,7 +865,7 @@ def main(argv=None) -> int:
                          "matrix every launch)")
     args = ap.parse_args(argv)
     headline = not (args.all_workloads or args.shape_sweep or args.ladder or args.valu_probe or args.lds_probe
-                    or args.copy_rate or args.row != "gemm")
+                    or args.copy_rate or args.ksplit_timeline or args.row != "gemm")
     if args.settle_s is not None:
         globals()["SETTLE_S"] = max(0.0, args.settle_s)
     elif headline:
@@ -837,6 +901,8 @@ def main(argv=None) -> int:
         return bench_valu_probe(args)
     if args.lds_probe:
         return bench_lds_probe(args)
+    if args.ksplit_timeline:
+        return bench_ksplit_timeline(args)
     if args.copy_rate:
         return bench_copy_rate(args)
     if args.all_workloads:

@@ -236,6 +236,29 @@ int gemm_f32_lds_probe(int form, const int32_t *offsets, int iters, uint32_t *ou
 int gemm_f32_copy_probe(int mode, int64_t blocks, int iters, const void *src, uint32_t *out, uint64_t *cycles,
                         void *stream);
 
+/* Measurement helper, this library's own (no page defines it): gemm_f32's
+ * k-split kernel (64 x 64 tiles whose four waves each take every fourth
+ * phase of the tile; gemm_f32 runs it for square1000-sized products) on an
+ * instantiation that also records when each wave passes five points.  A, B,
+ * C and every size, leading dimension and status as for gemm_f32 with both
+ * factors as stored; C receives the same bits as gemm_f32 gives with the
+ * k-split kernel.  The problem must be one that kernel takes (M, N, K
+ * multiples of 4, K > 0, M and N > 0), else GEMM_F32_ERR_INVALID_DIM.
+ *   timeline        device buffer of timeline_words uint32 words, 4-byte
+ *                   aligned; timeline_words a positive multiple of 32
+ *                   (GEMM_F32_ERR_INVALID_DIM otherwise)
+ * Block b < timeline_words / 32 (in launch order), wave w, writes words
+ * 8 (4 b + w) .. + 7: the 100 MHz real-time counter at the wave's start,
+ * when its first phase has landed in LDS, after its last matrix instruction
+ * is issued, after the barrier before the partial tiles are added, and after
+ * its stores have completed; its shader-clock cycles between the first and
+ * the last; its phase count; b.  Other words are not written.  The
+ * instantiation waits for its stores before the last stamp, which the
+ * product kernel does not.  Enqueue-only on `stream`. */
+int gemm_f32_ksplit_timeline(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                             int64_t ldb, float *C, int64_t ldc, uint32_t *timeline, int64_t timeline_words,
+                             void *stream);
+
 /* Static, NUL-terminated description of a status code (the by-name report
  * of the chapter 2 error check cited with the codes above); "unknown status"
  * for any other number. */

@@ -92,6 +92,8 @@ def load_library():
         lib.gemm_f32_lds_probe.restype = ctypes.c_int
         lib.gemm_f32_copy_probe.argtypes = [ctypes.c_int, _i64, ctypes.c_int, _vp, _vp, _vp, _vp]
         lib.gemm_f32_copy_probe.restype = ctypes.c_int
+        lib.gemm_f32_ksplit_timeline.argtypes = sig[:-1] + [_vp, _i64, _vp]
+        lib.gemm_f32_ksplit_timeline.restype = ctypes.c_int
         lib.reduce_sum_f32_variant_noalloc.argtypes = [ctypes.c_int, _i64, _vp, _vp, _vp]
         lib.reduce_sum_f32_variant_noalloc.restype = ctypes.c_int
         lib.reduce_sum_f32_num_variants.argtypes = []
@@ -280,6 +282,13 @@ def gemm_f32_copy_probe(mode, blocks, iters, src, out, cycles, stream=None) -> N
     lib = load_library()
     _check(lib.gemm_f32_copy_probe(int(mode), int(blocks), int(iters), _addr(src), _addr(out), _addr(cycles),
                                    _stream(stream)))
+
+
+def gemm_f32_ksplit_timeline(M, N, K, A, lda, B, ldb, C, ldc, timeline, timeline_words, stream=None) -> None:
+    """gemm_f32's k-split kernel with its per-wave timeline (measurement helper)."""
+    lib = load_library()
+    _check(lib.gemm_f32_ksplit_timeline(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _addr(timeline),
+                                        int(timeline_words), _stream(stream)))
 
 
 REDUCE_DEFAULT = 4

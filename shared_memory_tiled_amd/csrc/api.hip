@@ -227,6 +227,27 @@ extern "C" int gemm_f32_copy_probe(int mode, int64_t blocks, int iters, const vo
     return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
 }
 
+// A measurement helper: gemm_f32's k-split launch on the kernel's timeline
+// instantiation (mfma_sched.hip).
+extern "C" int gemm_f32_ksplit_timeline(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                                        const float* B, int64_t ldb, float* C, int64_t ldc, uint32_t* timeline,
+                                        int64_t timeline_words, void* stream) {
+    const int st = validate(GEMM_F32_OP_N, GEMM_F32_OP_N, M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != GEMM_F32_OK) return st;
+    if (timeline == nullptr) return GEMM_F32_ERR_NULL_PTR;
+    if (misaligned(timeline)) return GEMM_F32_ERR_MISALIGNED;
+    if (timeline_words < 32 || timeline_words % 32 != 0) return GEMM_F32_ERR_INVALID_DIM;
+    GemmArgs p{(int)M, (int)N, (int)K, A, lda, B, ldb, C, ldc};
+    if (M == 0 || N == 0 || !ksplit_f32_fits(p, GEMM_F32_OP_N, GEMM_F32_OP_N)) return GEMM_F32_ERR_INVALID_DIM;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_F32_ERR_DEVICE;
+    const int64_t blocks = timeline_words / 32;
+    const hipError_t e = launch_ksplit_f32_timeline(p, reinterpret_cast<hipStream_t>(stream),
+                                                    mfma_config_group_m(kMfmaKsplitConfig), timeline,
+                                                    (int)(blocks < 0x7FFFFFFF ? blocks : 0x7FFFFFFF));
+    return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
+}
+
 // ---------------------------------------------------------------- transpose
 
 namespace {

@@ -79,6 +79,15 @@ hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b
 // below 2^31 bytes), and its launcher.
 bool ksplit_f32_fits(const GemmArgs& p, int op_a, int op_b);
 hipError_t launch_ksplit_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m);
+// Measurement helper: the same launch (factors as stored) on the kernel's
+// timeline instantiation, which also writes 8 words per wave of the first
+// timeline_blocks blocks to `timeline`.
+hipError_t launch_ksplit_f32_timeline(const GemmArgs& p, hipStream_t s, int group_m, uint32_t* timeline,
+                                      int timeline_blocks);
+// The tile-group height a configuration of launch_mfma launches with, and
+// the configuration gemm_f32 runs the k-split kernel as.
+int mfma_config_group_m(int config);
+constexpr int kMfmaKsplitConfig = 20;
 // Small products (small.hip): 16 x 16 or 32 x 32 output tiles whose k
 // groups are split over the waves of each block, operands loaded straight
 // into registers (shape 0: 16 x 16 on 4 waves, 1: 32 x 32 on 4 waves, 2: 16

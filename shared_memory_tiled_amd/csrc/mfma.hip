@@ -763,6 +763,10 @@ int mfma_pick_config(int M, int N, int K) {
     return pick;
 }
 
+int mfma_config_group_m(int config) {
+    return kConfigs[(config >= 0 && config < kNumConfigs) ? config : 0].group_m;
+}
+
 // hipErrorInvalidValue: the grid would exceed the launch limits.
 // hipErrorNotSupported: this configuration is not built for the op pair.
 hipError_t launch_mfma(const GemmArgs& p, hipStream_t s, int config, int op_a, int op_b) {

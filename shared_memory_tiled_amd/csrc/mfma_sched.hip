@@ -458,9 +458,18 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
 // phase g covering k = K - 32 (P - g) .. + 31 for P = ceil(K / 32) phases,
 // so only phase 0 can reach below k = 0, and its lanes there are pointed
 // past the end of their descriptor and copy zeros.
-template <bool KCA, bool KCB>
+//
+// TL (a measurement build, never the product's): every wave of the first
+// timeline_blocks blocks also records, at words 8 (4 b + w) .. + 7 of
+// `timeline`, the 100 MHz real-time counter at its start, when its first
+// phase has landed, after its last matrix instruction is issued, after the
+// barrier before the partial tiles are added, and once its stores have
+// completed; then its shader-clock cycles between the first and the last,
+// its phase count and its block.
+template <bool KCA, bool KCB, bool TL = false>
 __global__ __launch_bounds__(256)
-void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
+void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m, uint32_t* timeline,
+                            int timeline_blocks) {
     constexpr int FM = 2, FN = 2, BM = 64, BN = 64;
     using TA = SchedTileF32<KCA, BM, FM>;
     using TB = SchedTileF32<KCB, BN, FN>;
@@ -479,6 +488,21 @@ void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, lh = lane >> 5;
+    uint32_t tl[5] = {};
+    uint32_t tl_cycles = 0;
+    auto mark = [&](int i) __attribute__((always_inline)) {
+        if constexpr (TL) {
+            __builtin_amdgcn_sched_barrier(0);
+            tl[i] = (uint32_t)__builtin_amdgcn_s_memrealtime();
+            if (i == 0) {                     // a wave without phases: empty phase loop
+                tl_cycles = (uint32_t)__builtin_amdgcn_s_memtime();
+                tl[1] = tl[2] = tl[0];
+            }
+            if (i == 4) tl_cycles = (uint32_t)__builtin_amdgcn_s_memtime() - tl_cycles;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    mark(0);
 
     const int logical = xcd_contiguous((int)blockIdx.x, tiles_m * tiles_n);
     const int group_size = group_m * tiles_n;
@@ -645,6 +669,7 @@ void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     if (P > 0) {
         copy_first();
         wait_copies();
+        mark(1);
 #pragma unroll
         for (int i = 0; i < NREAD; ++i) read_op(0, 0, i);
         if (P > 1) {
@@ -671,6 +696,7 @@ void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         }
         steps012(no{}, 0, 0);
         step(1, no{}, 0, c0{}, c0{}, 0, 0);
+        mark(2);
     }
 
     // Partial tiles.  Wave v adds, in wave order, block row v / 2,
@@ -703,6 +729,7 @@ void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
                 }
     }
     __syncthreads();
+    mark(3);
     const int bi = w >> 1, r0 = 8 * (w & 1);
     floatx4 sum[FN][2];
 #pragma unroll
@@ -734,13 +761,24 @@ void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
                 if (n0 + 32 * j + li < p.N) crow[32 * j + li] = sum[j][rr >> 2][rr & 3];
         }
     }
+    if constexpr (TL) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        mark(4);
+        if (lane == 0 && (int)blockIdx.x < timeline_blocks) {
+            uint32_t* o = timeline + 8 * (4 * (int64_t)blockIdx.x + w);
+            for (int i = 0; i < 5; ++i) o[i] = tl[i];
+            o[5] = tl_cycles;
+            o[6] = (uint32_t)P;
+            o[7] = blockIdx.x;
+        }
+    }
 }
 
 template <bool KCA, bool KCB>
 hipError_t launch_ksplit_f32_kernel(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
                                     unsigned blocks) {
     hipLaunchKernelGGL((gemm_f32_ksplit_kernel<KCA, KCB>), dim3(blocks), dim3(256), 0, s, p, tiles_m, tiles_n,
-                       group_m);
+                       group_m, nullptr, 0);
     return hipGetLastError();
 }
 
@@ -786,6 +824,17 @@ bool ksplit_f32_fits(const GemmArgs& p, int op_a, int op_b) {
     const int64_t a_rows = op_a ? p.K : p.M, b_rows = op_b ? p.N : p.K;
     const int64_t lim = (int64_t)1 << 31;
     return 4 * (a_rows + 256) * p.lda < lim && 4 * (b_rows + 256) * p.ldb < lim;
+}
+
+// The product's k-split launch (A and B as stored) on its measurement
+// instantiation, which also records the timeline described at the kernel.
+hipError_t launch_ksplit_f32_timeline(const GemmArgs& p, hipStream_t s, int group_m, uint32_t* timeline,
+                                      int timeline_blocks) {
+    const int tiles_m = ceil_div(p.M, 64), tiles_n = ceil_div(p.N, 64);
+    const unsigned blocks = (unsigned)((int64_t)tiles_m * tiles_n);
+    hipLaunchKernelGGL((gemm_f32_ksplit_kernel<true, false, true>), dim3(blocks), dim3(256), 0, s, p, tiles_m,
+                       tiles_n, group_m, timeline, timeline_blocks);
+    return hipGetLastError();
 }
 
 hipError_t launch_ksplit_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m) {

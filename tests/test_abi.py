@@ -239,6 +239,20 @@ def test_copy_probe_validation_without_launch(lib, args, code):
     assert lib.gemm_f32_copy_probe(*args, None) == declared_codes()[code]
 
 
+@pytest.mark.parametrize("args,code", [
+    ((64, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 16), "GEMM_F32_ERR_INVALID_DIM"),
+    ((64, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 48), "GEMM_F32_ERR_INVALID_DIM"),
+    ((64, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, None, 64), "GEMM_F32_ERR_NULL_PTR"),
+    ((64, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, FAKE + 2, 64), "GEMM_F32_ERR_MISALIGNED"),
+    ((64, 64, 6, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 64), "GEMM_F32_ERR_INVALID_DIM"),   # K % 4 != 0
+    ((0, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 64), "GEMM_F32_ERR_INVALID_DIM"),
+    ((64, 64, 64, FAKE, 32, FAKE, 64, FAKE, 64, FAKE, 64), "GEMM_F32_ERR_INVALID_LD"),
+    ((64, 64, 64, None, 64, FAKE, 64, FAKE, 64, FAKE, 64), "GEMM_F32_ERR_NULL_PTR"),
+])
+def test_ksplit_timeline_validation_without_launch(lib, args, code):
+    assert lib.gemm_f32_ksplit_timeline(*args, None) == declared_codes()[code]
+
+
 def test_reduce_noalloc_scratch_limit(binding):
     """The declared scratch size, and the largest n each tree version takes
     in it: exactly where the workspace the version needs passes 1 MiB."""

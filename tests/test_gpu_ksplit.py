@@ -216,3 +216,30 @@ def test_planted_infinity_stays_in_its_row_or_column(ops, factor):
     assert np.array_equal(bad, want), f"non-finite entries outside row/column: {np.argwhere(bad & ~want)[:4]}"
     Cref, S = oracle.gemm(prob.A.view, prob.B.view, op_a=op_a, op_b=op_b, threads=8)
     check_close(C[~want], Cref[~want], S[~want], f"planted {factor} {op_a}{op_b}")
+
+
+@pytest.mark.parametrize("shape", [(1000, 1000, 1000), (200, 136, 388), (64, 64, 4)])
+def test_timeline_helper_runs_the_same_kernel(shape):
+    """The measurement helper's instantiation gives gemm_f32's bits, and every
+    wave's five stamps come in order, with its phase count and block."""
+    M, N, K = shape
+    assert default_name(M, N, K) == KS or shape != (1000, 1000, 1000)
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    A = torch.rand((M, K), device="cuda", generator=gen) * 2 - 1
+    B = torch.rand((K, N), device="cuda", generator=gen) * 2 - 1
+    ref = torch.empty((M, N), device="cuda")
+    out = torch.empty((M, N), device="cuda")
+    binding.gemm_f32_variant(variant_number(KS), M, N, K, A, K, B, N, ref, N)
+    blocks = ((M + 63) // 64) * ((N + 63) // 64)
+    tl = torch.zeros(32 * blocks, dtype=torch.int32, device="cuda")
+    say(f"ksplit timeline {shape}")
+    binding.gemm_f32_ksplit_timeline(M, N, K, A, K, B, N, out, N, tl, tl.numel())
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    rows = tl.view(-1, 8).cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    nph = (K + 31) // 32
+    for i, r in enumerate(rows):
+        steps = [(r[t + 1] - r[t]) & 0xFFFFFFFF for t in range(4)]
+        assert all(0 <= d < 100_000_000 for d in steps), (i, r)          # under a second each
+        assert r[6] == (max(nph - 1 - i % 4, -1) // 4 + 1 if nph > i % 4 else 0), (i, r)
+        assert r[7] == i // 4
