@@ -393,10 +393,11 @@ int reduce_sum_f32_variant_noalloc(int variant, int64_t n, const float *x, float
  * gemm_mixed_op's choice once there are 128 tiles of 256 x 256),
  * mixed256x256_bk64_w4_sched (the same schedule on v_mfma_f32_32x32x16) and
  * mixed256x256_bk32_w4_wide4stage (16x16x32 with four 32-deep LDS stages) --
- * take K a multiple of 8, N even (M too for A stored transposed in
- * gemm_mixed_op, and not N for B stored transposed), 4-byte aligned operands
- * with even leading dimensions and operands under 2^31 bytes; edge tiles run
- * whole and store only inside C, and k positions past K copy zeros.  Other
+ * take K a multiple of 8 (mixed256x256_bk64_w4_wide: K even), N even (M
+ * too for A stored transposed in gemm_mixed_op, and not N for B stored
+ * transposed), 4-byte aligned operands with even leading dimensions and
+ * operands under 2^31 bytes; edge tiles run whole and store only inside C,
+ * and k positions past K contribute zeros.  Other
  * problems given to them run mixed256x256_bk64_w2x4_directAB (for the
  * 32 x 32 x 16 configuration the same tiles and summation order, the same
  * bits; for the 16 x 16 x 32 ones another instruction, other bits within the

@@ -45,8 +45,10 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
 bool ksplit16_fits(const Gemm16Args& p, int op_a, int op_b);
 hipError_t launch_ksplit16(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b);
 // The scheduled 256 x 256 kernel on the 16 x 16 x 32 instruction
-// (mfma16_wide.hip); it takes the problems the 32 x 32 x 16 scheduled kernel
-// takes (the caller checks), with tile-row groups of group_m.
+// (mfma16_wide.hip): whether it takes the problem (those of the 32 x 32 x 16
+// scheduled kernel, with any even K), and its launcher (the caller checks),
+// with tile-row groups of group_m.
+bool wide_fits(const Gemm16Args& p, int op_a, int op_b);
 hipError_t launch_wide16(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m);
 // The same product with four 32-deep LDS stages (mfma16_wide4.hip), as
 // stored (A k-contiguous, B mn-contiguous) only.

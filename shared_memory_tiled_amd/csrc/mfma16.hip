@@ -1095,7 +1095,7 @@ hipError_t launch_ksplit16_cfg(const Gemm16Args& p, hipStream_t s, int tiles_m, 
 template <int FMT>
 hipError_t launch_wide_cfg(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int /*group_m*/,
                            unsigned blocks) {
-    if (!sched_fits(p, 0, 0))
+    if (!wide_fits(p, 0, 0))
         return launch16<FMT, 256, 256, 2, 4, true, true, true>(p, s, tiles_m, tiles_n, kDirectGroupM, blocks);
     return launch_wide16(p, s, FMT, 0, 0, kSchedGroupM);
 }
@@ -1185,7 +1185,7 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
     const int tiles_m = ceil_div(p.M, tile), tiles_n = ceil_div(p.N, tile);
     const int64_t blocks = (int64_t)tiles_m * tiles_n;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    if (big && sched_fits(p, op_a, op_b)) return launch_wide16(p, s, format, op_a, op_b, kSchedGroupM);
+    if (big && wide_fits(p, op_a, op_b)) return launch_wide16(p, s, format, op_a, op_b, kSchedGroupM);
     Launch16 fn;
     if (big) fn = format ? op_launcher<1, 256, 256, 2, 4>(op_a, op_b, vec) : op_launcher<0, 256, 256, 2, 4>(op_a, op_b, vec);
     else fn = format ? op_launcher<1, 128, 128, 2, 2>(op_a, op_b, vec) : op_launcher<0, 128, 128, 2, 2>(op_a, op_b, vec);

@@ -48,7 +48,9 @@
 // take per-lane offsets with the phase folded in and a scalar offset of 0);
 // the column overhang of an MC factor reads the next row (only C entries
 // outside the matrix use it) or, in the last row, its dwords up to the end
-// and zeros past it.
+// and zeros past it.  K need only be even: the one chunk per row of a KC
+// factor that straddles K is copied whole, and its values past K are zeroed
+// in the last phase's fragments.
 //
 // The k order inside each instruction (k = 32 s + 8 (l / 16) + e of lane l)
 // does not depend on how a factor is stored, so the four op pairs give the
@@ -339,9 +341,31 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
         phase(ph, no{}, no{});
         ++ph;
     }
+    // The last phase.  With K not a multiple of 8, the 16-byte chunk of a
+    // k-contiguous factor that holds k = K - 1 also holds values past K (the
+    // row's next elements, or padding); lane l's fragments of step s hold
+    // k = klast + 32 s + 8 (l / 16) + e, e = 0..7, and those at k >= K are
+    // set to zero here, so that they meet zeros of the other factor (its
+    // rows at k >= K copied as zeros, or its own fragments so masked).
+    auto mask_last = [&](int t, int s) __attribute__((always_inline)) {
+        if constexpr (KCA || KCB) {
+            const int kv = p.K - klast - 32 * s - 8 * (lane >> 4);   // values of the chunk below K
+            u32x4 m;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                m[d] = (2 * d < kv ? 0x0000FFFFu : 0u) | (2 * d + 1 < kv ? 0xFFFF0000u : 0u);
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                if constexpr (KCA) aq[t][f] &= m;
+                if constexpr (KCB) bq[t][f] &= m;
+            }
+        }
+    };
     wait_set(0);
+    mask_last(0, 0);
     step(0, yes{}, 1, no{}, 0, 0, no{});
     wait_set(1);
+    mask_last(1, 1);
     step(1, no{}, 0, no{}, 0, 0, no{});
 
     // Guarded store (edge tiles run whole and store only what lies inside
@@ -372,6 +396,23 @@ hipError_t launch_wide_kernel(const Gemm16Args& p, hipStream_t s, int tiles_m, i
 }
 
 }  // namespace
+
+// K even and > 0 (the last phase's values past K are masked), an
+// mn-contiguous factor's width (M for A stored transposed, N for B as
+// stored) even, 4-byte aligned bases, even leading dimensions, and stored
+// factors below 2^31 bytes with a tile's overhang.  Every descriptor then
+// ends on a dword boundary: the range check is per dword, so with K odd the
+// last row's last value would share a dword with the bytes past the end and
+// read as zero.
+bool wide_fits(const Gemm16Args& p, int op_a, int op_b) {
+    const bool vec = ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 3) == 0 &&
+                     (p.lda % 2) == 0 && (p.ldb % 2) == 0;
+    const int64_t a_rows = op_a ? p.K : p.M, b_rows = op_b ? p.N : p.K;
+    const bool widths = (op_a == 0 || p.M % 2 == 0) && (op_b != 0 || p.N % 2 == 0);
+    return vec && widths && p.K > 0 && p.K % 2 == 0 && p.M > 0 && p.N > 0 &&
+           2 * (a_rows + 256) * p.lda < (1ll << 31) &&
+           2 * (b_rows + 256) * p.ldb < (1ll << 31);
+}
 
 hipError_t launch_wide16(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m) {
     const int tiles_m = ceil_div(p.M, 256), tiles_n = ceil_div(p.N, 256);

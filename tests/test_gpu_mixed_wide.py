@@ -1,7 +1,8 @@
 """The scheduled 256 x 256 kernel on v_mfma_f32_16x16x32 (configuration
 mixed256x256_bk64_w4_wide) against the 16-bit oracle: exact on integer
 inputs, within 1e-5 S on uniform ones; edge tiles on both sides, K % 64 in
-{0, 8, 40, ...} (a last phase reaching past K), one to sixteen phases,
+{0, 8, 40, ...} (a last phase reaching past K) and K % 8 != 0 (the last
+chunk of a k-contiguous factor masked), one to sixteen phases,
 offset views with padding, and 40 rows of NaN after every factor (a copy
 that read memory past a factor instead of taking zeros would poison a stored
 result); every op pair through gemm_mixed_op, with the bits of the plain
@@ -81,6 +82,31 @@ def test_variant_against_oracle(fmt, dist):
         check_padding_untouched(C)
 
 
+# K not a multiple of 8: the chunk of A (k-contiguous) that holds k = K - 1
+# also holds values past K, which the last phase masks; (M, N, K, pad of A's
+# leading dimension): K % 64 in {4, 10, 44, 46}, the straddling chunk in step
+# 0 or step 1 of the last phase; then odd K with an even leading dimension,
+# which the configuration hands to its fallback (the last row's last value
+# would share a dword with the bytes past the descriptor's end)
+RAGGED = [(256, 256, 4, 4), (300, 520, 138, 4), (520, 1030, 1004, 4), (770, 258, 46, 6), (1024, 768, 517, 5),
+          (258, 516, 63, 3)]
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.parametrize("dist", ["int", "uniform"])
+def test_variant_ragged_k(fmt, dist):
+    v = variant_number(WIDE)
+    for (M, N, K, pa) in RAGGED:
+        say(f"wide16 ragged K {fmt} {dist} {(M, N, K)}")
+        C, ref, S = run(fmt, "N", "N", M, N, K, dist, [M, N, K, 7], pad=(pa, 6, 2), variant=v)
+        what = f"{WIDE} ragged {fmt} {dist} {(M, N, K)}"
+        if dist == "int":
+            check_exact(C.view, ref, what)
+        else:
+            check_close(C.view, ref, S, what)
+        check_padding_untouched(C)
+
+
 def test_variant_repeats_bit_for_bit():
     """Fixed k order: a second call gives the same bits."""
     v = variant_number(WIDE)
@@ -95,8 +121,10 @@ def test_variant_repeats_bit_for_bit():
 
 
 OPS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
-# shapes gemm_mixed_op gives to the kernel (at least 128 tiles of 256 x 256)
-OP_SHAPES = [(3072, 2816, 72), (2824, 3080, 136)]
+# shapes gemm_mixed_op gives to the kernel (at least 128 tiles of 256 x 256);
+# the last two with K % 8 != 0 (a k-contiguous factor's last chunk straddles
+# K in step 0, then step 1, of the last phase)
+OP_SHAPES = [(3072, 2816, 72), (2824, 3080, 136), (2824, 3080, 76), (3072, 2816, 110)]
 
 
 @pytest.mark.parametrize("ops", OPS, ids=["".join(o) for o in OPS])
@@ -118,12 +146,14 @@ def test_op_pairs_against_oracle(ops, fmt):
             check_padding_untouched(C)
 
 
+@pytest.mark.parametrize("K", [1000, 1002])
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
-def test_op_pairs_bit_identical_on_transposed_copies(fmt):
+def test_op_pairs_bit_identical_on_transposed_copies(fmt, K):
     """The k order inside each instruction does not depend on how a factor
     is stored: gemm_mixed_op on explicitly transposed copies gives the bits
-    of the plain product."""
-    M, N, K = 3072, 2816, 1000
+    of the plain product (also with K % 8 != 0, where a k-contiguous
+    factor's last chunk is masked)."""
+    M, N = 3072, 2816
     gen = torch.Generator(device="cuda").manual_seed(23)
     dt = torch.bfloat16 if fmt == "bf16" else torch.float16
     X = (torch.rand((M, K), device="cuda", generator=gen) * 2 - 1).to(dt)
