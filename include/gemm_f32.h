@@ -388,7 +388,11 @@ int reduce_sum_f32_variant_noalloc(int variant, int64_t n, const float *x, float
  * 32-deep phase (mixed64x64_bk32_w4_ksplit, v_mfma_f32_16x16x32; partial
  * tiles added in wave order, so every op pair gives the same bits); it needs
  * what the scheduled configurations need (below), and a problem it does not
- * take runs the element-wise 64 x 64 kernel.  The scheduled configurations
+ * take runs the element-wise 64 x 64 kernel.  With 128 to 256 tiles of
+ * 128 x 128 and K >= 1024 (a multiple of 8) they take the same split on
+ * 128 x 128 tiles (mixed128x128_bk32_w4_ksplit), with the same needs; a
+ * problem it does not take runs mixed128x128_bk64_w2x2_directAB (aligned) or
+ * the element-wise 128 x 128 kernel.  The scheduled configurations
  * -- mixed256x256_bk64_w4_wide (v_mfma_f32_16x16x32; gemm_mixed's and
  * gemm_mixed_op's choice once there are 128 tiles of 256 x 256),
  * mixed256x256_bk64_w4_sched (the same schedule on v_mfma_f32_32x32x16) and

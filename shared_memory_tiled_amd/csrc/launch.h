@@ -44,6 +44,11 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
 // stored transposed).
 bool ksplit16_fits(const Gemm16Args& p, int op_a, int op_b);
 hipError_t launch_ksplit16(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b);
+// The same split on 128 x 128 tiles, for a few hundred of them
+// (mfma16_ksplit128.hip): whether it takes the problem (as above), and its
+// launcher, with tile-row groups of group_m.
+bool ksplit128_fits(const Gemm16Args& p, int op_a, int op_b);
+hipError_t launch_ksplit128(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m);
 // The scheduled 256 x 256 kernel on the 16 x 16 x 32 instruction
 // (mfma16_wide.hip): whether it takes the problem (those of the 32 x 32 x 16
 // scheduled kernel, with any even K), and its launcher (the caller checks),

@@ -1089,6 +1089,18 @@ hipError_t launch_ksplit16_cfg(const Gemm16Args& p, hipStream_t s, int tiles_m, 
     return launch_ksplit16(p, s, FMT, 0, 0);
 }
 
+// Configuration 12 (128 x 128 tiles whose four waves split the phases,
+// mfma16_ksplit128.hip) where it takes the problem; else the 128 x 128
+// tiles of configuration 7.
+constexpr int kKsplit128GroupM = 8;
+template <int FMT>
+hipError_t launch_ksplit128_cfg(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                                unsigned blocks) {
+    if (!ksplit128_fits(p, 0, 0))
+        return launch16<FMT, 128, 128, 2, 2, true, true, true>(p, s, tiles_m, tiles_n, group_m, blocks);
+    return launch_ksplit128(p, s, FMT, 0, 0, kKsplit128GroupM);
+}
+
 // Configuration 10 (the scheduled kernel on v_mfma_f32_16x16x32,
 // mfma16_wide.hip) where it takes the problem; else the 8-wave kernel, as
 // for configuration 8 (its bits differ: another instruction).
@@ -1137,11 +1149,17 @@ const MixedConfig kMixed[] = {
     {"mixed256x256_bk32_w4_wide4stage", 256, 256, kSchedGroupM,
      {{launch16<0, 256, 256, 2, 4, false, false, false>, launch_wide4_cfg<0>},
       {launch16<1, 256, 256, 2, 4, false, false, false>, launch_wide4_cfg<1>}}},
+    // four waves, each the whole 128 x 128 tile over every fourth phase;
+    // misaligned operands: the element-wise 128 x 128 kernel
+    {"mixed128x128_bk32_w4_ksplit", 128, 128, kKsplit128GroupM,
+     {{launch16<0, 128, 128, 2, 2, false, false, false>, launch_ksplit128_cfg<0>},
+      {launch16<1, 128, 128, 2, 2, false, false, false>, launch_ksplit128_cfg<1>}}},
 };
 #undef MIXED
 constexpr int kNumMixed = (int)(sizeof(kMixed) / sizeof(kMixed[0]));
 constexpr int kKsplitConfig = 9;          // mixed64x64_bk32_w4_ksplit
 constexpr int kWideConfig = 10;           // mixed256x256_bk64_w4_wide
+constexpr int kKsplit128Config = 12;      // mixed128x128_bk32_w4_ksplit
 
 // op kernels, chosen by tile, op pair and load path
 template <int FMT, int BM, int BN, int WM, int WN, bool KCA, bool KCB, bool VEC>
@@ -1178,8 +1196,10 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
     const bool vec = ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 3) == 0 &&
                      (p.lda % 2) == 0 && (p.ldb % 2) == 0;
     const int64_t t256 = (int64_t)ceil_div(p.M, 256) * ceil_div(p.N, 256);
-    if (mixed_pick_config(p.M, p.N, p.K) == kKsplitConfig && ksplit16_fits(p, op_a, op_b))
-        return launch_ksplit16(p, s, format, op_a, op_b);
+    const int pick = mixed_pick_config(p.M, p.N, p.K);
+    if (pick == kKsplitConfig && ksplit16_fits(p, op_a, op_b)) return launch_ksplit16(p, s, format, op_a, op_b);
+    if (pick == kKsplit128Config && ksplit128_fits(p, op_a, op_b))
+        return launch_ksplit128(p, s, format, op_a, op_b, kKsplit128GroupM);
     const bool big = t256 >= 128;
     const int tile = big ? 256 : 128;
     const int tiles_m = ceil_div(p.M, tile), tiles_n = ceil_div(p.N, tile);
@@ -1205,13 +1225,19 @@ const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed
 // four waves split the phases (mfma16_ksplit.hip; measured bf16: 1024^2 x
 // 4096 479 against 186 TFLOP/s on the 128 x 128 tiles, 1000^3 234 against
 // 53, 1024^3 297 against 160; 1536^3, with 144 tiles of 128 x 128, 321
-// against 339).  Else 128 x 128 tiles with both factors copied straight into
-// LDS from 128 of them (64 for K of at least 2048), else 64 x 64 tiles.
+// against 339).  Else, with at most 256 tiles of 128 x 128 (one per CU) and
+// K of at least 1024 (a multiple of 8), 128 x 128 tiles whose four waves
+// split the phases (mfma16_ksplit128.hip; measured bf16: 2048^3 697 against
+// 586 TFLOP/s on the 128 x 128 tiles with direct copies, 1536^3 355 against
+// 344; with 400 tiles (2560^3) or K = 256 they lose).  Else 128 x 128 tiles
+// with both factors copied straight into LDS from 128 of them (64 for K of
+// at least 2048), else 64 x 64 tiles.
 int mixed_pick_config(int M, int N, int K) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
     if (t256 >= 128) return kWideConfig;
     if (t128 < 128 && K % 8 == 0 && K > 0) return kKsplitConfig;
+    if (t128 <= 256 && K >= 1024 && K % 8 == 0) return kKsplit128Config;
     if (t128 >= 128 || (t128 >= 64 && K >= 2048)) return 7;
     return 3;
 }

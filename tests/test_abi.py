@@ -410,8 +410,10 @@ def test_default_variant_choices(binding):
         (3072, 3072, 3072): "mixed256x256_bk64_w4_wide",          # 144 tiles of 256
         (4100, 4100, 4096): "mixed256x256_bk64_w4_wide",          # edge tiles, N even
         (2560, 2560, 2560): "mixed128x128_bk64_w2x2_directAB",    # 100 tiles of 256, 400 of 128
-        (2048, 2048, 2048): "mixed128x128_bk64_w2x2_directAB",
-        (1536, 1536, 1536): "mixed128x128_bk64_w2x2_directAB",    # 144 tiles of 128
+        (2048, 2048, 2048): "mixed128x128_bk32_w4_ksplit",        # 256 tiles of 128, long K
+        (1536, 1536, 1536): "mixed128x128_bk32_w4_ksplit",        # 144 tiles of 128
+        (2048, 2048, 256): "mixed128x128_bk64_w2x2_directAB",     # 256 tiles of 128, short K
+        (2048, 2048, 2044): "mixed128x128_bk64_w2x2_directAB",    # K % 8 = 4
         (1024, 1024, 4096): "mixed64x64_bk32_w4_ksplit",          # 64 tiles of 128: k-split
         (1024, 1024, 1024): "mixed64x64_bk32_w4_ksplit",
         (1000, 1000, 1000): "mixed64x64_bk32_w4_ksplit",

@@ -966,3 +966,174 @@ def test_wide4_copies_never_depend_on_the_scalar_offset(kc, shape):
                         wants_zero = b is None or k >= K or (kc and mn >= ext)
                         in_matrix = b is not None and ((k + 7 < K and mn < ext) if kc else (k < K and mn + 7 < ext))
                         _check_copy(voff, soff, nrec, 16, wants_zero, in_matrix, what)
+
+
+def ks128_copy(kc, j, lane):
+    """(stored row, logical chunk, LDS byte of the lane's 16 bytes) of lane
+    `lane` of copy j (0..7) in the 16-bit k-split kernel's 128 x 32 tile:
+    KC rows of 32 k (4 chunks of 8) at 64 bytes, chunk c of row r at
+    c ^ (2 ((r / 8) mod 2)), 16 rows per 1 KB copy; MC k rows of 128 values
+    (16 chunks) in groups of four, group Q at byte 1056 Q, k row
+    r = 8 g + 4 h + q (g = 0..3, h = 0..1, q = 0..3) in group
+    q + 4 (g mod 2) at position 2 (g / 2) + h, one group per copy."""
+    if kc:
+        row = 16 * j + lane // 4
+        return row, (lane % 4) ^ (((row >> 3) & 1) << 1), 1024 * j + 16 * lane
+    pos, chunk = lane // 16, lane % 16
+    q, g = j & 3, 2 * (pos >> 1) + (j >> 2)
+    return 8 * g + 4 * (pos & 1) + q, chunk, 1056 * j + 16 * lane
+
+
+def ks128_read(kc, f, i, lane):
+    """(per-lane base, instruction offset) of read i of block f."""
+    j, g = lane & 15, lane >> 4
+    if kc:
+        return 64 * j + 16 * (g ^ (((j >> 3) & 1) << 1)), 1024 * f
+    q, jj = j >> 2, j & 3
+    return 1056 * (q + 4 * (g & 1)) + 512 * (g >> 1) + 8 * jj, 256 * i + 32 * f
+
+
+@pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
+def test_ksplit16_128_kernel_layout(kc):
+    """The 128 x 128 k-split kernel's tile (128 mn x 32 k per stage),
+    restated: the eight 1 KB copies fill the stage exactly once (the
+    mn-contiguous stage's 32-byte pads after each group of four rows
+    aside); every lane's fragment reads (one per-lane base per factor plus
+    an instruction offset; 128-bit for a k-contiguous tile, two
+    ds_read_b64_tr_b16 for an mn-contiguous one) deliver the operands
+    v_mfma_f32_16x16x32 needs -- for block f, lane l supplies
+    op(X)[16 f + l % 16][8 (l / 16) + e], e = 0..7 -- and the reads are free
+    of bank conflicts on 64 banks (128-bit: the measured quad grouping;
+    64-bit: 32 lanes per cycle, 8 k rows in 8 groups 1056 bytes apart)."""
+    where = {}                                   # LDS byte of an element -> (mn, k)
+    for j in range(8):
+        for lane in range(64):
+            row, c, dst = ks128_copy(kc, j, lane)
+            for e in range(8):
+                assert dst + 2 * e not in where
+                where[dst + 2 * e] = (row, 8 * c + e) if kc else (8 * c + e, row)
+    assert len(where) == 128 * 32
+    size = 8192 if kc else 8 * 1056
+    assert max(where) < size
+    for f in range(8):
+        if kc:
+            words = []
+            for lane in range(64):
+                base, imm = ks128_read(True, f, 0, lane)
+                addr = base + imm
+                assert addr % 16 == 0 and imm < 1 << 16
+                got = [where[addr + 2 * e] for e in range(8)]
+                assert got == [(16 * f + lane % 16, 8 * (lane // 16) + e) for e in range(8)], (f, lane)
+                words.append(addr // 4)
+            assert degree128(words) == 1
+        else:
+            vals = {lane: [] for lane in range(64)}
+            for i in range(2):
+                addrs = []
+                for lane in range(64):
+                    base, imm = ks128_read(False, f, i, lane)
+                    assert (base + imm) % 8 == 0 and imm < 1 << 16
+                    addrs.append(base + imm)
+                for lane in range(64):
+                    grp, i16 = lane - lane % 16, lane % 16
+                    for e in range(4):
+                        src = addrs[grp + 4 * e + i16 // 4]
+                        vals[lane].append(where[src + 2 * (i16 % 4)])
+                assert degree([a // 4 for a in addrs], 2, 64, 32) == 1
+            for lane in range(64):
+                assert vals[lane] == [(16 * f + lane % 16, 8 * (lane // 16) + e) for e in range(8)], (f, lane)
+
+
+def ks128_positions(K, w):
+    """The 128 x 128 k-split kernel's order for wave w: (P, P2, phase at
+    each position, or None for a position that copies zeros)."""
+    nph = -(-K // 32)
+    P = (nph - 1 - w) // 4 + 1 if nph > w else 0
+    odd = P & 1
+    P2 = max(2, P + odd)
+    at = []
+    for s in range(P2):
+        lp = P - 1 if s == 0 else s - 1 - odd
+        at.append(lp if 0 <= lp < P else None)
+    return P, P2, at
+
+
+@pytest.mark.parametrize("K", [8, 32, 40, 96, 128, 160, 200, 256, 288, 1000, 1024, 1536, 2048, 2056])
+def test_ksplit16_128_positions_cover_each_phase_once(K):
+    """Every phase of every wave runs at exactly one position; position 0
+    holds the wave's last phase, phase 0 sits at position 1 or 2 and every
+    position from 4 on holds a phase in 2 .. P - 2 (so the loop's copies,
+    which take the phase in the scalar offset, never meet the first or the
+    last phase, nor a position that copies zeros); the count is even."""
+    nph = -(-K // 32)
+    seen = []
+    for w in range(4):
+        P, P2, at = ks128_positions(K, w)
+        assert P2 % 2 == 0 and P2 >= 2
+        phases = [lp for lp in at if lp is not None]
+        assert sorted(phases) == list(range(P))
+        if P:
+            assert at[0] == P - 1
+        if P >= 2:
+            assert at.index(0) in (1, 2)
+        for s in range(4, P2):
+            assert at[s] is not None and 2 <= at[s] <= P - 2, (K, w, s)
+        seen += [4 * lp + w for lp in phases]
+    assert sorted(seen) == list(range(nph))
+
+
+@pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
+@pytest.mark.parametrize("shape", [(2048, 2048, 2048), (300, 1000, 304), (128, 8, 128), (1000, 1544, 1002),
+                                   (258, 200, 2600)])
+def test_ksplit16_128_copies_never_depend_on_the_scalar_offset(kc, shape):
+    """128 x 128 k-split kernel: positions 0 .. 3 copy with the phase folded
+    into each lane's offset (scalar offset 0), lanes below k = 0 or at
+    k >= K, chunks of an MC factor wholly past its last column and positions
+    without a phase past the end; positions 4 .. P2 - 1 take the phase in
+    the scalar offset (phases 2 .. P - 2 only), with MC chunks past the last
+    column past the end by their own offset.  Only a chunk of the MC
+    factor's last row across its last column may straddle the descriptor's
+    end, by its per-lane offset alone (the last phase is at position 0) and
+    by whole dwords (the width is even).  Positions past P2 - 1 are copied
+    but never read."""
+    ext, K, ld_mn = shape
+    assert K % 8 == 0 and ext % 2 == 0
+    rows, cols = (ext, K) if kc else (K, ext)
+    ld = (K + 8) if kc else max(ld_mn, ext)
+    nrec = 2 * ((rows - 1) * ld + cols)
+    nph = -(-K // 32)
+    kbase = K - 32 * nph
+    for mn0 in sorted({0, (ext - 1) // 128 * 128}):
+        for w in range(4):
+            P, P2, at = ks128_positions(K, w)
+            odd = P & 1
+            for j in range(8):
+                for lane in range(64):
+                    row, c, _ = ks128_copy(kc, j, lane)
+                    kl, mn = (8 * c, mn0 + row) if kc else (row, mn0 + 8 * c)
+                    doff = 2 * (mn * ld + kl) if kc else 2 * (kl * ld + mn)
+                    if not kc and mn >= ext:
+                        doff = PAST_END
+                    for s in range(P2):
+                        lp = at[s]
+                        what = (kc, shape, mn0, w, j, lane, s)
+                        if s < 4:
+                            k0 = kbase + 32 * (4 * (P - 1 if s == 0 else s - 1 - odd) + w)
+                            k = k0 + kl
+                            pb = 2 * k0 if kc else 2 * k0 * ld
+                            inside = lp is not None and 0 <= k < K and doff != PAST_END
+                            voff, soff = (doff + pb if inside else PAST_END), 0
+                        else:
+                            k0 = kbase + 32 * (4 * (s - 1 - odd) + w)
+                            k = k0 + kl
+                            voff, soff = doff, (2 * k0 if kc else 2 * k0 * ld)
+                            assert lp is not None and 0 <= k0 and k0 + 31 < K, what
+                        if lp is None:
+                            assert voff >= nrec, what
+                            continue
+                        if not kc and 0 <= k < K and mn < ext < mn + 8 and voff < nrec < voff + soff + 16:
+                            assert k == K - 1 and soff == 0 and (nrec - voff) % 4 == 0, what
+                            continue
+                        wants_zero = k < 0 or k >= K or mn >= ext
+                        in_matrix = 0 <= k < K and (mn < ext if kc else mn + 7 < ext)
+                        _check_copy(voff, soff, nrec, 16, wants_zero, in_matrix, what)
