@@ -49,6 +49,7 @@ const Diagnostic kDiagnostics[] = {
     {"mfma16x16_w4_small", 3, 21},
     {"mfma32x32_w4_small", 3, 22},
     {"mfma16x16_w8_small", 3, 23},
+    {"mfma96x96_bk16_w1x1_k4_sched", 3, 24},
 };
 constexpr int kNumDiagnostics = (int)(sizeof(kDiagnostics) / sizeof(kDiagnostics[0]));
 

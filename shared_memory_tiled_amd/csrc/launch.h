@@ -86,6 +86,11 @@ hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b
 // below 2^31 bytes), and its launcher.
 bool ksplit_f32_fits(const GemmArgs& p, int op_a, int op_b);
 hipError_t launch_ksplit_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m);
+// Four waves splitting the phases of one 96 x 96 tile (mfma_ksplit96.hip):
+// whether it takes the problem (K, M and N multiples of 4, stored factors
+// below 2^31 bytes), and its launcher.
+bool ksplit96_f32_fits(const GemmArgs& p, int op_a, int op_b);
+hipError_t launch_ksplit96_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m);
 // Measurement helper: the same launch (factors as stored) on the kernel's
 // timeline instantiation, which also writes 8 words per wave of the first
 // timeline_blocks blocks to `timeline`.

@@ -605,6 +605,16 @@ hipError_t launch_ksplit_or_splitk(const GemmArgs& p, hipStream_t s, int tiles_m
     if (ksplit_f32_fits(p, TRA, TRB)) return launch_ksplit_f32(p, s, TRA, TRB, group_m);
     return launch_splitk<64, 64, 32, 4, TRA, TRB>(p, s, tiles_m, tiles_n, group_m, blocks);
 }
+// Four waves splitting the phases of one 96 x 96 tile where it takes the
+// problem, else configuration 20.
+template <bool TRA, bool TRB>
+hipError_t launch_ksplit96_or_ksplit(const GemmArgs& p, hipStream_t s, int, int, int group_m, unsigned) {
+    if (ksplit96_f32_fits(p, TRA, TRB)) return launch_ksplit96_f32(p, s, TRA, TRB, group_m);
+    return launch_mfma(p, s, 20, TRA, TRB);
+}
+#define KSPLIT96_OPS                                                                          \
+    {launch_ksplit96_or_ksplit<false, false>, launch_ksplit96_or_ksplit<false, true>,          \
+     launch_ksplit96_or_ksplit<true, false>, launch_ksplit96_or_ksplit<true, true>}
 #define KSPLIT_OPS                                                                       \
     {launch_ksplit_or_splitk<false, false>, launch_ksplit_or_splitk<false, true>,          \
      launch_ksplit_or_splitk<true, false>, launch_ksplit_or_splitk<true, true>}
@@ -668,6 +678,8 @@ const MfmaConfig kConfigs[] = {
     {"mfma16x16_w4_small", 16, 16, 256, 8, SMALL_OPS(0)},
     {"mfma32x32_w4_small", 32, 32, 256, 8, SMALL_OPS(1)},
     {"mfma16x16_w8_small", 16, 16, 512, 8, SMALL_OPS(2)},
+    // four waves, each the whole 96 x 96 tile over every fourth 16-deep phase
+    {"mfma96x96_bk16_w1x1_k4_sched", 96, 96, 1024, 8, KSPLIT96_OPS},
 };
 #undef NN_ONLY
 #undef ALL_OPS
@@ -676,6 +688,7 @@ const MfmaConfig kConfigs[] = {
 #undef SCHED128_OPS
 #undef SPLITK_OPS
 #undef KSPLIT_OPS
+#undef KSPLIT96_OPS
 #undef SMALL_OPS
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 }  // namespace
@@ -707,7 +720,12 @@ const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConf
 // from 512^3 to 8192^3; below K = 448 the model misjudges them against
 // two co-resident 128 x 128 workgroups per CU, e.g. at 3000 x 3000 x 384:
 // there they only replace the split-phase tiles, from K = 384, three
-// phases per wave).  Last, products of at most 1024 output tiles of 16 x 16
+// phases per wave).  The 96 x 96 k-split tiles (mfma_ksplit96.hip) replace
+// the choice in turn where the model gives them the shorter time, at 0.9925
+// and 12 us (fitted to 1536^3 and 4608^3, the fixed cost raised from 10 us so
+// that 3584^3, 5.6 rounds of them against 12.25 rounds of 64 x 64 k-split
+// tiles, keeps the latter, 2-3 % faster there; within 4 % of the measured
+// time at 2048^3, 2560^3, 3072^3, 5120^3, 6144^3 and 7168^3).  Last, products of at most 1024 output tiles of 16 x 16
 // take the small-tile kernels (16 x 16 tiles on 8 waves up to 512 such
 // tiles, else 32 x 32 tiles on 4 waves).  Every picked configuration
 // is built for all four op combinations.
@@ -716,14 +734,15 @@ namespace {
 // + fixed cost); tile work at the per-CU peak of 2 x 64 x 64 x K flops per
 // 64 x 64 tile at 614.5 GFLOP/s, 13.33 ns per k.
 double model_ns(int config, int M, int N, int K) {
-    int tile, rel;
-    double eff, fixed;
+    int tile;
+    double rel, eff, fixed;
     switch (config) {
         case 16: tile = 256; rel = 16; eff = 0.985; fixed = 11000; break;
         case 18: tile = 128; rel = 4; eff = 0.975; fixed = 5300; break;
         case 7: tile = 256; rel = 16; eff = 0.92; fixed = 11000; break;
         case 1: tile = 128; rel = 4; eff = 0.85; fixed = 5300; break;
         case 20: tile = 64; rel = 1; eff = 0.914; fixed = 3000; break;
+        case 24: tile = 96; rel = 2.25; eff = 0.9925; fixed = 12000; break;
         default: return 1e300;                    // the split-phase 64 x 64 tiles: never kept over 20
     }
     const int64_t tiles = (int64_t)ceil_div(M, tile) * ceil_div(N, tile);
@@ -751,6 +770,7 @@ int mfma_pick_config(int M, int N, int K) {
     const bool split_fits = K % 4 == 0 && M % 4 == 0 && N % 4 == 0;
     if (split_fits && ((pick == small && K >= 384) || (K >= 448 && model_ns(20, M, N, K) < model_ns(pick, M, N, K))))
         pick = 20;
+    if (split_fits && K >= 448 && model_ns(24, M, N, K) < model_ns(pick, M, N, K)) pick = 24;
     // Few output elements: small tiles whose k groups are split over the
     // waves of a block (small.hip), any shape and K.  Measured kernel times
     // (256^3: 3.9 us against 8.7 for the split-phase tiles; 512^3: 9.2

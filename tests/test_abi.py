@@ -351,7 +351,8 @@ def test_default_variant_choices(binding):
     tiles (32-deep phases for at most 256 tiles).  Then, with K, M and N
     multiples of 4, the 64 x 64 tiles whose four waves split the phases where
     a cost model of rounds, efficiency and fixed cost per tile gives them the
-    shorter time (K >= 448), or in place of the split-phase tiles (K >= 384).
+    shorter time (K >= 448), or in place of the split-phase tiles (K >= 384),
+    and the 96 x 96 ones where the same model gives those the shorter time.
     Last, at most 512 output tiles of 16 x 16 take the 16 x 16 small-tile
     kernel on 8 waves, at most 1024 the 32 x 32 one on 4 waves, whatever K.
     For the 16-bit product the
@@ -365,26 +366,28 @@ def test_default_variant_choices(binding):
         (8192, 4096, 2048): "mfma256x256_bk32_w2x2_sched",
         (4096, 4096, 32): "mfma256x256_bk32_w2x2_sched",
         (7940, 8132, 32): "mfma256x256_bk32_w2x2_sched",         # 1024 tiles with edges
-        (8200, 8200, 8192): "mfma128x128_bk32_w2x2_sched",       # 1089 tiles of 256: 85 % of 5 rounds
+        (8200, 8200, 8192): "mfma96x96_bk16_w1x1_k4_sched",       # 1089 tiles of 256: 85 % of 5 rounds
         (4100, 4104, 4096): "mfma64x64_bk32_w1x1_k4_sched",       # 4225 tiles of 64: 16.5 rounds
         (4000, 5000, 4096): "mfma128x128_bk32_w2x2_sched",
         (2048, 2048, 2048): "mfma128x128_bk32_w2x2_sched",
         (6144, 6144, 6144): "mfma128x128_bk32_w2x2_sched",
-        (7168, 7168, 7168): "mfma128x128_bk32_w2x2_sched",
+        (7168, 7168, 7168): "mfma96x96_bk16_w1x1_k4_sched",       # 5625 tiles of 96: 21.97 rounds
         (3000, 3000, 384): "mfma128x128_bk32_w2x2_sched",        # K < 512: no cost model
-        (1536, 1536, 1536): "mfma64x64_bk32_w1x1_k4_sched",       # 144 tiles of 128, 576 of 64
-        (3072, 3072, 3072): "mfma64x64_bk32_w1x1_k4_sched",       # 2304 tiles of 64: 9 full rounds
+        (3072, 3072, 3072): "mfma96x96_bk16_w1x1_k4_sched",       # 1024 tiles of 96: 4 full rounds
+        (1536, 1536, 1536): "mfma96x96_bk16_w1x1_k4_sched",       # 256 tiles of 96: one round
+        (5120, 5120, 5120): "mfma64x64_bk32_w1x1_k4_sched",       # 6400 tiles of 64: 25 full rounds
         (1024, 1024, 1024): "mfma64x64_bk32_w1x1_k4_sched",
         (4096, 4096, 48): "mfma256x256_bk32_w2x2_sched",          # K % 32 = 16: last phase past K
         (8193, 8190, 96): "mfma256x256_bk32_w2x4_direct",
         (4096, 4096, 0): "mfma256x256_bk32_w2x4_direct",
         (6000, 6000, 6000): "mfma128x128_bk32_w2x2_sched",        # K % 32 = 16: last phase past K
         (5000, 3000, 2000): "mfma128x128_bk32_w2x2_sched",
-        (4608, 4608, 4608): "mfma64x64_bk32_w1x1_k4_sched",       # 5184 tiles of 64: 20.25 rounds
+        (4608, 4608, 4608): "mfma96x96_bk16_w1x1_k4_sched",       # 2304 tiles of 96: 9 full rounds
         (3840, 2048, 100): "mfma128x128_bk32_w2x2_sched",
         (3840, 2048, 102): "mfma128x128_bk16_w2x2",               # K % 4 = 2
         (4100, 4097, 515): "mfma64x64_bk16_w2x2_k4",              # K % 4 = 3
-        (3000, 3000, 3000): "mfma64x64_bk32_w1x1_k4_sched",
+        (3000, 3000, 3000): "mfma96x96_bk16_w1x1_k4_sched",       # 1024 tiles of 96
+        (2300, 2300, 2304): "mfma64x64_bk32_w1x1_k4_sched",
         (1000, 1000, 1000): "mfma64x64_bk32_w1x1_k4_sched",
         (1000, 2000, 500): "mfma64x64_bk32_w1x1_k4_sched",        # in place of the split-phase tiles
         (1000, 1000, 380): "mfma64x64_bk32_w2x2_k4",              # K < 384

@@ -80,8 +80,8 @@ class Problem:
 
 
 def test_kernel_is_the_default_for_its_shapes():
-    for shape in [(1000, 1000, 1000), (560, 548, 1000), (540, 516, 516), (3072, 3072, 3072),
-                  (4608, 4608, 4608), (1000, 2000, 500), (4100, 4104, 4100), (2000, 1000, 996)]:
+    for shape in [(1000, 1000, 1000), (560, 548, 1000), (540, 516, 516), (5120, 5120, 5120),
+                  (2300, 2300, 2304), (1000, 2000, 500), (4100, 4104, 4100), (2000, 1000, 996)]:
         assert default_name(*shape) == KS, shape
     for shape in [(1000, 1000, 380), (1002, 1000, 1000), (1000, 1000, 1001), (8192, 8192, 8192),
                   (2048, 2048, 2048)]:
@@ -126,7 +126,7 @@ def test_full_oracle(shape, ops, dist):
 SAMPLED = [
     # shape, offset, (pad A, pad B, pad C)
     ((1000, 1000, 1000), 1, (3, 5, 7)),
-    ((3072, 3072, 3072), 0, (0, 0, 0)),
+    ((5120, 5120, 5120), 0, (0, 0, 0)),
     ((4100, 4104, 4100), 3, (1, 2, 1)),
     ((2000, 1000, 996), 1, (4, 0, 3)),
 ]

@@ -1137,3 +1137,63 @@ def test_ksplit16_128_copies_never_depend_on_the_scalar_offset(kc, shape):
                         wants_zero = k < 0 or k >= K or mn >= ext
                         in_matrix = 0 <= k < K and (mn < ext if kc else mn + 7 < ext)
                         _check_copy(voff, soff, nrec, 16, wants_zero, in_matrix, what)
+
+
+def ks96_copy(kc, j, lane):
+    """(stored row, first float of the lane's 16 bytes within the row, LDS
+    byte) of lane `lane` of copy j in the fp32 96 x 96 k-split kernel's
+    tile (96 mn x 16 k per stage): KC rows of 16 k (64 bytes), the 16-byte
+    chunk c (4 k) of row r at c ^ ((r / 4) mod 4), 16 rows per 1 KB copy (6
+    copies); MC k rows of 96 floats at a 512-byte stride, 2 rows per copy
+    (8 copies), lanes 24..31 of each row landing in the 128-byte pad."""
+    if kc:
+        row = 16 * j + lane // 4
+        return row, 4 * ((lane % 4) ^ ((row >> 2) & 3)), 1024 * j + 16 * lane
+    return 2 * j + lane // 32, 4 * (lane % 32), 1024 * j + 16 * lane
+
+
+def ks96_read(kc, f, s, e, lane):
+    """LDS byte of lane `lane`'s read for block f at step s (k 8 s .. 8 s + 7
+    of the phase): KC, the 128-bit read of row 32 f + l % 32, k = 8 s +
+    4 (l / 32) .. + 3 (values e = 0..3 for the step's four instructions);
+    MC, the 32-bit read of k row 8 s + 4 (l / 32) + e, column 32 f + l % 32."""
+    li, lh = lane % 32, lane // 32
+    if kc:
+        row = 32 * f + li
+        return 64 * row + 16 * ((2 * s + lh) ^ ((row >> 2) & 3))
+    return 512 * (8 * s + 4 * lh + e) + 4 * (32 * f + li)
+
+
+@pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
+def test_ksplit_f32_96_kernel_layout(kc):
+    """The fp32 96 x 96 k-split kernel's tile, restated: the copies fill the
+    stage's 96 x 16 values exactly once (the mn-contiguous pad lanes aside);
+    every read delivers the operand v_mfma_f32_32x32x2_f32 takes for the
+    step's instruction e -- lane l supplies op(X)[32 f + l % 32][8 s +
+    4 (l / 32) + e] -- and the reads are free of bank conflicts (128-bit:
+    the measured quad grouping; 32-bit: 32 lanes per cycle)."""
+    where = {}
+    for j in range(6 if kc else 8):
+        for lane in range(64):
+            row, x0, dst = ks96_copy(kc, j, lane)
+            if not kc and x0 >= 96:
+                continue                              # pad lanes: past the end, never read
+            for e in range(4):
+                assert dst + 4 * e not in where
+                where[dst + 4 * e] = (row, x0 + e) if kc else (x0 + e, row)
+    assert len(where) == 96 * 16
+    assert max(where) < (6144 if kc else 8192)
+    for f in range(3):
+        for s in range(2):
+            if kc:
+                addrs = [ks96_read(True, f, s, 0, lane) for lane in range(64)]
+                for lane in range(64):
+                    got = [where[addrs[lane] + 4 * e] for e in range(4)]
+                    assert got == [(32 * f + lane % 32, 8 * s + 4 * (lane // 32) + e) for e in range(4)]
+                assert degree128([a // 4 for a in addrs]) == 1
+            else:
+                for e in range(4):
+                    addrs = [ks96_read(False, f, s, e, lane) for lane in range(64)]
+                    for lane in range(64):
+                        assert where[addrs[lane]] == (32 * f + lane % 32, 8 * s + 4 * (lane // 32) + e)
+                    assert degree([a // 4 for a in addrs], 1, 64, 32) == 1
