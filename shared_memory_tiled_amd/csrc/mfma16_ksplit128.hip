@@ -21,18 +21,21 @@
 // copies, not the instructions, set the pace.
 //
 // A phase is 64 matrix instructions (block (q / 8, q % 8) for instruction
-// q, 1024 matrix-core clocks).  During local phase lp a wave copies local
-// phase lp + 2 into the stage phase lp came from (16 copies of 1 KB, one
-// after every odd instruction below 32), then, once the copies of phase
-// lp + 1 have landed, reads phase lp + 1's fragments into its other register
-// set (one read after each instruction from 24 on).  Every phase runs this
-// same body, so the loop has no branch inside (a branch between phases
-// keeps an unread register set live across it, and 256 accumulators leave
-// no room for that): a wave runs an even number of phases, at least two,
-// the ones past its own copying zeros (their products add +0), and the
-// copies and reads aimed past the last phase bring zeros into, and read,
-// stages that nothing uses afterwards.
-//
+// q, 1024 matrix-core clocks).  A wave runs its phases at positions: the
+// last phase first, then (with an odd count) a position that copies zeros,
+// then phases 0, 1, ..; at least two positions, an even number.  During
+// position s it copies position s + 2 into the stage position s came from
+// (16 copies of 1 KB, one after every odd instruction below 32), then, once
+// the copies of position s + 1 have landed, reads position s + 1's fragments
+// into its other register set (one read after each instruction from 24
+// on).  The two phases that need per-lane copy offsets -- the last and the
+// first -- sit at positions 0 to 2, copied in the prologue and by the first
+// two positions (peeled); every later position runs one and the same body
+// with one kind of copy, so the loop has no branch inside (a branch between
+// phases keeps an unread register set live across it, and 256 accumulators
+// leave no room for that).  Copies and reads aimed past the last position
+// fill, and read, stages that nothing uses afterwards.
+
 // Tiles (per stage, 128 mn x 32 k):
 //   KC (k-contiguous factor: A as stored, B stored transposed): 128 rows of
 //      32 k (64 bytes), the 16-byte chunk c (8 k) of row r at
@@ -54,8 +57,8 @@
 // a multiple of 8), so only phase 0 reaches below k = 0; every copy that
 // must bring zeros is past its descriptor's end by its per-lane offset
 // alone (rows of a KC factor past the tile's edge, chunks of an MC factor
-// wholly past its last column, lanes of phase 0 below k = 0, phases past
-// the wave's last); the wave's first and last phases take the phase in
+// wholly past its last column, lanes of phase 0 below k = 0, positions
+// holding no phase); the wave's first and last phases take the phase in
 // their per-lane offsets with a scalar offset of 0, so that a chunk of an
 // MC factor's last row across its last column meets the descriptor's end by
 // its own offset (the range check is per dword, and the width is even).
