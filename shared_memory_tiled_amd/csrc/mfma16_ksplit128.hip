@@ -301,17 +301,29 @@ void gemm16_ksplit128_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Partial tiles, in two rounds.  In round a, wave v adds block row
-    // 4 a + v of the tile over the four waves, in wave order, and stores it.
-    // Each wave writes its blocks of those rows into its own stages (no copy
-    // in flight and no read pending, and no other wave reads them before the
-    // barrier): block (4 a + v, j), lane l's four values at float
-    // 2048 v + 256 j + 4 l -- one 128-bit write or read per block, consecutive
-    // lanes on consecutive 16 bytes.  Register r of block (i, j) of lane l is
-    // row 16 i + 4 (l / 16) + r, column 16 j + l % 16 of the tile.  (Taking
-    // the rows in order keeps the allocator from moving accumulators inside
-    // the phase loop.)
-    float* const mine = reinterpret_cast<float*>(wl);
-    const int row_l = 4 * (lane >> 4), col = n0 + (lane & 15);
+    // 4 a + v of the tile (16 rows) over the four waves, in wave order, and
+    // stores it.  Each wave writes its four block rows of the round into its
+    // own stages (no copy in flight and no read pending, and no other wave
+    // reads them before the barrier), block row 4 a + v at float 2048 v, each
+    // as 16 rows of 128 floats, row-major, the 16-float segments of row rho
+    // XORed by 16 ((rho / 4) mod 2): register r of block (i, j) of lane l
+    // (row 4 (l / 16) + r, column 16 j + l % 16) is one 32-bit write per
+    // (j, r), conflict free at 32 lanes a cycle.  Wave v then reads, for
+    // it = 0..7, row 2 it + l / 32, columns 4 (l % 32) .. + 3 of its block
+    // row from each wave -- one 128-bit read, conflict free under the
+    // measured grouping -- adds them and stores the four values with one
+    // 128-bit store (32 lanes: 512 contiguous bytes of a row of C).  (Taking
+    // the block rows in order keeps the allocator from moving accumulators
+    // inside the phase loop.)
+    // (rho / 4) mod 2 is (l / 16) mod 2 for a write and (it / 2) mod 2 for a
+    // read, so two per-lane bases each serve every address (instruction
+    // offsets): writes of even and of odd j; reads without and with the XOR.
+    const int b16 = (lane >> 4) & 1;
+    float* const wbase_even = reinterpret_cast<float*>(wl) + 512 * (lane >> 4) + (lane & 15) + 16 * b16;
+    float* const wbase_odd = reinterpret_cast<float*>(wl) + 512 * (lane >> 4) + (lane & 15) - 16 * b16;
+    const int colq = 4 * (lane & 31);
+    const float* const rbase0 = reinterpret_cast<const float*>(lds) + 2048 * w + 128 * (lane >> 5) + colq;
+    const float* const rbase1 = reinterpret_cast<const float*>(lds) + 2048 * w + 128 * (lane >> 5) + (colq ^ 16);
     unroll<2>([&](auto ac) __attribute__((always_inline)) {
         constexpr int a = decltype(ac)::value;
         if constexpr (a == 1) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // round 0 is read
@@ -319,27 +331,28 @@ void gemm16_ksplit128_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m
             constexpr int v = decltype(vc)::value;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<floatx4*>(mine + 2048 * v + 256 * j + 4 * lane) = acc[4 * a + v][j];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    ((j & 1) ? wbase_odd : wbase_even)[2048 * v + 128 * r + 16 * j] = acc[4 * a + v][j][r];
         });
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        floatx4 sum[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int it = 0; it < 8; ++it) {
+            const int rho = 2 * it + (lane >> 5);
+            const float* const rb = ((it >> 1) & 1) ? rbase1 : rbase0;
+            floatx4 sum = *reinterpret_cast<const floatx4*>(rb + 256 * it);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const floatx4 x = *reinterpret_cast<const floatx4*>(
-                    reinterpret_cast<const float*>(lds + u * WAVE_BYTES) + 2048 * w + 256 * j + 4 * lane);
-                if (u == 0) sum[j] = x;
-                else sum[j] += x;
-            }
-        const int row0 = m0 + 16 * (4 * a + w) + row_l;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = row0 + r;
+            for (int u = 1; u < 4; ++u) sum += *reinterpret_cast<const floatx4*>(rb + (WAVE_BYTES / 4) * u + 256 * it);
+            const int row = m0 + 16 * (4 * a + w) + rho, col = n0 + colq;
             if (row >= p.M) continue;
+            float* const c = p.C + (int64_t)row * p.ldc + col;
+            if (col + 3 < p.N && ((reinterpret_cast<uintptr_t>(c) & 15) == 0)) {
+                *reinterpret_cast<floatx4*>(c) = sum;
+            } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (col + 16 * j < p.N) p.C[(int64_t)row * p.ldc + col + 16 * j] = sum[j][r];
+                for (int e = 0; e < 4; ++e)
+                    if (col + e < p.N) c[e] = sum[e];
+            }
         }
     });
 }

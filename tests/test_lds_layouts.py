@@ -1197,3 +1197,36 @@ def test_ksplit_f32_96_kernel_layout(kc):
                     for lane in range(64):
                         assert where[addrs[lane]] == (32 * f + lane % 32, 8 * s + 4 * (lane // 32) + e)
                     assert degree([a // 4 for a in addrs], 1, 64, 32) == 1
+
+
+def test_ksplit16_128_partial_rows_conflict_free():
+    """The 128 x 128 k-split kernel's partial block rows in LDS: 16 rows of
+    128 floats, row-major, each row's 16-float segments XORed by 16 (r / 4)
+    mod 2 positions.  Writing register r of block j (lane l: row
+    4 (l / 16) + r, column 16 j + l % 16) is one 32-bit write per (j, r),
+    free of conflicts at 32 lanes per cycle; reading lane l's four
+    consecutive floats of row 2 it + l / 32, columns 4 (l % 32) .. + 3, is
+    one 128-bit read, free of conflicts under the measured quad grouping;
+    together they move every value once."""
+    def phys(row, col):
+        return 128 * row + (col ^ (16 * ((row >> 2) & 1)))
+    written = {}
+    for j in range(8):
+        for r in range(4):
+            words = []
+            for lane in range(64):
+                row, col = 4 * (lane // 16) + r, 16 * j + lane % 16
+                w = phys(row, col)
+                assert w not in written
+                written[w] = (row, col)
+                words.append(w)
+            assert degree(words, 1, 64, 32) == 1
+    assert sorted(written) == list(range(16 * 128))
+    for it in range(8):
+        words = []
+        for lane in range(64):
+            row, col = 2 * it + lane // 32, 4 * (lane % 32)
+            w = phys(row, col)
+            assert [written[w + e] for e in range(4)] == [(row, col + e) for e in range(4)]
+            words.append(w)
+        assert degree128(words) == 1
