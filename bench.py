@@ -471,7 +471,8 @@ SWEEP_SHAPES = ([(n, n, n) for n in (512, 768, 1024, 1536, 2048, 2560, 3072, 358
                  (8192, 4096, 2048), (2048, 8192, 4096), (16384, 1024, 4096), (1024, 16384, 2048),
                  (5000, 3000, 2000), (3000, 7000, 1024), (1000, 2000, 500), (2048, 2048, 256),
                  (4096, 4096, 256), (1024, 1024, 4096), (1000, 1000, 1000), (3000, 3000, 384),
-                 (8192, 8192, 8100), (4096, 4096, 4100)])
+                 (8192, 8192, 8100), (4096, 4096, 4100), (2304, 2304, 2304), (2816, 2816, 2816),
+                 (2048, 4096, 1024), (2048, 3072, 512)])
 SWEEP_CANDIDATES = ["mfma64x64_bk32_w2x2_k4", "mfma64x64_bk16_w2x2_k4", "mfma64x64_bk32_w1x1_k4_sched",
                     "mfma128x128_bk16_w2x2",
                     "mfma128x128_bk32_w2x2_sched", "mfma256x256_bk32_w2x4_direct",
@@ -480,7 +481,8 @@ SWEEP_CANDIDATES = ["mfma64x64_bk32_w2x2_k4", "mfma64x64_bk16_w2x2_k4", "mfma64x
 
 MIXED_SWEEP_CANDIDATES = ["mixed64x64_bk64_w1x2", "mixed64x64_bk32_w4_ksplit", "mixed128x128_bk64_w2x2_directAB",
                           "mixed256x256_bk64_w2x4_directAB", "mixed256x256_bk64_w4_sched",
-                          "mixed256x256_bk64_w4_wide", "mixed256x256_bk32_w4_wide4stage", "mixed128x128_bk32_w4_ksplit"]
+                          "mixed256x256_bk64_w4_wide", "mixed256x256_bk32_w4_wide4stage", "mixed128x128_bk32_w4_ksplit",
+                          "mixed192x192_bk64_w4_wide"]
 
 
 def bench_shape_sweep(args) -> int:

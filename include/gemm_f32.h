@@ -395,9 +395,14 @@ int reduce_sum_f32_variant_noalloc(int variant, int64_t n, const float *x, float
  * the element-wise 128 x 128 kernel.  The scheduled configurations
  * -- mixed256x256_bk64_w4_wide (v_mfma_f32_16x16x32; gemm_mixed's and
  * gemm_mixed_op's choice once there are 128 tiles of 256 x 256),
+ * mixed192x192_bk64_w4_wide (the same kernel on 192 x 192 tiles; their
+ * choice, with K even, where its tiles need fewer rounds of the 256 CUs at
+ * 0.8 of a 256 tile's time each, or, below 128 tiles of 256 x 256, with at
+ * least 140 of 192 x 192 or, for K % 8 != 0, 32 of them with K < 1536 (or
+ * K % 4 == 2 and fewer than 128 tiles of 128 x 128)),
  * mixed256x256_bk64_w4_sched (the same schedule on v_mfma_f32_32x32x16) and
  * mixed256x256_bk32_w4_wide4stage (16x16x32 with four 32-deep LDS stages) --
- * take K a multiple of 8 (mixed256x256_bk64_w4_wide: K even), N even (M
+ * take K a multiple of 8 (the two 16x16x32 wide ones: K even), N even (M
  * too for A stored transposed in gemm_mixed_op, and not N for B stored
  * transposed), 4-byte aligned operands with even leading dimensions and
  * operands under 2^31 bytes; edge tiles run whole and store only inside C,

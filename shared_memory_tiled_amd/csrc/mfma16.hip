@@ -1069,7 +1069,7 @@ hipError_t launch_sched_kernel(const Gemm16Args& p, hipStream_t s, int tiles_m, 
 }
 // Tile-row groups: 4 for the scheduled kernel, 8 for the 8-wave kernel (each
 // the fastest measured at 8192^3).
-constexpr int kSchedGroupM = 4, kDirectGroupM = 8;
+constexpr int kSchedGroupM = 4, kDirectGroupM = 8, kWide192GroupM = 4;
 template <int FMT>
 hipError_t launch_sched(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int /*group_m*/,
                         unsigned blocks) {
@@ -1110,6 +1110,20 @@ hipError_t launch_wide_cfg(const Gemm16Args& p, hipStream_t s, int tiles_m, int 
     if (!wide_fits(p, 0, 0))
         return launch16<FMT, 256, 256, 2, 4, true, true, true>(p, s, tiles_m, tiles_n, kDirectGroupM, blocks);
     return launch_wide16(p, s, FMT, 0, 0, kSchedGroupM);
+}
+
+// Configuration 13 (the same kernel on 192 x 192 tiles) where it takes the
+// problem; else the 8-wave kernel on 256 x 256 tiles, as configuration 10
+// runs it (VEC: vector-aligned operands; the tile counts it is given are
+// those of 192 x 192 tiles, so they are taken again for 256 x 256 ones).
+template <int FMT, bool VEC>
+hipError_t launch_wide192_cfg(const Gemm16Args& p, hipStream_t s, int /*tiles_m*/, int /*tiles_n*/,
+                              int /*group_m*/, unsigned /*blocks*/) {
+    if (VEC && wide_fits(p, 0, 0)) return launch_wide16_192(p, s, FMT, 0, 0, kWide192GroupM);
+    const int tm = ceil_div(p.M, 256), tn = ceil_div(p.N, 256);
+    const unsigned nb = (unsigned)((int64_t)tm * tn);
+    if (VEC) return launch16<FMT, 256, 256, 2, 4, true, true, true>(p, s, tm, tn, kDirectGroupM, nb);
+    return launch16<FMT, 256, 256, 2, 4, false, false, false>(p, s, tm, tn, kSchedGroupM, nb);
 }
 
 // Configuration 11 (the four-stage form, mfma16_wide4.hip) where it takes
@@ -1154,12 +1168,18 @@ const MixedConfig kMixed[] = {
     {"mixed128x128_bk32_w4_ksplit", 128, 128, kKsplit128GroupM,
      {{launch16<0, 128, 128, 2, 2, false, false, false>, launch_ksplit128_cfg<0>},
       {launch16<1, 128, 128, 2, 2, false, false, false>, launch_ksplit128_cfg<1>}}},
+    // configuration 10's kernel on 192 x 192 tiles; misaligned operands: the
+    // element-wise 8-wave kernel on 256 x 256 tiles, as for 6
+    {"mixed192x192_bk64_w4_wide", 192, 192, kWide192GroupM,
+     {{launch_wide192_cfg<0, false>, launch_wide192_cfg<0, true>},
+      {launch_wide192_cfg<1, false>, launch_wide192_cfg<1, true>}}},
 };
 #undef MIXED
 constexpr int kNumMixed = (int)(sizeof(kMixed) / sizeof(kMixed[0]));
 constexpr int kKsplitConfig = 9;          // mixed64x64_bk32_w4_ksplit
 constexpr int kWideConfig = 10;           // mixed256x256_bk64_w4_wide
 constexpr int kKsplit128Config = 12;      // mixed128x128_bk32_w4_ksplit
+constexpr int kWide192Config = 13;        // mixed192x192_bk64_w4_wide
 
 // op kernels, chosen by tile, op pair and load path
 template <int FMT, int BM, int BN, int WM, int WN, bool KCA, bool KCB, bool VEC>
@@ -1186,10 +1206,12 @@ Launch16 op_launcher(int op_a, int op_b, bool vec) {
 }
 }  // namespace
 
-// op(A) x op(B): 256 x 256 tiles once there are 128 of them (the scheduled
+// op(A) x op(B): the tiles gemm_mixed picks -- 256 x 256 (the scheduled
 // kernel on v_mfma_f32_16x16x32, mfma16_wide.hip, where it fits, else eight
-// waves of gemm16_op_kernel), else the k-split kernel or 128 x 128 tiles of
-// four waves, as gemm_mixed picks.  A and B are the stored matrices; vector loads (and
+// waves of gemm16_op_kernel) or 192 x 192 (the same kernel) once there are
+// 128 tiles of 256, else the k-split kernels, 192 x 192 tiles or 128 x 128
+// tiles of four waves; where the 192 x 192 or k-split kernels do not fit,
+// the 256 x 256 or 128 x 128 tiles by the same count.  A and B are the stored matrices; vector loads (and
 // the direct copies) need 4-byte aligned bases and even leading dimensions,
 // as for gemm_mixed.
 hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b) {
@@ -1200,6 +1222,8 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
     if (pick == kKsplitConfig && ksplit16_fits(p, op_a, op_b)) return launch_ksplit16(p, s, format, op_a, op_b);
     if (pick == kKsplit128Config && ksplit128_fits(p, op_a, op_b))
         return launch_ksplit128(p, s, format, op_a, op_b, kKsplit128GroupM);
+    if (pick == kWide192Config && wide_fits(p, op_a, op_b))
+        return launch_wide16_192(p, s, format, op_a, op_b, kWide192GroupM);
     const bool big = t256 >= 128;
     const int tile = big ? 256 : 128;
     const int tiles_m = ceil_div(p.M, tile), tiles_n = ceil_div(p.N, tile);
@@ -1220,7 +1244,14 @@ const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed
 // not take) from 128 of them, half the CUs: measured, 144 such tiles
 // (3072^3) still beat 576 of 128 x 128 by 40 %; at 8192^3 it runs bf16 at
 // 1395 TFLOP/s against 1332 for the 32 x 32 x 16 form (configuration 8) on
-// the same box, f16 at 1340 against 1250.  Else, below
+// the same box, f16 at 1340 against 1250.  There, 192 x 192 tiles of the
+// same kernel (configuration 13; K even) where they need fewer rounds of
+// 256 CUs by the measured cost of a 192 tile, 0.8 of a 256 tile per phase
+// (its copies, 48 KB per 64-deep phase, take longer than its matrix
+// instructions): 4 rounds of 192 < 5 rounds of 256 (bf16: 3072^3 1169
+// against 944 TFLOP/s, 4100^2 x 4096 1078 against 830, 2048 x 4096 x 1024
+// 709 against 581; 3584^3, one round of 256 against two of 192, 1278
+// against 893).  Else, below
 // 128 tiles of 128 x 128 and with K a multiple of 8, 64 x 64 tiles whose
 // four waves split the phases (mfma16_ksplit.hip; measured bf16: 1024^2 x
 // 4096 479 against 186 TFLOP/s on the 128 x 128 tiles, 1000^3 234 against
@@ -1229,15 +1260,30 @@ const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed
 // K of at least 1024 (a multiple of 8), 128 x 128 tiles whose four waves
 // split the phases (mfma16_ksplit128.hip; measured bf16: 2048^3 697 against
 // 586 TFLOP/s on the 128 x 128 tiles with direct copies, 1536^3 355 against
-// 344; with 400 tiles (2560^3) or K = 256 they lose).  Else 128 x 128 tiles
-// with both factors copied straight into LDS from 128 of them (64 for K of
-// at least 2048), else 64 x 64 tiles.
+// 344; with 400 tiles (2560^3) or K = 256 they lose).  Else, with at least
+// 140 tiles of 192 x 192 (more than half a round; K even), those tiles
+// (bf16: 2816^3 967 against 847 on 128 x 128 tiles, 2560^3 798 against 764,
+// 2048 x 3072 x 512 408 against 385; with 132 (1024 x 4096 x 1024) 410
+// against 476); and with K % 8 != 0 (even) from 32 of them if K is below
+// 1536, or, with fewer than 128 tiles of 128 x 128, K % 4 = 2 (the 128 x
+// 128 and 64 x 64 tiles then run without direct copies, and with K % 4 = 2
+// element by element: 1000 x 2000 x 500 145 against 94, 1500 x 3000 x 700
+// 331 against 185, 1000^2 x 2002 102 against 50 on 64 x 64 tiles, 800 x
+// 1200 x 3002 105 against 50; 1536^2 x 1538 244 against 274, 1024^2 x 4092
+// 129 against 155).  Else 128 x 128 tiles with
+// both factors copied straight into LDS from 128 of them (64 for K of at
+// least 2048), else 64 x 64 tiles.
 int mixed_pick_config(int M, int N, int K) {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
+    const int64_t t192 = (int64_t)ceil_div(M, 192) * ceil_div(N, 192);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
-    if (t256 >= 128) return kWideConfig;
+    const bool even_k = K > 0 && K % 2 == 0;
+    const int64_t r256 = (t256 + 255) / 256, r192 = (t192 + 255) / 256;   // rounds of 256 CUs
+    if (t256 >= 128) return even_k && 4 * r192 < 5 * r256 ? kWide192Config : kWideConfig;
     if (t128 < 128 && K % 8 == 0 && K > 0) return kKsplitConfig;
     if (t128 <= 256 && K >= 1024 && K % 8 == 0) return kKsplit128Config;
+    const bool ragged_k = K % 8 != 0 && t192 >= 32 && (K < 1536 || (t128 < 128 && K % 4 == 2));
+    if (even_k && (t192 >= 140 || ragged_k)) return kWide192Config;
     if (t128 >= 128 || (t128 >= 64 && K >= 2048)) return 7;
     return 3;
 }

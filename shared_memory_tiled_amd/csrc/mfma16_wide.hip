@@ -61,14 +61,17 @@ namespace gemmf32 {
 
 namespace {
 
+template <int BT>
 struct WideTileKC {
     static constexpr bool IS_KC = true;
-    static constexpr int STAGE_BYTES = 32768;
-    static constexpr int READS = 8;                       // LDS reads per step (8 fragments)
+    static constexpr int STAGE_BYTES = 128 * BT;
+    static constexpr int COPIES = BT / 32;                // 1 KB copies per wave and phase
+    static constexpr int READS = BT / 32;                 // LDS reads per step (one per fragment)
     static constexpr int BASES = 2;                       // read bases (one per step)
     __host__ __device__ static constexpr int swz(int r) { return (r >> 1) & 7; }
-    // Copy j (0..7) of wave w fills stage bytes 1024 q .. + 1023, q = w + 4 j:
-    // rows 8 q .. + 7; lane l fills physical chunk l % 8 of row 8 q + l / 8.
+    // Copy j (0 .. COPIES - 1) of wave w fills stage bytes 1024 q .. + 1023,
+    // q = w + 4 j: rows 8 q .. + 7; lane l fills physical chunk l % 8 of row
+    // 8 q + l / 8.
     __host__ __device__ static int copy_q(int w, int j) { return w + 4 * j; }
     __host__ __device__ static int copy_dst(int w, int j) { return 1024 * copy_q(w, j); }
     __host__ __device__ static int copy_row(int w, int j, int lane) { return 8 * copy_q(w, j) + lane / 8; }
@@ -93,10 +96,12 @@ struct WideTileKC {
     __host__ __device__ static constexpr uint32_t read_imm(int s, int f, int h) { return 2048u * f + 0u * (s + h); }
 };
 
+template <int BT>
 struct WideTileMC {
     static constexpr bool IS_KC = false;
     static constexpr int STAGE_BYTES = 32 * 1056;
-    static constexpr int READS = 16;                      // LDS reads per step (8 fragments x 2)
+    static constexpr int COPIES = 8;                      // 1 KB copies per wave and phase
+    static constexpr int READS = BT / 16;                 // LDS reads per step (two per fragment)
     static constexpr int BASES = 1;
     // Pair and row in the pair of the phase's k row kappa.
     __host__ __device__ static constexpr int pair(int kappa) {
@@ -104,7 +109,8 @@ struct WideTileMC {
     }
     __host__ __device__ static constexpr int half(int kappa) { return (kappa >> 2) & 1; }
     // Copy j (0..7) of wave w fills pair q = w + 4 j; lane l brings row
-    // l / 32 of the pair, values 8 (l % 32) .. + 7.
+    // l / 32 of the pair, values 8 (l % 32) .. + 7 (a 512-byte row slot; with
+    // a tile of 192 values the lanes of values 192 .. 255 copy zeros).
     __host__ __device__ static int copy_q(int w, int j) { return w + 4 * j; }
     __host__ __device__ static int copy_dst(int w, int j) { return 1056 * copy_q(w, j); }
     __host__ __device__ static int copy_k(int w, int j, int lane) {
@@ -129,19 +135,32 @@ struct WideTileMC {
     }
 };
 
-template <bool KC>
-using WideTile = std::conditional_t<KC, WideTileKC, WideTileMC>;
+template <bool KC, int BT>
+using WideTile = std::conditional_t<KC, WideTileKC<BT>, WideTileMC<BT>>;
 
-template <int FMT, bool KCA, bool KCB>
+// Waits until at most N copies of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_copies_below() {
+    static_assert(N == 12 || N == 14 || N == 16, "copy count");
+    if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    if constexpr (N == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+    if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+}
+
+// BT: the tile's extent in M and N (256, or 192 for problems whose 256 x 256
+// tiles fill the CUs' rounds badly); each wave holds a quarter of it.
+template <int FMT, bool KCA, bool KCB, int BT = 256>
 __global__ __launch_bounds__(256)
 void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
-    constexpr int BM = 256, BN = 256, WM = 128, WN = 128, BK = 64, FM = 8, FN = 8;
-    using TA = WideTile<KCA>;
-    using TB = WideTile<KCB>;
+    static_assert(BT == 256 || BT == 192, "tile");
+    constexpr int BM = BT, BN = BT, WM = BT / 2, WN = BT / 2, BK = 64, FM = BT / 32, FN = BT / 32;
+    using TA = WideTile<KCA, BT>;
+    using TB = WideTile<KCB, BT>;
     constexpr int SA = TA::STAGE_BYTES, SB = TB::STAGE_BYTES;
-    constexpr int A_COPIES = 8, NCOPY = 16;               // 1 KB copies per wave and phase
+    constexpr int A_COPIES = TA::COPIES, NCOPY = TA::COPIES + TB::COPIES;   // per wave and phase
+    constexpr int NMFMA = FM * FN;                        // matrix instructions per step
     constexpr int NREAD = TA::READS + TB::READS;          // LDS reads per step
-    static_assert(NREAD <= 32, "one read per matrix instruction, in the first half of a step");
+    static_assert(NREAD <= 2 * NMFMA / 3, "one read per matrix instruction, in the first two thirds of a step");
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * (SA + SB)];
 
     const int tid = threadIdx.x;
@@ -160,11 +179,20 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
 
     // Copies 0..7 fill A's tile, 8..15 B's (byte offsets: the launcher keeps
     // both operands below 2^31 bytes with a tile's overhang).
+    // Lanes of an mn-contiguous factor's copies beyond a 192-wide tile copy
+    // zeros into unread bytes: their offsets lie past the end.
+    constexpr uint32_t kPastEnd = 0x80000000u;              // beyond any descriptor here
+    constexpr int CMAX = TA::COPIES > TB::COPIES ? TA::COPIES : TB::COPIES;
+    constexpr bool DEAD_A = !KCA && BT < 256, DEAD_B = !KCB && BT < 256;   // such lanes exist
     uint32_t doff[NCOPY];
 #pragma unroll
-    for (int j = 0; j < A_COPIES; ++j) {
-        doff[j] = (uint32_t)TA::copy_src(wave_u, j, lane, m0, p.lda);
-        doff[A_COPIES + j] = (uint32_t)TB::copy_src(wave_u, j, lane, n0, p.ldb);
+    for (int j = 0; j < CMAX; ++j) {
+        if (j < TA::COPIES) doff[j] = (uint32_t)TA::copy_src(wave_u, j, lane, m0, p.lda);
+        if (j < TB::COPIES) doff[A_COPIES + j] = (uint32_t)TB::copy_src(wave_u, j, lane, n0, p.ldb);
+        if constexpr (DEAD_A)
+            if (j < TA::COPIES && TA::copy_mn(wave_u, j, lane) >= BT) doff[j] = kPastEnd;
+        if constexpr (DEAD_B)
+            if (j < TB::COPIES && TB::copy_mn(wave_u, j, lane) >= BT) doff[A_COPIES + j] = kPastEnd;
     }
     constexpr int kRawBufferWord3 = 0x00020000;
     const int64_t a_rows = KCA ? p.M : p.K, a_cols = KCA ? p.K : p.M;
@@ -174,15 +202,19 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(p.B), (short)0, (int)(2 * ((b_rows - 1) * p.ldb + b_cols)), kRawBufferWord3);
     const int P = ceil_div(p.K, BK);
-    constexpr uint32_t kPastEnd = 0x80000000u;              // beyond any descriptor here
     const int klast = (P - 1) * BK;                         // the last phase's first k
     uint32_t dlast[NCOPY];
 #pragma unroll
-    for (int j = 0; j < A_COPIES; ++j) {
+    for (int j = 0; j < CMAX; ++j) {
         const int ka = klast + TA::copy_k(wave_u, j, lane);
         const int kb = klast + TB::copy_k(wave_u, j, lane);
-        dlast[j] = ka >= p.K ? kPastEnd : doff[j] + (uint32_t)TA::phase_bytes(klast, p.lda);
-        dlast[A_COPIES + j] = kb >= p.K ? kPastEnd : doff[A_COPIES + j] + (uint32_t)TB::phase_bytes(klast, p.ldb);
+        if (j < TA::COPIES)
+            dlast[j] = ka >= p.K || (DEAD_A && doff[j] == kPastEnd) ? kPastEnd
+                                                                     : doff[j] + (uint32_t)TA::phase_bytes(klast, p.lda);
+        if (j < TB::COPIES)
+            dlast[A_COPIES + j] = kb >= p.K || (DEAD_B && doff[A_COPIES + j] == kPastEnd)
+                                      ? kPastEnd
+                                      : doff[A_COPIES + j] + (uint32_t)TB::phase_bytes(klast, p.ldb);
     }
     // Copy j of the phase at k0 into stage buf; LAST: the phase is the last
     // (its offsets hold the phase; k0 is not used).
@@ -219,9 +251,10 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     // trip of the loop).
     u32x4 aq[2][FM], bq[2][FN];
     u32x2 ah[2][FM][2], bh[2][FN][2];
+    static_assert(FM == FN, "square tiles");
     // Read i (0 .. READS - 1) of one factor's fragments of step s into set
     // (q, h): KC, fragment i; MC, half i % 2 of fragment i / 2.
-    auto read_one = [&](auto tile, u32x4 (&q)[8], u32x2 (&hv)[8][2], const uint32_t* base, int s, int i)
+    auto read_one = [&](auto tile, u32x4 (&q)[FM], u32x2 (&hv)[FM][2], const uint32_t* base, int s, int i)
                         __attribute__((always_inline)) {
         using T = decltype(tile);
         if constexpr (T::IS_KC) q[i] = lds_read128(base[s] + T::read_imm(s, i, 0));
@@ -259,24 +292,26 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // One step: the 64 matrix instructions on set t (block (q / 8, q % 8)
-    // for instruction q); after instruction q, read q of step rs into set
-    // t ^ 1 (if R and q < NREAD) and, after every fourth, copy q / 4 of the
-    // phase at k_copy into stage cbuf (if C; the last phase if lastc).
+    // One step: the NMFMA matrix instructions on set t (block (q / FN, q %
+    // FN) for instruction q); after instruction q, read q of step rs into set
+    // t ^ 1 (if R and q < NREAD) and, if C, copy c of the phase at k_copy
+    // into stage cbuf (the last phase if lastc) after instruction
+    // NMFMA (c + 1) / NCOPY - 1 (every fourth for a 256 tile).
     auto step = [&](int t, auto reads, int rs, auto copies, int k_copy, int cbuf, auto lastc)
                     __attribute__((always_inline)) {
         constexpr bool R = decltype(reads)::value;
         constexpr bool C = decltype(copies)::value;
-        unroll<FM * FN>([&](auto qc) __attribute__((always_inline)) {
+        unroll<NMFMA>([&](auto qc) __attribute__((always_inline)) {
             constexpr int q = decltype(qc)::value;
+            constexpr int c = (NCOPY * (q + 1) - 1) / NMFMA;   // the copy that ends at q, if any
             acc[q / FN][q % FN] = mfma16x16<FMT>(frag_a(t, q / FN), frag_b(t, q % FN), acc[q / FN][q % FN]);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (R && q < NREAD) {
                 read_op(rs, t ^ 1, q);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (C && q % 4 == 3) {
-                copy(q / 4, k_copy, cbuf, lastc);
+            if constexpr (C && NMFMA * (c + 1) / NCOPY - 1 == q) {
+                copy(c, k_copy, cbuf, lastc);
                 __builtin_amdgcn_sched_barrier(0);
             }
         });
@@ -324,7 +359,7 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
             for (int j = 0; j < NCOPY; ++j) copy(j, BK, 1, no{});
         }
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        wait_copies_below<NCOPY>();
     }
     __syncthreads();
     asm volatile("" ::: "memory");
@@ -355,7 +390,7 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
             for (int d = 0; d < 4; ++d)
                 m[d] = (2 * d < kv ? 0x0000FFFFu : 0u) | (2 * d + 1 < kv ? 0xFFFF0000u : 0u);
 #pragma unroll
-            for (int f = 0; f < 8; ++f) {
+            for (int f = 0; f < FM; ++f) {
                 if constexpr (KCA) aq[t][f] &= m;
                 if constexpr (KCB) bq[t][f] &= m;
             }
@@ -371,8 +406,8 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     // Guarded store (edge tiles run whole and store only what lies inside
     // C): register r of block (i, j) of lane l is row 16 i + 4 (l / 16) + r,
     // column 16 j + l % 16 of the wave's span.  Consecutive stores cover one
-    // row across the eight blocks (512 contiguous bytes per lane group;
-    // measured 1 % faster at 8192^3 than block by block).
+    // row across the blocks (512 contiguous bytes per lane group for a 256
+    // tile; measured 1 % faster at 8192^3 than block by block).
     const int row0 = m0 + wm * WM + 4 * (lane >> 4), col0 = n0 + wn * WN + (lane & 15);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -387,12 +422,30 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
         }
 }
 
-template <int FMT, bool KCA, bool KCB>
+template <int FMT, bool KCA, bool KCB, int BT>
 hipError_t launch_wide_kernel(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
                               unsigned blocks) {
-    hipLaunchKernelGGL((gemm16_wide_kernel<FMT, KCA, KCB>), dim3(blocks), dim3(256), 0, s, p, tiles_m, tiles_n,
+    hipLaunchKernelGGL((gemm16_wide_kernel<FMT, KCA, KCB, BT>), dim3(blocks), dim3(256), 0, s, p, tiles_m, tiles_n,
                        group_m);
     return hipGetLastError();
+}
+
+template <int BT>
+hipError_t launch_wide_tiles(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m) {
+    const int tiles_m = ceil_div(p.M, BT), tiles_n = ceil_div(p.N, BT);
+    const int64_t blocks = (int64_t)tiles_m * tiles_n;
+    if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const unsigned nb = (unsigned)blocks;
+    switch (4 * (format ? 1 : 0) + 2 * (op_a ? 1 : 0) + (op_b ? 1 : 0)) {
+        case 0: return launch_wide_kernel<0, true, false, BT>(p, s, tiles_m, tiles_n, group_m, nb);
+        case 1: return launch_wide_kernel<0, true, true, BT>(p, s, tiles_m, tiles_n, group_m, nb);
+        case 2: return launch_wide_kernel<0, false, false, BT>(p, s, tiles_m, tiles_n, group_m, nb);
+        case 3: return launch_wide_kernel<0, false, true, BT>(p, s, tiles_m, tiles_n, group_m, nb);
+        case 4: return launch_wide_kernel<1, true, false, BT>(p, s, tiles_m, tiles_n, group_m, nb);
+        case 5: return launch_wide_kernel<1, true, true, BT>(p, s, tiles_m, tiles_n, group_m, nb);
+        case 6: return launch_wide_kernel<1, false, false, BT>(p, s, tiles_m, tiles_n, group_m, nb);
+        default: return launch_wide_kernel<1, false, true, BT>(p, s, tiles_m, tiles_n, group_m, nb);
+    }
 }
 
 }  // namespace
@@ -415,20 +468,11 @@ bool wide_fits(const Gemm16Args& p, int op_a, int op_b) {
 }
 
 hipError_t launch_wide16(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m) {
-    const int tiles_m = ceil_div(p.M, 256), tiles_n = ceil_div(p.N, 256);
-    const int64_t blocks = (int64_t)tiles_m * tiles_n;
-    if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    const unsigned nb = (unsigned)blocks;
-    switch (4 * (format ? 1 : 0) + 2 * (op_a ? 1 : 0) + (op_b ? 1 : 0)) {
-        case 0: return launch_wide_kernel<0, true, false>(p, s, tiles_m, tiles_n, group_m, nb);
-        case 1: return launch_wide_kernel<0, true, true>(p, s, tiles_m, tiles_n, group_m, nb);
-        case 2: return launch_wide_kernel<0, false, false>(p, s, tiles_m, tiles_n, group_m, nb);
-        case 3: return launch_wide_kernel<0, false, true>(p, s, tiles_m, tiles_n, group_m, nb);
-        case 4: return launch_wide_kernel<1, true, false>(p, s, tiles_m, tiles_n, group_m, nb);
-        case 5: return launch_wide_kernel<1, true, true>(p, s, tiles_m, tiles_n, group_m, nb);
-        case 6: return launch_wide_kernel<1, false, false>(p, s, tiles_m, tiles_n, group_m, nb);
-        default: return launch_wide_kernel<1, false, true>(p, s, tiles_m, tiles_n, group_m, nb);
-    }
+    return launch_wide_tiles<256>(p, s, format, op_a, op_b, group_m);
+}
+
+hipError_t launch_wide16_192(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m) {
+    return launch_wide_tiles<192>(p, s, format, op_a, op_b, group_m);
 }
 
 }  // namespace gemmf32

@@ -410,18 +410,33 @@ def test_default_variant_choices(binding):
     mixed = {
         (8192, 8192, 8192): "mixed256x256_bk64_w4_wide",
         (4096, 4096, 64): "mixed256x256_bk64_w4_wide",
-        (3072, 3072, 3072): "mixed256x256_bk64_w4_wide",          # 144 tiles of 256
-        (4100, 4100, 4096): "mixed256x256_bk64_w4_wide",          # edge tiles, N even
-        (2560, 2560, 2560): "mixed128x128_bk64_w2x2_directAB",    # 100 tiles of 256, 400 of 128
+        (3072, 3072, 3072): "mixed192x192_bk64_w4_wide",          # one round of 256 tiles of 192
+        (3072, 3072, 3071): "mixed256x256_bk64_w4_wide",          # odd K
+        (4100, 4100, 4096): "mixed192x192_bk64_w4_wide",          # 2 rounds of 192 (484) as of 256 (289)
+        (3584, 3584, 3584): "mixed256x256_bk64_w4_wide",          # 196 tiles of 256, 361 of 192
+        (4608, 4608, 4608): "mixed256x256_bk64_w4_wide",          # 2 rounds of 256, 3 of 192
+        (2048, 4096, 1024): "mixed192x192_bk64_w4_wide",          # 128 tiles of 256, 242 of 192
+        (1024, 8192, 2048): "mixed256x256_bk64_w4_wide",          # 258 tiles of 192: 2 rounds
+        (2816, 2816, 2816): "mixed192x192_bk64_w4_wide",          # 121 of 256, 225 of 192
+        (2560, 2560, 2560): "mixed192x192_bk64_w4_wide",          # 100 tiles of 256, 196 of 192
+        (2304, 2304, 2304): "mixed192x192_bk64_w4_wide",          # 144 tiles of 192
+        (1024, 4096, 1024): "mixed128x128_bk32_w4_ksplit",        # 256 tiles of 128, long K
+        (1536, 2560, 768): "mixed128x128_bk64_w2x2_directAB",     # 112 tiles of 192
+        (2560, 2560, 2561): "mixed128x128_bk64_w2x2_directAB",    # odd K
         (2048, 2048, 2048): "mixed128x128_bk32_w4_ksplit",        # 256 tiles of 128, long K
         (1536, 1536, 1536): "mixed128x128_bk32_w4_ksplit",        # 144 tiles of 128
         (2048, 2048, 256): "mixed128x128_bk64_w2x2_directAB",     # 256 tiles of 128, short K
-        (2048, 2048, 2044): "mixed128x128_bk64_w2x2_directAB",    # K % 8 = 4
+        (2048, 2048, 2044): "mixed128x128_bk64_w2x2_directAB",    # K % 8 = 4, 256 tiles of 128, long K
         (1024, 1024, 4096): "mixed64x64_bk32_w4_ksplit",          # 64 tiles of 128: k-split
         (1024, 1024, 1024): "mixed64x64_bk32_w4_ksplit",
         (1000, 1000, 1000): "mixed64x64_bk32_w4_ksplit",
         (512, 512, 8192): "mixed64x64_bk32_w4_ksplit",
-        (1024, 1024, 4092): "mixed128x128_bk64_w2x2_directAB",    # K % 8 = 4: 64 tiles of 128, K >= 2048
+        (1024, 1024, 4092): "mixed128x128_bk64_w2x2_directAB",    # K % 8 = 4, long K: 64 tiles of 128
+        (1000, 1000, 2002): "mixed192x192_bk64_w4_wide",          # K % 4 = 2, 64 tiles of 128
+        (800, 1200, 3002): "mixed192x192_bk64_w4_wide",           # K % 4 = 2, 35 tiles of 192
+        (1000, 2000, 500): "mixed192x192_bk64_w4_wide",           # K % 8 = 4: 66 tiles of 192
+        (1536, 1536, 1538): "mixed128x128_bk64_w2x2_directAB",    # K % 8 = 2, 144 tiles of 128, long K
+        (512, 512, 1002): "mixed64x64_bk64_w1x2",                 # K % 8 = 2, 9 tiles of 192
         (1000, 1000, 1001): "mixed64x64_bk64_w1x2",
     }
     for (M, N, K), name in mixed.items():

@@ -34,7 +34,7 @@ FP32_CASES = {
     "mfma128x128_bk32_w2x2_sched": (1532, 1404, 164),
     "mfma64x64_bk32_w1x1_k4_sched": (556, 572, 1004),
 }
-MIXED_CASES = {"mixed256x256_bk64_w4_wide": (3068, 3068, 200)}
+MIXED_CASES = {"mixed256x256_bk64_w4_wide": (3580, 3330, 200), "mixed192x192_bk64_w4_wide": (3068, 3068, 200)}
 
 
 def stored(op, rows, cols):

@@ -121,10 +121,11 @@ def test_variant_repeats_bit_for_bit():
 
 
 OPS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
-# shapes gemm_mixed_op gives to the kernel (at least 128 tiles of 256 x 256);
-# the last two with K % 8 != 0 (a k-contiguous factor's last chunk straddles
-# K in step 0, then step 1, of the last phase)
-OP_SHAPES = [(3072, 2816, 72), (2824, 3080, 136), (2824, 3080, 76), (3072, 2816, 110)]
+# shapes gemm_mixed_op gives to the kernel (at least 128 tiles of 256 x 256,
+# one round of them against two of 192 x 192); edge tiles in N, then in
+# both; the last two with K % 8 != 0 (a k-contiguous factor's last chunk
+# straddles K in step 0, then step 1, of the last phase)
+OP_SHAPES = [(3584, 3330, 72), (3580, 3336, 136), (3580, 3336, 76), (3584, 3330, 110)]
 
 
 @pytest.mark.parametrize("ops", OPS, ids=["".join(o) for o in OPS])

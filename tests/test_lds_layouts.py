@@ -727,33 +727,39 @@ def wide_read(kc, lane, mn, s, f, h):
     return 1056 * (j // 4 + 4 * g) + 2 * (mn + 4 * (j % 4)) + (16896 * s + 32 * f + 512 * h)
 
 
+@pytest.mark.parametrize("bt", [256, 192])
 @pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
-def test_wide16_kernel_layout(kc):
-    """The 16 x 16 x 32 scheduled kernel's tile stage (256 mn x 64 k),
-    restated: the 32 copies (8 per wave) fill every (mn, k) exactly once
-    (the MC stage's padding is never written); every lane's fragment reads
-    deliver the operands v_mfma_f32_16x16x32 needs -- for the wave's span at
-    mn, block f of step s, lane l supplies op(X)[mn + 16 f + l % 16][32 s +
-    8 (l / 16) + e], e = 0..7; both reads conflict free on 64 banks (128-bit:
-    the measured quad grouping; 64-bit transposed: 32 lanes per cycle) with
-    instruction offsets below 2^16."""
-    stage = 32768 if kc else 32 * 1056
-    where = {}                                   # LDS byte (even) -> (mn, k)
+def test_wide16_kernel_layout(kc, bt):
+    """The 16 x 16 x 32 scheduled kernel's tile stage (bt mn x 64 k, bt =
+    256 or 192), restated: the copies (KC bt / 32 per wave, MC 8) fill every
+    (mn, k) exactly once (the MC stage's padding is never written; with bt =
+    192 the lanes of an MC copy past the tile bring zeros into the last 128
+    bytes of each 512-byte row slot, which no read touches); every lane's
+    fragment reads deliver the operands v_mfma_f32_16x16x32 needs -- for the
+    wave's span at mn, block f of step s, lane l supplies op(X)[mn + 16 f + l
+    % 16][32 s + 8 (l / 16) + e], e = 0..7; both reads conflict free on 64
+    banks (128-bit: the measured quad grouping; 64-bit transposed: 32 lanes
+    per cycle) with instruction offsets below 2^16."""
+    stage = 128 * bt if kc else 32 * 1056
+    copies = bt // 32 if kc else 8
+    where = {}                                   # LDS byte (even) -> (mn, k), or None for a zero
     for w in range(4):
-        for j in range(8):
+        for j in range(copies):
             for lane in range(64):
                 dst, mn, k = wide_copy(kc, w, j, lane)
+                dead = not kc and mn >= bt       # offset past the end: zeros
                 for e in range(8):
                     assert dst + 2 * e not in where
-                    where[dst + 2 * e] = (mn, k + e) if kc else (mn + e, k)
-    assert sorted(set(where.values())) == [(m, k) for m in range(256) for k in range(64)]
+                    where[dst + 2 * e] = None if dead else ((mn, k + e) if kc else (mn + e, k))
+    assert sorted(v for v in set(where.values()) if v) == [(m, k) for m in range(bt) for k in range(64)]
     assert max(where) < stage
     if not kc:
         pads = {1056 * m + 1024 + 2 * x for m in range(32) for x in range(16)}
         assert not pads & set(where)
-    for mn in (0, 128):
+    nf = bt // 32
+    for mn in (0, bt // 2):
         for s in range(2):
-            for f in range(8):
+            for f in range(nf):
                 imm = (2048 * f) if kc else (16896 * s + 32 * f + 512)
                 assert imm < 1 << 16
                 if kc:
@@ -781,37 +787,44 @@ def test_wide16_kernel_layout(kc):
                         assert vals[lane] == want, (mn, s, f, lane)
 
 
+@pytest.mark.parametrize("bt", [256, 192])
 @pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
 @pytest.mark.parametrize("shape", [(3068, 200, 3072), (2814, 72, 2818), (256, 64, 256), (4100, 8, 4100)])
-def test_wide16_copies_never_depend_on_the_scalar_offset(kc, shape):
-    """16 x 16 x 32 scheduled kernel: the rule of the 32 x 32 x 16 one with
-    its own copy map -- phases before the last take the phase in the scalar
-    offset, the last phase's per-lane offsets hold it with a scalar offset
-    of 0 and point lanes at k >= K past the end; only a chunk of the
-    mn-contiguous factor's last row across its last column may straddle the
-    descriptor's end, by whole dwords."""
+def test_wide16_copies_never_depend_on_the_scalar_offset(kc, shape, bt):
+    """16 x 16 x 32 scheduled kernel (256 or 192 tiles): the rule of the 32 x
+    32 x 16 one with its own copy map -- phases before the last take the
+    phase in the scalar offset, the last phase's per-lane offsets hold it
+    with a scalar offset of 0 and point lanes at k >= K past the end; lanes
+    of an mn-contiguous copy beyond a 192 tile are past the end in every
+    phase; only a chunk of the mn-contiguous factor's last row across its
+    last column may straddle the descriptor's end, by whole dwords."""
     ext, K, ld_mn = shape
     rows, cols = (ext, K) if kc else (K, ext)
     ld = (K + 8) if kc else ld_mn
     nrec = 2 * ((rows - 1) * ld + cols)
     assert nrec % 4 == 0
     P = -(-K // 64)
-    for mn0 in sorted({0, (ext - 1) // 256 * 256}):
+    copies = bt // 32 if kc else 8
+    for mn0 in sorted({0, (ext - 1) // bt * bt}):
         for w in range(4):
-            for j in range(8):
+            for j in range(copies):
                 for lane in range(64):
                     _, mnl, kl = wide_copy(kc, w, j, lane)
                     mn = mn0 + mnl
-                    doff = 2 * (mn * ld + kl) if kc else 2 * (kl * ld + mn)
+                    dead = not kc and mnl >= bt
+                    doff = PAST_END if dead else (2 * (mn * ld + kl) if kc else 2 * (kl * ld + mn))
                     for ph in range(P):
                         k0 = 64 * ph
                         k = k0 + kl
                         pb = 2 * k0 if kc else 2 * k0 * ld
                         if ph == P - 1:
-                            voff, soff = (PAST_END if k >= K else doff + pb), 0
+                            voff, soff = (PAST_END if k >= K or dead else doff + pb), 0
                         else:
                             voff, soff = doff, pb
                         what = (kc, shape, mn0, w, j, lane, ph)
+                        if dead:
+                            _check_copy(voff, soff, nrec, 16, True, False, what)
+                            continue
                         if not kc and k < K and mn < ext < mn + 8 and voff < nrec < voff + soff + 16:
                             assert k == K - 1 and ph == P - 1 and soff == 0, what
                             assert (nrec - voff) % 4 == 0 and nrec - voff == 2 * (ext - mn), what
