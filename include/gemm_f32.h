@@ -400,6 +400,11 @@ int reduce_sum_f32_variant_noalloc(int variant, int64_t n, const float *x, float
  * 0.8 of a 256 tile's time each, or, below 128 tiles of 256 x 256, with at
  * least 140 of 192 x 192 or, for K % 8 != 0, 32 of them with K < 1536 (or
  * K % 4 == 2 and fewer than 128 tiles of 128 x 128)),
+ * mixed256x256_rowsplit (their choice, with K a multiple of 8, where the
+ * last round of 256 x 256 tiles would be under 40 % full: the rows filling
+ * the other rounds on the 256 x 256 kernel, the remaining rows on k-split
+ * 128 x 128 tiles if at most 256 of them, else on 192 x 192 tiles; two
+ * launches in stream order),
  * mixed256x256_bk64_w4_sched (the same schedule on v_mfma_f32_32x32x16) and
  * mixed256x256_bk32_w4_wide4stage (16x16x32 with four 32-deep LDS stages) --
  * take K a multiple of 8 (the two 16x16x32 wide ones: K even), N even (M

@@ -1126,6 +1126,42 @@ hipError_t launch_wide192_cfg(const Gemm16Args& p, hipStream_t s, int /*tiles_m*
     return launch16<FMT, 256, 256, 2, 4, false, false, false>(p, s, tm, tn, kSchedGroupM, nb);
 }
 
+// Rows split (configuration 14): the first 256 m1 rows of op(A) -- whole
+// tile rows filling all but the last round of 256 CUs -- on 256 x 256 tiles
+// of the 16 x 16 x 32 scheduled kernel, the rest on 128 x 128 tiles whose
+// four waves split the phases (if those are at most 256 and it takes the
+// problem), else on 192 x 192 tiles; two launches in stream order, each part
+// with the bits its kernel gives alone.  Where the 256 x 256 kernel does
+// not take the problem, or there is no such split, configuration 10 runs
+// the whole product.  op_a / op_b: 1 if that factor is stored transposed.
+int rowsplit_rows(int M, int N) {
+    const int64_t tm = ceil_div(M, 256), tn = ceil_div(N, 256);
+    const int64_t rounds = (tm * tn + 255) / 256;
+    const int64_t m1 = 256 * (rounds - 1) / tn;
+    return (rounds >= 2 && m1 >= 1 && m1 < tm) ? (int)(256 * m1) : 0;
+}
+hipError_t launch_rowsplit(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b) {
+    const int rows = rowsplit_rows(p.M, p.N);
+    if (rows == 0 || !wide_fits(p, op_a, op_b)) return hipErrorNotSupported;
+    Gemm16Args top = p, rest = p;
+    top.M = rows;
+    rest.M = p.M - rows;
+    rest.A = p.A + (op_a ? (int64_t)rows : (int64_t)rows * p.lda);
+    rest.C = p.C + (int64_t)rows * p.ldc;
+    hipError_t e = launch_wide16(top, s, format, op_a, op_b, kSchedGroupM);
+    if (e != hipSuccess) return e;
+    const int64_t t128 = (int64_t)ceil_div(rest.M, 128) * ceil_div(rest.N, 128);
+    if (t128 <= 256 && ksplit128_fits(rest, op_a, op_b))
+        return launch_ksplit128(rest, s, format, op_a, op_b, kKsplit128GroupM);
+    return launch_wide16_192(rest, s, format, op_a, op_b, kWide192GroupM);
+}
+template <int FMT>
+hipError_t launch_rowsplit_cfg(const Gemm16Args& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
+                               unsigned blocks) {
+    if (rowsplit_rows(p.M, p.N) == 0 || !wide_fits(p, 0, 0)) return launch_wide_cfg<FMT>(p, s, tiles_m, tiles_n, group_m, blocks);
+    return launch_rowsplit(p, s, FMT, 0, 0);
+}
+
 // Configuration 11 (the four-stage form, mfma16_wide4.hip) where it takes
 // the problem; else the 8-wave kernel, as for configuration 8.
 template <int FMT>
@@ -1173,6 +1209,12 @@ const MixedConfig kMixed[] = {
     {"mixed192x192_bk64_w4_wide", 192, 192, kWide192GroupM,
      {{launch_wide192_cfg<0, false>, launch_wide192_cfg<0, true>},
       {launch_wide192_cfg<1, false>, launch_wide192_cfg<1, true>}}},
+    // the rows of all but the last round of 256 x 256 tiles on them, the rest
+    // on k-split 128 x 128 or on 192 x 192 tiles; misaligned operands: the
+    // element-wise 8-wave kernel, as for 6
+    {"mixed256x256_rowsplit", 256, 256, kSchedGroupM,
+     {{launch16<0, 256, 256, 2, 4, false, false, false>, launch_rowsplit_cfg<0>},
+      {launch16<1, 256, 256, 2, 4, false, false, false>, launch_rowsplit_cfg<1>}}},
 };
 #undef MIXED
 constexpr int kNumMixed = (int)(sizeof(kMixed) / sizeof(kMixed[0]));
@@ -1180,6 +1222,7 @@ constexpr int kKsplitConfig = 9;          // mixed64x64_bk32_w4_ksplit
 constexpr int kWideConfig = 10;           // mixed256x256_bk64_w4_wide
 constexpr int kKsplit128Config = 12;      // mixed128x128_bk32_w4_ksplit
 constexpr int kWide192Config = 13;        // mixed192x192_bk64_w4_wide
+constexpr int kRowsplitConfig = 14;       // mixed256x256_rowsplit
 
 // op kernels, chosen by tile, op pair and load path
 template <int FMT, int BM, int BN, int WM, int WN, bool KCA, bool KCB, bool VEC>
@@ -1224,6 +1267,8 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
         return launch_ksplit128(p, s, format, op_a, op_b, kKsplit128GroupM);
     if (pick == kWide192Config && wide_fits(p, op_a, op_b))
         return launch_wide16_192(p, s, format, op_a, op_b, kWide192GroupM);
+    if (pick == kRowsplitConfig && rowsplit_rows(p.M, p.N) > 0 && wide_fits(p, op_a, op_b))
+        return launch_rowsplit(p, s, format, op_a, op_b);
     const bool big = t256 >= 128;
     const int tile = big ? 256 : 128;
     const int tiles_m = ceil_div(p.M, tile), tiles_n = ceil_div(p.N, tile);
@@ -1251,7 +1296,11 @@ const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed
 // instructions): 4 rounds of 192 < 5 rounds of 256 (bf16: 3072^3 1169
 // against 944 TFLOP/s, 4100^2 x 4096 1078 against 830, 2048 x 4096 x 1024
 // 709 against 581; 3584^3, one round of 256 against two of 192, 1278
-// against 893).  Else, below
+// against 893).  Else, with K a multiple of 8 and the last round of 256 x
+// 256 tiles under 40 % full, the rows split (configuration 14): 4352^3 1173
+// against 955, 4608^3 1170 against 1074, 7168^3 1373 against 1253, 8200^2 x
+// 4096 1303 against 1254, 4000 x 5000 x 4096 1079 against 996 (6144^3 1219
+// against 1266: the one loss measured).  Else, below
 // 128 tiles of 128 x 128 and with K a multiple of 8, 64 x 64 tiles whose
 // four waves split the phases (mfma16_ksplit.hip; measured bf16: 1024^2 x
 // 4096 479 against 186 TFLOP/s on the 128 x 128 tiles, 1000^3 234 against
@@ -1279,7 +1328,11 @@ int mixed_pick_config(int M, int N, int K) {
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
     const bool even_k = K > 0 && K % 2 == 0;
     const int64_t r256 = (t256 + 255) / 256, r192 = (t192 + 255) / 256;   // rounds of 256 CUs
-    if (t256 >= 128) return even_k && 4 * r192 < 5 * r256 ? kWide192Config : kWideConfig;
+    if (t256 >= 128) {
+        if (even_k && 4 * r192 < 5 * r256) return kWide192Config;
+        const int64_t last = t256 - 256 * (r256 - 1);      // tiles in the last round
+        return K % 8 == 0 && 5 * last < 2 * 256 && rowsplit_rows(M, N) > 0 ? kRowsplitConfig : kWideConfig;
+    }
     if (t128 < 128 && K % 8 == 0 && K > 0) return kKsplitConfig;
     if (t128 <= 256 && K >= 1024 && K % 8 == 0) return kKsplit128Config;
     const bool ragged_k = K % 8 != 0 && t192 >= 32 && (K < 1536 || (t128 < 128 && K % 4 == 2));

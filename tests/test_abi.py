@@ -414,7 +414,12 @@ def test_default_variant_choices(binding):
         (3072, 3072, 3071): "mixed256x256_bk64_w4_wide",          # odd K
         (4100, 4100, 4096): "mixed192x192_bk64_w4_wide",          # 2 rounds of 192 (484) as of 256 (289)
         (3584, 3584, 3584): "mixed256x256_bk64_w4_wide",          # 196 tiles of 256, 361 of 192
-        (4608, 4608, 4608): "mixed256x256_bk64_w4_wide",          # 2 rounds of 256, 3 of 192
+        (4608, 4608, 4608): "mixed256x256_rowsplit",              # 324 tiles of 256: last round 68
+        (4352, 4352, 4352): "mixed256x256_rowsplit",              # 289: last round 33
+        (4352, 4352, 4350): "mixed256x256_bk64_w4_wide",          # K % 8 != 0
+        (7168, 7168, 7168): "mixed256x256_rowsplit",              # 784: last round 16
+        (5120, 5120, 5120): "mixed256x256_bk64_w4_wide",          # 400: last round 144
+        (8192, 4096, 2048): "mixed256x256_bk64_w4_wide",          # 512: two full rounds
         (2048, 4096, 1024): "mixed192x192_bk64_w4_wide",          # 128 tiles of 256, 242 of 192
         (1024, 8192, 2048): "mixed256x256_bk64_w4_wide",          # 258 tiles of 192: 2 rounds
         (2816, 2816, 2816): "mixed192x192_bk64_w4_wide",          # 121 of 256, 225 of 192
