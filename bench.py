@@ -459,9 +459,10 @@ def bench_transpose(args, w) -> int:
     return 0
 
 
-# Timed launches per workload: many for the microsecond-scale small products,
+# Timed launches per workload: many for the microsecond-scale small products
+# (100 per timed window, so that the event between windows weighs little),
 # fewer for the large ones.
-WORKLOAD_LAUNCHES = {"square256": 200, "square1000": 100, "square4096": 20,
+WORKLOAD_LAUNCHES = {"square256": 1000, "square1000": 1000, "square4096": 20,
                      "rect8192x4096x2048_padded": 20, "square8192": 10}
 
 
@@ -482,7 +483,7 @@ SWEEP_CANDIDATES = ["mfma64x64_bk32_w2x2_k4", "mfma64x64_bk16_w2x2_k4", "mfma64x
 MIXED_SWEEP_CANDIDATES = ["mixed64x64_bk64_w1x2", "mixed64x64_bk32_w4_ksplit", "mixed128x128_bk64_w2x2_directAB",
                           "mixed256x256_bk64_w2x4_directAB", "mixed256x256_bk64_w4_sched",
                           "mixed256x256_bk64_w4_wide", "mixed256x256_bk32_w4_wide4stage", "mixed128x128_bk32_w4_ksplit",
-                          "mixed192x192_bk64_w4_wide"]
+                          "mixed192x192_bk64_w4_wide", "mixed256x256_rowsplit"]
 
 
 def bench_shape_sweep(args) -> int:
