@@ -16,6 +16,15 @@
 // 32-deep steps of 64 instructions (the same matrix-core clocks).  In a bare
 // loop this form sustains a higher clock on MI355X than 32 x 32 x 16.
 //
+// The same kernel runs 192 x 192 tiles (template parameter BT): waves of 96
+// x 96 (6 x 6 blocks), steps of 36 instructions, 6 copies per wave and phase
+// for a k-contiguous factor (rows 0..191 of the layout below) and 8 for an
+// mn-contiguous one (the layout below with each 512-byte k-row slot holding
+// 192 values, the lanes of values 192..255 copying zeros).  Its copies need
+// 42.7 bytes per clock per CU at the full matrix rate against 32 for 256 x
+// 256 tiles: it is chosen only where its tile count fills the rounds of 256
+// CUs much better.
+//
 // The LDS tiles are laid out so that at most two per-lane bases per factor
 // serve every fragment, step and read of a phase (all the rest are
 // instruction offsets), and both kinds read without bank conflicts (64 banks
@@ -177,10 +186,11 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     const int m0 = (first_m + in_g % gm) * BM;
     const int n0 = (in_g / gm) * BN;
 
-    // Copies 0..7 fill A's tile, 8..15 B's (byte offsets: the launcher keeps
-    // both operands below 2^31 bytes with a tile's overhang).
+    // Copies 0 .. A_COPIES - 1 fill A's tile, the rest B's (byte offsets: the
+    // launcher keeps both operands below 2^31 bytes with a tile's overhang, so
+    // a past-the-end offset plus any phase's scalar offset stays below 2^32).
     // Lanes of an mn-contiguous factor's copies beyond a 192-wide tile copy
-    // zeros into unread bytes: their offsets lie past the end.
+    // zeros into unread bytes: their offsets lie past the end in every phase.
     constexpr uint32_t kPastEnd = 0x80000000u;              // beyond any descriptor here
     constexpr int CMAX = TA::COPIES > TB::COPIES ? TA::COPIES : TB::COPIES;
     constexpr bool DEAD_A = !KCA && BT < 256, DEAD_B = !KCB && BT < 256;   // such lanes exist
