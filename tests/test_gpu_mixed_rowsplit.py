@@ -88,3 +88,22 @@ def test_op_pairs_bit_identical_on_transposed_copies(fmt):
         out = binding.gemm16(A, B, op_a=op_a, op_b=op_b)
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"{op_a}{op_b} differs from the plain product"
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.parametrize("dist", ["int", "uniform"])
+def test_full_size_sampled(fmt, dist):
+    """Shapes gemm_mixed splits at full size (4352^3: the rest on k-split
+    tiles; 4608^3: on 192 x 192 tiles), on sampled entries of both parts
+    and the whole of the two rows either side of the split."""
+    from test_gpu_mixed_wide import run_sampled
+    for (M, N, K), split in [((4352, 4352, 4352), 3840), ((4608, 4608, 4608), 3584)]:
+        assert binding.gemm_mixed_variant_name(binding.gemm_mixed_default_variant(M, N, K)) == SPLIT
+        say(f"rowsplit sampled {fmt} {dist} {(M, N, K)}")
+        C, got, ref, S = run_sampled(fmt, M, N, K, dist, M + 5, rows=(split - 1, split))
+        what = f"{SPLIT} {fmt} {dist} {(M, N, K)} sampled"
+        if dist == "int":
+            check_exact(got, ref, what)
+        else:
+            check_close(got, ref, S, what)
+        check_padding_untouched(C)

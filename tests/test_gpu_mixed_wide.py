@@ -177,3 +177,29 @@ def test_misaligned_operands_fall_back_correctly():
     C, ref, _ = run("bf16", "N", "N", 300, 520, 136, "int", [1, 2, 3], offset=1, pad=(3, 5, 2), variant=v)
     check_exact(C.view, ref, "misaligned fallback")
     check_padding_untouched(C)
+
+
+def run_sampled(fmt, M, N, K, dist, seed, count=4096, rows=()):
+    """gemm_mixed on padded, offset, guarded operands of a full-size shape,
+    checked on `count` sampled entries plus the corners, every tile edge's
+    last row and column and the whole of each row in `rows`: returns (C,
+    the results at those entries, the oracle's values, the oracle's S)."""
+    gen = np.random.default_rng(seed)
+    Ab = inputs.to16(inputs.random_matrix(gen, M, K, dist), fmt)
+    Bb = inputs.to16(inputs.random_matrix(gen, K, N, dist), fmt)
+    A = inputs.padded16(Ab, K + 4, 2, fmt, guard=GUARD_ROWS * (K + 4) + 64)
+    B = inputs.padded16(Bb, N + 6, 2, fmt, guard=GUARD_ROWS * (N + 6) + 64)
+    ldc = N + 2
+    C0 = inputs.padded_output(M, N, ldc, 1)
+    a = torch.from_numpy(A.buf.view(np.int16)).cuda()
+    b = torch.from_numpy(B.buf.view(np.int16)).cuda()
+    c = torch.from_numpy(C0.buf).cuda()
+    binding.gemm_mixed(fmt, M, N, K, a.data_ptr() + 4, A.ld, b.data_ptr() + 4, B.ld, c.data_ptr() + 4, ldc)
+    torch.cuda.synchronize()
+    C = inputs.Padded(c.cpu().numpy(), M, N, ldc, 1)
+    ii, jj = inputs.sample_pairs(M, N, count, np.random.default_rng([seed, 1]), tiles=(64, 128, 192, 256))
+    if len(rows):
+        ii = np.concatenate([ii, np.repeat(np.asarray(rows, np.int64), N)])
+        jj = np.concatenate([jj, np.tile(np.arange(N, dtype=np.int64), len(rows))])
+    ref, S = oracle.gemm16_entries(fmt, A.view, B.view, ii, jj)
+    return C, C.view[ii, jj], ref, S

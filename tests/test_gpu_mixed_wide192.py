@@ -116,3 +116,21 @@ def test_op_pairs_bit_identical_on_transposed_copies(fmt):
         out = binding.gemm16(A, B, op_a=op_a, op_b=op_b)
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"{op_a}{op_b} differs from the plain product"
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.parametrize("dist", ["int", "uniform"])
+def test_full_size_sampled(fmt, dist):
+    """Shapes gemm_mixed gives to this kernel at full size (3072^3: 256
+    tiles; 4100^2 x 4096: edge tiles, two rounds), on sampled entries."""
+    from test_gpu_mixed_wide import run_sampled
+    for (M, N, K) in [(3072, 3072, 3072), (4100, 4100, 4096)]:
+        assert binding.gemm_mixed_variant_name(binding.gemm_mixed_default_variant(M, N, K)) == W192
+        say(f"wide192 sampled {fmt} {dist} {(M, N, K)}")
+        C, got, ref, S = run_sampled(fmt, M, N, K, dist, M + 3)
+        what = f"{W192} {fmt} {dist} {(M, N, K)} sampled"
+        if dist == "int":
+            check_exact(got, ref, what)
+        else:
+            check_close(got, ref, S, what)
+        check_padding_untouched(C)
