@@ -50,6 +50,7 @@ const Diagnostic kDiagnostics[] = {
     {"mfma32x32_w4_small", 3, 22},
     {"mfma16x16_w8_small", 3, 23},
     {"mfma96x96_bk16_w1x1_k4_sched", 3, 24},
+    {"mfma64x64_bk32_w2x2_sched", 3, 25},
 };
 constexpr int kNumDiagnostics = (int)(sizeof(kDiagnostics) / sizeof(kDiagnostics[0]));
 

@@ -612,6 +612,16 @@ hipError_t launch_ksplit96_or_ksplit(const GemmArgs& p, hipStream_t s, int, int,
     if (ksplit96_f32_fits(p, TRA, TRB)) return launch_ksplit96_f32(p, s, TRA, TRB, group_m);
     return launch_mfma(p, s, 20, TRA, TRB);
 }
+// The four-wave schedule on 64 x 64 tiles (one 32 x 32 block per wave, the
+// whole K) where it takes the problem, else configuration 20.
+template <bool TRA, bool TRB>
+hipError_t launch_sched64_or_ksplit(const GemmArgs& p, hipStream_t s, int, int, int group_m, unsigned) {
+    if (sched_f32_fits(p, TRA, TRB)) return launch_sched_f32(p, s, TRA, TRB, group_m, 64);
+    return launch_mfma(p, s, 20, TRA, TRB);
+}
+#define SCHED64_OPS                                                                          \
+    {launch_sched64_or_ksplit<false, false>, launch_sched64_or_ksplit<false, true>,          \
+     launch_sched64_or_ksplit<true, false>, launch_sched64_or_ksplit<true, true>}
 #define KSPLIT96_OPS                                                                          \
     {launch_ksplit96_or_ksplit<false, false>, launch_ksplit96_or_ksplit<false, true>,          \
      launch_ksplit96_or_ksplit<true, false>, launch_ksplit96_or_ksplit<true, true>}
@@ -680,6 +690,8 @@ const MfmaConfig kConfigs[] = {
     {"mfma16x16_w8_small", 16, 16, 512, 8, SMALL_OPS(2)},
     // four waves, each the whole 96 x 96 tile over every fourth 16-deep phase
     {"mfma96x96_bk16_w1x1_k4_sched", 96, 96, 1024, 8, KSPLIT96_OPS},
+    // four waves of one 32 x 32 block each over the whole K (2 x 2 per tile)
+    {"mfma64x64_bk32_w2x2_sched", 64, 64, 256, 8, SCHED64_OPS},
 };
 #undef NN_ONLY
 #undef ALL_OPS
@@ -689,6 +701,7 @@ const MfmaConfig kConfigs[] = {
 #undef SPLITK_OPS
 #undef KSPLIT_OPS
 #undef KSPLIT96_OPS
+#undef SCHED64_OPS
 #undef SMALL_OPS
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 }  // namespace
@@ -725,7 +738,16 @@ const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConf
 // and 12 us (fitted to 1536^3 and 4608^3, the fixed cost raised from 10 us so
 // that 3584^3, 5.6 rounds of them against 12.25 rounds of 64 x 64 k-split
 // tiles, keeps the latter, 2-3 % faster there; within 4 % of the measured
-// time at 2048^3, 2560^3, 3072^3, 5120^3, 6144^3 and 7168^3).  Last, products of at most 1024 output tiles of 16 x 16
+// time at 2048^3, 2560^3, 3072^3, 5120^3, 6144^3 and 7168^3).  Then 64 x 64
+// tiles on the four-wave schedule (one 32 x 32 block per wave over the whole
+// K, mfma_sched.hip) replace the choice, from K = 256, where the model gives
+// them the shorter time at 0.85 and 4 us once per launch (four of their
+// blocks share a CU; fitted to 22 shapes with K from 256 to 5120: 3000^2 x
+// 384 117 TFLOP/s against 98 on 128 x 128 tiles, 2048 x 3072 x 512 124
+// against 107 on the k-split tiles, 3072^2 x 768 132 against 120, 1000 x
+// 2000 x 500 102 against 93, 3000 x 7000 x 1024 131 against 123; with one
+// block per CU, 1000^3, they lose, 98 against 104: two stages of 32 k hide
+// less of the copies' latency than the k-split waves' longer phases).  Last, products of at most 1024 output tiles of 16 x 16
 // take the small-tile kernels (16 x 16 tiles on 8 waves up to 512 such
 // tiles, else 32 x 32 tiles on 4 waves).  Every picked configuration
 // is built for all four op combinations.
@@ -743,10 +765,15 @@ double model_ns(int config, int M, int N, int K) {
         case 1: tile = 128; rel = 4; eff = 0.85; fixed = 5300; break;
         case 20: tile = 64; rel = 1; eff = 0.914; fixed = 3000; break;
         case 24: tile = 96; rel = 2.25; eff = 0.9925; fixed = 12000; break;
+        case 25: tile = 64; rel = 1; eff = 0.85; fixed = 4000; break;
         default: return 1e300;                    // the split-phase 64 x 64 tiles: never kept over 20
     }
     const int64_t tiles = (int64_t)ceil_div(M, tile) * ceil_div(N, tile);
     const double rounds = (double)((tiles + 255) / 256);
+    // Configuration 25's blocks (32 KB of LDS) share a CU four at a time, so
+    // the start and end of one overlap the work of others: its fixed cost is
+    // paid once per launch, not per round.
+    if (config == 25) return rounds * rel * 13.33 * K / eff + fixed;
     return rounds * (rel * 13.33 * K / eff + fixed);
 }
 }  // namespace
@@ -771,6 +798,8 @@ int mfma_pick_config(int M, int N, int K) {
     if (split_fits && ((pick == small && K >= 384) || (K >= 448 && model_ns(20, M, N, K) < model_ns(pick, M, N, K))))
         pick = 20;
     if (split_fits && K >= 448 && model_ns(24, M, N, K) < model_ns(pick, M, N, K)) pick = 24;
+    if (split_fits && K >= 256 && model_ns(25, M, N, K) < model_ns(pick, M, N, K) && model_ns(pick, M, N, K) < 1e300)
+        pick = 25;
     // Few output elements: small tiles whose k groups are split over the
     // waves of a block (small.hip), any shape and K.  Measured kernel times
     // (256^3: 3.9 us against 8.7 for the split-phase tiles; 512^3: 9.2

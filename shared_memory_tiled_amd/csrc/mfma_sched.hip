@@ -76,6 +76,9 @@ __device__ __forceinline__ floatx2 lds_read64(uint32_t lds_byte_addr) {
     typedef const __attribute__((address_space(3))) floatx2 lds_floatx2;
     return *(lds_floatx2*)(uintptr_t)lds_byte_addr;
 }
+__device__ __forceinline__ float lds_read32(uint32_t lds_byte_addr) {
+    return *(const __attribute__((address_space(3))) float*)(uintptr_t)lds_byte_addr;
+}
 
 // Byte address inside LDS of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -90,12 +93,12 @@ __device__ __forceinline__ void wait_tied(floatx4 (&x)[4]) {
 }
 
 // One factor's tile: MNT (256, 128 or 64) rows or columns of op(X) by 32 k
-// per stage; each wave holds F (4 or 2) blocks of 32 of it.  KC: stored
+// per stage; each wave holds F (4, 2 or 1) blocks of 32 of it.  KC: stored
 // k-contiguous.  Copy j of wave w: one of the 4 MNT / 32 copies of a stage,
 // dealt to four waves in turn.
 template <bool KC, int MNT, int F>
 struct SchedTileF32 {
-    static_assert((MNT == 256 || MNT == 128 || MNT == 64) && (F == 4 || F == 2), "tile shape");
+    static_assert((MNT == 256 || MNT == 128 || MNT == 64) && (F == 4 || F == 2 || F == 1), "tile shape");
     static constexpr int WORDS = MNT * kSBK;              // floats per stage
     static constexpr int COPIES = MNT / 32;               // 1 KB copies per wave and phase
     static constexpr int RPC = KC ? 8 : 256 / MNT;        // stored rows per copy
@@ -157,7 +160,10 @@ __device__ __forceinline__ float operand(const floatx4 (&x)[4], int f, int e) {
 }
 
 // FM x FN blocks of 32 x 32 per wave, 2 x 2 waves: 256 x 256 tiles (FM =
-// FN = 4) or 128 x 128 (FM = FN = 2).
+// FN = 4), 128 x 128 (FM = FN = 2) or 64 x 64 (FM = FN = 1).  With one
+// block a wave keeps two accumulators, for even and odd instructions of a
+// step (so no instruction waits for the one before; they are added at the
+// end), and the last phase skips its 8-deep steps that lie wholly at k >= K.
 template <int FM, int FN, bool KCA, bool KCB>
 __global__ __launch_bounds__(256)
 void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
@@ -168,7 +174,9 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     constexpr int NREAD = TA::READS + TB::READS;
     constexpr int NMFMA = 4 * FM * FN;                    // matrix instructions per step
     constexpr int CSTRIDE = NMFMA / HALF;                 // a copy after every CSTRIDE-th of them
-    static_assert(NCOPY % 2 == 0 && NREAD <= NMFMA && CSTRIDE >= 1, "schedule");
+    constexpr int RPS = (NREAD + NMFMA - 1) / NMFMA;      // fragment reads after each of them
+    constexpr bool ONE = FM * FN == 1;                    // one block per wave
+    static_assert(NCOPY % 2 == 0 && NREAD <= RPS * NMFMA && CSTRIDE >= 1, "schedule");
     constexpr int A_ST = TA::WORDS, B_ST = TB::WORDS;
     // A stage 0, A stage 1, B stage 0, B stage 1.
     __shared__ __attribute__((aligned(16))) float lds[2 * (A_ST + B_ST)];
@@ -271,10 +279,12 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         const uint32_t addr = base + T::read_imm(s, i);
         if constexpr (T::IS_KC || T::FV == 4) {
             x[i] = lds_read128(addr);
-        } else {
+        } else if constexpr (T::FV == 2) {
             const floatx2 v = lds_read64(addr);
             x[i][0] = v[0];
             x[i][1] = v[1];
+        } else {
+            x[i][0] = lds_read32(addr);
         }
     };
     auto read_op = [&](int s, int t, int i) __attribute__((always_inline)) {
@@ -298,12 +308,17 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    floatx16 acc_odd;                                     // ONE: the odd instructions' sums
+    if constexpr (ONE)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_odd[r] = 0.0f;
 
     // One step: the 4 FM FN matrix instructions on fragment set t
     // (instruction q: e = q / (FM FN), block (q / FN % FM, q % FN)); after the
-    // q-th (q < NREAD), read q of step rs into set t ^ 1 (if R) and, after
-    // every CSTRIDE-th, copy CB + q / CSTRIDE (while below CE) of the phase at
-    // k_copy (the last phase if lastc) into stage cbuf.
+    // q-th, reads RPS q .. RPS q + RPS - 1 (below NREAD) of step rs into set
+    // t ^ 1 (if R) and, after every CSTRIDE-th, copy CB + q / CSTRIDE (while
+    // below CE) of the phase at k_copy (the last phase if lastc) into stage
+    // cbuf.
     auto step = [&](int t, auto reads, int rs, auto cb, auto ce, int k_copy, int cbuf,
                     auto lastc) __attribute__((always_inline)) {
         constexpr bool R = decltype(reads)::value;
@@ -311,11 +326,16 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         unroll<NMFMA>([&](auto qc) __attribute__((always_inline)) {
             constexpr int q = decltype(qc)::value;
             constexpr int e = q / (FM * FN), i = (q / FN) % FM, j = q % FN;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(operand<KCA>(a[t], i, e),
-                                                             operand<KCB>(b[t], j, e), acc[i][j], 0, 0, 0);
+            if constexpr (ONE && e % 2 == 1)
+                acc_odd = __builtin_amdgcn_mfma_f32_32x32x2f32(operand<KCA>(a[t], i, e), operand<KCB>(b[t], j, e),
+                                                               acc_odd, 0, 0, 0);
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(operand<KCA>(a[t], i, e),
+                                                                 operand<KCB>(b[t], j, e), acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (R && q < NREAD) {
-                read_op(rs, t ^ 1, q);
+            if constexpr (R && RPS * q < NREAD) {
+                read_op(rs, t ^ 1, RPS * q);
+                if constexpr (RPS == 2 && RPS * q + 1 < NREAD) read_op(rs, t ^ 1, RPS * q + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (q % CSTRIDE == CSTRIDE - 1 && CB + q / CSTRIDE < CE) {
@@ -407,8 +427,29 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         step(1, yes{}, 0, c0{}, c0{}, 0, 0, no{});
         ++ph;
     }
-    steps012(no{}, 0, 0, no{});
-    step(1, no{}, 0, c0{}, c0{}, 0, 0, no{});
+    if constexpr (ONE) {
+        // The last phase's steps s (k = klast + 8 s .. + 7) that hold k < K;
+        // step 0 always does.  Reads of a skipped step's fragments land in
+        // registers nothing uses.
+        const int kin = p.K - klast;                        // 1 .. 32
+        wait_set(0);
+        step(0, yes{}, 1, c0{}, c0{}, 0, 0, no{});
+        wait_set(1);
+        if (kin > 8) {
+            step(1, yes{}, 2, c0{}, c0{}, 0, 0, no{});
+            wait_set(0);
+            if (kin > 16) {
+                step(0, yes{}, 3, c0{}, c0{}, 0, 0, no{});
+                wait_set(1);
+                if (kin > 24) step(1, no{}, 0, c0{}, c0{}, 0, 0, no{});
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[0][0][r] += acc_odd[r];
+    } else {
+        steps012(no{}, 0, 0, no{});
+        step(1, no{}, 0, c0{}, c0{}, 0, 0, no{});
+    }
 
     // Guarded store.  Register r of lane (li, lh) is row rho = 8 (r / 4) +
     // 4 lh + r % 4 and column li of its 32 x 32 block; block (i, j) of a
@@ -430,6 +471,8 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
                     if constexpr (FN == 4) {
                         const floatx4 v = {acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
                         *reinterpret_cast<floatx4*>(crow + 4 * li) = v;
+                    } else if constexpr (FN == 1) {
+                        crow[li] = acc[i][0][r];
                     } else {
                         const floatx2 v = {acc[i][0][r], acc[i][1][r]};
                         *reinterpret_cast<floatx2*>(crow + 2 * li) = v;
@@ -849,6 +892,7 @@ hipError_t launch_ksplit_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_
 }
 
 hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m, int tile) {
+    if (tile == 64) return launch_sched_f32_tile<1>(p, s, op_a, op_b, group_m);
     return tile == 128 ? launch_sched_f32_tile<2>(p, s, op_a, op_b, group_m)
                        : launch_sched_f32_tile<4>(p, s, op_a, op_b, group_m);
 }

@@ -372,7 +372,14 @@ def test_default_variant_choices(binding):
         (2048, 2048, 2048): "mfma128x128_bk32_w2x2_sched",
         (6144, 6144, 6144): "mfma128x128_bk32_w2x2_sched",
         (7168, 7168, 7168): "mfma96x96_bk16_w1x1_k4_sched",       # 5625 tiles of 96: 21.97 rounds
-        (3000, 3000, 384): "mfma128x128_bk32_w2x2_sched",        # K < 512: no cost model
+        (3000, 3000, 384): "mfma64x64_bk32_w2x2_sched",          # 2209 tiles of 64, four per CU
+        (2048, 3072, 512): "mfma64x64_bk32_w2x2_sched",
+        (3072, 3072, 768): "mfma64x64_bk32_w2x2_sched",
+        (3000, 7000, 1024): "mfma64x64_bk32_w2x2_sched",
+        (2048, 2048, 256): "mfma128x128_bk32_w2x2_sched",        # 256 tiles of 128: one round
+        (2048, 2048, 512): "mfma128x128_bk32_w2x2_sched",
+        (4096, 4096, 256): "mfma256x256_bk32_w2x2_sched",
+        (1024, 1024, 512): "mfma64x64_bk32_w1x1_k4_sched",
         (3072, 3072, 3072): "mfma96x96_bk16_w1x1_k4_sched",       # 1024 tiles of 96: 4 full rounds
         (1536, 1536, 1536): "mfma96x96_bk16_w1x1_k4_sched",       # 256 tiles of 96: one round
         (5120, 5120, 5120): "mfma64x64_bk32_w1x1_k4_sched",       # 6400 tiles of 64: 25 full rounds
@@ -389,7 +396,7 @@ def test_default_variant_choices(binding):
         (3000, 3000, 3000): "mfma96x96_bk16_w1x1_k4_sched",       # 1024 tiles of 96
         (2300, 2300, 2304): "mfma64x64_bk32_w1x1_k4_sched",
         (1000, 1000, 1000): "mfma64x64_bk32_w1x1_k4_sched",
-        (1000, 2000, 500): "mfma64x64_bk32_w1x1_k4_sched",        # in place of the split-phase tiles
+        (1000, 2000, 500): "mfma64x64_bk32_w2x2_sched",          # 512 tiles of 64, two per CU
         (1000, 1000, 380): "mfma64x64_bk32_w2x2_k4",              # K < 384
         (1002, 1000, 1000): "mfma64x64_bk32_w2x2_k4",             # M % 4 = 2
         (256, 256, 256): "mfma16x16_w8_small",                   # 256 tiles of 16 x 16

@@ -1,6 +1,6 @@
 """The scheduled kernels' zero copies never depend on memory past a factor.
 
-Where a copy of the four-wave fp32 kernels (256 x 256 and 128 x 128 tiles),
+Where a copy of the four-wave fp32 kernels (256 x 256, 128 x 128 and 64 x 64 tiles),
 the k-split fp32 kernel or the scheduled 16-bit kernel must bring zeros -- a
 last phase that reaches past K, phase 0 of the k-split kernel reaching below
 k = 0, the column overhang of an edge tile -- its per-lane offset lies past
@@ -33,6 +33,7 @@ FP32_CASES = {
     "mfma256x256_bk32_w2x2_sched": (4092, 4092, 100),
     "mfma128x128_bk32_w2x2_sched": (1532, 1404, 164),
     "mfma64x64_bk32_w1x1_k4_sched": (556, 572, 1004),
+    "mfma64x64_bk32_w2x2_sched": (1532, 1028, 388),
 }
 MIXED_CASES = {"mixed256x256_bk64_w4_wide": (3580, 3330, 200), "mixed192x192_bk64_w4_wide": (3068, 3068, 200)}
 

@@ -131,11 +131,11 @@ SAMPLED = [
     ("tile256", (4096, 4096, 256), 3, (1, 2, 1)),
     ("tile256", (7940, 8132, 160), 1, (3, 5, 7)),
     ("tile256", (8132, 7940, 96), 0, (0, 0, 0)),
-    ("tile128", (3000, 7000, 1024), 0, (0, 0, 0)),
+    ("tile128", (4000, 6000, 1024), 0, (0, 0, 0)),
     ("tile128", (5000, 5004, 128), 1, (3, 5, 7)),
     ("tile128", (4100, 6200, 160), 3, (1, 2, 1)),
     ("tile256", (8192, 4096, 2020), 1, (3, 5, 7)),
-    ("tile128", (3000, 7000, 1020), 0, (0, 0, 0)),
+    ("tile128", (4000, 6000, 1020), 0, (0, 0, 0)),
 ]
 
 

@@ -300,11 +300,13 @@ def sched_f32_swz(r):
     return (r >> 1) & 7
 
 
-@pytest.mark.parametrize("mnt,f", [(256, 4), (128, 2), (64, 2)], ids=["tile256", "tile128", "ksplit64"])
+@pytest.mark.parametrize("mnt,f", [(256, 4), (128, 2), (64, 1), (64, 2)],
+                         ids=["tile256", "tile128", "tile64", "ksplit64"])
 @pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
 def test_scheduled_fp32_kernel_layout(kc, mnt, f):
     """The four-wave fp32 kernel on MNT x MNT tiles (two waves along each
-    dimension, F = MNT / 64 blocks of 32 per wave), and the k-split kernel's
+    dimension, F = MNT / 64 blocks of 32 per wave; with F = 1 an
+    mn-contiguous read is one float), and the k-split kernel's
     64 x 64 tile (MNT = 64, F = 2: one wave issues all eight copies of a
     factor, copy j as copy j / 4 of wave j % 4 below, and reads the whole
     tile from its own stages): each factor tile is MNT
@@ -369,6 +371,28 @@ def test_scheduled_fp32_kernel_layout(kc, mnt, f):
                         want = [(span + f * li + e, 8 * s + 4 * lh + i) for e in range(f)]
                     assert got == want, (span, s, i, lane)
                 assert degree(words, width, 64, 16 if width == 4 else 32) == 1
+
+
+@pytest.mark.parametrize("K", list(range(4, 100, 4)) + [1000, 1004, 1020, 1024])
+def test_sched64_last_phase_skips_only_steps_past_k(K):
+    """The 64 x 64 four-wave tiles skip, in the last phase (k0 = 32 (P - 1)),
+    step s (k = k0 + 8 s .. + 7, read by instructions e = 0..3 as k = k0 + 8
+    s + e and + 4 + e) unless k0 + 8 s < K: every k < K is in a step that
+    runs, and every k in a skipped step is at or past K (copied as zero, so
+    the instructions skipped would have added nothing)."""
+    P = -(-K // 32)
+    k0 = 32 * (P - 1)
+    kin = K - k0
+    assert 1 <= kin <= 32
+    run = [0] + [s for s, limit in ((1, 8), (2, 16), (3, 24)) if kin > limit]   # the kernel's tests
+    for s in range(4):
+        ks = {k0 + 8 * s + e + 4 * h for e in range(4) for h in range(2)}
+        assert ks == set(range(k0 + 8 * s, k0 + 8 * s + 8))
+        if s in run:
+            assert min(ks) < K
+        else:
+            assert min(ks) >= K
+    assert sorted(k for s in run for k in range(k0 + 8 * s, k0 + 8 * s + 8) if k < K) == list(range(k0, K))
 
 
 @pytest.mark.parametrize("K", [4, 8, 28, 32, 36, 60, 64, 96, 100, 124, 128, 132, 260, 388, 516, 1000, 1024])
