@@ -477,7 +477,7 @@ SWEEP_SHAPES = ([(n, n, n) for n in (512, 768, 1024, 1536, 2048, 2560, 3072, 358
 SWEEP_CANDIDATES = ["mfma64x64_bk32_w2x2_k4", "mfma64x64_bk16_w2x2_k4", "mfma64x64_bk32_w1x1_k4_sched",
                     "mfma128x128_bk16_w2x2",
                     "mfma128x128_bk32_w2x2_sched", "mfma256x256_bk32_w2x4_direct",
-                    "mfma256x256_bk32_w2x2_sched", "mfma96x96_bk16_w1x1_k4_sched"]
+                    "mfma256x256_bk32_w2x2_sched", "mfma96x96_bk16_w1x1_k4_sched", "mfma64x64_bk32_w2x2_sched"]
 
 
 MIXED_SWEEP_CANDIDATES = ["mixed64x64_bk64_w1x2", "mixed64x64_bk32_w4_ksplit", "mixed128x128_bk64_w2x2_directAB",
