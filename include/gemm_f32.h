@@ -103,8 +103,8 @@ extern "C" {
  *      per tile gives them the shorter time (K >= 448), or in place of the
  *      split-phase tiles (K >= 384); then 96 x 96 tiles of the same kind
  *      (16-deep phases) where the model gives them the shorter time (K >=
- *      448), and, from K = 256, 64 x 64 tiles on the four-wave schedule
- *      with one 32 x 32 block per wave (four blocks sharing a CU) where the
+ *      448), and, from K = 256, 64 x 64 tiles of four waves with one 32 x
+ *      32 block each over the whole K (three blocks sharing a CU) where the
  *      model, charging their fixed cost once per launch, does.  Products of at most 1024 output tiles
  *      of 16 x 16 take small tiles instead (16 x 16 on 8 waves up to 512 of
  *      them, else 32 x 32 on 4 waves), whose K is split over the waves of

@@ -51,6 +51,8 @@ const Diagnostic kDiagnostics[] = {
     {"mfma16x16_w8_small", 3, 23},
     {"mfma96x96_bk16_w1x1_k4_sched", 3, 24},
     {"mfma64x64_bk32_w2x2_sched", 3, 25},
+    {"mfma64x64_bk32_w2x2_4stage", 3, 26},
+    {"mfma64x64_bk32_w2x2_2stage", 3, 27},
 };
 constexpr int kNumDiagnostics = (int)(sizeof(kDiagnostics) / sizeof(kDiagnostics[0]));
 

@@ -84,6 +84,9 @@ int mfma_pick_config(int M, int N, int K);
 // (op 1: factor stored transposed; tile 256 or 128).
 bool sched_f32_fits(const GemmArgs& p, int op_a, int op_b);
 hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m, int tile);
+// 64 x 64 tiles of 2 x 2 waves of one 32 x 32 block each, from `stages`
+// (2 or 4) LDS stages (mfma_sched.hip); the problems sched_f32_fits takes.
+hipError_t launch_tile64_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m, int stages);
 // Four waves splitting the phases of one 64 x 64 tile (mfma_sched.hip):
 // whether it takes the problem (K, M and N multiples of 4, stored factors
 // below 2^31 bytes), and its launcher.

@@ -612,16 +612,17 @@ hipError_t launch_ksplit96_or_ksplit(const GemmArgs& p, hipStream_t s, int, int,
     if (ksplit96_f32_fits(p, TRA, TRB)) return launch_ksplit96_f32(p, s, TRA, TRB, group_m);
     return launch_mfma(p, s, 20, TRA, TRB);
 }
-// The four-wave schedule on 64 x 64 tiles (one 32 x 32 block per wave, the
-// whole K) where it takes the problem, else configuration 20.
-template <bool TRA, bool TRB>
-hipError_t launch_sched64_or_ksplit(const GemmArgs& p, hipStream_t s, int, int, int group_m, unsigned) {
-    if (sched_f32_fits(p, TRA, TRB)) return launch_sched_f32(p, s, TRA, TRB, group_m, 64);
+// 64 x 64 tiles of 2 x 2 waves, one 32 x 32 block each over the whole K,
+// from NST LDS stages (gemm_f32_tile64_kernel), where they take the
+// problem, else configuration 20.
+template <int NST, bool TRA, bool TRB>
+hipError_t launch_tile64_or_ksplit(const GemmArgs& p, hipStream_t s, int, int, int group_m, unsigned) {
+    if (sched_f32_fits(p, TRA, TRB)) return launch_tile64_f32(p, s, TRA, TRB, group_m, NST);
     return launch_mfma(p, s, 20, TRA, TRB);
 }
-#define SCHED64_OPS                                                                          \
-    {launch_sched64_or_ksplit<false, false>, launch_sched64_or_ksplit<false, true>,          \
-     launch_sched64_or_ksplit<true, false>, launch_sched64_or_ksplit<true, true>}
+#define TILE64_OPS(NST)                                                                          \
+    {launch_tile64_or_ksplit<NST, false, false>, launch_tile64_or_ksplit<NST, false, true>,          \
+     launch_tile64_or_ksplit<NST, true, false>, launch_tile64_or_ksplit<NST, true, true>}
 #define KSPLIT96_OPS                                                                          \
     {launch_ksplit96_or_ksplit<false, false>, launch_ksplit96_or_ksplit<false, true>,          \
      launch_ksplit96_or_ksplit<true, false>, launch_ksplit96_or_ksplit<true, true>}
@@ -690,8 +691,13 @@ const MfmaConfig kConfigs[] = {
     {"mfma16x16_w8_small", 16, 16, 512, 8, SMALL_OPS(2)},
     // four waves, each the whole 96 x 96 tile over every fourth 16-deep phase
     {"mfma96x96_bk16_w1x1_k4_sched", 96, 96, 1024, 8, KSPLIT96_OPS},
-    // four waves of one 32 x 32 block each over the whole K (2 x 2 per tile)
-    {"mfma64x64_bk32_w2x2_sched", 64, 64, 256, 8, SCHED64_OPS},
+    // four waves of one 32 x 32 block each over the whole K (2 x 2 per
+    // tile), three LDS stages (three blocks to a CU); then the same tiles
+    // with four stages (copies three phases ahead, two blocks to a CU) and
+    // with two (four blocks to a CU)
+    {"mfma64x64_bk32_w2x2_sched", 64, 64, 256, 8, TILE64_OPS(3)},
+    {"mfma64x64_bk32_w2x2_4stage", 64, 64, 256, 8, TILE64_OPS(4)},
+    {"mfma64x64_bk32_w2x2_2stage", 64, 64, 256, 8, TILE64_OPS(2)},
 };
 #undef NN_ONLY
 #undef ALL_OPS
@@ -701,7 +707,7 @@ const MfmaConfig kConfigs[] = {
 #undef SPLITK_OPS
 #undef KSPLIT_OPS
 #undef KSPLIT96_OPS
-#undef SCHED64_OPS
+#undef TILE64_OPS
 #undef SMALL_OPS
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 }  // namespace
@@ -739,15 +745,15 @@ const char* mfma_config_name(int c) { return (c >= 0 && c < kNumConfigs) ? kConf
 // that 3584^3, 5.6 rounds of them against 12.25 rounds of 64 x 64 k-split
 // tiles, keeps the latter, 2-3 % faster there; within 4 % of the measured
 // time at 2048^3, 2560^3, 3072^3, 5120^3, 6144^3 and 7168^3).  Then 64 x 64
-// tiles on the four-wave schedule (one 32 x 32 block per wave over the whole
-// K, mfma_sched.hip) replace the choice, from K = 256, where the model gives
-// them the shorter time at 0.85 and 4 us once per launch (four of their
+// tiles of 2 x 2 one-block waves over the whole K (gemm_f32_tile64_kernel,
+// three LDS stages) replace the choice, from K = 256, where the model gives
+// them the shorter time at 0.85 and 4 us once per launch (three of their
 // blocks share a CU; fitted to 22 shapes with K from 256 to 5120: 3000^2 x
-// 384 117 TFLOP/s against 98 on 128 x 128 tiles, 2048 x 3072 x 512 124
-// against 107 on the k-split tiles, 3072^2 x 768 132 against 120, 1000 x
-// 2000 x 500 102 against 93, 3000 x 7000 x 1024 131 against 123; with one
-// block per CU, 1000^3, they lose, 98 against 104: two stages of 32 k hide
-// less of the copies' latency than the k-split waves' longer phases).  Last, products of at most 1024 output tiles of 16 x 16
+// 384 115 TFLOP/s against 98 on 128 x 128 tiles, 2048 x 3072 x 512 122
+// against 106 on the k-split tiles, 3072^2 x 768 132 against 120, 1000 x
+// 2000 x 500 99 against 92, 3000 x 7000 x 1024 131 against 123; with one
+// block per CU, 1000^3, they lose, 102 against 105: a barrier every phase
+// of 16 instructions against none in the k-split waves).  Last, products of at most 1024 output tiles of 16 x 16
 // take the small-tile kernels (16 x 16 tiles on 8 waves up to 512 such
 // tiles, else 32 x 32 tiles on 4 waves).  Every picked configuration
 // is built for all four op combinations.

@@ -76,9 +76,6 @@ __device__ __forceinline__ floatx2 lds_read64(uint32_t lds_byte_addr) {
     typedef const __attribute__((address_space(3))) floatx2 lds_floatx2;
     return *(lds_floatx2*)(uintptr_t)lds_byte_addr;
 }
-__device__ __forceinline__ float lds_read32(uint32_t lds_byte_addr) {
-    return *(const __attribute__((address_space(3))) float*)(uintptr_t)lds_byte_addr;
-}
 
 // Byte address inside LDS of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -160,10 +157,7 @@ __device__ __forceinline__ float operand(const floatx4 (&x)[4], int f, int e) {
 }
 
 // FM x FN blocks of 32 x 32 per wave, 2 x 2 waves: 256 x 256 tiles (FM =
-// FN = 4), 128 x 128 (FM = FN = 2) or 64 x 64 (FM = FN = 1).  With one
-// block a wave keeps two accumulators, for even and odd instructions of a
-// step (so no instruction waits for the one before; they are added at the
-// end), and the last phase skips its 8-deep steps that lie wholly at k >= K.
+// FN = 4) or 128 x 128 (FM = FN = 2).
 template <int FM, int FN, bool KCA, bool KCB>
 __global__ __launch_bounds__(256)
 void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
@@ -174,9 +168,7 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     constexpr int NREAD = TA::READS + TB::READS;
     constexpr int NMFMA = 4 * FM * FN;                    // matrix instructions per step
     constexpr int CSTRIDE = NMFMA / HALF;                 // a copy after every CSTRIDE-th of them
-    constexpr int RPS = (NREAD + NMFMA - 1) / NMFMA;      // fragment reads after each of them
-    constexpr bool ONE = FM * FN == 1;                    // one block per wave
-    static_assert(NCOPY % 2 == 0 && NREAD <= RPS * NMFMA && CSTRIDE >= 1, "schedule");
+    static_assert(NCOPY % 2 == 0 && NREAD <= NMFMA && CSTRIDE >= 1, "schedule");
     constexpr int A_ST = TA::WORDS, B_ST = TB::WORDS;
     // A stage 0, A stage 1, B stage 0, B stage 1.
     __shared__ __attribute__((aligned(16))) float lds[2 * (A_ST + B_ST)];
@@ -279,12 +271,10 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         const uint32_t addr = base + T::read_imm(s, i);
         if constexpr (T::IS_KC || T::FV == 4) {
             x[i] = lds_read128(addr);
-        } else if constexpr (T::FV == 2) {
+        } else {
             const floatx2 v = lds_read64(addr);
             x[i][0] = v[0];
             x[i][1] = v[1];
-        } else {
-            x[i][0] = lds_read32(addr);
         }
     };
     auto read_op = [&](int s, int t, int i) __attribute__((always_inline)) {
@@ -308,17 +298,12 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    floatx16 acc_odd;                                     // ONE: the odd instructions' sums
-    if constexpr (ONE)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_odd[r] = 0.0f;
 
     // One step: the 4 FM FN matrix instructions on fragment set t
     // (instruction q: e = q / (FM FN), block (q / FN % FM, q % FN)); after the
-    // q-th, reads RPS q .. RPS q + RPS - 1 (below NREAD) of step rs into set
-    // t ^ 1 (if R) and, after every CSTRIDE-th, copy CB + q / CSTRIDE (while
-    // below CE) of the phase at k_copy (the last phase if lastc) into stage
-    // cbuf.
+    // q-th (q < NREAD), read q of step rs into set t ^ 1 (if R) and, after
+    // every CSTRIDE-th, copy CB + q / CSTRIDE (while below CE) of the phase at
+    // k_copy (the last phase if lastc) into stage cbuf.
     auto step = [&](int t, auto reads, int rs, auto cb, auto ce, int k_copy, int cbuf,
                     auto lastc) __attribute__((always_inline)) {
         constexpr bool R = decltype(reads)::value;
@@ -326,16 +311,11 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         unroll<NMFMA>([&](auto qc) __attribute__((always_inline)) {
             constexpr int q = decltype(qc)::value;
             constexpr int e = q / (FM * FN), i = (q / FN) % FM, j = q % FN;
-            if constexpr (ONE && e % 2 == 1)
-                acc_odd = __builtin_amdgcn_mfma_f32_32x32x2f32(operand<KCA>(a[t], i, e), operand<KCB>(b[t], j, e),
-                                                               acc_odd, 0, 0, 0);
-            else
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(operand<KCA>(a[t], i, e),
-                                                                 operand<KCB>(b[t], j, e), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(operand<KCA>(a[t], i, e),
+                                                             operand<KCB>(b[t], j, e), acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (R && RPS * q < NREAD) {
-                read_op(rs, t ^ 1, RPS * q);
-                if constexpr (RPS == 2 && RPS * q + 1 < NREAD) read_op(rs, t ^ 1, RPS * q + 1);
+            if constexpr (R && q < NREAD) {
+                read_op(rs, t ^ 1, q);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (q % CSTRIDE == CSTRIDE - 1 && CB + q / CSTRIDE < CE) {
@@ -427,29 +407,8 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         step(1, yes{}, 0, c0{}, c0{}, 0, 0, no{});
         ++ph;
     }
-    if constexpr (ONE) {
-        // The last phase's steps s (k = klast + 8 s .. + 7) that hold k < K;
-        // step 0 always does.  Reads of a skipped step's fragments land in
-        // registers nothing uses.
-        const int kin = p.K - klast;                        // 1 .. 32
-        wait_set(0);
-        step(0, yes{}, 1, c0{}, c0{}, 0, 0, no{});
-        wait_set(1);
-        if (kin > 8) {
-            step(1, yes{}, 2, c0{}, c0{}, 0, 0, no{});
-            wait_set(0);
-            if (kin > 16) {
-                step(0, yes{}, 3, c0{}, c0{}, 0, 0, no{});
-                wait_set(1);
-                if (kin > 24) step(1, no{}, 0, c0{}, c0{}, 0, 0, no{});
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[0][0][r] += acc_odd[r];
-    } else {
-        steps012(no{}, 0, 0, no{});
-        step(1, no{}, 0, c0{}, c0{}, 0, 0, no{});
-    }
+    steps012(no{}, 0, 0, no{});
+    step(1, no{}, 0, c0{}, c0{}, 0, 0, no{});
 
     // Guarded store.  Register r of lane (li, lh) is row rho = 8 (r / 4) +
     // 4 lh + r % 4 and column li of its 32 x 32 block; block (i, j) of a
@@ -471,8 +430,6 @@ void gemm_f32_sched_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
                     if constexpr (FN == 4) {
                         const floatx4 v = {acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
                         *reinterpret_cast<floatx4*>(crow + 4 * li) = v;
-                    } else if constexpr (FN == 1) {
-                        crow[li] = acc[i][0][r];
                     } else {
                         const floatx2 v = {acc[i][0][r], acc[i][1][r]};
                         *reinterpret_cast<floatx2*>(crow + 2 * li) = v;
@@ -817,6 +774,234 @@ void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m, u
     }
 }
 
+// 64 x 64 tiles of 2 x 2 waves, each one 32 x 32 block over the whole K,
+// from NST (2 or 4) LDS stages of the four-wave schedule's layouts.  Phase
+// ph reads stage ph % NST and, after its barrier, copies phase ph + NST
+// into that stage.  With two stages (16 KB each) four blocks share a CU and
+// one block's waits overlap the others' work; with four, copies run three
+// phases ahead, for products with one block per CU (a phase is only 16
+// matrix instructions, about 1000 clocks).  The barrier of phase ph comes
+// between steps 2 and 3, once every wave's copies of phase ph + 1 have
+// landed and its reads of phase ph's fragments have completed; it is the
+// bare s_barrier, as a fence would also wait for the copies of later
+// phases.  Every phase issues the four copies of phase ph + NST, past the
+// end (zeros into a stage nothing reads) when there is no such phase, so the
+// wait before the barrier is always for all but the last 4 (NST - 2)
+// copies.  The loop is unrolled by the stages (each stage's offset an
+// instruction offset); two accumulators take the even and odd instructions
+// of a step (none waits for the one before), added at the end; the last
+// phase skips its 8-deep steps wholly at k >= K.
+template <bool KCA, bool KCB, int NST>
+__global__ __launch_bounds__(256)
+void gemm_f32_tile64_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
+    static_assert(NST >= 2 && NST <= 4, "stages");
+    constexpr int BM = 64, BN = 64, WM = 32, WN = 32, NMFMA = 4;
+    using TA = SchedTileF32<KCA, BM, 1>;
+    using TB = SchedTileF32<KCB, BN, 1>;
+    constexpr int A_COPIES = TA::COPIES, NCOPY = TA::COPIES + TB::COPIES;
+    constexpr int NREAD = TA::READS + TB::READS;          // 2, 5 or 8
+    constexpr int RPS = (NREAD + NMFMA - 1) / NMFMA;      // reads after each matrix instruction
+    static_assert(NCOPY == NMFMA && NREAD <= RPS * NMFMA && RPS <= 2, "schedule");
+    constexpr int A_ST = TA::WORDS, B_ST = TB::WORDS;    // floats per stage
+    __shared__ __attribute__((aligned(16))) float lds[NST * (A_ST + B_ST)];   // A's stages, then B's
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave_u / 2, wn = wave_u % 2;
+    const int li = lane & 31, lh = lane >> 5;
+
+    const int logical = xcd_contiguous((int)blockIdx.x, tiles_m * tiles_n);
+    const int group_size = group_m * tiles_n;
+    const int g = logical / group_size;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int in_g = logical - g * group_size;
+    const int m0 = (first_m + in_g % gm) * BM;
+    const int n0 = (in_g / gm) * BN;
+
+    // Copies 0, 1 fill A's tile, 2, 3 B's; descriptors and zeros as in
+    // gemm_f32_sched_kernel (the last phase's offsets hold the phase, lanes
+    // at k >= K point past the end).
+    uint32_t doff[NCOPY];
+#pragma unroll
+    for (int j = 0; j < A_COPIES; ++j) {
+        doff[j] = TA::copy_src(wave_u, j, lane, m0, p.lda);
+        doff[A_COPIES + j] = TB::copy_src(wave_u, j, lane, n0, p.ldb);
+    }
+    constexpr int kRawBufferWord3 = 0x00020000;
+    const int64_t a_rows = KCA ? p.M : p.K, a_cols = KCA ? p.K : p.M;
+    const int64_t b_rows = KCB ? p.N : p.K, b_cols = KCB ? p.K : p.N;
+    const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.A), (short)0, (int)(4 * ((a_rows - 1) * p.lda + a_cols)), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.B), (short)0, (int)(4 * ((b_rows - 1) * p.ldb + b_cols)), kRawBufferWord3);
+    const int P = ceil_div(p.K, kSBK);
+    constexpr uint32_t kPastEnd = 0x80000000u;
+    const int klast = (P - 1) * kSBK;
+    uint32_t dlast[NCOPY];
+#pragma unroll
+    for (int j = 0; j < A_COPIES; ++j) {
+        const int ka = klast + TA::copy_k(wave_u, j, lane);
+        const int kb = klast + TB::copy_k(wave_u, j, lane);
+        dlast[j] = ka >= p.K ? kPastEnd : doff[j] + (uint32_t)TA::phase_bytes(klast, p.lda);
+        dlast[A_COPIES + j] = kb >= p.K ? kPastEnd : doff[A_COPIES + j] + (uint32_t)TB::phase_bytes(klast, p.ldb);
+    }
+    // Per-lane and scalar offsets of the copies of phase ph (any ph >= 0).
+    uint32_t cv[NCOPY];
+    int cs_a = 0, cs_b = 0;
+    auto plan = [&](int ph) __attribute__((always_inline)) {
+        const bool normal = ph < P - 1, last = ph == P - 1;
+#pragma unroll
+        for (int j = 0; j < NCOPY; ++j) cv[j] = normal ? doff[j] : (last ? dlast[j] : kPastEnd);
+        cs_a = normal ? TA::phase_bytes(ph * kSBK, p.lda) : 0;
+        cs_b = normal ? TB::phase_bytes(ph * kSBK, p.ldb) : 0;
+    };
+    auto copy = [&](int j, int st) __attribute__((always_inline)) {
+        if (j < A_COPIES) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_a, (__attribute__((address_space(3))) void*)(lds + st * A_ST + TA::copy_dst(wave_u, j)), 16,
+                (int)cv[j], cs_a, 0, 0);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_b,
+                (__attribute__((address_space(3))) void*)(lds + NST * A_ST + st * B_ST +
+                                                         TB::copy_dst(wave_u, j - A_COPIES)),
+                16, (int)cv[j], cs_b, 0, 0);
+        }
+    };
+
+    // Read bases (stage 0): KC one per step, MC one in all; the stage and
+    // the read are instruction offsets.
+    constexpr int SA = KCA ? 4 : 1, SB = KCB ? 4 : 1;
+    uint32_t abase[SA], bbase[SB];
+    const uint32_t lds0 = lds_addr(lds);
+#pragma unroll
+    for (int s = 0; s < SA; ++s) abase[s] = lds0 + TA::read_base(wm * WM, s, li, lh);
+#pragma unroll
+    for (int s = 0; s < SB; ++s) bbase[s] = lds0 + 4u * NST * A_ST + TB::read_base(wn * WN, s, li, lh);
+
+    // A fragment is one floatx4 either way: a k-contiguous one read whole,
+    // an mn-contiguous one value i of its four reads (k rows apart), so the
+    // reads land where the instructions take them (value e for instruction
+    // e) and no register move waits for them.
+    floatx4 a[2][1], b[2][1];
+    auto read_one = [&](auto tile, floatx4 (&x)[1], uint32_t base, int s, int i, int st) __attribute__((always_inline)) {
+        using T = decltype(tile);
+        const uint32_t addr = base + T::read_imm(s, i) + 4u * st * T::WORDS;
+        if constexpr (T::IS_KC) x[0] = lds_read128(addr);
+        else x[0][i] = *(volatile const __attribute__((address_space(3))) float*)(uintptr_t)addr;   // unmerged
+    };
+    auto read_op = [&](int s, int t, int i, int st) __attribute__((always_inline)) {
+        if (i < TA::READS) read_one(TA{}, a[t], abase[KCA ? s : 0], s, i, st);
+        else read_one(TB{}, b[t], bbase[KCB ? s : 0], s, i - TA::READS, st);
+    };
+    auto wait_set = [&](int t) __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[t][0]), "+v"(b[t][0]) : : "memory");
+    };
+
+    floatx16 acc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[h][r] = 0.0f;
+
+    using yes = std::true_type;
+    using no = std::false_type;
+    // One step on set t: instruction e on accumulator e % 2; after it, reads
+    // RPS e .. of step rs (stage rst) into set t ^ 1 if R, and copy e into
+    // stage cst if C.
+    auto step = [&](int t, auto reads, int rs, int rst, auto copies, int cst) __attribute__((always_inline)) {
+        constexpr bool R = decltype(reads)::value;
+        constexpr bool C = decltype(copies)::value;
+        unroll<NMFMA>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int e = decltype(qc)::value;
+            acc[e & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t][0][e], b[t][0][e], acc[e & 1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (R && RPS * e < NREAD) {
+                read_op(rs, t ^ 1, RPS * e, rst);
+                if constexpr (RPS == 2 && RPS * e + 1 < NREAD) read_op(rs, t ^ 1, RPS * e + 1, rst);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (C) {
+                copy(e, cst);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    };
+    // The barrier alone: each wave has waited for its own copies, and a
+    // fence here would make the compiler wait for every copy in flight.
+    auto barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    // Prologue: phases 0 .. NST - 1 into stages 0 .. NST - 1 (past the end
+    // beyond P - 1), then wait for phase 0 (all but the last 4 (NST - 1)
+    // copies).
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+        plan(st);
+#pragma unroll
+        for (int j = 0; j < NCOPY; ++j) copy(j, st);
+    }
+    if constexpr (NST == 4) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if constexpr (NST == 3) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    barrier();
+#pragma unroll
+    for (int i = 0; i < NREAD; ++i) read_op(0, 0, i, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Phase ph on stage ST.  Steps that run: all but in the last phase,
+    // where only those holding some k < K.
+    auto phase = [&](auto stc, int ph) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stc)::value, NX = (ST + 1) % NST;
+        const int steps = ph == P - 1 ? (p.K - klast + 7) / 8 : 4;
+        wait_set(0);
+        step(0, yes{}, 1, ST, no{}, 0);
+        wait_set(1);
+        if (steps > 1) {
+            step(1, yes{}, 2, ST, no{}, 0);
+            wait_set(0);
+            if (steps > 2) {
+                step(0, yes{}, 3, ST, no{}, 0);
+                wait_set(1);
+            }
+        }
+        plan(ph + NST);
+        if constexpr (NST == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // this wave's copies of phase ph + 1
+        else if constexpr (NST == 3) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier();
+        if (steps > 3) step(1, yes{}, 0, NX, yes{}, ST);    // reads step 0 of phase ph + 1
+        else {
+#pragma unroll
+            for (int j = 0; j < NCOPY; ++j) copy(j, ST);   // the count of copies stays four per phase
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int ph = 0;
+    for (; ph + NST <= P; ph += NST)
+        unroll<NST>([&](auto stc) __attribute__((always_inline)) { phase(stc, ph + decltype(stc)::value); });
+    unroll<NST - 1>([&](auto stc) __attribute__((always_inline)) {
+        if (ph < P) phase(stc, ph++);
+    });
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // the dummy copies, before the block ends
+
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[0][r] += acc[1][r];
+    // Guarded store: register r of lane (li, lh) is row 8 (r / 4) + 4 lh + r
+    // % 4 and column li of the wave's block.
+    const int col = n0 + wn * WN + li;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * WM + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = acc[0][r];
+    }
+}
+
 template <bool KCA, bool KCB>
 hipError_t launch_ksplit_f32_kernel(const GemmArgs& p, hipStream_t s, int tiles_m, int tiles_n, int group_m,
                                     unsigned blocks) {
@@ -891,8 +1076,26 @@ hipError_t launch_ksplit_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_
     }
 }
 
+template <int NST>
+hipError_t launch_tile64_stages(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m) {
+    const int tiles_m = ceil_div(p.M, 64), tiles_n = ceil_div(p.N, 64);
+    const dim3 grid((unsigned)((int64_t)tiles_m * tiles_n)), block(256);
+    switch (2 * (op_a ? 1 : 0) + (op_b ? 1 : 0)) {
+        case 0: hipLaunchKernelGGL((gemm_f32_tile64_kernel<true, false, NST>), grid, block, 0, s, p, tiles_m, tiles_n, group_m); break;
+        case 1: hipLaunchKernelGGL((gemm_f32_tile64_kernel<true, true, NST>), grid, block, 0, s, p, tiles_m, tiles_n, group_m); break;
+        case 2: hipLaunchKernelGGL((gemm_f32_tile64_kernel<false, false, NST>), grid, block, 0, s, p, tiles_m, tiles_n, group_m); break;
+        default: hipLaunchKernelGGL((gemm_f32_tile64_kernel<false, true, NST>), grid, block, 0, s, p, tiles_m, tiles_n, group_m); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_tile64_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m, int stages) {
+    if (stages == 4) return launch_tile64_stages<4>(p, s, op_a, op_b, group_m);
+    if (stages == 3) return launch_tile64_stages<3>(p, s, op_a, op_b, group_m);
+    return launch_tile64_stages<2>(p, s, op_a, op_b, group_m);
+}
+
 hipError_t launch_sched_f32(const GemmArgs& p, hipStream_t s, int op_a, int op_b, int group_m, int tile) {
-    if (tile == 64) return launch_sched_f32_tile<1>(p, s, op_a, op_b, group_m);
     return tile == 128 ? launch_sched_f32_tile<2>(p, s, op_a, op_b, group_m)
                        : launch_sched_f32_tile<4>(p, s, op_a, op_b, group_m);
 }

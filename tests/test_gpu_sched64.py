@@ -1,13 +1,17 @@
-"""64 x 64 tiles on the four-wave schedule, each wave one 32 x 32 block over
-the whole K (diagnostic variant mfma64x64_bk32_w2x2_sched) against the fp32
-oracle: exact on integer inputs, within 1e-5 S on uniform ones.
+"""64 x 64 tiles of 2 x 2 waves, each one 32 x 32 block over the whole K
+(gemm_f32_tile64_kernel: diagnostic variant mfma64x64_bk32_w2x2_sched, three
+LDS stages, the default for short-K shapes with several tiles per CU; and
+its four- and two-stage forms) against the fp32 oracle: exact on integer
+inputs, within 1e-5 S on uniform ones.
 
 The last phase skips its 8-deep steps that lie wholly at k >= K, so the
 shapes take every count of k in the last phase that a multiple of 4 allows
-(4 .. 32), with one phase in all and with several; edge tiles on both sides;
-offset views whose pad words are NaN; a second call with the same bits; and
-problems it does not take (K % 4 != 0) handed to configuration 20's
-kernels."""
+(4 .. 32), with one phase in all and with several, and phase counts that
+leave every stage count's unrolled loop a tail of each length; edge tiles on
+both sides; offset views whose pad words are NaN; a second call with the
+same bits, and the same bits from every stage count; problems it does not
+take (K % 4 != 0) handed to configuration 20's kernels; every op pair
+through gemm_f32_op where it is the default."""
 from __future__ import annotations
 
 import numpy as np
@@ -22,6 +26,8 @@ from test_gpu_ksplit import variant_number
 pytestmark = pytest.mark.gpu
 
 S64 = "mfma64x64_bk32_w2x2_sched"
+S64_4 = "mfma64x64_bk32_w2x2_4stage"        # the same tiles, four LDS stages
+S64_2 = "mfma64x64_bk32_w2x2_2stage"        # two
 
 # (M, N, K) and the k in the last phase: 4 (one phase), 8, 12, 20, 4 (two
 # phases), 28, 24, 8 (32 phases), 32 (16 phases)
@@ -29,7 +35,7 @@ SHAPES = [(64, 64, 4), (100, 136, 8), (64, 128, 12), (136, 200, 20), (200, 64, 3
           (128, 192, 88), (300, 392, 1000), (1000, 1000, 512)]
 
 
-def run_variant(M, N, K, dist, seed):
+def run_variant(M, N, K, dist, seed, name=S64):
     gen = np.random.default_rng(seed)
     A = inputs.padded(inputs.random_matrix(gen, M, K, dist), K + 3, 1)
     B = inputs.padded(inputs.random_matrix(gen, K, N, dist), N + 5, 1)
@@ -38,27 +44,29 @@ def run_variant(M, N, K, dist, seed):
     B_dev = torch.from_numpy(B.buf).cuda()
     C_init = inputs.padded_output(M, N, N + 7, 1)
     C_dev = torch.from_numpy(C_init.buf).cuda()
-    binding.gemm_f32_variant(variant_number(S64), M, N, K, A_dev.data_ptr() + 4, A.ld, B_dev.data_ptr() + 4,
+    binding.gemm_f32_variant(variant_number(name), M, N, K, A_dev.data_ptr() + 4, A.ld, B_dev.data_ptr() + 4,
                              B.ld, C_dev.data_ptr() + 4, N + 7)
     torch.cuda.synchronize()
     return inputs.Padded(C_dev.cpu().numpy(), M, N, N + 7, 1), Cref, S
 
 
+@pytest.mark.parametrize("name", [S64, S64_2, S64_4])
 @pytest.mark.parametrize("dist", ["int", "uniform"])
-def test_variant_against_oracle(dist):
+def test_variant_against_oracle(dist, name):
     for (M, N, K) in SHAPES:
-        say(f"sched64 variant {dist} {(M, N, K)}")
-        C, Cref, S = run_variant(M, N, K, dist, [M, N, K, dist == "int", 19])
+        say(f"{name} variant {dist} {(M, N, K)}")
+        C, Cref, S = run_variant(M, N, K, dist, [M, N, K, dist == "int", 19], name)
         check_padding_untouched(C)
-        what = f"{S64} {dist} {(M, N, K)}"
+        what = f"{name} {dist} {(M, N, K)}"
         if dist == "int":
             check_exact(C.view, Cref, what)
         else:
             check_close(C.view, Cref, S, what)
 
 
-def test_variant_repeats_bit_for_bit():
-    v = variant_number(S64)
+@pytest.mark.parametrize("name", [S64, S64_2, S64_4])
+def test_variant_repeats_bit_for_bit(name):
+    v = variant_number(name)
     gen = torch.Generator(device="cuda").manual_seed(9)
     X = torch.rand((580, 1000), device="cuda", generator=gen) * 2 - 1
     Y = torch.rand((1000, 520), device="cuda", generator=gen) * 2 - 1
@@ -69,14 +77,31 @@ def test_variant_repeats_bit_for_bit():
         binding.gemm_f32_variant(v, 580, 520, 1000, X, 1000, Y, 520, C, 520)
         outs.append(C)
     torch.cuda.synchronize()
-    assert torch.equal(outs[0], outs[1])
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
 
 
-def test_fallback_for_k_not_multiple_of_4():
-    say("sched64 fallback")
-    C, Cref, _ = run_variant(200, 136, 102, "int", [5, 6, 8])
+@pytest.mark.parametrize("name", [S64, S64_2, S64_4])
+def test_fallback_for_k_not_multiple_of_4(name):
+    say(f"{name} fallback")
+    C, Cref, _ = run_variant(200, 136, 102, "int", [5, 6, 8], name)
     check_padding_untouched(C)
-    check_exact(C.view, Cref, f"{S64} fallback")
+    check_exact(C.view, Cref, f"{name} fallback")
+
+
+def test_stage_counts_give_the_same_bits():
+    """The forms run the same instructions on the same fragments in the same
+    order: the same bits."""
+    outs = []
+    gen = torch.Generator(device="cuda").manual_seed(10)
+    X = torch.rand((1000, 1000), device="cuda", generator=gen) * 2 - 1
+    Y = torch.rand((1000, 1000), device="cuda", generator=gen) * 2 - 1
+    for name in (S64, S64_2, S64_4):
+        say(f"{name} same bits")
+        C = torch.empty((1000, 1000), device="cuda")
+        binding.gemm_f32_variant(variant_number(name), 1000, 1000, 1000, X, 1000, Y, 1000, C, 1000)
+        outs.append(C)
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
 
 
 OPS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
