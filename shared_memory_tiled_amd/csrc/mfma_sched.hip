@@ -775,12 +775,13 @@ void gemm_f32_ksplit_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m, u
 }
 
 // 64 x 64 tiles of 2 x 2 waves, each one 32 x 32 block over the whole K,
-// from NST (2 or 4) LDS stages of the four-wave schedule's layouts.  Phase
-// ph reads stage ph % NST and, after its barrier, copies phase ph + NST
-// into that stage.  With two stages (16 KB each) four blocks share a CU and
-// one block's waits overlap the others' work; with four, copies run three
-// phases ahead, for products with one block per CU (a phase is only 16
-// matrix instructions, about 1000 clocks).  The barrier of phase ph comes
+// from NST (2, 3 or 4) LDS stages of 16 KB in the four-wave schedule's
+// layouts.  Phase ph reads stage ph % NST and, after its barrier, copies
+// phase ph + NST into that stage.  Several blocks share a CU -- four with
+// two stages, three with three (the configuration the tile choice runs),
+// two with four -- so one block's start, end and waits overlap the others'
+// work, and the copies run NST - 1 phases ahead (a phase is only 16 matrix
+// instructions, about 1000 clocks).  The barrier of phase ph comes
 // between steps 2 and 3, once every wave's copies of phase ph + 1 have
 // landed and its reads of phase ph's fragments have completed; it is the
 // bare s_barrier, as a fence would also wait for the copies of later
