@@ -522,7 +522,10 @@ def bench_shape_sweep(args) -> int:
         return flop / statistics.median(graph_ms_per_launch(fn, reps, replays=3)) / 1e9
 
     gen = torch.Generator(device="cuda").manual_seed(20261202)
-    for (M, N, K) in SWEEP_SHAPES:
+    shapes = SWEEP_SHAPES
+    if args.shapes:                     # e.g. 3072x3072x3072,4352x4352x4352
+        shapes = [tuple(int(x) for x in sh.split("x")) for sh in args.shapes.split(",")]
+    for (M, N, K) in shapes:
         X = (torch.rand((M, K), device="cuda", generator=gen) * 2 - 1).to(dtype)
         Y = (torch.rand((K, N), device="cuda", generator=gen) * 2 - 1).to(dtype)
         out = torch.empty((M, N), device="cuda")
@@ -854,6 +857,7 @@ def main(argv=None) -> int:
     ap.add_argument("--valu-probe", action="store_true",
                     help="issue rate of non-packed v_fmac_f32 (the register-blocked rung's instruction)")
     ap.add_argument("--shape-sweep", action="store_true")
+    ap.add_argument("--shapes", default=None, help="--shape-sweep on these MxNxK shapes (comma separated) only")
     ap.add_argument("--settle-s", type=float, default=None,
                     help="untimed run of each timed step, in seconds, before its warm-up steps "
                          f"(default {SETTLE_S}; {HEADLINE_SETTLE_S} for the headline line)")
