@@ -48,12 +48,13 @@ Extra modes (used for counter runs under rocprofv3):
     --valu-probe        the issue rate of non-packed v_fmac_f32 on the vector
                         ALU in three operand forms, with the measured clock
                         (the register-blocked rung's ceiling)
-    --shape-sweep       the tile choice on 33 shapes (512^3 .. 8192^3,
+    --shape-sweep       the tile choice on 37 shapes (512^3 .. 8192^3,
                         rectangular and awkward ones): TFLOP/s of the default
                         configuration, of every candidate configuration and
                         of torch.matmul (hipBLASLt, for context), one JSON
                         line per shape (see bench_shape_sweep); with --row
-                        mixed, of gemm_mixed in --format
+                        mixed, of gemm_mixed in --format; --shapes MxNxK,...
+                        runs those shapes only
 """
 from __future__ import annotations
 
