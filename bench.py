@@ -484,7 +484,7 @@ SWEEP_CANDIDATES = ["mfma64x64_bk32_w2x2_k4", "mfma64x64_bk16_w2x2_k4", "mfma64x
 MIXED_SWEEP_CANDIDATES = ["mixed64x64_bk64_w1x2", "mixed64x64_bk32_w4_ksplit", "mixed128x128_bk64_w2x2_directAB",
                           "mixed256x256_bk64_w2x4_directAB", "mixed256x256_bk64_w4_sched",
                           "mixed256x256_bk64_w4_wide", "mixed256x256_bk32_w4_wide4stage", "mixed128x128_bk32_w4_ksplit",
-                          "mixed192x192_bk64_w4_wide", "mixed256x256_rowsplit"]
+                          "mixed192x192_bk64_w4_wide", "mixed256x256_rowsplit", "mixed160x160_bk64_w4_wide"]
 
 
 def bench_shape_sweep(args) -> int:

@@ -55,9 +55,11 @@ hipError_t launch_ksplit128(const Gemm16Args& p, hipStream_t s, int format, int 
 // with tile-row groups of group_m.
 bool wide_fits(const Gemm16Args& p, int op_a, int op_b);
 hipError_t launch_wide16(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m);
-// The same kernel on 192 x 192 tiles (each wave 96 x 96), for problems whose
-// 256 x 256 tiles fill the CUs' rounds badly; the same problems fit.
+// The same kernel on 192 x 192 tiles (each wave 96 x 96) or 160 x 160 tiles
+// (80 x 80), for problems whose 256 x 256 tiles fill the CUs' rounds badly;
+// the same problems fit.
 hipError_t launch_wide16_192(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m);
+hipError_t launch_wide16_160(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m);
 // The same product with four 32-deep LDS stages (mfma16_wide4.hip), as
 // stored (A k-contiguous, B mn-contiguous) only.
 hipError_t launch_wide16_4stage(const Gemm16Args& p, hipStream_t s, int format, int group_m);

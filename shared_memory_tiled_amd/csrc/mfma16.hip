@@ -1126,6 +1126,15 @@ hipError_t launch_wide192_cfg(const Gemm16Args& p, hipStream_t s, int /*tiles_m*
     return launch16<FMT, 256, 256, 2, 4, false, false, false>(p, s, tm, tn, kSchedGroupM, nb);
 }
 
+// Configuration 15 (the same kernel on 160 x 160 tiles), with the same
+// fallback as configuration 13.
+template <int FMT, bool VEC>
+hipError_t launch_wide160_cfg(const Gemm16Args& p, hipStream_t s, int /*tiles_m*/, int /*tiles_n*/,
+                              int /*group_m*/, unsigned /*blocks*/) {
+    if (VEC && wide_fits(p, 0, 0)) return launch_wide16_160(p, s, FMT, 0, 0, kWide192GroupM);
+    return launch_wide192_cfg<FMT, VEC>(p, s, 0, 0, 0, 0u);   // wide_fits fails there too
+}
+
 // Rows split (configuration 14): the first 256 m1 rows of op(A) -- whole
 // tile rows filling all but the last round of 256 CUs -- on 256 x 256 tiles
 // of the 16 x 16 x 32 scheduled kernel, the rest on 128 x 128 tiles whose
@@ -1215,6 +1224,11 @@ const MixedConfig kMixed[] = {
     {"mixed256x256_rowsplit", 256, 256, kSchedGroupM,
      {{launch16<0, 256, 256, 2, 4, false, false, false>, launch_rowsplit_cfg<0>},
       {launch16<1, 256, 256, 2, 4, false, false, false>, launch_rowsplit_cfg<1>}}},
+    // configuration 10's kernel on 160 x 160 tiles; misaligned operands: the
+    // element-wise 8-wave kernel on 256 x 256 tiles, as for 13
+    {"mixed160x160_bk64_w4_wide", 160, 160, kWide192GroupM,
+     {{launch_wide160_cfg<0, false>, launch_wide160_cfg<0, true>},
+      {launch_wide160_cfg<1, false>, launch_wide160_cfg<1, true>}}},
 };
 #undef MIXED
 constexpr int kNumMixed = (int)(sizeof(kMixed) / sizeof(kMixed[0]));
@@ -1223,6 +1237,7 @@ constexpr int kWideConfig = 10;           // mixed256x256_bk64_w4_wide
 constexpr int kKsplit128Config = 12;      // mixed128x128_bk32_w4_ksplit
 constexpr int kWide192Config = 13;        // mixed192x192_bk64_w4_wide
 constexpr int kRowsplitConfig = 14;       // mixed256x256_rowsplit
+constexpr int kWide160Config = 15;        // mixed160x160_bk64_w4_wide
 
 // op kernels, chosen by tile, op pair and load path
 template <int FMT, int BM, int BN, int WM, int WN, bool KCA, bool KCB, bool VEC>
@@ -1253,7 +1268,8 @@ Launch16 op_launcher(int op_a, int op_b, bool vec) {
 // kernel on v_mfma_f32_16x16x32, mfma16_wide.hip, where it fits, else eight
 // waves of gemm16_op_kernel) or 192 x 192 (the same kernel) once there are
 // 128 tiles of 256, else the k-split kernels, 192 x 192 tiles or 128 x 128
-// tiles of four waves; where the 192 x 192 or k-split kernels do not fit,
+// tiles of four waves, or 160 x 160 tiles; where the 192 x 192, 160 x 160 or
+// k-split kernels do not fit,
 // the 256 x 256 or 128 x 128 tiles by the same count.  A and B are the stored matrices; vector loads (and
 // the direct copies) need 4-byte aligned bases and even leading dimensions,
 // as for gemm_mixed.
@@ -1267,6 +1283,8 @@ hipError_t launch_mixed_op(const Gemm16Args& p, hipStream_t s, int format, int o
         return launch_ksplit128(p, s, format, op_a, op_b, kKsplit128GroupM);
     if (pick == kWide192Config && wide_fits(p, op_a, op_b))
         return launch_wide16_192(p, s, format, op_a, op_b, kWide192GroupM);
+    if (pick == kWide160Config && wide_fits(p, op_a, op_b))
+        return launch_wide16_160(p, s, format, op_a, op_b, kWide192GroupM);
     if (pick == kRowsplitConfig && rowsplit_rows(p.M, p.N) > 0 && wide_fits(p, op_a, op_b))
         return launch_rowsplit(p, s, format, op_a, op_b);
     const bool big = t256 >= 128;
@@ -1319,7 +1337,12 @@ const char* mixed_config_name(int c) { return (c >= 0 && c < kNumMixed) ? kMixed
 // element by element: 1000 x 2000 x 500 145 against 94, 1500 x 3000 x 700
 // 331 against 185, 1000^2 x 2002 102 against 50 on 64 x 64 tiles, 800 x
 // 1200 x 3002 105 against 50; 1536^2 x 1538 244 against 274, 1024^2 x 4092
-// 129 against 155).  Else 128 x 128 tiles with
+// 129 against 155).  Wherever 192 x 192 tiles are chosen, 160 x 160 ones
+// (configuration 15) if they need no more rounds of 256 CUs: a round of
+// them is the cheaper, its tiles having 0.69 of the area (bf16: 2560^3 861
+// against 796 TFLOP/s, 2304^3 707 against 660, 1280 x 5120 x 2048 834
+// against 780, 2560^2 x 1024 655 against 602; with one round more they lose:
+// 2816^3 590 against 988, 2048 x 4096 x 1024 500 against 724).  Else 128 x 128 tiles with
 // both factors copied straight into LDS from 128 of them (64 for K of at
 // least 2048), else 64 x 64 tiles.
 int mixed_pick_config(int M, int N, int K) {
@@ -1327,16 +1350,19 @@ int mixed_pick_config(int M, int N, int K) {
     const int64_t t192 = (int64_t)ceil_div(M, 192) * ceil_div(N, 192);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
     const bool even_k = K > 0 && K % 2 == 0;
+    const int64_t t160 = (int64_t)ceil_div(M, 160) * ceil_div(N, 160);
     const int64_t r256 = (t256 + 255) / 256, r192 = (t192 + 255) / 256;   // rounds of 256 CUs
+    const int64_t r160 = (t160 + 255) / 256;
+    const int narrow = r160 <= r192 ? kWide160Config : kWide192Config;    // where 192 tiles win
     if (t256 >= 128) {
-        if (even_k && 4 * r192 < 5 * r256) return kWide192Config;
+        if (even_k && 4 * r192 < 5 * r256) return narrow;
         const int64_t last = t256 - 256 * (r256 - 1);      // tiles in the last round
         return K % 8 == 0 && 5 * last < 2 * 256 && rowsplit_rows(M, N) > 0 ? kRowsplitConfig : kWideConfig;
     }
     if (t128 < 128 && K % 8 == 0 && K > 0) return kKsplitConfig;
     if (t128 <= 256 && K >= 1024 && K % 8 == 0) return kKsplit128Config;
     const bool ragged_k = K % 8 != 0 && t192 >= 32 && (K < 1536 || (t128 < 128 && K % 4 == 2));
-    if (even_k && (t192 >= 140 || ragged_k)) return kWide192Config;
+    if (even_k && (t192 >= 140 || ragged_k)) return narrow;
     if (t128 >= 128 || (t128 >= 64 && K >= 2048)) return 7;
     return 3;
 }

@@ -38,11 +38,16 @@ __device__ __forceinline__ u32x2 read_tr16(uint32_t lds_byte_addr) {
 // as operands, so no use of them can be scheduled before it.
 template <int N>
 __device__ __forceinline__ void wait_tied(u32x4 (&b)[N]) {
-    static_assert(N == 1 || N == 2 || N == 4 || N == 6 || N == 8, "fragment count");
+    static_assert(N == 1 || N == 2 || N == 4 || N == 5 || N == 6 || N == 8, "fragment count");
     if constexpr (N == 1) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]) : : "memory");
     if constexpr (N == 2) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]) : : "memory");
     if constexpr (N == 4)
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : : "memory");
+    if constexpr (N == 5)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4])
+                     :
+                     : "memory");
     if constexpr (N == 6)
         asm volatile("s_waitcnt lgkmcnt(0)"
                      : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]), "+v"(b[5])
@@ -61,6 +66,14 @@ __device__ __forceinline__ void wait_tied(u32x2 (&h)[8][2]) {
                  : "+v"(h[0][0]), "+v"(h[0][1]), "+v"(h[1][0]), "+v"(h[1][1]), "+v"(h[2][0]), "+v"(h[2][1]),
                    "+v"(h[3][0]), "+v"(h[3][1]), "+v"(h[4][0]), "+v"(h[4][1]), "+v"(h[5][0]), "+v"(h[5][1]),
                    "+v"(h[6][0]), "+v"(h[6][1]), "+v"(h[7][0]), "+v"(h[7][1])
+                 :
+                 : "memory");
+}
+
+__device__ __forceinline__ void wait_tied(u32x2 (&h)[5][2]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(h[0][0]), "+v"(h[0][1]), "+v"(h[1][0]), "+v"(h[1][1]), "+v"(h[2][0]), "+v"(h[2][1]),
+                   "+v"(h[3][0]), "+v"(h[3][1]), "+v"(h[4][0]), "+v"(h[4][1])
                  :
                  : "memory");
 }

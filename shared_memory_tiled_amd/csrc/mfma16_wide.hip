@@ -23,7 +23,11 @@
 // 192 values, the lanes of values 192..255 copying zeros).  Its copies need
 // 42.7 bytes per clock per CU at the full matrix rate against 32 for 256 x
 // 256 tiles: it is chosen only where its tile count fills the rounds of 256
-// CUs much better.
+// CUs much better.  Likewise 160 x 160 tiles: waves of 80 x 80 (5 x 5
+// blocks), steps of 25 instructions, 5 copies per wave and phase for a
+// k-contiguous factor and 8 for an mn-contiguous one (lanes of values
+// 160..255 copying zeros); 51.2 bytes per clock per CU at the full matrix
+// rate.
 //
 // The LDS tiles are laid out so that at most two per-lane bases per factor
 // serve every fragment, step and read of a phase (all the rest are
@@ -150,18 +154,21 @@ using WideTile = std::conditional_t<KC, WideTileKC<BT>, WideTileMC<BT>>;
 // Waits until at most N copies of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_copies_below() {
-    static_assert(N == 12 || N == 14 || N == 16, "copy count");
+    static_assert(N == 10 || N == 12 || N == 13 || N == 14 || N == 16, "copy count");
+    if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    if constexpr (N == 13) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
     if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     if constexpr (N == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
     if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
 }
 
-// BT: the tile's extent in M and N (256, or 192 for problems whose 256 x 256
-// tiles fill the CUs' rounds badly); each wave holds a quarter of it.
+// BT: the tile's extent in M and N (256, or 192 or 160 for problems whose
+// 256 x 256 tiles fill the CUs' rounds badly); each wave holds a quarter of
+// it.
 template <int FMT, bool KCA, bool KCB, int BT = 256>
 __global__ __launch_bounds__(256)
 void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
-    static_assert(BT == 256 || BT == 192, "tile");
+    static_assert(BT == 256 || BT == 192 || BT == 160, "tile");
     constexpr int BM = BT, BN = BT, WM = BT / 2, WN = BT / 2, BK = 64, FM = BT / 32, FN = BT / 32;
     using TA = WideTile<KCA, BT>;
     using TB = WideTile<KCB, BT>;
@@ -169,7 +176,10 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     constexpr int A_COPIES = TA::COPIES, NCOPY = TA::COPIES + TB::COPIES;   // per wave and phase
     constexpr int NMFMA = FM * FN;                        // matrix instructions per step
     constexpr int NREAD = TA::READS + TB::READS;          // LDS reads per step
-    static_assert(NREAD <= 2 * NMFMA / 3, "one read per matrix instruction, in the first two thirds of a step");
+    // One read after each of the first NREAD matrix instructions of a step:
+    // within its first two thirds, or four fifths for the 25 instructions of
+    // a 160 tile with both factors mn-contiguous (20 reads).
+    static_assert(NREAD <= (BT == 160 ? 4 * NMFMA / 5 : 2 * NMFMA / 3), "reads within the step");
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * (SA + SB)];
 
     const int tid = threadIdx.x;
@@ -189,7 +199,7 @@ void gemm16_wide_kernel(Gemm16Args p, int tiles_m, int tiles_n, int group_m) {
     // Copies 0 .. A_COPIES - 1 fill A's tile, the rest B's (byte offsets: the
     // launcher keeps both operands below 2^31 bytes with a tile's overhang, so
     // a past-the-end offset plus any phase's scalar offset stays below 2^32).
-    // Lanes of an mn-contiguous factor's copies beyond a 192-wide tile copy
+    // Lanes of an mn-contiguous factor's copies beyond a narrower tile copy
     // zeros into unread bytes: their offsets lie past the end in every phase.
     constexpr uint32_t kPastEnd = 0x80000000u;              // beyond any descriptor here
     constexpr int CMAX = TA::COPIES > TB::COPIES ? TA::COPIES : TB::COPIES;
@@ -483,6 +493,10 @@ hipError_t launch_wide16(const Gemm16Args& p, hipStream_t s, int format, int op_
 
 hipError_t launch_wide16_192(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m) {
     return launch_wide_tiles<192>(p, s, format, op_a, op_b, group_m);
+}
+
+hipError_t launch_wide16_160(const Gemm16Args& p, hipStream_t s, int format, int op_a, int op_b, int group_m) {
+    return launch_wide_tiles<160>(p, s, format, op_a, op_b, group_m);
 }
 
 }  // namespace gemmf32

@@ -430,8 +430,11 @@ def test_default_variant_choices(binding):
         (2048, 4096, 1024): "mixed192x192_bk64_w4_wide",          # 128 tiles of 256, 242 of 192
         (1024, 8192, 2048): "mixed256x256_bk64_w4_wide",          # 258 tiles of 192: 2 rounds
         (2816, 2816, 2816): "mixed192x192_bk64_w4_wide",          # 121 of 256, 225 of 192
-        (2560, 2560, 2560): "mixed192x192_bk64_w4_wide",          # 100 tiles of 256, 196 of 192
-        (2304, 2304, 2304): "mixed192x192_bk64_w4_wide",          # 144 tiles of 192
+        (2816, 2816, 1024): "mixed192x192_bk64_w4_wide",          # 324 tiles of 160: 2 rounds
+        (2560, 2560, 2560): "mixed160x160_bk64_w4_wide",          # 196 of 192, 256 of 160: 1 round
+        (2304, 2304, 2304): "mixed160x160_bk64_w4_wide",          # 144 tiles of 192, 225 of 160
+        (1280, 5120, 2048): "mixed160x160_bk64_w4_wide",          # 189 of 192, 256 of 160
+        (2390, 2470, 200): "mixed160x160_bk64_w4_wide",           # 169 of 192, 240 of 160
         (1024, 4096, 1024): "mixed128x128_bk32_w4_ksplit",        # 256 tiles of 128, long K
         (1536, 2560, 768): "mixed128x128_bk64_w2x2_directAB",     # 112 tiles of 192
         (2560, 2560, 2561): "mixed128x128_bk64_w2x2_directAB",    # odd K
@@ -444,9 +447,9 @@ def test_default_variant_choices(binding):
         (1000, 1000, 1000): "mixed64x64_bk32_w4_ksplit",
         (512, 512, 8192): "mixed64x64_bk32_w4_ksplit",
         (1024, 1024, 4092): "mixed128x128_bk64_w2x2_directAB",    # K % 8 = 4, long K: 64 tiles of 128
-        (1000, 1000, 2002): "mixed192x192_bk64_w4_wide",          # K % 4 = 2, 64 tiles of 128
-        (800, 1200, 3002): "mixed192x192_bk64_w4_wide",           # K % 4 = 2, 35 tiles of 192
-        (1000, 2000, 500): "mixed192x192_bk64_w4_wide",           # K % 8 = 4: 66 tiles of 192
+        (1000, 1000, 2002): "mixed160x160_bk64_w4_wide",          # K % 4 = 2, 64 tiles of 128
+        (800, 1200, 3002): "mixed160x160_bk64_w4_wide",           # K % 4 = 2, 35 tiles of 192
+        (1000, 2000, 500): "mixed160x160_bk64_w4_wide",           # K % 8 = 4: 66 tiles of 192
         (1536, 1536, 1538): "mixed128x128_bk64_w2x2_directAB",    # K % 8 = 2, 144 tiles of 128, long K
         (512, 512, 1002): "mixed64x64_bk64_w1x2",                 # K % 8 = 2, 9 tiles of 192
         (1000, 1000, 1001): "mixed64x64_bk64_w1x2",

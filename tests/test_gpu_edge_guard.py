@@ -35,7 +35,8 @@ FP32_CASES = {
     "mfma64x64_bk32_w1x1_k4_sched": (556, 572, 1004),
     "mfma64x64_bk32_w2x2_sched": (1532, 1028, 388),
 }
-MIXED_CASES = {"mixed256x256_bk64_w4_wide": (3580, 3330, 200), "mixed192x192_bk64_w4_wide": (3068, 3068, 200)}
+MIXED_CASES = {"mixed256x256_bk64_w4_wide": (3580, 3330, 200), "mixed192x192_bk64_w4_wide": (3068, 3068, 200),
+               "mixed160x160_bk64_w4_wide": (2390, 2470, 200)}
 
 
 def stored(op, rows, cols):

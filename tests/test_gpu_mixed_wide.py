@@ -179,8 +179,9 @@ def test_misaligned_operands_fall_back_correctly():
     check_padding_untouched(C)
 
 
-def run_sampled(fmt, M, N, K, dist, seed, count=4096, rows=()):
-    """gemm_mixed on padded, offset, guarded operands of a full-size shape,
+def run_sampled(fmt, M, N, K, dist, seed, count=4096, rows=(), variant=None):
+    """gemm_mixed (or configuration `variant`) on padded, offset, guarded
+    operands of a full-size shape,
     checked on `count` sampled entries plus the corners, every tile edge's
     last row and column and the whole of each row in `rows`: returns (C,
     the results at those entries, the oracle's values, the oracle's S)."""
@@ -194,10 +195,14 @@ def run_sampled(fmt, M, N, K, dist, seed, count=4096, rows=()):
     a = torch.from_numpy(A.buf.view(np.int16)).cuda()
     b = torch.from_numpy(B.buf.view(np.int16)).cuda()
     c = torch.from_numpy(C0.buf).cuda()
-    binding.gemm_mixed(fmt, M, N, K, a.data_ptr() + 4, A.ld, b.data_ptr() + 4, B.ld, c.data_ptr() + 4, ldc)
+    args = (fmt, M, N, K, a.data_ptr() + 4, A.ld, b.data_ptr() + 4, B.ld, c.data_ptr() + 4, ldc)
+    if variant is not None:
+        binding.gemm_mixed_variant(variant, *args)
+    else:
+        binding.gemm_mixed(*args)
     torch.cuda.synchronize()
     C = inputs.Padded(c.cpu().numpy(), M, N, ldc, 1)
-    ii, jj = inputs.sample_pairs(M, N, count, np.random.default_rng([seed, 1]), tiles=(64, 128, 192, 256))
+    ii, jj = inputs.sample_pairs(M, N, count, np.random.default_rng([seed, 1]), tiles=(64, 128, 160, 192, 256))
     if len(rows):
         ii = np.concatenate([ii, np.repeat(np.asarray(rows, np.int64), N)])
         jj = np.concatenate([jj, np.tile(np.arange(N, dtype=np.int64), len(rows))])

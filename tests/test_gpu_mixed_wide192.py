@@ -74,9 +74,10 @@ def test_fallback_for_problems_it_does_not_take(case):
 
 
 OPS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
-# shapes gemm_mixed_op gives to this kernel: 144 tiles of 192 (fewer than
-# 128 of 256, more than 256 of 128); 12 x 14 edge tiles with K % 8 = 2
-OP_SHAPES = [(2304, 2304, 64), (2200, 2500, 130)]
+# shapes gemm_mixed_op gives to this kernel: 225 tiles of 192 (fewer than
+# 128 of 256, more than 256 of 128 or of 160); 15 x 16 edge tiles with K %
+# 8 = 2
+OP_SHAPES = [(2816, 2816, 64), (2700, 2900, 130)]
 
 
 @pytest.mark.parametrize("ops", OPS, ids=["".join(o) for o in OPS])

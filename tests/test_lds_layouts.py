@@ -751,14 +751,14 @@ def wide_read(kc, lane, mn, s, f, h):
     return 1056 * (j // 4 + 4 * g) + 2 * (mn + 4 * (j % 4)) + (16896 * s + 32 * f + 512 * h)
 
 
-@pytest.mark.parametrize("bt", [256, 192])
+@pytest.mark.parametrize("bt", [256, 192, 160])
 @pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
 def test_wide16_kernel_layout(kc, bt):
     """The 16 x 16 x 32 scheduled kernel's tile stage (bt mn x 64 k, bt =
-    256 or 192), restated: the copies (KC bt / 32 per wave, MC 8) fill every
-    (mn, k) exactly once (the MC stage's padding is never written; with bt =
-    192 the lanes of an MC copy past the tile bring zeros into the last 128
-    bytes of each 512-byte row slot, which no read touches); every lane's
+    256, 192 or 160), restated: the copies (KC bt / 32 per wave, MC 8) fill
+    every (mn, k) exactly once (the MC stage's padding is never written; with
+    bt < 256 the lanes of an MC copy past the tile bring zeros into the last
+    512 - 2 bt bytes of each 512-byte row slot, which no read touches); every lane's
     fragment reads deliver the operands v_mfma_f32_16x16x32 needs -- for the
     wave's span at mn, block f of step s, lane l supplies op(X)[mn + 16 f + l
     % 16][32 s + 8 (l / 16) + e], e = 0..7; both reads conflict free on 64
@@ -811,15 +811,15 @@ def test_wide16_kernel_layout(kc, bt):
                         assert vals[lane] == want, (mn, s, f, lane)
 
 
-@pytest.mark.parametrize("bt", [256, 192])
+@pytest.mark.parametrize("bt", [256, 192, 160])
 @pytest.mark.parametrize("kc", [True, False], ids=["k_contiguous", "mn_contiguous"])
 @pytest.mark.parametrize("shape", [(3068, 200, 3072), (2814, 72, 2818), (256, 64, 256), (4100, 8, 4100)])
 def test_wide16_copies_never_depend_on_the_scalar_offset(kc, shape, bt):
-    """16 x 16 x 32 scheduled kernel (256 or 192 tiles): the rule of the 32 x
+    """16 x 16 x 32 scheduled kernel (256, 192 or 160 tiles): the rule of the 32 x
     32 x 16 one with its own copy map -- phases before the last take the
     phase in the scalar offset, the last phase's per-lane offsets hold it
     with a scalar offset of 0 and point lanes at k >= K past the end; lanes
-    of an mn-contiguous copy beyond a 192 tile are past the end in every
+    of an mn-contiguous copy beyond a narrower tile are past the end in every
     phase; only a chunk of the mn-contiguous factor's last row across its
     last column may straddle the descriptor's end, by whole dwords."""
     ext, K, ld_mn = shape
