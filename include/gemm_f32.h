@@ -404,6 +404,9 @@ int reduce_sum_f32_variant_noalloc(int variant, int64_t n, const float *x, float
  * 0.8 of a 256 tile's time each, or, below 128 tiles of 256 x 256, with at
  * least 140 of 192 x 192 or, for K % 8 != 0, 32 of them with K < 1536 (or
  * K % 4 == 2 and fewer than 128 tiles of 128 x 128)),
+ * mixed160x160_bk64_w4_wide (the same kernel on 160 x 160 tiles; their
+ * choice wherever 192 x 192 tiles would be, if the 160 x 160 ones need no
+ * more rounds of the 256 CUs),
  * mixed256x256_rowsplit (their choice, with K a multiple of 8, where the
  * last round of 256 x 256 tiles would be under 40 % full: the rows filling
  * the other rounds on the 256 x 256 kernel, the remaining rows on k-split
@@ -411,7 +414,7 @@ int reduce_sum_f32_variant_noalloc(int variant, int64_t n, const float *x, float
  * launches in stream order),
  * mixed256x256_bk64_w4_sched (the same schedule on v_mfma_f32_32x32x16) and
  * mixed256x256_bk32_w4_wide4stage (16x16x32 with four 32-deep LDS stages) --
- * take K a multiple of 8 (the two 16x16x32 wide ones: K even), N even (M
+ * take K a multiple of 8 (the 16x16x32 wide ones on 256, 192 and 160 tiles: K even), N even (M
  * too for A stored transposed in gemm_mixed_op, and not N for B stored
  * transposed), 4-byte aligned operands with even leading dimensions and
  * operands under 2^31 bytes; edge tiles run whole and store only inside C,
