@@ -1139,7 +1139,9 @@ hipError_t launch_wide160_cfg(const Gemm16Args& p, hipStream_t s, int /*tiles_m*
 // tile rows filling all but the last round of 256 CUs -- on 256 x 256 tiles
 // of the 16 x 16 x 32 scheduled kernel, the rest on 128 x 128 tiles whose
 // four waves split the phases (if those are at most 256 and it takes the
-// problem), else on 192 x 192 tiles; two launches in stream order, each part
+// problem), else on 160 x 160 tiles if they need no more rounds of 256 CUs
+// than 192 x 192 ones, else on 192 x 192 tiles; two launches in stream
+// order, each part
 // with the bits its kernel gives alone.  Where the 256 x 256 kernel does
 // not take the problem, or there is no such split, configuration 10 runs
 // the whole product.  op_a / op_b: 1 if that factor is stored transposed.
@@ -1162,6 +1164,9 @@ hipError_t launch_rowsplit(const Gemm16Args& p, hipStream_t s, int format, int o
     const int64_t t128 = (int64_t)ceil_div(rest.M, 128) * ceil_div(rest.N, 128);
     if (t128 <= 256 && ksplit128_fits(rest, op_a, op_b))
         return launch_ksplit128(rest, s, format, op_a, op_b, kKsplit128GroupM);
+    const int64_t r160 = ((int64_t)ceil_div(rest.M, 160) * ceil_div(rest.N, 160) + 255) / 256;
+    const int64_t r192 = ((int64_t)ceil_div(rest.M, 192) * ceil_div(rest.N, 192) + 255) / 256;
+    if (r160 <= r192) return launch_wide16_160(rest, s, format, op_a, op_b, kWide192GroupM);
     return launch_wide16_192(rest, s, format, op_a, op_b, kWide192GroupM);
 }
 template <int FMT>

@@ -1,13 +1,15 @@
 """The row-split configuration (mixed256x256_rowsplit): the rows of op(A)
 that fill all but the last round of 256 CUs with 256 x 256 tiles of the
 16 x 16 x 32 scheduled kernel, the remaining rows on k-split 128 x 128
-tiles (at most 256 of them) or on 192 x 192 tiles, against the 16-bit
-oracle: exact on integer inputs, within 1e-5 S on uniform ones.
+tiles (at most 256 of them), on 160 x 160 tiles (if they need no more
+rounds of 256 CUs than 192 x 192 ones) or on 192 x 192 tiles, against the
+16-bit oracle: exact on integer inputs, within 1e-5 S on uniform ones.
 
 The shapes put the split at 3840 rows with 512 left (k-split rest), at
-3584 with 1024 left (192 x 192 rest), the same with K % 8 = 2 (192 x 192
-rest: the k-split kernel takes K a multiple of 8 only), and edge tiles on
-both sides with 766 rows left; offset views with padding and 40 rows of NaN
+3584 with 1024 left (160 x 160 rest), at 3328 with 1280 left and K % 8 = 2
+(160 x 160 rest: the k-split kernel takes K a multiple of 8 only), at 2560
+with 2048 left of 6400 columns (192 x 192 rest: 374 tiles, against 520 of
+160 x 160), and edge tiles on both sides with 766 rows left; offset views with padding and 40 rows of NaN
 after every factor; every op pair through gemm_mixed_op, bit-identical to
 the plain product on transposed copies; problems it does not take
 (misaligned views, odd K) run configuration 10's kernels."""
@@ -24,7 +26,7 @@ pytestmark = pytest.mark.gpu
 
 SPLIT = "mixed256x256_rowsplit"
 
-SHAPES = [(4352, 4352, 64), (4608, 4608, 72), (4608, 4610, 66), (4350, 4354, 136)]
+SHAPES = [(4352, 4352, 64), (4608, 4608, 72), (4608, 4610, 66), (4608, 6400, 64), (4350, 4354, 136)]
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
