@@ -410,8 +410,9 @@ int reduce_sum_f32_variant_noalloc(int variant, int64_t n, const float *x, float
  * mixed256x256_rowsplit (their choice, with K a multiple of 8, where the
  * last round of 256 x 256 tiles would be under 40 % full: the rows filling
  * the other rounds on the 256 x 256 kernel, the remaining rows on k-split
- * 128 x 128 tiles if at most 256 of them, else on 192 x 192 tiles; two
- * launches in stream order),
+ * 128 x 128 tiles if at most 256 of them, else on 160 x 160 tiles if they
+ * need no more rounds of the 256 CUs than 192 x 192 ones, else on 192 x 192
+ * tiles; two launches in stream order),
  * mixed256x256_bk64_w4_sched (the same schedule on v_mfma_f32_32x32x16) and
  * mixed256x256_bk32_w4_wide4stage (16x16x32 with four 32-deep LDS stages) --
  * take K a multiple of 8 (the 16x16x32 wide ones on 256, 192 and 160 tiles: K even), N even (M
